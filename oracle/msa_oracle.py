@@ -1,0 +1,322 @@
+"""fp64 CPU oracle for block-sparse attention over a paged KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+baseline leg of the benchmark may import this module; the library's product
+path never does, and this module imports nothing from the library.
+
+What is computed (plain definitions, no blocking, fusion or split):
+
+* Sources.  The sglang page ``minimax_sparse_backend.py``
+  (``MiniMaxSparseAttnBackend.__init__``) derives ``init_blocks``,
+  ``local_blocks`` and ``topk_blocks`` for a per-token selection
+  (``block_size_q = 1``, ``block_size_k`` = 128) and hands the index-head
+  query/keys to the sparse decode/prefill ops; the vLLM page
+  ``sparse_attention_msa.py`` (``MiniMaxM3SparseMSAImpl.forward``) runs
+  causal attention (``causal=True``) over the selected 128-token KV blocks of
+  a paged cache, with fp8 K/V scales (``k_scale``/``v_scale``).  The score
+  type is left open by the pages; the reading used here is: a block's score
+  is the maximum over its visible tokens of ``q_idx . k_idx``, and equal
+  scores go to the lower block index.
+
+* Every floating-point value is decoded exactly to float64 first (bf16 by
+  its bit layout, fp8-e4m3fn through a table built from the format
+  definition); all arithmetic after that is float64.
+
+Readings of the pages taken here (each also recorded with the design notes):
+
+* top-k is drawn from the blocks that are not forced, and the result is the
+  union with the forced init and local blocks (|S| = min(nb, |F| + topk));
+* local blocks are the trailing ``local`` blocks ending at the query's own,
+  possibly partial, block; init blocks are the first ``init`` blocks;
+* tokens after the query position are invisible both to scoring and to
+  attention; decode attends to its own (already written) token;
+* head maps: q head ``hq`` reads kv head ``hq // (Hq/Hkv)``; kv head ``g``
+  uses index head ``g // (Hkv/Hidx)``;
+* selections are listed in ascending block order, -1 padded.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+BLOCK = 128
+
+
+# --------------------------------------------------------------------------
+# Exact decoding of stored values
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f64(u16: np.ndarray) -> np.ndarray:
+    """bfloat16 is the top half of an IEEE binary32: shift the 16 stored
+    bits into the high half of a 32-bit word and reinterpret."""
+    u32 = np.asarray(u16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return u32.view(np.float32).astype(np.float64)
+
+
+def fp8_e4m3fn_table() -> np.ndarray:
+    """Values of the 256 OCP FP8 E4M3 ("e4m3fn") codes.
+
+    Layout s.eeee.mmm, exponent bias 7; exponent field 0 encodes subnormals
+    m/8 * 2^-6; no infinities; s.1111.111 is NaN.  The vLLM page's query
+    dequantisation notes that every E4M3 value is exact in bf16.
+    """
+    tab = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            tab[code] = math.nan
+        elif e == 0:
+            tab[code] = sign * (m / 8.0) * 2.0 ** (1 - 7)
+        else:
+            tab[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return tab
+
+
+_FP8_TABLE = None
+
+
+def decode(arr: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Stored representation -> float64 values (times ``scale`` for fp8)."""
+    global _FP8_TABLE
+    if dtype == "bf16":
+        return bf16_bits_to_f64(arr)
+    if dtype == "f32":
+        return np.asarray(arr, dtype=np.float32).astype(np.float64)
+    if dtype == "fp8":
+        if _FP8_TABLE is None:
+            _FP8_TABLE = fp8_e4m3fn_table()
+        return _FP8_TABLE[np.asarray(arr, dtype=np.uint8)] * float(scale)
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------
+# Query positions
+# --------------------------------------------------------------------------
+
+def query_positions(seq_lens: np.ndarray, cu_seqlens_q: Optional[np.ndarray]):
+    """List of (sequence b, position p) per query token.
+
+    Decode (no cu_seqlens_q): one query per sequence at p = L_b - 1.
+    Prefill: the n_b = cu[b+1]-cu[b] new tokens are the sequence's last ones,
+    p = L_b - n_b + i (the sglang page passes prefix lengths alongside
+    ``cu_seqlens``; the prefix is L_b - n_b).
+    """
+    out = []
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    if cu_seqlens_q is None:
+        for b, L in enumerate(seq_lens):
+            out.append((b, int(L) - 1))
+    else:
+        cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+        for b, L in enumerate(seq_lens):
+            n = int(cu[b + 1] - cu[b])
+            for i in range(n):
+                out.append((b, int(L) - n + i))
+    return out
+
+
+def num_visible_blocks(p: int) -> int:
+    """Blocks holding at least one token t <= p."""
+    return 0 if p < 0 else p // BLOCK + 1
+
+
+# --------------------------------------------------------------------------
+# Step 1: block scores from the index heads
+# --------------------------------------------------------------------------
+
+def block_scores_for_query(iq: np.ndarray, ik_rows: np.ndarray, p: int) -> np.ndarray:
+    """score[j] = max over tokens t of block j with t <= p of iq . ik[t].
+
+    ``ik_rows`` holds at least the sequence's tokens 0..p (float64).
+    """
+    nb = num_visible_blocks(p)
+    if nb == 0:
+        return np.zeros(0)
+    dots = ik_rows[: p + 1] @ iq                      # [p+1]
+    pad = nb * BLOCK - (p + 1)
+    dots = np.concatenate([dots, np.full(pad, -np.inf)])
+    return dots.reshape(nb, BLOCK).max(axis=1)
+
+
+def block_scores(inp: dict) -> np.ndarray:
+    """Scores [T, Hidx, max_blocks] float64; -inf for blocks past the query.
+
+    The queries of one sequence and index head are scored together with one
+    matrix product (chunks of 1024 queries); each row is then masked to its
+    own position and reduced per block exactly as ``block_scores_for_query``.
+    """
+    iq_all = decode(inp["idx_q"], inp["idx_dtype"])
+    T, Hidx, _ = iq_all.shape
+    MB = inp["block_table"].shape[1]
+    out = np.full((T, Hidx, MB), -np.inf)
+    pos = query_positions(inp["seq_lens"], inp.get("cu_seqlens_q"))
+    by_seq = {}
+    for t, (b, p) in enumerate(pos):
+        by_seq.setdefault(b, []).append((t, p))
+    for b, items in by_seq.items():
+        L = int(inp["seq_lens"][b])
+        if L <= 0:
+            continue
+        nbL = num_visible_blocks(L - 1)
+        for h in range(Hidx):
+            ik = decode(_gather_rows_raw(inp["idx_k_pool"], inp["block_table"][b], h, L),
+                        inp["idx_dtype"])
+            for c0 in range(0, len(items), 1024):
+                chunk = items[c0:c0 + 1024]
+                ts = np.array([t for t, _ in chunk])
+                ps = np.array([p for _, p in chunk])
+                dots = np.full((len(chunk), nbL * BLOCK), -np.inf)
+                dots[:, :L] = iq_all[ts, h] @ ik.T
+                tok = np.arange(nbL * BLOCK)
+                dots[tok[None, :] > ps[:, None]] = -np.inf
+                s = dots.reshape(len(chunk), nbL, BLOCK).max(axis=2)
+                for r, (t, p) in enumerate(chunk):
+                    nb = num_visible_blocks(p)
+                    out[t, h, :nb] = s[r, :nb]
+    return out
+
+
+def _gather_rows_raw(pool: np.ndarray, bt_row: np.ndarray, head: int, n_tokens: int):
+    """Raw stored rows 0..n_tokens-1 of one head of a sequence."""
+    nbk = (n_tokens + BLOCK - 1) // BLOCK
+    pages = np.asarray(bt_row[:nbk], dtype=np.int64)
+    rows = pool[pages, head].reshape(nbk * BLOCK, pool.shape[-1])
+    return rows[:n_tokens]
+
+
+# --------------------------------------------------------------------------
+# Step 2: forced blocks and top-k selection
+# --------------------------------------------------------------------------
+
+def forced_blocks(nb: int, init: int, local: int) -> list:
+    """Init blocks {0..init-1} and local blocks {nb-local..nb-1}, within [0,nb)."""
+    f = set(range(min(init, nb)))
+    f.update(range(max(0, nb - local), nb))
+    return sorted(f)
+
+
+def select_for_query(scores: np.ndarray, nb: int, topk: int, init: int, local: int) -> list:
+    """S = forced blocks plus the top-k of the others by (score desc, index asc),
+    returned in ascending block order."""
+    forced = forced_blocks(nb, init, local)
+    fset = set(forced)
+    cand = [j for j in range(nb) if j not in fset]
+    cand.sort(key=lambda j: (-float(scores[j]), j))
+    chosen = cand[: min(topk, len(cand))]
+    return sorted(fset.union(chosen))
+
+
+def kmax(topk: int, init: int, local: int) -> int:
+    return topk + init + local
+
+
+def select(inp: dict, scores: np.ndarray):
+    """sel [T, Hidx, Kmax] int32 (-1 padded, ascending) and count [T, Hidx]."""
+    T, Hidx, _ = scores.shape
+    K = kmax(inp["topk"], inp["init"], inp["local"])
+    sel = np.full((T, Hidx, K), -1, dtype=np.int32)
+    cnt = np.zeros((T, Hidx), dtype=np.int32)
+    pos = query_positions(inp["seq_lens"], inp.get("cu_seqlens_q"))
+    for t, (b, p) in enumerate(pos):
+        nb = num_visible_blocks(p)
+        for h in range(Hidx):
+            s = select_for_query(scores[t, h], nb, inp["topk"], inp["init"], inp["local"])
+            sel[t, h, : len(s)] = s
+            cnt[t, h] = len(s)
+    return sel, cnt
+
+
+# --------------------------------------------------------------------------
+# Step 3: exact softmax attention restricted to the selected blocks
+# --------------------------------------------------------------------------
+
+def visible_rows(blocks, p: int) -> np.ndarray:
+    """Token positions of the selected blocks that are <= p, ascending."""
+    rows = []
+    for j in sorted(blocks):
+        lo = j * BLOCK
+        hi = min(lo + BLOCK - 1, p)
+        rows.extend(range(lo, hi + 1))
+    return np.asarray(rows, dtype=np.int64)
+
+
+def softmax_attention(qh: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                      return_weights: bool = False):
+    """out[h] = sum_t w[h,t] v[t], w = softmax_t(scale * q[h] . k[t]);
+    lse[h] = log sum_t exp(scale * q[h] . k[t]).  qh [G,D], k/v [n,D]."""
+    G = qh.shape[0]
+    if k.shape[0] == 0:
+        o = np.zeros((G, v.shape[1]))
+        lse = np.full(G, -np.inf)
+        return (o, lse, np.zeros((G, 0))) if return_weights else (o, lse)
+    z = scale * (qh @ k.T)                            # [G, n]
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    s = e.sum(axis=1, keepdims=True)
+    w = e / s
+    o = w @ v
+    lse = (m + np.log(s))[:, 0]
+    return (o, lse, w) if return_weights else (o, lse)
+
+
+def attend(inp: dict, sel: np.ndarray, cnt: np.ndarray, scale: Optional[float] = None):
+    """out [T, Hq, D] and lse [T, Hq] for the given selection."""
+    q_all = decode(inp["q"], inp["q_dtype"])
+    T, Hq, D = q_all.shape
+    Hkv, Hidx = inp["Hkv"], inp["Hidx"]
+    G = Hq // Hkv
+    gpi = Hkv // Hidx
+    sc = (1.0 / math.sqrt(D)) if not scale else float(scale)
+    out = np.zeros((T, Hq, D))
+    lse = np.full((T, Hq), -np.inf)
+    pos = query_positions(inp["seq_lens"], inp.get("cu_seqlens_q"))
+    by_seq = {}
+    for t, (b, p) in enumerate(pos):
+        by_seq.setdefault(b, []).append((t, p))
+    for b, items in by_seq.items():
+        L = int(inp["seq_lens"][b])
+        if L <= 0:
+            continue
+        for g in range(Hkv):
+            kr = decode(_gather_rows_raw(inp["k_pool"], inp["block_table"][b], g, L),
+                        inp["kv_dtype"], inp.get("k_scale", 1.0))
+            vr = decode(_gather_rows_raw(inp["v_pool"], inp["block_table"][b], g, L),
+                        inp["kv_dtype"], inp.get("v_scale", 1.0))
+            h = g // gpi
+            for t, p in items:
+                blocks = sel[t, h, : cnt[t, h]]
+                rows = visible_rows(blocks, p)
+                o, l = softmax_attention(q_all[t, g * G:(g + 1) * G], kr[rows], vr[rows], sc)
+                out[t, g * G:(g + 1) * G] = o
+                lse[t, g * G:(g + 1) * G] = l
+    return out, lse
+
+
+def lse_combine(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Merge attention over disjoint key sets: lse = log sum_c exp(lse_c),
+    out = sum_c exp(lse_c - lse) o_c.  o_parts [C, ..., D], lse_parts [C, ...]."""
+    m = np.max(lse_parts, axis=0)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(lse_parts - m_safe)
+    s = w.sum(axis=0)
+    lse = np.where(s > 0, m_safe + np.log(np.where(s > 0, s, 1.0)), -np.inf)
+    wn = np.where(s > 0, w / np.where(s > 0, s, 1.0), 0.0)
+    return (wn[..., None] * o_parts).sum(axis=0), lse
+
+
+# --------------------------------------------------------------------------
+# Whole path
+# --------------------------------------------------------------------------
+
+def sparse_attention(inp: dict, scale: Optional[float] = None) -> dict:
+    """Score, select and attend for every query token (decode or prefill)."""
+    scores = block_scores(inp)
+    sel, cnt = select(inp, scores)
+    out, lse = attend(inp, sel, cnt, scale)
+    return dict(scores=scores, sel=sel, count=cnt, out=out, lse=lse)

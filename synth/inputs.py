@@ -1,0 +1,267 @@
+"""Seeded generator for paged block-sparse attention inputs.
+
+Recipe (applies to every workload below):
+
+* block = page = 128 tokens; pools are head-major per page ("HND"):
+  K, V ``[P, Hkv, 128, D]`` and index-K ``[P, Hidx, 128, Di]``.
+* Values are float32 N(0,1) draws rounded to the storage type with
+  round-to-nearest-even (bf16 / f32), or, for fp8-e4m3 pools, divided by the
+  per-tensor scale, clamped to +-448 and rounded to e4m3fn.
+* Physical page ids come from a seeded permutation; ``P`` = pages used plus
+  ``max(8, ceil(1%))`` spare pages.  Unused block-table entries are -1.
+* Poison: spare pages and the token slots past ``seq_len`` in every
+  sequence's last page hold NaN in K/V (bf16 0x7FC0, f32 NaN, fp8 0x7F) and
+  +1e4 in index-K, so that any read of an invalid slot shows up in results.
+* Draw order on one ``torch.Generator`` seeded with ``seed``: seq_lens,
+  permutation, q, idx_q, K, V, idx_K; pools are drawn in chunks of 256 pages.
+  The generator lives on ``device``, so CPU and GPU draws differ; every
+  consumer gets the bytes of one draw.
+
+Decode: one query per sequence at position ``seq_len - 1``.  Prefill: the
+``n_new`` new tokens of a sequence are its last ones, at positions
+``seq_len - n_new .. seq_len - 1``.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+BLOCK = 128
+PAGE_CHUNK = 256
+
+# The five workloads the library is measured and checked on, by shape.
+WORKLOADS = {
+    "decode_b2_l2048": dict(
+        kind="decode", B=2, seq_lens=("fixed", 2048), Hq=8, Hkv=1, Hidx=1,
+        D=128, Di=64, topk=4, init=1, local=2, q="bf16", kv="bf16", idx="bf16"),
+    "decode_b32_l32k": dict(
+        kind="decode", B=32, seq_lens=("fixed", 32768), Hq=16, Hkv=2, Hidx=2,
+        D=128, Di=128, topk=16, init=1, local=2, q="bf16", kv="bf16", idx="bf16"),
+    "decode_b64_lvar": dict(
+        kind="decode", B=64, seq_lens=("uniform", 4096, 131072), Hq=16, Hkv=2,
+        Hidx=2, D=128, Di=128, topk=32, init=1, local=2, q="bf16", kv="bf16",
+        idx="bf16"),
+    "prefill_4x4096_p16k": dict(
+        kind="prefill", B=4, n_new=4096, prefix=16384, Hq=16, Hkv=2, Hidx=2,
+        D=128, Di=128, topk=16, init=1, local=2, q="bf16", kv="bf16", idx="bf16"),
+    "decode_fp8_b32_l64k": dict(
+        kind="decode", B=32, seq_lens=("fixed", 65536), Hq=16, Hkv=2, Hidx=2,
+        D=128, Di=128, topk=32, init=1, local=2, q="bf16", kv="fp8", idx="bf16",
+        k_scale=1.0 / 16, v_scale=1.0 / 16),
+}
+
+# Seeds of the five workloads, in the order above.
+WORKLOAD_SEEDS = {name: 1001 + i for i, name in enumerate(WORKLOADS)}
+
+_TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}
+_POISON_KV = {"bf16": float("nan"), "f32": float("nan")}
+FP8_NAN_BYTE = 0x7F
+IDX_POISON = 1.0e4
+
+
+def workload(name: str, **overrides) -> dict:
+    spec = dict(WORKLOADS[name])
+    spec.update(overrides)
+    spec["name"] = name
+    return spec
+
+
+@dataclasses.dataclass
+class Case:
+    spec: dict
+    seq_lens: torch.Tensor          # [B] int32
+    cu_seqlens_q: Optional[torch.Tensor]  # [B+1] int32 (prefill) or None (decode)
+    block_table: torch.Tensor       # [B, MB] int32, -1 padded
+    q: torch.Tensor                 # [T, Hq, D]
+    idx_q: torch.Tensor             # [T, Hidx, Di]
+    k_pool: torch.Tensor            # [P, Hkv, 128, D] (fp8 pools are uint8)
+    v_pool: torch.Tensor
+    idx_k_pool: torch.Tensor        # [P, Hidx, 128, Di]
+    num_pages: int
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def B(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def T(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_table.shape[1])
+
+    def to(self, device) -> "Case":
+        f = {}
+        for fld in dataclasses.fields(self):
+            v = getattr(self, fld.name)
+            f[fld.name] = v.to(device) if isinstance(v, torch.Tensor) else v
+        return Case(**f)
+
+
+def _draw_seq_lens(spec, g, device) -> torch.Tensor:
+    B = spec["B"]
+    if spec["kind"] == "prefill":
+        n_new = spec["n_new"]
+        n_new = list(n_new) if isinstance(n_new, Sequence) else [n_new] * B
+        prefix = spec["prefix"]
+        prefix = list(prefix) if isinstance(prefix, Sequence) else [prefix] * B
+        return torch.tensor([a + b for a, b in zip(prefix, n_new)], dtype=torch.int32)
+    sl = spec["seq_lens"]
+    if isinstance(sl, (list, tuple)) and sl and sl[0] == "fixed":
+        return torch.full((B,), int(sl[1]), dtype=torch.int32)
+    if isinstance(sl, (list, tuple)) and sl and sl[0] == "uniform":
+        lo, hi = int(sl[1]), int(sl[2])
+        r = torch.randint(lo, hi + 1, (B,), generator=g, device=device)
+        return r.to(torch.int32).cpu()
+    return torch.tensor(list(sl), dtype=torch.int32)
+
+
+def _quantise(x: torch.Tensor, dtype: str, scale: float) -> torch.Tensor:
+    if dtype == "fp8":
+        y = (x / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+        return y.view(torch.uint8)
+    return x.to(_TORCH_DT[dtype])
+
+
+def _draw_pool(P, H, Dm, dtype, scale, g, device) -> torch.Tensor:
+    out_dt = torch.uint8 if dtype == "fp8" else _TORCH_DT[dtype]
+    pool = torch.empty((P, H, BLOCK, Dm), dtype=out_dt, device=device)
+    for p0 in range(0, P, PAGE_CHUNK):
+        p1 = min(P, p0 + PAGE_CHUNK)
+        x = torch.randn((p1 - p0, H, BLOCK, Dm), generator=g, device=device,
+                        dtype=torch.float32)
+        pool[p0:p1] = _quantise(x, dtype, scale)
+    return pool
+
+
+def _poison(pool: torch.Tensor, valid: torch.Tensor, dtype: str, value: float):
+    """Overwrite token slots ``t >= valid[page]`` of every page."""
+    tok = torch.arange(BLOCK, device=pool.device)
+    bad = tok[None, :] >= valid.to(pool.device)[:, None]          # [P,128]
+    bad = bad[:, None, :, None].expand(pool.shape)
+    if dtype == "fp8":
+        pool.masked_fill_(bad, FP8_NAN_BYTE)
+    else:
+        pool.masked_fill_(bad, value)
+
+
+def generate(spec: dict, seed: int, device="cpu", max_blocks: Optional[int] = None,
+             poison: bool = True, spare_pages: Optional[int] = None) -> Case:
+    """Draw one seeded case of ``spec`` on ``device`` (see the module recipe)."""
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    B, Hq, Hkv, Hidx = spec["B"], spec["Hq"], spec["Hkv"], spec["Hidx"]
+    D, Di = spec["D"], spec["Di"]
+    qd, kvd, idd = spec.get("q", "bf16"), spec.get("kv", "bf16"), spec.get("idx", "bf16")
+    k_scale = float(spec.get("k_scale", 1.0))
+    v_scale = float(spec.get("v_scale", 1.0))
+
+    # 1. sequence lengths
+    seq_lens = _draw_seq_lens(spec, g, device)
+    nb = [(int(L) + BLOCK - 1) // BLOCK for L in seq_lens.tolist()]
+    used = sum(nb)
+    spare = spare_pages if spare_pages is not None else max(8, math.ceil(used / 100))
+    P = used + spare
+    MB = max(nb) if nb else 1
+    if max_blocks is not None:
+        if max_blocks < MB:
+            raise ValueError("max_blocks smaller than the longest sequence")
+        MB = max_blocks
+    MB = max(MB, 1)
+
+    # 2. page permutation -> block table
+    perm = torch.randperm(P, generator=g, device=device).to(torch.int32).cpu()
+    bt = torch.full((B, MB), -1, dtype=torch.int32)
+    valid = torch.zeros(P, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        L = int(seq_lens[b])
+        for j in range(nb[b]):
+            page = int(perm[off + j])
+            bt[b, j] = page
+            valid[page] = min(BLOCK, L - j * BLOCK)
+        off += nb[b]
+
+    if spec["kind"] == "prefill":
+        n_new = spec["n_new"]
+        n_new = list(n_new) if isinstance(n_new, Sequence) else [n_new] * B
+        cu = torch.zeros(B + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(torch.tensor(n_new, dtype=torch.int32), 0)
+        T = int(cu[-1])
+    else:
+        cu = None
+        T = B
+
+    # 3-4. queries
+    q = torch.randn((T, Hq, D), generator=g, device=device).to(_TORCH_DT[qd])
+    idx_q = torch.randn((T, Hidx, Di), generator=g, device=device).to(_TORCH_DT[idd])
+
+    # 5-7. pools
+    k_pool = _draw_pool(P, Hkv, D, kvd, k_scale, g, device)
+    v_pool = _draw_pool(P, Hkv, D, kvd, v_scale, g, device)
+    idx_k_pool = _draw_pool(P, Hidx, Di, idd, 1.0, g, device)
+
+    if poison:
+        _poison(k_pool, valid, kvd, _POISON_KV.get(kvd, 0.0))
+        _poison(v_pool, valid, kvd, _POISON_KV.get(kvd, 0.0))
+        _poison(idx_k_pool, valid, idd, IDX_POISON)
+
+    return Case(spec=dict(spec), seq_lens=seq_lens.to(device),
+                cu_seqlens_q=None if cu is None else cu.to(device),
+                block_table=bt.to(device), q=q, idx_q=idx_q, k_pool=k_pool,
+                v_pool=v_pool, idx_k_pool=idx_k_pool, num_pages=P,
+                k_scale=k_scale, v_scale=v_scale)
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype == torch.uint8:
+        return t.numpy()
+    if t.dtype == torch.int32:
+        return t.numpy()
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def host_view(case: Case, pages: Optional[np.ndarray] = None) -> dict:
+    """Raw host copies of a case's bytes, tagged with their storage types.
+
+    bf16 tensors come back as uint16 bit patterns, fp8 pools as uint8 codes,
+    f32 as float32.  ``pages`` (optional) copies only those physical pages of
+    the pools; the others are left as zero-filled placeholders, which keeps
+    host memory bounded when only a few sequences are checked.
+    """
+    spec = case.spec
+
+    def pool(t):
+        if pages is None:
+            return _bits(t)
+        host = np.zeros(tuple(t.shape), dtype=_bits(t[:1]).dtype)
+        idx = torch.as_tensor(np.asarray(pages, dtype=np.int64), device=t.device)
+        host[np.asarray(pages, dtype=np.int64)] = _bits(t.index_select(0, idx))
+        return host
+
+    return dict(
+        q=_bits(case.q), idx_q=_bits(case.idx_q),
+        k_pool=pool(case.k_pool), v_pool=pool(case.v_pool),
+        idx_k_pool=pool(case.idx_k_pool),
+        block_table=_bits(case.block_table), seq_lens=_bits(case.seq_lens),
+        cu_seqlens_q=None if case.cu_seqlens_q is None else _bits(case.cu_seqlens_q),
+        q_dtype=spec.get("q", "bf16"), kv_dtype=spec.get("kv", "bf16"),
+        idx_dtype=spec.get("idx", "bf16"),
+        k_scale=case.k_scale, v_scale=case.v_scale,
+        topk=spec["topk"], init=spec["init"], local=spec["local"],
+        Hq=spec["Hq"], Hkv=spec["Hkv"], Hidx=spec["Hidx"],
+    )

@@ -1,0 +1,405 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each test checks the oracle against something fixed independently of its
+code: exact format definitions checked against torch's own casts, planted
+scores with hand-derived selections, pure-Python brute force on tiny inputs,
+dense attention from ``torch.nn.functional.scaled_dot_product_attention`` in
+float64, closed forms, invariances and the log-sum-exp merge identity.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import generate, host_view
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- decoding
+
+def test_bf16_decode_matches_torch_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zero survives
+    assert math.copysign(1.0, ours[0x8000]) == -1.0
+
+
+def test_fp8_table_matches_torch_all_codes():
+    tab = oracle.fp8_e4m3fn_table()
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(np.isnan(tab), nan)
+    assert np.array_equal(tab[~nan], ref[~nan])
+
+
+def test_fp8_table_hand_values():
+    tab = oracle.fp8_e4m3fn_table()
+    assert tab[0x00] == 0.0 and math.copysign(1, tab[0x80]) == -1
+    assert tab[0x38] == 1.0 and tab[0xB8] == -1.0
+    assert tab[0x7E] == 448.0 and tab[0xFE] == -448.0
+    assert tab[0x01] == 2.0 ** -9          # smallest subnormal
+    assert tab[0x08] == 2.0 ** -6          # smallest normal
+    assert tab[0x07] == 7 * 2.0 ** -9      # largest subnormal
+    # every finite code is exact in bf16: round trip through bf16 bits
+    fin = tab[np.isfinite(tab)]
+    as_bf16 = torch.from_numpy(fin).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(as_bf16, fin)
+
+
+def test_fp8_scale_applied():
+    codes = np.array([0x38, 0x40, 0xC8], dtype=np.uint8)
+    v = oracle.decode(codes, "fp8", 1.0 / 16)
+    assert list(v) == [1.0 / 16, 2.0 / 16, -4.0 / 16]
+
+
+# ------------------------------------------------------- planted selection
+
+def _bf16_bits(x):
+    return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _planted_inputs(case, Di=16, D=16, seed=0):
+    """Build a one-sequence decode input whose block scores are the planted ones."""
+    rng = np.random.default_rng(seed)
+    nb, tail = case["nb"], case["tail"]
+    scores = [(-0.0 if s == "-0" else float(s)) for s in case["scores"]]
+    L = (nb - 1) * 128 + tail
+    P = nb + 3
+    perm = rng.permutation(P)
+    bt = perm[:nb].astype(np.int32)[None, :]
+    ik = rng.standard_normal((P, 1, 128, Di)).astype(np.float32)
+    ik[:, :, :, 0] = -1000.0
+    for j in range(nb):
+        valid = 128 if j < nb - 1 else tail
+        t = (37 * j + 11) % valid
+        ik[bt[0, j], 0, t, 0] = scores[j]
+    if "decoy" in case and tail < 128:
+        ik[bt[0, nb - 1], 0, tail:, 0] = case["decoy"]
+    iq = np.zeros((1, 1, Di), dtype=np.float32)
+    iq[0, 0, 0] = 1.0
+    kv = rng.standard_normal((P, 1, 128, D)).astype(np.float32)
+    return dict(
+        q=_bf16_bits(rng.standard_normal((1, 2, D))), idx_q=_bf16_bits(iq),
+        k_pool=_bf16_bits(kv), v_pool=_bf16_bits(kv[::-1].copy()),
+        idx_k_pool=_bf16_bits(ik), block_table=bt,
+        seq_lens=np.array([L], dtype=np.int32), cu_seqlens_q=None,
+        q_dtype="bf16", kv_dtype="bf16", idx_dtype="bf16",
+        topk=case["topk"], init=case["init"], local=case["local"],
+        Hq=2, Hkv=1, Hidx=1), scores
+
+
+def _golden_cases():
+    with open(os.path.join(GOLDEN, "planted_selection.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_planted_scores_and_selection(case):
+    inp, planted = _planted_inputs(case)
+    sc = oracle.block_scores(inp)
+    nb = case["nb"]
+    got = sc[0, 0, :nb]
+    assert all(g == p for g, p in zip(got, planted)), (got, planted)
+    assert np.all(np.isneginf(sc[0, 0, nb:]))
+    sel, cnt = oracle.select(inp, sc)
+    assert list(sel[0, 0, : cnt[0, 0]]) == case["expected"]
+    assert np.all(sel[0, 0, cnt[0, 0]:] == -1)
+
+
+# ---------------------------------------------------- brute force, tiny
+
+def _tiny_case(seed, B=2, lens=(300, 77), Hq=4, Hkv=2, Hidx=1, D=8, Di=8, topk=2,
+               init=1, local=1, kv="bf16", prefill_new=None):
+    spec = dict(kind="decode", B=B, seq_lens=list(lens), Hq=Hq, Hkv=Hkv, Hidx=Hidx,
+                D=D, Di=Di, topk=topk, init=init, local=local, q="bf16", kv=kv,
+                idx="bf16", k_scale=0.5 if kv == "fp8" else 1.0,
+                v_scale=0.25 if kv == "fp8" else 1.0)
+    if prefill_new is not None:
+        spec.update(kind="prefill", n_new=list(prefill_new),
+                    prefix=[L - n for L, n in zip(lens, prefill_new)])
+    return host_view(generate(spec, seed))
+
+
+def _py_value(raw, dtype, scale=1.0):
+    if dtype == "bf16":
+        return torch.tensor(int(np.int16(raw.view(np.int16)))).to(torch.int16).view(
+            torch.bfloat16).double().item()
+    if dtype == "fp8":
+        return torch.tensor(int(raw), dtype=torch.uint8).view(
+            torch.float8_e4m3fn).double().item() * scale
+    return float(raw)
+
+
+def _py_scores(inp):
+    """Block scores with explicit loops over blocks and tokens."""
+    out = {}
+    for t, (b, p) in enumerate(oracle.query_positions(inp["seq_lens"], inp["cu_seqlens_q"])):
+        for h in range(inp["Hidx"]):
+            iq = [_py_value(x, "bf16") for x in inp["idx_q"][t, h]]
+            row = []
+            j = 0
+            while j * 128 <= p:
+                page = int(inp["block_table"][b, j])
+                best = -math.inf
+                for s in range(128):
+                    if j * 128 + s > p:
+                        break
+                    ik = [_py_value(x, "bf16") for x in inp["idx_k_pool"][page, h, s]]
+                    best = max(best, sum(a * c for a, c in zip(iq, ik)))
+                row.append(best)
+                j += 1
+            out[(t, h)] = row
+    return out
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_scores_brute_force(seed):
+    inp = _tiny_case(seed)
+    sc = oracle.block_scores(inp)
+    ref = _py_scores(inp)
+    for (t, h), row in ref.items():
+        assert np.allclose(sc[t, h, : len(row)], row, rtol=1e-13, atol=1e-13)
+        assert np.all(np.isneginf(sc[t, h, len(row):]))
+
+
+def test_batched_scores_equal_per_query_definition():
+    inp = _tiny_case(5, lens=(700, 260), prefill_new=(40, 260))
+    sc = oracle.block_scores(inp)
+    pos = oracle.query_positions(inp["seq_lens"], inp["cu_seqlens_q"])
+    for t, (b, p) in enumerate(pos):
+        for h in range(inp["Hidx"]):
+            ik = oracle.decode(inp["idx_k_pool"][inp["block_table"][b, : (p // 128 + 1)], h]
+                               .reshape(-1, inp["idx_k_pool"].shape[-1]), "bf16")
+            one = oracle.block_scores_for_query(oracle.decode(inp["idx_q"][t, h], "bf16"), ik, p)
+            assert np.array_equal(sc[t, h, : len(one)], one)
+
+
+@pytest.mark.parametrize("nb,init,local,topk", [(7, 1, 2, 2), (9, 0, 0, 3), (8, 2, 1, 4),
+                                                (6, 1, 2, 8), (10, 0, 3, 1)])
+def test_selection_brute_force(nb, init, local, topk):
+    rng = np.random.default_rng(nb * 100 + topk)
+    for trial in range(30):
+        # integer scores to force many exact ties
+        s = rng.integers(-3, 4, size=nb).astype(np.float64)
+        S = oracle.select_for_query(s, nb, topk, init, local)
+        F = set(range(min(init, nb))) | set(range(max(0, nb - local), nb))
+        C = [j for j in range(nb) if j not in F]
+        k = min(topk, len(C))
+
+        def beats(a, b):  # a ranks before b
+            return s[a] > s[b] or (s[a] == s[b] and a < b)
+
+        winners = [set(T) for T in itertools.combinations(C, k)
+                   if all(beats(a, b) for a in T for b in C if b not in T)]
+        assert len(winners) == 1
+        assert S == sorted(F | winners[0])
+        assert len(S) == min(nb, len(F) + topk)
+
+
+def _py_attend(inp, sel, cnt, scale):
+    """Attention with explicit loops over heads and tokens."""
+    Hq, Hkv, Hidx = inp["Hq"], inp["Hkv"], inp["Hidx"]
+    G = Hq // Hkv
+    outs = {}
+    for t, (b, p) in enumerate(oracle.query_positions(inp["seq_lens"], inp["cu_seqlens_q"])):
+        for hq in range(Hq):
+            g = hq // G
+            h = g // (Hkv // Hidx)
+            q = [_py_value(x, inp["q_dtype"]) for x in inp["q"][t, hq]]
+            zs, vs = [], []
+            for j in sel[t, h, : cnt[t, h]]:
+                page = int(inp["block_table"][b, j])
+                for s in range(128):
+                    if j * 128 + s > p:
+                        break
+                    k = [_py_value(x, inp["kv_dtype"], inp["k_scale"]) for x in inp["k_pool"][page, g, s]]
+                    v = [_py_value(x, inp["kv_dtype"], inp["v_scale"]) for x in inp["v_pool"][page, g, s]]
+                    zs.append(scale * sum(a * c for a, c in zip(q, k)))
+                    vs.append(v)
+            m = max(zs)
+            e = [math.exp(z - m) for z in zs]
+            tot = sum(e)
+            o = [sum(e[i] * vs[i][d] for i in range(len(e))) / tot for d in range(len(q))]
+            outs[(t, hq)] = (o, m + math.log(tot))
+    return outs
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_attention_brute_force(kv):
+    inp = _tiny_case(3, lens=(300, 130), Hq=4, Hkv=2, Hidx=2, kv=kv)
+    res = oracle.sparse_attention(inp)
+    ref = _py_attend(inp, res["sel"], res["count"], 1.0 / math.sqrt(8))
+    for (t, hq), (o, l) in ref.items():
+        assert np.allclose(res["out"][t, hq], o, rtol=1e-12, atol=1e-12)
+        assert abs(res["lse"][t, hq] - l) < 1e-12
+
+
+# ------------------------------------------ dense equivalence (library pin)
+
+def _dense_sdpa(inp, scale=None):
+    """All visible tokens, via torch SDPA in float64 with an explicit causal mask."""
+    q = torch.from_numpy(oracle.decode(inp["q"], inp["q_dtype"]))
+    T, Hq, D = q.shape
+    G = Hq // inp["Hkv"]
+    out = torch.zeros(T, Hq, D, dtype=torch.float64)
+    pos = oracle.query_positions(inp["seq_lens"], inp["cu_seqlens_q"])
+    for b in range(len(inp["seq_lens"])):
+        L = int(inp["seq_lens"][b])
+        toks = [t for t, (bb, _) in enumerate(pos) if bb == b]
+        if L == 0 or not toks:
+            continue
+        nbk = (L + 127) // 128
+        pages = inp["block_table"][b, :nbk].astype(np.int64)
+        k = oracle.decode(inp["k_pool"][pages], inp["kv_dtype"], inp["k_scale"])
+        v = oracle.decode(inp["v_pool"][pages], inp["kv_dtype"], inp["v_scale"])
+        k = torch.from_numpy(k).permute(1, 0, 2, 3).reshape(inp["Hkv"], nbk * 128, D)[:, :L]
+        v = torch.from_numpy(v).permute(1, 0, 2, 3).reshape(inp["Hkv"], nbk * 128, D)[:, :L]
+        k = k.repeat_interleave(G, dim=0)
+        v = v.repeat_interleave(G, dim=0)
+        qs = q[toks].permute(1, 0, 2)                                  # [Hq, n, D]
+        ps = torch.tensor([pos[t][1] for t in toks])
+        mask = torch.arange(L)[None, :] <= ps[:, None]                 # [n, L]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qs, k, v, attn_mask=mask, scale=scale)
+        out[toks] = o.permute(1, 0, 2)
+    return out.numpy()
+
+
+@pytest.mark.parametrize("kv,prefill", [("bf16", None), ("f32", None), ("fp8", None),
+                                        ("bf16", (100, 256))])
+def test_full_coverage_equals_dense_attention(kv, prefill):
+    # topk + |F| >= nb for every query: selection covers all visible blocks
+    inp = _tiny_case(11, lens=(1000, 600), Hq=6, Hkv=3, Hidx=1, D=16, Di=8, topk=8,
+                     kv=kv, prefill_new=prefill)
+    res = oracle.sparse_attention(inp)
+    dense = _dense_sdpa(inp)
+    assert np.allclose(res["out"], dense, rtol=1e-11, atol=1e-12)
+
+
+def test_dense_equivalence_with_explicit_scale():
+    inp = _tiny_case(12, lens=(500, 900), Hq=4, Hkv=2, Hidx=2, D=16, Di=8, topk=8)
+    res = oracle.sparse_attention(inp, scale=0.37)
+    dense = _dense_sdpa(inp, scale=0.37)
+    assert np.allclose(res["out"], dense, rtol=1e-11, atol=1e-12)
+
+
+# ----------------------------------------------------------- invariances
+
+def test_softmax_weights_sum_to_one():
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((8, 32))
+    k = rng.standard_normal((300, 32)) * 4
+    v = rng.standard_normal((300, 32))
+    _, _, w = oracle.softmax_attention(q, k, v, 1 / math.sqrt(32), return_weights=True)
+    assert np.all(np.abs(w.sum(axis=1) - 1.0) < 1e-12)
+    assert np.all(w >= 0)
+
+
+def test_page_permutation_invariance():
+    inp = _tiny_case(21, lens=(1500, 900), Hq=4, Hkv=2, Hidx=2, D=16, Di=16, topk=3)
+    res = oracle.sparse_attention(inp)
+    P = inp["k_pool"].shape[0]
+    perm = np.random.default_rng(3).permutation(P)
+    inp2 = dict(inp)
+    for key in ("k_pool", "v_pool", "idx_k_pool"):
+        new = np.empty_like(inp[key])
+        new[perm] = inp[key]
+        inp2[key] = new
+    bt = inp["block_table"].copy()
+    bt[bt >= 0] = perm[bt[bt >= 0]]
+    inp2["block_table"] = bt
+    res2 = oracle.sparse_attention(inp2)
+    for key in ("sel", "count", "out", "lse"):
+        assert np.array_equal(res[key], res2[key]), key
+    assert np.array_equal(res["scores"], res2["scores"])
+
+
+# ------------------------------------------------------------ closed forms
+
+def test_constant_values_give_constant_output():
+    inp = _tiny_case(31, lens=(800, 260), topk=2)
+    inp["v_pool"] = np.full_like(inp["v_pool"], _bf16_bits([0.75])[0])
+    res = oracle.sparse_attention(inp)
+    assert np.all(np.abs(res["out"] - 0.75) < 1e-14)
+
+
+def test_zero_query_gives_mean_of_selected_values():
+    inp = _tiny_case(32, lens=(800, 260), Hq=2, Hkv=1, Hidx=1, topk=2)
+    inp["q"] = np.zeros_like(inp["q"])
+    res = oracle.sparse_attention(inp)
+    for t, (b, p) in enumerate(oracle.query_positions(inp["seq_lens"], None)):
+        S = res["sel"][t, 0, : res["count"][t, 0]]
+        rows = []
+        for j in S:
+            page = inp["block_table"][b, j]
+            n = min(128, p + 1 - 128 * j)
+            rows.append(oracle.decode(inp["v_pool"][page, 0, :n], "bf16"))
+        mean = np.concatenate(rows).mean(axis=0)
+        assert np.allclose(res["out"][t, 0], mean, rtol=1e-13, atol=1e-14)
+        # z = 0 everywhere: lse = log(number of visible selected tokens)
+        assert abs(res["lse"][t, 0] - math.log(sum(r.shape[0] for r in rows))) < 1e-13
+
+
+def test_single_token_sequence_returns_its_value():
+    inp = _tiny_case(33, lens=(1, 1), topk=2)
+    res = oracle.sparse_attention(inp)
+    G = inp["Hq"] // inp["Hkv"]
+    for b in range(2):
+        page = inp["block_table"][b, 0]
+        for hq in range(inp["Hq"]):
+            v0 = oracle.decode(inp["v_pool"][page, hq // G, 0], "bf16")
+            assert np.array_equal(res["out"][b, hq], v0)
+
+
+def test_empty_sequence_gives_zero_output():
+    inp = _tiny_case(34, lens=(0, 300), topk=2)
+    res = oracle.sparse_attention(inp)
+    assert res["count"][0].sum() == 0 and np.all(res["sel"][0] == -1)
+    assert np.all(res["out"][0] == 0) and np.all(np.isneginf(res["lse"][0]))
+    assert res["count"][1, 0] == 3          # nb = 3 blocks, all selected
+
+
+def test_lse_combine_equals_unsplit():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((8, 64))
+    k = rng.standard_normal((700, 64))
+    v = rng.standard_normal((700, 64))
+    full_o, full_l = oracle.softmax_attention(q, k, v, 0.125)
+    for trial in range(5):
+        cuts = np.sort(rng.choice(np.arange(1, 700), size=rng.integers(1, 9), replace=False))
+        parts = np.split(np.arange(700), cuts)
+        os_, ls_ = zip(*[oracle.softmax_attention(q, k[ix], v[ix], 0.125) for ix in parts])
+        o, l = oracle.lse_combine(np.stack(os_), np.stack(ls_))
+        assert np.allclose(o, full_o, rtol=1e-13, atol=1e-13)
+        assert np.allclose(l, full_l, rtol=1e-13, atol=1e-13)
+    # an empty part (lse = -inf, o = 0) changes nothing
+    o, l = oracle.lse_combine(np.stack([full_o, np.zeros_like(full_o)]),
+                              np.stack([full_l, np.full_like(full_l, -np.inf)]))
+    assert np.allclose(o, full_o, rtol=1e-15) and np.allclose(l, full_l, rtol=1e-15)
+
+
+def test_selection_structure_on_random_case():
+    inp = _tiny_case(41, lens=(3000, 2000), Hq=4, Hkv=2, Hidx=2, D=8, Di=8, topk=3,
+                     init=1, local=2)
+    res = oracle.sparse_attention(inp)
+    for t, (b, p) in enumerate(oracle.query_positions(inp["seq_lens"], None)):
+        nb = p // 128 + 1
+        for h in range(2):
+            S = list(res["sel"][t, h, : res["count"][t, h]])
+            assert S == sorted(set(S))
+            F = oracle.forced_blocks(nb, 1, 2)
+            assert set(F) <= set(S)
+            assert len(S) == min(nb, len(F) + 3)
