@@ -1,0 +1,237 @@
+"""Benchmark of block-sparse decode attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one msa_sparse_decode call (score every block of the index keys,
+select, split-K attend over the selected blocks, combine) over one batch of
+synthetic inputs already resident in HBM.  Before every timed step a 1 GiB
+buffer is overwritten so that no input is served from the L2 or the 256 MB
+Infinity Cache; HIP events on the library's stream bracket each step.
+
+Prints ONE JSON line: queries/s (value), achieved HBM GB/s on the touched
+bytes of the step, the roofline of the dominant kernel (the index-key scan,
+timed standalone through msa_block_score on the same inputs) and the fp64
+oracle timed on the host cores over a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "sparse-decode queries/sec + achieved HBM GB/s (touched bytes) at 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "decode_b32_l32k"
+FLUSH_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def elem_bytes(dt: str) -> int:
+    return {"bf16": 2, "f32": 4, "fp8": 1}[dt]
+
+
+def step_bytes(spec, seq_lens, sel, cnt):
+    """Algorithmic bytes of one decode step (what the method must move)."""
+    B, Hq, Hkv, Hidx = spec["B"], spec["Hq"], spec["Hkv"], spec["Hidx"]
+    D, Di = spec["D"], spec["Di"]
+    ei, ekv, eq = elem_bytes(spec["idx"]), elem_bytes(spec["kv"]), elem_bytes(spec["q"])
+    L = seq_lens.astype(np.int64)
+    nb = (L + 127) // 128
+    idx_keys = int((Hidx * L * Di * ei).sum())
+    gpi = Hkv // Hidx
+    kv = 0
+    for b in range(B):
+        for g in range(Hkv):
+            h = g // gpi
+            for j in sel[b, h, : cnt[b, h]]:
+                valid = min(128, int(L[b]) - 128 * int(j))
+                kv += valid * D * 2 * ekv
+    small = int(B * Hq * D * 2 * eq + B * Hidx * Di * eq + 4 * (nb.sum() + Hkv * cnt.sum()))
+    return idx_keys, kv, small
+
+
+def score_kernel_bytes(spec, seq_lens, max_blocks):
+    """Algorithmic bytes of one standalone scoring launch: index keys of every
+    visible token, the index queries, the block table rows read and the score
+    rows written."""
+    B, Hidx, Di = spec["B"], spec["Hidx"], spec["Di"]
+    ei = elem_bytes(spec["idx"])
+    L = seq_lens.astype(np.int64)
+    nb = (L + 127) // 128
+    return int((Hidx * L * Di * ei).sum() + B * Hidx * Di * ei + 4 * nb.sum() * Hidx
+               + 4 * B * Hidx * max_blocks)
+
+
+def cpu_baseline(case, spec, seconds):
+    """The oracle as it stands, on the first n sequences of the same inputs."""
+    import torch  # noqa: F401
+
+    import oracle
+    from synth import host_view
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    B = case.B
+    lens = case.seq_lens.cpu().numpy()
+    bt = case.block_table.cpu().numpy()
+    done, t_used, n = 0, 0.0, 1
+    while done < B and t_used < seconds:
+        rows = list(range(done, min(B, done + n)))
+        pages = np.unique(bt[rows].reshape(-1))
+        pages = pages[pages >= 0]
+        inp = host_view(case, pages=pages)
+        sub = dict(inp)
+        sub["q"] = inp["q"][rows]
+        sub["idx_q"] = inp["idx_q"][rows]
+        sub["block_table"] = inp["block_table"][rows]
+        sub["seq_lens"] = inp["seq_lens"][rows]
+        t0 = time.perf_counter()
+        oracle.sparse_attention(sub)
+        t_used += time.perf_counter() - t0
+        done += len(rows)
+        n = min(2 * n, 8)
+    return dict(value=done / t_used, unit="queries/s", cores=int(blas_threads),
+                host_cpus=len(os.sched_getaffinity(0)), kind="oracle",
+                sample=f"first {done} of {B} sequences of {spec['name']} (all heads), "
+                       f"{t_used:.1f} s of fp64 numpy")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_score_amd as msa
+    from synth import WORKLOAD_SEEDS, generate, workload
+
+    spec = workload(args.workload)
+    if spec["kind"] != "decode":
+        print(f"{args.workload} is not a decode workload", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = generate(spec, WORKLOAD_SEEDS[args.workload], device=dev)
+    cfg = msa.MsaConfig.from_spec(spec)
+    B, MB = case.B, case.max_blocks
+    ws = msa.alloc_workspace(msa.decode_workspace_size(cfg, B, MB), dev)
+    out = torch.empty_like(case.q)
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+
+    def step():
+        msa.sparse_decode(cfg, case.q, case.idx_q, case.k_pool, case.v_pool, case.idx_k_pool,
+                          case.block_table, case.seq_lens, out=out, workspace=ws)
+
+    # selection of this batch, for the touched-bytes count
+    _, _, sel, cnt = msa.sparse_decode(cfg, case.q, case.idx_q, case.k_pool, case.v_pool,
+                                       case.idx_k_pool, case.block_table, case.seq_lens,
+                                       workspace=ws, return_selection=True)
+    torch.cuda.synchronize()
+    lens = case.seq_lens.cpu().numpy()
+    idx_b, kv_b, small_b = step_bytes(spec, lens, sel.cpu().numpy(), cnt.cpu().numpy())
+    total_b = idx_b + kv_b + small_b
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, cold caches, events on the library's stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        flush.fill_(i)
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    step_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms = float(step_ms.mean())
+
+    # ---- warm back-to-back steps (context only)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / args.steps
+
+    # ---- dominant kernel: the index-key scan, standalone, cold caches
+    scores = torch.empty((B, cfg.num_idx_heads, MB), dtype=torch.float32, device=dev)
+    kevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush.fill_(i)
+        kevs[i][0].record(stream)
+        msa.block_score(cfg, case.idx_q, case.idx_k_pool, case.block_table, case.seq_lens,
+                        scores=scores)
+        kevs[i][1].record(stream)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in kevs]))
+    k_bytes = score_kernel_bytes(spec, lens, MB)
+    k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": B / (ms * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec["kv"] if spec["kv"] != "bf16" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "seq_lens": spec["seq_lens"],
+                   "q_heads": spec["Hq"], "kv_heads": spec["Hkv"], "idx_heads": spec["Hidx"],
+                   "head_dim": spec["D"], "idx_dim": spec["Di"], "topk": spec["topk"],
+                   "init": spec["init"], "local": spec["local"], "kv_dtype": spec["kv"],
+                   "page": 128, "parallelism": "none"},
+        "hbm_gbps": total_b / (ms * 1e-3) / 1e9,
+        "hbm_frac": total_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "touched_bytes": {"idx_keys": idx_b, "selected_kv": kv_b, "small": small_b},
+        "ms_per_step_median": float(np.median(step_ms)),
+        "ms_per_step_warm": warm_ms,
+        "wall_s_timed_region": t_wall,
+        "roofline": {"kernel": "decode_score_kernel (index-key scan)", "bound": "hbm",
+                     "achieved": k_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": k_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": k_bytes, "ms_per_launch": k_ms},
+        "device": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, spec, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,250 @@
+"""Python entry points with the names of the C ABI (argument marshalling only).
+
+Tensors are torch tensors on the GPU; each call passes their device pointers
+and the current stream to libmsa.so, which does every step of the path in its
+own kernels.  The only thing this layer does besides marshalling is allocate
+the caller-side outputs and workspace with torch when they are not given.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MSA_BF16, MSA_F32, MSA_FP8_E4M3, Params, check, load
+
+BLOCK = 128
+
+
+@dataclass
+class MsaConfig:
+    """Model parameters (see msa_params_t in include/msa.h)."""
+
+    num_q_heads: int
+    num_kv_heads: int
+    num_idx_heads: int
+    head_dim: int = 128
+    idx_dim: int = 128
+    topk: int = 16
+    init_blocks: int = 1
+    local_blocks: int = 2
+    softmax_scale: float = 0.0
+    q_dtype: str = "bf16"
+    kv_dtype: str = "bf16"
+    idx_dtype: str = "bf16"
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    block_size: int = BLOCK
+
+    @property
+    def kmax(self) -> int:
+        return self.topk + self.init_blocks + self.local_blocks
+
+    def params(self) -> Params:
+        code = {"bf16": MSA_BF16, "f32": MSA_F32, "fp8": MSA_FP8_E4M3}
+        return Params(self.num_q_heads, self.num_kv_heads, self.num_idx_heads, self.head_dim,
+                      self.idx_dim, self.block_size, self.topk, self.init_blocks,
+                      self.local_blocks, self.softmax_scale, code[self.q_dtype],
+                      code[self.kv_dtype], code[self.idx_dtype], self.k_scale, self.v_scale)
+
+    @staticmethod
+    def from_spec(spec: dict) -> "MsaConfig":
+        return MsaConfig(num_q_heads=spec["Hq"], num_kv_heads=spec["Hkv"],
+                         num_idx_heads=spec["Hidx"], head_dim=spec["D"], idx_dim=spec["Di"],
+                         topk=spec["topk"], init_blocks=spec["init"],
+                         local_blocks=spec["local"], q_dtype=spec.get("q", "bf16"),
+                         kv_dtype=spec.get("kv", "bf16"), idx_dtype=spec.get("idx", "bf16"),
+                         k_scale=float(spec.get("k_scale", 1.0)),
+                         v_scale=float(spec.get("v_scale", 1.0)))
+
+
+def blocks_from_tokens(init_tokens: int, local_tokens: int, block_size: int = BLOCK):
+    """Block counts for token-denominated settings, as the sglang backend derives
+    them: init = ceil(init_tokens / bs); local = ceil(local_tokens / bs) + 1 (the
+    extra block is the query's own, partially filled one)."""
+    init = (init_tokens + block_size - 1) // block_size
+    local = (local_tokens + block_size - 1) // block_size + 1
+    return init, local
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_i32(*ts):
+    for t in ts:
+        if t is not None and t.dtype != torch.int32:
+            raise ValueError("index tensors must be int32")
+
+
+def version() -> int:
+    return int(load().msa_version())
+
+
+def decode_workspace_size(cfg: MsaConfig, num_seqs: int, max_blocks: int) -> int:
+    p = cfg.params()
+    n = load().msa_decode_workspace_size(ctypes.byref(p), num_seqs, max_blocks)
+    if n == 0:
+        check(_lib.MSA_ERR_INVALID_ARG if num_seqs >= 0 else _lib.MSA_ERR_INVALID_ARG)
+    return int(n)
+
+
+def prefill_workspace_size(cfg: MsaConfig, num_seqs: int, num_q_tokens: int,
+                           max_blocks: int) -> int:
+    p = cfg.params()
+    n = load().msa_prefill_workspace_size(ctypes.byref(p), num_seqs, num_q_tokens, max_blocks)
+    if n == 0:
+        check(_lib.MSA_ERR_UNSUPPORTED)
+    return int(n)
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns blocks aligned to at least 512 bytes
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def block_score(cfg: MsaConfig, idx_q, idx_k_pool, block_table, seq_lens,
+                cu_seqlens_q=None, scores=None, stream=None) -> torch.Tensor:
+    """Step 1: scores [T, Hidx, max_blocks] (float32)."""
+    _check_i32(block_table, seq_lens, cu_seqlens_q)
+    B, MB = block_table.shape
+    T = idx_q.shape[0]
+    if scores is None:
+        scores = torch.empty((T, cfg.num_idx_heads, MB), dtype=torch.float32,
+                             device=idx_q.device)
+    p = cfg.params()
+    check(load().msa_block_score(ctypes.byref(p), _ptr(idx_q), _ptr(idx_k_pool),
+                                 idx_k_pool.shape[0], _ptr(block_table), MB, _ptr(seq_lens),
+                                 _ptr(cu_seqlens_q), B, T, _ptr(scores), _stream(stream)))
+    return scores
+
+
+def select_blocks(cfg: MsaConfig, scores, seq_lens, cu_seqlens_q=None, sel_blocks=None,
+                  sel_count=None, stream=None):
+    """Step 2: (sel_blocks [T, Hidx, Kmax], sel_count [T, Hidx]) int32."""
+    _check_i32(seq_lens, cu_seqlens_q)
+    T, Hidx, MB = scores.shape
+    B = seq_lens.shape[0]
+    dev = scores.device
+    if sel_blocks is None:
+        sel_blocks = torch.empty((T, Hidx, cfg.kmax), dtype=torch.int32, device=dev)
+    if sel_count is None:
+        sel_count = torch.empty((T, Hidx), dtype=torch.int32, device=dev)
+    p = cfg.params()
+    check(load().msa_select_blocks(ctypes.byref(p), _ptr(scores), MB, _ptr(seq_lens),
+                                   _ptr(cu_seqlens_q), B, T, _ptr(sel_blocks),
+                                   _ptr(sel_count), _stream(stream)))
+    return sel_blocks, sel_count
+
+
+def sparse_decode(cfg: MsaConfig, q, idx_q, k_pool, v_pool, idx_k_pool, block_table,
+                  seq_lens, out=None, lse=None, sel_blocks=None, sel_count=None,
+                  workspace=None, return_selection=False, stream=None):
+    """Steps 1-3 for decode (one query per sequence).  Returns out [B, Hq, D]
+    (and lse [B, Hq], sel_blocks, sel_count when asked for)."""
+    _check_i32(block_table, seq_lens)
+    B, MB = block_table.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if return_selection:
+        if lse is None:
+            lse = torch.empty((B, cfg.num_q_heads), dtype=torch.float32, device=dev)
+        if sel_blocks is None:
+            sel_blocks = torch.empty((B, cfg.num_idx_heads, cfg.kmax), dtype=torch.int32,
+                                     device=dev)
+        if sel_count is None:
+            sel_count = torch.empty((B, cfg.num_idx_heads), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(decode_workspace_size(cfg, B, MB), dev)
+    p = cfg.params()
+    check(load().msa_sparse_decode(
+        ctypes.byref(p), _ptr(q), _ptr(idx_q), _ptr(k_pool), _ptr(v_pool), _ptr(idx_k_pool),
+        k_pool.shape[0], _ptr(block_table), MB, _ptr(seq_lens), B, _ptr(out), _ptr(lse),
+        _ptr(sel_blocks), _ptr(sel_count), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    if return_selection:
+        return out, lse, sel_blocks, sel_count
+    return out
+
+
+def sparse_attend(cfg: MsaConfig, q, k_pool, v_pool, block_table, seq_lens, sel_blocks,
+                  sel_count, out=None, lse=None, workspace=None, stream=None):
+    """Step 3 alone (decode) over a given selection.  Returns (out, lse)."""
+    _check_i32(block_table, seq_lens, sel_blocks, sel_count)
+    B, MB = block_table.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, cfg.num_q_heads), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(decode_workspace_size(cfg, B, MB), dev)
+    p = cfg.params()
+    check(load().msa_sparse_attend(
+        ctypes.byref(p), _ptr(q), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+        _ptr(block_table), MB, _ptr(seq_lens), B, _ptr(sel_blocks), _ptr(sel_count),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def sparse_prefill(cfg: MsaConfig, q, idx_q, k_pool, v_pool, idx_k_pool, block_table,
+                   seq_lens, cu_seqlens_q, out=None, lse=None, sel_blocks=None,
+                   sel_count=None, workspace=None, return_selection=False, stream=None):
+    """Steps 1-3 for chunked prefill (query tokens laid out by cu_seqlens_q)."""
+    _check_i32(block_table, seq_lens, cu_seqlens_q)
+    B, MB = block_table.shape
+    T = q.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if return_selection:
+        if lse is None:
+            lse = torch.empty((T, cfg.num_q_heads), dtype=torch.float32, device=dev)
+        if sel_blocks is None:
+            sel_blocks = torch.empty((T, cfg.num_idx_heads, cfg.kmax), dtype=torch.int32,
+                                     device=dev)
+        if sel_count is None:
+            sel_count = torch.empty((T, cfg.num_idx_heads), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(prefill_workspace_size(cfg, B, T, MB), dev)
+    p = cfg.params()
+    check(load().msa_sparse_prefill(
+        ctypes.byref(p), _ptr(q), _ptr(idx_q), _ptr(k_pool), _ptr(v_pool), _ptr(idx_k_pool),
+        k_pool.shape[0], _ptr(block_table), MB, _ptr(seq_lens), _ptr(cu_seqlens_q), B, T,
+        _ptr(out), _ptr(lse), _ptr(sel_blocks), _ptr(sel_count), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    if return_selection:
+        return out, lse, sel_blocks, sel_count
+    return out
+
+
+def fp8_dequant(codes: torch.Tensor, scale: float = 1.0, out=None, stream=None):
+    """fp8-e4m3 codes (uint8) -> float32 values times scale, as the loaders do it."""
+    if codes.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise ValueError("codes must be uint8 or float8_e4m3fn")
+    if out is None:
+        out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+    check(load().msa_fp8_e4m3_dequant(_ptr(codes), _ptr(out), codes.numel(), float(scale),
+                                      _stream(stream)))
+    return out
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

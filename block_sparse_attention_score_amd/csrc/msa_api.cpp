@@ -1,0 +1,396 @@
+// C ABI of libmsa: argument validation, workspace layout and kernel launches.
+// Every entry point validates everything it can on the host before it
+// enqueues anything; it never allocates, copies or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "msa.h"
+#include "msa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+msa_status_t fail(msa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+msa_status_t ok() {
+  g_err[0] = '\0';
+  return MSA_OK;
+}
+
+constexpr int kMaxBlocksLimit = 8192;  // 1M tokens per sequence
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int kmax_of(const msa_params_t& p) { return p.topk + p.init_blocks + p.local_blocks; }
+int group_of(const msa_params_t& p) { return p.num_q_heads / p.num_kv_heads; }
+
+msa_status_t check_params(const msa_params_t* p) {
+  if (p == nullptr) return fail(MSA_ERR_INVALID_ARG, "params is NULL");
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_idx_heads <= 0)
+    return fail(MSA_ERR_INVALID_ARG, "head counts must be positive (Hq=%d Hkv=%d Hidx=%d)",
+                p->num_q_heads, p->num_kv_heads, p->num_idx_heads);
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(MSA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", p->num_q_heads,
+                p->num_kv_heads);
+  const int G = p->num_q_heads / p->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(MSA_ERR_UNSUPPORTED, "Hq/Hkv=%d not in {1,2,4,8,16}", G);
+  if (p->num_kv_heads % p->num_idx_heads != 0)
+    return fail(MSA_ERR_UNSUPPORTED, "Hkv=%d is not a multiple of Hidx=%d", p->num_kv_heads,
+                p->num_idx_heads);
+  if (p->block_size != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "block_size=%d (only 128, equal to the page size)",
+                p->block_size);
+  if (p->head_dim != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "head_dim=%d (only 128)", p->head_dim);
+  if (p->idx_dim != 64 && p->idx_dim != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "idx_dim=%d (only 64 or 128)", p->idx_dim);
+  if (p->topk != 4 && p->topk != 8 && p->topk != 16 && p->topk != 32)
+    return fail(MSA_ERR_UNSUPPORTED, "topk=%d not in {4,8,16,32}", p->topk);
+  if (p->init_blocks < 0 || p->local_blocks < 0)
+    return fail(MSA_ERR_INVALID_ARG, "negative init/local block count");
+  if (p->init_blocks > 64 || p->local_blocks > 64)
+    return fail(MSA_ERR_UNSUPPORTED, "init/local block counts above 64");
+  if (!std::isfinite(p->softmax_scale) || p->softmax_scale < 0.f)
+    return fail(MSA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  const bool qkv_ok = (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_BF16) ||
+                      (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_FP8_E4M3) ||
+                      (p->q_dtype == MSA_F32 && p->kv_dtype == MSA_F32);
+  if (!qkv_ok)
+    return fail(MSA_ERR_UNSUPPORTED, "(q_dtype=%d, kv_dtype=%d) not supported", p->q_dtype,
+                p->kv_dtype);
+  if (p->idx_dtype != MSA_BF16 && p->idx_dtype != MSA_F32)
+    return fail(MSA_ERR_UNSUPPORTED, "idx_dtype=%d not supported", p->idx_dtype);
+  if (p->kv_dtype == MSA_FP8_E4M3 &&
+      (!std::isfinite(p->k_scale) || !std::isfinite(p->v_scale) || p->k_scale <= 0.f ||
+       p->v_scale <= 0.f))
+    return fail(MSA_ERR_INVALID_ARG, "fp8 k_scale/v_scale must be finite and > 0");
+  return MSA_OK;
+}
+
+msa_status_t check_shape(int32_t num_seqs, int32_t max_blocks) {
+  if (num_seqs < 0) return fail(MSA_ERR_INVALID_ARG, "num_seqs=%d < 0", num_seqs);
+  if (max_blocks < 1) return fail(MSA_ERR_INVALID_ARG, "max_blocks=%d < 1", max_blocks);
+  if (max_blocks > kMaxBlocksLimit)
+    return fail(MSA_ERR_UNSUPPORTED, "max_blocks=%d above %d", max_blocks, kMaxBlocksLimit);
+  return MSA_OK;
+}
+
+float softmax_scale_of(const msa_params_t& p) {
+  return p.softmax_scale > 0.f ? p.softmax_scale : 1.0f / std::sqrt(float(p.head_dim));
+}
+
+// Selected blocks handled by one split-K workgroup.
+int blocks_per_split(const msa_params_t& /*p*/, int32_t /*num_seqs*/) { return 1; }
+
+// Pages scored by one workgroup in the decode scan.
+constexpr int kPagesPerItem = 8;
+
+struct DecodeLayout {
+  size_t scores, sel, cnt, part_o, part_lse, tk_score, tk_attend, total;
+  int bps, nsplit_max;
+};
+
+DecodeLayout decode_layout(const msa_params_t& p, int32_t B, int32_t MB) {
+  DecodeLayout l{};
+  const int kmax = kmax_of(p);
+  const int G = group_of(p);
+  l.bps = blocks_per_split(p, B);
+  l.nsplit_max = (kmax + l.bps - 1) / l.bps;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  l.scores = take(sizeof(float) * size_t(B) * p.num_idx_heads * MB);
+  l.sel = take(sizeof(int32_t) * size_t(B) * p.num_idx_heads * kmax);
+  l.cnt = take(sizeof(int32_t) * size_t(B) * p.num_idx_heads);
+  l.part_o = take(sizeof(float) * size_t(B) * p.num_kv_heads * l.nsplit_max * G * p.head_dim);
+  l.part_lse = take(sizeof(float) * size_t(B) * p.num_kv_heads * l.nsplit_max * G);
+  l.tk_score = take(sizeof(uint32_t) * size_t(B) * p.num_idx_heads);
+  l.tk_attend = take(sizeof(uint32_t) * size_t(B) * p.num_kv_heads);
+  l.total = off;
+  return l;
+}
+
+msa_status_t check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (ws == nullptr) return fail(MSA_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
+    return fail(MSA_ERR_WORKSPACE, "workspace not %zu-byte aligned", kAlign);
+  if (ws_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  return MSA_OK;
+}
+
+msa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MSA_OK;
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Split-K attention over an existing selection (decode).
+msa_status_t enqueue_attend(const msa_params_t& p, const void* q, const void* k_pool,
+                            const void* v_pool, int64_t num_pages,
+                            const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* seq_lens, int32_t num_seqs, const int32_t* sel,
+                            const int32_t* cnt, void* out, float* lse_out, void* ws,
+                            const DecodeLayout& l, hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  msa::AttendArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.sel = sel;
+  a.cnt = cnt;
+  a.kmax = kmax_of(p);
+  a.hkv = p.num_kv_heads;
+  a.hidx = p.num_idx_heads;
+  a.bps = l.bps;
+  a.nsplit_max = l.nsplit_max;
+  const float ks = p.kv_dtype == MSA_FP8_E4M3 ? p.k_scale : 1.f;
+  a.qk_scale_log2 = softmax_scale_of(p) * ks * 1.4426950408889634f;
+  a.v_scale = p.kv_dtype == MSA_FP8_E4M3 ? p.v_scale : 1.f;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.part_o = reinterpret_cast<float*>(w + l.part_o);
+  a.part_lse = reinterpret_cast<float*>(w + l.part_lse);
+  a.tickets = reinterpret_cast<uint32_t*>(w + l.tk_attend);
+  return hip_status(msa::launch_decode_attend(a, p.q_dtype, p.kv_dtype, group_of(p), s),
+                    "decode attend launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t msa_version(void) { return (1 << 16) | 0; }
+
+const char* msa_status_string(msa_status_t st) {
+  switch (st) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_INVALID_ARG: return "invalid argument";
+    case MSA_ERR_UNSUPPORTED: return "unsupported";
+    case MSA_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MSA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* msa_last_error(void) { return g_err; }
+
+size_t msa_decode_workspace_size(const msa_params_t* params, int32_t num_seqs,
+                                 int32_t max_blocks) {
+  if (check_params(params) != MSA_OK) return 0;
+  if (check_shape(num_seqs, max_blocks) != MSA_OK) return 0;
+  return decode_layout(*params, num_seqs, max_blocks).total;
+}
+
+size_t msa_prefill_workspace_size(const msa_params_t* params, int32_t num_seqs,
+                                  int32_t num_q_tokens, int32_t max_blocks) {
+  if (check_params(params) != MSA_OK) return 0;
+  if (check_shape(num_seqs, max_blocks) != MSA_OK) return 0;
+  (void)num_q_tokens;
+  fail(MSA_ERR_UNSUPPORTED, "chunked prefill is not available in this build");
+  return 0;
+}
+
+msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
+                             const void* idx_k_pool, int64_t num_pages,
+                             const int32_t* block_table, int32_t max_blocks,
+                             const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                             int32_t num_seqs, int32_t num_q_tokens, float* scores,
+                             void* stream) {
+  msa_status_t st = check_params(params);
+  if (st != MSA_OK) return st;
+  if ((st = check_shape(num_seqs, max_blocks)) != MSA_OK) return st;
+  if (!idx_q || !idx_k_pool || !block_table || !seq_lens || !scores)
+    return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
+  if (cu_seqlens_q != nullptr)
+    return fail(MSA_ERR_UNSUPPORTED, "prefill scoring is not available in this build");
+  (void)num_q_tokens;
+  if (num_seqs == 0) return ok();
+  msa::ScoreArgs a{};
+  a.idx_q = idx_q;
+  a.idx_k = idx_k_pool;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.hidx = params->num_idx_heads;
+  a.pages_per_item = kPagesPerItem;
+  a.chunks_per_pair = (max_blocks + kPagesPerItem - 1) / kPagesPerItem;
+  a.scores = scores;
+  a.fill_tail = 1;
+  a.fuse_select = 0;
+  st = hip_status(msa::launch_decode_score(a, params->idx_dtype, params->idx_dim,
+                                           static_cast<hipStream_t>(stream)),
+                  "block score launch");
+  return st == MSA_OK ? ok() : st;
+}
+
+msa_status_t msa_select_blocks(const msa_params_t* params, const float* scores,
+                               int32_t max_blocks, const int32_t* seq_lens,
+                               const int32_t* cu_seqlens_q, int32_t num_seqs,
+                               int32_t num_q_tokens, int32_t* sel_blocks,
+                               int32_t* sel_count, void* stream) {
+  msa_status_t st = check_params(params);
+  if (st != MSA_OK) return st;
+  if ((st = check_shape(num_seqs, max_blocks)) != MSA_OK) return st;
+  if (!scores || !seq_lens || !sel_blocks || !sel_count)
+    return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  const int32_t T = cu_seqlens_q == nullptr ? num_seqs : num_q_tokens;
+  if (T < 0) return fail(MSA_ERR_INVALID_ARG, "num_q_tokens=%d < 0", T);
+  if (T == 0) return ok();
+  msa::SelectArgs a{};
+  a.scores = scores;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.num_seqs = num_seqs;
+  a.num_tokens = T;
+  a.hidx = params->num_idx_heads;
+  a.topk = params->topk;
+  a.init = params->init_blocks;
+  a.local = params->local_blocks;
+  a.kmax = kmax_of(*params);
+  a.sel = sel_blocks;
+  a.cnt = sel_count;
+  st = hip_status(msa::launch_select(a, static_cast<hipStream_t>(stream)), "select launch");
+  return st == MSA_OK ? ok() : st;
+}
+
+msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const void* idx_q,
+                               const void* k_pool, const void* v_pool,
+                               const void* idx_k_pool, int64_t num_pages,
+                               const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* seq_lens, int32_t num_seqs, void* out,
+                               float* lse_out, int32_t* sel_blocks_out,
+                               int32_t* sel_count_out, void* ws, size_t ws_bytes,
+                               void* stream) {
+  msa_status_t st = check_params(params);
+  if (st != MSA_OK) return st;
+  if ((st = check_shape(num_seqs, max_blocks)) != MSA_OK) return st;
+  if (!q || !idx_q || !k_pool || !v_pool || !idx_k_pool || !block_table || !seq_lens || !out)
+    return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if ((sel_blocks_out == nullptr) != (sel_count_out == nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "sel_blocks_out and sel_count_out go together");
+  if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
+  const msa_params_t& p = *params;
+  const DecodeLayout l = decode_layout(p, num_seqs, max_blocks);
+  if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
+  if (num_seqs == 0) return ok();
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  int32_t* sel = sel_blocks_out ? sel_blocks_out : reinterpret_cast<int32_t*>(w + l.sel);
+  int32_t* cnt = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + l.cnt);
+
+  // Tickets of both fused stages start at zero (one fill over both arrays).
+  const int64_t ntk = int64_t(l.total - l.tk_score) / int64_t(sizeof(uint32_t));
+  st = hip_status(msa::launch_fill_u32(reinterpret_cast<uint32_t*>(w + l.tk_score), ntk, 0u, s),
+                  "ticket reset launch");
+  if (st != MSA_OK) return st;
+
+  msa::ScoreArgs a{};
+  a.idx_q = idx_q;
+  a.idx_k = idx_k_pool;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.hidx = p.num_idx_heads;
+  a.pages_per_item = kPagesPerItem;
+  a.chunks_per_pair = (max_blocks + kPagesPerItem - 1) / kPagesPerItem;
+  a.scores = reinterpret_cast<float*>(w + l.scores);
+  a.fill_tail = 0;
+  a.fuse_select = 1;
+  a.tickets = reinterpret_cast<uint32_t*>(w + l.tk_score);
+  a.topk = p.topk;
+  a.init = p.init_blocks;
+  a.local = p.local_blocks;
+  a.kmax = kmax_of(p);
+  a.sel = sel;
+  a.cnt = cnt;
+  st = hip_status(msa::launch_decode_score(a, p.idx_dtype, p.idx_dim, s),
+                  "score/select launch");
+  if (st != MSA_OK) return st;
+  st = enqueue_attend(p, q, k_pool, v_pool, num_pages, block_table, max_blocks, seq_lens,
+                      num_seqs, sel, cnt, out, lse_out, ws, l, s);
+  return st == MSA_OK ? ok() : st;
+}
+
+msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q, const void* k_pool,
+                               const void* v_pool, int64_t num_pages,
+                               const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* seq_lens, int32_t num_seqs,
+                               const int32_t* sel_blocks, const int32_t* sel_count, void* out,
+                               float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+  msa_status_t st = check_params(params);
+  if (st != MSA_OK) return st;
+  if ((st = check_shape(num_seqs, max_blocks)) != MSA_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !sel_blocks || !sel_count || !out)
+    return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
+  const DecodeLayout l = decode_layout(*params, num_seqs, max_blocks);
+  if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
+  if (num_seqs == 0) return ok();
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  st = hip_status(msa::launch_fill_u32(reinterpret_cast<uint32_t*>(w + l.tk_attend),
+                                       int64_t(params->num_kv_heads) * num_seqs, 0u, s),
+                  "ticket reset launch");
+  if (st != MSA_OK) return st;
+  st = enqueue_attend(*params, q, k_pool, v_pool, num_pages, block_table, max_blocks, seq_lens,
+                      num_seqs, sel_blocks, sel_count, out, lse_out, ws, l, s);
+  return st == MSA_OK ? ok() : st;
+}
+
+msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const void* idx_q,
+                                const void* k_pool, const void* v_pool,
+                                const void* idx_k_pool, int64_t num_pages,
+                                const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                                int32_t num_seqs, int32_t num_q_tokens, void* out,
+                                float* lse_out, int32_t* sel_blocks_out,
+                                int32_t* sel_count_out, void* ws, size_t ws_bytes,
+                                void* stream) {
+  msa_status_t st = check_params(params);
+  if (st != MSA_OK) return st;
+  (void)q; (void)idx_q; (void)k_pool; (void)v_pool; (void)idx_k_pool; (void)num_pages;
+  (void)block_table; (void)max_blocks; (void)seq_lens; (void)cu_seqlens_q; (void)num_seqs;
+  (void)num_q_tokens; (void)out; (void)lse_out; (void)sel_blocks_out; (void)sel_count_out;
+  (void)ws; (void)ws_bytes; (void)stream;
+  return fail(MSA_ERR_UNSUPPORTED, "chunked prefill is not available in this build");
+}
+
+msa_status_t msa_fp8_e4m3_dequant(const uint8_t* in, float* out, int64_t n, float scale,
+                                  void* stream) {
+  if (n < 0) return fail(MSA_ERR_INVALID_ARG, "n=%lld < 0", (long long)n);
+  if (n > 0 && (!in || !out)) return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!std::isfinite(scale)) return fail(MSA_ERR_INVALID_ARG, "scale must be finite");
+  const msa_status_t st = hip_status(
+      msa::launch_fp8_dequant(in, out, n, scale, static_cast<hipStream_t>(stream)),
+      "fp8 dequant launch");
+  return st == MSA_OK ? ok() : st;
+}
+
+}  // extern "C"

@@ -1,0 +1,193 @@
+// Device helpers for the gfx950 kernels of libmsa: storage-type unpacking,
+// wavefront reductions over 16-lane DPP rows, order-preserving score keys and
+// 256-thread workgroup scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kBlock = 128;      // tokens per block == tokens per page
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kWgThreads = 256;  // 4 waves per workgroup
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Storage tags.
+struct BF16 {};
+struct F32 {};
+struct FP8 {};
+
+// ---------------------------------------------------------------- loads
+
+// Raw storage of eight consecutive elements, loaded with one (fp8, bf16) or
+// two (f32) vector loads and widened to float only when used.
+template <class T>
+struct Raw8;
+template <>
+struct Raw8<BF16> {
+  uint4 v;
+};
+template <>
+struct Raw8<F32> {
+  float4 a, b;
+};
+template <>
+struct Raw8<FP8> {
+  uint2 v;
+};
+
+__device__ __forceinline__ Raw8<BF16> load_raw(const BF16*, const void* base,
+                                               int64_t idx) {
+  return {*reinterpret_cast<const uint4*>(
+      reinterpret_cast<const uint16_t*>(base) + idx)};
+}
+__device__ __forceinline__ Raw8<F32> load_raw(const F32*, const void* base,
+                                              int64_t idx) {
+  const float4* p = reinterpret_cast<const float4*>(
+      reinterpret_cast<const float*>(base) + idx);
+  return {p[0], p[1]};
+}
+__device__ __forceinline__ Raw8<FP8> load_raw(const FP8*, const void* base,
+                                              int64_t idx) {
+  return {*reinterpret_cast<const uint2*>(
+      reinterpret_cast<const uint8_t*>(base) + idx)};
+}
+
+__device__ __forceinline__ void unpack(const Raw8<BF16>& r, float (&x)[8]) {
+  const uint32_t u[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(u[i] << 16);
+    x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack(const Raw8<F32>& r, float (&x)[8]) {
+  x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+  x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+}
+
+// OCP e4m3 codes -> float with the gfx950 conversion instruction (two codes
+// per instruction, selected by word).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* x) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
+}
+__device__ __forceinline__ void unpack(const Raw8<FP8>& r, float (&x)[8]) {
+  fp8x4_to_f32(r.v.x, x);
+  fp8x4_to_f32(r.v.y, x + 4);
+}
+
+template <class T>
+__device__ __forceinline__ void load8(const T* tag, const void* base, int64_t idx,
+                                      float (&x)[8]) {
+  unpack(load_raw(tag, base, idx), x);
+}
+
+// Eight consecutive elements packed as bf16 for an MFMA operand.  fp8 codes
+// convert exactly (every e4m3 value is a bf16 value).
+__device__ __forceinline__ bf16x8_t load8_bf16(const BF16*, const void* base,
+                                               int64_t idx) {
+  return *reinterpret_cast<const bf16x8_t*>(
+      reinterpret_cast<const uint16_t*>(base) + idx);
+}
+
+__device__ __forceinline__ bf16x8_t load8_bf16(const FP8*, const void* base,
+                                               int64_t idx) {
+  float x[8];
+  load8(static_cast<const FP8*>(nullptr), base, idx, x);
+  uint32_t u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    u[i] = (__float_as_uint(x[2 * i]) >> 16) |
+           (__float_as_uint(x[2 * i + 1]) & 0xffff0000u);
+  bf16x8_t r;
+  __builtin_memcpy(&r, u, 16);
+  return r;
+}
+
+// float -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ------------------------------------------------------------ DPP rows
+
+// DPP control words (GFX9 encoding).
+constexpr int kDppXor1 = 0xB1;          // quad_perm(1,0,3,2)
+constexpr int kDppXor2 = 0x4E;          // quad_perm(2,3,0,1)
+constexpr int kDppHalfMirror = 0x141;   // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;       // lane i <- lane 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over groups of N consecutive lanes (N in {8, 16}); every lane of the
+// group receives the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (N == 16) v += dpp_f<kDppMirror>(v);
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  if constexpr (N == 16) v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return v;
+}
+
+// Max over the whole wavefront, result in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+  v = group_max<16>(v);
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+// --------------------------------------------------------- score keys
+
+// Order-preserving map float -> uint32 (larger float, larger key); -0 and +0
+// map to the same key so that they tie.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------- block scans
+
+// Inclusive prefix sum over the 256 threads of a workgroup.  `wsum` is LDS
+// scratch of 4 ints.  Contains barriers: every thread must call it.
+__device__ __forceinline__ int block_incl_scan(int v, int* wsum) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int n = __shfl_up(v, o);
+    if (lane >= o) v += n;
+  }
+  if (lane == kWave - 1) wsum[w] = v;
+  __syncthreads();
+  int add = 0;
+  for (int i = 0; i < w; ++i) add += wsum[i];
+  __syncthreads();
+  return v + add;
+}
+
+__device__ __forceinline__ int div_up(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace msa

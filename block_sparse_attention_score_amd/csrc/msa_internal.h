@@ -1,0 +1,79 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+// Decode block scoring, optionally fused with the per-row selection.
+struct ScoreArgs {
+  const void* idx_q;         // [B, Hidx, Di]
+  const void* idx_k;         // [P, Hidx, 128, Di]
+  int64_t num_pages;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  int32_t num_seqs;
+  int32_t hidx;
+  int32_t pages_per_item;    // blocks scored by one workgroup
+  int32_t chunks_per_pair;   // ceil(max_blocks / pages_per_item)
+  float* scores;             // [B, Hidx, max_blocks]
+  int32_t fill_tail;         // write -inf past each row's last block
+  // fused selection (fuse_select != 0)
+  int32_t fuse_select;
+  uint32_t* tickets;         // [B * Hidx], zero on entry
+  int32_t topk, init, local, kmax;
+  int32_t* sel;              // [B, Hidx, kmax]
+  int32_t* cnt;              // [B, Hidx]
+};
+
+// Standalone selection over precomputed score rows.
+struct SelectArgs {
+  const float* scores;       // [T, Hidx, max_blocks]
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens_q;  // nullptr: decode
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t hidx;
+  int32_t topk, init, local, kmax;
+  int32_t* sel;
+  int32_t* cnt;
+};
+
+// Decode split-K attention with a fused log-sum-exp combine.
+struct AttendArgs {
+  const void* q;             // [B, Hq, D]
+  const void* k_pool;        // [P, Hkv, 128, D]
+  const void* v_pool;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  int32_t num_seqs;
+  const int32_t* sel;        // [B, Hidx, kmax]
+  const int32_t* cnt;        // [B, Hidx]
+  int32_t kmax;
+  int32_t hkv, hidx;
+  int32_t bps;               // selected blocks per split
+  int32_t nsplit_max;        // ceil(kmax / bps)
+  float qk_scale_log2;       // softmax_scale * k_scale * log2(e)
+  float v_scale;
+  void* out;                 // [B, Hq, D] in the query dtype
+  float* lse_out;            // [B, Hq] or nullptr
+  float* part_o;             // [B, Hkv, nsplit_max, G, D]
+  float* part_lse;           // [B, Hkv, nsplit_max, G]
+  uint32_t* tickets;         // [B * Hkv], zero on entry
+};
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
+hipError_t launch_decode_score(const ScoreArgs& a, int idx_dtype, int idx_dim,
+                               hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_decode_attend(const AttendArgs& a, int q_dtype, int kv_dtype,
+                                int group, hipStream_t s);
+hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale,
+                              hipStream_t s);
+
+}  // namespace msa

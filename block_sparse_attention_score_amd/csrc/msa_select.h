@@ -1,0 +1,136 @@
+// Per-query block selection on one 256-thread workgroup.
+//
+// Selection rule (sglang page minimax_sparse_backend.py,
+// MiniMaxSparseAttnBackend.__init__: init, local and top-k block counts for a
+// per-token selection): for nb visible blocks the forced set is
+// F = {0..init-1} U {nb-local..nb-1}; the top-k of the other blocks by
+// (score desc, block asc) join F; the result is written in ascending block
+// order, -1 padded, with |S| = |F| + min(topk, nb - |F|).
+//
+// Method: scores become order-preserving 32-bit keys (-0 folded onto +0).  A
+// 4-pass, 8-bit radix select over the candidates finds the key T of the k-th
+// best candidate and how many candidates with key == T still fit; those are
+// taken in ascending block order (ranks from a workgroup scan), which is the
+// lower-index tie rule.  Each thread owns a contiguous run of blocks, so one
+// more scan gives every selected block its output slot.
+#pragma once
+
+#include "msa_device.h"
+
+namespace msa {
+
+struct SelectLds {
+  int hist[256];
+  int wsum[4];
+  int digit;
+  int need;
+};
+
+// Number of forced blocks among nb visible ones.
+__device__ __forceinline__ int forced_count(int nb, int init, int local) {
+  const int a = min(init, nb);
+  const int lo = max(0, nb - local);
+  return a + (nb - lo) - max(0, a - lo);
+}
+
+// s: nb scores of one (query, index head) row.  MAXPER >= ceil(nb / 256).
+// Must be called by all 256 threads of the workgroup.
+template <int MAXPER>
+__device__ void select_row(const float* __restrict__ s, int nb, int topk,
+                           int init, int local, int kmax,
+                           int32_t* __restrict__ sel, int32_t* __restrict__ cnt,
+                           SelectLds& L) {
+  const int tid = threadIdx.x;
+  const int per = div_up(nb, kWgThreads);
+  const int j0 = tid * per;
+  const int lo_init = min(init, nb);       // j <  lo_init  -> forced (init)
+  const int hi_local = max(0, nb - local);  // j >= hi_local -> forced (local)
+  const int nforced = forced_count(nb, init, local);
+  const int ncand = nb - nforced;
+  const int keff = min(topk, ncand);
+  const bool take_all = keff == ncand;
+
+  uint32_t key[MAXPER];
+#pragma unroll
+  for (int i = 0; i < MAXPER; ++i) {
+    const int j = j0 + i;
+    key[i] = (i < per && j < nb) ? score_key(s[j]) : 0u;
+  }
+  auto is_cand = [&](int j) { return j < nb && j >= lo_init && j < hi_local; };
+
+  uint32_t T = 0u;
+  int need = 0;
+  if (!take_all) {
+    uint32_t prefix = 0u;
+    need = keff;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+      L.hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MAXPER; ++i) {
+        const int j = j0 + i;
+        if (i < per && is_cand(j) && (key[i] & hi_mask) == prefix)
+          atomicAdd(&L.hist[(key[i] >> shift) & 0xFF], 1);
+      }
+      __syncthreads();
+      // Thread tid looks at digit 255 - tid: an inclusive scan counts the
+      // candidates whose digit is >= that one.
+      const int d = 255 - tid;
+      const int c = L.hist[d];
+      const int incl = block_incl_scan(c, L.wsum);
+      const int excl = incl - c;
+      if (excl < need && need <= incl) {
+        L.digit = d;
+        L.need = need - excl;
+      }
+      __syncthreads();
+      prefix |= static_cast<uint32_t>(L.digit) << shift;
+      need = L.need;
+      __syncthreads();
+    }
+    T = prefix;
+  }
+
+  // Rank of each key == T candidate among equals, in block order.
+  int eq_local = 0;
+  if (!take_all) {
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+      const int j = j0 + i;
+      eq_local += (i < per && is_cand(j) && key[i] == T) ? 1 : 0;
+    }
+  }
+  int r = block_incl_scan(eq_local, L.wsum) - eq_local;
+
+  bool flag[MAXPER];
+  int sel_local = 0;
+#pragma unroll
+  for (int i = 0; i < MAXPER; ++i) {
+    const int j = j0 + i;
+    bool f = false;
+    if (i < per && j < nb) {
+      if (!is_cand(j) || take_all) {
+        f = true;
+      } else if (key[i] > T) {
+        f = true;
+      } else if (key[i] == T) {
+        f = r < need;
+        ++r;
+      }
+    }
+    flag[i] = f;
+    sel_local += f ? 1 : 0;
+  }
+  int pos = block_incl_scan(sel_local, L.wsum) - sel_local;
+#pragma unroll
+  for (int i = 0; i < MAXPER; ++i)
+    if (flag[i]) sel[pos++] = j0 + i;
+  const int total = nforced + keff;
+  for (int i = total + tid; i < kmax; i += kWgThreads) sel[i] = -1;
+  if (tid == 0) *cnt = total;
+  __syncthreads();
+}
+
+}  // namespace msa

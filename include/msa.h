@@ -1,0 +1,215 @@
+/*
+ * msa.h -- block-sparse attention over a paged KV cache, for AMD Instinct
+ * MI355X (gfx950).  C ABI of libmsa.so.
+ *
+ * The method (sglang page minimax_sparse_backend.py, MiniMaxSparseAttnBackend:
+ * per-token block selection with block_size_q = 1, block_size_k = 128, init,
+ * local and top-k block counts; vLLM page sparse_attention_msa.py,
+ * MiniMaxM3SparseMSAImpl.forward: causal attention over the selected 128-token
+ * blocks of a paged cache, decode by split-K):
+ *
+ *   1. score  -- for query position p and index head h, block j < nb(p) =
+ *                p/128 + 1 scores max over its tokens t <= p of
+ *                q_idx[h] . k_idx[t, h]  (blocks >= nb(p) score -inf);
+ *   2. select -- S = {init blocks 0..init-1} U {local blocks nb-local..nb-1}
+ *                U top-k of the remaining blocks by (score desc, block asc),
+ *                listed ascending, |S| = min(nb, |F| + topk);
+ *   3. attend -- exact softmax attention of each q head over the tokens
+ *                t <= p of the blocks in S of its index head, split along the
+ *                selected-block axis and merged with a log-sum-exp combine.
+ *
+ * Layouts (all row-major, contiguous, caller-owned device memory):
+ *   q          [T, Hq, D]           q_dtype
+ *   idx_q      [T, Hidx, Di]        idx_dtype
+ *   k_pool     [P, Hkv, 128, D]     kv_dtype  (per page, per head: 128 tokens)
+ *   v_pool     [P, Hkv, 128, D]     kv_dtype
+ *   idx_k_pool [P, Hidx, 128, Di]   idx_dtype
+ *   block_table[B, max_blocks] int32: logical block j of sequence b lives in
+ *              physical page block_table[b*max_blocks + j]; entries past a
+ *              sequence's last block are ignored (-1 by convention)
+ *   seq_lens   [B] int32: tokens of sequence b, including the query token(s)
+ *   cu_seqlens_q [B+1] int32 (prefill only): query tokens of sequence b are
+ *              rows cu[b]..cu[b+1]-1 and are the sequence's LAST tokens, at
+ *              positions seq_lens[b] - n_b + i
+ *   scores     [T, Hidx, max_blocks] float32
+ *   sel_blocks [T, Hidx, Kmax] int32, Kmax = topk + init + local, ascending,
+ *              -1 padded;  sel_count [T, Hidx] int32
+ *   out        [T, Hq, D] q_dtype;  lse [T, Hq] float32 (natural log, of the
+ *              scaled logits; -inf and out = 0 for a query with no tokens)
+ *
+ * Head maps: q head hq reads kv head g = hq / (Hq/Hkv); kv head g uses index
+ * head h = g / (Hkv/Hidx).
+ *
+ * Conventions:
+ *  - The caller owns every buffer.  The library allocates nothing, frees
+ *    nothing, copies nothing between host and device and never synchronises:
+ *    every call only enqueues kernels on `stream` (a hipStream_t; NULL is the
+ *    null stream), so calls can be captured into a HIP graph.  Host integers
+ *    (num_seqs, max_blocks, num_q_tokens, num_pages) are shapes or upper
+ *    bounds; per-step data (seq_lens, tables) is read on the device.
+ *  - Arguments are validated before anything is enqueued; on any error the
+ *    call returns a non-zero status and enqueues nothing.  Block-table
+ *    entries outside [0, num_pages) are never dereferenced (such a block
+ *    reads as empty); faults in the caller's memory surface at the caller's
+ *    next synchronisation, as usual in HIP.
+ *  - A sequence with seq_len 0 yields out = 0, lse = -inf, sel_count = 0.
+ *  - Workspaces are plain device memory of msa_*_workspace_size() bytes,
+ *    256-byte aligned; their contents on entry do not matter.  Calls that
+ *    share a workspace must be ordered on one stream.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1, /* null pointer, bad shape or range            */
+  MSA_ERR_UNSUPPORTED = 2, /* outside the supported parameter set         */
+  MSA_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned  */
+  MSA_ERR_HIP = 4          /* a HIP launch failed; see msa_last_error()   */
+} msa_status_t;
+
+typedef enum {
+  MSA_BF16 = 0,
+  MSA_F32 = 1,
+  MSA_FP8_E4M3 = 2 /* OCP e4m3 ("e4m3fn"): bias 7, no inf, S.1111.111 = NaN */
+} msa_dtype_t;
+
+/*
+ * Model parameters (sglang page, MiniMaxSparseAttnBackend.__init__: sparse
+ * index dim, block size, init / local / top-k block counts; vLLM page: k/v
+ * scales of an fp8 cache).  Supported set:
+ *   block_size == 128 (page size == block size), head_dim == 128,
+ *   idx_dim in {64, 128}, topk in {4, 8, 16, 32}, 0 <= init, local <= 64,
+ *   Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8, 16}, Hkv % Hidx == 0,
+ *   (q_dtype, kv_dtype) in {(bf16, bf16), (bf16, fp8_e4m3), (f32, f32)},
+ *   idx_dtype in {bf16, f32} (idx_q and idx_k share it).
+ */
+typedef struct {
+  int32_t num_q_heads;   /* Hq   */
+  int32_t num_kv_heads;  /* Hkv  */
+  int32_t num_idx_heads; /* Hidx */
+  int32_t head_dim;      /* D    */
+  int32_t idx_dim;       /* Di   */
+  int32_t block_size;    /* tokens per block == tokens per page           */
+  int32_t topk;          /* top-k blocks chosen among non-forced blocks   */
+  int32_t init_blocks;   /* leading blocks always kept (attention sink)   */
+  int32_t local_blocks;  /* trailing blocks always kept, incl. own block  */
+  float softmax_scale;   /* 0 => 1/sqrt(head_dim)                         */
+  int32_t q_dtype;       /* msa_dtype_t */
+  int32_t kv_dtype;      /* msa_dtype_t */
+  int32_t idx_dtype;     /* msa_dtype_t */
+  float k_scale;         /* fp8 only: k = code value * k_scale            */
+  float v_scale;         /* fp8 only: v = code value * v_scale            */
+} msa_params_t;
+
+/* Library version, (major << 16) | minor. */
+int32_t msa_version(void);
+const char* msa_status_string(msa_status_t status);
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* msa_last_error(void);
+
+/*
+ * Workspace sizes in bytes for msa_sparse_decode / msa_sparse_attend
+ * (decode: num_q_tokens == num_seqs) and msa_sparse_prefill.  Returns 0 for
+ * an invalid or unsupported parameter set (see msa_last_error()).
+ */
+size_t msa_decode_workspace_size(const msa_params_t* params, int32_t num_seqs,
+                                 int32_t max_blocks);
+size_t msa_prefill_workspace_size(const msa_params_t* params, int32_t num_seqs,
+                                  int32_t num_q_tokens, int32_t max_blocks);
+
+/*
+ * Step 1 (score).  Writes scores[T, Hidx, max_blocks] (float32; -inf for
+ * blocks past each query).  cu_seqlens_q == NULL: decode, T = num_seqs, one
+ * query per sequence at position seq_len - 1.  Otherwise T = num_q_tokens
+ * query tokens laid out by cu_seqlens_q.  Accumulation is float32.
+ */
+msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
+                             const void* idx_k_pool, int64_t num_pages,
+                             const int32_t* block_table, int32_t max_blocks,
+                             const int32_t* seq_lens,
+                             const int32_t* cu_seqlens_q, int32_t num_seqs,
+                             int32_t num_q_tokens, float* scores,
+                             void* stream);
+
+/*
+ * Step 2 (select).  From scores[T, Hidx, max_blocks] writes
+ * sel_blocks[T, Hidx, Kmax] and sel_count[T, Hidx].  Only the first nb(p)
+ * scores of each row are read.  Deterministic: equal scores (+0 and -0 are
+ * equal) go to the lower block index.
+ */
+msa_status_t msa_select_blocks(const msa_params_t* params,
+                               const float* scores, int32_t max_blocks,
+                               const int32_t* seq_lens,
+                               const int32_t* cu_seqlens_q, int32_t num_seqs,
+                               int32_t num_q_tokens, int32_t* sel_blocks,
+                               int32_t* sel_count, void* stream);
+
+/*
+ * Steps 1-3 for decode (one query per sequence): score, select, split-K
+ * attention over the selected blocks and log-sum-exp combine.  out [B, Hq, D]
+ * in q_dtype.  lse_out, sel_blocks_out and sel_count_out may be NULL; when
+ * given they receive the per-head lse and the selection.  ws: a workspace of
+ * msa_decode_workspace_size() bytes.
+ */
+msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q,
+                               const void* idx_q, const void* k_pool,
+                               const void* v_pool, const void* idx_k_pool,
+                               int64_t num_pages, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seq_lens,
+                               int32_t num_seqs, void* out, float* lse_out,
+                               int32_t* sel_blocks_out,
+                               int32_t* sel_count_out, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/*
+ * Step 3 alone (decode): attention over a given selection sel_blocks
+ * [B, Hidx, Kmax] / sel_count [B, Hidx] (ascending block ids < nb).  Same
+ * outputs and workspace as msa_sparse_decode.
+ */
+msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q,
+                               const void* k_pool, const void* v_pool,
+                               int64_t num_pages, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seq_lens,
+                               int32_t num_seqs, const int32_t* sel_blocks,
+                               const int32_t* sel_count, void* out,
+                               float* lse_out, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
+ * Steps 1-3 for chunked prefill: num_q_tokens new tokens laid out by
+ * cu_seqlens_q [B+1], each attending causally to its sequence's tokens
+ * t <= p through its own selection.  Outputs as for decode, per token.
+ * ws: msa_prefill_workspace_size() bytes.
+ */
+msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q,
+                                const void* idx_q, const void* k_pool,
+                                const void* v_pool, const void* idx_k_pool,
+                                int64_t num_pages, const int32_t* block_table,
+                                int32_t max_blocks, const int32_t* seq_lens,
+                                const int32_t* cu_seqlens_q, int32_t num_seqs,
+                                int32_t num_q_tokens, void* out,
+                                float* lse_out, int32_t* sel_blocks_out,
+                                int32_t* sel_count_out, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/*
+ * fp8-e4m3 dequantisation exactly as the attention loaders do it (sglang
+ * page: the sparse path dequantises an fp8 main KV cache on load):
+ * out[i] = value(in[i]) * scale for n codes.
+ */
+msa_status_t msa_fp8_e4m3_dequant(const uint8_t* in, float* out, int64_t n,
+                                  float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -8,6 +8,7 @@ oracle can be fed the very same bytes without sharing any of the method.
 
 from .inputs import (  # noqa: F401
     WORKLOADS,
+    WORKLOAD_SEEDS,
     Case,
     generate,
     host_view,

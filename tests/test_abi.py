@@ -1,0 +1,145 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host before touching the GPU (runs without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_score_amd as msa
+from block_sparse_attention_score_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+FAKE = ctypes.c_void_p(0x10000)          # never dereferenced: validation fails first
+FAKE_WS_MISALIGNED = ctypes.c_void_p(0x10010)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for need in ("msa_block_score", "msa_select_blocks", "msa_sparse_decode",
+                 "msa_sparse_attend", "msa_sparse_prefill", "msa_decode_workspace_size",
+                 "msa_prefill_workspace_size", "msa_fp8_e4m3_dequant", "msa_status_string",
+                 "msa_last_error", "msa_version"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = msa.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_params_struct_layout_matches_header():
+    # 13 int32/float fields + 2 floats, no padding
+    assert ctypes.sizeof(_lib.Params) == 15 * 4
+
+
+def base_cfg(**kw):
+    c = dict(num_q_heads=16, num_kv_heads=2, num_idx_heads=2, head_dim=128, idx_dim=128,
+             topk=16, init_blocks=1, local_blocks=2)
+    c.update(kw)
+    return msa.MsaConfig(**c)
+
+
+def decode_call(cfg, num_seqs=4, max_blocks=16, ws=FAKE, ws_bytes=1 << 30, q=FAKE,
+                num_pages=64):
+    p = cfg.params()
+    return msa.load().msa_sparse_decode(
+        ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, num_pages, FAKE, max_blocks, FAKE, num_seqs,
+        FAKE, None, None, None, ws, ws_bytes, None)
+
+
+BAD_PARAMS = [
+    (dict(topk=5), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(topk=64), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(head_dim=64), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(idx_dim=96), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(block_size=64), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=15), _lib.MSA_ERR_INVALID_ARG),
+    (dict(num_q_heads=48, num_kv_heads=2), _lib.MSA_ERR_UNSUPPORTED),   # G = 24
+    (dict(num_idx_heads=3, num_kv_heads=2), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(num_kv_heads=0), _lib.MSA_ERR_INVALID_ARG),
+    (dict(init_blocks=-1), _lib.MSA_ERR_INVALID_ARG),
+    (dict(local_blocks=65), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(softmax_scale=float("nan")), _lib.MSA_ERR_INVALID_ARG),
+    (dict(q_dtype="fp8", kv_dtype="fp8"), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(q_dtype="f32", kv_dtype="bf16"), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(idx_dtype="fp8"), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(kv_dtype="fp8", k_scale=0.0), _lib.MSA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_PARAMS, ids=[str(k) for k, _ in BAD_PARAMS])
+def test_bad_params_rejected(kw, code):
+    assert decode_call(base_cfg(**kw)) == code
+    assert msa.load().msa_last_error().decode()
+    p = base_cfg(**kw).params()
+    assert msa.load().msa_decode_workspace_size(ctypes.byref(p), 4, 16) == 0
+
+
+def test_null_params_and_pointers():
+    lib = msa.load()
+    assert lib.msa_sparse_decode(None, *([FAKE] * 5), 64, FAKE, 16, FAKE, 4, FAKE, None, None,
+                                 None, FAKE, 1 << 20, None) == _lib.MSA_ERR_INVALID_ARG
+    assert decode_call(base_cfg(), q=None) == _lib.MSA_ERR_INVALID_ARG
+    assert "NULL" in lib.msa_last_error().decode()
+
+
+def test_shape_checks():
+    assert decode_call(base_cfg(), max_blocks=0) == _lib.MSA_ERR_INVALID_ARG
+    assert decode_call(base_cfg(), max_blocks=8193) == _lib.MSA_ERR_UNSUPPORTED
+    assert decode_call(base_cfg(), num_seqs=-1) == _lib.MSA_ERR_INVALID_ARG
+    assert decode_call(base_cfg(), num_pages=0) == _lib.MSA_ERR_INVALID_ARG
+
+
+def test_workspace_checks():
+    cfg = base_cfg()
+    need = msa.decode_workspace_size(cfg, 4, 16)
+    assert need > 0
+    assert decode_call(cfg, ws=None) == _lib.MSA_ERR_WORKSPACE
+    assert decode_call(cfg, ws_bytes=need - 1) == _lib.MSA_ERR_WORKSPACE
+    assert decode_call(cfg, ws=FAKE_WS_MISALIGNED) == _lib.MSA_ERR_WORKSPACE
+
+
+def test_workspace_size_grows_with_shape():
+    cfg = base_cfg()
+    a = msa.decode_workspace_size(cfg, 32, 256)
+    b = msa.decode_workspace_size(cfg, 64, 256)
+    c = msa.decode_workspace_size(cfg, 32, 1024)
+    assert 0 < a < b and a < c
+    # scores alone need B * Hidx * MB floats
+    assert a >= 32 * 2 * 256 * 4
+
+
+def test_selection_pairing_required():
+    cfg = base_cfg()
+    p = cfg.params()
+    st = msa.load().msa_sparse_decode(
+        ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 16, FAKE, 4, FAKE, None,
+        FAKE, None, FAKE, 1 << 30, None)
+    assert st == _lib.MSA_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    lib = msa.load()
+    for code in range(5):
+        assert lib.msa_status_string(code)
+    assert lib.msa_status_string(99) == b"unknown status"
+
+
+def test_block_token_conversion_follows_backend_rule():
+    # sglang backend: init = ceil(tokens / bs); local = ceil(tokens / bs) + 1
+    assert msa.blocks_from_tokens(1, 1) == (1, 2)
+    assert msa.blocks_from_tokens(128, 256) == (1, 3)
+    assert msa.blocks_from_tokens(0, 0) == (0, 1)
+    assert msa.blocks_from_tokens(129, 129) == (2, 3)

@@ -1,0 +1,227 @@
+"""GPU parity of the decode path (score, select, split-K attend, combine)
+against the fp64 oracle, through the C ABI."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from synth import WORKLOAD_SEEDS, generate, host_view, workload
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def msa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_score_amd as m
+    m.load()
+    return m
+
+
+def _spec(B, lens, Hq=8, Hkv=2, Hidx=1, Di=128, topk=4, init=1, local=2, q="bf16",
+          kv="bf16", idx="bf16", scale=None):
+    s = dict(kind="decode", B=B, seq_lens=list(lens), Hq=Hq, Hkv=Hkv, Hidx=Hidx, D=128, Di=Di,
+             topk=topk, init=init, local=local, q=q, kv=kv, idx=idx)
+    if kv == "fp8":
+        s.update(k_scale=1.0 / 16 if scale is None else scale[0],
+                 v_scale=1.0 / 16 if scale is None else scale[1])
+    return s
+
+
+SMALL = {
+    "cfg_b2_l2048": workload("decode_b2_l2048"),
+    "ragged": _spec(5, [1, 127, 128, 129, 1000]),
+    "with_empty": _spec(3, [0, 300, 5000], Hq=16, Hkv=4, Hidx=2),
+    "dense_equiv": _spec(2, [2000, 4480], Hq=16, Hkv=2, Hidx=2, topk=32),
+    "g16": _spec(2, [3000, 9000], Hq=16, Hkv=1, Hidx=1, topk=8),
+    "g1": _spec(3, [700, 2100, 6000], Hq=2, Hkv=2, Hidx=2, topk=4),
+    "g2_shared_idx": _spec(2, [5000, 9000], Hq=4, Hkv=2, Hidx=1, topk=8),
+    "idx_f32_di64": _spec(3, [1500, 4000, 8000], Di=64, idx="f32", topk=8),
+    "f32_path": _spec(3, [1500, 4000, 9000], Hq=8, Hkv=2, Hidx=2, q="f32", kv="f32", idx="f32",
+                      topk=8),
+    "fp8_small": _spec(3, [3000, 7000, 12345], Hq=16, Hkv=2, Hidx=2, kv="fp8", topk=8),
+    "fp8_odd_scales": _spec(2, [4000, 6000], Hq=8, Hkv=1, Hidx=1, kv="fp8", topk=4,
+                            scale=(0.37, 0.11)),
+    "topk16_init0_local0": _spec(2, [9000, 20000], Hq=8, Hkv=1, Hidx=1, topk=16, init=0,
+                                 local=0),
+    "topk32_init3_local3": _spec(2, [20000, 30000], Hq=8, Hkv=2, Hidx=2, topk=32, init=3,
+                                 local=3),
+}
+
+
+def _run(msa, spec, seed, max_blocks=None, stream=None):
+    case = generate(spec, seed, device="cuda", max_blocks=max_blocks)
+    cfg = msa.MsaConfig.from_spec(spec)
+    out, lse, sel, cnt = msa.sparse_decode(
+        cfg, case.q, case.idx_q, case.k_pool, case.v_pool, case.idx_k_pool, case.block_table,
+        case.seq_lens, return_selection=True, stream=stream)
+    scores = msa.block_score(cfg, case.idx_q, case.idx_k_pool, case.block_table, case.seq_lens,
+                             stream=stream)
+    sel2, cnt2 = msa.select_blocks(cfg, scores, case.seq_lens, stream=stream)
+    out3, lse3 = msa.sparse_attend(cfg, case.q, case.k_pool, case.v_pool, case.block_table,
+                                   case.seq_lens, sel, cnt, stream=stream)
+    torch.cuda.synchronize()
+    return case, cfg, dict(out=out, lse=lse, sel=sel, cnt=cnt, scores=scores, sel2=sel2,
+                           cnt2=cnt2, out3=out3, lse3=lse3)
+
+
+def _compare(inp, g, spec, rows=None):
+    """Oracle on `inp`; rows restricts the check to some sequences (decode: token == seq)."""
+    f32 = spec.get("q", "bf16") == "f32"
+    ora_scores = oracle.block_scores(inp)
+    ora_sel, ora_cnt = oracle.select(inp, ora_scores)
+    pos = oracle.query_positions(inp["seq_lens"], None)
+    rows = list(range(len(pos))) if rows is None else rows
+    gs = parity.to_np(g["scores"])
+    parity.check_scores(gs[rows], ora_scores[rows])
+    gsel, gcnt = parity.to_np(g["sel"]), parity.to_np(g["cnt"])
+    nband = parity.check_selection(gsel, gcnt, ora_scores, ora_sel, ora_cnt, pos,
+                                   spec["init"], spec["local"], rows=rows)
+    # the standalone select over the standalone scores agrees with the fused one
+    assert np.array_equal(parity.to_np(g["sel2"])[rows], gsel[rows])
+    assert np.array_equal(parity.to_np(g["cnt2"])[rows], gcnt[rows])
+    # oracle attention over the GPU's own selection
+    ora_out, ora_lse = oracle.attend(inp, gsel, gcnt)
+    go = parity.to_np(g["out"])
+    err = parity.check_output(go[rows], ora_out[rows], f32)
+    parity.check_lse(parity.to_np(g["lse"])[rows], ora_lse[rows], f32)
+    # step 3 alone reproduces the fused path bit for bit
+    assert torch.equal(g["out3"], g["out"])
+    assert torch.equal(g["lse3"], g["lse"])
+    return err, nband
+
+
+def test_fp8_dequant_all_codes(msa):
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).cuda()
+    for scale in (1.0, 1.0 / 16, 0.37):
+        got = msa.fp8_dequant(codes, scale).cpu().numpy().astype(np.float64)
+        ref = oracle.fp8_e4m3fn_table() * np.float32(scale).astype(np.float64)
+        ref = ref.astype(np.float32).astype(np.float64)   # the loader multiplies in fp32
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_small(msa, name):
+    spec = SMALL[name]
+    seed = 77 + sorted(SMALL).index(name)
+    print(f"[decode_small] {name} seed={seed}", flush=True)
+    case, cfg, g = _run(msa, spec, seed)
+    err, nband = _compare(host_view(case), g, spec)
+    print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
+
+
+def test_decode_extra_table_columns(msa):
+    """max_blocks larger than any sequence needs; unused entries are -1."""
+    spec = _spec(3, [900, 5000, 2200], Hq=8, Hkv=2, Hidx=2, topk=4)
+    case, cfg, g = _run(msa, spec, 5, max_blocks=97)
+    _compare(host_view(case), g, spec)
+    s = parity.to_np(g["scores"])
+    assert s.shape[2] == 97 and np.isneginf(s[:, :, 40:]).all()
+
+
+def test_decode_on_side_stream(msa):
+    spec = SMALL["ragged"]
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        case, cfg, g = _run(msa, spec, 9, stream=st)
+    st.synchronize()
+    _compare(host_view(case), g, spec)
+
+
+def test_decode_deterministic(msa):
+    spec = _spec(4, [30000, 12000, 64000, 5000], Hq=16, Hkv=2, Hidx=2, topk=16)
+    case = generate(spec, 123, device="cuda")
+    cfg = msa.MsaConfig.from_spec(spec)
+    ws = msa.alloc_workspace(msa.decode_workspace_size(cfg, 4, case.max_blocks), "cuda")
+    runs = []
+    for _ in range(3):
+        runs.append(msa.sparse_decode(cfg, case.q, case.idx_q, case.k_pool, case.v_pool,
+                                      case.idx_k_pool, case.block_table, case.seq_lens,
+                                      workspace=ws, return_selection=True))
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b)
+
+
+def _golden_cases():
+    with open(os.path.join(GOLDEN, "planted_selection.json")) as f:
+        return json.load(f)["cases"]
+
+
+def _bf16(x):
+    return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_planted_selection_exact(msa, case):
+    """Planted scores are exact in float32 as well: selection must match exactly."""
+    nb, tail, Di = case["nb"], case["tail"], 64
+    L = (nb - 1) * 128 + tail
+    P = nb + 3
+    g = torch.Generator().manual_seed(nb)
+    perm = torch.randperm(P, generator=g)
+    bt = perm[:nb].to(torch.int32)[None, :]
+    ik = torch.randn((P, 1, 128, Di), generator=g)
+    ik[:, :, :, 0] = -1000.0
+    scores = [(-0.0 if s == "-0" else float(s)) for s in case["scores"]]
+    for j in range(nb):
+        valid = 128 if j < nb - 1 else tail
+        ik[bt[0, j], 0, (37 * j + 11) % valid, 0] = scores[j]
+    if "decoy" in case and tail < 128:
+        ik[bt[0, nb - 1], 0, tail:, 0] = case["decoy"]
+    iq = torch.zeros((1, 1, Di))
+    iq[0, 0, 0] = 1.0
+    cfg = msa.MsaConfig(num_q_heads=1, num_kv_heads=1, num_idx_heads=1, idx_dim=Di,
+                        topk=case["topk"], init_blocks=case["init"],
+                        local_blocks=case["local"])
+    sl = torch.tensor([L], dtype=torch.int32).cuda()
+    s = msa.block_score(cfg, iq.to(torch.bfloat16).cuda(), ik.to(torch.bfloat16).cuda(),
+                        bt.cuda(), sl)
+    sel, cnt = msa.select_blocks(cfg, s, sl)
+    torch.cuda.synchronize()
+    got = s.cpu()[0, 0, :nb].tolist()
+    assert got == scores
+    assert sel.cpu()[0, 0, : int(cnt.cpu()[0, 0])].tolist() == case["expected"]
+
+
+# ----------------------------------------------------------- full sizes
+
+FULL = ["decode_b32_l32k", "decode_b64_lvar", "decode_fp8_b32_l64k"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_decode_full_size_sampled(msa, name):
+    """The full workload in the launch configuration the benchmark times; the
+    oracle checks a sample of sequences (all their heads and blocks)."""
+    spec = workload(name)
+    seed = WORKLOAD_SEEDS[name]
+    print(f"[decode_full] {name} seed={seed}", flush=True)
+    case, cfg, g = _run(msa, spec, seed)
+    B = case.B
+    rng = np.random.default_rng(seed)
+    lens = case.seq_lens.cpu().numpy()
+    rows = sorted(set([int(np.argmax(lens)), int(np.argmin(lens))] +
+                      [int(x) for x in rng.choice(B, size=2, replace=False)]))
+    pages = np.unique(np.concatenate([case.block_table.cpu().numpy()[b] for b in rows]))
+    pages = pages[pages >= 0]
+    inp = host_view(case, pages=pages)
+    err, nband = _compare(inp, g, spec, rows=rows)
+    print(f"  rows {rows} max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
+    # every row: well-formed selections and finite outputs
+    cnt = parity.to_np(g["cnt"])
+    kmax = spec["topk"] + spec["init"] + spec["local"]
+    nb = (lens + 127) // 128
+    assert (cnt == np.minimum(nb, kmax)[:, None]).all()
+    assert torch.isfinite(g["out"].float()).all()
