@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kWgThreads) void decode_attend_kernel(AttendArgs a)
     if (nsplit == 1) {
       store_out(qtag, a.out, (hq0 + hh) * 128 + d, o);
     } else {
-      a.part_o[(part0 + hh) * 128 + d] = o;
+      store_shared_f32(a.part_o + (part0 + hh) * 128 + d, o);
     }
   }
   if (tid < G) {
@@ -303,27 +303,19 @@ __global__ __launch_bounds__(kWgThreads) void decode_attend_kernel(AttendArgs a)
     if (nsplit == 1) {
       if (a.lse_out != nullptr) a.lse_out[hq0 + tid] = lse;
     } else {
-      a.part_lse[part0 + tid] = lse;
+      store_shared_f32(a.part_lse + part0 + tid, lse);
     }
   }
   if (nsplit == 1) return;
 
-  // Publish the partial; the last split of (b, g) merges all of them.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(&a.tickets[b * a.hkv + g], 1u);
-    is_last = prev == static_cast<uint32_t>(nsplit - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+  // The last split of (b, g) to finish merges all partials.
+  if (!take_last_ticket(&a.tickets[b * a.hkv + g], nsplit, &is_last)) return;
   const int64_t base0 = (static_cast<int64_t>(b) * a.hkv + g) * a.nsplit_max * G;
   for (int i = tid; i < G * 128; i += kWgThreads) {
     const int hh = i / 128;
     const int d = i % 128;
     float mx = -INFINITY;
-    for (int c = 0; c < nsplit; ++c) mx = fmaxf(mx, a.part_lse[base0 + c * G + hh]);
+    for (int c = 0; c < nsplit; ++c) mx = fmaxf(mx, load_shared_f32(a.part_lse + base0 + c * G + hh));
     float wsum = 0.f, o = 0.f;
     if (mx == -INFINITY) {  // no visible token in any split (invalid selection)
       store_out(qtag, a.out, (hq0 + hh) * 128 + d, 0.f);
@@ -331,9 +323,9 @@ __global__ __launch_bounds__(kWgThreads) void decode_attend_kernel(AttendArgs a)
       continue;
     }
     for (int c = 0; c < nsplit; ++c) {
-      const float wc = __expf(a.part_lse[base0 + c * G + hh] - mx);
+      const float wc = __expf(load_shared_f32(a.part_lse + base0 + c * G + hh) - mx);
       wsum += wc;
-      o = fmaf(wc, a.part_o[(base0 + c * G + hh) * 128 + d], o);
+      o = fmaf(wc, load_shared_f32(a.part_o + (base0 + c * G + hh) * 128 + d), o);
     }
     store_out(qtag, a.out, (hq0 + hh) * 128 + d, o / wsum);
     if (d == 0 && a.lse_out != nullptr) a.lse_out[hq0 + hh] = mx + __logf(wsum);

@@ -190,4 +190,38 @@ __device__ __forceinline__ int block_incl_scan(int v, int* wsum) {
 
 __device__ __forceinline__ int div_up(int a, int b) { return (a + b - 1) / b; }
 
+// ------------------------------------------- cross-workgroup hand-off
+//
+// Workgroups of one launch hand results to the workgroup that finishes a unit
+// last (atomic ticket).  The data travels only through relaxed device-scope
+// atomic loads and stores, which the gfx950 memory model makes coherent across
+// the XCDs' separate L2 caches by themselves (no whole-cache write-back or
+// invalidate, which agent-scope fences would issue per wave).  A writer waits
+// for its stores to complete before it takes a ticket; the last taker reads
+// only after its ticket returned.
+
+__device__ __forceinline__ void store_shared_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_shared_f32(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// All of this wave's memory operations have completed.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Ticket of a unit of `parts` workgroups; returns true in every thread of the
+// workgroup that took the last ticket.  Every thread must call it after its
+// last hand-off store.
+__device__ __forceinline__ bool take_last_ticket(uint32_t* ticket, int parts, int* lds_flag) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = prev == static_cast<uint32_t>(parts - 1);
+  }
+  __syncthreads();
+  return *lds_flag != 0;
+}
+
 }  // namespace msa

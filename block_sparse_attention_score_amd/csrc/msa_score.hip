@@ -95,22 +95,16 @@ __global__ __launch_bounds__(kWgThreads) void decode_score_kernel(ScoreArgs a) {
       }
       m = wave_max(m);
     }
-    if (lane == 0) srow[j] = m;
+    if (lane == 0) {
+      if (a.fuse_select) store_shared_f32(srow + j, m); else srow[j] = m;
+    }
   }
 
   if (!a.fuse_select) return;
-  // Publish this chunk's scores; the last chunk of the pair selects.
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(&a.tickets[pair], 1u);
-    is_last = prev == static_cast<uint32_t>(nchunks - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  select_row<MAXPER>(srow, nb, a.topk, a.init, a.local, a.kmax,
-                     a.sel + static_cast<int64_t>(pair) * a.kmax, a.cnt + pair, sl);
+  // The last chunk of the pair to finish selects over all of the pair's scores.
+  if (!take_last_ticket(&a.tickets[pair], nchunks, &is_last)) return;
+  select_row<MAXPER, true>(srow, nb, a.topk, a.init, a.local, a.kmax,
+                           a.sel + static_cast<int64_t>(pair) * a.kmax, a.cnt + pair, sl);
 }
 
 // One workgroup per (query token, index head) row.

@@ -35,7 +35,9 @@ __device__ __forceinline__ int forced_count(int nb, int init, int local) {
 
 // s: nb scores of one (query, index head) row.  MAXPER >= ceil(nb / 256).
 // Must be called by all 256 threads of the workgroup.
-template <int MAXPER>
+// `coherent`: the scores were written by other workgroups of this launch and
+// are read through device-coherent loads.
+template <int MAXPER, bool COHERENT = false>
 __device__ void select_row(const float* __restrict__ s, int nb, int topk,
                            int init, int local, int kmax,
                            int32_t* __restrict__ sel, int32_t* __restrict__ cnt,
@@ -54,7 +56,10 @@ __device__ void select_row(const float* __restrict__ s, int nb, int topk,
 #pragma unroll
   for (int i = 0; i < MAXPER; ++i) {
     const int j = j0 + i;
-    key[i] = (i < per && j < nb) ? score_key(s[j]) : 0u;
+    if (i < per && j < nb)
+      key[i] = score_key(COHERENT ? load_shared_f32(s + j) : s[j]);
+    else
+      key[i] = 0u;
   }
   auto is_cand = [&](int j) { return j < nb && j >= lo_init && j < hi_local; };
 
