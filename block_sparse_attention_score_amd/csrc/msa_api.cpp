@@ -96,10 +96,10 @@ float softmax_scale_of(const msa_params_t& p) {
 int blocks_per_split(const msa_params_t& /*p*/, int32_t /*num_seqs*/) { return 1; }
 
 // Pages scored by one workgroup in the decode scan.
-constexpr int kPagesPerItem = 8;
+constexpr int kPagesPerItem = 4;
 
 struct DecodeLayout {
-  size_t scores, sel, cnt, part_o, part_lse, tk_score, tk_attend, total;
+  size_t scores, sel, cnt, sel_pages, part_o, part_lse, tk_score, tk_attend, total;
   int bps, nsplit_max;
 };
 
@@ -118,6 +118,7 @@ DecodeLayout decode_layout(const msa_params_t& p, int32_t B, int32_t MB) {
   l.scores = take(sizeof(float) * size_t(B) * p.num_idx_heads * MB);
   l.sel = take(sizeof(int32_t) * size_t(B) * p.num_idx_heads * kmax);
   l.cnt = take(sizeof(int32_t) * size_t(B) * p.num_idx_heads);
+  l.sel_pages = take(sizeof(int32_t) * size_t(B) * p.num_idx_heads * kmax);
   l.part_o = take(sizeof(float) * size_t(B) * p.num_kv_heads * l.nsplit_max * G * p.head_dim);
   l.part_lse = take(sizeof(float) * size_t(B) * p.num_kv_heads * l.nsplit_max * G);
   l.tk_score = take(sizeof(uint32_t) * size_t(B) * p.num_idx_heads);
@@ -145,8 +146,8 @@ msa_status_t enqueue_attend(const msa_params_t& p, const void* q, const void* k_
                             const void* v_pool, int64_t num_pages,
                             const int32_t* block_table, int32_t max_blocks,
                             const int32_t* seq_lens, int32_t num_seqs, const int32_t* sel,
-                            const int32_t* cnt, void* out, float* lse_out, void* ws,
-                            const DecodeLayout& l, hipStream_t s) {
+                            const int32_t* cnt, const int32_t* sel_pages, void* out,
+                            float* lse_out, void* ws, const DecodeLayout& l, hipStream_t s) {
   char* w = static_cast<char*>(ws);
   msa::AttendArgs a{};
   a.q = q;
@@ -159,6 +160,7 @@ msa_status_t enqueue_attend(const msa_params_t& p, const void* q, const void* k_
   a.num_seqs = num_seqs;
   a.sel = sel;
   a.cnt = cnt;
+  a.sel_pages = sel_pages;
   a.kmax = kmax_of(p);
   a.hkv = p.num_kv_heads;
   a.hidx = p.num_idx_heads;
@@ -330,11 +332,12 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const 
   a.kmax = kmax_of(p);
   a.sel = sel;
   a.cnt = cnt;
+  a.sel_pages = reinterpret_cast<int32_t*>(w + l.sel_pages);
   st = hip_status(msa::launch_decode_score(a, p.idx_dtype, p.idx_dim, s),
                   "score/select launch");
   if (st != MSA_OK) return st;
   st = enqueue_attend(p, q, k_pool, v_pool, num_pages, block_table, max_blocks, seq_lens,
-                      num_seqs, sel, cnt, out, lse_out, ws, l, s);
+                      num_seqs, sel, cnt, a.sel_pages, out, lse_out, ws, l, s);
   return st == MSA_OK ? ok() : st;
 }
 
@@ -360,7 +363,7 @@ msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q, const 
                   "ticket reset launch");
   if (st != MSA_OK) return st;
   st = enqueue_attend(*params, q, k_pool, v_pool, num_pages, block_table, max_blocks, seq_lens,
-                      num_seqs, sel_blocks, sel_count, out, lse_out, ws, l, s);
+                      num_seqs, sel_blocks, sel_count, nullptr, out, lse_out, ws, l, s);
   return st == MSA_OK ? ok() : st;
 }
 

@@ -95,11 +95,11 @@ __device__ __forceinline__ f32x4_t qk_tile(const QFrag<BF16>& f, const void* kp,
 template <class KT>
 __device__ __forceinline__ f32x4_t qk_tile(const QFrag<F32>& f, const void* kp,
                                            int64_t krow, int kgrp) {
-  float4 kb[8];
+  f32x4v_t kb[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m)
-    kb[m] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(kp) + krow +
-                                             16 * m + 4 * kgrp);
+    kb[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(
+        reinterpret_cast<const float*>(kp) + krow + 16 * m + 4 * kgrp));
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
@@ -139,9 +139,11 @@ __global__ __launch_bounds__(kWgThreads) void decode_attend_kernel(AttendArgs a)
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int h = g / (a.hkv / a.hidx);
-  const int L = a.seq_lens[b];
   const int sel_row = b * a.hidx + h;
-  const int count = L > 0 ? min(max(a.cnt[sel_row], 0), a.kmax) : 0;
+  // independent loads, all in flight together
+  const int L = a.seq_lens[b];
+  const int cnt_raw = a.cnt[sel_row];
+  const int count = L > 0 ? min(max(cnt_raw, 0), a.kmax) : 0;
   const int nsplit = div_up(count, a.bps);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -182,11 +184,16 @@ __global__ __launch_bounds__(kWgThreads) void decode_attend_kernel(AttendArgs a)
   const int bi1 = min(count, bi0 + a.bps);
   __syncthreads();
 
+  const int32_t* pagerow =
+      a.sel_pages != nullptr ? a.sel_pages + static_cast<int64_t>(sel_row) * a.kmax : nullptr;
   for (int bi = bi0; bi < bi1; ++bi) {
     const int j = selrow[bi];
-    const int page = j >= 0 && j < a.max_blocks
-                         ? a.block_table[static_cast<int64_t>(b) * a.max_blocks + j]
-                         : -1;
+    int page;
+    if (pagerow != nullptr)
+      page = pagerow[bi];
+    else
+      page = j >= 0 && j < a.max_blocks ? a.block_table[static_cast<int64_t>(b) * a.max_blocks + j]
+                                        : -1;
     const bool ok = page >= 0 && page < a.num_pages;
     const int nvalid = ok ? min(kBlock, p + 1 - j * kBlock) : 0;
     const int64_t kvb = ok ? (static_cast<int64_t>(page) * a.hkv + g) * kBlock * 128 : 0;
@@ -311,24 +318,41 @@ __global__ __launch_bounds__(kWgThreads) void decode_attend_kernel(AttendArgs a)
   // The last split of (b, g) to finish merges all partials.
   if (!take_last_ticket(&a.tickets[b * a.hkv + g], nsplit, &is_last)) return;
   const int64_t base0 = (static_cast<int64_t>(b) * a.hkv + g) * a.nsplit_max * G;
+  // Split weights exp(lse_c - lse) of every head, once, in LDS (the partial
+  // lse values are loaded by many threads at once).
+  float* w_lds = &red_o[0][0][0];  // reused: nsplit_max * G <= 4 * G * 128 floats
+  for (int i = tid; i < nsplit * G; i += kWgThreads) w_lds[i] = load_shared_f32(a.part_lse + base0 + i);
+  __syncthreads();
+  if (tid < G) {
+    float mx = -INFINITY;
+    for (int c = 0; c < nsplit; ++c) mx = fmaxf(mx, w_lds[c * G + tid]);
+    float ws = 0.f;
+    if (mx != -INFINITY)
+      for (int c = 0; c < nsplit; ++c) ws += __expf(w_lds[c * G + tid] - mx);
+    const float inv = ws > 0.f ? 1.f / ws : 0.f;
+    for (int c = 0; c < nsplit; ++c)
+      w_lds[c * G + tid] = mx != -INFINITY ? __expf(w_lds[c * G + tid] - mx) * inv : 0.f;
+    if (a.lse_out != nullptr) a.lse_out[hq0 + tid] = ws > 0.f ? mx + __logf(ws) : -INFINITY;
+  }
+  __syncthreads();
+  // out = sum_c w_c o_c, partials read in independent batches of 8.
   for (int i = tid; i < G * 128; i += kWgThreads) {
     const int hh = i / 128;
     const int d = i % 128;
-    float mx = -INFINITY;
-    for (int c = 0; c < nsplit; ++c) mx = fmaxf(mx, load_shared_f32(a.part_lse + base0 + c * G + hh));
-    float wsum = 0.f, o = 0.f;
-    if (mx == -INFINITY) {  // no visible token in any split (invalid selection)
-      store_out(qtag, a.out, (hq0 + hh) * 128 + d, 0.f);
-      if (d == 0 && a.lse_out != nullptr) a.lse_out[hq0 + hh] = -INFINITY;
-      continue;
+    const float* po = a.part_o + (base0 + hh) * 128 + d;
+    float o = 0.f;
+    for (int c0 = 0; c0 < nsplit; c0 += 8) {
+      // straight-line batch: indices past the last split re-read the last one
+      // and get weight 0
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = load_shared_f32(po + static_cast<int64_t>(min(c0 + u, nsplit - 1)) * G * 128);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        o = fmaf(c0 + u < nsplit ? w_lds[(c0 + u) * G + hh] : 0.f, v[u], o);
     }
-    for (int c = 0; c < nsplit; ++c) {
-      const float wc = __expf(load_shared_f32(a.part_lse + base0 + c * G + hh) - mx);
-      wsum += wc;
-      o = fmaf(wc, load_shared_f32(a.part_o + (base0 + c * G + hh) * 128 + d), o);
-    }
-    store_out(qtag, a.out, (hq0 + hh) * 128 + d, o / wsum);
-    if (d == 0 && a.lse_out != nullptr) a.lse_out[hq0 + hh] = mx + __logf(wsum);
+    store_out(qtag, a.out, (hq0 + hh) * 128 + d, o);
   }
 }
 

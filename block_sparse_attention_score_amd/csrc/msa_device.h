@@ -39,21 +39,34 @@ struct Raw8<FP8> {
   uint2 v;
 };
 
+// Pages of the pools are streamed once per call: their loads are
+// non-temporal, so they do not displace (or force the write-back of) lines
+// that other work keeps in the L2 and the Infinity Cache.  On MI355X this
+// about doubles the achieved read bandwidth of the page scans when the caches
+// hold dirty data.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ Raw8<BF16> load_raw(const BF16*, const void* base,
                                                int64_t idx) {
-  return {*reinterpret_cast<const uint4*>(
-      reinterpret_cast<const uint16_t*>(base) + idx)};
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+      reinterpret_cast<const uint16_t*>(base) + idx));
+  return {uint4{v.x, v.y, v.z, v.w}};
 }
 __device__ __forceinline__ Raw8<F32> load_raw(const F32*, const void* base,
                                               int64_t idx) {
-  const float4* p = reinterpret_cast<const float4*>(
+  const f32x4v_t* p = reinterpret_cast<const f32x4v_t*>(
       reinterpret_cast<const float*>(base) + idx);
-  return {p[0], p[1]};
+  const f32x4v_t a = __builtin_nontemporal_load(p);
+  const f32x4v_t b = __builtin_nontemporal_load(p + 1);
+  return {float4{a.x, a.y, a.z, a.w}, float4{b.x, b.y, b.z, b.w}};
 }
 __device__ __forceinline__ Raw8<FP8> load_raw(const FP8*, const void* base,
                                               int64_t idx) {
-  return {*reinterpret_cast<const uint2*>(
-      reinterpret_cast<const uint8_t*>(base) + idx)};
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(
+      reinterpret_cast<const uint8_t*>(base) + idx));
+  return {uint2{v.x, v.y}};
 }
 
 __device__ __forceinline__ void unpack(const Raw8<BF16>& r, float (&x)[8]) {
@@ -91,8 +104,11 @@ __device__ __forceinline__ void load8(const T* tag, const void* base, int64_t id
 // convert exactly (every e4m3 value is a bf16 value).
 __device__ __forceinline__ bf16x8_t load8_bf16(const BF16*, const void* base,
                                                int64_t idx) {
-  return *reinterpret_cast<const bf16x8_t*>(
-      reinterpret_cast<const uint16_t*>(base) + idx);
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+      reinterpret_cast<const uint16_t*>(base) + idx));
+  bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
 }
 
 __device__ __forceinline__ bf16x8_t load8_bf16(const FP8*, const void* base,

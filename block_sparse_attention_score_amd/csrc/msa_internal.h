@@ -26,6 +26,7 @@ struct ScoreArgs {
   int32_t topk, init, local, kmax;
   int32_t* sel;              // [B, Hidx, kmax]
   int32_t* cnt;              // [B, Hidx]
+  int32_t* sel_pages;        // [B, Hidx, kmax] physical pages of sel, or nullptr
 };
 
 // Standalone selection over precomputed score rows.
@@ -54,6 +55,7 @@ struct AttendArgs {
   int32_t num_seqs;
   const int32_t* sel;        // [B, Hidx, kmax]
   const int32_t* cnt;        // [B, Hidx]
+  const int32_t* sel_pages;  // [B, Hidx, kmax] pages of sel, or nullptr (table lookup)
   int32_t kmax;
   int32_t hkv, hidx;
   int32_t bps;               // selected blocks per split

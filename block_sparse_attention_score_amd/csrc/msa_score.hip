@@ -28,7 +28,9 @@ __global__ __launch_bounds__(kWgThreads) void decode_score_kernel(ScoreArgs a) {
   constexpr int LPR = DI / 8;          // lanes per token row
   constexpr int RPL = kWave / LPR;     // token rows per wave load
   constexpr int NLOAD = kBlock / RPL;  // loads per page per lane
-  constexpr int BATCH = __is_same(IT, F32) ? 8 : 16;
+  // up to 128 VGPRs of loads in flight per lane
+  constexpr int BATCH = (__is_same(IT, F32) ? 16 : 32) < NLOAD ? (__is_same(IT, F32) ? 16 : 32)
+                                                               : NLOAD;
   static_assert(NLOAD % BATCH == 0, "batch must divide the page");
 
   __shared__ SelectLds sl;
@@ -48,8 +50,10 @@ __global__ __launch_bounds__(kWgThreads) void decode_score_kernel(ScoreArgs a) {
     for (int j = nb + threadIdx.x; j < a.max_blocks; j += kWgThreads) srow[j] = -INFINITY;
   if (nb == 0) {
     if (a.fuse_select && chunk == 0) {
-      for (int i = threadIdx.x; i < a.kmax; i += kWgThreads)
+      for (int i = threadIdx.x; i < a.kmax; i += kWgThreads) {
         a.sel[static_cast<int64_t>(pair) * a.kmax + i] = -1;
+        if (a.sel_pages) a.sel_pages[static_cast<int64_t>(pair) * a.kmax + i] = -1;
+      }
       if (threadIdx.x == 0) a.cnt[pair] = 0;
     }
     return;
@@ -104,7 +108,10 @@ __global__ __launch_bounds__(kWgThreads) void decode_score_kernel(ScoreArgs a) {
   // The last chunk of the pair to finish selects over all of the pair's scores.
   if (!take_last_ticket(&a.tickets[pair], nchunks, &is_last)) return;
   select_row<MAXPER, true>(srow, nb, a.topk, a.init, a.local, a.kmax,
-                           a.sel + static_cast<int64_t>(pair) * a.kmax, a.cnt + pair, sl);
+                           a.sel + static_cast<int64_t>(pair) * a.kmax, a.cnt + pair, sl,
+                           a.block_table + static_cast<int64_t>(b) * a.max_blocks,
+                           a.sel_pages ? a.sel_pages + static_cast<int64_t>(pair) * a.kmax
+                                       : nullptr);
 }
 
 // One workgroup per (query token, index head) row.

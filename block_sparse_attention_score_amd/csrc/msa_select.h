@@ -37,11 +37,14 @@ __device__ __forceinline__ int forced_count(int nb, int init, int local) {
 // Must be called by all 256 threads of the workgroup.
 // `coherent`: the scores were written by other workgroups of this launch and
 // are read through device-coherent loads.
+// `pages`: when not null, the block-table row of the sequence; the physical
+// page of every selected block is then written to sel_pages as well.
 template <int MAXPER, bool COHERENT = false>
 __device__ void select_row(const float* __restrict__ s, int nb, int topk,
                            int init, int local, int kmax,
                            int32_t* __restrict__ sel, int32_t* __restrict__ cnt,
-                           SelectLds& L) {
+                           SelectLds& L, const int32_t* __restrict__ pages = nullptr,
+                           int32_t* __restrict__ sel_pages = nullptr) {
   const int tid = threadIdx.x;
   const int per = div_up(nb, kWgThreads);
   const int j0 = tid * per;
@@ -52,14 +55,21 @@ __device__ void select_row(const float* __restrict__ s, int nb, int topk,
   const int keff = min(topk, ncand);
   const bool take_all = keff == ncand;
 
+  // Straight-line loads (slots past the row re-read its last score and are
+  // discarded), so that all of a thread's loads are in flight at once.
   uint32_t key[MAXPER];
+  if (nb > 0) {
+    float v[MAXPER];
 #pragma unroll
-  for (int i = 0; i < MAXPER; ++i) {
-    const int j = j0 + i;
-    if (i < per && j < nb)
-      key[i] = score_key(COHERENT ? load_shared_f32(s + j) : s[j]);
-    else
-      key[i] = 0u;
+    for (int i = 0; i < MAXPER; ++i) {
+      const int j = min(j0 + i, nb - 1);
+      v[i] = COHERENT ? load_shared_f32(s + j) : s[j];
+    }
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) key[i] = (i < per && j0 + i < nb) ? score_key(v[i]) : 0u;
+  } else {
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) key[i] = 0u;
   }
   auto is_cand = [&](int j) { return j < nb && j >= lo_init && j < hi_local; };
 
@@ -130,10 +140,17 @@ __device__ void select_row(const float* __restrict__ s, int nb, int topk,
   }
   int pos = block_incl_scan(sel_local, L.wsum) - sel_local;
 #pragma unroll
-  for (int i = 0; i < MAXPER; ++i)
-    if (flag[i]) sel[pos++] = j0 + i;
+  for (int i = 0; i < MAXPER; ++i) {
+    if (flag[i]) {
+      if (sel_pages != nullptr) sel_pages[pos] = pages[j0 + i];
+      sel[pos++] = j0 + i;
+    }
+  }
   const int total = nforced + keff;
-  for (int i = total + tid; i < kmax; i += kWgThreads) sel[i] = -1;
+  for (int i = total + tid; i < kmax; i += kWgThreads) {
+    sel[i] = -1;
+    if (sel_pages != nullptr) sel_pages[i] = -1;
+  }
   if (tid == 0) *cnt = total;
   __syncthreads();
 }
