@@ -92,15 +92,26 @@ float softmax_scale_of(const msa_params_t& p) {
   return p.softmax_scale > 0.f ? p.softmax_scale : 1.0f / std::sqrt(float(p.head_dim));
 }
 
-// Selected blocks handled by one split-K workgroup.
-int blocks_per_split(const msa_params_t& /*p*/, int32_t /*num_seqs*/) { return 1; }
+// Selected blocks handled by one split-K workgroup: enough splits that about
+// kAttendWgTarget workgroups cover the batch (two resident per CU on the 256
+// CUs), each streaming its blocks through a two-stage load pipeline.
+constexpr int kAttendWgTarget = 2048;
+constexpr int kMaxBlocksPerSplit = 32;  // the attention kernel's limit
+int blocks_per_split(const msa_params_t& p, int32_t num_seqs) {
+  const int kmax = kmax_of(p);
+  const int units = num_seqs * p.num_kv_heads > 0 ? num_seqs * p.num_kv_heads : 1;
+  const int splits = kAttendWgTarget / units > 1 ? kAttendWgTarget / units : 1;
+  const int bps = (kmax + splits - 1) / splits;
+  return bps < 1 ? 1 : (bps > kMaxBlocksPerSplit ? kMaxBlocksPerSplit : bps);
+}
 
 // Pages scored by one workgroup in the decode scan.
-constexpr int kPagesPerItem = 4;
+constexpr int kPagesPerItem = 16;
 
 struct DecodeLayout {
-  size_t scores, sel, cnt, sel_pages, part_o, part_lse, tk_score, tk_attend, total;
-  int bps, nsplit_max;
+  size_t scores, sel, cnt, sel_pages, part_o, part_lse, items, n_items;
+  size_t counter, tk_score, ready, tk_attend, total;  // hand-off words, contiguous, zeroed per call
+  int bps, nsplit_max, chunks_per_pair;
 };
 
 DecodeLayout decode_layout(const msa_params_t& p, int32_t B, int32_t MB) {
@@ -121,10 +132,98 @@ DecodeLayout decode_layout(const msa_params_t& p, int32_t B, int32_t MB) {
   l.sel_pages = take(sizeof(int32_t) * size_t(B) * p.num_idx_heads * kmax);
   l.part_o = take(sizeof(float) * size_t(B) * p.num_kv_heads * l.nsplit_max * G * p.head_dim);
   l.part_lse = take(sizeof(float) * size_t(B) * p.num_kv_heads * l.nsplit_max * G);
-  l.tk_score = take(sizeof(uint32_t) * size_t(B) * p.num_idx_heads);
-  l.tk_attend = take(sizeof(uint32_t) * size_t(B) * p.num_kv_heads);
+  l.chunks_per_pair = (MB + kPagesPerItem - 1) / kPagesPerItem;
+  l.items = take(sizeof(int32_t) * 2 *
+                 (size_t(B) * p.num_idx_heads * l.chunks_per_pair +
+                  size_t(B) * p.num_kv_heads * l.nsplit_max));
+  l.n_items = take(sizeof(int32_t));
+  // hand-off words: one contiguous run of 32-bit words (no padding between)
+  l.counter = off;
+  l.tk_score = l.counter + sizeof(uint32_t);
+  l.ready = l.tk_score + sizeof(uint32_t) * size_t(B) * p.num_idx_heads;
+  l.tk_attend = l.ready + sizeof(uint32_t) * size_t(B) * p.num_idx_heads;
+  off = l.tk_attend + sizeof(uint32_t) * size_t(B) * p.num_kv_heads;
+  l.total = align_up(off);
+  return l;
+}
+
+// Prefill workspace: scores, selection, split partials and tickets per token.
+struct PrefillLayout {
+  size_t scores, sel, cnt, part_o, part_lse, tickets, total;
+  int bps, nsplit_max;
+};
+
+PrefillLayout prefill_layout(const msa_params_t& p, int32_t T, int32_t MB) {
+  PrefillLayout l{};
+  const int kmax = kmax_of(p);
+  const int G = group_of(p);
+  l.bps = blocks_per_split(p, T);
+  l.nsplit_max = (kmax + l.bps - 1) / l.bps;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  l.scores = take(sizeof(float) * size_t(T) * p.num_idx_heads * MB);
+  l.sel = take(sizeof(int32_t) * size_t(T) * p.num_idx_heads * kmax);
+  l.cnt = take(sizeof(int32_t) * size_t(T) * p.num_idx_heads);
+  const size_t parts = l.nsplit_max > 1 ? size_t(T) * p.num_kv_heads * l.nsplit_max * G : 0;
+  l.part_o = take(sizeof(float) * parts * p.head_dim);
+  l.part_lse = take(sizeof(float) * parts);
+  l.tickets = take(sizeof(uint32_t) * size_t(T) * p.num_kv_heads);
   l.total = off;
   return l;
+}
+
+// Blocks of keys per prefill scoring workgroup.
+constexpr int kPrefillBlocksPerChunk = 32;
+
+msa::PrefillScoreArgs prefill_score_args(const msa_params_t& p, const void* idx_q,
+                                         const void* idx_k_pool, int64_t num_pages,
+                                         const int32_t* block_table, int32_t max_blocks,
+                                         const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                                         int32_t num_seqs, int32_t T, float* scores) {
+  msa::PrefillScoreArgs a{};
+  a.idx_q = idx_q;
+  a.idx_k = idx_k_pool;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.num_seqs = num_seqs;
+  a.hidx = p.num_idx_heads;
+  a.max_tiles = (T + 255) / 256;
+  a.blocks_per_chunk = kPrefillBlocksPerChunk;
+  a.kchunks = (max_blocks + kPrefillBlocksPerChunk - 1) / kPrefillBlocksPerChunk;
+  a.scores = scores;
+  return a;
+}
+
+msa::SelectArgs select_args(const msa_params_t& p, const float* scores, int32_t max_blocks,
+                            const int32_t* seq_lens, const int32_t* cu_seqlens_q,
+                            int32_t num_seqs, int32_t T, int32_t* sel, int32_t* cnt) {
+  msa::SelectArgs a{};
+  a.scores = scores;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.num_seqs = num_seqs;
+  a.num_tokens = T;
+  a.hidx = p.num_idx_heads;
+  a.topk = p.topk;
+  a.init = p.init_blocks;
+  a.local = p.local_blocks;
+  a.kmax = kmax_of(p);
+  a.sel = sel;
+  a.cnt = cnt;
+  return a;
+}
+
+hipError_t launch_selection(const msa::SelectArgs& a, hipStream_t s) {
+  return msa::select_wave_fits(a.max_blocks) ? msa::launch_select_wave(a, s)
+                                             : msa::launch_select(a, s);
 }
 
 msa_status_t check_ws(const void* ws, size_t ws_bytes, size_t need) {
@@ -141,13 +240,12 @@ msa_status_t hip_status(hipError_t e, const char* what) {
   return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Split-K attention over an existing selection (decode).
-msa_status_t enqueue_attend(const msa_params_t& p, const void* q, const void* k_pool,
-                            const void* v_pool, int64_t num_pages,
-                            const int32_t* block_table, int32_t max_blocks,
-                            const int32_t* seq_lens, int32_t num_seqs, const int32_t* sel,
-                            const int32_t* cnt, const int32_t* sel_pages, void* out,
-                            float* lse_out, void* ws, const DecodeLayout& l, hipStream_t s) {
+// Arguments of the split-K attention (decode).
+msa::AttendArgs attend_args(const msa_params_t& p, const void* q, const void* k_pool,
+                            const void* v_pool, int64_t num_pages, const int32_t* block_table,
+                            int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs,
+                            const int32_t* sel, const int32_t* cnt, const int32_t* sel_pages,
+                            void* out, float* lse_out, void* ws, const DecodeLayout& l) {
   char* w = static_cast<char*>(ws);
   msa::AttendArgs a{};
   a.q = q;
@@ -157,7 +255,9 @@ msa_status_t enqueue_attend(const msa_params_t& p, const void* q, const void* k_
   a.block_table = block_table;
   a.max_blocks = max_blocks;
   a.seq_lens = seq_lens;
+  a.cu_seqlens_q = nullptr;
   a.num_seqs = num_seqs;
+  a.num_tokens = num_seqs;
   a.sel = sel;
   a.cnt = cnt;
   a.sel_pages = sel_pages;
@@ -174,8 +274,7 @@ msa_status_t enqueue_attend(const msa_params_t& p, const void* q, const void* k_
   a.part_o = reinterpret_cast<float*>(w + l.part_o);
   a.part_lse = reinterpret_cast<float*>(w + l.part_lse);
   a.tickets = reinterpret_cast<uint32_t*>(w + l.tk_attend);
-  return hip_status(msa::launch_decode_attend(a, p.q_dtype, p.kv_dtype, group_of(p), s),
-                    "decode attend launch");
+  return a;
 }
 
 }  // namespace
@@ -208,9 +307,11 @@ size_t msa_prefill_workspace_size(const msa_params_t* params, int32_t num_seqs,
                                   int32_t num_q_tokens, int32_t max_blocks) {
   if (check_params(params) != MSA_OK) return 0;
   if (check_shape(num_seqs, max_blocks) != MSA_OK) return 0;
-  (void)num_q_tokens;
-  fail(MSA_ERR_UNSUPPORTED, "chunked prefill is not available in this build");
-  return 0;
+  if (num_q_tokens < 0) {
+    fail(MSA_ERR_INVALID_ARG, "num_q_tokens=%d < 0", num_q_tokens);
+    return 0;
+  }
+  return prefill_layout(*params, num_q_tokens, max_blocks).total;
 }
 
 msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
@@ -225,10 +326,23 @@ msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
   if (!idx_q || !idx_k_pool || !block_table || !seq_lens || !scores)
     return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
-  if (cu_seqlens_q != nullptr)
-    return fail(MSA_ERR_UNSUPPORTED, "prefill scoring is not available in this build");
-  (void)num_q_tokens;
   if (num_seqs == 0) return ok();
+  if (cu_seqlens_q != nullptr) {
+    if (num_q_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "num_q_tokens=%d < 0", num_q_tokens);
+    if (params->idx_dtype != MSA_BF16)
+      return fail(MSA_ERR_UNSUPPORTED, "prefill scoring needs bf16 index keys");
+    if (num_q_tokens == 0) return ok();
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(msa::launch_fill_f32(scores, int64_t(num_q_tokens) * params->num_idx_heads *
+                                                     max_blocks, -INFINITY, s),
+                    "score fill launch");
+    if (st != MSA_OK) return st;
+    const msa::PrefillScoreArgs pa =
+        prefill_score_args(*params, idx_q, idx_k_pool, num_pages, block_table, max_blocks,
+                           seq_lens, cu_seqlens_q, num_seqs, num_q_tokens, scores);
+    st = hip_status(msa::launch_prefill_score(pa, params->idx_dim, s), "prefill score launch");
+    return st == MSA_OK ? ok() : st;
+  }
   msa::ScoreArgs a{};
   a.idx_q = idx_q;
   a.idx_k = idx_k_pool;
@@ -242,7 +356,6 @@ msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
   a.chunks_per_pair = (max_blocks + kPagesPerItem - 1) / kPagesPerItem;
   a.scores = scores;
   a.fill_tail = 1;
-  a.fuse_select = 0;
   st = hip_status(msa::launch_decode_score(a, params->idx_dtype, params->idx_dim,
                                            static_cast<hipStream_t>(stream)),
                   "block score launch");
@@ -262,21 +375,9 @@ msa_status_t msa_select_blocks(const msa_params_t* params, const float* scores,
   const int32_t T = cu_seqlens_q == nullptr ? num_seqs : num_q_tokens;
   if (T < 0) return fail(MSA_ERR_INVALID_ARG, "num_q_tokens=%d < 0", T);
   if (T == 0) return ok();
-  msa::SelectArgs a{};
-  a.scores = scores;
-  a.max_blocks = max_blocks;
-  a.seq_lens = seq_lens;
-  a.cu_seqlens_q = cu_seqlens_q;
-  a.num_seqs = num_seqs;
-  a.num_tokens = T;
-  a.hidx = params->num_idx_heads;
-  a.topk = params->topk;
-  a.init = params->init_blocks;
-  a.local = params->local_blocks;
-  a.kmax = kmax_of(*params);
-  a.sel = sel_blocks;
-  a.cnt = sel_count;
-  st = hip_status(msa::launch_select(a, static_cast<hipStream_t>(stream)), "select launch");
+  const msa::SelectArgs a = select_args(*params, scores, max_blocks, seq_lens, cu_seqlens_q,
+                                        num_seqs, T, sel_blocks, sel_count);
+  st = hip_status(launch_selection(a, static_cast<hipStream_t>(stream)), "select launch");
   return st == MSA_OK ? ok() : st;
 }
 
@@ -297,6 +398,9 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const 
     return fail(MSA_ERR_INVALID_ARG, "sel_blocks_out and sel_count_out go together");
   if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
   const msa_params_t& p = *params;
+  if (int64_t(num_seqs) * p.num_idx_heads > msa::kMaxPairs)
+    return fail(MSA_ERR_UNSUPPORTED, "num_seqs * Hidx = %lld above %d",
+                (long long)num_seqs * p.num_idx_heads, msa::kMaxPairs);
   const DecodeLayout l = decode_layout(p, num_seqs, max_blocks);
   if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
   if (num_seqs == 0) return ok();
@@ -305,12 +409,29 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const 
   int32_t* sel = sel_blocks_out ? sel_blocks_out : reinterpret_cast<int32_t*>(w + l.sel);
   int32_t* cnt = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + l.cnt);
 
-  // Tickets of both fused stages start at zero (one fill over both arrays).
-  const int64_t ntk = int64_t(l.total - l.tk_score) / int64_t(sizeof(uint32_t));
-  st = hip_status(msa::launch_fill_u32(reinterpret_cast<uint32_t*>(w + l.tk_score), ntk, 0u, s),
-                  "ticket reset launch");
+  const int grid = msa::decode_fused_grid(p.idx_dtype, p.idx_dim, p.q_dtype, p.kv_dtype,
+                                          group_of(p));
+  if (grid <= 0) return fail(MSA_ERR_UNSUPPORTED, "no decode kernel for this parameter set");
+
+  // 1. planner: zero the hand-off words, order the work items
+  msa::PlanArgs pa{};
+  pa.seq_lens = seq_lens;
+  pa.num_seqs = num_seqs;
+  pa.hidx = p.num_idx_heads;
+  pa.kv_per_idx = p.num_kv_heads / p.num_idx_heads;
+  pa.max_blocks = max_blocks;
+  pa.pages_per_item = kPagesPerItem;
+  pa.nsplit_max = l.nsplit_max;
+  pa.lag = 2 * grid;
+  pa.zero_begin = reinterpret_cast<uint32_t*>(w + l.counter);
+  pa.zero_count = int64_t(l.tk_attend - l.counter) / int64_t(sizeof(uint32_t)) +
+                  int64_t(num_seqs) * p.num_kv_heads;
+  pa.items = reinterpret_cast<int2*>(w + l.items);
+  pa.n_items = reinterpret_cast<int32_t*>(w + l.n_items);
+  st = hip_status(msa::launch_decode_plan(pa, s), "decode plan launch");
   if (st != MSA_OK) return st;
 
+  // 2. persistent score -> select -> attend -> combine
   msa::ScoreArgs a{};
   a.idx_q = idx_q;
   a.idx_k = idx_k_pool;
@@ -324,8 +445,8 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const 
   a.chunks_per_pair = (max_blocks + kPagesPerItem - 1) / kPagesPerItem;
   a.scores = reinterpret_cast<float*>(w + l.scores);
   a.fill_tail = 0;
-  a.fuse_select = 1;
   a.tickets = reinterpret_cast<uint32_t*>(w + l.tk_score);
+  a.ready = reinterpret_cast<uint32_t*>(w + l.ready);
   a.topk = p.topk;
   a.init = p.init_blocks;
   a.local = p.local_blocks;
@@ -333,11 +454,17 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const 
   a.sel = sel;
   a.cnt = cnt;
   a.sel_pages = reinterpret_cast<int32_t*>(w + l.sel_pages);
-  st = hip_status(msa::launch_decode_score(a, p.idx_dtype, p.idx_dim, s),
-                  "score/select launch");
-  if (st != MSA_OK) return st;
-  st = enqueue_attend(p, q, k_pool, v_pool, num_pages, block_table, max_blocks, seq_lens,
-                      num_seqs, sel, cnt, a.sel_pages, out, lse_out, ws, l, s);
+  const msa::AttendArgs aa = attend_args(p, q, k_pool, v_pool, num_pages, block_table,
+                                         max_blocks, seq_lens, num_seqs, sel, cnt, a.sel_pages,
+                                         out, lse_out, ws, l);
+  msa::FusedArgs fa{};
+  fa.counter = reinterpret_cast<uint32_t*>(w + l.counter);
+  fa.items = reinterpret_cast<const int2*>(w + l.items);
+  fa.n_items = reinterpret_cast<const int32_t*>(w + l.n_items);
+  fa.nsplit_max = l.nsplit_max;
+  st = hip_status(msa::launch_decode_fused(a, aa, fa, p.idx_dtype, p.idx_dim, p.q_dtype,
+                                           p.kv_dtype, group_of(p), s),
+                  "decode launch");
   return st == MSA_OK ? ok() : st;
 }
 
@@ -362,8 +489,12 @@ msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q, const 
                                        int64_t(params->num_kv_heads) * num_seqs, 0u, s),
                   "ticket reset launch");
   if (st != MSA_OK) return st;
-  st = enqueue_attend(*params, q, k_pool, v_pool, num_pages, block_table, max_blocks, seq_lens,
-                      num_seqs, sel_blocks, sel_count, nullptr, out, lse_out, ws, l, s);
+  const msa::AttendArgs aa =
+      attend_args(*params, q, k_pool, v_pool, num_pages, block_table, max_blocks, seq_lens,
+                  num_seqs, sel_blocks, sel_count, nullptr, out, lse_out, ws, l);
+  st = hip_status(msa::launch_decode_attend(aa, params->q_dtype, params->kv_dtype,
+                                            group_of(*params), s),
+                  "decode attend launch");
   return st == MSA_OK ? ok() : st;
 }
 
@@ -378,11 +509,74 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
                                 void* stream) {
   msa_status_t st = check_params(params);
   if (st != MSA_OK) return st;
-  (void)q; (void)idx_q; (void)k_pool; (void)v_pool; (void)idx_k_pool; (void)num_pages;
-  (void)block_table; (void)max_blocks; (void)seq_lens; (void)cu_seqlens_q; (void)num_seqs;
-  (void)num_q_tokens; (void)out; (void)lse_out; (void)sel_blocks_out; (void)sel_count_out;
-  (void)ws; (void)ws_bytes; (void)stream;
-  return fail(MSA_ERR_UNSUPPORTED, "chunked prefill is not available in this build");
+  if ((st = check_shape(num_seqs, max_blocks)) != MSA_OK) return st;
+  if (!q || !idx_q || !k_pool || !v_pool || !idx_k_pool || !block_table || !seq_lens ||
+      !cu_seqlens_q || !out)
+    return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if ((sel_blocks_out == nullptr) != (sel_count_out == nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "sel_blocks_out and sel_count_out go together");
+  if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
+  if (num_q_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "num_q_tokens=%d < 0", num_q_tokens);
+  const msa_params_t& p = *params;
+  if (p.idx_dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "prefill scoring needs bf16 index keys");
+  const PrefillLayout l = prefill_layout(p, num_q_tokens, max_blocks);
+  if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
+  if (num_seqs == 0 || num_q_tokens == 0) return ok();
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  int32_t* sel = sel_blocks_out ? sel_blocks_out : reinterpret_cast<int32_t*>(w + l.sel);
+  int32_t* cnt = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + l.cnt);
+  float* scores = reinterpret_cast<float*>(w + l.scores);
+
+  if (l.nsplit_max > 1) {
+    st = hip_status(msa::launch_fill_u32(reinterpret_cast<uint32_t*>(w + l.tickets),
+                                         int64_t(num_q_tokens) * p.num_kv_heads, 0u, s),
+                    "ticket reset launch");
+    if (st != MSA_OK) return st;
+  }
+  // 1. scores (causal GEMM, block max)
+  const msa::PrefillScoreArgs pa =
+      prefill_score_args(p, idx_q, idx_k_pool, num_pages, block_table, max_blocks, seq_lens,
+                         cu_seqlens_q, num_seqs, num_q_tokens, scores);
+  st = hip_status(msa::launch_prefill_score(pa, p.idx_dim, s), "prefill score launch");
+  if (st != MSA_OK) return st;
+  // 2. per-token selection
+  const msa::SelectArgs sa = select_args(p, scores, max_blocks, seq_lens, cu_seqlens_q, num_seqs,
+                                         num_q_tokens, sel, cnt);
+  st = hip_status(launch_selection(sa, s), "prefill select launch");
+  if (st != MSA_OK) return st;
+  // 3. attention over each token's selection
+  msa::AttendArgs aa{};
+  aa.q = q;
+  aa.k_pool = k_pool;
+  aa.v_pool = v_pool;
+  aa.num_pages = num_pages;
+  aa.block_table = block_table;
+  aa.max_blocks = max_blocks;
+  aa.seq_lens = seq_lens;
+  aa.cu_seqlens_q = cu_seqlens_q;
+  aa.num_seqs = num_seqs;
+  aa.num_tokens = num_q_tokens;
+  aa.sel = sel;
+  aa.cnt = cnt;
+  aa.sel_pages = nullptr;
+  aa.kmax = kmax_of(p);
+  aa.hkv = p.num_kv_heads;
+  aa.hidx = p.num_idx_heads;
+  aa.bps = l.bps;
+  aa.nsplit_max = l.nsplit_max;
+  const float ks = p.kv_dtype == MSA_FP8_E4M3 ? p.k_scale : 1.f;
+  aa.qk_scale_log2 = softmax_scale_of(p) * ks * 1.4426950408889634f;
+  aa.v_scale = p.kv_dtype == MSA_FP8_E4M3 ? p.v_scale : 1.f;
+  aa.out = out;
+  aa.lse_out = lse_out;
+  aa.part_o = reinterpret_cast<float*>(w + l.part_o);
+  aa.part_lse = reinterpret_cast<float*>(w + l.part_lse);
+  aa.tickets = reinterpret_cast<uint32_t*>(w + l.tickets);
+  st = hip_status(msa::launch_decode_attend(aa, p.q_dtype, p.kv_dtype, group_of(p), s),
+                  "prefill attend launch");
+  return st == MSA_OK ? ok() : st;
 }
 
 msa_status_t msa_fp8_e4m3_dequant(const uint8_t* in, float* out, int64_t n, float scale,

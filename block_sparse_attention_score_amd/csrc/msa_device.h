@@ -100,6 +100,50 @@ __device__ __forceinline__ void load8(const T* tag, const void* base, int64_t id
   unpack(load_raw(tag, base, idx), x);
 }
 
+// Four consecutive elements (8-, 4- or 16-byte non-temporal loads).
+template <class T>
+struct Raw4;
+template <>
+struct Raw4<BF16> {
+  uint2 v;
+};
+template <>
+struct Raw4<F32> {
+  float4 v;
+};
+template <>
+struct Raw4<FP8> {
+  uint32_t v;
+};
+
+__device__ __forceinline__ Raw4<BF16> load_raw4(const BF16*, const void* base, int64_t idx) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(
+      reinterpret_cast<const uint16_t*>(base) + idx));
+  return {uint2{v.x, v.y}};
+}
+__device__ __forceinline__ Raw4<F32> load_raw4(const F32*, const void* base, int64_t idx) {
+  const f32x4v_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(
+      reinterpret_cast<const float*>(base) + idx));
+  return {float4{v.x, v.y, v.z, v.w}};
+}
+__device__ __forceinline__ Raw4<FP8> load_raw4(const FP8*, const void* base, int64_t idx) {
+  return {__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(
+      reinterpret_cast<const uint8_t*>(base) + idx))};
+}
+
+__device__ __forceinline__ void unpack4(const Raw4<BF16>& r, float (&x)[4]) {
+  x[0] = __uint_as_float(r.v.x << 16);
+  x[1] = __uint_as_float(r.v.x & 0xffff0000u);
+  x[2] = __uint_as_float(r.v.y << 16);
+  x[3] = __uint_as_float(r.v.y & 0xffff0000u);
+}
+__device__ __forceinline__ void unpack4(const Raw4<F32>& r, float (&x)[4]) {
+  x[0] = r.v.x; x[1] = r.v.y; x[2] = r.v.z; x[3] = r.v.w;
+}
+__device__ __forceinline__ void unpack4(const Raw4<FP8>& r, float (&x)[4]) {
+  fp8x4_to_f32(r.v, x);
+}
+
 // Eight consecutive elements packed as bf16 for an MFMA operand.  fp8 codes
 // convert exactly (every e4m3 value is a bf16 value).
 __device__ __forceinline__ bf16x8_t load8_bf16(const BF16*, const void* base,
@@ -221,6 +265,12 @@ __device__ __forceinline__ void store_shared_f32(float* p, float v) {
 }
 __device__ __forceinline__ float load_shared_f32(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_shared_i32(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_shared_i32(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // All of this wave's memory operations have completed.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }

@@ -19,14 +19,57 @@ struct ScoreArgs {
   int32_t pages_per_item;    // blocks scored by one workgroup
   int32_t chunks_per_pair;   // ceil(max_blocks / pages_per_item)
   float* scores;             // [B, Hidx, max_blocks]
-  int32_t fill_tail;         // write -inf past each row's last block
-  // fused selection (fuse_select != 0)
-  int32_t fuse_select;
+  int32_t fill_tail;         // write -inf past each row's last block (unfused)
+  // fused selection (persistent decode kernel only)
   uint32_t* tickets;         // [B * Hidx], zero on entry
+  uint32_t* ready;           // [B * Hidx], zero on entry; set once a pair is selected
   int32_t topk, init, local, kmax;
   int32_t* sel;              // [B, Hidx, kmax]
   int32_t* cnt;              // [B, Hidx]
   int32_t* sel_pages;        // [B, Hidx, kmax] physical pages of sel, or nullptr
+};
+
+// Decode planner: zeroes the hand-off words and orders the work items.
+struct PlanArgs {
+  const int32_t* seq_lens;
+  int32_t num_seqs;
+  int32_t hidx;
+  int32_t kv_per_idx;        // Hkv / Hidx
+  int32_t max_blocks;
+  int32_t pages_per_item;
+  int32_t nsplit_max;
+  int32_t lag;               // score items between a pair's last chunk and its attention
+  uint32_t* zero_begin;      // counters, tickets and ready flags
+  int64_t zero_count;
+  int2* items;               // score (pair, chunk) or attention (-1 - unit, split)
+  int32_t* n_items;
+};
+
+// Persistent decode kernel: work items claimed in order from one counter.
+struct FusedArgs {
+  uint32_t* counter;         // zero on entry
+  const int2* items;         // from the planner
+  const int32_t* n_items;
+  int32_t nsplit_max;
+};
+
+constexpr int kMaxPairs = 8192;  // (sequence, index head) pairs per decode call
+
+// Prefill index scoring (causal GEMM with a block-max epilogue).
+struct PrefillScoreArgs {
+  const void* idx_q;         // [T, Hidx, Di] bf16
+  const void* idx_k;         // [P, Hidx, 128, Di] bf16
+  int64_t num_pages;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens_q;
+  int32_t num_seqs;
+  int32_t hidx;
+  int32_t max_tiles;         // 256-row query tiles of the longest possible sequence
+  int32_t blocks_per_chunk;  // key blocks per workgroup
+  int32_t kchunks;           // ceil(max_blocks / blocks_per_chunk)
+  float* scores;             // [T, Hidx, max_blocks]
 };
 
 // Standalone selection over precomputed score rows.
@@ -52,8 +95,10 @@ struct AttendArgs {
   const int32_t* block_table;
   int32_t max_blocks;
   const int32_t* seq_lens;
+  const int32_t* cu_seqlens_q;  // nullptr: decode (query t is sequence t)
   int32_t num_seqs;
-  const int32_t* sel;        // [B, Hidx, kmax]
+  int32_t num_tokens;        // query tokens (decode: num_seqs)
+  const int32_t* sel;        // [T, Hidx, kmax]
   const int32_t* cnt;        // [B, Hidx]
   const int32_t* sel_pages;  // [B, Hidx, kmax] pages of sel, or nullptr (table lookup)
   int32_t kmax;
@@ -70,9 +115,19 @@ struct AttendArgs {
 };
 
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
+hipError_t launch_decode_plan(const PlanArgs& a, hipStream_t s);
+// Resident workgroups of the persistent decode kernel of a call (0: none).
+int decode_fused_grid(int idx_dtype, int idx_dim, int q_dtype, int kv_dtype, int group);
+hipError_t launch_decode_fused(const ScoreArgs& sa, const AttendArgs& aa, const FusedArgs& fa,
+                               int idx_dtype, int idx_dim, int q_dtype, int kv_dtype, int group,
+                               hipStream_t s);
 hipError_t launch_decode_score(const ScoreArgs& a, int idx_dtype, int idx_dim,
                                hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_prefill_score(const PrefillScoreArgs& a, int idx_dim, hipStream_t s);
+bool select_wave_fits(int max_blocks);
+hipError_t launch_select_wave(const SelectArgs& a, hipStream_t s);
+hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
 hipError_t launch_decode_attend(const AttendArgs& a, int q_dtype, int kv_dtype,
                                 int group, hipStream_t s);
 hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale,

@@ -1,0 +1,264 @@
+// Chunked prefill: index-head scoring as a causal bf16 GEMM on the matrix
+// cores with a block-max epilogue, and a wavefront-per-row top-k selection.
+//
+// vLLM page sparse_attention_msa.py (MiniMaxM3SparseMSAImpl.forward, prefill
+// part): prefill tokens attend causally to the selected 128-token blocks of
+// their sequence; sglang page minimax_sparse_backend.py (forward_extend): the
+// new tokens of a sequence follow its cached prefix (cu_seqlens over the
+// extend lengths, prefix lengths alongside).
+//
+// Scoring.  For the n_b new tokens of sequence b (positions p_i = L_b - n_b +
+// i) and index head h, score[i][j] = max over tokens t <= p_i of block j of
+// q_idx[i] . k_idx[t].  A workgroup takes 256 query rows (4 waves x 64) and a
+// run of key blocks; the query rows stay in registers as MFMA A operands; each
+// key block (128 tokens x Di) is staged once in LDS (double-buffered, rows
+// padded against bank conflicts) and read by all four waves as B operands of
+// v_mfma_f32_16x16x32_bf16; each 16x16 result tile is masked causally and
+// folded into per-row maxima, which DPP reduces across the tile's 16 token
+// lanes.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+constexpr int kPrefillRows = 256;  // query rows per scoring workgroup
+
+template <int DI>
+__global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillScoreArgs a) {
+  constexpr int KS = DI / 32;              // 32-dim k-steps
+  constexpr int ROW_BYTES = DI * 2 + 16;   // padded LDS row
+  constexpr int CHUNKS = DI * 2 / 16;      // 16-byte chunks per key row
+  constexpr int LOADS = 128 * CHUNKS / kWgThreads;  // per thread per block
+  __shared__ __attribute__((aligned(16))) char kbuf[2][128 * ROW_BYTES];
+
+  // workgroup -> (sequence, 256-row query tile, index head, key-block chunk);
+  // tiles past a sequence's new tokens exit at once
+  const int per_seq = a.max_tiles * a.hidx * a.kchunks;
+  const int b = blockIdx.x / per_seq;
+  int rem = blockIdx.x - b * per_seq;
+  const int qt = rem / (a.hidx * a.kchunks);
+  rem -= qt * a.hidx * a.kchunks;
+  const int h = rem / a.kchunks;
+  const int kc = rem - h * a.kchunks;
+  const int cu0 = a.cu_seqlens_q[b];
+  const int nq = a.cu_seqlens_q[b + 1] - cu0;
+  const int i0 = qt * kPrefillRows;
+  if (i0 >= nq) return;
+  const int L = a.seq_lens[b];
+  const int prefix = L - nq;
+  const int p_last = prefix + min(nq, i0 + kPrefillRows) - 1;
+  if (p_last < 0) return;
+  const int nb_tile = min(p_last / kBlock + 1, a.max_blocks);
+  const int j0 = kc * a.blocks_per_chunk;
+  const int j1 = min(nb_tile, j0 + a.blocks_per_chunk);
+  if (j0 >= j1) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = tid / kWave;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
+
+  // A operands: this wave's 64 query rows (4 row tiles of 16).
+  bf16x8_t qa[4][KS];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int i = i0 + 64 * w + 16 * rt + l16;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (i < nq) {
+        qa[rt][s] = *reinterpret_cast<const bf16x8_t*>(
+            reinterpret_cast<const uint16_t*>(a.idx_q) +
+            (static_cast<int64_t>(cu0 + i) * a.hidx + h) * DI + 32 * s + 8 * q4);
+      } else {
+        qa[rt][s] = bf16x8_t{};
+      }
+    }
+  }
+
+  // Cooperative copy of one key block: thread chunk c = tid + 256 * k covers
+  // row c / CHUNKS, bytes 16 * (c % CHUNKS).
+  auto block_base = [&](int j) -> const char* {
+    int page = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
+    if (page < 0 || page >= a.num_pages) page = 0;  // never read: rows get masked below
+    return reinterpret_cast<const char*>(a.idx_k) +
+           ((static_cast<int64_t>(page) * a.hidx + h) * kBlock * DI) * 2;
+  };
+  uint4 stage[LOADS];
+  auto fetch = [&](int j) {
+    const char* src = block_base(j);
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) {
+      const int c = tid + kWgThreads * k;
+      const u32x4_t v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(src + (c / CHUNKS) * (DI * 2) + 16 * (c % CHUNKS)));
+      stage[k] = uint4{v.x, v.y, v.z, v.w};
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) {
+      const int c = tid + kWgThreads * k;
+      *reinterpret_cast<uint4*>(&kbuf[buf][(c / CHUNKS) * ROW_BYTES + 16 * (c % CHUNKS)]) = stage[k];
+    }
+  };
+
+  fetch(j0);
+  store(0);
+  __syncthreads();
+  for (int j = j0; j < j1; ++j) {
+    const int buf = (j - j0) & 1;
+    const bool more = j + 1 < j1;
+    if (more) fetch(j + 1);
+    const bool page_ok = [&] {
+      const int pg = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
+      return pg >= 0 && pg < a.num_pages;
+    }();
+
+    float mx[4][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx[rt][r] = -INFINITY;
+#pragma unroll 2
+    for (int n = 0; n < 8; ++n) {
+      f32x4_t acc[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8_t kb = *reinterpret_cast<const bf16x8_t*>(
+            &kbuf[buf][(16 * n + l16) * ROW_BYTES + 2 * (32 * s + 8 * q4)]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][s], kb, acc[rt], 0, 0, 0);
+      }
+      const int tok = kBlock * j + 16 * n + l16;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pos = prefix + i0 + 64 * w + 16 * rt + 4 * q4 + r;
+          mx[rt][r] = fmaxf(mx[rt][r], (tok <= pos && page_ok) ? acc[rt][r] : -INFINITY);
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float m = group_max<16>(mx[rt][r]);
+        const int i = i0 + 64 * w + 16 * rt + 4 * q4 + r;
+        if (l16 == 0 && i < nq)
+          a.scores[(static_cast<int64_t>(cu0 + i) * a.hidx + h) * a.max_blocks + j] = m;
+      }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+// One wavefront per (query token, index head) row, for rows of up to 64 * E
+// blocks.  Keys are order-preserving 32-bit images of the scores (-0 folded
+// onto +0); the k-th largest candidate key T is found bit by bit from the top
+// with ballot counts; candidates above T are taken, and of those equal to T
+// the first ones in block order (ranks by ballot prefix counts), which is the
+// lower-index tie rule.  Output slots come from the same prefix counts, so the
+// list is ascending.
+template <int E>
+__global__ __launch_bounds__(kWgThreads) void select_wave_kernel(SelectArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row = blockIdx.x * (kWgThreads / kWave) + threadIdx.x / kWave;
+  if (row >= a.num_tokens * a.hidx) return;
+  const int t = row / a.hidx;
+  int p;
+  if (a.cu_seqlens_q == nullptr) {
+    p = a.seq_lens[t] - 1;
+  } else {
+    int lo = 0, hi = a.num_seqs;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (a.cu_seqlens_q[mid] <= t) lo = mid; else hi = mid;
+    }
+    p = a.seq_lens[lo] - (a.cu_seqlens_q[lo + 1] - a.cu_seqlens_q[lo]) + (t - a.cu_seqlens_q[lo]);
+  }
+  const int nb = p >= 0 ? min(p / kBlock + 1, a.max_blocks) : 0;
+  const int lo_init = min(a.init, nb);
+  const int hi_local = max(0, nb - a.local);
+  const int na = min(a.init, nb);
+  const int nforced = na + (nb - hi_local) - max(0, na - hi_local);
+  const int ncand = nb - nforced;
+  const int keff = min(a.topk, ncand);
+  const bool take_all = keff == ncand;
+  const float* srow = a.scores + static_cast<int64_t>(row) * a.max_blocks;
+
+  uint32_t key[E];
+  bool cand[E], valid[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + kWave * e;
+    valid[e] = j < nb;
+    cand[e] = valid[e] && j >= lo_init && j < hi_local;
+    key[e] = cand[e] ? score_key(srow[j]) : 0u;
+  }
+  uint32_t T = 0u;
+  int need = 0;
+  if (!take_all) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(cand[e] && key[e] >= c));
+      if (cnt >= keff) T = c;
+    }
+    int above = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) above += __popcll(__ballot(cand[e] && key[e] > T));
+    need = keff - above;
+  }
+  auto below = [&](uint64_t m) {  // set bits of m in lanes below this one
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+  };
+  int eq_before = 0, pos_before = 0;
+  int32_t* sel = a.sel + static_cast<int64_t>(row) * a.kmax;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t eqm = __ballot(!take_all && cand[e] && key[e] == T);
+    const bool is_eq = !take_all && cand[e] && key[e] == T;
+    const int rank = eq_before + below(eqm);
+    const bool pick = valid[e] && (!cand[e] || take_all || key[e] > T || (is_eq && rank < need));
+    const uint64_t pm = __ballot(pick);
+    if (pick) sel[pos_before + below(pm)] = lane + kWave * e;
+    eq_before += __popcll(eqm);
+    pos_before += __popcll(pm);
+  }
+  const int total = nforced + keff;
+  for (int i = total + lane; i < a.kmax; i += kWave) sel[i] = -1;
+  if (lane == 0) a.cnt[row] = total;
+}
+
+// ------------------------------------------------------------- launchers
+
+hipError_t launch_prefill_score(const PrefillScoreArgs& a, int idx_dim, hipStream_t s) {
+  const int grid = a.num_seqs * a.max_tiles * a.hidx * a.kchunks;
+  if (grid == 0) return hipSuccess;
+  if (idx_dim == 128)
+    prefill_score_kernel<128><<<grid, kWgThreads, 0, s>>>(a);
+  else
+    prefill_score_kernel<64><<<grid, kWgThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+bool select_wave_fits(int max_blocks) { return max_blocks <= 1024; }
+
+hipError_t launch_select_wave(const SelectArgs& a, hipStream_t s) {
+  const int rows = a.num_tokens * a.hidx;
+  if (rows == 0) return hipSuccess;
+  const int grid = (rows + 3) / 4;
+  if (a.max_blocks <= 256)
+    select_wave_kernel<4><<<grid, kWgThreads, 0, s>>>(a);
+  else
+    select_wave_kernel<16><<<grid, kWgThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,124 @@
+// Decode block scoring (index-head scan) of one chunk of pages, with the
+// per-pair selection fused behind it.
+//
+// Scoring (sglang page minimax_sparse_backend.py: the index query idx_q,
+// sparse_index_dim wide, is scored against the index-key cache of every
+// block_size_k block; the score is the max over the block's tokens of
+// q_idx . k_idx, tokens after the query excluded):
+//
+// A workgroup (4 waves) scores `pages_per_item` consecutive blocks of one
+// (sequence, index head) pair; each wave streams whole 128-token pages.  A
+// page of index keys is one contiguous run of 128 * Di elements (head-major
+// pages), read with non-temporal 16-byte loads, 32 per lane in flight: Di/8
+// lanes cover one token row, so a wave instruction reads 64/(Di/8) full rows.
+// Every lane keeps the 8 query elements of its column slice in registers,
+// forms an 8-term partial dot product, the row is summed across its lanes
+// with DPP, tokens past the query are masked by select (never by
+// multiplying, so stale bytes cannot leak), and the wave reduces the block
+// max.  In the fused form the workgroup that finishes a pair last (atomic
+// ticket) selects that pair's blocks and raises the pair's ready flag.
+#pragma once
+
+#include "msa_device.h"
+#include "msa_internal.h"
+#include "msa_select.h"
+
+namespace msa {
+
+// Raises a pair's ready flag after every thread's selection stores landed.
+__device__ __forceinline__ void publish_ready(uint32_t* flag) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class IT, int DI, int MAXPER, bool FUSED>
+__device__ void score_chunk(const ScoreArgs& a, int pair, int chunk, SelectLds& sl,
+                            int* lds_flag) {
+  constexpr int LPR = DI / 8;          // lanes per token row
+  constexpr int RPL = kWave / LPR;     // token rows per wave load
+  constexpr int NLOAD = kBlock / RPL;  // loads per page per lane
+  // up to 128 VGPRs of loads in flight per lane
+  constexpr int BATCH = (__is_same(IT, F32) ? 16 : 32) < NLOAD ? (__is_same(IT, F32) ? 16 : 32)
+                                                               : NLOAD;
+  static_assert(NLOAD % BATCH == 0, "batch must divide the page");
+
+  const int b = pair / a.hidx;
+  const int h = pair - b * a.hidx;
+  const int L = a.seq_lens[b];
+  // (a sequence longer than its table row is a caller error: clamp to the row)
+  const int nb = L > 0 ? min((L - 1) / kBlock + 1, a.max_blocks) : 0;
+  const int nchunks = div_up(nb, a.pages_per_item);
+  float* srow = a.scores + static_cast<int64_t>(pair) * a.max_blocks;
+
+  if (!FUSED && a.fill_tail && chunk == 0)
+    for (int j = nb + threadIdx.x; j < a.max_blocks; j += kWgThreads) srow[j] = -INFINITY;
+  if (nb == 0) {
+    if (FUSED && chunk == 0) {
+      for (int i = threadIdx.x; i < a.kmax; i += kWgThreads) {
+        store_shared_i32(a.sel + static_cast<int64_t>(pair) * a.kmax + i, -1);
+        if (a.sel_pages) store_shared_i32(a.sel_pages + static_cast<int64_t>(pair) * a.kmax + i, -1);
+      }
+      if (threadIdx.x == 0) store_shared_i32(a.cnt + pair, 0);
+      publish_ready(a.ready + pair);
+    }
+    return;
+  }
+  if (chunk >= nchunks) return;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int row = lane / LPR;
+  const int col = lane % LPR;
+  const IT* tag = nullptr;
+
+  float qv[8];
+  load8(tag, a.idx_q, (static_cast<int64_t>(b) * a.hidx + h) * DI + col * 8, qv);
+
+  const int p = L - 1;
+  const int j0 = chunk * a.pages_per_item;
+  const int j1 = min(nb, j0 + a.pages_per_item);
+  for (int j = j0 + w; j < j1; j += kWgThreads / kWave) {
+    const int page = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
+    float m = -INFINITY;
+    if (page >= 0 && page < a.num_pages) {
+      const int nvalid = min(kBlock, p + 1 - j * kBlock);
+      const int64_t base =
+          (static_cast<int64_t>(page) * a.hidx + h) * kBlock * DI + row * DI + col * 8;
+#pragma unroll
+      for (int i0 = 0; i0 < NLOAD; i0 += BATCH) {
+        Raw8<IT> raw[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i)
+          raw[i] = load_raw(tag, a.idx_k, base + static_cast<int64_t>((i0 + i) * RPL) * DI);
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          float x[8];
+          unpack(raw[i], x);
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d = fmaf(qv[e], x[e], d);
+          d = group_sum<LPR>(d);
+          const int t = (i0 + i) * RPL + row;
+          m = fmaxf(m, t < nvalid ? d : -INFINITY);
+        }
+      }
+      m = wave_max(m);
+    }
+    if (lane == 0) {
+      if (FUSED) store_shared_f32(srow + j, m); else srow[j] = m;
+    }
+  }
+
+  if (!FUSED) return;
+  // The last chunk of the pair to finish selects over all of the pair's scores.
+  if (!take_last_ticket(&a.tickets[pair], nchunks, lds_flag)) return;
+  select_row<MAXPER, true>(srow, nb, a.topk, a.init, a.local, a.kmax,
+                           a.sel + static_cast<int64_t>(pair) * a.kmax, a.cnt + pair, sl,
+                           a.block_table + static_cast<int64_t>(b) * a.max_blocks,
+                           a.sel_pages ? a.sel_pages + static_cast<int64_t>(pair) * a.kmax
+                                       : nullptr);
+  publish_ready(a.ready + pair);
+}
+
+}  // namespace msa

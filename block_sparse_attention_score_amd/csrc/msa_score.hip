@@ -1,117 +1,16 @@
-// Decode block scoring (index-head scan) with the selection fused behind it,
-// the standalone selection kernel, and small utility kernels.
-//
-// Scoring (sglang page minimax_sparse_backend.py: the index query
-// idx_q, sparse_index_dim wide, is scored against the index-key cache of
-// every block_size_k block; the score is the max over the block's tokens of
-// q_idx . k_idx, tokens after the query excluded):
-//
-// One workgroup (4 waves) scores `pages_per_item` consecutive blocks of one
-// (sequence, index head) pair; each wave streams whole 128-token pages.  A
-// page of index keys is one contiguous run of 128 * Di elements (head-major
-// pages), read with 16-byte loads: Di/8 lanes cover one token row, so a wave
-// instruction reads 64/(Di/8) full rows.  Every lane keeps the 8 query
-// elements of its column slice in registers, forms an 8-term partial dot
-// product, the row is summed across its lanes with DPP, tokens past the query
-// are masked by select (never by multiplying, so stale bytes cannot leak),
-// and the wave reduces the block max.  The workgroup that finishes last for a
-// pair (atomic ticket, agent-scope fences) runs the selection for that pair
-// while other workgroups keep streaming.
-#include "msa_device.h"
-#include "msa_internal.h"
-#include "msa_select.h"
+// Standalone kernels: decode block scoring (step 1 alone), per-row selection
+// (step 2 alone), the decode work planner, and fp8 dequantisation.
+#include "msa_score.h"
 
 namespace msa {
 
-template <class IT, int DI, int MAXPER>
+// One workgroup per (pair, chunk); scores only.
+template <class IT, int DI>
 __global__ __launch_bounds__(kWgThreads) void decode_score_kernel(ScoreArgs a) {
-  constexpr int LPR = DI / 8;          // lanes per token row
-  constexpr int RPL = kWave / LPR;     // token rows per wave load
-  constexpr int NLOAD = kBlock / RPL;  // loads per page per lane
-  // up to 128 VGPRs of loads in flight per lane
-  constexpr int BATCH = (__is_same(IT, F32) ? 16 : 32) < NLOAD ? (__is_same(IT, F32) ? 16 : 32)
-                                                               : NLOAD;
-  static_assert(NLOAD % BATCH == 0, "batch must divide the page");
-
   __shared__ SelectLds sl;
-  __shared__ int is_last;
-
+  __shared__ int flag;
   const int pair = blockIdx.x / a.chunks_per_pair;
-  const int chunk = blockIdx.x - pair * a.chunks_per_pair;
-  const int b = pair / a.hidx;
-  const int h = pair - b * a.hidx;
-  const int L = a.seq_lens[b];
-  // (a sequence longer than its table row is a caller error: clamp to the row)
-  const int nb = L > 0 ? min((L - 1) / kBlock + 1, a.max_blocks) : 0;
-  const int nchunks = div_up(nb, a.pages_per_item);
-  float* srow = a.scores + static_cast<int64_t>(pair) * a.max_blocks;
-
-  if (a.fill_tail && chunk == 0)
-    for (int j = nb + threadIdx.x; j < a.max_blocks; j += kWgThreads) srow[j] = -INFINITY;
-  if (nb == 0) {
-    if (a.fuse_select && chunk == 0) {
-      for (int i = threadIdx.x; i < a.kmax; i += kWgThreads) {
-        a.sel[static_cast<int64_t>(pair) * a.kmax + i] = -1;
-        if (a.sel_pages) a.sel_pages[static_cast<int64_t>(pair) * a.kmax + i] = -1;
-      }
-      if (threadIdx.x == 0) a.cnt[pair] = 0;
-    }
-    return;
-  }
-  if (chunk >= nchunks) return;
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-  const int row = lane / LPR;
-  const int col = lane % LPR;
-  const IT* tag = nullptr;
-
-  float qv[8];
-  load8(tag, a.idx_q, (static_cast<int64_t>(b) * a.hidx + h) * DI + col * 8, qv);
-
-  const int p = L - 1;
-  const int j0 = chunk * a.pages_per_item;
-  const int j1 = min(nb, j0 + a.pages_per_item);
-  for (int j = j0 + w; j < j1; j += kWgThreads / kWave) {
-    const int page = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
-    float m = -INFINITY;
-    if (page >= 0 && page < a.num_pages) {
-      const int nvalid = min(kBlock, p + 1 - j * kBlock);
-      const int64_t base =
-          (static_cast<int64_t>(page) * a.hidx + h) * kBlock * DI + row * DI + col * 8;
-#pragma unroll
-      for (int i0 = 0; i0 < NLOAD; i0 += BATCH) {
-        Raw8<IT> raw[BATCH];
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i)
-          raw[i] = load_raw(tag, a.idx_k, base + static_cast<int64_t>((i0 + i) * RPL) * DI);
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-          float x[8];
-          unpack(raw[i], x);
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) d = fmaf(qv[e], x[e], d);
-          d = group_sum<LPR>(d);
-          const int t = (i0 + i) * RPL + row;
-          m = fmaxf(m, t < nvalid ? d : -INFINITY);
-        }
-      }
-      m = wave_max(m);
-    }
-    if (lane == 0) {
-      if (a.fuse_select) store_shared_f32(srow + j, m); else srow[j] = m;
-    }
-  }
-
-  if (!a.fuse_select) return;
-  // The last chunk of the pair to finish selects over all of the pair's scores.
-  if (!take_last_ticket(&a.tickets[pair], nchunks, &is_last)) return;
-  select_row<MAXPER, true>(srow, nb, a.topk, a.init, a.local, a.kmax,
-                           a.sel + static_cast<int64_t>(pair) * a.kmax, a.cnt + pair, sl,
-                           a.block_table + static_cast<int64_t>(b) * a.max_blocks,
-                           a.sel_pages ? a.sel_pages + static_cast<int64_t>(pair) * a.kmax
-                                       : nullptr);
+  score_chunk<IT, DI, 4, false>(a, pair, blockIdx.x - pair * a.chunks_per_pair, sl, &flag);
 }
 
 // One workgroup per (query token, index head) row.
@@ -140,6 +39,88 @@ __global__ __launch_bounds__(kWgThreads) void select_kernel(SelectArgs a) {
                      a.cnt + rowi, sl);
 }
 
+// Workgroup-wide inclusive scan over 1024 threads (16 waves).
+__device__ __forceinline__ int block1024_incl_scan(int v, int* wsum) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int n = __shfl_up(v, o);
+    if (lane >= o) v += n;
+  }
+  if (lane == kWave - 1) wsum[w] = v;
+  __syncthreads();
+  int add = 0;
+  for (int i = 0; i < w; ++i) add += wsum[i];
+  __syncthreads();
+  return v + add;
+}
+
+// Decode planner (one workgroup).  Zeroes the hand-off words and writes the
+// order in which the persistent decode kernel claims its work: the score
+// items (pair, chunk) of every (sequence, index head) pair, pair-major, with
+// the attention splits of a pair's kv heads placed `lag` score items after
+// the pair's last score item (or at the end), so that they are claimed about
+// when the pair's selection is done.  A pair with no tokens gets one score
+// item, which publishes its empty selection.  Every attention item follows
+// all score items of its pair, which is what keeps the kernel's waits finite.
+__global__ __launch_bounds__(1024) void decode_plan_kernel(PlanArgs a) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  __shared__ int s_end[kMaxPairs];  // inclusive end of each pair's score items
+  for (int64_t i = threadIdx.x; i < a.zero_count; i += 1024) a.zero_begin[i] = 0u;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  const int npairs = a.num_seqs * a.hidx;
+  for (int base = 0; base < npairs; base += 1024) {
+    const int pair = base + static_cast<int>(threadIdx.x);
+    int n = 0;
+    if (pair < npairs) {
+      const int L = a.seq_lens[pair / a.hidx];
+      const int nb = L > 0 ? min((L - 1) / kBlock + 1, a.max_blocks) : 0;
+      n = max(1, div_up(nb, a.pages_per_item));
+    }
+    const int incl = block1024_incl_scan(n, wsum);
+    if (pair < npairs) s_end[pair] = carry + incl;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry += incl;
+    __syncthreads();
+  }
+  const int n_score = carry;
+  const int per_pair = a.kv_per_idx * a.nsplit_max;  // attention items of a pair
+  // number of pairs q with s_end[q] <= v (s_end is increasing)
+  auto count_le = [&](int v) {
+    int lo = 0, hi = npairs;
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (s_end[mid] <= v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
+  // attention items: pair p's group sits before score item min(n_score, end + lag)
+  for (int i = threadIdx.x; i < per_pair * npairs; i += 1024) {
+    const int pair = i / per_pair;
+    const int r = i - pair * per_pair;
+    const int ins = min(n_score, s_end[pair] + a.lag);
+    const int unit = pair * a.kv_per_idx + r / a.nsplit_max;
+    a.items[ins + per_pair * pair + r] = make_int2(-1 - unit, r % a.nsplit_max);
+  }
+  // score item k follows the attention groups of every pair q with
+  // end(q) + lag <= k
+  for (int k = threadIdx.x; k < n_score; k += 1024) {
+    const int pair = count_le(k);  // first pair whose end exceeds k
+    const int start = pair > 0 ? s_end[pair - 1] : 0;
+    a.items[k + per_pair * count_le(k - a.lag)] = make_int2(pair, k - start);
+  }
+  if (threadIdx.x == 0) *a.n_items = n_score + per_pair * npairs;
+}
+
+__global__ void fill_f32_kernel(float* p, int64_t n, float value) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = value;
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t value) {
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -165,13 +146,22 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s
   return hipGetLastError();
 }
 
+hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  fill_f32_kernel<<<static_cast<int>(blocks < 2048 ? blocks : 2048), 256, 0, s>>>(p, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_plan(const PlanArgs& a, hipStream_t s) {
+  decode_plan_kernel<<<1, 1024, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 template <class IT, int DI>
 static void launch_score_t(const ScoreArgs& a, hipStream_t s) {
   const int grid = a.num_seqs * a.hidx * a.chunks_per_pair;
-  if (a.max_blocks <= 1024)
-    decode_score_kernel<IT, DI, 4><<<grid, kWgThreads, 0, s>>>(a);
-  else
-    decode_score_kernel<IT, DI, 32><<<grid, kWgThreads, 0, s>>>(a);
+  decode_score_kernel<IT, DI><<<grid, kWgThreads, 0, s>>>(a);
 }
 
 hipError_t launch_decode_score(const ScoreArgs& a, int idx_dtype, int idx_dim,

@@ -35,8 +35,8 @@ __device__ __forceinline__ int forced_count(int nb, int init, int local) {
 
 // s: nb scores of one (query, index head) row.  MAXPER >= ceil(nb / 256).
 // Must be called by all 256 threads of the workgroup.
-// `coherent`: the scores were written by other workgroups of this launch and
-// are read through device-coherent loads.
+// COHERENT: the scores were written by other workgroups of this launch (read
+// with device-coherent loads) and the selection is written the same way.
 // `pages`: when not null, the block-table row of the sequence; the physical
 // page of every selected block is then written to sel_pages as well.
 template <int MAXPER, bool COHERENT = false>
@@ -139,19 +139,24 @@ __device__ void select_row(const float* __restrict__ s, int nb, int topk,
     sel_local += f ? 1 : 0;
   }
   int pos = block_incl_scan(sel_local, L.wsum) - sel_local;
+  // COHERENT: the selection is read by other workgroups of this launch.
+  auto put = [&](int32_t* q, int32_t v) {
+    if (COHERENT) store_shared_i32(q, v); else *q = v;
+  };
 #pragma unroll
   for (int i = 0; i < MAXPER; ++i) {
     if (flag[i]) {
-      if (sel_pages != nullptr) sel_pages[pos] = pages[j0 + i];
-      sel[pos++] = j0 + i;
+      if (sel_pages != nullptr) put(sel_pages + pos, pages[j0 + i]);
+      put(sel + pos, j0 + i);
+      ++pos;
     }
   }
   const int total = nforced + keff;
   for (int i = total + tid; i < kmax; i += kWgThreads) {
-    sel[i] = -1;
-    if (sel_pages != nullptr) sel_pages[i] = -1;
+    put(sel + i, -1);
+    if (sel_pages != nullptr) put(sel_pages + i, -1);
   }
-  if (tid == 0) *cnt = total;
+  if (tid == 0) put(cnt, total);
   __syncthreads();
 }
 

@@ -99,14 +99,19 @@ def decode(arr: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
 # Query positions
 # --------------------------------------------------------------------------
 
-def query_positions(seq_lens: np.ndarray, cu_seqlens_q: Optional[np.ndarray]):
+def query_positions(seq_lens: np.ndarray, cu_seqlens_q: Optional[np.ndarray],
+                    positions=None):
     """List of (sequence b, position p) per query token.
 
     Decode (no cu_seqlens_q): one query per sequence at p = L_b - 1.
     Prefill: the n_b = cu[b+1]-cu[b] new tokens are the sequence's last ones,
     p = L_b - n_b + i (the sglang page passes prefix lengths alongside
-    ``cu_seqlens``; the prefix is L_b - n_b).
+    ``cu_seqlens``; the prefix is L_b - n_b).  ``positions`` (a list of
+    (b, p)) names the query rows explicitly instead, e.g. a sample of a
+    prefill's tokens.
     """
+    if positions is not None:
+        return [(int(b), int(p)) for b, p in positions]
     out = []
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     if cu_seqlens_q is None:
@@ -155,7 +160,7 @@ def block_scores(inp: dict) -> np.ndarray:
     T, Hidx, _ = iq_all.shape
     MB = inp["block_table"].shape[1]
     out = np.full((T, Hidx, MB), -np.inf)
-    pos = query_positions(inp["seq_lens"], inp.get("cu_seqlens_q"))
+    pos = query_positions(inp["seq_lens"], inp.get("cu_seqlens_q"), inp.get("positions"))
     by_seq = {}
     for t, (b, p) in enumerate(pos):
         by_seq.setdefault(b, []).append((t, p))
@@ -222,7 +227,7 @@ def select(inp: dict, scores: np.ndarray):
     K = kmax(inp["topk"], inp["init"], inp["local"])
     sel = np.full((T, Hidx, K), -1, dtype=np.int32)
     cnt = np.zeros((T, Hidx), dtype=np.int32)
-    pos = query_positions(inp["seq_lens"], inp.get("cu_seqlens_q"))
+    pos = query_positions(inp["seq_lens"], inp.get("cu_seqlens_q"), inp.get("positions"))
     for t, (b, p) in enumerate(pos):
         nb = num_visible_blocks(p)
         for h in range(Hidx):
@@ -275,7 +280,7 @@ def attend(inp: dict, sel: np.ndarray, cnt: np.ndarray, scale: Optional[float] =
     sc = (1.0 / math.sqrt(D)) if not scale else float(scale)
     out = np.zeros((T, Hq, D))
     lse = np.full((T, Hq), -np.inf)
-    pos = query_positions(inp["seq_lens"], inp.get("cu_seqlens_q"))
+    pos = query_positions(inp["seq_lens"], inp.get("cu_seqlens_q"), inp.get("positions"))
     by_seq = {}
     for t, (b, p) in enumerate(pos):
         by_seq.setdefault(b, []).append((t, p))
