@@ -1,8 +1,12 @@
-"""Benchmark of block-sparse decode attention on one MI355X.
+"""Benchmark of block-sparse attention on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-A step is one msa_sparse_decode call (score every block of the index keys,
+Default workload: decode, batch 32 x 32768 tokens (the headline metric).
+``--workload prefill_4x4096_p16k`` measures chunked prefill instead (tokens/s,
+MFMA roofline of its dominant kernel).
+
+A decode step is one msa_sparse_decode call (score every block of the index keys,
 select, split-K attend over the selected blocks, combine) over one batch of
 synthetic inputs already resident in HBM.  Before every timed step a 1 GiB
 buffer is overwritten so that no input is served from the L2 or the 256 MB
@@ -78,6 +82,38 @@ def score_kernel_bytes(spec, seq_lens, max_blocks):
                + 4 * B * Hidx * max_blocks)
 
 
+def prefill_flops(spec, seq_lens, cu, sel_valid):
+    """Algorithmic flops of one prefill step: the causal index-score GEMM
+    (2 * Di per visible token per query and index head) and the attention over
+    each query's selected visible tokens (4 * D per token and q head: q.k and
+    p.v).  ``sel_valid`` sums the selected visible tokens over (query, index
+    head); every index head serves Hq / Hidx q heads."""
+    Hq, Hidx, D, Di = spec["Hq"], spec["Hidx"], spec["D"], spec["Di"]
+    score = 0
+    for b in range(len(seq_lens)):
+        n = int(cu[b + 1] - cu[b])
+        p0 = int(seq_lens[b]) - n
+        score += n * (p0 + 1) + n * (n - 1) // 2   # sum of (p + 1) over the queries
+    score *= 2 * Hidx * Di
+    attn = 4 * D * (Hq // Hidx) * int(sel_valid)
+    return score, attn
+
+
+def selected_valid_tokens(seq_lens, cu, sel, cnt):
+    """Sum over (query, index head) of the visible tokens of the selected blocks."""
+    tot = 0
+    for b in range(len(seq_lens)):
+        n = int(cu[b + 1] - cu[b])
+        L = int(seq_lens[b])
+        for i in range(n):
+            t = int(cu[b]) + i
+            p = L - n + i
+            for h in range(sel.shape[1]):
+                js = sel[t, h, : cnt[t, h]].astype(np.int64)
+                tot += int(np.minimum(128, p + 1 - 128 * js).sum())
+    return tot
+
+
 def cpu_baseline(case, spec, seconds):
     """The oracle as it stands, on the first n sequences of the same inputs."""
     import torch  # noqa: F401
@@ -129,9 +165,8 @@ def main():
     from synth import WORKLOAD_SEEDS, generate, workload
 
     spec = workload(args.workload)
-    if spec["kind"] != "decode":
-        print(f"{args.workload} is not a decode workload", file=sys.stderr)
-        sys.exit(2)
+    if spec["kind"] == "prefill":
+        return bench_prefill(args, spec)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     case = generate(spec, WORKLOAD_SEEDS[args.workload], device=dev)
@@ -231,6 +266,145 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, spec, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def bench_prefill(args, spec):
+    """Chunked prefill: tokens/s of msa_sparse_prefill, with the index-score
+    GEMM and the selection timed standalone on the same inputs (attention is
+    the remainder of the step)."""
+    import torch
+
+    import block_sparse_attention_score_amd as msa
+    from synth import WORKLOAD_SEEDS, generate
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = generate(spec, WORKLOAD_SEEDS[args.workload], device=dev)
+    cfg = msa.MsaConfig.from_spec(spec)
+    B, MB, T = case.B, case.max_blocks, case.T
+    ws = msa.alloc_workspace(msa.prefill_workspace_size(cfg, B, T, MB), dev)
+    out = torch.empty_like(case.q)
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+
+    def step():
+        msa.sparse_prefill(cfg, case.q, case.idx_q, case.k_pool, case.v_pool, case.idx_k_pool,
+                           case.block_table, case.seq_lens, case.cu_seqlens_q, out=out,
+                           workspace=ws)
+
+    _, _, sel, cnt = msa.sparse_prefill(cfg, case.q, case.idx_q, case.k_pool, case.v_pool,
+                                        case.idx_k_pool, case.block_table, case.seq_lens,
+                                        case.cu_seqlens_q, workspace=ws, return_selection=True)
+    torch.cuda.synchronize()
+    lens = case.seq_lens.cpu().numpy()
+    cu = case.cu_seqlens_q.cpu().numpy()
+    valid = selected_valid_tokens(lens, cu, sel.cpu().numpy(), cnt.cpu().numpy())
+    f_score, f_attn = prefill_flops(spec, lens, cu, valid)
+
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i in range(n):
+            flush.fill_(i)
+            evs[i][0].record(stream)
+            fn()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    step_ms = timed(step, args.steps)
+    t_wall = time.perf_counter() - t_wall0
+    ms = float(step_ms.mean())
+    scores = torch.empty((T, cfg.num_idx_heads, MB), dtype=torch.float32, device=dev)
+    score_ms = float(timed(lambda: msa.block_score(cfg, case.idx_q, case.idx_k_pool,
+                                                   case.block_table, case.seq_lens,
+                                                   cu_seqlens_q=case.cu_seqlens_q,
+                                                   scores=scores), args.steps).mean())
+    sel_ms = float(timed(lambda: msa.select_blocks(cfg, scores, case.seq_lens,
+                                                   cu_seqlens_q=case.cu_seqlens_q),
+                         args.steps).mean())
+    attn_ms = max(ms - score_ms - sel_ms, 1e-6)
+    peak = 2500.0
+    score_tf = f_score / (score_ms * 1e-3) / 1e12
+    attn_tf = f_attn / (attn_ms * 1e-3) / 1e12
+    dominant = "attention" if attn_ms >= score_ms else "score"
+    roof = {"kernel": "prefill attention (split-K over each token's selection)",
+            "bound": "mfma", "achieved": attn_tf, "peak": peak, "unit": "TFLOP/s",
+            "frac": attn_tf / peak, "traffic": None, "flops_per_launch": f_attn,
+            "ms_per_launch": attn_ms} if dominant == "attention" else \
+           {"kernel": "prefill_score_kernel (causal index-score GEMM)", "bound": "mfma",
+            "achieved": score_tf, "peak": peak, "unit": "TFLOP/s", "frac": score_tf / peak,
+            "traffic": None, "flops_per_launch": f_score, "ms_per_launch": score_ms}
+    res = {
+        "metric": "chunked-prefill tokens/sec at 1 MI355X",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "new_tokens": spec["n_new"],
+                   "prefix": spec["prefix"], "q_heads": spec["Hq"], "kv_heads": spec["Hkv"],
+                   "idx_heads": spec["Hidx"], "head_dim": spec["D"], "idx_dim": spec["Di"],
+                   "topk": spec["topk"], "init": spec["init"], "local": spec["local"],
+                   "page": 128, "parallelism": "none"},
+        "stages_ms": {"score_gemm": score_ms, "select": sel_ms, "attention": attn_ms},
+        "mfma_tflops": {"score_gemm": score_tf, "attention": attn_tf},
+        "flops": {"score_gemm": f_score, "attention": f_attn},
+        "wall_s_timed_region": t_wall,
+        "roofline": roof,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(case, spec, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_prefill(case, spec, seconds):
+    """The oracle on a bounded sample of prefill tokens (every sequence's new
+    tokens, strided), as tokens/s."""
+    import oracle
+    from synth import host_view
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    inp = host_view(case)
+    cu = case.cu_seqlens_q.cpu().numpy()
+    L = case.seq_lens.cpu().numpy()
+    done, t_used, stride = 0, 0.0, 64
+    offset = 0
+    while t_used < seconds and offset < stride:
+        rows, pos = [], []
+        for b in range(case.B):
+            n = int(cu[b + 1] - cu[b])
+            for i in range(offset, n, stride):
+                rows.append(int(cu[b]) + i)
+                pos.append((b, int(L[b]) - n + i))
+        sub = dict(inp)
+        sub["q"] = inp["q"][rows]
+        sub["idx_q"] = inp["idx_q"][rows]
+        sub["positions"] = pos
+        t0 = time.perf_counter()
+        oracle.sparse_attention(sub)
+        t_used += time.perf_counter() - t0
+        done += len(rows)
+        offset += 1
+    return dict(value=done / t_used, unit="tokens/s", cores=int(blas_threads),
+                host_cpus=len(os.sched_getaffinity(0)), kind="oracle",
+                sample=f"{done} of {case.T} prefill tokens of {spec['name']} (every 64th "
+                       f"token per sequence, all heads), {t_used:.1f} s of fp64 numpy")
 
 
 if __name__ == "__main__":
