@@ -94,19 +94,25 @@ float softmax_scale_of(const msa_params_t& p) {
 
 // Selected blocks handled by one split-K workgroup: enough splits that about
 // kAttendWgTarget workgroups cover the batch (two resident per CU on the 256
-// CUs), each streaming its blocks through a two-stage load pipeline.
-constexpr int kAttendWgTarget = 2048;
+// CUs); a multiple of 4, since each of a workgroup's four waves streams its
+// own blocks.
+constexpr int kAttendWgTarget = 512;
 constexpr int kMaxBlocksPerSplit = 32;  // the attention kernel's limit
-int blocks_per_split(const msa_params_t& p, int32_t num_seqs) {
+int blocks_per_split(const msa_params_t& p, int32_t num_units) {
   const int kmax = kmax_of(p);
-  const int units = num_seqs * p.num_kv_heads > 0 ? num_seqs * p.num_kv_heads : 1;
+  const int units = num_units * p.num_kv_heads > 0 ? num_units * p.num_kv_heads : 1;
   const int splits = kAttendWgTarget / units > 1 ? kAttendWgTarget / units : 1;
-  const int bps = (kmax + splits - 1) / splits;
-  return bps < 1 ? 1 : (bps > kMaxBlocksPerSplit ? kMaxBlocksPerSplit : bps);
+  int bps = (kmax + splits - 1) / splits;
+  bps = (bps + 3) / 4 * 4;
+  return bps > kMaxBlocksPerSplit ? kMaxBlocksPerSplit : bps;
 }
 
 // Pages scored by one workgroup in the decode scan.
 constexpr int kPagesPerItem = 16;
+// Decode as one persistent kernel (score, select and attention hand off work
+// through device memory) rather than a score kernel followed by an attention
+// kernel that selects inside each workgroup.
+constexpr bool kDecodeFused = false;
 
 struct DecodeLayout {
   size_t scores, sel, cnt, sel_pages, part_o, part_lse, items, n_items;
@@ -408,6 +414,41 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const 
   char* w = static_cast<char*>(ws);
   int32_t* sel = sel_blocks_out ? sel_blocks_out : reinterpret_cast<int32_t*>(w + l.sel);
   int32_t* cnt = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + l.cnt);
+
+  if (!kDecodeFused) {
+    // 1. scores of every visible block; workgroup 0 also zeroes the split
+    //    tickets of step 2
+    msa::ScoreArgs a{};
+    a.idx_q = idx_q;
+    a.idx_k = idx_k_pool;
+    a.num_pages = num_pages;
+    a.block_table = block_table;
+    a.max_blocks = max_blocks;
+    a.seq_lens = seq_lens;
+    a.num_seqs = num_seqs;
+    a.hidx = p.num_idx_heads;
+    a.pages_per_item = kPagesPerItem;
+    a.chunks_per_pair = (max_blocks + kPagesPerItem - 1) / kPagesPerItem;
+    a.scores = reinterpret_cast<float*>(w + l.scores);
+    a.fill_tail = 0;
+    a.zero_words = reinterpret_cast<uint32_t*>(w + l.tk_attend);
+    a.zero_count = num_seqs * p.num_kv_heads;
+    st = hip_status(msa::launch_decode_score(a, p.idx_dtype, p.idx_dim, s), "score launch");
+    if (st != MSA_OK) return st;
+    // 2. selection inside each attention workgroup, split-K attention, combine
+    msa::AttendArgs aa = attend_args(p, q, k_pool, v_pool, num_pages, block_table, max_blocks,
+                                     seq_lens, num_seqs, nullptr, nullptr, nullptr, out,
+                                     lse_out, ws, l);
+    aa.scores = a.scores;
+    aa.topk = p.topk;
+    aa.init = p.init_blocks;
+    aa.local = p.local_blocks;
+    aa.sel_out = sel_blocks_out;
+    aa.cnt_out = sel_count_out;
+    st = hip_status(msa::launch_decode_attend(aa, p.q_dtype, p.kv_dtype, group_of(p), s),
+                    "attention launch");
+    return st == MSA_OK ? ok() : st;
+  }
 
   const int grid = msa::decode_fused_grid(p.idx_dtype, p.idx_dim, p.q_dtype, p.kv_dtype,
                                           group_of(p));

@@ -29,6 +29,7 @@
 
 #include "msa_device.h"
 #include "msa_internal.h"
+#include "msa_select.h"
 
 namespace msa {
 
@@ -82,50 +83,60 @@ __device__ __forceinline__ void load_qfrag(const F32*, const void* q, int64_t ro
   }
 }
 
-// K rows of one block for this wave's two 16-token tiles (the B operand of
-// S = q K^T), kept as loaded until the MFMAs consume them.
+// ------------------------------------------------- per-lane token rows
+//
+// In the MFMA tiles below a lane serves token row (lane % 16) of a 16-token
+// tile and k-slot group q = lane / 16.  Row<KT> holds the elements of that
+// token row the lane feeds to the matrix cores: for bf16/fp8 four 8-element
+// chunks (dims 32c + 8q .. +8, c = 0..3), for f32 eight 4-element chunks
+// (dims 16c + 4q .. +4, c = 0..7).  The same dims are used for K (A operand
+// of S^T = K q^T) and for V (A operand of the exact 0/1 transpose below).
+
 template <class KT>
-struct KFrag;
+struct Row;
 template <>
-struct KFrag<BF16> {
-  bf16x8_t k[2][4];
+struct Row<BF16> {
+  bf16x8_t c[4];
 };
 template <>
-struct KFrag<FP8> {
-  Raw8<FP8> k[2][4];
+struct Row<FP8> {
+  Raw8<FP8> c[4];
 };
 template <>
-struct KFrag<F32> {
-  f32x4v_t k[2][8];
+struct Row<F32> {
+  f32x4v_t c[8];
 };
 
-// `row0` indexes element 0 of token (16 * tile0 + lane % 16) of the block.
-__device__ __forceinline__ void load_kfrag(const void* kp, int64_t row0, int kgrp,
-                                           KFrag<BF16>& f) {
+__device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, Row<BF16>& r) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      f.k[tt][s] = load8_bf16(static_cast<const BF16*>(nullptr), kp,
-                              row0 + tt * 16 * 128 + 32 * s + 8 * kgrp);
+  for (int c = 0; c < 4; ++c)
+    r.c[c] = load8_bf16(static_cast<const BF16*>(nullptr), pool, row0 + 32 * c + 8 * q);
 }
-__device__ __forceinline__ void load_kfrag(const void* kp, int64_t row0, int kgrp,
-                                           KFrag<FP8>& f) {
+__device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, Row<FP8>& r) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      f.k[tt][s] = load_raw(static_cast<const FP8*>(nullptr), kp,
-                            row0 + tt * 16 * 128 + 32 * s + 8 * kgrp);
+  for (int c = 0; c < 4; ++c)
+    r.c[c] = load_raw(static_cast<const FP8*>(nullptr), pool, row0 + 32 * c + 8 * q);
 }
-__device__ __forceinline__ void load_kfrag(const void* kp, int64_t row0, int kgrp,
-                                           KFrag<F32>& f) {
+__device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, Row<F32>& r) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int c = 0; c < 8; ++c)
+    r.c[c] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(
+        reinterpret_cast<const float*>(pool) + row0 + 16 * c + 4 * q));
+}
+
+// Rows past the query hold stale bytes (possibly NaN): zero them so that
+// 0 * NaN never enters an MFMA sum.
+// Clears the row when `keep` is false, without a branch: an AND with an
+// all-ones or all-zero mask, so no divergent region splits the chunk loop.
+template <class KT>
+__device__ __forceinline__ void mask_row(Row<KT>& r, bool keep) {
+  constexpr int kWords = sizeof(Row<KT>) / 4;
+  uint32_t u[kWords];
+  __builtin_memcpy(u, &r, sizeof(r));
+  const uint32_t m = keep ? 0xffffffffu : 0u;
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-      f.k[tt][m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(
-          reinterpret_cast<const float*>(kp) + row0 + tt * 16 * 128 + 16 * m + 4 * kgrp));
+  for (int i = 0; i < kWords; ++i) u[i] &= m;
+  __builtin_memcpy(&r, u, sizeof(r));
 }
 
 __device__ __forceinline__ bf16x8_t fp8_to_bf16x8(const Raw8<FP8>& r) {
@@ -139,32 +150,88 @@ __device__ __forceinline__ bf16x8_t fp8_to_bf16x8(const Raw8<FP8>& r) {
   __builtin_memcpy(&v, u, 16);
   return v;
 }
+__device__ __forceinline__ bf16x8_t as_bf16(const bf16x8_t& v) { return v; }
+__device__ __forceinline__ bf16x8_t as_bf16(const Raw8<FP8>& v) { return fp8_to_bf16x8(v); }
 
-// S tile tt (16 head rows x 16 tokens) from a K fragment.
-__device__ __forceinline__ f32x4_t qk_tile(const QFrag<BF16>& q, const KFrag<BF16>& f, int tt) {
+// S^T tile (16 tokens x 16 heads): lane holds S^T[4q + r][lane % 16].
+__device__ __forceinline__ f32x4_t st_tile(const QFrag<BF16>& qf, const Row<BF16>& k) {
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[s], f.k[tt][s], acc, 0, 0, 0);
+  for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k.c[c], qf.a[c], acc, 0, 0, 0);
   return acc;
 }
-__device__ __forceinline__ f32x4_t qk_tile(const QFrag<BF16>& q, const KFrag<FP8>& f, int tt) {
+__device__ __forceinline__ f32x4_t st_tile(const QFrag<BF16>& qf, const Row<FP8>& k) {
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q.a[s], fp8_to_bf16x8(f.k[tt][s]), acc, 0, 0, 0);
+  for (int c = 0; c < 4; ++c)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8_to_bf16x8(k.c[c]), qf.a[c], acc, 0, 0, 0);
   return acc;
 }
-__device__ __forceinline__ f32x4_t qk_tile(const QFrag<F32>& q, const KFrag<F32>& f, int tt) {
+__device__ __forceinline__ f32x4_t st_tile(const QFrag<F32>& qf, const Row<F32>& k) {
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(q.a[m].x, f.k[tt][m].x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(q.a[m].y, f.k[tt][m].y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(q.a[m].z, f.k[tt][m].z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(q.a[m].w, f.k[tt][m].w, acc, 0, 0, 0);
+  for (int c = 0; c < 8; ++c) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.c[c].x, qf.a[c].x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.c[c].y, qf.a[c].y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.c[c].z, qf.a[c].z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k.c[c].w, qf.a[c].w, acc, 0, 0, 0);
   }
   return acc;
+}
+
+// Transpose of a 16-token x 16-dim V tile (dims 16m .. +16) by an MFMA with a
+// 0/1 selector as the B operand: the result lane holds V[4q + r][16m + lane%16]
+// for r = 0..3, exactly (one product by 1.0, the rest by 0.0, rows zeroed
+// where V is stale).  `sel` is the selector of half m % 2 of a 32-dim chunk.
+__device__ __forceinline__ f32x4_t vt_tile(const Row<BF16>& v, int m, const bf16x8_t (&sel)[2]) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(v.c[m >> 1], sel[m & 1], f32x4_t{0.f, 0.f, 0.f, 0.f},
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t vt_tile(const Row<FP8>& v, int m, const bf16x8_t (&sel)[2]) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8_to_bf16x8(v.c[m >> 1]), sel[m & 1],
+                                                 f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+// f32: four 16x16x4 steps; step e contracts dim 16m + 4q + e against the
+// selector column (4q + e == lane % 16).
+__device__ __forceinline__ f32x4_t vt_tile(const Row<F32>& v, int m, const float (&self)[4]) {
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v.c[m].x, self[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v.c[m].y, self[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v.c[m].z, self[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v.c[m].w, self[3], acc, 0, 0, 0);
+  return acc;
+}
+
+// O^T[16m + 4q + r][head] += sum over tokens of V^T * P^T for two token tiles
+// a, b.  The k-slots of lane group q are the tokens 4q + r of tile a and of
+// tile b, which is where both the transposed V and P^T already sit.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+// Round-to-nearest-even through the hardware pair conversion (one
+// v_cvt_pk_bf16_f32 on gfx950, no branch for NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  uint32_t u;
+  __builtin_memcpy(&u, &v, 4);
+  return u;
+}
+__device__ __forceinline__ bf16x8_t pack8_exact(const f32x4_t& a, const f32x4_t& b) {
+  uint32_t u[4] = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                   pack_bf16x2(b[2], b[3])};
+  bf16x8_t v;
+  __builtin_memcpy(&v, u, 16);
+  return v;
+}
+__device__ __forceinline__ bf16x8_t pack8_rne(const f32x4_t& a, const f32x4_t& b) {
+  uint32_t u[4] = {pack_bf16x2_rne(a[0], a[1]), pack_bf16x2_rne(a[2], a[3]),
+                   pack_bf16x2_rne(b[0], b[1]), pack_bf16x2_rne(b[2], b[3])};
+  bf16x8_t v;
+  __builtin_memcpy(&v, u, 16);
+  return v;
 }
 
 __device__ __forceinline__ void store_out(const BF16*, void* out, int64_t idx, float v) {
@@ -182,16 +249,16 @@ __device__ __forceinline__ float exp2_or_zero(float x, float m) {
 
 template <int G>
 struct AttendLds {
-  alignas(16) float Ps[kBlock][G < 4 ? 4 : G];  // probabilities of the current block, token-major
-  float red_max[4][16];
-  float red_sum[4][16];
-  float m_run[16];
-  float l_run[16];
-  float alpha_s[16];
-  float red_o[4][G][kBlock];
+  float o[4][16][kBlock];  // per-wave partial outputs, [head][dim]
+  float m[4][16];          // per-wave running max (base 2, scaled logits)
+  float l[4][16];          // per-wave running sum
+  float m_all[16];
+  float l_all[16];
   int blk_nvalid[kMaxBps];
   int blk_page[kMaxBps];
+  int blk_j[kMaxBps];      // block ids of the split (selection inside the kernel)
   int is_last;
+  SelectLds sl;
 };
 
 // Sequence and position of query token t: decode has one query per sequence
@@ -222,9 +289,23 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   const int sel_row = t * a.hidx + h;
   int b, p;
   query_of(a, t, b, p);
-  const int cnt_raw = FUSED ? load_shared_i32(a.cnt + sel_row) : a.cnt[sel_row];
-  const int count = p >= 0 ? min(max(cnt_raw, 0), a.kmax) : 0;
+  const bool self_select = !FUSED && a.scores != nullptr;
+  // Blocks visible to the query, and the selection size that follows from
+  // them alone (init and local blocks plus min(topk, rest)).
+  const int nb_vis = p >= 0 ? min(p / kBlock + 1, a.max_blocks) : 0;
+  int count;
+  if (self_select) {
+    const int nf = forced_count(nb_vis, a.init, a.local);
+    count = nf + min(a.topk, nb_vis - nf);
+  } else {
+    const int cnt_raw = FUSED ? load_shared_i32(a.cnt + sel_row) : a.cnt[sel_row];
+    count = p >= 0 ? min(max(cnt_raw, 0), a.kmax) : 0;
+  }
   const int nsplit = div_up(count, a.bps);
+  // The writer of the selection outputs: split 0 of the first kv head of
+  // the index head.
+  const bool sel_writer = self_select && a.sel_out != nullptr && split == 0 &&
+                          g % (a.hkv / a.hidx) == 0;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
@@ -232,6 +313,11 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   const QT* qtag = nullptr;
   const KT* ktag = nullptr;
 
+  if (sel_writer && count == 0) {
+    for (int i = threadIdx.x; i < a.kmax; i += kWgThreads)
+      a.sel_out[static_cast<int64_t>(sel_row) * a.kmax + i] = -1;
+    if (threadIdx.x == 0) a.cnt_out[sel_row] = 0;
+  }
   if (count == 0) {
     if (split == 0) {
       for (int i = tid; i < G * 128; i += kWgThreads) store_out(qtag, a.out, hq0 * 128 + i, 0.f);
@@ -241,32 +327,35 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   }
   if (split >= nsplit) return;
 
-  const int qrow = lane & 15;   // MFMA row (head) / column (token) index
-  const int kgrp = lane >> 4;   // MFMA k-slot group; D rows 4*kgrp .. +3
-  const int prow = lane >> 5;   // P V: token row within a pair
-  const int pcol = lane & 31;   // P V: dims 4*pcol .. +4
-  constexpr int GP = G < 4 ? 4 : G;  // row stride of Ps
+  const int l16 = lane & 15;  // token row (MFMA A rows) / head column (B, D columns)
+  const int q4 = lane >> 4;   // k-slot group; D rows 4*q4 .. +3
 
+  // q^T as the B operand of S^T = K q^T (heads past G are zero columns).
   QFrag<QT> qf;
-  load_qfrag<G>(qtag, a.q, hq0, qrow, kgrp, qf);
-  if (tid < 16) {
-    S.m_run[tid] = -INFINITY;
-    S.l_run[tid] = 0.f;
-  }
-  float acc[G][4];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[hh][e] = 0.f;
+  load_qfrag<G>(qtag, a.q, hq0, l16, q4, qf);
 
   // Block ids and pages of this split (at most kMaxBps), resolved up front.
   const int bi0 = split * a.bps;
   const int nblk = min(count, bi0 + a.bps) - bi0;
+  if (self_select) {
+    // Every split of the row runs the same selection; each keeps its slots.
+    int32_t* so = sel_writer ? a.sel_out + static_cast<int64_t>(sel_row) * a.kmax : nullptr;
+    select_core<32, false>(a.scores + static_cast<int64_t>(sel_row) * a.max_blocks, nb_vis,
+                           a.topk, a.init, a.local, S.sl, [&](int pos, int j) {
+                             if (pos >= bi0 && pos < bi0 + nblk) S.blk_j[pos - bi0] = j;
+                             if (sel_writer) so[pos] = j;
+                           });
+    if (sel_writer) {
+      for (int i = count + tid; i < a.kmax; i += kWgThreads) so[i] = -1;
+      if (tid == 0) a.cnt_out[sel_row] = count;
+    }
+    __syncthreads();
+  }
   if (tid < nblk) {
     const int64_t at = static_cast<int64_t>(sel_row) * a.kmax + bi0 + tid;
-    const int j = FUSED ? load_shared_i32(a.sel + at) : a.sel[at];
+    const int j = self_select ? S.blk_j[tid] : FUSED ? load_shared_i32(a.sel + at) : a.sel[at];
     int page;
-    if (a.sel_pages != nullptr)
+    if (a.sel_pages != nullptr && !self_select)
       page = FUSED ? load_shared_i32(a.sel_pages + at) : a.sel_pages[at];
     else
       page = j >= 0 && j < a.max_blocks ? a.block_table[static_cast<int64_t>(b) * a.max_blocks + j]
@@ -277,122 +366,151 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   }
   __syncthreads();
 
-  // Element 0 of this lane's K row (tile 2w) and V row (token row prow) of block i.
-  auto k_row0 = [&](int i) {
-    return (static_cast<int64_t>(S.blk_page[i]) * a.hkv + g) * kBlock * 128 +
-           static_cast<int64_t>(32 * w + qrow) * 128;
-  };
-  auto v_row0 = [&](int i) {
-    return (static_cast<int64_t>(S.blk_page[i]) * a.hkv + g) * kBlock * 128 +
-           static_cast<int64_t>(32 * w + prow) * 128 + 4 * pcol;
-  };
+  // Wave w streams blocks w, w+4, ... of the split in chunks of TILES 16-token
+  // tiles, with its own online softmax; no barrier until the final merge.
+  constexpr bool kF32 = __is_same(KT, F32);
+  constexpr int TILES = kF32 ? 2 : 4;           // tiles per chunk
+  constexpr int CPB = 8 / TILES;                // chunks per 128-token block
+  const int my_blocks = nblk > w ? (nblk - w + 3) / 4 : 0;
+  const int nchunk = my_blocks * CPB;
 
-  // Two-stage pipeline: the next block's K and V are in flight while the
-  // current block is computed.
-  KFrag<KT> kc, kn;
-  Raw4<KT> vc[16], vn[16];
-  load_kfrag(a.k_pool, k_row0(0), kgrp, kc);
+  // 0/1 selectors for the V transpose.
+  bf16x8_t sel_bf[2];
+  float sel_f[4];
+  {
+    uint16_t e0[8], e1[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    vc[i] = load_raw4(ktag, a.v_pool, v_row0(0) + static_cast<int64_t>(2 * i) * 128);
-
-  for (int bi = 0; bi < nblk; ++bi) {
-    const int nvalid = S.blk_nvalid[bi];
-    const bool more = bi + 1 < nblk;
-    if (more) load_kfrag(a.k_pool, k_row0(bi + 1), kgrp, kn);
-
-    // S for this wave's 32 tokens: tiles n = 2w and 2w+1.
-    f32x4_t s[2];
+    for (int e = 0; e < 8; ++e) {
+      e0[e] = (8 * q4 + e == l16) ? 0x3F80 : 0;
+      e1[e] = (8 * q4 + e == 16 + l16) ? 0x3F80 : 0;
+    }
+    __builtin_memcpy(&sel_bf[0], e0, 16);
+    __builtin_memcpy(&sel_bf[1], e1, 16);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int tok = 32 * w + 16 * tt + qrow;
-      s[tt] = qk_tile(qf, kc, tt);
+    for (int e = 0; e < 4; ++e) sel_f[e] = (4 * q4 + e == l16) ? 1.f : 0.f;
+  }
+
+  auto chunk_block = [&](int c) { return w + 4 * (c / CPB); };
+  auto row0 = [&](int c, int tt) {
+    const int blk = chunk_block(c);
+    const int tok = (c % CPB) * TILES * 16 + 16 * tt + l16;
+    return (static_cast<int64_t>(S.blk_page[blk]) * a.hkv + g) * kBlock * 128 +
+           static_cast<int64_t>(tok) * 128;
+  };
+  auto tok_valid = [&](int c, int tt) {
+    return (c % CPB) * TILES * 16 + 16 * tt + l16 < S.blk_nvalid[chunk_block(c)];
+  };
+
+  Row<KT> kr[TILES], vr[TILES];
+  if (nchunk > 0) {
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt) load_row(a.k_pool, row0(0, tt), q4, kr[tt]);
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt) load_row(a.v_pool, row0(0, tt), q4, vr[tt]);
+  }
+  float m_run = -INFINITY, l_run = 0.f;  // for head column l16
+  f32x4_t acc[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // One chunk: S^T, online softmax, O^T += V^T P^T.  The loads of the next
+  // chunk are issued between the stages (K after S^T, V after P V); the loop
+  // below runs all chunks but the last with `next` set and then the last one
+  // without, so every load inside the loop is unconditional and the waits
+  // before S^T and before P V cover only the loads they need.
+  auto chunk = [&](int c, bool next) {
+    const int nvalid = S.blk_nvalid[chunk_block(c)];
+    const int tok0 = (c % CPB) * TILES * 16;
+    f32x4_t st[TILES];
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt) {
+      st[tt] = st_tile(qf, kr[tt]);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        s[tt][r] = tok < nvalid ? s[tt][r] * a.qk_scale_log2 : -INFINITY;
+        st[tt][r] = tok0 + 16 * tt + 4 * q4 + r < nvalid ? st[tt][r] * a.qk_scale_log2 : -INFINITY;
     }
+    if (next) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mx = group_max<16>(fmaxf(s[0][r], s[1][r]));
-      if (qrow == 0) S.red_max[w][4 * kgrp + r] = mx;
+      for (int tt = 0; tt < TILES; ++tt) load_row(a.k_pool, row0(c + 1, tt), q4, kr[tt]);
     }
-    __syncthreads();
-    if (tid < 16) {
-      const float mb = fmaxf(fmaxf(S.red_max[0][tid], S.red_max[1][tid]),
-                             fmaxf(S.red_max[2][tid], S.red_max[3][tid]));
-      const float mo = S.m_run[tid];
-      const float mn = fmaxf(mo, mb);
-      S.alpha_s[tid] = mo == mn ? 1.f : exp2f(mo - mn);
-      S.m_run[tid] = mn;
-    }
-    __syncthreads();
+    float mc = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hr = 4 * kgrp + r;
-      const float mr = S.m_run[hr];
-      const float p0 = exp2_or_zero(s[0][r], mr);
-      const float p1 = exp2_or_zero(s[1][r], mr);
-      if (hr < G) {
-        S.Ps[32 * w + qrow][hr] = p0;
-        S.Ps[32 * w + 16 + qrow][hr] = p1;
+    for (int tt = 0; tt < TILES; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mc = fmaxf(mc, st[tt][r]);
+    mc = fmaxf(mc, __shfl_xor(mc, 16));
+    mc = fmaxf(mc, __shfl_xor(mc, 32));
+    const float mn = fmaxf(m_run, mc);
+    const float alpha = m_run == mn ? 1.f : exp2f(m_run - mn);
+    float ls = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < TILES; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        st[tt][r] = exp2_or_zero(st[tt][r], mn);
+        ls += st[tt][r];
       }
-      const float sm = group_sum<16>(p0 + p1);
-      if (qrow == 0) S.red_sum[w][hr] = sm;
-    }
-    __syncthreads();
-    if (more) {
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    l_run = l_run * alpha + ls;
+    m_run = mn;
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        vn[i] = load_raw4(ktag, a.v_pool, v_row0(bi + 1) + static_cast<int64_t>(2 * i) * 128);
-    }
-    if (tid < 16)
-      S.l_run[tid] = S.l_run[tid] * S.alpha_s[tid] +
-                   (S.red_sum[0][tid] + S.red_sum[1][tid]) + (S.red_sum[2][tid] + S.red_sum[3][tid]);
+    for (int m = 0; m < 8; ++m) acc[m] *= alpha;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float al = S.alpha_s[hh];
+    for (int tt = 0; tt < TILES; ++tt)
+      mask_row(vr[tt], tok_valid(c, tt));
+    if constexpr (kF32) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[hh][e] *= al;
-    }
+      for (int m = 0; m < 8; ++m) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tok = 32 * w + 2 * i + prow;
-      float v[4];
-      unpack4(vc[i], v);
-      const bool valid = tok < nvalid;
+        for (int tt = 0; tt < TILES; ++tt) {
+          const f32x4_t vt = vt_tile(vr[tt], m, sel_f);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = valid ? v[e] : 0.f;
+          for (int r = 0; r < 4; ++r)
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(vt[r], st[tt][r], acc[m], 0, 0, 0);
+        }
+      }
+    } else {
 #pragma unroll
-      for (int h4 = 0; h4 < GP; h4 += 4) {
-        const float4 pp = *reinterpret_cast<const float4*>(&S.Ps[tok][h4]);
-        const float pv[4] = {pp.x, pp.y, pp.z, pp.w};
+      for (int tp = 0; tp < TILES; tp += 2) {
+        const bf16x8_t pb = pack8_rne(st[tp], st[tp + 1]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (h4 + u < G) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[h4 + u][e] = fmaf(pv[u], v[e], acc[h4 + u][e]);
-          }
+        for (int m = 0; m < 8; ++m) {
+          const f32x4_t va = vt_tile(vr[tp], m, sel_bf);
+          const f32x4_t vb = vt_tile(vr[tp + 1], m, sel_bf);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8_exact(va, vb), pb, acc[m], 0, 0, 0);
         }
       }
     }
-    __syncthreads();
-    if (more) {
-      kc = kn;
+    if (next) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) vc[i] = vn[i];
+      for (int tt = 0; tt < TILES; ++tt) load_row(a.v_pool, row0(c + 1, tt), q4, vr[tt]);
     }
-  }
+  };
+  for (int c = 0; c + 1 < nchunk; ++c) chunk(c, true);
+  if (nchunk > 0) chunk(nchunk - 1, false);
 
-  // Sum the two token rows of each wave, then the four waves.
+  // Merge the four waves: lane (l16, q4) holds O^T[16m + 4q4 + r][head l16].
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+  for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], 32);
-  if (prow == 0) {
+    for (int r = 0; r < 4; ++r) S.o[w][l16][16 * m + 4 * q4 + r] = acc[m][r];
+  if (q4 == 0) {
+    S.m[w][l16] = m_run;
+    S.l[w][l16] = l_run;
+  }
+  __syncthreads();
+  if (tid < 16) {
+    const float M = fmaxf(fmaxf(S.m[0][tid], S.m[1][tid]), fmaxf(S.m[2][tid], S.m[3][tid]));
+    float lsum = 0.f;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S.red_o[w][hh][4 * pcol + e] = acc[hh][e];
+    for (int ww = 0; ww < 4; ++ww) {
+      const float sc = S.m[ww][tid] == -INFINITY ? 0.f : exp2f(S.m[ww][tid] - M);
+      S.m[ww][tid] = sc;  // becomes the wave's weight
+      lsum += S.l[ww][tid] * sc;
+    }
+    S.m_all[tid] = M;
+    S.l_all[tid] = lsum;
   }
   __syncthreads();
 
@@ -401,9 +519,10 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   for (int i = tid; i < G * 128; i += kWgThreads) {
     const int hh = i / 128;
     const int d = i % 128;
-    const float l = S.l_run[hh];
-    const float o = l > 0.f ? ((S.red_o[0][hh][d] + S.red_o[1][hh][d]) +
-                               (S.red_o[2][hh][d] + S.red_o[3][hh][d])) * (a.v_scale / l)
+    const float l = S.l_all[hh];
+    const float o = l > 0.f ? ((S.o[0][hh][d] * S.m[0][hh] + S.o[1][hh][d] * S.m[1][hh]) +
+                               (S.o[2][hh][d] * S.m[2][hh] + S.o[3][hh][d] * S.m[3][hh])) *
+                                  (a.v_scale / l)
                             : 0.f;
     if (nsplit == 1) {
       store_out(qtag, a.out, (hq0 + hh) * 128 + d, o);
@@ -412,7 +531,7 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
     }
   }
   if (tid < G) {
-    const float lse = S.l_run[tid] > 0.f ? (S.m_run[tid] + log2f(S.l_run[tid])) * kLn2 : -INFINITY;
+    const float lse = S.l_all[tid] > 0.f ? (S.m_all[tid] + log2f(S.l_all[tid])) * kLn2 : -INFINITY;
     if (nsplit == 1) {
       if (a.lse_out != nullptr) a.lse_out[hq0 + tid] = lse;
     } else {
@@ -427,7 +546,7 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   const int64_t base0 = (static_cast<int64_t>(t) * a.hkv + g) * a.nsplit_max * G;
   // Split weights exp(lse_c - lse) of every head, once, in LDS (the partial
   // lse values are loaded by many threads at once).
-  float* w_lds = &S.red_o[0][0][0];  // reused: nsplit_max * G <= 4 * G * 128 floats
+  float* w_lds = &S.o[0][0][0];  // reused: nsplit_max * G <= 4 * 16 * 128 floats
   for (int i = tid; i < nsplit * G; i += kWgThreads) w_lds[i] = load_shared_f32(a.part_lse + base0 + i);
   __syncthreads();
   if (tid < G) {

@@ -27,6 +27,9 @@ struct ScoreArgs {
   int32_t* sel;              // [B, Hidx, kmax]
   int32_t* cnt;              // [B, Hidx]
   int32_t* sel_pages;        // [B, Hidx, kmax] physical pages of sel, or nullptr
+  // words zeroed by workgroup 0 (hand-off counters of a later kernel), or nullptr
+  uint32_t* zero_words;
+  int32_t zero_count;
 };
 
 // Decode planner: zeroes the hand-off words and orders the work items.
@@ -101,6 +104,14 @@ struct AttendArgs {
   const int32_t* sel;        // [T, Hidx, kmax]
   const int32_t* cnt;        // [B, Hidx]
   const int32_t* sel_pages;  // [B, Hidx, kmax] pages of sel, or nullptr (table lookup)
+  // Selection inside the kernel (decode): when `scores` is set, every workgroup
+  // selects its (sequence, index head) row itself and sel/cnt/sel_pages are
+  // ignored; split 0 of the first kv head of each index head writes the
+  // selection to sel_out/cnt_out when they are set.
+  const float* scores;       // [B, Hidx, max_blocks] or nullptr
+  int32_t topk, init, local;
+  int32_t* sel_out;          // [B, Hidx, kmax] or nullptr
+  int32_t* cnt_out;          // [B, Hidx] or nullptr
   int32_t kmax;
   int32_t hkv, hidx;
   int32_t bps;               // selected blocks per split

@@ -9,6 +9,8 @@ template <class IT, int DI>
 __global__ __launch_bounds__(kWgThreads) void decode_score_kernel(ScoreArgs a) {
   __shared__ SelectLds sl;
   __shared__ int flag;
+  if (blockIdx.x == 0 && a.zero_words != nullptr)
+    for (int i = threadIdx.x; i < a.zero_count; i += kWgThreads) a.zero_words[i] = 0u;
   const int pair = blockIdx.x / a.chunks_per_pair;
   score_chunk<IT, DI, 4, false>(a, pair, blockIdx.x - pair * a.chunks_per_pair, sl, &flag);
 }

@@ -34,17 +34,14 @@ __device__ __forceinline__ int forced_count(int nb, int init, int local) {
 }
 
 // s: nb scores of one (query, index head) row.  MAXPER >= ceil(nb / 256).
-// Must be called by all 256 threads of the workgroup.
+// Must be called by all 256 threads of the workgroup.  Calls emit(pos, j) for
+// every selected block j, pos being its slot in ascending block order, and
+// returns the selection size.  No barrier after the last emit.
 // COHERENT: the scores were written by other workgroups of this launch (read
-// with device-coherent loads) and the selection is written the same way.
-// `pages`: when not null, the block-table row of the sequence; the physical
-// page of every selected block is then written to sel_pages as well.
-template <int MAXPER, bool COHERENT = false>
-__device__ void select_row(const float* __restrict__ s, int nb, int topk,
-                           int init, int local, int kmax,
-                           int32_t* __restrict__ sel, int32_t* __restrict__ cnt,
-                           SelectLds& L, const int32_t* __restrict__ pages = nullptr,
-                           int32_t* __restrict__ sel_pages = nullptr) {
+// with device-coherent loads).
+template <int MAXPER, bool COHERENT, class Emit>
+__device__ int select_core(const float* __restrict__ s, int nb, int topk, int init, int local,
+                           SelectLds& L, Emit emit) {
   const int tid = threadIdx.x;
   const int per = div_up(nb, kWgThreads);
   const int j0 = tid * per;
@@ -139,19 +136,35 @@ __device__ void select_row(const float* __restrict__ s, int nb, int topk,
     sel_local += f ? 1 : 0;
   }
   int pos = block_incl_scan(sel_local, L.wsum) - sel_local;
-  // COHERENT: the selection is read by other workgroups of this launch.
-  auto put = [&](int32_t* q, int32_t v) {
-    if (COHERENT) store_shared_i32(q, v); else *q = v;
-  };
 #pragma unroll
   for (int i = 0; i < MAXPER; ++i) {
     if (flag[i]) {
-      if (sel_pages != nullptr) put(sel_pages + pos, pages[j0 + i]);
-      put(sel + pos, j0 + i);
+      emit(pos, j0 + i);
       ++pos;
     }
   }
-  const int total = nforced + keff;
+  return nforced + keff;
+}
+
+// select_core writing the selection to sel[0..kmax) (-1 padded) and its size
+// to *cnt, ending with a barrier.
+// COHERENT: scores from, and selection for, other workgroups of this launch.
+// `pages`: when not null, the block-table row of the sequence; the physical
+// page of every selected block is then written to sel_pages as well.
+template <int MAXPER, bool COHERENT = false>
+__device__ void select_row(const float* __restrict__ s, int nb, int topk,
+                           int init, int local, int kmax,
+                           int32_t* __restrict__ sel, int32_t* __restrict__ cnt,
+                           SelectLds& L, const int32_t* __restrict__ pages = nullptr,
+                           int32_t* __restrict__ sel_pages = nullptr) {
+  const int tid = threadIdx.x;
+  auto put = [&](int32_t* q, int32_t v) {
+    if (COHERENT) store_shared_i32(q, v); else *q = v;
+  };
+  const int total = select_core<MAXPER, COHERENT>(s, nb, topk, init, local, L, [&](int pos, int j) {
+    if (sel_pages != nullptr) put(sel_pages + pos, pages[j]);
+    put(sel + pos, j);
+  });
   for (int i = total + tid; i < kmax; i += kWgThreads) {
     put(sel + i, -1);
     if (sel_pages != nullptr) put(sel_pages + i, -1);
