@@ -340,11 +340,20 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   if (self_select) {
     // Every split of the row runs the same selection; each keeps its slots.
     int32_t* so = sel_writer ? a.sel_out + static_cast<int64_t>(sel_row) * a.kmax : nullptr;
-    select_core<32, false>(a.scores + static_cast<int64_t>(sel_row) * a.max_blocks, nb_vis,
-                           a.topk, a.init, a.local, S.sl, [&](int pos, int j) {
-                             if (pos >= bi0 && pos < bi0 + nblk) S.blk_j[pos - bi0] = j;
-                             if (sel_writer) so[pos] = j;
-                           });
+    const float* srow = a.scores + static_cast<int64_t>(sel_row) * a.max_blocks;
+    auto emit = [&](int pos, int j) {
+      if (pos >= bi0 && pos < bi0 + nblk) S.blk_j[pos - bi0] = j;
+      if (sel_writer) so[pos] = j;
+    };
+    // One wave selects rows of up to 1024 blocks; longer rows take the
+    // workgroup radix select.
+    if (nb_vis <= 256) {
+      if (w == 0) select_wave<4>(srow, nb_vis, a.topk, a.init, a.local, emit);
+    } else if (nb_vis <= 1024) {
+      if (w == 0) select_wave<16>(srow, nb_vis, a.topk, a.init, a.local, emit);
+    } else {
+      select_core<32, false>(srow, nb_vis, a.topk, a.init, a.local, S.sl, emit);
+    }
     if (sel_writer) {
       for (int i = count + tid; i < a.kmax; i += kWgThreads) so[i] = -1;
       if (tid == 0) a.cnt_out[sel_row] = count;

@@ -18,6 +18,7 @@
 // lanes.
 #include "msa_device.h"
 #include "msa_internal.h"
+#include "msa_select.h"
 
 namespace msa {
 
@@ -157,12 +158,7 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
 }
 
 // One wavefront per (query token, index head) row, for rows of up to 64 * E
-// blocks.  Keys are order-preserving 32-bit images of the scores (-0 folded
-// onto +0); the k-th largest candidate key T is found bit by bit from the top
-// with ballot counts; candidates above T are taken, and of those equal to T
-// the first ones in block order (ranks by ballot prefix counts), which is the
-// lower-index tie rule.  Output slots come from the same prefix counts, so the
-// list is ascending.
+// blocks (select_wave).
 template <int E>
 __global__ __launch_bounds__(kWgThreads) void select_wave_kernel(SelectArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -181,57 +177,10 @@ __global__ __launch_bounds__(kWgThreads) void select_wave_kernel(SelectArgs a) {
     p = a.seq_lens[lo] - (a.cu_seqlens_q[lo + 1] - a.cu_seqlens_q[lo]) + (t - a.cu_seqlens_q[lo]);
   }
   const int nb = p >= 0 ? min(p / kBlock + 1, a.max_blocks) : 0;
-  const int lo_init = min(a.init, nb);
-  const int hi_local = max(0, nb - a.local);
-  const int na = min(a.init, nb);
-  const int nforced = na + (nb - hi_local) - max(0, na - hi_local);
-  const int ncand = nb - nforced;
-  const int keff = min(a.topk, ncand);
-  const bool take_all = keff == ncand;
-  const float* srow = a.scores + static_cast<int64_t>(row) * a.max_blocks;
-
-  uint32_t key[E];
-  bool cand[E], valid[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = lane + kWave * e;
-    valid[e] = j < nb;
-    cand[e] = valid[e] && j >= lo_init && j < hi_local;
-    key[e] = cand[e] ? score_key(srow[j]) : 0u;
-  }
-  uint32_t T = 0u;
-  int need = 0;
-  if (!take_all) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = T | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) cnt += __popcll(__ballot(cand[e] && key[e] >= c));
-      if (cnt >= keff) T = c;
-    }
-    int above = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) above += __popcll(__ballot(cand[e] && key[e] > T));
-    need = keff - above;
-  }
-  auto below = [&](uint64_t m) {  // set bits of m in lanes below this one
-    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-        static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
-  };
-  int eq_before = 0, pos_before = 0;
   int32_t* sel = a.sel + static_cast<int64_t>(row) * a.kmax;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint64_t eqm = __ballot(!take_all && cand[e] && key[e] == T);
-    const bool is_eq = !take_all && cand[e] && key[e] == T;
-    const int rank = eq_before + below(eqm);
-    const bool pick = valid[e] && (!cand[e] || take_all || key[e] > T || (is_eq && rank < need));
-    const uint64_t pm = __ballot(pick);
-    if (pick) sel[pos_before + below(pm)] = lane + kWave * e;
-    eq_before += __popcll(eqm);
-    pos_before += __popcll(pm);
-  }
-  const int total = nforced + keff;
+  const int total = select_wave<E>(a.scores + static_cast<int64_t>(row) * a.max_blocks, nb,
+                                   a.topk, a.init, a.local,
+                                   [&](int pos, int j) { sel[pos] = j; });
   for (int i = total + lane; i < a.kmax; i += kWave) sel[i] = -1;
   if (lane == 0) a.cnt[row] = total;
 }

@@ -146,6 +146,73 @@ __device__ int select_core(const float* __restrict__ s, int nb, int topk, int in
   return nforced + keff;
 }
 
+// The same selection on one wave (no barrier, no LDS): block j sits in lane
+// j % 64, slot j / 64, with E >= ceil(nb / 64).  T, the key of the k-th best
+// candidate, is found bit by bit from the top with ballot counts; candidates
+// above T are taken, and of those equal to T the first ones in block order
+// (ranks from ballot prefix counts), which is the lower-index tie rule.
+// Output slots come from the same prefix counts, so the list is ascending.
+// Calls emit(pos, j) from the lane owning block j; returns the selection size.
+template <int E, class Emit>
+__device__ int select_wave(const float* __restrict__ s, int nb, int topk, int init, int local,
+                           Emit emit) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int lo_init = min(init, nb);
+  const int hi_local = max(0, nb - local);
+  const int nforced = forced_count(nb, init, local);
+  const int ncand = nb - nforced;
+  const int keff = min(topk, ncand);
+  const bool take_all = keff == ncand;
+
+  uint32_t key[E];
+  bool cand[E], valid[E];
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = s[min(lane + kWave * e, max(nb - 1, 0))];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + kWave * e;
+    valid[e] = j < nb;
+    cand[e] = valid[e] && j >= lo_init && j < hi_local;
+    key[e] = cand[e] ? score_key(v[e]) : 0u;
+  }
+  // Non-candidates carry key 0, and every probe c below is >= 1, so the bit
+  // loop needs no candidate mask.
+  auto count = [](bool x) { return __popcll(__builtin_amdgcn_ballot_w64(x)); };
+  uint32_t T = 0u;
+  int need = 0;
+  if (!take_all) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      int n = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) n += count(key[e] >= c);
+      if (n >= keff) T = c;
+    }
+    int above = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) above += count(cand[e] && key[e] > T);
+    need = keff - above;
+  }
+  auto below = [&](uint64_t m) {  // set bits of m in lanes below this one
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+  };
+  int eq_before = 0, pos_before = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool is_eq = !take_all && cand[e] && key[e] == T;
+    const uint64_t eqm = __builtin_amdgcn_ballot_w64(is_eq);
+    const int rank = eq_before + below(eqm);
+    const bool pick = valid[e] && (!cand[e] || take_all || key[e] > T || (is_eq && rank < need));
+    const uint64_t pm = __builtin_amdgcn_ballot_w64(pick);
+    if (pick) emit(pos_before + below(pm), lane + kWave * e);
+    eq_before += __popcll(eqm);
+    pos_before += __popcll(pm);
+  }
+  return nforced + keff;
+}
+
 // select_core writing the selection to sel[0..kmax) (-1 padded) and its size
 // to *cnt, ending with a barrier.
 // COHERENT: scores from, and selection for, other workgroups of this launch.
