@@ -3,6 +3,7 @@
 // enqueues anything; it never allocates, copies or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -109,6 +110,8 @@ int blocks_per_split(const msa_params_t& p, int32_t num_units) {
 
 // Pages scored by one workgroup in the decode scan.
 constexpr int kPagesPerItem = 16;
+// Prefill list entries pack a token index above an 8-bit selection slot.
+constexpr int kMaxPrefillTokens = 1 << 23;
 // Decode as one persistent kernel (score, select and attention hand off work
 // through device memory) rather than a score kernel followed by an attention
 // kernel that selects inside each workgroup.
@@ -154,17 +157,24 @@ DecodeLayout decode_layout(const msa_params_t& p, int32_t B, int32_t MB) {
 }
 
 // Prefill workspace: scores, selection, split partials and tickets per token.
+// Key-major prefill attention (k2q lists) serves bf16 queries over bf16 or
+// fp8 pools; f32 runs the per-token split-K attention.
+bool prefill_key_major(const msa_params_t& p) {
+  return p.q_dtype == MSA_BF16 && (p.kv_dtype == MSA_BF16 || p.kv_dtype == MSA_FP8_E4M3);
+}
+
 struct PrefillLayout {
-  size_t scores, sel, cnt, part_o, part_lse, tickets, total;
+  size_t scores, sel, cnt, part_o, part_lse, tickets;
+  size_t counts, cursor, tok_off, csr, items, n_items;  // key-major only
+  size_t total;
   int bps, nsplit_max;
+  int tq, max_items;  // key-major only
 };
 
-PrefillLayout prefill_layout(const msa_params_t& p, int32_t T, int32_t MB) {
+PrefillLayout prefill_layout(const msa_params_t& p, int32_t B, int32_t T, int32_t MB) {
   PrefillLayout l{};
   const int kmax = kmax_of(p);
   const int G = group_of(p);
-  l.bps = blocks_per_split(p, T);
-  l.nsplit_max = (kmax + l.bps - 1) / l.bps;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -174,10 +184,28 @@ PrefillLayout prefill_layout(const msa_params_t& p, int32_t T, int32_t MB) {
   l.scores = take(sizeof(float) * size_t(T) * p.num_idx_heads * MB);
   l.sel = take(sizeof(int32_t) * size_t(T) * p.num_idx_heads * kmax);
   l.cnt = take(sizeof(int32_t) * size_t(T) * p.num_idx_heads);
-  const size_t parts = l.nsplit_max > 1 ? size_t(T) * p.num_kv_heads * l.nsplit_max * G : 0;
-  l.part_o = take(sizeof(float) * parts * p.head_dim);
-  l.part_lse = take(sizeof(float) * parts);
-  l.tickets = take(sizeof(uint32_t) * size_t(T) * p.num_kv_heads);
+  if (prefill_key_major(p)) {
+    const size_t lists = size_t(B) * p.num_idx_heads * MB;
+    const size_t entries = size_t(T) * p.num_idx_heads * kmax;
+    l.tq = 128 / G;
+    l.max_items = int(entries / l.tq + std::min(lists, entries));
+    l.counts = take(sizeof(int32_t) * 2 * lists);  // counts, then cursor
+    l.cursor = l.counts + sizeof(int32_t) * lists;
+    l.tok_off = take(sizeof(int32_t) * lists);
+    l.csr = take(sizeof(int32_t) * entries);
+    l.items = take(sizeof(int32_t) * 2 * size_t(l.max_items));
+    l.n_items = take(sizeof(int32_t));
+    const size_t parts = size_t(T) * p.num_kv_heads * kmax * G;
+    l.part_o = take(sizeof(float) * parts * p.head_dim);
+    l.part_lse = take(sizeof(float) * parts);
+  } else {
+    l.bps = blocks_per_split(p, T);
+    l.nsplit_max = (kmax + l.bps - 1) / l.bps;
+    const size_t parts = l.nsplit_max > 1 ? size_t(T) * p.num_kv_heads * l.nsplit_max * G : 0;
+    l.part_o = take(sizeof(float) * parts * p.head_dim);
+    l.part_lse = take(sizeof(float) * parts);
+    l.tickets = take(sizeof(uint32_t) * size_t(T) * p.num_kv_heads);
+  }
   l.total = off;
   return l;
 }
@@ -317,7 +345,11 @@ size_t msa_prefill_workspace_size(const msa_params_t* params, int32_t num_seqs,
     fail(MSA_ERR_INVALID_ARG, "num_q_tokens=%d < 0", num_q_tokens);
     return 0;
   }
-  return prefill_layout(*params, num_q_tokens, max_blocks).total;
+  if (num_q_tokens >= kMaxPrefillTokens) {
+    fail(MSA_ERR_UNSUPPORTED, "num_q_tokens=%d above %d", num_q_tokens, kMaxPrefillTokens - 1);
+    return 0;
+  }
+  return prefill_layout(*params, num_seqs, num_q_tokens, max_blocks).total;
 }
 
 msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
@@ -561,7 +593,10 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
   const msa_params_t& p = *params;
   if (p.idx_dtype != MSA_BF16)
     return fail(MSA_ERR_UNSUPPORTED, "prefill scoring needs bf16 index keys");
-  const PrefillLayout l = prefill_layout(p, num_q_tokens, max_blocks);
+  if (num_q_tokens >= kMaxPrefillTokens)
+    return fail(MSA_ERR_UNSUPPORTED, "num_q_tokens=%d above %d", num_q_tokens,
+                kMaxPrefillTokens - 1);
+  const PrefillLayout l = prefill_layout(p, num_seqs, num_q_tokens, max_blocks);
   if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
   if (num_seqs == 0 || num_q_tokens == 0) return ok();
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -570,7 +605,14 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
   int32_t* cnt = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + l.cnt);
   float* scores = reinterpret_cast<float*>(w + l.scores);
 
-  if (l.nsplit_max > 1) {
+  const bool key_major = prefill_key_major(p);
+  if (key_major) {
+    st = hip_status(msa::launch_fill_u32(reinterpret_cast<uint32_t*>(w + l.counts),
+                                         2 * int64_t(num_seqs) * p.num_idx_heads * max_blocks,
+                                         0u, s),
+                    "list reset launch");
+    if (st != MSA_OK) return st;
+  } else if (l.nsplit_max > 1) {
     st = hip_status(msa::launch_fill_u32(reinterpret_cast<uint32_t*>(w + l.tickets),
                                          int64_t(num_q_tokens) * p.num_kv_heads, 0u, s),
                     "ticket reset launch");
@@ -588,6 +630,44 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
   st = hip_status(launch_selection(sa, s), "prefill select launch");
   if (st != MSA_OK) return st;
   // 3. attention over each token's selection
+  if (key_major) {
+    msa::PrefillAttnArgs ka{};
+    ka.q = q;
+    ka.k_pool = k_pool;
+    ka.v_pool = v_pool;
+    ka.num_pages = num_pages;
+    ka.block_table = block_table;
+    ka.max_blocks = max_blocks;
+    ka.seq_lens = seq_lens;
+    ka.cu_seqlens_q = cu_seqlens_q;
+    ka.num_seqs = num_seqs;
+    ka.num_tokens = num_q_tokens;
+    ka.sel = sel;
+    ka.cnt = cnt;
+    ka.kmax = kmax_of(p);
+    ka.hkv = p.num_kv_heads;
+    ka.hidx = p.num_idx_heads;
+    ka.tq = l.tq;
+    ka.counts = reinterpret_cast<int32_t*>(w + l.counts);
+    ka.cursor = reinterpret_cast<int32_t*>(w + l.cursor);
+    ka.tok_off = reinterpret_cast<int32_t*>(w + l.tok_off);
+    ka.csr = reinterpret_cast<int32_t*>(w + l.csr);
+    ka.items = reinterpret_cast<int2*>(w + l.items);
+    ka.n_items = reinterpret_cast<int32_t*>(w + l.n_items);
+    ka.max_items = l.max_items;
+    const float ks = p.kv_dtype == MSA_FP8_E4M3 ? p.k_scale : 1.f;
+    ka.qk_scale_log2 = softmax_scale_of(p) * ks * 1.4426950408889634f;
+    ka.v_scale = p.kv_dtype == MSA_FP8_E4M3 ? p.v_scale : 1.f;
+    ka.part_o = reinterpret_cast<float*>(w + l.part_o);
+    ka.part_lse = reinterpret_cast<float*>(w + l.part_lse);
+    ka.out = out;
+    ka.lse_out = lse_out;
+    st = hip_status(msa::launch_prefill_k2q(ka, s), "prefill k2q launch");
+    if (st != MSA_OK) return st;
+    st = hip_status(msa::launch_prefill_attend(ka, p.kv_dtype, group_of(p), s),
+                    "prefill attention launch");
+    return st == MSA_OK ? ok() : st;
+  }
   msa::AttendArgs aa{};
   aa.q = q;
   aa.k_pool = k_pool;

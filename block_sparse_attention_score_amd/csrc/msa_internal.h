@@ -125,6 +125,40 @@ struct AttendArgs {
   uint32_t* tickets;         // [B * Hkv], zero on entry
 };
 
+// Key-major prefill attention over the k2q lists (bf16 q; bf16 or fp8 K/V).
+constexpr int kMaxSelect = 160;  // topk + init + local, at most
+struct PrefillAttnArgs {
+  const void* q;             // [T, Hq, D] bf16
+  const void* k_pool;        // [P, Hkv, 128, D]
+  const void* v_pool;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens_q;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  const int32_t* sel;        // [T, Hidx, kmax]
+  const int32_t* cnt;        // [T, Hidx]
+  int32_t kmax;
+  int32_t hkv, hidx;
+  int32_t tq;                // tokens per tile: 128 / G
+  // k2q lists, per (b, index head, block j): counts and cursor zero on entry
+  int32_t* counts;           // [B * Hidx * max_blocks]
+  int32_t* cursor;           // [B * Hidx * max_blocks]
+  int32_t* tok_off;          // [B * Hidx * max_blocks] list offsets
+  int32_t* csr;              // [T * Hidx * kmax] entries token << 8 | slot
+  int2* items;               // [max_items] (b, h, j) list and tile index
+  int32_t* n_items;          // [1]
+  int32_t max_items;         // upper bound of the tile count
+  float qk_scale_log2;       // softmax_scale * k_scale * log2(e)
+  float v_scale;
+  float* part_o;             // [T, Hkv, kmax, G, D] normalised partial outputs
+  float* part_lse;           // [T, Hkv, kmax, G]
+  void* out;                 // [T, Hq, D] bf16
+  float* lse_out;            // [T, Hq] or nullptr
+};
+
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
 hipError_t launch_decode_plan(const PlanArgs& a, hipStream_t s);
 // Resident workgroups of the persistent decode kernel of a call (0: none).
@@ -141,6 +175,9 @@ hipError_t launch_select_wave(const SelectArgs& a, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
 hipError_t launch_decode_attend(const AttendArgs& a, int q_dtype, int kv_dtype,
                                 int group, hipStream_t s);
+hipError_t launch_prefill_k2q(const PrefillAttnArgs& a, hipStream_t s);
+hipError_t launch_prefill_attend(const PrefillAttnArgs& a, int kv_dtype, int group,
+                                 hipStream_t s);
 hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale,
                               hipStream_t s);
 
