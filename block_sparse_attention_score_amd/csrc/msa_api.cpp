@@ -193,10 +193,10 @@ PrefillLayout prefill_layout(const msa_params_t& p, int32_t B, int32_t T, int32_
     l.cursor = l.counts + sizeof(int32_t) * lists;
     l.tok_off = take(sizeof(int32_t) * lists);
     l.csr = take(sizeof(int32_t) * entries);
-    l.items = take(sizeof(int32_t) * 2 * size_t(l.max_items));
+    l.items = take(sizeof(int32_t) * 4 * size_t(l.max_items));
     l.n_items = take(sizeof(int32_t));
     const size_t parts = size_t(T) * p.num_kv_heads * kmax * G;
-    l.part_o = take(sizeof(float) * parts * p.head_dim);
+    l.part_o = take(sizeof(uint16_t) * parts * p.head_dim);  // bf16
     l.part_lse = take(sizeof(float) * parts);
   } else {
     l.bps = blocks_per_split(p, T);
@@ -652,13 +652,13 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
     ka.cursor = reinterpret_cast<int32_t*>(w + l.cursor);
     ka.tok_off = reinterpret_cast<int32_t*>(w + l.tok_off);
     ka.csr = reinterpret_cast<int32_t*>(w + l.csr);
-    ka.items = reinterpret_cast<int2*>(w + l.items);
+    ka.items = reinterpret_cast<int4*>(w + l.items);
     ka.n_items = reinterpret_cast<int32_t*>(w + l.n_items);
     ka.max_items = l.max_items;
     const float ks = p.kv_dtype == MSA_FP8_E4M3 ? p.k_scale : 1.f;
     ka.qk_scale_log2 = softmax_scale_of(p) * ks * 1.4426950408889634f;
     ka.v_scale = p.kv_dtype == MSA_FP8_E4M3 ? p.v_scale : 1.f;
-    ka.part_o = reinterpret_cast<float*>(w + l.part_o);
+    ka.part_o = reinterpret_cast<uint16_t*>(w + l.part_o);
     ka.part_lse = reinterpret_cast<float*>(w + l.part_lse);
     ka.out = out;
     ka.lse_out = lse_out;

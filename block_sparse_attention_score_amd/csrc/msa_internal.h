@@ -148,12 +148,12 @@ struct PrefillAttnArgs {
   int32_t* cursor;           // [B * Hidx * max_blocks]
   int32_t* tok_off;          // [B * Hidx * max_blocks] list offsets
   int32_t* csr;              // [T * Hidx * kmax] entries token << 8 | slot
-  int2* items;               // [max_items] (b, h, j) list and tile index
+  int4* items;               // [max_items] (b, h, j) list, first entry, tokens, 0
   int32_t* n_items;          // [1]
   int32_t max_items;         // upper bound of the tile count
   float qk_scale_log2;       // softmax_scale * k_scale * log2(e)
   float v_scale;
-  float* part_o;             // [T, Hkv, kmax, G, D] normalised partial outputs
+  uint16_t* part_o;          // [T, Hkv, kmax, G, D] normalised partial outputs, bf16
   float* part_lse;           // [T, Hkv, kmax, G]
   void* out;                 // [T, Hq, D] bf16
   float* lse_out;            // [T, Hq] or nullptr

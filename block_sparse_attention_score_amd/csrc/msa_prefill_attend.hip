@@ -12,7 +12,8 @@
 //   2. one workgroup per tile: up to 128 query rows (tokens x GQA heads of one
 //      kv head) against block j, staged once in LDS (K as [key][dim], V as
 //      [dim][key]); S^T = K Q^T and O^T = V^T P^T on bf16 MFMA, causal mask
-//      per row; a normalised partial (o, lse) per (token, kv head, slot);
+//      per row; a normalised partial (o in bf16, lse in f32) per (token, kv
+//      head, slot);
 //   3. per (token, kv head), the log-sum-exp combine of its partials.
 #include "msa_device.h"
 #include "msa_internal.h"
@@ -32,16 +33,6 @@ struct PfLds {
   int slot[kRows];                // its slot in the token's selection
   int pos[kRows];                 // its position in the sequence
 };
-
-// Sequence of query token t (cu_seqlens_q[b] <= t < cu_seqlens_q[b + 1]).
-__device__ __forceinline__ int seq_of(const int32_t* cu, int num_seqs, int t) {
-  int lo = 0, hi = num_seqs;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= t) lo = mid; else hi = mid;
-  }
-  return lo;
-}
 
 __device__ __forceinline__ bf16x8_t lds_b128(const uint16_t* p) {
   bf16x8_t r;
@@ -85,19 +76,33 @@ __device__ __forceinline__ uint32_t pack2_rne(float lo, float hi) {
 
 // ---------------------------------------------------------------- k2q CSR
 
-// One thread per (token, index head) row: count its selected blocks.
+// Workgroup (chunk c, sequence b, index head h): the 256 tokens
+// cu[b] + 256 c + tid count their selected blocks in an LDS histogram of the
+// sequence's max_blocks bins, then add the non-zero bins to the lists' counts
+// (the forced blocks are shared by every token: one global atomic per bin).
 __global__ __launch_bounds__(kWgThreads) void k2q_count_kernel(PrefillAttnArgs a) {
-  const int row = blockIdx.x * kWgThreads + threadIdx.x;
-  if (row >= a.num_tokens * a.hidx) return;
-  const int t = row / a.hidx;
-  const int h = row - t * a.hidx;
-  const int b = seq_of(a.cu_seqlens_q, a.num_seqs, t);
-  const int n = min(max(a.cnt[row], 0), a.kmax);
-  int32_t* c = a.counts + (static_cast<int64_t>(b) * a.hidx + h) * a.max_blocks;
-  for (int s = 0; s < n; ++s) {
-    const int j = a.sel[static_cast<int64_t>(row) * a.kmax + s];
-    if (j >= 0 && j < a.max_blocks) atomicAdd(c + j, 1);
+  extern __shared__ int hist[];
+  const int b = blockIdx.y;
+  const int h = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int cu0 = a.cu_seqlens_q[b];
+  const int n_b = a.cu_seqlens_q[b + 1] - cu0;
+  if (static_cast<int>(blockIdx.x) * kWgThreads >= n_b) return;
+  for (int i = tid; i < a.max_blocks; i += kWgThreads) hist[i] = 0;
+  __syncthreads();
+  const int i_tok = blockIdx.x * kWgThreads + tid;
+  if (i_tok < n_b) {
+    const int row = (cu0 + i_tok) * a.hidx + h;
+    const int n = min(max(a.cnt[row], 0), a.kmax);
+    for (int s = 0; s < n; ++s) {
+      const int j = a.sel[static_cast<int64_t>(row) * a.kmax + s];
+      if (j >= 0 && j < a.max_blocks) atomicAdd(&hist[j], 1);
+    }
   }
+  __syncthreads();
+  int32_t* c = a.counts + (static_cast<int64_t>(b) * a.hidx + h) * a.max_blocks;
+  for (int i = tid; i < a.max_blocks; i += kWgThreads)
+    if (hist[i] > 0) atomicAdd(c + i, hist[i]);
 }
 
 // One workgroup: exclusive scans of the counts (list offsets) and of the
@@ -121,29 +126,45 @@ __global__ __launch_bounds__(1024) void k2q_scan_kernel(PrefillAttnArgs a, int n
     const int nt = (c + a.tq - 1) / a.tq;
     a.tok_off[i] = ec;
     for (int k = 0; k < nt; ++k)
-      if (et + k < a.max_items) a.items[et + k] = make_int2(i, k);
+      if (et + k < a.max_items) a.items[et + k] = make_int4(i, ec + k * a.tq, min(a.tq, c - k * a.tq), 0);
     ec += c;
     et += nt;
   }
   if (tid == 1023) *a.n_items = min(et, a.max_items);
 }
 
-// Same rows as the count: append (token, slot) to the list of every selected
-// block.  The order inside a list is arbitrary; every query row of a tile is
-// computed independently, so results do not depend on it.
+// Same workgroups as the count: append (token, slot) to the list of every
+// selected block.  Each non-zero bin reserves its range of the list with one
+// global atomic; LDS atomics hand out the places inside it.  The order inside
+// a list is arbitrary; every query row of a tile is computed on its own, so
+// results do not depend on it.
 __global__ __launch_bounds__(kWgThreads) void k2q_fill_kernel(PrefillAttnArgs a) {
-  const int row = blockIdx.x * kWgThreads + threadIdx.x;
-  if (row >= a.num_tokens * a.hidx) return;
-  const int t = row / a.hidx;
-  const int h = row - t * a.hidx;
-  const int b = seq_of(a.cu_seqlens_q, a.num_seqs, t);
-  const int n = min(max(a.cnt[row], 0), a.kmax);
+  extern __shared__ int hist[];
+  const int b = blockIdx.y;
+  const int h = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int cu0 = a.cu_seqlens_q[b];
+  const int n_b = a.cu_seqlens_q[b + 1] - cu0;
+  if (static_cast<int>(blockIdx.x) * kWgThreads >= n_b) return;
+  for (int i = tid; i < a.max_blocks; i += kWgThreads) hist[i] = 0;
+  __syncthreads();
+  const int i_tok = blockIdx.x * kWgThreads + tid;
+  const int t = cu0 + i_tok;
+  const int row = t * a.hidx + h;
+  const int n = i_tok < n_b ? min(max(a.cnt[row], 0), a.kmax) : 0;
+  for (int s = 0; s < n; ++s) {
+    const int j = a.sel[static_cast<int64_t>(row) * a.kmax + s];
+    if (j >= 0 && j < a.max_blocks) atomicAdd(&hist[j], 1);
+  }
+  __syncthreads();
   const int64_t bh0 = (static_cast<int64_t>(b) * a.hidx + h) * a.max_blocks;
+  for (int i = tid; i < a.max_blocks; i += kWgThreads)
+    if (hist[i] > 0) hist[i] = a.tok_off[bh0 + i] + atomicAdd(a.cursor + bh0 + i, hist[i]);
+  __syncthreads();
   for (int s = 0; s < n; ++s) {
     const int j = a.sel[static_cast<int64_t>(row) * a.kmax + s];
     if (j < 0 || j >= a.max_blocks) continue;
-    const int at = atomicAdd(a.cursor + bh0 + j, 1);
-    a.csr[a.tok_off[bh0 + j] + at] = (t << 8) | s;
+    a.csr[atomicAdd(&hist[j], 1)] = (t << 8) | s;
   }
 }
 
@@ -163,8 +184,10 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_attend_kernel(PrefillAt
   if (x / 8 >= per) return;
   const int item = (x % 8) * per + x / 8;
   if (item >= total) return;
-  const int2 it = a.items[item];
+  const int4 it = a.items[item];
   const int bhj = it.x;
+  const int c0 = it.y;    // first list entry of the tile
+  const int ntok = it.z;  // tokens in the tile
   const int j = bhj % a.max_blocks;
   const int bh = bhj / a.max_blocks;
   const int h = bh % a.hidx;
@@ -179,8 +202,22 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_attend_kernel(PrefillAt
   const int L = a.seq_lens[b];
   const int cu0 = a.cu_seqlens_q[b];
   const int p0 = L - (a.cu_seqlens_q[b + 1] - cu0) - cu0;  // position of token t: p0 + t
-  const int c0 = a.tok_off[bhj] + it.y * TQ;
-  const int ntok = min(TQ, a.counts[bhj] - it.y * TQ);
+  // Query rows of this wave: 32 w + 16 nt + l16 = token slot * G + head.
+  // Their loads go out first, to overlap with the staging of the block.
+  const int hq_stride = a.hkv * G;
+  bf16x8_t qf[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = 32 * w + 16 * nt + l16;
+    const int ts = r / G;
+    const int hh = r - ts * G;
+    const int t = ts < ntok ? (a.csr[c0 + ts] >> 8) : -1;
+    const int64_t q0 = (static_cast<int64_t>(t) * hq_stride + g * G + hh) * 128 + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qf[nt][ks] = t >= 0 ? load8_cached(static_cast<const BF16*>(nullptr), a.q, q0 + 32 * ks)
+                          : bf16x8_t{};
+  }
   if (tid < TQ) {
     if (tid < ntok) {
       const int e = a.csr[c0 + tid];
@@ -238,23 +275,9 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_attend_kernel(PrefillAt
   }
   __syncthreads();
 
-  // Query rows of this wave: 32 w + 16 nt + l16 = token slot * G + head.
-  const int hq_stride = a.hkv * G;
-  bf16x8_t qf[2][4];
   int rpos[2];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = 32 * w + 16 * nt + l16;
-    const int ts = r / G;
-    const int hh = r - ts * G;
-    const int t = S.tok[ts];
-    rpos[nt] = S.pos[ts];
-    const int64_t q0 = (static_cast<int64_t>(t) * hq_stride + g * G + hh) * 128 + 8 * q4;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qf[nt][ks] = t >= 0 ? load8_bf16(static_cast<const BF16*>(nullptr), a.q, q0 + 32 * ks)
-                          : bf16x8_t{};
-  }
+  for (int nt = 0; nt < 2; ++nt) rpos[nt] = S.pos[(32 * w + 16 * nt + l16) / G];
 
   // S^T tiles: keys 16 mt + 4 q4 + r (rows), query rows 16 nt + l16 (columns).
   f32x4_t st[8][2];
@@ -350,12 +373,12 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_attend_kernel(PrefillAt
     const float inv = l > 0.f ? a.v_scale / l : 0.f;
     const int64_t base =
         ((static_cast<int64_t>(t) * a.hkv + g) * a.kmax + S.slot[ts]) * G + hh;
-    float* po = a.part_o + base * 128 + 4 * q4;
+    uint16_t* po = a.part_o + base * 128 + 4 * q4;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const f32x4v_t v = {o[dt][nt][0] * inv, o[dt][nt][1] * inv, o[dt][nt][2] * inv,
-                          o[dt][nt][3] * inv};
-      *reinterpret_cast<f32x4v_t*>(po + 16 * dt) = v;
+      const u32x2_t v = {pack2_rne(o[dt][nt][0] * inv, o[dt][nt][1] * inv),
+                         pack2_rne(o[dt][nt][2] * inv, o[dt][nt][3] * inv)};
+      *reinterpret_cast<u32x2_t*>(po + 16 * dt) = v;
     }
     if (q4 == 0)
       a.part_lse[base] = l > 0.f ? (mrow[nt] + log2f(l)) * kLn2f : -INFINITY;
@@ -389,34 +412,44 @@ __global__ __launch_bounds__(kWgThreads) void prefill_combine_kernel(PrefillAttn
     if (a.lse_out != nullptr) a.lse_out[out0 + tid] = sum > 0.f ? mx + __logf(sum) : -INFINITY;
   }
   __syncthreads();
-  for (int i = tid; i < G * 128; i += kWgThreads) {
-    const int hh = i / 128;
-    const int d = i - hh * 128;
-    const float* po = a.part_o + (base + hh) * 128 + d;
-    float acc = 0.f;
+  // Thread i: head i / 32, dims 4 (i % 32) .. + 4 (one 8-byte load per slot).
+  for (int i = tid; i < G * 32; i += kWgThreads) {
+    const int hh = i / 32;
+    const int d = 4 * (i - hh * 32);
+    const uint16_t* po = a.part_o + (base + hh) * 128 + d;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < n; s0 += 8) {
       // straight-line batch: slots past the last re-read it with weight 0
-      float v[8];
+      u32x2_t v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        v[u] = po[static_cast<int64_t>(min(s0 + u, n - 1)) * G * 128];
+        v[u] = *reinterpret_cast<const u32x2_t*>(
+            po + static_cast<int64_t>(min(s0 + u, n - 1)) * G * 128);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc = fmaf(s0 + u < n ? wgt[(s0 + u) * G + hh] : 0.f, v[u], acc);
+      for (int u = 0; u < 8; ++u) {
+        const float wv = s0 + u < n ? wgt[(s0 + u) * G + hh] : 0.f;
+        acc[0] = fmaf(wv, __uint_as_float(v[u][0] << 16), acc[0]);
+        acc[1] = fmaf(wv, __uint_as_float(v[u][0] & 0xffff0000u), acc[1]);
+        acc[2] = fmaf(wv, __uint_as_float(v[u][1] << 16), acc[2]);
+        acc[3] = fmaf(wv, __uint_as_float(v[u][1] & 0xffff0000u), acc[3]);
+      }
     }
-    reinterpret_cast<uint16_t*>(a.out)[(out0 + hh) * 128 + d] = f32_to_bf16(acc);
+    const u32x2_t r = {pack2_rne(acc[0], acc[1]), pack2_rne(acc[2], acc[3])};
+    *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.out) + (out0 + hh) * 128 + d) = r;
   }
 }
 
 // -------------------------------------------------------------- launchers
 
 hipError_t launch_prefill_k2q(const PrefillAttnArgs& a, hipStream_t s) {
-  const int rows = a.num_tokens * a.hidx;
-  if (rows == 0) return hipSuccess;
-  const int grid = (rows + kWgThreads - 1) / kWgThreads;
+  if (a.num_tokens == 0 || a.num_seqs == 0) return hipSuccess;
+  // chunks of 256 tokens of the longest possible sequence (all T tokens)
+  const dim3 grid((a.num_tokens + kWgThreads - 1) / kWgThreads, a.num_seqs, a.hidx);
+  const size_t lds = sizeof(int) * static_cast<size_t>(a.max_blocks);
   const int n = a.num_seqs * a.hidx * a.max_blocks;
-  k2q_count_kernel<<<grid, kWgThreads, 0, s>>>(a);
+  k2q_count_kernel<<<grid, kWgThreads, lds, s>>>(a);
   k2q_scan_kernel<<<1, 1024, 0, s>>>(a, n);
-  k2q_fill_kernel<<<grid, kWgThreads, 0, s>>>(a);
+  k2q_fill_kernel<<<grid, kWgThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 
