@@ -112,15 +112,11 @@ int blocks_per_split(const msa_params_t& p, int32_t num_units) {
 constexpr int kPagesPerItem = 16;
 // Prefill list entries pack a token index above an 8-bit selection slot.
 constexpr int kMaxPrefillTokens = 1 << 23;
-// Decode as one persistent kernel (score, select and attention hand off work
-// through device memory) rather than a score kernel followed by an attention
-// kernel that selects inside each workgroup.
-constexpr bool kDecodeFused = false;
 
+// Decode workspace: block scores, split partials and the split tickets.
 struct DecodeLayout {
-  size_t scores, sel, cnt, sel_pages, part_o, part_lse, items, n_items;
-  size_t counter, tk_score, ready, tk_attend, total;  // hand-off words, contiguous, zeroed per call
-  int bps, nsplit_max, chunks_per_pair;
+  size_t scores, part_o, part_lse, tickets, total;
+  int bps, nsplit_max;
 };
 
 DecodeLayout decode_layout(const msa_params_t& p, int32_t B, int32_t MB) {
@@ -136,23 +132,10 @@ DecodeLayout decode_layout(const msa_params_t& p, int32_t B, int32_t MB) {
     return at;
   };
   l.scores = take(sizeof(float) * size_t(B) * p.num_idx_heads * MB);
-  l.sel = take(sizeof(int32_t) * size_t(B) * p.num_idx_heads * kmax);
-  l.cnt = take(sizeof(int32_t) * size_t(B) * p.num_idx_heads);
-  l.sel_pages = take(sizeof(int32_t) * size_t(B) * p.num_idx_heads * kmax);
   l.part_o = take(sizeof(float) * size_t(B) * p.num_kv_heads * l.nsplit_max * G * p.head_dim);
   l.part_lse = take(sizeof(float) * size_t(B) * p.num_kv_heads * l.nsplit_max * G);
-  l.chunks_per_pair = (MB + kPagesPerItem - 1) / kPagesPerItem;
-  l.items = take(sizeof(int32_t) * 2 *
-                 (size_t(B) * p.num_idx_heads * l.chunks_per_pair +
-                  size_t(B) * p.num_kv_heads * l.nsplit_max));
-  l.n_items = take(sizeof(int32_t));
-  // hand-off words: one contiguous run of 32-bit words (no padding between)
-  l.counter = off;
-  l.tk_score = l.counter + sizeof(uint32_t);
-  l.ready = l.tk_score + sizeof(uint32_t) * size_t(B) * p.num_idx_heads;
-  l.tk_attend = l.ready + sizeof(uint32_t) * size_t(B) * p.num_idx_heads;
-  off = l.tk_attend + sizeof(uint32_t) * size_t(B) * p.num_kv_heads;
-  l.total = align_up(off);
+  l.tickets = take(sizeof(uint32_t) * size_t(B) * p.num_kv_heads);
+  l.total = off;
   return l;
 }
 
@@ -278,8 +261,8 @@ msa_status_t hip_status(hipError_t e, const char* what) {
 msa::AttendArgs attend_args(const msa_params_t& p, const void* q, const void* k_pool,
                             const void* v_pool, int64_t num_pages, const int32_t* block_table,
                             int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs,
-                            const int32_t* sel, const int32_t* cnt, const int32_t* sel_pages,
-                            void* out, float* lse_out, void* ws, const DecodeLayout& l) {
+                            const int32_t* sel, const int32_t* cnt, void* out,
+                            float* lse_out, void* ws, const DecodeLayout& l) {
   char* w = static_cast<char*>(ws);
   msa::AttendArgs a{};
   a.q = q;
@@ -294,7 +277,6 @@ msa::AttendArgs attend_args(const msa_params_t& p, const void* q, const void* k_
   a.num_tokens = num_seqs;
   a.sel = sel;
   a.cnt = cnt;
-  a.sel_pages = sel_pages;
   a.kmax = kmax_of(p);
   a.hkv = p.num_kv_heads;
   a.hidx = p.num_idx_heads;
@@ -307,7 +289,7 @@ msa::AttendArgs attend_args(const msa_params_t& p, const void* q, const void* k_
   a.lse_out = lse_out;
   a.part_o = reinterpret_cast<float*>(w + l.part_o);
   a.part_lse = reinterpret_cast<float*>(w + l.part_lse);
-  a.tickets = reinterpret_cast<uint32_t*>(w + l.tk_attend);
+  a.tickets = reinterpret_cast<uint32_t*>(w + l.tickets);
   return a;
 }
 
@@ -436,75 +418,14 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const 
     return fail(MSA_ERR_INVALID_ARG, "sel_blocks_out and sel_count_out go together");
   if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
   const msa_params_t& p = *params;
-  if (int64_t(num_seqs) * p.num_idx_heads > msa::kMaxPairs)
-    return fail(MSA_ERR_UNSUPPORTED, "num_seqs * Hidx = %lld above %d",
-                (long long)num_seqs * p.num_idx_heads, msa::kMaxPairs);
   const DecodeLayout l = decode_layout(p, num_seqs, max_blocks);
   if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
   if (num_seqs == 0) return ok();
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  int32_t* sel = sel_blocks_out ? sel_blocks_out : reinterpret_cast<int32_t*>(w + l.sel);
-  int32_t* cnt = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + l.cnt);
 
-  if (!kDecodeFused) {
-    // 1. scores of every visible block; workgroup 0 also zeroes the split
-    //    tickets of step 2
-    msa::ScoreArgs a{};
-    a.idx_q = idx_q;
-    a.idx_k = idx_k_pool;
-    a.num_pages = num_pages;
-    a.block_table = block_table;
-    a.max_blocks = max_blocks;
-    a.seq_lens = seq_lens;
-    a.num_seqs = num_seqs;
-    a.hidx = p.num_idx_heads;
-    a.pages_per_item = kPagesPerItem;
-    a.chunks_per_pair = (max_blocks + kPagesPerItem - 1) / kPagesPerItem;
-    a.scores = reinterpret_cast<float*>(w + l.scores);
-    a.fill_tail = 0;
-    a.zero_words = reinterpret_cast<uint32_t*>(w + l.tk_attend);
-    a.zero_count = num_seqs * p.num_kv_heads;
-    st = hip_status(msa::launch_decode_score(a, p.idx_dtype, p.idx_dim, s), "score launch");
-    if (st != MSA_OK) return st;
-    // 2. selection inside each attention workgroup, split-K attention, combine
-    msa::AttendArgs aa = attend_args(p, q, k_pool, v_pool, num_pages, block_table, max_blocks,
-                                     seq_lens, num_seqs, nullptr, nullptr, nullptr, out,
-                                     lse_out, ws, l);
-    aa.scores = a.scores;
-    aa.topk = p.topk;
-    aa.init = p.init_blocks;
-    aa.local = p.local_blocks;
-    aa.sel_out = sel_blocks_out;
-    aa.cnt_out = sel_count_out;
-    st = hip_status(msa::launch_decode_attend(aa, p.q_dtype, p.kv_dtype, group_of(p), s),
-                    "attention launch");
-    return st == MSA_OK ? ok() : st;
-  }
-
-  const int grid = msa::decode_fused_grid(p.idx_dtype, p.idx_dim, p.q_dtype, p.kv_dtype,
-                                          group_of(p));
-  if (grid <= 0) return fail(MSA_ERR_UNSUPPORTED, "no decode kernel for this parameter set");
-
-  // 1. planner: zero the hand-off words, order the work items
-  msa::PlanArgs pa{};
-  pa.seq_lens = seq_lens;
-  pa.num_seqs = num_seqs;
-  pa.hidx = p.num_idx_heads;
-  pa.kv_per_idx = p.num_kv_heads / p.num_idx_heads;
-  pa.max_blocks = max_blocks;
-  pa.pages_per_item = kPagesPerItem;
-  pa.nsplit_max = l.nsplit_max;
-  pa.lag = 2 * grid;
-  pa.zero_begin = reinterpret_cast<uint32_t*>(w + l.counter);
-  pa.zero_count = int64_t(l.tk_attend - l.counter) / int64_t(sizeof(uint32_t)) +
-                  int64_t(num_seqs) * p.num_kv_heads;
-  pa.items = reinterpret_cast<int2*>(w + l.items);
-  pa.n_items = reinterpret_cast<int32_t*>(w + l.n_items);
-  st = hip_status(msa::launch_decode_plan(pa, s), "decode plan launch");
-  if (st != MSA_OK) return st;
-
-  // 2. persistent score -> select -> attend -> combine
+  // 1. scores of every visible block; workgroup 0 also zeroes the split
+  //    tickets of step 2
   msa::ScoreArgs a{};
   a.idx_q = idx_q;
   a.idx_k = idx_k_pool;
@@ -518,26 +439,21 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const 
   a.chunks_per_pair = (max_blocks + kPagesPerItem - 1) / kPagesPerItem;
   a.scores = reinterpret_cast<float*>(w + l.scores);
   a.fill_tail = 0;
-  a.tickets = reinterpret_cast<uint32_t*>(w + l.tk_score);
-  a.ready = reinterpret_cast<uint32_t*>(w + l.ready);
-  a.topk = p.topk;
-  a.init = p.init_blocks;
-  a.local = p.local_blocks;
-  a.kmax = kmax_of(p);
-  a.sel = sel;
-  a.cnt = cnt;
-  a.sel_pages = reinterpret_cast<int32_t*>(w + l.sel_pages);
-  const msa::AttendArgs aa = attend_args(p, q, k_pool, v_pool, num_pages, block_table,
-                                         max_blocks, seq_lens, num_seqs, sel, cnt, a.sel_pages,
-                                         out, lse_out, ws, l);
-  msa::FusedArgs fa{};
-  fa.counter = reinterpret_cast<uint32_t*>(w + l.counter);
-  fa.items = reinterpret_cast<const int2*>(w + l.items);
-  fa.n_items = reinterpret_cast<const int32_t*>(w + l.n_items);
-  fa.nsplit_max = l.nsplit_max;
-  st = hip_status(msa::launch_decode_fused(a, aa, fa, p.idx_dtype, p.idx_dim, p.q_dtype,
-                                           p.kv_dtype, group_of(p), s),
-                  "decode launch");
+  a.zero_words = reinterpret_cast<uint32_t*>(w + l.tickets);
+  a.zero_count = num_seqs * p.num_kv_heads;
+  st = hip_status(msa::launch_decode_score(a, p.idx_dtype, p.idx_dim, s), "score launch");
+  if (st != MSA_OK) return st;
+  // 2. selection inside each attention workgroup, split-K attention, combine
+  msa::AttendArgs aa = attend_args(p, q, k_pool, v_pool, num_pages, block_table, max_blocks,
+                                   seq_lens, num_seqs, nullptr, nullptr, out, lse_out, ws, l);
+  aa.scores = a.scores;
+  aa.topk = p.topk;
+  aa.init = p.init_blocks;
+  aa.local = p.local_blocks;
+  aa.sel_out = sel_blocks_out;
+  aa.cnt_out = sel_count_out;
+  st = hip_status(msa::launch_decode_attend(aa, p.q_dtype, p.kv_dtype, group_of(p), s),
+                  "attention launch");
   return st == MSA_OK ? ok() : st;
 }
 
@@ -558,13 +474,13 @@ msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q, const 
   if (num_seqs == 0) return ok();
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  st = hip_status(msa::launch_fill_u32(reinterpret_cast<uint32_t*>(w + l.tk_attend),
+  st = hip_status(msa::launch_fill_u32(reinterpret_cast<uint32_t*>(w + l.tickets),
                                        int64_t(params->num_kv_heads) * num_seqs, 0u, s),
                   "ticket reset launch");
   if (st != MSA_OK) return st;
   const msa::AttendArgs aa =
       attend_args(*params, q, k_pool, v_pool, num_pages, block_table, max_blocks, seq_lens,
-                  num_seqs, sel_blocks, sel_count, nullptr, out, lse_out, ws, l);
+                  num_seqs, sel_blocks, sel_count, out, lse_out, ws, l);
   st = hip_status(msa::launch_decode_attend(aa, params->q_dtype, params->kv_dtype,
                                             group_of(*params), s),
                   "decode attend launch");
@@ -681,7 +597,6 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
   aa.num_tokens = num_q_tokens;
   aa.sel = sel;
   aa.cnt = cnt;
-  aa.sel_pages = nullptr;
   aa.kmax = kmax_of(p);
   aa.hkv = p.num_kv_heads;
   aa.hidx = p.num_idx_heads;

@@ -280,16 +280,14 @@ __device__ __forceinline__ void query_of(const AttendArgs& a, int t, int& b, int
 }
 
 // One split (blocks split*bps ..) of the (query token t, kv head g) unit.
-// Called by all 256 threads of a workgroup.  FUSED: the selection was produced
-// by other workgroups of the same launch (coherent loads, after the pair's
-// ready flag).
-template <class QT, class KT, int G, bool FUSED>
+// Called by all 256 threads of a workgroup.
+template <class QT, class KT, int G>
 __device__ void attend_split(const AttendArgs& a, int split, int g, int t, AttendLds<G>& S) {
   const int h = g / (a.hkv / a.hidx);
   const int sel_row = t * a.hidx + h;
   int b, p;
   query_of(a, t, b, p);
-  const bool self_select = !FUSED && a.scores != nullptr;
+  const bool self_select = a.scores != nullptr;
   // Blocks visible to the query, and the selection size that follows from
   // them alone (init and local blocks plus min(topk, rest)).
   const int nb_vis = p >= 0 ? min(p / kBlock + 1, a.max_blocks) : 0;
@@ -298,7 +296,7 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
     const int nf = forced_count(nb_vis, a.init, a.local);
     count = nf + min(a.topk, nb_vis - nf);
   } else {
-    const int cnt_raw = FUSED ? load_shared_i32(a.cnt + sel_row) : a.cnt[sel_row];
+    const int cnt_raw = a.cnt[sel_row];
     count = p >= 0 ? min(max(cnt_raw, 0), a.kmax) : 0;
   }
   const int nsplit = div_up(count, a.bps);
@@ -352,7 +350,7 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
     } else if (nb_vis <= 1024) {
       if (w == 0) select_wave<16>(srow, nb_vis, a.topk, a.init, a.local, emit);
     } else {
-      select_core<32, false>(srow, nb_vis, a.topk, a.init, a.local, S.sl, emit);
+      select_core<32>(srow, nb_vis, a.topk, a.init, a.local, S.sl, emit);
     }
     if (sel_writer) {
       for (int i = count + tid; i < a.kmax; i += kWgThreads) so[i] = -1;
@@ -362,13 +360,9 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   }
   if (tid < nblk) {
     const int64_t at = static_cast<int64_t>(sel_row) * a.kmax + bi0 + tid;
-    const int j = self_select ? S.blk_j[tid] : FUSED ? load_shared_i32(a.sel + at) : a.sel[at];
-    int page;
-    if (a.sel_pages != nullptr && !self_select)
-      page = FUSED ? load_shared_i32(a.sel_pages + at) : a.sel_pages[at];
-    else
-      page = j >= 0 && j < a.max_blocks ? a.block_table[static_cast<int64_t>(b) * a.max_blocks + j]
-                                        : -1;
+    const int j = self_select ? S.blk_j[tid] : a.sel[at];
+    const int page =
+        j >= 0 && j < a.max_blocks ? a.block_table[static_cast<int64_t>(b) * a.max_blocks + j] : -1;
     const bool ok = page >= 0 && page < a.num_pages && j >= 0;
     S.blk_nvalid[tid] = ok ? max(0, min(kBlock, p + 1 - j * kBlock)) : 0;
     S.blk_page[tid] = ok ? page : 0;

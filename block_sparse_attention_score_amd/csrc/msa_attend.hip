@@ -7,7 +7,7 @@ namespace msa {
 template <class QT, class KT, int G>
 __global__ __launch_bounds__(kWgThreads, 2) void decode_attend_kernel(AttendArgs a) {
   __shared__ AttendLds<G> lds;
-  attend_split<QT, KT, G, false>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+  attend_split<QT, KT, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
 // ------------------------------------------------------------ launcher

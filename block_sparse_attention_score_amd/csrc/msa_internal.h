@@ -6,7 +6,7 @@
 
 namespace msa {
 
-// Decode block scoring, optionally fused with the per-row selection.
+// Decode block scoring.
 struct ScoreArgs {
   const void* idx_q;         // [B, Hidx, Di]
   const void* idx_k;         // [P, Hidx, 128, Di]
@@ -19,44 +19,11 @@ struct ScoreArgs {
   int32_t pages_per_item;    // blocks scored by one workgroup
   int32_t chunks_per_pair;   // ceil(max_blocks / pages_per_item)
   float* scores;             // [B, Hidx, max_blocks]
-  int32_t fill_tail;         // write -inf past each row's last block (unfused)
-  // fused selection (persistent decode kernel only)
-  uint32_t* tickets;         // [B * Hidx], zero on entry
-  uint32_t* ready;           // [B * Hidx], zero on entry; set once a pair is selected
-  int32_t topk, init, local, kmax;
-  int32_t* sel;              // [B, Hidx, kmax]
-  int32_t* cnt;              // [B, Hidx]
-  int32_t* sel_pages;        // [B, Hidx, kmax] physical pages of sel, or nullptr
+  int32_t fill_tail;         // write -inf past each row's last block
   // words zeroed by workgroup 0 (hand-off counters of a later kernel), or nullptr
   uint32_t* zero_words;
   int32_t zero_count;
 };
-
-// Decode planner: zeroes the hand-off words and orders the work items.
-struct PlanArgs {
-  const int32_t* seq_lens;
-  int32_t num_seqs;
-  int32_t hidx;
-  int32_t kv_per_idx;        // Hkv / Hidx
-  int32_t max_blocks;
-  int32_t pages_per_item;
-  int32_t nsplit_max;
-  int32_t lag;               // score items between a pair's last chunk and its attention
-  uint32_t* zero_begin;      // counters, tickets and ready flags
-  int64_t zero_count;
-  int2* items;               // score (pair, chunk) or attention (-1 - unit, split)
-  int32_t* n_items;
-};
-
-// Persistent decode kernel: work items claimed in order from one counter.
-struct FusedArgs {
-  uint32_t* counter;         // zero on entry
-  const int2* items;         // from the planner
-  const int32_t* n_items;
-  int32_t nsplit_max;
-};
-
-constexpr int kMaxPairs = 8192;  // (sequence, index head) pairs per decode call
 
 // Prefill index scoring (causal GEMM with a block-max epilogue).
 struct PrefillScoreArgs {
@@ -103,7 +70,6 @@ struct AttendArgs {
   int32_t num_tokens;        // query tokens (decode: num_seqs)
   const int32_t* sel;        // [T, Hidx, kmax]
   const int32_t* cnt;        // [B, Hidx]
-  const int32_t* sel_pages;  // [B, Hidx, kmax] pages of sel, or nullptr (table lookup)
   // Selection inside the kernel (decode): when `scores` is set, every workgroup
   // selects its (sequence, index head) row itself and sel/cnt/sel_pages are
   // ignored; split 0 of the first kv head of each index head writes the
@@ -160,12 +126,6 @@ struct PrefillAttnArgs {
 };
 
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
-hipError_t launch_decode_plan(const PlanArgs& a, hipStream_t s);
-// Resident workgroups of the persistent decode kernel of a call (0: none).
-int decode_fused_grid(int idx_dtype, int idx_dim, int q_dtype, int kv_dtype, int group);
-hipError_t launch_decode_fused(const ScoreArgs& sa, const AttendArgs& aa, const FusedArgs& fa,
-                               int idx_dtype, int idx_dim, int q_dtype, int kv_dtype, int group,
-                               hipStream_t s);
 hipError_t launch_decode_score(const ScoreArgs& a, int idx_dtype, int idx_dim,
                                hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);

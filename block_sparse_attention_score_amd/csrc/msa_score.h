@@ -1,5 +1,4 @@
-// Decode block scoring (index-head scan) of one chunk of pages, with the
-// per-pair selection fused behind it.
+// Decode block scoring (index-head scan) of one chunk of pages.
 //
 // Scoring (sglang page minimax_sparse_backend.py: the index query idx_q,
 // sparse_index_dim wide, is scored against the index-key cache of every
@@ -15,26 +14,16 @@
 // forms an 8-term partial dot product, the row is summed across its lanes
 // with DPP, tokens past the query are masked by select (never by
 // multiplying, so stale bytes cannot leak), and the wave reduces the block
-// max.  In the fused form the workgroup that finishes a pair last (atomic
-// ticket) selects that pair's blocks and raises the pair's ready flag.
+// max.
 #pragma once
 
 #include "msa_device.h"
 #include "msa_internal.h"
-#include "msa_select.h"
 
 namespace msa {
 
-// Raises a pair's ready flag after every thread's selection stores landed.
-__device__ __forceinline__ void publish_ready(uint32_t* flag) {
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <class IT, int DI, int MAXPER, bool FUSED>
-__device__ void score_chunk(const ScoreArgs& a, int pair, int chunk, SelectLds& sl,
-                            int* lds_flag) {
+template <class IT, int DI>
+__device__ void score_chunk(const ScoreArgs& a, int pair, int chunk) {
   constexpr int LPR = DI / 8;          // lanes per token row
   constexpr int RPL = kWave / LPR;     // token rows per wave load
   constexpr int NLOAD = kBlock / RPL;  // loads per page per lane
@@ -51,19 +40,8 @@ __device__ void score_chunk(const ScoreArgs& a, int pair, int chunk, SelectLds& 
   const int nchunks = div_up(nb, a.pages_per_item);
   float* srow = a.scores + static_cast<int64_t>(pair) * a.max_blocks;
 
-  if (!FUSED && a.fill_tail && chunk == 0)
+  if (a.fill_tail && chunk == 0)
     for (int j = nb + threadIdx.x; j < a.max_blocks; j += kWgThreads) srow[j] = -INFINITY;
-  if (nb == 0) {
-    if (FUSED && chunk == 0) {
-      for (int i = threadIdx.x; i < a.kmax; i += kWgThreads) {
-        store_shared_i32(a.sel + static_cast<int64_t>(pair) * a.kmax + i, -1);
-        if (a.sel_pages) store_shared_i32(a.sel_pages + static_cast<int64_t>(pair) * a.kmax + i, -1);
-      }
-      if (threadIdx.x == 0) store_shared_i32(a.cnt + pair, 0);
-      publish_ready(a.ready + pair);
-    }
-    return;
-  }
   if (chunk >= nchunks) return;
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -105,20 +83,8 @@ __device__ void score_chunk(const ScoreArgs& a, int pair, int chunk, SelectLds& 
       }
       m = wave_max(m);
     }
-    if (lane == 0) {
-      if (FUSED) store_shared_f32(srow + j, m); else srow[j] = m;
-    }
+    if (lane == 0) srow[j] = m;
   }
-
-  if (!FUSED) return;
-  // The last chunk of the pair to finish selects over all of the pair's scores.
-  if (!take_last_ticket(&a.tickets[pair], nchunks, lds_flag)) return;
-  select_row<MAXPER, true>(srow, nb, a.topk, a.init, a.local, a.kmax,
-                           a.sel + static_cast<int64_t>(pair) * a.kmax, a.cnt + pair, sl,
-                           a.block_table + static_cast<int64_t>(b) * a.max_blocks,
-                           a.sel_pages ? a.sel_pages + static_cast<int64_t>(pair) * a.kmax
-                                       : nullptr);
-  publish_ready(a.ready + pair);
 }
 
 }  // namespace msa

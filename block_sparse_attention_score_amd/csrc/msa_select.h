@@ -37,9 +37,7 @@ __device__ __forceinline__ int forced_count(int nb, int init, int local) {
 // Must be called by all 256 threads of the workgroup.  Calls emit(pos, j) for
 // every selected block j, pos being its slot in ascending block order, and
 // returns the selection size.  No barrier after the last emit.
-// COHERENT: the scores were written by other workgroups of this launch (read
-// with device-coherent loads).
-template <int MAXPER, bool COHERENT, class Emit>
+template <int MAXPER, class Emit>
 __device__ int select_core(const float* __restrict__ s, int nb, int topk, int init, int local,
                            SelectLds& L, Emit emit) {
   const int tid = threadIdx.x;
@@ -60,7 +58,7 @@ __device__ int select_core(const float* __restrict__ s, int nb, int topk, int in
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
       const int j = min(j0 + i, nb - 1);
-      v[i] = COHERENT ? load_shared_f32(s + j) : s[j];
+      v[i] = s[j];
     }
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) key[i] = (i < per && j0 + i < nb) ? score_key(v[i]) : 0u;
@@ -215,28 +213,16 @@ __device__ int select_wave(const float* __restrict__ s, int nb, int topk, int in
 
 // select_core writing the selection to sel[0..kmax) (-1 padded) and its size
 // to *cnt, ending with a barrier.
-// COHERENT: scores from, and selection for, other workgroups of this launch.
-// `pages`: when not null, the block-table row of the sequence; the physical
-// page of every selected block is then written to sel_pages as well.
-template <int MAXPER, bool COHERENT = false>
+template <int MAXPER>
 __device__ void select_row(const float* __restrict__ s, int nb, int topk,
                            int init, int local, int kmax,
                            int32_t* __restrict__ sel, int32_t* __restrict__ cnt,
-                           SelectLds& L, const int32_t* __restrict__ pages = nullptr,
-                           int32_t* __restrict__ sel_pages = nullptr) {
+                           SelectLds& L) {
   const int tid = threadIdx.x;
-  auto put = [&](int32_t* q, int32_t v) {
-    if (COHERENT) store_shared_i32(q, v); else *q = v;
-  };
-  const int total = select_core<MAXPER, COHERENT>(s, nb, topk, init, local, L, [&](int pos, int j) {
-    if (sel_pages != nullptr) put(sel_pages + pos, pages[j]);
-    put(sel + pos, j);
-  });
-  for (int i = total + tid; i < kmax; i += kWgThreads) {
-    put(sel + i, -1);
-    if (sel_pages != nullptr) put(sel_pages + i, -1);
-  }
-  if (tid == 0) put(cnt, total);
+  const int total =
+      select_core<MAXPER>(s, nb, topk, init, local, L, [&](int pos, int j) { sel[pos] = j; });
+  for (int i = total + tid; i < kmax; i += kWgThreads) sel[i] = -1;
+  if (tid == 0) *cnt = total;
   __syncthreads();
 }
 

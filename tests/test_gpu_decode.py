@@ -86,7 +86,8 @@ def _compare(inp, g, spec, rows=None):
     gsel, gcnt = parity.to_np(g["sel"]), parity.to_np(g["cnt"])
     nband = parity.check_selection(gsel, gcnt, ora_scores, ora_sel, ora_cnt, pos,
                                    spec["init"], spec["local"], rows=rows)
-    # the standalone select over the standalone scores agrees with the fused one
+    # the standalone select over the standalone scores agrees with the one the
+    # attention workgroups run inside msa_sparse_decode
     assert np.array_equal(parity.to_np(g["sel2"])[rows], gsel[rows])
     assert np.array_equal(parity.to_np(g["cnt2"])[rows], gcnt[rows])
     # oracle attention over the GPU's own selection
@@ -94,7 +95,7 @@ def _compare(inp, g, spec, rows=None):
     go = parity.to_np(g["out"])
     err = parity.check_output(go[rows], ora_out[rows], f32)
     parity.check_lse(parity.to_np(g["lse"])[rows], ora_lse[rows], f32)
-    # step 3 alone reproduces the fused path bit for bit
+    # step 3 alone, over that selection, reproduces msa_sparse_decode bit for bit
     assert torch.equal(g["out3"], g["out"])
     assert torch.equal(g["lse3"], g["lse"])
     return err, nband
@@ -229,10 +230,11 @@ def test_decode_full_size_sampled(msa, name):
     assert torch.isfinite(g["out"].float()).all()
 
 
-def test_fused_handoff_matches_unfused_path(msa):
-    """The fused kernels hand scores and split partials between workgroups through
-    atomic tickets; repeated calls must agree bit for bit with each other and
-    with the unfused composition block_score -> select_blocks -> sparse_attend."""
+def test_decode_repeats_match_composition(msa):
+    """Split partials pass between workgroups through atomic tickets, and every
+    split workgroup re-runs its row's selection; repeated calls must agree bit
+    for bit with each other and with the composition block_score ->
+    select_blocks -> sparse_attend."""
     spec = _spec(8, [131072, 70000, 4096, 33000, 100000, 129, 65536, 9000], Hq=16, Hkv=2,
                  Hidx=2, topk=32, init=1, local=2)
     case = generate(spec, 321, device="cuda")
