@@ -332,7 +332,7 @@ def bench_prefill(args, spec):
     score_tf = f_score / (score_ms * 1e-3) / 1e12
     attn_tf = f_attn / (attn_ms * 1e-3) / 1e12
     dominant = "attention" if attn_ms >= score_ms else "score"
-    roof = {"kernel": "prefill attention (split-K over each token's selection)",
+    roof = {"kernel": "prefill attention stage (k2q lists, key-major MFMA tiles, combine)",
             "bound": "mfma", "achieved": attn_tf, "peak": peak, "unit": "TFLOP/s",
             "frac": attn_tf / peak, "traffic": None, "flops_per_launch": f_attn,
             "ms_per_launch": attn_ms} if dominant == "attention" else \

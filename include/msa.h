@@ -187,7 +187,8 @@ msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q,
  * Steps 1-3 for chunked prefill: num_q_tokens new tokens laid out by
  * cu_seqlens_q [B+1], each attending causally to its sequence's tokens
  * t <= p through its own selection.  Outputs as for decode, per token.
- * ws: msa_prefill_workspace_size() bytes.
+ * Needs bf16 index keys and num_q_tokens < 2^23 (MSA_ERR_UNSUPPORTED
+ * otherwise).  ws: msa_prefill_workspace_size() bytes.
  */
 msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q,
                                 const void* idx_q, const void* k_pool,

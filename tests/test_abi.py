@@ -143,3 +143,20 @@ def test_block_token_conversion_follows_backend_rule():
     assert msa.blocks_from_tokens(128, 256) == (1, 3)
     assert msa.blocks_from_tokens(0, 0) == (0, 1)
     assert msa.blocks_from_tokens(129, 129) == (2, 3)
+
+
+def test_prefill_workspace_and_token_limit():
+    cfg = base_cfg()
+    p = cfg.params()
+    lib = msa.load()
+    # key-major prefill (bf16 q): scores, selection, k2q lists and bf16 partials
+    T, B, MB = 4096, 2, 64
+    need = lib.msa_prefill_workspace_size(ctypes.byref(p), B, T, MB)
+    kmax = cfg.topk + cfg.init_blocks + cfg.local_blocks
+    G = cfg.num_q_heads // cfg.num_kv_heads
+    partials = T * cfg.num_kv_heads * kmax * G * cfg.head_dim * 2
+    assert need >= T * cfg.num_idx_heads * MB * 4 + partials
+    # list entries pack the token index above an 8-bit slot
+    assert lib.msa_prefill_workspace_size(ctypes.byref(p), B, (1 << 23) - 1, MB) > 0
+    assert lib.msa_prefill_workspace_size(ctypes.byref(p), B, 1 << 23, MB) == 0
+    assert "num_q_tokens" in lib.msa_last_error().decode()
