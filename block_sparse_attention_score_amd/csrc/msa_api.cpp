@@ -93,18 +93,17 @@ float softmax_scale_of(const msa_params_t& p) {
   return p.softmax_scale > 0.f ? p.softmax_scale : 1.0f / std::sqrt(float(p.head_dim));
 }
 
-// Selected blocks handled by one split-K workgroup: enough splits that about
-// kAttendWgTarget workgroups cover the batch (two resident per CU on the 256
-// CUs); a multiple of 4, since each of a workgroup's four waves streams its
-// own blocks.
-constexpr int kAttendWgTarget = 512;
+// Selected blocks handled by one split-K workgroup.  The attention kernel is
+// bound by how many blocks the busiest CU streams, so the batch is cut into
+// about one workgroup per CU (256 on MI355X, floor, so that no CU gets two
+// while others idle): a unit (query, kv head) gets 256 / units splits.
+constexpr int kAttendWgTarget = 256;
 constexpr int kMaxBlocksPerSplit = 32;  // the attention kernel's limit
 int blocks_per_split(const msa_params_t& p, int32_t num_units) {
   const int kmax = kmax_of(p);
   const int units = num_units * p.num_kv_heads > 0 ? num_units * p.num_kv_heads : 1;
   const int splits = kAttendWgTarget / units > 1 ? kAttendWgTarget / units : 1;
-  int bps = (kmax + splits - 1) / splits;
-  bps = (bps + 3) / 4 * 4;
+  const int bps = (kmax + splits - 1) / splits;
   return bps > kMaxBlocksPerSplit ? kMaxBlocksPerSplit : bps;
 }
 

@@ -547,6 +547,38 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   if (!take_last_ticket(&a.tickets[static_cast<int64_t>(t) * a.hkv + g], nsplit, &S.is_last))
     return;
   const int64_t base0 = (static_cast<int64_t>(t) * a.hkv + g) * a.nsplit_max * G;
+  if (nsplit <= 8) {
+    // One round trip: every thread loads the lse and the partial of each
+    // split for its (head, dim) and weights them itself.  Slots past the last
+    // split re-read it and get weight 0.
+    for (int i = tid; i < G * 128; i += kWgThreads) {
+      const int hh = i / 128;
+      const int d = i % 128;
+      float ls[8], v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = min(u, nsplit - 1);
+        ls[u] = load_shared_f32(a.part_lse + base0 + c * G + hh);
+        v[u] = load_shared_f32(a.part_o + (base0 + c * G + hh) * 128 + d);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mx = fmaxf(mx, u < nsplit ? ls[u] : -INFINITY);
+      float ws = 0.f, o = 0.f;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float e = u < nsplit ? __expf(ls[u] - mx) : 0.f;
+          ws += e;
+          o = fmaf(e, v[u], o);
+        }
+      }
+      store_out(qtag, a.out, (hq0 + hh) * 128 + d, ws > 0.f ? o / ws : 0.f);
+      if (d == 0 && a.lse_out != nullptr)
+        a.lse_out[hq0 + hh] = ws > 0.f ? mx + __logf(ws) : -INFINITY;
+    }
+    return;
+  }
   // Split weights exp(lse_c - lse) of every head, once, in LDS (the partial
   // lse values are loaded by many threads at once).
   float* w_lds = &S.o[0][0][0];  // reused: nsplit_max * G <= 4 * 16 * 128 floats

@@ -185,7 +185,12 @@ __device__ int select_wave(const float* __restrict__ s, int nb, int topk, int in
       int n = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) n += count(key[e] >= c);
-      if (n >= keff) T = c;
+      if (n == keff) {
+        // exactly the selection: it is {key > c - 1}, with no tie to break
+        T = c - 1;
+        break;
+      }
+      if (n > keff) T = c;
     }
     int above = 0;
 #pragma unroll
