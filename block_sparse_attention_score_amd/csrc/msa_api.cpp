@@ -169,13 +169,13 @@ PrefillLayout prefill_layout(const msa_params_t& p, int32_t B, int32_t T, int32_
   if (prefill_key_major(p)) {
     const size_t lists = size_t(B) * p.num_idx_heads * MB;
     const size_t entries = size_t(T) * p.num_idx_heads * kmax;
-    l.tq = 128 / G;
+    l.tq = msa::kPrefillTileRows / G;
     l.max_items = int(entries / l.tq + std::min(lists, entries));
     l.counts = take(sizeof(int32_t) * 2 * lists);  // counts, then cursor
     l.cursor = l.counts + sizeof(int32_t) * lists;
     l.tok_off = take(sizeof(int32_t) * lists);
     l.csr = take(sizeof(int32_t) * entries);
-    l.items = take(sizeof(int32_t) * 4 * size_t(l.max_items));
+    l.items = take(sizeof(msa::Tile) * size_t(l.max_items));
     l.n_items = take(sizeof(int32_t));
     const size_t parts = size_t(T) * p.num_kv_heads * kmax * G;
     l.part_o = take(sizeof(uint16_t) * parts * p.head_dim);  // bf16
@@ -567,7 +567,7 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
     ka.cursor = reinterpret_cast<int32_t*>(w + l.cursor);
     ka.tok_off = reinterpret_cast<int32_t*>(w + l.tok_off);
     ka.csr = reinterpret_cast<int32_t*>(w + l.csr);
-    ka.items = reinterpret_cast<int4*>(w + l.items);
+    ka.items = reinterpret_cast<msa::Tile*>(w + l.items);
     ka.n_items = reinterpret_cast<int32_t*>(w + l.n_items);
     ka.max_items = l.max_items;
     const float ks = p.kv_dtype == MSA_FP8_E4M3 ? p.k_scale : 1.f;

@@ -91,8 +91,21 @@ struct AttendArgs {
   uint32_t* tickets;         // [B * Hkv], zero on entry
 };
 
+// One prefill attention tile: up to kPrefillTileRows query rows of one k2q
+// list against its key block, resolved by the planning kernel.
+struct Tile {
+  int32_t c0;      // first list entry of the tile
+  int32_t ntok;    // tokens in the tile
+  int32_t j;       // key block
+  int32_t nvalid;  // keys of the block before the sequence end (0: no page)
+  int32_t p0;      // position of token t is p0 + t
+  int32_t g0;      // first kv head of the list's index head
+  int64_t head0;   // element offset of (page, kv head g0) in the K/V pools
+};
+
 // Key-major prefill attention over the k2q lists (bf16 q; bf16 or fp8 K/V).
-constexpr int kMaxSelect = 160;  // topk + init + local, at most
+constexpr int kMaxSelect = 160;        // topk + init + local, at most
+constexpr int kPrefillTileRows = 256;  // query rows (token x GQA head) per tile
 struct PrefillAttnArgs {
   const void* q;             // [T, Hq, D] bf16
   const void* k_pool;        // [P, Hkv, 128, D]
@@ -114,7 +127,7 @@ struct PrefillAttnArgs {
   int32_t* cursor;           // [B * Hidx * max_blocks]
   int32_t* tok_off;          // [B * Hidx * max_blocks] list offsets
   int32_t* csr;              // [T * Hidx * kmax] entries token << 8 | slot
-  int4* items;               // [max_items] (b, h, j) list, first entry, tokens, 0
+  struct Tile* items;        // [max_items] resolved work tiles
   int32_t* n_items;          // [1]
   int32_t max_items;         // upper bound of the tile count
   float qk_scale_log2;       // softmax_scale * k_scale * log2(e)

@@ -9,8 +9,8 @@
 // same on gfx950:
 //   1. k2q CSR: count the selecting tokens of every (b, index head, j), scan
 //      the counts into list offsets and 128-row work tiles, fill the lists;
-//   2. one workgroup per tile: up to 128 query rows (tokens x GQA heads of one
-//      kv head) against block j, staged once in LDS (K as [key][dim], V as
+//   2. per tile: up to 256 query rows (tokens x GQA heads of one kv head)
+//      against block j, staged once in LDS (K as [key][dim], V as
 //      [dim][key]); S^T = K Q^T and O^T = V^T P^T on bf16 MFMA, causal mask
 //      per row; a normalised partial (o in bf16, lse in f32) per (token, kv
 //      head, slot);
@@ -22,16 +22,24 @@ namespace msa {
 
 namespace {
 
-constexpr int kRows = 128;       // query rows (token x head) per tile
+constexpr int kPfWaves = 8;                 // waves of a tile workgroup
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kRows = kPrefillTileRows;     // query rows (token x head) per tile
+static_assert(kRows == 32 * kPfWaves, "each wave owns 32 query rows");
 constexpr int kStride = 136;     // LDS row stride in bf16 elements (128 + 8)
 constexpr float kLn2f = 0.69314718055994531f;
 
-struct PfLds {
+struct PfStage {
   uint16_t k[kBlock * kStride];   // K   [key][dim]
   uint16_t vt[kBlock * kStride];  // V^T [dim][key]
   int tok[kRows];                 // token of each token slot of the tile (-1: none)
   int slot[kRows];                // its slot in the token's selection
   int pos[kRows];                 // its position in the sequence
+};
+// Two stages: tile i is computed from one while tile i+1 is written to the
+// other.
+struct PfLds {
+  PfStage st[2];
 };
 
 __device__ __forceinline__ bf16x8_t lds_b128(const uint16_t* p) {
@@ -61,6 +69,72 @@ __device__ __forceinline__ bf16x8_t load8_cached(const FP8*, const void* base, i
   __builtin_memcpy(&r, u, 16);
   return r;
 }
+
+// Buffer descriptor of one (page, head) run of a pool: base = pool + byte
+// offset, raw 32-bit words, 64 KB of records (bounds beyond read as 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t run_rsrc(const void* pool, int64_t byte_off) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(reinterpret_cast<const char*>(pool) + byte_off), 0, kBlock * 128 * 4,
+      0x00020000);
+}
+template <class T>
+struct RawOf;
+template <>
+struct RawOf<BF16> {
+  typedef uint16_t elem;
+};
+template <>
+struct RawOf<FP8> {
+  typedef uint8_t elem;
+};
+// Eight elements at byte offset voff + soff of a run, as bf16.
+__device__ __forceinline__ bf16x8_t load8_buf(const BF16*, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ bf16x8_t load8_buf(const FP8*, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
+  const auto raw = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  float x[8];
+  fp8x4_to_f32(raw[0], x);
+  fp8x4_to_f32(raw[1], x + 4);
+  uint32_t u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    u[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xffff0000u);
+  bf16x8_t v;
+  __builtin_memcpy(&v, u, 16);
+  return v;
+}
+
+// load8_cached at element base + h0 + off: the uniform part and the 32-bit
+// lane offset are kept apart.
+__device__ __forceinline__ bf16x8_t load8_at(const BF16*, const void* base, int64_t h0,
+                                             uint32_t off) {
+  const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + h0;
+  bf16x8_t r;
+  __builtin_memcpy(&r, p + off, 16);
+  return r;
+}
+__device__ __forceinline__ bf16x8_t load8_at(const FP8*, const void* base, int64_t h0,
+                                             uint32_t off) {
+  return load8_cached(static_cast<const FP8*>(nullptr),
+                      reinterpret_cast<const uint8_t*>(base) + h0, off);
+}
+
+// Clears v unless keep, without a branch.
+__device__ __forceinline__ void mask_bf16x8(bf16x8_t& v, bool keep) {
+  uint32_t u[4];
+  __builtin_memcpy(u, &v, 16);
+  const uint32_t m = keep ? 0xffffffffu : 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] &= m;
+  __builtin_memcpy(&v, u, 16);
+}
+
+// 2^x on the hardware instruction: 2^-inf = 0, results below 2^-126 flush
+// to zero (probabilities that small do not change a bf16 P or an f32 sum).
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint32_t pack2_rne(float lo, float hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -106,7 +180,8 @@ __global__ __launch_bounds__(kWgThreads) void k2q_count_kernel(PrefillAttnArgs a
 }
 
 // One workgroup: exclusive scans of the counts (list offsets) and of the
-// tiles per list (work-item offsets), then the work items themselves.
+// tiles per list (work-item offsets), then the work tiles themselves, with
+// the page, the sequence bounds and the pool offset already resolved.
 __global__ __launch_bounds__(1024) void k2q_scan_kernel(PrefillAttnArgs a, int n) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x;
@@ -125,8 +200,28 @@ __global__ __launch_bounds__(1024) void k2q_scan_kernel(PrefillAttnArgs a, int n
     const int c = a.counts[i];
     const int nt = (c + a.tq - 1) / a.tq;
     a.tok_off[i] = ec;
-    for (int k = 0; k < nt; ++k)
-      if (et + k < a.max_items) a.items[et + k] = make_int4(i, ec + k * a.tq, min(a.tq, c - k * a.tq), 0);
+    if (nt > 0) {
+      Tile m;
+      m.j = i % a.max_blocks;
+      const int bh = i / a.max_blocks;
+      const int h = bh % a.hidx;
+      const int b = bh / a.hidx;
+      m.g0 = h * (a.hkv / a.hidx);
+      const int L = a.seq_lens[b];
+      const int cu0 = a.cu_seqlens_q[b];
+      m.p0 = L - (a.cu_seqlens_q[b + 1] - cu0) - cu0;
+      const int page = a.block_table[static_cast<int64_t>(b) * a.max_blocks + m.j];
+      const bool page_ok = page >= 0 && page < a.num_pages;
+      // keys at or past the sequence end hold stale bytes: staged as zeros
+      m.nvalid = page_ok ? max(0, min(kBlock, L - m.j * kBlock)) : 0;
+      m.head0 = (static_cast<int64_t>(page_ok ? page : 0) * a.hkv + m.g0) * kBlock * 128;
+      for (int k = 0; k < nt; ++k) {
+        if (et + k >= a.max_items) break;
+        m.c0 = ec + k * a.tq;
+        m.ntok = min(a.tq, c - k * a.tq);
+        a.items[et + k] = m;
+      }
+    }
     ec += c;
     et += nt;
   }
@@ -170,218 +265,319 @@ __global__ __launch_bounds__(kWgThreads) void k2q_fill_kernel(PrefillAttnArgs a)
 
 // ------------------------------------------------------------ attention tile
 
+// Persistent: the workgroups of one XCD (x, x + 8, ...) walk a contiguous
+// range of tiles, so the tiles of a key block run on one XCD and its L2 serves
+// the block to all of them.  Software pipeline over a workgroup's tiles
+// i, i+1, i+2, i+3: while tile i is computed, the key block of tile i+1 and,
+// after S^T, its query rows are in flight; the list entries of tile i+2 and
+// the record of tile i+3 are being fetched.
 template <class KT, int G>
-__global__ __launch_bounds__(kWgThreads, 2) void prefill_attend_kernel(PrefillAttnArgs a) {
+__global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAttnArgs a) {
   __shared__ PfLds S;
   constexpr int TQ = kRows / G;  // tokens per tile
   const KT* ktag = nullptr;
-  // Work item: tiles of one key block are consecutive; spread them so that
-  // each XCD (workgroups x, x + 8, ...) takes a contiguous range and its L2
-  // serves the block to all of them.
+  const BF16* qtag = nullptr;
   const int total = *a.n_items;
   const int per = (total + 7) / 8;
-  const int x = blockIdx.x;
-  if (x / 8 >= per) return;
-  const int item = (x % 8) * per + x / 8;
-  if (item >= total) return;
-  const int4 it = a.items[item];
-  const int bhj = it.x;
-  const int c0 = it.y;    // first list entry of the tile
-  const int ntok = it.z;  // tokens in the tile
-  const int j = bhj % a.max_blocks;
-  const int bh = bhj / a.max_blocks;
-  const int h = bh % a.hidx;
-  const int b = bh / a.hidx;
-  const int g = h * (a.hkv / a.hidx) + blockIdx.y;
+  const int stride = gridDim.x / 8;  // workgroups per XCD (grid is a multiple of 8)
+  const int hi = min((blockIdx.x % 8 + 1) * per, total);
+  int item = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (item >= hi) return;
+  const int kv = blockIdx.y;                         // kv head within the index head's group
+  const int64_t kv_off = static_cast<int64_t>(kv) * kBlock * 128;
+
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
-
-  const int L = a.seq_lens[b];
-  const int cu0 = a.cu_seqlens_q[b];
-  const int p0 = L - (a.cu_seqlens_q[b + 1] - cu0) - cu0;  // position of token t: p0 + t
-  // Query rows of this wave: 32 w + 16 nt + l16 = token slot * G + head.
-  // Their loads go out first, to overlap with the staging of the block.
+  const int kr = tid >> 4;           // staging: K key 32 i + kr, V keys 4 kr .. + 4
+  const int dc = (tid & 15) * 8;     // staging dims dc .. dc + 8
   const int hq_stride = a.hkv * G;
-  bf16x8_t qf[2][4];
+
+  // Query row r = 32 w + 16 nt + l16 of a tile is token slot r / G, head r % G.
+  int qts[2], qhh[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int r = 32 * w + 16 * nt + l16;
-    const int ts = r / G;
-    const int hh = r - ts * G;
-    const int t = ts < ntok ? (a.csr[c0 + ts] >> 8) : -1;
-    const int64_t q0 = (static_cast<int64_t>(t) * hq_stride + g * G + hh) * 128 + 8 * q4;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qf[nt][ks] = t >= 0 ? load8_cached(static_cast<const BF16*>(nullptr), a.q, q0 + 32 * ks)
-                          : bf16x8_t{};
-  }
-  if (tid < TQ) {
-    if (tid < ntok) {
-      const int e = a.csr[c0 + tid];
-      S.tok[tid] = e >> 8;
-      S.slot[tid] = e & 255;
-      S.pos[tid] = p0 + (e >> 8);
-    } else {
-      S.tok[tid] = -1;
-      S.slot[tid] = 0;
-      S.pos[tid] = -1;
-    }
-  }
-  const int page = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
-  const bool page_ok = page >= 0 && page < a.num_pages;
-  // keys at or past the sequence end hold stale bytes: staged as zeros
-  const int nvalid = page_ok ? max(0, min(kBlock, L - j * kBlock)) : 0;
-  const int64_t head0 = (static_cast<int64_t>(page_ok ? page : 0) * a.hkv + g) * kBlock * 128;
-
-  // K rows: instruction i of thread tid reads key 16 i + tid / 16, dims
-  // 8 (tid % 16) .. + 8 (full 256-byte rows per 16 lanes).
-  {
-    const int kr = tid >> 4;
-    const int dc = (tid & 15) * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = 16 * i + kr;
-      bf16x8_t v = bf16x8_t{};
-      if (key < nvalid) v = load8_cached(ktag, a.k_pool, head0 + key * 128 + dc);
-      __builtin_memcpy(&S.k[key * kStride + dc], &v, 16);
-    }
-  }
-  // V transposed: thread tid reads keys 64 hf + 4 (tid / 16) + kk, dims
-  // 8 (tid % 16) .. + 8, and writes each dim's four consecutive keys at once.
-  {
-    const int kq = tid >> 4;
-    const int dc = (tid & 15) * 8;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      uint16_t v[4][8];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key = 64 * hf + 4 * kq + kk;
-        bf16x8_t x = bf16x8_t{};
-        if (key < nvalid) x = load8_cached(ktag, a.v_pool, head0 + key * 128 + dc);
-        __builtin_memcpy(&v[kk][0], &x, 16);
-      }
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const uint32_t w0 = static_cast<uint32_t>(v[0][d]) | (static_cast<uint32_t>(v[1][d]) << 16);
-        const uint32_t w1 = static_cast<uint32_t>(v[2][d]) | (static_cast<uint32_t>(v[3][d]) << 16);
-        const u32x2_t pr = {w0, w1};
-        __builtin_memcpy(&S.vt[(dc + d) * kStride + 64 * hf + 4 * kq], &pr, 8);
-      }
-    }
-  }
-  __syncthreads();
-
-  int rpos[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) rpos[nt] = S.pos[(32 * w + 16 * nt + l16) / G];
-
-  // S^T tiles: keys 16 mt + 4 q4 + r (rows), query rows 16 nt + l16 (columns).
-  f32x4_t st[8][2];
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    st[mt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    st[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t kf = lds_b128(&S.k[(16 * mt + l16) * kStride + 32 * ks + 8 * q4]);
-      st[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], st[mt][0], 0, 0, 0);
-      st[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], st[mt][1], 0, 0, 0);
-    }
+    qts[nt] = r / G;
+    qhh[nt] = r - qts[nt] * G;
   }
 
-  // Softmax of each query row over the block's visible keys (base 2).
-  const int tok0 = j * kBlock;
-  float mrow[2], lrow[2];
+  bf16x8_t qf[2][4];
+  bf16x8_t kraw[4], vraw[4];
+  // list entry of token slot tid (tid < TQ) and of this lane's two query rows
+  // (t: a copy of the thread index).  Clamped loads, no branch; whether an
+  // entry exists (slot < ntok) is decided where it is used, so nothing here
+  // waits for the loads.
+  auto load_entries = [&](const Tile& m, int t, int& et, int (&eq)[2]) {
+    const int* lst = a.csr + m.c0;
+    et = lst[min(t, m.ntok - 1)];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    float m = -INFINITY;
+    for (int nt = 0; nt < 2; ++nt)
+      eq[nt] = lst[min((32 * (t / kWave) + 16 * nt + (t & 15)) / G, m.ntok - 1)];
+  };
+  // Every row of the (page, head) run is loaded (a missing page reads page
+  // 0, rows past the sequence end hold stale bytes) and cleared afterwards
+  // by a select, so the loads carry no branch.  Buffer loads: the run's base
+  // in a descriptor, one loop-invariant lane offset and a scalar offset per
+  // load, so the addressing costs no VGPR pairs.
+  constexpr int kEb = sizeof(typename RawOf<KT>::elem);  // bytes per element
+  const uint32_t k_lane = static_cast<uint32_t>(kr * 128 + dc) * kEb;
+  const uint32_t v_lane = static_cast<uint32_t>(4 * kr * 128 + dc) * kEb;
+  auto load_block = [&](const Tile& m) {
+    const int64_t h0 = m.head0 + kv_off;
+    const auto kr_src = run_rsrc(a.k_pool, h0 * kEb);
+    const auto vr_src = run_rsrc(a.v_pool, h0 * kEb);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int i = 0; i < 4; ++i) kraw[i] = load8_buf(ktag, kr_src, k_lane, 32 * i * 128 * kEb);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = 16 * mt + 4 * q4 + r;
-        const bool ok = key < nvalid && tok0 + key <= rpos[nt];
-        const float s = ok ? st[mt][nt][r] * a.qk_scale_log2 : -INFINITY;
-        st[mt][nt][r] = s;
-        m = fmaxf(m, s);
-      }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    float l = 0.f;
+    for (int kk = 0; kk < 4; ++kk) vraw[kk] = load8_buf(ktag, vr_src, v_lane, kk * 128 * kEb);
+  };
+  auto clear_stale = [&](const Tile& m, int krow) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int i = 0; i < 4; ++i) mask_bf16x8(kraw[i], 32 * i + krow < m.nvalid);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float s = st[mt][nt][r];
-        const float e = s == -INFINITY ? 0.f : exp2f(s - m);
-        st[mt][nt][r] = e;
-        l += e;
-      }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    mrow[nt] = m;
-    lrow[nt] = l;
-  }
-
-  // O^T = V^T P^T: dims 16 dt + 4 q4 + r (rows), query rows 16 nt + l16.
-  // k-slots e of a 32-key step kk: keys 32 kk + 4 q4 + e (e < 4) and
-  // 32 kk + 16 + 4 q4 + (e - 4), the keys the S^T tiles 2 kk, 2 kk + 1 hold.
-  f32x4_t o[8][2];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    o[dt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    o[dt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    bf16x8_t pb[2];
+    for (int kk = 0; kk < 4; ++kk) mask_bf16x8(vraw[kk], 4 * krow + kk < m.nvalid);
+  };
+  // (the clamped entries of rows past the tile read a real token; the rows
+  // are cleared before use)
+  auto load_q = [&](const Tile& m, const int (&eq)[2]) {
+    const int gg = m.g0 + kv;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const uint32_t u[4] = {pack2_rne(st[2 * kk][nt][0], st[2 * kk][nt][1]),
-                             pack2_rne(st[2 * kk][nt][2], st[2 * kk][nt][3]),
-                             pack2_rne(st[2 * kk + 1][nt][0], st[2 * kk + 1][nt][1]),
-                             pack2_rne(st[2 * kk + 1][nt][2], st[2 * kk + 1][nt][3])};
-      __builtin_memcpy(&pb[nt], u, 16);
-    }
+      const int t = eq[nt] >> 8;
+      const int64_t q0 =
+          (static_cast<int64_t>(t) * hq_stride + gg * G + qhh[nt]) * 128 + 8 * q4;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint16_t* row = &S.vt[(16 * dt + l16) * kStride + 32 * kk + 4 * q4];
-      u32x2_t lo, hi;
-      __builtin_memcpy(&lo, row, 8);
-      __builtin_memcpy(&hi, row + 16, 8);
-      const u32x4_t cat = {lo[0], lo[1], hi[0], hi[1]};
-      bf16x8_t vf;
-      __builtin_memcpy(&vf, &cat, 16);
-      o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[0], o[dt][0], 0, 0, 0);
-      o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[1], o[dt][1], 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks) qf[nt][ks] = load8_cached(qtag, a.q, q0 + 32 * ks);
     }
-  }
+  };
+  auto clear_q = [&](const Tile& m) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) mask_bf16x8(qf[nt][ks], qts[nt] < m.ntok);
+  };
 
-  // Normalised partial and its log-sum-exp (natural log of the scaled logits).
+  // Writes tile m (block in kraw/vraw, entry et of token slot tid) to stage
+  // buffer B.  The LDS addresses come from a fresh copy of the thread index
+  // each time rather than being kept live across the loop.
+  auto stage = [&](PfStage& B, const Tile& m, int et) {
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    const int krl = tl >> 4;
+    const int dcl = (tl & 15) * 8;
+    clear_stale(m, krl);
+    if (tl < TQ) {
+      const bool ok = tl < m.ntok;
+      B.tok[tl] = ok ? et >> 8 : -1;
+      B.slot[tl] = ok ? et & 255 : 0;
+      B.pos[tl] = ok ? m.p0 + (et >> 8) : -1;
+    }
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = 32 * w + 16 * nt + l16;
-    const int ts = r / G;
-    const int hh = r - ts * G;
-    const int t = S.tok[ts];
-    if (t < 0) continue;
-    const float l = lrow[nt];
-    const float inv = l > 0.f ? a.v_scale / l : 0.f;
-    const int64_t base =
-        ((static_cast<int64_t>(t) * a.hkv + g) * a.kmax + S.slot[ts]) * G + hh;
-    uint16_t* po = a.part_o + base * 128 + 4 * q4;
+    for (int i = 0; i < 4; ++i) __builtin_memcpy(&B.k[(32 * i + krl) * kStride + dcl], &kraw[i], 16);
+    uint16_t v[4][8];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) __builtin_memcpy(&v[kk][0], &vraw[kk], 16);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t w0 = static_cast<uint32_t>(v[0][d]) | (static_cast<uint32_t>(v[1][d]) << 16);
+      const uint32_t w1 = static_cast<uint32_t>(v[2][d]) | (static_cast<uint32_t>(v[3][d]) << 16);
+      const u32x2_t pr = {w0, w1};
+      __builtin_memcpy(&B.vt[(dcl + d) * kStride + 4 * krl], &pr, 8);
+    }
+  };
+
+  // pipeline state: tiles i (m0, staged), i+1 (m1, block in flight),
+  // i+2 (m2, entries in flight).  The records are read-only here.
+  const Tile* __restrict__ tiles = a.items;
+  Tile m0 = tiles[item];
+  bool has1 = item + stride < hi;
+  bool has2 = item + 2 * stride < hi;
+  Tile m1 = tiles[has1 ? item + stride : item];
+  Tile m2 = tiles[has2 ? item + 2 * stride : item];
+  int e0_tok, e0_q[2];
+  load_entries(m0, tid, e0_tok, e0_q);
+  int e1_tok = 0, e1_q[2] = {0, 0};
+  if (has1) load_entries(m1, tid, e1_tok, e1_q);
+  load_q(m0, e0_q);
+  load_block(m0);
+  stage(S.st[0], m0, e0_tok);
+  if (has1) load_block(m1);
+  __syncthreads();
+  int buf = 0;
+
+  while (true) {
+    // ---- tile i+1 into the other stage (its block is in registers); then
+    // the record of tile i+3, the entries and the block of tile i+2 go out
+    if (has1) stage(S.st[buf ^ 1], m1, e1_tok);
+    const bool has3 = item + 3 * stride < hi;
+    const Tile m3 = tiles[has3 ? item + 3 * stride : item];
+    int e2_tok = 0, e2_q[2] = {0, 0};
+    if (has2) {
+      load_entries(m2, tid, e2_tok, e2_q);
+      load_block(m2);
+    }
+    const PfStage& B = S.st[buf];
+
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    // token slots of this lane's rows, from the fresh thread index
+    int qtl[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) qtl[nt] = (32 * (tl / kWave) + 16 * nt + (tl & 15)) / G;
+    int rpos[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) rpos[nt] = B.pos[qtl[nt]];
+    clear_q(m0);
+
+    // ---- the block in two halves of 64 keys, online softmax across them.
+    // S^T tiles: keys 64 kh + 16 mt + 4 q4 + r (rows), query rows 16 nt + l16.
+    // O^T = V^T P^T: dims 16 dt + 4 q4 + r (rows), query rows 16 nt + l16;
+    // k-slots e of the 32-key step kk: keys 32 kk + 4 q4 + e (e < 4) and
+    // 32 kk + 16 + 4 q4 + (e - 4), the keys the S^T tiles 2 kk, 2 kk + 1 hold.
+    const int tok0 = m0.j * kBlock;
+    float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+    f32x4_t o[8][2];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const u32x2_t v = {pack2_rne(o[dt][nt][0] * inv, o[dt][nt][1] * inv),
-                         pack2_rne(o[dt][nt][2] * inv, o[dt][nt][3] * inv)};
-      *reinterpret_cast<u32x2_t*>(po + 16 * dt) = v;
+      o[dt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      o[dt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    if (q4 == 0)
-      a.part_lse[base] = l > 0.f ? (mrow[nt] + log2f(l)) * kLn2f : -INFINITY;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      f32x4_t st[4][2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        st[mt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        st[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8_t kf =
+              lds_b128(&B.k[(64 * kh + 16 * mt + l16) * kStride + 32 * ks + 8 * q4]);
+          st[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], st[mt][0], 0, 0, 0);
+          st[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], st[mt][1], 0, 0, 0);
+        }
+      }
+      // the query rows of tile i+1, once S^T no longer needs qf
+      if (kh == 1 && has1) load_q(m1, e1_q);
+
+      // Softmax over this half in base 2: p = 2^(s c - m), c = scale * log2(e)
+      // > 0, so the row max of the raw scores gives m.  Masking (keys past the
+      // sequence end or after the row's position) only where the half is not
+      // entirely visible to every row of the wave.
+      const bool full = 64 * kh + 63 < m0.nvalid && tok0 + 64 * kh + 63 <= min(rpos[0], rpos[1]);
+      if (__builtin_amdgcn_ballot_w64(!full) != 0) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = 64 * kh + 16 * mt + 4 * q4 + r;
+              const bool ok = key < m0.nvalid && tok0 + key <= rpos[nt];
+              st[mt][nt][r] = ok ? st[mt][nt][r] : -INFINITY;
+            }
+      }
+      float alpha[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float mr = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mr = fmaxf(mr, st[mt][nt][r]);
+        mr = fmaxf(mr, __shfl_xor(mr, 16));
+        mr = fmaxf(mr, __shfl_xor(mr, 32));
+        const float mn = fmaxf(mrow[nt], mr * a.qk_scale_log2);
+        // a row with nothing visible yet keeps m = -inf; its p are 2^-inf = 0
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        alpha[nt] = exp2_raw(mrow[nt] - mu);
+        float l = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = exp2_raw(fmaf(st[mt][nt][r], a.qk_scale_log2, -mu));
+            st[mt][nt][r] = e;
+            l += e;
+          }
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        mrow[nt] = mn;
+        lrow[nt] = lrow[nt] * alpha[nt] + l;
+      }
+      // P as bf16 B operands
+      bf16x8_t pb[2][2];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const uint32_t u[4] = {pack2_rne(st[2 * k2][nt][0], st[2 * k2][nt][1]),
+                                 pack2_rne(st[2 * k2][nt][2], st[2 * k2][nt][3]),
+                                 pack2_rne(st[2 * k2 + 1][nt][0], st[2 * k2 + 1][nt][1]),
+                                 pack2_rne(st[2 * k2 + 1][nt][2], st[2 * k2 + 1][nt][3])};
+          __builtin_memcpy(&pb[k2][nt], u, 16);
+        }
+      if (kh == 1) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[dt][nt][r] *= alpha[nt];
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int kk = 2 * kh + k2;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const uint16_t* row = &B.vt[(16 * dt + l16) * kStride + 32 * kk + 4 * q4];
+          u32x2_t lo, hi2;
+          __builtin_memcpy(&lo, row, 8);
+          __builtin_memcpy(&hi2, row + 16, 8);
+          const u32x4_t cat = {lo[0], lo[1], hi2[0], hi2[1]};
+          bf16x8_t vf;
+          __builtin_memcpy(&vf, &cat, 16);
+          o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[k2][0], o[dt][0], 0, 0, 0);
+          o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[k2][1], o[dt][1], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- normalised partial and its log-sum-exp (natural log of the scaled logits)
+    const int g = m0.g0 + kv;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int t = B.tok[qtl[nt]];
+      if (t < 0) continue;
+      const float l = lrow[nt];
+      const float inv = l > 0.f ? a.v_scale / l : 0.f;
+      const int64_t base =
+          ((static_cast<int64_t>(t) * a.hkv + g) * a.kmax + B.slot[qtl[nt]]) * G + qhh[nt];
+      uint16_t* po = a.part_o + base * 128 + 4 * q4;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const u32x2_t v = {pack2_rne(o[dt][nt][0] * inv, o[dt][nt][1] * inv),
+                           pack2_rne(o[dt][nt][2] * inv, o[dt][nt][3] * inv)};
+        *reinterpret_cast<u32x2_t*>(po + 16 * dt) = v;
+      }
+      if (q4 == 0) a.part_lse[base] = l > 0.f ? (mrow[nt] + log2f(l)) * kLn2f : -INFINITY;
+    }
+    if (!has1) break;
+    // tile i+1 is staged and every wave is done with tile i's stage
+    __syncthreads();
+    buf ^= 1;
+    item += stride;
+    m0 = m1;
+    m1 = m2;
+    m2 = m3;
+    has1 = has2;
+    has2 = has3;
+    e1_tok = e2_tok;
+    e1_q[0] = e2_q[0];
+    e1_q[1] = e2_q[1];
   }
 }
 
@@ -453,15 +649,18 @@ hipError_t launch_prefill_k2q(const PrefillAttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Resident workgroups: one per CU, a multiple of 8 (one set per XCD).
+constexpr int kPrefillAttendGrid = 256;
+
 template <class KT>
 static bool launch_pf_attend_g(const PrefillAttnArgs& a, int group, hipStream_t s) {
-  const dim3 grid(a.max_items, a.hkv / a.hidx);
+  const dim3 grid(kPrefillAttendGrid, a.hkv / a.hidx);
   switch (group) {
-    case 1: prefill_attend_kernel<KT, 1><<<grid, kWgThreads, 0, s>>>(a); return true;
-    case 2: prefill_attend_kernel<KT, 2><<<grid, kWgThreads, 0, s>>>(a); return true;
-    case 4: prefill_attend_kernel<KT, 4><<<grid, kWgThreads, 0, s>>>(a); return true;
-    case 8: prefill_attend_kernel<KT, 8><<<grid, kWgThreads, 0, s>>>(a); return true;
-    case 16: prefill_attend_kernel<KT, 16><<<grid, kWgThreads, 0, s>>>(a); return true;
+    case 1: prefill_attend_kernel<KT, 1><<<grid, kPfThreads, 0, s>>>(a); return true;
+    case 2: prefill_attend_kernel<KT, 2><<<grid, kPfThreads, 0, s>>>(a); return true;
+    case 4: prefill_attend_kernel<KT, 4><<<grid, kPfThreads, 0, s>>>(a); return true;
+    case 8: prefill_attend_kernel<KT, 8><<<grid, kPfThreads, 0, s>>>(a); return true;
+    case 16: prefill_attend_kernel<KT, 16><<<grid, kPfThreads, 0, s>>>(a); return true;
     default: return false;
   }
 }

@@ -41,6 +41,10 @@ SMALL = {
     "fp8": _spec([260, 100], [4000, 1500], Hq=16, Hkv=2, Hidx=2, kv="fp8", topk=8),
     "f32_qkv": _spec([150, 200], [1000, 2500], Hq=8, Hkv=2, Hidx=2, q="f32", kv="f32", topk=8),
     "topk32_long": _spec([512], [8000], Hq=16, Hkv=2, Hidx=2, topk=32, init=1, local=2),
+    # one q head per kv head: 256-token tiles, lists longer than a tile
+    "g1_long_lists": _spec([700, 300], [300, 0], Hq=2, Hkv=2, Hidx=1, topk=4, init=1,
+                           local=2),
+    "g2": _spec([400], [1200], Hq=4, Hkv=2, Hidx=2, topk=8),
 }
 
 
