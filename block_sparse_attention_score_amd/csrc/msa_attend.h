@@ -241,9 +241,9 @@ __device__ __forceinline__ void store_out(const F32*, void* out, int64_t idx, fl
   reinterpret_cast<float*>(out)[idx] = v;
 }
 
-__device__ __forceinline__ float exp2_or_zero(float x, float m) {
-  return x == -INFINITY ? 0.f : exp2f(x - m);
-}
+// 2^x on the hardware instruction: 2^-inf = 0, results below 2^-126 flush
+// to zero (probabilities that small change neither a bf16 P nor an f32 sum).
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------- split unit
 
@@ -444,13 +444,15 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
     mc = fmaxf(mc, __shfl_xor(mc, 16));
     mc = fmaxf(mc, __shfl_xor(mc, 32));
     const float mn = fmaxf(m_run, mc);
-    const float alpha = m_run == mn ? 1.f : exp2f(m_run - mn);
+    // a column with nothing visible yet keeps m = -inf; its p are 2^-inf = 0
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    const float alpha = exp2_raw(m_run - mu);
     float ls = 0.f;
 #pragma unroll
     for (int tt = 0; tt < TILES; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        st[tt][r] = exp2_or_zero(st[tt][r], mn);
+        st[tt][r] = exp2_raw(st[tt][r] - mu);
         ls += st[tt][r];
       }
     ls += __shfl_xor(ls, 16);
