@@ -193,7 +193,7 @@ PrefillLayout prefill_layout(const msa_params_t& p, int32_t B, int32_t T, int32_
 }
 
 // Blocks of keys per prefill scoring workgroup.
-constexpr int kPrefillBlocksPerChunk = 32;
+constexpr int kPrefillBlocksPerChunk = 16;
 
 msa::PrefillScoreArgs prefill_score_args(const msa_params_t& p, const void* idx_q,
                                          const void* idx_k_pool, int64_t num_pages,

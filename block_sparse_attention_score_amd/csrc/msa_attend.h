@@ -369,13 +369,14 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   }
   __syncthreads();
 
-  // Wave w streams blocks w, w+4, ... of the split in chunks of TILES 16-token
-  // tiles, with its own online softmax; no barrier until the final merge.
+  // The split's blocks are cut into chunks of TILES 16-token tiles, and wave w
+  // streams chunks w, w+4, ... (so a split whose block count is not a multiple
+  // of 4 still spreads evenly), with its own online softmax; no barrier until
+  // the final merge.
   constexpr bool kF32 = __is_same(KT, F32);
   constexpr int TILES = kF32 ? 2 : 4;           // tiles per chunk
   constexpr int CPB = 8 / TILES;                // chunks per 128-token block
-  const int my_blocks = nblk > w ? (nblk - w + 3) / 4 : 0;
-  const int nchunk = my_blocks * CPB;
+  const int nchunk = nblk * CPB > w ? (nblk * CPB - w + 3) / 4 : 0;
 
   // 0/1 selectors for the V transpose.
   bf16x8_t sel_bf[2];
@@ -393,15 +394,16 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
     for (int e = 0; e < 4; ++e) sel_f[e] = (4 * q4 + e == l16) ? 1.f : 0.f;
   }
 
-  auto chunk_block = [&](int c) { return w + 4 * (c / CPB); };
+  auto chunk_block = [&](int c) { return (w + 4 * c) / CPB; };
+  auto chunk_tok0 = [&](int c) { return ((w + 4 * c) % CPB) * TILES * 16; };
   auto row0 = [&](int c, int tt) {
     const int blk = chunk_block(c);
-    const int tok = (c % CPB) * TILES * 16 + 16 * tt + l16;
+    const int tok = chunk_tok0(c) + 16 * tt + l16;
     return (static_cast<int64_t>(S.blk_page[blk]) * a.hkv + g) * kBlock * 128 +
            static_cast<int64_t>(tok) * 128;
   };
   auto tok_valid = [&](int c, int tt) {
-    return (c % CPB) * TILES * 16 + 16 * tt + l16 < S.blk_nvalid[chunk_block(c)];
+    return chunk_tok0(c) + 16 * tt + l16 < S.blk_nvalid[chunk_block(c)];
   };
 
   Row<KT> kr[TILES], vr[TILES];
@@ -423,7 +425,7 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   // before S^T and before P V cover only the loads they need.
   auto chunk = [&](int c, bool next) {
     const int nvalid = S.blk_nvalid[chunk_block(c)];
-    const int tok0 = (c % CPB) * TILES * 16;
+    const int tok0 = chunk_tok0(c);
     f32x4_t st[TILES];
 #pragma unroll
     for (int tt = 0; tt < TILES; ++tt) {

@@ -10,12 +10,13 @@
 // Scoring.  For the n_b new tokens of sequence b (positions p_i = L_b - n_b +
 // i) and index head h, score[i][j] = max over tokens t <= p_i of block j of
 // q_idx[i] . k_idx[t].  A workgroup takes 256 query rows (4 waves x 64) and a
-// run of key blocks; the query rows stay in registers as MFMA A operands; each
+// run of key blocks; the query rows stay in registers as MFMA B operands; each
 // key block (128 tokens x Di) is staged once in LDS (double-buffered, rows
-// padded against bank conflicts) and read by all four waves as B operands of
-// v_mfma_f32_16x16x32_bf16; each 16x16 result tile is masked causally and
-// folded into per-row maxima, which DPP reduces across the tile's 16 token
-// lanes.
+// padded against bank conflicts) and read by all four waves as A operands of
+// v_mfma_f32_16x16x32_bf16, so each result tile is S^T (tokens down, queries
+// across) and a lane folds its four tokens per tile into its query's maximum
+// with no cross-lane step until the block ends.  Blocks that end before a
+// wave's first query skip the causal mask.
 #include "msa_device.h"
 #include "msa_internal.h"
 #include "msa_select.h"
@@ -60,28 +61,33 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
 
-  // A operands: this wave's 64 query rows (4 row tiles of 16).
-  bf16x8_t qa[4][KS];
+  // B operands of S^T = K Q^T: this wave's 64 query rows as columns (4 column
+  // tiles of 16); lane holds dims 32s + 8*q4 .. +8 of query row l16 of tile rt.
+  bf16x8_t qb[4][KS];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const int i = i0 + 64 * w + 16 * rt + l16;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (i < nq) {
-        qa[rt][s] = *reinterpret_cast<const bf16x8_t*>(
+        qb[rt][s] = *reinterpret_cast<const bf16x8_t*>(
             reinterpret_cast<const uint16_t*>(a.idx_q) +
             (static_cast<int64_t>(cu0 + i) * a.hidx + h) * DI + 32 * s + 8 * q4);
       } else {
-        qa[rt][s] = bf16x8_t{};
+        qb[rt][s] = bf16x8_t{};
       }
     }
   }
+  // Position of this wave's first query row: a block ending at or before it
+  // is visible to all 64 rows and needs no causal mask.
+  const int pos_w0 = prefix + i0 + 64 * __builtin_amdgcn_readfirstlane(w);
 
   // Cooperative copy of one key block: thread chunk c = tid + 256 * k covers
   // row c / CHUNKS, bytes 16 * (c % CHUNKS).
+  auto page_of = [&](int j) { return a.block_table[static_cast<int64_t>(b) * a.max_blocks + j]; };
   auto block_base = [&](int j) -> const char* {
-    int page = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
-    if (page < 0 || page >= a.num_pages) page = 0;  // never read: rows get masked below
+    int page = page_of(j);
+    if (page < 0 || page >= a.num_pages) page = 0;  // never read: the block scores -inf
     return reinterpret_cast<const char*>(a.idx_k) +
            ((static_cast<int64_t>(page) * a.hidx + h) * kBlock * DI) * 2;
   };
@@ -104,6 +110,21 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
     }
   };
 
+  // 16 tokens x 64 queries of S^T for token tile n: lane holds tokens
+  // 16n + 4*q4 + r of query column 16rt + l16.
+  auto tile = [&](int buf, int n, f32x4_t (&acc)[4]) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(
+          &kbuf[buf][(16 * n + l16) * ROW_BYTES + 2 * (32 * s + 8 * q4)]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[rt][s], acc[rt], 0, 0, 0);
+    }
+  };
+
   fetch(j0);
   store(0);
   __syncthreads();
@@ -111,47 +132,43 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
     const int buf = (j - j0) & 1;
     const bool more = j + 1 < j1;
     if (more) fetch(j + 1);
-    const bool page_ok = [&] {
-      const int pg = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
-      return pg >= 0 && pg < a.num_pages;
-    }();
+    const int pg = page_of(j);
+    const bool page_ok = pg >= 0 && pg < a.num_pages;
 
-    float mx[4][4];
+    float mx[4];  // per query column: max over this lane's tokens
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx[rt][r] = -INFINITY;
+    for (int rt = 0; rt < 4; ++rt) mx[rt] = -INFINITY;
+    if (page_ok && kBlock * j + kBlock - 1 <= pos_w0) {
 #pragma unroll 2
-    for (int n = 0; n < 8; ++n) {
-      f32x4_t acc[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8_t kb = *reinterpret_cast<const bf16x8_t*>(
-            &kbuf[buf][(16 * n + l16) * ROW_BYTES + 2 * (32 * s + 8 * q4)]);
+      for (int n = 0; n < 8; ++n) {
+        f32x4_t acc[4];
+        tile(buf, n, acc);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
-          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][s], kb, acc[rt], 0, 0, 0);
+          mx[rt] = fmaxf(fmaxf(fmaxf(mx[rt], acc[rt][0]), fmaxf(acc[rt][1], acc[rt][2])), acc[rt][3]);
       }
-      const int tok = kBlock * j + 16 * n + l16;
+    } else if (page_ok) {
+#pragma unroll 2
+      for (int n = 0; n < 8; ++n) {
+        f32x4_t acc[4];
+        tile(buf, n, acc);
+        const int tok = kBlock * j + 16 * n + 4 * q4;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < 4; ++rt) {
+          const int pos = pos_w0 + 16 * rt + l16;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int pos = prefix + i0 + 64 * w + 16 * rt + 4 * q4 + r;
-          mx[rt][r] = fmaxf(mx[rt][r], (tok <= pos && page_ok) ? acc[rt][r] : -INFINITY);
+          for (int r = 0; r < 4; ++r) mx[rt] = fmaxf(mx[rt], tok + r <= pos ? acc[rt][r] : -INFINITY);
         }
+      }
     }
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float m = group_max<16>(mx[rt][r]);
-        const int i = i0 + 64 * w + 16 * rt + 4 * q4 + r;
-        if (l16 == 0 && i < nq)
-          a.scores[(static_cast<int64_t>(cu0 + i) * a.hidx + h) * a.max_blocks + j] = m;
-      }
+    for (int rt = 0; rt < 4; ++rt) {
+      float m = fmaxf(mx[rt], __shfl_xor(mx[rt], 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const int i = i0 + 64 * w + 16 * rt + l16;
+      if (q4 == 0 && i < nq)
+        a.scores[(static_cast<int64_t>(cu0 + i) * a.hidx + h) * a.max_blocks + j] = m;
+    }
     if (more) store(buf ^ 1);
     __syncthreads();
   }
