@@ -147,7 +147,7 @@ bool prefill_key_major(const msa_params_t& p) {
 
 struct PrefillLayout {
   size_t scores, sel, cnt, part_o, part_lse, tickets;
-  size_t counts, cursor, tok_off, csr, items, n_items;  // key-major only
+  size_t counts, cursor, tok_off, csr, items, n_items, sink;  // key-major only
   size_t total;
   int bps, nsplit_max;
   int tq, max_items;  // key-major only
@@ -180,6 +180,7 @@ PrefillLayout prefill_layout(const msa_params_t& p, int32_t B, int32_t T, int32_
     const size_t parts = size_t(T) * p.num_kv_heads * kmax * G;
     l.part_o = take(sizeof(uint16_t) * parts * p.head_dim);  // bf16
     l.part_lse = take(sizeof(float) * parts);
+    l.sink = take(sizeof(uint16_t) * G * p.head_dim + sizeof(float) * G);
   } else {
     l.bps = blocks_per_split(p, T);
     l.nsplit_max = (kmax + l.bps - 1) / l.bps;
@@ -575,6 +576,8 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
     ka.v_scale = p.kv_dtype == MSA_FP8_E4M3 ? p.v_scale : 1.f;
     ka.part_o = reinterpret_cast<uint16_t*>(w + l.part_o);
     ka.part_lse = reinterpret_cast<float*>(w + l.part_lse);
+    ka.sink_o = reinterpret_cast<uint16_t*>(w + l.sink);
+    ka.sink_lse = reinterpret_cast<float*>(w + l.sink + sizeof(uint16_t) * group_of(p) * p.head_dim);
     ka.out = out;
     ka.lse_out = lse_out;
     st = hip_status(msa::launch_prefill_k2q(ka, s), "prefill k2q launch");

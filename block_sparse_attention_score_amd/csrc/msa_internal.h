@@ -134,6 +134,10 @@ struct PrefillAttnArgs {
   float v_scale;
   uint16_t* part_o;          // [T, Hkv, kmax, G, D] normalised partial outputs, bf16
   float* part_lse;           // [T, Hkv, kmax, G]
+  // write-only sink of the rows past a tile's last token (G * D bf16, then
+  // G floats), so that every row stores unconditionally
+  uint16_t* sink_o;
+  float* sink_lse;
   void* out;                 // [T, Hq, D] bf16
   float* lse_out;            // [T, Hq] or nullptr
 };

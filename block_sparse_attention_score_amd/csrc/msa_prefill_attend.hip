@@ -30,8 +30,8 @@ constexpr int kStride = 136;     // LDS row stride in bf16 elements (128 + 8)
 constexpr float kLn2f = 0.69314718055994531f;
 
 struct PfStage {
-  uint16_t k[kBlock * kStride];   // K   [key][dim]
-  uint16_t vt[kBlock * kStride];  // V^T [dim][key]
+  alignas(16) uint16_t k[kBlock * kStride];   // K   [key][dim]
+  alignas(16) uint16_t vt[kBlock * kStride];  // V^T [dim][key]
   int tok[kRows];                 // token of each token slot of the tile (-1: none)
   int slot[kRows];                // its slot in the token's selection
   int pos[kRows];                 // its position in the sequence
@@ -42,10 +42,29 @@ struct PfLds {
   PfStage st[2];
 };
 
+// LDS fragments through 16- and 8-byte vector types (single ds_read_b128 /
+// ds_read_b64; every address below is aligned to the type).
 __device__ __forceinline__ bf16x8_t lds_b128(const uint16_t* p) {
-  bf16x8_t r;
-  __builtin_memcpy(&r, p, 16);
-  return r;
+  return *reinterpret_cast<const bf16x8_t*>(p);
+}
+__device__ __forceinline__ u32x2_t lds_b64(const uint16_t* p) {
+  return *reinterpret_cast<const u32x2_t*>(p);
+}
+
+// Sum and max over the four 16-lane rows (lanes l, l^16, l^32, l^48) with
+// the gfx950 row-swap moves instead of LDS permutes; every lane gets the
+// same result.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
 // Eight consecutive K/V elements as bf16, through the caches (a key block is
@@ -144,6 +163,19 @@ __device__ __forceinline__ uint32_t pack2_rne(float lo, float hi) {
   uint32_t u;
   __builtin_memcpy(&u, &v, 4);
   return u;
+}
+
+typedef const __attribute__((address_space(4))) Tile ConstTile;
+__device__ __forceinline__ Tile read_tile(const ConstTile* p) {
+  Tile m;
+  m.c0 = p->c0;
+  m.ntok = p->ntok;
+  m.j = p->j;
+  m.nvalid = p->nvalid;
+  m.p0 = p->p0;
+  m.g0 = p->g0;
+  m.head0 = p->head0;
+  return m;
 }
 
 }  // namespace
@@ -334,30 +366,30 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) vraw[kk] = load8_buf(ktag, vr_src, v_lane, kk * 128 * kEb);
   };
+  // V rows at or past the sequence end (stale bytes, possibly NaN) are
+  // cleared: their probabilities are 0, but 0 * NaN would reach the MFMA
+  // sums.  Stale K rows need nothing: their scores are replaced by -inf (a
+  // block with such rows always takes the masked softmax path).
   auto clear_stale = [&](const Tile& m, int krow) {
+    if (m.nvalid < kBlock) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mask_bf16x8(kraw[i], 32 * i + krow < m.nvalid);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) mask_bf16x8(vraw[kk], 4 * krow + kk < m.nvalid);
-  };
-  // (the clamped entries of rows past the tile read a real token; the rows
-  // are cleared before use)
-  auto load_q = [&](const Tile& m, const int (&eq)[2]) {
-    const int gg = m.g0 + kv;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int t = eq[nt] >> 8;
-      const int64_t q0 =
-          (static_cast<int64_t>(t) * hq_stride + gg * G + qhh[nt]) * 128 + 8 * q4;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[nt][ks] = load8_cached(qtag, a.q, q0 + 32 * ks);
+      for (int kk = 0; kk < 4; ++kk) mask_bf16x8(vraw[kk], 4 * krow + kk < m.nvalid);
     }
   };
-  auto clear_q = [&](const Tile& m) {
+  // (rows past the tile's last token gather the clamped entry's real, finite
+  // query row; their position -1 masks every key, so they produce zeros,
+  // stored into the sink)
+  auto q_rows = [&](const Tile& m, const int (&eq)[2], int64_t (&qo)[2]) {
+    const int gg = m.g0 + kv;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      qo[nt] = (static_cast<int64_t>(eq[nt] >> 8) * hq_stride + gg * G + qhh[nt]) * 128 + 8 * q4;
+  };
+  auto load_q = [&](const int64_t (&qo)[2]) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) mask_bf16x8(qf[nt][ks], qts[nt] < m.ntok);
+      for (int ks = 0; ks < 4; ++ks) qf[nt][ks] = load8_cached(qtag, a.q, qo[nt] + 32 * ks);
   };
 
   // Writes tile m (block in kraw/vraw, entry et of token slot tid) to stage
@@ -376,7 +408,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
       B.pos[tl] = ok ? m.p0 + (et >> 8) : -1;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_memcpy(&B.k[(32 * i + krl) * kStride + dcl], &kraw[i], 16);
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8_t*>(&B.k[(32 * i + krl) * kStride + dcl]) = kraw[i];
     uint16_t v[4][8];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) __builtin_memcpy(&v[kk][0], &vraw[kk], 16);
@@ -385,40 +417,57 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
       const uint32_t w0 = static_cast<uint32_t>(v[0][d]) | (static_cast<uint32_t>(v[1][d]) << 16);
       const uint32_t w1 = static_cast<uint32_t>(v[2][d]) | (static_cast<uint32_t>(v[3][d]) << 16);
       const u32x2_t pr = {w0, w1};
-      __builtin_memcpy(&B.vt[(dcl + d) * kStride + 4 * krl], &pr, 8);
+      *reinterpret_cast<u32x2_t*>(&B.vt[(dcl + d) * kStride + 4 * krl]) = pr;
     }
   };
 
-  // pipeline state: tiles i (m0, staged), i+1 (m1, block in flight),
-  // i+2 (m2, entries in flight).  The records are read-only here.
-  const Tile* __restrict__ tiles = a.items;
-  Tile m0 = tiles[item];
+  // Pipeline state: tiles i (m0, staged), i+1 (m1: block in flight), i+2
+  // (m2).  One register set each for the block, the list entries and the
+  // query rows, each reloaded right after its last use, so nothing loaded is
+  // copied between registers at the loop edge.  Every load is issued
+  // unconditionally (past the last tile, the clamped record re-reads tile i)
+  // and every iteration issues the same memory operations in the same order;
+  // the prologue issues the same sequence, ending with stores into the sink,
+  // so the waits the compiler derives at the loop head hold on both edges and
+  // never drain the previous tile's partial stores.
+  // (read through the constant address space: the records are not written by
+  // this kernel, and scalar loads keep them off the vector memory counter,
+  // whose in-order waits would otherwise drain the previous tile's stores)
+  const ConstTile* tiles = (const ConstTile*)(reinterpret_cast<uintptr_t>(a.items));
+  Tile m0 = read_tile(tiles + item);
   bool has1 = item + stride < hi;
   bool has2 = item + 2 * stride < hi;
-  Tile m1 = tiles[has1 ? item + stride : item];
-  Tile m2 = tiles[has2 ? item + 2 * stride : item];
-  int e0_tok, e0_q[2];
-  load_entries(m0, tid, e0_tok, e0_q);
-  int e1_tok = 0, e1_q[2] = {0, 0};
-  if (has1) load_entries(m1, tid, e1_tok, e1_q);
-  load_q(m0, e0_q);
+  Tile m1 = read_tile(tiles + (has1 ? item + stride : item));
+  Tile m2 = read_tile(tiles + (has2 ? item + 2 * stride : item));
+  int e_tok, e_q[2];
+  int64_t q_off[2];
+  load_entries(m0, tid, e_tok, e_q);
   load_block(m0);
-  stage(S.st[0], m0, e0_tok);
-  if (has1) load_block(m1);
+  stage(S.st[0], m0, e_tok);
+  q_rows(m0, e_q, q_off);
+  load_entries(m1, tid, e_tok, e_q);
+  load_block(m1);
+  load_q(q_off);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    uint16_t* po = a.sink_o + qhh[nt] * 128 + 4 * q4;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<u32x2_t*>(po + 16 * dt) = u32x2_t{0u, 0u};
+    a.sink_lse[qhh[nt]] = 0.f;
+  }
   __syncthreads();
   int buf = 0;
 
   while (true) {
-    // ---- tile i+1 into the other stage (its block is in registers); then
-    // the record of tile i+3, the entries and the block of tile i+2 go out
-    if (has1) stage(S.st[buf ^ 1], m1, e1_tok);
+    // ---- tile i+1 into the other stage (its block and entries are in
+    // registers); then the record of tile i+3, the entries and the block of
+    // tile i+2 go out
+    if (has1) stage(S.st[buf ^ 1], m1, e_tok);
+    q_rows(m1, e_q, q_off);
     const bool has3 = item + 3 * stride < hi;
-    const Tile m3 = tiles[has3 ? item + 3 * stride : item];
-    int e2_tok = 0, e2_q[2] = {0, 0};
-    if (has2) {
-      load_entries(m2, tid, e2_tok, e2_q);
-      load_block(m2);
-    }
+    const Tile m3 = read_tile(tiles + (has3 ? item + 3 * stride : item));
+    load_entries(m2, tid, e_tok, e_q);
+    load_block(m2);
     const PfStage& B = S.st[buf];
 
     int tl = tid;
@@ -430,7 +479,6 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
     int rpos[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) rpos[nt] = B.pos[qtl[nt]];
-    clear_q(m0);
 
     // ---- the block in two halves of 64 keys, online softmax across them.
     // S^T tiles: keys 64 kh + 16 mt + 4 q4 + r (rows), query rows 16 nt + l16.
@@ -461,7 +509,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
         }
       }
       // the query rows of tile i+1, once S^T no longer needs qf
-      if (kh == 1 && has1) load_q(m1, e1_q);
+      if (kh == 1) load_q(q_off);
 
       // Softmax over this half in base 2: p = 2^(s c - m), c = scale * log2(e)
       // > 0, so the row max of the raw scores gives m.  Masking (keys past the
@@ -488,9 +536,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) mr = fmaxf(mr, st[mt][nt][r]);
-        mr = fmaxf(mr, __shfl_xor(mr, 16));
-        mr = fmaxf(mr, __shfl_xor(mr, 32));
-        const float mn = fmaxf(mrow[nt], mr * a.qk_scale_log2);
+        const float mn = fmaxf(mrow[nt], rows_max(mr) * a.qk_scale_log2);
         // a row with nothing visible yet keeps m = -inf; its p are 2^-inf = 0
         const float mu = mn == -INFINITY ? 0.f : mn;
         alpha[nt] = exp2_raw(mrow[nt] - mu);
@@ -503,8 +549,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
             st[mt][nt][r] = e;
             l += e;
           }
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        l = rows_sum(l);
         mrow[nt] = mn;
         lrow[nt] = lrow[nt] * alpha[nt] + l;
       }
@@ -534,9 +579,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           const uint16_t* row = &B.vt[(16 * dt + l16) * kStride + 32 * kk + 4 * q4];
-          u32x2_t lo, hi2;
-          __builtin_memcpy(&lo, row, 8);
-          __builtin_memcpy(&hi2, row + 16, 8);
+          const u32x2_t lo = lds_b64(row), hi2 = lds_b64(row + 16);
           const u32x4_t cat = {lo[0], lo[1], hi2[0], hi2[1]};
           bf16x8_t vf;
           __builtin_memcpy(&vf, &cat, 16);
@@ -547,23 +590,27 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
     }
 
     // ---- normalised partial and its log-sum-exp (natural log of the scaled logits)
+    // Every row stores (rows past the tile's last token into the sink), so
+    // the number of memory operations per iteration is fixed and later waits
+    // on the prefetches never have to drain these stores.
     const int g = m0.g0 + kv;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int t = B.tok[qtl[nt]];
-      if (t < 0) continue;
       const float l = lrow[nt];
-      const float inv = l > 0.f ? a.v_scale / l : 0.f;
+      const float inv = l > 0.f ? a.v_scale * __builtin_amdgcn_rcpf(l) : 0.f;
       const int64_t base =
-          ((static_cast<int64_t>(t) * a.hkv + g) * a.kmax + B.slot[qtl[nt]]) * G + qhh[nt];
-      uint16_t* po = a.part_o + base * 128 + 4 * q4;
+          ((static_cast<int64_t>(max(t, 0)) * a.hkv + g) * a.kmax + B.slot[qtl[nt]]) * G + qhh[nt];
+      uint16_t* po = (t >= 0 ? a.part_o + base * 128 : a.sink_o + qhh[nt] * 128) + 4 * q4;
+      float* pl = t >= 0 ? a.part_lse + base : a.sink_lse + qhh[nt];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const u32x2_t v = {pack2_rne(o[dt][nt][0] * inv, o[dt][nt][1] * inv),
                            pack2_rne(o[dt][nt][2] * inv, o[dt][nt][3] * inv)};
         *reinterpret_cast<u32x2_t*>(po + 16 * dt) = v;
       }
-      if (q4 == 0) a.part_lse[base] = l > 0.f ? (mrow[nt] + log2f(l)) * kLn2f : -INFINITY;
+      // (the four lanes of the row store the same value)
+      *pl = l > 0.f ? (mrow[nt] + __builtin_amdgcn_logf(l)) * kLn2f : -INFINITY;
     }
     if (!has1) break;
     // tile i+1 is staged and every wave is done with tile i's stage
@@ -575,9 +622,6 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
     m2 = m3;
     has1 = has2;
     has2 = has3;
-    e1_tok = e2_tok;
-    e1_q[0] = e2_q[0];
-    e1_q[1] = e2_q[1];
   }
 }
 
