@@ -627,56 +627,65 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
 
 // ---------------------------------------------------------------- combine
 
-// One workgroup per (token, kv head): out = sum_s exp(lse_s - lse) o_s.
+// out = sum_s exp(lse_s - lse) o_s per (token, kv head), lse = log sum_s
+// exp(lse_s).  A thread owns 8 dims of one q head (16 threads per head row,
+// 16 head rows per workgroup, so 16 / G (token, kv head) units per
+// workgroup) and walks the slots in batches of 8 with an online max: each
+// batch is one round trip of 8 partial loads (16 bytes each) and 8 lse
+// loads, with no LDS and no barrier.
 template <int G>
 __global__ __launch_bounds__(kWgThreads) void prefill_combine_kernel(PrefillAttnArgs a) {
-  __shared__ float wgt[kMaxSelect * G];
-  const int t = blockIdx.x;
-  const int g = blockIdx.y;
-  const int h = g / (a.hkv / a.hidx);
+  constexpr int kUnits = 16 / G;  // (token, kv head) units per workgroup
   const int tid = threadIdx.x;
+  const int unit = blockIdx.x * kUnits + tid / (16 * G);
+  if (unit >= a.num_tokens * a.hkv) return;
+  const int t = unit / a.hkv;
+  const int g = unit - t * a.hkv;
+  const int hh = (tid / 16) % G;
+  const int d0 = (tid % 16) * 8;
+  const int h = g / (a.hkv / a.hidx);
   const int n = min(max(a.cnt[t * a.hidx + h], 0), a.kmax);
-  const int64_t base = (static_cast<int64_t>(t) * a.hkv + g) * a.kmax * G;  // slot 0, head 0
-  const int64_t out0 = (static_cast<int64_t>(t) * a.hkv + g) * G;           // q head row
-  for (int i = tid; i < n * G; i += kWgThreads) wgt[i] = a.part_lse[base + i];
-  __syncthreads();
-  if (tid < G) {
-    float mx = -INFINITY;
-    for (int s = 0; s < n; ++s) mx = fmaxf(mx, wgt[s * G + tid]);
-    float sum = 0.f;
-    if (mx != -INFINITY)
-      for (int s = 0; s < n; ++s) sum += __expf(wgt[s * G + tid] - mx);
-    const float inv = sum > 0.f ? 1.f / sum : 0.f;
-    for (int s = 0; s < n; ++s)
-      wgt[s * G + tid] = mx != -INFINITY ? __expf(wgt[s * G + tid] - mx) * inv : 0.f;
-    if (a.lse_out != nullptr) a.lse_out[out0 + tid] = sum > 0.f ? mx + __logf(sum) : -INFINITY;
-  }
-  __syncthreads();
-  // Thread i: head i / 32, dims 4 (i % 32) .. + 4 (one 8-byte load per slot).
-  for (int i = tid; i < G * 32; i += kWgThreads) {
-    const int hh = i / 32;
-    const int d = 4 * (i - hh * 32);
-    const uint16_t* po = a.part_o + (base + hh) * 128 + d;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < n; s0 += 8) {
-      // straight-line batch: slots past the last re-read it with weight 0
-      u32x2_t v[8];
+  const int64_t row0 = (static_cast<int64_t>(t) * a.hkv + g) * a.kmax * G + hh;  // slot 0
+  const float* lse_p = a.part_lse + row0;
+  const uint16_t* po = a.part_o + row0 * 128 + d0;
+  float m = -INFINITY, wsum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n; s0 += 8) {
+    // straight-line batch: slots past the last re-read it and get weight 0
+    float ls[8];
+    u32x4_t v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[u] = *reinterpret_cast<const u32x2_t*>(
-            po + static_cast<int64_t>(min(s0 + u, n - 1)) * G * 128);
+    for (int u = 0; u < 8; ++u) {
+      const int64_t s = min(s0 + u, n - 1);
+      ls[u] = lse_p[s * G];
+      v[u] = *reinterpret_cast<const u32x4_t*>(po + s * G * 128);
+    }
+    float mb = m;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wv = s0 + u < n ? wgt[(s0 + u) * G + hh] : 0.f;
-        acc[0] = fmaf(wv, __uint_as_float(v[u][0] << 16), acc[0]);
-        acc[1] = fmaf(wv, __uint_as_float(v[u][0] & 0xffff0000u), acc[1]);
-        acc[2] = fmaf(wv, __uint_as_float(v[u][1] << 16), acc[2]);
-        acc[3] = fmaf(wv, __uint_as_float(v[u][1] & 0xffff0000u), acc[3]);
+    for (int u = 0; u < 8; ++u) mb = fmaxf(mb, s0 + u < n ? ls[u] : -INFINITY);
+    if (mb == -INFINITY) continue;  // nothing visible in any slot so far
+    const float sc = __expf(m - mb);  // 0 while m is still -inf
+    wsum *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wv = s0 + u < n ? __expf(ls[u] - mb) : 0.f;
+      wsum += wv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(wv, __uint_as_float(v[u][q] << 16), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(wv, __uint_as_float(v[u][q] & 0xffff0000u), acc[2 * q + 1]);
       }
     }
-    const u32x2_t r = {pack2_rne(acc[0], acc[1]), pack2_rne(acc[2], acc[3])};
-    *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.out) + (out0 + hh) * 128 + d) = r;
+    m = mb;
   }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t out0 = (static_cast<int64_t>(t) * a.hkv + g) * G + hh;  // q head row
+  const u32x4_t r = {pack2_rne(acc[0] * inv, acc[1] * inv), pack2_rne(acc[2] * inv, acc[3] * inv),
+                     pack2_rne(acc[4] * inv, acc[5] * inv), pack2_rne(acc[6] * inv, acc[7] * inv)};
+  *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(a.out) + out0 * 128 + d0) = r;
+  if (d0 == 0 && a.lse_out != nullptr) a.lse_out[out0] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }
 
 // -------------------------------------------------------------- launchers
@@ -718,13 +727,15 @@ hipError_t launch_prefill_attend(const PrefillAttnArgs& a, int kv_dtype, int gro
     else if (kv_dtype == 2) ok = launch_pf_attend_g<FP8>(a, group, s);
     if (!ok) return hipErrorInvalidValue;
   }
-  const dim3 cgrid(a.num_tokens, a.hkv);
+  // 16 / G (token, kv head) units per combine workgroup
+  const int64_t units = static_cast<int64_t>(a.num_tokens) * a.hkv;
+  auto cgrid = [&](int g) { return static_cast<unsigned>((units + 16 / g - 1) / (16 / g)); };
   switch (group) {
-    case 1: prefill_combine_kernel<1><<<cgrid, kWgThreads, 0, s>>>(a); break;
-    case 2: prefill_combine_kernel<2><<<cgrid, kWgThreads, 0, s>>>(a); break;
-    case 4: prefill_combine_kernel<4><<<cgrid, kWgThreads, 0, s>>>(a); break;
-    case 8: prefill_combine_kernel<8><<<cgrid, kWgThreads, 0, s>>>(a); break;
-    case 16: prefill_combine_kernel<16><<<cgrid, kWgThreads, 0, s>>>(a); break;
+    case 1: prefill_combine_kernel<1><<<cgrid(1), kWgThreads, 0, s>>>(a); break;
+    case 2: prefill_combine_kernel<2><<<cgrid(2), kWgThreads, 0, s>>>(a); break;
+    case 4: prefill_combine_kernel<4><<<cgrid(4), kWgThreads, 0, s>>>(a); break;
+    case 8: prefill_combine_kernel<8><<<cgrid(8), kWgThreads, 0, s>>>(a); break;
+    case 16: prefill_combine_kernel<16><<<cgrid(16), kWgThreads, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
