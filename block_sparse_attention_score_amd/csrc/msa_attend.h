@@ -247,11 +247,11 @@ __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp
 
 // ---------------------------------------------------------- split unit
 
-template <int G>
+template <int G, int W>
 struct AttendLds {
-  float o[4][16][kBlock];  // per-wave partial outputs, [head][dim]
-  float m[4][16];          // per-wave running max (base 2, scaled logits)
-  float l[4][16];          // per-wave running sum
+  float o[W][16][kBlock];  // per-wave partial outputs, [head][dim]
+  float m[W][16];          // per-wave running max (base 2, scaled logits)
+  float l[W][16];          // per-wave running sum
   float m_all[16];
   float l_all[16];
   int blk_nvalid[kMaxBps];
@@ -280,9 +280,10 @@ __device__ __forceinline__ void query_of(const AttendArgs& a, int t, int& b, int
 }
 
 // One split (blocks split*bps ..) of the (query token t, kv head g) unit.
-// Called by all 256 threads of a workgroup.
-template <class QT, class KT, int G>
-__device__ void attend_split(const AttendArgs& a, int split, int g, int t, AttendLds<G>& S) {
+// Called by all 64 * W threads (W waves) of a workgroup.
+template <class QT, class KT, int G, int W>
+__device__ void attend_split(const AttendArgs& a, int split, int g, int t, AttendLds<G, W>& S) {
+  constexpr int kThreads = kWave * W;
   const int h = g / (a.hkv / a.hidx);
   const int sel_row = t * a.hidx + h;
   int b, p;
@@ -312,13 +313,13 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   const KT* ktag = nullptr;
 
   if (sel_writer && count == 0) {
-    for (int i = threadIdx.x; i < a.kmax; i += kWgThreads)
+    for (int i = threadIdx.x; i < a.kmax; i += kThreads)
       a.sel_out[static_cast<int64_t>(sel_row) * a.kmax + i] = -1;
     if (threadIdx.x == 0) a.cnt_out[sel_row] = 0;
   }
   if (count == 0) {
     if (split == 0) {
-      for (int i = tid; i < G * 128; i += kWgThreads) store_out(qtag, a.out, hq0 * 128 + i, 0.f);
+      for (int i = tid; i < G * 128; i += kThreads) store_out(qtag, a.out, hq0 * 128 + i, 0.f);
       if (a.lse_out != nullptr && tid < G) a.lse_out[hq0 + tid] = -INFINITY;
     }
     return;
@@ -350,10 +351,10 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
     } else if (nb_vis <= 1024) {
       if (w == 0) select_wave<16>(srow, nb_vis, a.topk, a.init, a.local, emit);
     } else {
-      select_core<32>(srow, nb_vis, a.topk, a.init, a.local, S.sl, emit);
+      select_core<div_up(8192, kThreads), kThreads>(srow, nb_vis, a.topk, a.init, a.local, S.sl, emit);
     }
     if (sel_writer) {
-      for (int i = count + tid; i < a.kmax; i += kWgThreads) so[i] = -1;
+      for (int i = count + tid; i < a.kmax; i += kThreads) so[i] = -1;
       if (tid == 0) a.cnt_out[sel_row] = count;
     }
     __syncthreads();
@@ -370,13 +371,13 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   __syncthreads();
 
   // The split's blocks are cut into chunks of TILES 16-token tiles, and wave w
-  // streams chunks w, w+4, ... (so a split whose block count is not a multiple
-  // of 4 still spreads evenly), with its own online softmax; no barrier until
+  // streams chunks w, w+W, ... (so a split whose block count is not a multiple
+  // of W still spreads evenly), with its own online softmax; no barrier until
   // the final merge.
   constexpr bool kF32 = __is_same(KT, F32);
   constexpr int TILES = kF32 ? 2 : 4;           // tiles per chunk
   constexpr int CPB = 8 / TILES;                // chunks per 128-token block
-  const int nchunk = nblk * CPB > w ? (nblk * CPB - w + 3) / 4 : 0;
+  const int nchunk = nblk * CPB > w ? (nblk * CPB - w + W - 1) / W : 0;
 
   // 0/1 selectors for the V transpose.
   bf16x8_t sel_bf[2];
@@ -394,8 +395,8 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
     for (int e = 0; e < 4; ++e) sel_f[e] = (4 * q4 + e == l16) ? 1.f : 0.f;
   }
 
-  auto chunk_block = [&](int c) { return (w + 4 * c) / CPB; };
-  auto chunk_tok0 = [&](int c) { return ((w + 4 * c) % CPB) * TILES * 16; };
+  auto chunk_block = [&](int c) { return (w + W * c) / CPB; };
+  auto chunk_tok0 = [&](int c) { return ((w + W * c) % CPB) * TILES * 16; };
   auto row0 = [&](int c, int tt) {
     const int blk = chunk_block(c);
     const int tok = chunk_tok0(c) + 16 * tt + l16;
@@ -508,10 +509,12 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   }
   __syncthreads();
   if (tid < 16) {
-    const float M = fmaxf(fmaxf(S.m[0][tid], S.m[1][tid]), fmaxf(S.m[2][tid], S.m[3][tid]));
+    float M = S.m[0][tid];
+#pragma unroll
+    for (int ww = 1; ww < W; ++ww) M = fmaxf(M, S.m[ww][tid]);
     float lsum = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < W; ++ww) {
       const float sc = S.m[ww][tid] == -INFINITY ? 0.f : exp2f(S.m[ww][tid] - M);
       S.m[ww][tid] = sc;  // becomes the wave's weight
       lsum += S.l[ww][tid] * sc;
@@ -523,14 +526,16 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
 
   const int64_t part0 =
       ((static_cast<int64_t>(t) * a.hkv + g) * a.nsplit_max + split) * G;
-  for (int i = tid; i < G * 128; i += kWgThreads) {
+  for (int i = tid; i < G * 128; i += kThreads) {
     const int hh = i / 128;
     const int d = i % 128;
     const float l = S.l_all[hh];
-    const float o = l > 0.f ? ((S.o[0][hh][d] * S.m[0][hh] + S.o[1][hh][d] * S.m[1][hh]) +
-                               (S.o[2][hh][d] * S.m[2][hh] + S.o[3][hh][d] * S.m[3][hh])) *
-                                  (a.v_scale / l)
-                            : 0.f;
+    float o = 0.f;
+    if (l > 0.f) {
+#pragma unroll
+      for (int ww = 0; ww < W; ++ww) o = fmaf(S.o[ww][hh][d], S.m[ww][hh], o);
+      o *= a.v_scale / l;
+    }
     if (nsplit == 1) {
       store_out(qtag, a.out, (hq0 + hh) * 128 + d, o);
     } else {
@@ -555,7 +560,7 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
     // One round trip: every thread loads the lse and the partial of each
     // split for its (head, dim) and weights them itself.  Slots past the last
     // split re-read it and get weight 0.
-    for (int i = tid; i < G * 128; i += kWgThreads) {
+    for (int i = tid; i < G * 128; i += kThreads) {
       const int hh = i / 128;
       const int d = i % 128;
       float ls[8], v[8];
@@ -585,8 +590,8 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   }
   // Split weights exp(lse_c - lse) of every head, once, in LDS (the partial
   // lse values are loaded by many threads at once).
-  float* w_lds = &S.o[0][0][0];  // reused: nsplit_max * G <= 4 * 16 * 128 floats
-  for (int i = tid; i < nsplit * G; i += kWgThreads) w_lds[i] = load_shared_f32(a.part_lse + base0 + i);
+  float* w_lds = &S.o[0][0][0];  // reused: nsplit_max * G <= W * 16 * 128 floats
+  for (int i = tid; i < nsplit * G; i += kThreads) w_lds[i] = load_shared_f32(a.part_lse + base0 + i);
   __syncthreads();
   if (tid < G) {
     float mx = -INFINITY;
@@ -601,7 +606,7 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   }
   __syncthreads();
   // out = sum_c w_c o_c, partials read in independent batches of 8.
-  for (int i = tid; i < G * 128; i += kWgThreads) {
+  for (int i = tid; i < G * 128; i += kThreads) {
     const int hh = i / 128;
     const int d = i % 128;
     const float* po = a.part_o + (base0 + hh) * 128 + d;

@@ -4,10 +4,14 @@
 
 namespace msa {
 
+// Eight waves per workgroup: with one workgroup per CU (the split sizing
+// aims at that), two waves per SIMD stream blocks.
+constexpr int kAttendWaves = 8;
+
 template <class QT, class KT, int G>
-__global__ __launch_bounds__(kWgThreads, 2) void decode_attend_kernel(AttendArgs a) {
-  __shared__ AttendLds<G> lds;
-  attend_split<QT, KT, G>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+__global__ __launch_bounds__(kWave * kAttendWaves, 1) void decode_attend_kernel(AttendArgs a) {
+  __shared__ AttendLds<G, kAttendWaves> lds;
+  attend_split<QT, KT, G, kAttendWaves>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
 // ------------------------------------------------------------ launcher
@@ -15,7 +19,7 @@ __global__ __launch_bounds__(kWgThreads, 2) void decode_attend_kernel(AttendArgs
 template <class QT, class KT, int G>
 static void launch_attend_t(const AttendArgs& a, hipStream_t s) {
   const dim3 grid(a.nsplit_max, a.hkv, a.num_tokens);
-  decode_attend_kernel<QT, KT, G><<<grid, kWgThreads, 0, s>>>(a);
+  decode_attend_kernel<QT, KT, G><<<grid, kWave * kAttendWaves, 0, s>>>(a);
 }
 
 template <class QT, class KT>

@@ -248,7 +248,7 @@ __device__ __forceinline__ int block_incl_scan(int v, int* wsum) {
   return v + add;
 }
 
-__device__ __forceinline__ int div_up(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int div_up(int a, int b) { return (a + b - 1) / b; }
 
 // ------------------------------------------- cross-workgroup hand-off
 //

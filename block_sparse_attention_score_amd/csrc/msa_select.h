@@ -21,7 +21,7 @@ namespace msa {
 
 struct SelectLds {
   int hist[256];
-  int wsum[4];
+  int wsum[16];
   int digit;
   int need;
 };
@@ -33,15 +33,17 @@ __device__ __forceinline__ int forced_count(int nb, int init, int local) {
   return a + (nb - lo) - max(0, a - lo);
 }
 
-// s: nb scores of one (query, index head) row.  MAXPER >= ceil(nb / 256).
-// Must be called by all 256 threads of the workgroup.  Calls emit(pos, j) for
-// every selected block j, pos being its slot in ascending block order, and
-// returns the selection size.  No barrier after the last emit.
-template <int MAXPER, class Emit>
+// s: nb scores of one (query, index head) row.  MAXPER >= ceil(nb / NT).
+// Must be called by all NT (256 .. 1024) threads of the workgroup.  Calls
+// emit(pos, j) for every selected block j, pos being its slot in ascending
+// block order, and returns the selection size.  No barrier after the last
+// emit.
+template <int MAXPER, int NT = kWgThreads, class Emit>
 __device__ int select_core(const float* __restrict__ s, int nb, int topk, int init, int local,
                            SelectLds& L, Emit emit) {
+  static_assert(NT >= 256 && NT <= 1024, "one histogram bin per thread of the first 256");
   const int tid = threadIdx.x;
-  const int per = div_up(nb, kWgThreads);
+  const int per = div_up(nb, NT);
   const int j0 = tid * per;
   const int lo_init = min(init, nb);       // j <  lo_init  -> forced (init)
   const int hi_local = max(0, nb - local);  // j >= hi_local -> forced (local)
@@ -76,7 +78,7 @@ __device__ int select_core(const float* __restrict__ s, int nb, int topk, int in
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
       const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-      L.hist[tid] = 0;
+      if (tid < 256) L.hist[tid] = 0;
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < MAXPER; ++i) {
@@ -88,7 +90,7 @@ __device__ int select_core(const float* __restrict__ s, int nb, int topk, int in
       // Thread tid looks at digit 255 - tid: an inclusive scan counts the
       // candidates whose digit is >= that one.
       const int d = 255 - tid;
-      const int c = L.hist[d];
+      const int c = tid < 256 ? L.hist[d] : 0;
       const int incl = block_incl_scan(c, L.wsum);
       const int excl = incl - c;
       if (excl < need && need <= incl) {
