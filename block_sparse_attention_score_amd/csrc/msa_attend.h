@@ -8,22 +8,25 @@
 // selected blocks c*bps .. of the index head that serves g, for all G query
 // heads of g at once (the GQA group shares every K/V byte it loads).
 //
-// Per 128-token block:
-//  * S = q K^T on the matrix cores: q (G heads, zero-padded to 16 rows) is
-//    the A operand, K rows are read straight from the page into the B
-//    operand (16 tokens x 32 dims per instruction, 64 contiguous bytes per
-//    token), v_mfma_f32_16x16x32_bf16 (fp8 codes widen to bf16 exactly) or
+// The split's selected blocks are cut into 64-token chunks (32 for f32
+// caches) that the workgroup's waves take round-robin, each wave with its own
+// online softmax; per chunk:
+//  * S^T = K q^T on the matrix cores: K rows are read straight from the page
+//    into the A operand (16 tokens x 32 dims per instruction, 64 contiguous
+//    bytes per token), q^T (G heads, zero-padded to 16 columns) is the B
+//    operand; v_mfma_f32_16x16x32_bf16 (fp8 codes widen to bf16 exactly) or
 //    v_mfma_f32_16x16x4_f32 for f32 caches;
 //  * tokens past the query are masked to -inf by select; online softmax in
-//    base 2 (max and sum reduced over DPP rows, then across waves in LDS);
-//  * P V on the vector ALUs: each lane owns 4 dims of one token row (two rows
-//    per wave load), reads V with coalesced 8-byte loads, zeroes rows past
-//    the query (V may hold stale NaN bytes there) and accumulates all G heads,
-//    whose probabilities it reads from LDS as 16-byte vectors;
-//  * the next block's K and V loads are issued before the current block is
-//    computed (two-stage pipeline over the split's blocks).
-// The split writes its normalised partial output and lse; the last split to
-// finish (atomic ticket) merges the partials:
+//    base 2 per head column (max and sum over the lane's four tokens, then
+//    across the four 16-lane rows);
+//  * O^T = V^T P^T on the matrix cores: V^T is formed exactly by an MFMA of
+//    the V rows against a 0/1 selector, P is rounded to bf16 by the hardware
+//    pair conversion; V rows past the query are cleared first (stale bytes
+//    may be NaN, and 0 * NaN would reach the sums);
+//  * the next chunk's K loads are issued right after S^T and its V loads
+//    right after P V (two-stage pipeline over the wave's chunks).
+// The waves merge in LDS.  The split writes its normalised partial output
+// and lse; the last split to finish (atomic ticket) merges the partials:
 //   lse = log sum_c exp(lse_c),  out = sum_c exp(lse_c - lse) o_c.
 #pragma once
 
@@ -498,7 +501,7 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   for (int c = 0; c + 1 < nchunk; ++c) chunk(c, true);
   if (nchunk > 0) chunk(nchunk - 1, false);
 
-  // Merge the four waves: lane (l16, q4) holds O^T[16m + 4q4 + r][head l16].
+  // Merge the waves: lane (l16, q4) holds O^T[16m + 4q4 + r][head l16].
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll

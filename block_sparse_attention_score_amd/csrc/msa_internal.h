@@ -121,7 +121,7 @@ struct PrefillAttnArgs {
   const int32_t* cnt;        // [T, Hidx]
   int32_t kmax;
   int32_t hkv, hidx;
-  int32_t tq;                // tokens per tile: 128 / G
+  int32_t tq;                // tokens per tile: kPrefillTileRows / G
   // k2q lists, per (b, index head, block j): counts and cursor zero on entry
   int32_t* counts;           // [B * Hidx * max_blocks]
   int32_t* cursor;           // [B * Hidx * max_blocks]

@@ -8,12 +8,12 @@
 // those tokens and runs key-major attention tiles over it; this file does the
 // same on gfx950:
 //   1. k2q CSR: count the selecting tokens of every (b, index head, j), scan
-//      the counts into list offsets and 128-row work tiles, fill the lists;
-//   2. per tile: up to 256 query rows (tokens x GQA heads of one kv head)
-//      against block j, staged once in LDS (K as [key][dim], V as
-//      [dim][key]); S^T = K Q^T and O^T = V^T P^T on bf16 MFMA, causal mask
-//      per row; a normalised partial (o in bf16, lse in f32) per (token, kv
-//      head, slot);
+//      the counts into list offsets and 256-row work tiles, fill the lists;
+//   2. per tile: up to 256 query rows (tokens x GQA heads of one kv head,
+//      eight waves of 32 rows) against block j, staged once in LDS (K as
+//      [key][dim], V as [dim][key]); S^T = K Q^T and O^T = V^T P^T on bf16
+//      MFMA, causal mask per row; a normalised partial (o in bf16, lse in
+//      f32) per (token, kv head, slot);
 //   3. per (token, kv head), the log-sum-exp combine of its partials.
 #include "msa_device.h"
 #include "msa_internal.h"
