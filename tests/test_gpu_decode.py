@@ -55,6 +55,9 @@ SMALL = {
                                  local=0),
     "topk32_init3_local3": _spec(2, [20000, 30000], Hq=8, Hkv=2, Hidx=2, topk=32, init=3,
                                  local=3),
+    # rows of more than 1024 blocks: the workgroup radix select (inside the
+    # attention workgroups and in the standalone select kernel)
+    "long_rows": _spec(2, [200000, 150001], Hq=8, Hkv=1, Hidx=1, topk=16),
 }
 
 

@@ -45,6 +45,8 @@ SMALL = {
     "g1_long_lists": _spec([700, 300], [300, 0], Hq=2, Hkv=2, Hidx=1, topk=4, init=1,
                            local=2),
     "g2": _spec([400], [1200], Hq=4, Hkv=2, Hidx=2, topk=8),
+    # a prefix of more than 1024 blocks: the workgroup radix select per token
+    "long_prefix": _spec([40], [160000], Hq=8, Hkv=1, Hidx=1, topk=8),
 }
 
 
