@@ -661,8 +661,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
 // exp(lse_s).  A thread owns 8 dims of one q head (16 threads per head row,
 // 16 head rows per workgroup, so 16 / G (token, kv head) units per
 // workgroup) and walks the slots in batches of 8 with an online max: each
-// batch is one round trip of 8 partial loads (16 bytes each) and 8 lse
-// loads, with no LDS and no barrier.
+// batch is one round trip of 8 partial loads (16 bytes each, non-temporal:
+// the partials are read once) and 8 lse loads, with no LDS and no barrier.
 template <int G>
 __global__ __launch_bounds__(kWgThreads) void prefill_combine_kernel(PrefillAttnArgs a) {
   constexpr int kUnits = 16 / G;  // (token, kv head) units per workgroup
@@ -688,7 +688,7 @@ __global__ __launch_bounds__(kWgThreads) void prefill_combine_kernel(PrefillAttn
     for (int u = 0; u < 8; ++u) {
       const int64_t s = min(s0 + u, n - 1);
       ls[u] = lse_p[s * G];
-      v[u] = *reinterpret_cast<const u32x4_t*>(po + s * G * 128);
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(po + s * G * 128));
     }
     float mb = m;
 #pragma unroll
