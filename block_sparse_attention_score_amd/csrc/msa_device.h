@@ -250,6 +250,14 @@ __device__ __forceinline__ int block_incl_scan(int v, int* wsum) {
 
 __host__ __device__ constexpr int div_up(int a, int b) { return (a + b - 1) / b; }
 
+// max(a, b) that propagates NaN (v_maximum_f32 / v_maximum3_f32 on gfx950).
+// fmaxf must first quiet a signalling NaN, so every MFMA result it takes
+// costs one more VALU instruction; the maxima below only ever see finite
+// scores or -inf (masked entries are replaced before the max).
+__device__ __forceinline__ float max_nan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // ------------------------------------------- cross-workgroup hand-off
 //
 // Workgroups of one launch hand results to the workgroup that finishes a unit

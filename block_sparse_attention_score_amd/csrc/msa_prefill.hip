@@ -145,7 +145,8 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
         tile(buf, n, acc);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
-          mx[rt] = fmaxf(fmaxf(fmaxf(mx[rt], acc[rt][0]), fmaxf(acc[rt][1], acc[rt][2])), acc[rt][3]);
+          mx[rt] = max_nan(max_nan(max_nan(max_nan(mx[rt], acc[rt][0]), acc[rt][1]), acc[rt][2]),
+                           acc[rt][3]);
       }
     } else if (page_ok) {
 #pragma unroll 2
@@ -157,14 +158,14 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
         for (int rt = 0; rt < 4; ++rt) {
           const int pos = pos_w0 + 16 * rt + l16;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mx[rt] = fmaxf(mx[rt], tok + r <= pos ? acc[rt][r] : -INFINITY);
+          for (int r = 0; r < 4; ++r) mx[rt] = max_nan(mx[rt], tok + r <= pos ? acc[rt][r] : -INFINITY);
         }
       }
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      float m = fmaxf(mx[rt], __shfl_xor(mx[rt], 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
+      float m = max_nan(mx[rt], __shfl_xor(mx[rt], 16));
+      m = max_nan(m, __shfl_xor(m, 32));
       const int i = i0 + 64 * w + 16 * rt + l16;
       if (q4 == 0 && i < nq)
         a.scores[(static_cast<int64_t>(cu0 + i) * a.hidx + h) * a.max_blocks + j] = m;

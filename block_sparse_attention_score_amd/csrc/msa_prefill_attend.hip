@@ -56,9 +56,9 @@ __device__ __forceinline__ u32x2_t lds_b64(const uint16_t* p) {
 // same result.
 __device__ __forceinline__ float rows_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const float y = max_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
   const auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+  return max_nan(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
 }
 __device__ __forceinline__ float rows_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mr = fmaxf(mr, st[mt][nt][r]);
+          for (int r = 0; r < 4; ++r) mr = max_nan(mr, st[mt][nt][r]);
         const float mn = fmaxf(mrow[nt], rows_max(mr) * a.qk_scale_log2);
         // a row with nothing visible yet keeps m = -inf; its p are 2^-inf = 0
         const float mu = mn == -INFINITY ? 0.f : mn;
