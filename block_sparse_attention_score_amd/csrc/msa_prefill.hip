@@ -164,13 +164,19 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      float m = max_nan(mx[rt], __shfl_xor(mx[rt], 16));
-      m = max_nan(m, __shfl_xor(m, 32));
+      mx[rt] = max_nan(mx[rt], __shfl_xor(mx[rt], 16));
+      mx[rt] = max_nan(mx[rt], __shfl_xor(mx[rt], 32));
+    }
+    // The next block goes to LDS before this block's scores are stored: the
+    // staging waits for the block's loads, and loads and stores retire in
+    // order, so stores issued earlier would be waited for as well.
+    if (more) store(buf ^ 1);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
       const int i = i0 + 64 * w + 16 * rt + l16;
       if (q4 == 0 && i < nq)
-        a.scores[(static_cast<int64_t>(cu0 + i) * a.hidx + h) * a.max_blocks + j] = m;
+        a.scores[(static_cast<int64_t>(cu0 + i) * a.hidx + h) * a.max_blocks + j] = mx[rt];
     }
-    if (more) store(buf ^ 1);
     __syncthreads();
   }
 }
