@@ -82,31 +82,61 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
   // is visible to all 64 rows and needs no causal mask.
   const int pos_w0 = prefix + i0 + 64 * __builtin_amdgcn_readfirstlane(w);
 
-  // Cooperative copy of one key block: thread chunk c = tid + 256 * k covers
-  // row c / CHUNKS, bytes 16 * (c % CHUNKS).
-  auto page_of = [&](int j) { return a.block_table[static_cast<int64_t>(b) * a.max_blocks + j]; };
-  auto block_base = [&](int j) -> const char* {
+  // (the table is read through the constant address space: scalar loads,
+  // off the vector memory counter, whatever the stores below may alias)
+  const __attribute__((address_space(4))) int32_t* bt_row =
+      (const __attribute__((address_space(4))) int32_t*)(
+          reinterpret_cast<uintptr_t>(a.block_table + static_cast<int64_t>(b) * a.max_blocks));
+  auto page_of = [&](int j) { return bt_row[j]; };
+  // (32-bit page bound, so the checks below stay on the scalar unit)
+  const int np32 = static_cast<int>(a.num_pages < 0x7fffffff ? a.num_pages : 0x7fffffff);
+  // A key block is one contiguous run of 128 * Di bf16; thread chunk
+  // c = tid + 256 k sits at byte 16 c of it.  Buffer loads: the run's base in
+  // a scalar descriptor, the lane offset 16 tid loop-invariant, 4096 k as the
+  // scalar offset, so a fetch computes no vector addresses.
+  auto block_rsrc = [&](int j) {
     int page = page_of(j);
-    if (page < 0 || page >= a.num_pages) page = 0;  // never read: the block scores -inf
-    return reinterpret_cast<const char*>(a.idx_k) +
-           ((static_cast<int64_t>(page) * a.hidx + h) * kBlock * DI) * 2;
+    if (page < 0 || page >= np32) page = 0;  // never read: the block scores -inf
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(a.idx_k)) +
+            (static_cast<int64_t>(page) * a.hidx + h) * kBlock * DI * 2,
+        0, kBlock * DI * 2, 0x00020000);
   };
-  uint4 stage[LOADS];
-  auto fetch = [&](int j) {
-    const char* src = block_base(j);
+  // Two register sets take turns holding a block in flight, so each block's
+  // loads are issued two blocks ahead of its use.  Every iteration issues one
+  // block of loads (past the last block the clamped index re-reads it), so
+  // the wait before staging covers exactly the block it stages.
+  typedef uint4 Stage[LOADS];
+  const int lane_off = 16 * tid;
+  auto fetch = [&](int j, Stage& st) {
+    const auto r = block_rsrc(min(j, j1 - 1));
 #pragma unroll
     for (int k = 0; k < LOADS; ++k) {
-      const int c = tid + kWgThreads * k;
-      const u32x4_t v = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4_t*>(src + (c / CHUNKS) * (DI * 2) + 16 * (c % CHUNKS)));
-      stage[k] = uint4{v.x, v.y, v.z, v.w};
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, 16 * kWgThreads * k, 0);
+      st[k] = uint4{v.x, v.y, v.z, v.w};
     }
   };
-  auto store = [&](int buf) {
+  // Scores of this tile's rows through a buffer descriptor whose range ends
+  // at the sequence's last new token: stores of rows past it are dropped by
+  // the range check, so every lane stores unconditionally (the four lanes of
+  // a query store the same value), with a loop-invariant row offset and the
+  // block in the scalar offset.  A fixed store sequence keeps the waits the
+  // compiler derives from draining stores.
+  const int rows = min(nq - i0, kPrefillRows);
+  const auto srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      a.scores + (static_cast<int64_t>(cu0 + i0) * a.hidx + h) * a.max_blocks, 0,
+      rows * a.hidx * a.max_blocks * 4, 0x00020000);
+  int srow[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) srow[rt] = (64 * w + 16 * rt + l16) * a.hidx * a.max_blocks * 4;
+
+  // Staging into LDS: thread chunk c = tid + 256 k is row c / CHUNKS, bytes
+  // 16 (c % CHUNKS) of the block (rows padded to ROW_BYTES).
+  auto store = [&](int buf, const Stage& st) {
 #pragma unroll
     for (int k = 0; k < LOADS; ++k) {
       const int c = tid + kWgThreads * k;
-      *reinterpret_cast<uint4*>(&kbuf[buf][(c / CHUNKS) * ROW_BYTES + 16 * (c % CHUNKS)]) = stage[k];
+      *reinterpret_cast<uint4*>(&kbuf[buf][(c / CHUNKS) * ROW_BYTES + 16 * (c % CHUNKS)]) = st[k];
     }
   };
 
@@ -125,15 +155,12 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
     }
   };
 
-  fetch(j0);
-  store(0);
-  __syncthreads();
-  for (int j = j0; j < j1; ++j) {
-    const int buf = (j - j0) & 1;
-    const bool more = j + 1 < j1;
-    if (more) fetch(j + 1);
+  // Block j from LDS buffer buf; `next` holds block j+1 (in flight), `spare`
+  // receives block j+2.
+  auto step = [&](int j, int buf, Stage& next, Stage& spare) {
+    fetch(j + 2, spare);
     const int pg = page_of(j);
-    const bool page_ok = pg >= 0 && pg < a.num_pages;
+    const bool page_ok = pg >= 0 && pg < np32;
 
     float mx[4];  // per query column: max over this lane's tokens
 #pragma unroll
@@ -170,14 +197,21 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
     // The next block goes to LDS before this block's scores are stored: the
     // staging waits for the block's loads, and loads and stores retire in
     // order, so stores issued earlier would be waited for as well.
-    if (more) store(buf ^ 1);
+    if (j + 1 < j1) store(buf ^ 1, next);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int i = i0 + 64 * w + 16 * rt + l16;
-      if (q4 == 0 && i < nq)
-        a.scores[(static_cast<int64_t>(cu0 + i) * a.hidx + h) * a.max_blocks + j] = mx[rt];
-    }
+    for (int rt = 0; rt < 4; ++rt)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mx[rt]), srsrc, srow[rt], 4 * j, 0);
     __syncthreads();
+  };
+
+  Stage sa, sb;
+  fetch(j0, sb);
+  store(0, sb);
+  fetch(j0 + 1, sa);
+  __syncthreads();
+  for (int j = j0; j < j1; j += 2) {
+    step(j, 0, sa, sb);
+    if (j + 1 < j1) step(j + 1, 1, sb, sa);
   }
 }
 
