@@ -67,28 +67,13 @@ __device__ __forceinline__ float rows_sum(float x) {
   return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
-// Eight consecutive K/V elements as bf16, through the caches (a key block is
-// read by every tile of its list).
+// Eight consecutive bf16 elements through the caches (a query row is
+// gathered by every tile that holds one of its token's slots).
 __device__ __forceinline__ bf16x8_t load8_cached(const BF16*, const void* base, int64_t idx) {
   bf16x8_t r;
   __builtin_memcpy(&r, reinterpret_cast<const uint16_t*>(base) + idx, 16);
   return r;
 }
-__device__ __forceinline__ bf16x8_t load8_cached(const FP8*, const void* base, int64_t idx) {
-  uint2 raw;
-  __builtin_memcpy(&raw, reinterpret_cast<const uint8_t*>(base) + idx, 8);
-  float x[8];
-  fp8x4_to_f32(raw.x, x);
-  fp8x4_to_f32(raw.y, x + 4);
-  uint32_t u[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    u[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xffff0000u);
-  bf16x8_t r;
-  __builtin_memcpy(&r, u, 16);
-  return r;
-}
-
 // Buffer descriptor of one (page, head) run of a pool: base = pool + byte
 // offset, raw 32-bit words, 64 KB of records (bounds beyond read as 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t run_rsrc(const void* pool, int64_t byte_off) {
@@ -124,21 +109,6 @@ __device__ __forceinline__ bf16x8_t load8_buf(const FP8*, __amdgpu_buffer_rsrc_t
   bf16x8_t v;
   __builtin_memcpy(&v, u, 16);
   return v;
-}
-
-// load8_cached at element base + h0 + off: the uniform part and the 32-bit
-// lane offset are kept apart.
-__device__ __forceinline__ bf16x8_t load8_at(const BF16*, const void* base, int64_t h0,
-                                             uint32_t off) {
-  const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + h0;
-  bf16x8_t r;
-  __builtin_memcpy(&r, p + off, 16);
-  return r;
-}
-__device__ __forceinline__ bf16x8_t load8_at(const FP8*, const void* base, int64_t h0,
-                                             uint32_t off) {
-  return load8_cached(static_cast<const FP8*>(nullptr),
-                      reinterpret_cast<const uint8_t*>(base) + h0, off);
 }
 
 // Clears v unless keep, without a branch.
@@ -358,13 +328,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
   const int hq_stride = a.hkv * G;
 
   // Query row r = 32 w + 16 nt + l16 of a tile is token slot r / G, head r % G.
-  int qts[2], qhh[2];
+  int qhh[2];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = 32 * w + 16 * nt + l16;
-    qts[nt] = r / G;
-    qhh[nt] = r - qts[nt] * G;
-  }
+  for (int nt = 0; nt < 2; ++nt) qhh[nt] = (32 * w + 16 * nt + l16) % G;
 
   bf16x8_t qf[2][4];
   bf16x8_t kraw[4], vraw[4];
