@@ -107,8 +107,11 @@ int blocks_per_split(const msa_params_t& p, int32_t num_units) {
   return bps > kMaxBlocksPerSplit ? kMaxBlocksPerSplit : bps;
 }
 
-// Pages scored by one workgroup in the decode scan.
-constexpr int kPagesPerItem = 16;
+// Pages scored by one workgroup in the decode scan (two per wave): small
+// items spread sequences of very different lengths evenly over the CUs
+// (B = 64 with L from 4K to 128K: 361 -> 342 us for the scan), at no cost
+// for equal lengths.
+constexpr int kPagesPerItem = 8;
 // Prefill list entries pack a token index above an 8-bit selection slot.
 constexpr int kMaxPrefillTokens = 1 << 23;
 
