@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a read+write kernel over 1 GiB (HBM counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("SCAN_RD", "SCAN_WR", "COPY_RD",
+                                                          "COPY_WR"),
+                    help="rocprofv3 --pmc output folders -> profiles/ HBM traffic summary")
     return ap.parse_args()
 
 
@@ -153,8 +158,151 @@ def cpu_baseline(case, spec, seconds):
                        f"{spec['name']}, all heads), {t_used:.1f} s of fp64 numpy")
 
 
+# ---------------------------------------------------------------- HBM traffic
+#
+# The scan's HBM bytes come from the L2-to-memory request counters of two
+# rocprofv3 --pmc passes (reads, then writes), scaled by what the same
+# counters read for a kernel of known traffic (the copy probe: 1 GiB read and
+# 1 GiB written).  gfx950 issues 32-, 64- and 128-byte read requests; the
+# stock FETCH_SIZE expression counts the 128-byte ones only through
+# TCC_BUBBLE, which the scan's non-temporal loads do not raise, so reads are
+# counted here from TCC_EA0_RDREQ_128B / _32B directly.
+TRAFFIC_RD = ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_128B_sum", "TCC_EA0_RDREQ_32B_sum",
+              "TCC_BUBBLE_sum"]
+TRAFFIC_WR = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum"]
+TRAFFIC_JSON = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "decode_b32_l32k_scan_hbm_traffic.json")
+COPY_PROBE_BYTES = 1 << 30
+SCAN_SOURCES = ["msa_score.h", "msa_score.hip", "msa_device.h", "msa_internal.h"]
+
+
+def scan_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "block_sparse_attention_score_amd", "csrc")
+    for name in SCAN_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def copy_probe():
+    """1 GiB read and 1 GiB written by one elementwise kernel, three times."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES}), flush=True)
+
+
+def _counters(folder, kernel_substr):
+    """Per-dispatch counter values of the kernels whose name contains kernel_substr."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if kernel_substr not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatch of a kernel matching {kernel_substr!r} under {folder}")
+    return list(per.values())
+
+
+def _read_bytes(c):
+    rd, r128, r32 = c["TCC_EA0_RDREQ_sum"], c["TCC_EA0_RDREQ_128B_sum"], c["TCC_EA0_RDREQ_32B_sum"]
+    return 128 * r128 + 64 * (rd - r128 - r32) + 32 * r32
+
+
+def _fetch_size_bytes(c):  # the stock FETCH_SIZE expression, for comparison
+    rd, bub, r32 = c["TCC_EA0_RDREQ_sum"], c["TCC_BUBBLE_sum"], c["TCC_EA0_RDREQ_32B_sum"]
+    return 128 * bub + 64 * (rd - bub - r32) + 32 * r32
+
+
+def _write_bytes(c):
+    wr, w64 = c["TCC_EA0_WRREQ_sum"], c["TCC_EA0_WRREQ_64B_sum"]
+    return 64 * w64 + 32 * (wr - w64)
+
+
+def traffic_summary(scan_rd, scan_wr, copy_rd, copy_wr):
+    """Write the scan's calibrated HBM traffic to profiles/ (JSON for bench.py, Markdown for readers)."""
+    med = lambda xs: float(np.median(xs))
+    s_rd = _counters(scan_rd, "decode_score_kernel")
+    s_wr = _counters(scan_wr, "decode_score_kernel")
+    c_rd = _counters(copy_rd, "neg")
+    c_wr = _counters(copy_wr, "neg")
+    f_rd = COPY_PROBE_BYTES / med([_read_bytes(c) for c in c_rd])
+    f_wr = COPY_PROBE_BYTES / med([_write_bytes(c) for c in c_wr])
+    rd = med([_read_bytes(c) for c in s_rd]) * f_rd
+    wr = med([_write_bytes(c) for c in s_wr]) * f_wr
+    stock = med([_fetch_size_bytes(c) for c in s_rd])
+    res = {"kernel": "decode_score_kernel", "workload": DEFAULT_WORKLOAD,
+           "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+           "traffic_bytes_per_launch": rd + wr, "copy_factor_read": f_rd,
+           "copy_factor_write": f_wr, "stock_fetch_size_bytes": stock,
+           "dispatches": [len(s_rd), len(s_wr)], "source_sha256": scan_source_hash()}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(res, f, indent=1)
+    md = TRAFFIC_JSON[:-5] + ".md"
+    with open(md, "w") as f:
+        f.write(
+            "# HBM traffic of the decode index scan, decode_b32_l32k (B=32, L=32768, 2 index heads, Di=128)\n\n"
+            "Commands (run from the repository root on one MI355X; each pass alone):\n\n"
+            "    cd /tmp && export TMPDIR=/tmp\n"
+            f"    rocprofv3 --pmc {' '.join(TRAFFIC_RD)} --output-format csv -d <scan_rd> -- python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline\n"
+            f"    rocprofv3 --pmc {' '.join(TRAFFIC_WR)} --output-format csv -d <scan_wr> -- python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline\n"
+            f"    rocprofv3 --pmc {' '.join(TRAFFIC_RD)} --output-format csv -d <copy_rd> -- python3 <repo>/bench.py --copy-probe\n"
+            f"    rocprofv3 --pmc {' '.join(TRAFFIC_WR)} --output-format csv -d <copy_wr> -- python3 <repo>/bench.py --copy-probe\n"
+            "    python3 bench.py --traffic-summary <scan_rd> <scan_wr> <copy_rd> <copy_wr>\n\n"
+            "Bytes per launch are 128 x RDREQ_128B + 64 x (RDREQ - RDREQ_128B - RDREQ_32B) + 32 x RDREQ_32B\n"
+            "(reads) and 64 x WRREQ_64B + 32 x (WRREQ - WRREQ_64B) (writes), medians over the dispatches,\n"
+            "scaled by the copy probe (1 GiB read and written by one elementwise kernel).\n\n"
+            "| quantity | value |\n|---|---|\n"
+            f"| scan reads per launch | {rd / 1e6:.1f} MB |\n"
+            f"| scan writes per launch | {wr / 1e6:.3f} MB |\n"
+            f"| algorithmic bytes per launch | {score_kernel_bytes_default() / 1e6:.1f} MB |\n"
+            f"| copy-probe factor, reads / writes | {f_rd:.3f} / {f_wr:.3f} |\n"
+            f"| stock FETCH_SIZE expression for the scan | {stock / 1e6:.1f} MB |\n"
+            f"| dispatches (read pass, write pass) | {len(s_rd)}, {len(s_wr)} |\n"
+            f"| sha256 of {', '.join(SCAN_SOURCES)} | `{res['source_sha256'][:16]}...` |\n")
+    print(json.dumps(res))
+
+
+def score_kernel_bytes_default():
+    """Algorithmic bytes of one scan launch of the default workload (every
+    sequence at its fixed length)."""
+    from synth import workload
+    spec = workload(DEFAULT_WORKLOAD)
+    kind, length = spec["seq_lens"]
+    assert kind == "fixed"
+    lens = np.full(spec["B"], length, dtype=np.int64)
+    return score_kernel_bytes(spec, lens, int((length + 127) // 128))
+
+
+def measured_traffic():
+    """The calibrated scan traffic per launch, while the scan's sources are the
+    ones it was measured on; else None."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("source_sha256") != scan_source_hash():
+        return None
+    return t["traffic_bytes_per_launch"]
+
+
 def main():
     args = parse()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
+    if args.copy_probe:
+        return copy_probe()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -261,7 +409,8 @@ def main():
         "wall_s_timed_region": t_wall,
         "roofline": {"kernel": "decode_score_kernel (index-key scan)", "bound": "hbm",
                      "achieved": k_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": k_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": k_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if args.workload == DEFAULT_WORKLOAD else None,
                      "bytes_per_launch": k_bytes, "ms_per_launch": k_ms},
         "device": torch.cuda.get_device_name(dev),
     }
