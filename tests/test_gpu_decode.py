@@ -255,3 +255,16 @@ def test_decode_repeats_match_composition(msa):
                                                return_selection=True)
         assert torch.equal(sel, sel_u) and torch.equal(cnt, cnt_u), f"call {i}: selection"
         assert torch.equal(out, out_u) and torch.equal(lse, lse_u), f"call {i}: output"
+
+
+def test_decode_maximum_sizes(msa):
+    """The largest supported shapes: a sequence of 8192 blocks (1M tokens, the
+    max_blocks limit) beside a short one, and the largest selection (topk 32
+    with 64 init and 64 local blocks, 160 slots), so a row is cut into more
+    splits than the one-round-trip combine takes."""
+    spec = _spec(2, [8192 * 128, 5000], Hq=8, Hkv=1, Hidx=1, Di=64, topk=32, init=64, local=64)
+    print("[decode_max] seed=31", flush=True)
+    case, cfg, g = _run(msa, spec, 31)
+    assert case.max_blocks == 8192
+    err, nband = _compare(host_view(case), g, spec)
+    print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)

@@ -121,3 +121,16 @@ def test_prefill_full_size_sampled(msa):
     cnt = parity.to_np(g["cnt"])
     assert (cnt == spec["topk"] + spec["init"] + spec["local"]).all()
     assert torch.isfinite(g["out"].float()).all()
+
+
+def test_prefill_maximum_sizes(msa):
+    """A prefix that fills the table (8192 blocks, the max_blocks limit) with
+    the largest selection (160 slots: topk 32, 64 init, 64 local)."""
+    spec = _spec([24, 100], [8192 * 128 - 24, 3000], Hq=8, Hkv=1, Hidx=1, Di=64, topk=32,
+                 init=64, local=64)
+    print("[prefill_max] seed=41", flush=True)
+    case = generate(spec, 41, device="cuda")
+    assert case.max_blocks == 8192
+    g = _run(msa, case, spec)
+    err, nband = _compare(host_view(case), g, spec, np.arange(case.T))
+    print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
