@@ -143,15 +143,7 @@ __device__ __forceinline__ void mask_row(Row<KT>& r, bool keep) {
 }
 
 __device__ __forceinline__ bf16x8_t fp8_to_bf16x8(const Raw8<FP8>& r) {
-  float x[8];
-  unpack(r, x);
-  uint32_t u[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    u[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xffff0000u);
-  bf16x8_t v;
-  __builtin_memcpy(&v, u, 16);
-  return v;
+  return fp8x8_to_bf16x8(r.v.x, r.v.y);
 }
 __device__ __forceinline__ bf16x8_t as_bf16(const bf16x8_t& v) { return v; }
 __device__ __forceinline__ bf16x8_t as_bf16(const Raw8<FP8>& v) { return fp8_to_bf16x8(v); }

@@ -144,6 +144,18 @@ __device__ __forceinline__ void unpack4(const Raw4<FP8>& r, float (&x)[4]) {
   fp8x4_to_f32(r.v, x);
 }
 
+// Eight fp8-e4m3 codes (two little-endian words) to bf16, exactly (every
+// e4m3 value is a bf16 value; the scale operand is 1): the gfx950 packed
+// conversion, one instruction per two codes.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // Eight consecutive elements packed as bf16 for an MFMA operand.  fp8 codes
 // convert exactly (every e4m3 value is a bf16 value).
 __device__ __forceinline__ bf16x8_t load8_bf16(const BF16*, const void* base,
@@ -155,19 +167,6 @@ __device__ __forceinline__ bf16x8_t load8_bf16(const BF16*, const void* base,
   return r;
 }
 
-__device__ __forceinline__ bf16x8_t load8_bf16(const FP8*, const void* base,
-                                               int64_t idx) {
-  float x[8];
-  load8(static_cast<const FP8*>(nullptr), base, idx, x);
-  uint32_t u[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    u[i] = (__float_as_uint(x[2 * i]) >> 16) |
-           (__float_as_uint(x[2 * i + 1]) & 0xffff0000u);
-  bf16x8_t r;
-  __builtin_memcpy(&r, u, 16);
-  return r;
-}
 
 // float -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {

@@ -99,16 +99,7 @@ __device__ __forceinline__ bf16x8_t load8_buf(const BF16*, __amdgpu_buffer_rsrc_
 __device__ __forceinline__ bf16x8_t load8_buf(const FP8*, __amdgpu_buffer_rsrc_t r, uint32_t voff,
                                               uint32_t soff) {
   const auto raw = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-  float x[8];
-  fp8x4_to_f32(raw[0], x);
-  fp8x4_to_f32(raw[1], x + 4);
-  uint32_t u[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    u[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xffff0000u);
-  bf16x8_t v;
-  __builtin_memcpy(&v, u, 16);
-  return v;
+  return fp8x8_to_bf16x8(raw[0], raw[1]);
 }
 
 // Clears v unless keep, without a branch.
