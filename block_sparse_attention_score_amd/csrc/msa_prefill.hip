@@ -33,13 +33,16 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
   constexpr int LOADS = 128 * CHUNKS / kWgThreads;  // per thread per block
   __shared__ __attribute__((aligned(16))) char kbuf[2][128 * ROW_BYTES];
 
-  // workgroup -> (sequence, 256-row query tile, index head, key-block chunk);
-  // tiles past a sequence's new tokens exit at once
-  const int per_seq = a.max_tiles * a.hidx * a.kchunks;
-  const int b = blockIdx.x / per_seq;
-  int rem = blockIdx.x - b * per_seq;
-  const int qt = rem / (a.hidx * a.kchunks);
-  rem -= qt * a.hidx * a.kchunks;
+  // workgroup -> (256-row query tile, sequence, index head, key-block chunk),
+  // query tile outermost: the grid is sized for the longest possible
+  // sequence (all tokens), and tiles past a sequence's new tokens exit at
+  // once, so ordering by tile puts those empty workgroups after every real
+  // one (they are dispatched last instead of holding slots in between)
+  const int per_tile = a.num_seqs * a.hidx * a.kchunks;
+  const int qt = blockIdx.x / per_tile;
+  int rem = blockIdx.x - qt * per_tile;
+  const int b = rem / (a.hidx * a.kchunks);
+  rem -= b * a.hidx * a.kchunks;
   const int h = rem / a.kchunks;
   const int kc = rem - h * a.kchunks;
   const int cu0 = a.cu_seqlens_q[b];
