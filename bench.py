@@ -203,7 +203,9 @@ def _counters(folder, kernel_substr):
     import csv
     import glob
     per = {}
-    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+    paths = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    # one profiled run: the newest file (a folder reused across runs keeps older ones)
+    for path in sorted(paths, key=os.path.getmtime)[-1:]:
         for r in csv.DictReader(open(path)):
             if kernel_substr not in r["Kernel_Name"]:
                 continue
