@@ -325,3 +325,79 @@ def sparse_attention(inp: dict, scale: Optional[float] = None) -> dict:
     sel, cnt = select(inp, scores)
     out, lse = attend(inp, sel, cnt, scale)
     return dict(scores=scores, sel=sel, count=cnt, out=out, lse=lse)
+
+
+# --------------------------------------------------------------------------
+# Paged append of the new tokens (the step before the path)
+# --------------------------------------------------------------------------
+#
+# The sglang page's backend stores the new tokens' K, V and index keys into
+# its pool at ``out_cache_loc`` before it attends (the pool's
+# ``set_fused_kv_index_buffer``; its body is not on the pages).  Reading
+# taken here: ``out_cache_loc`` holds flat token slots of the paged pool, slot
+# s living in page s // 128 at offset s % 128; slots outside the pool (e.g.
+# -1 padding) are not written.  A bf16 or f32 pool stores the value as given;
+# an fp8 pool stores the e4m3fn code of x / scale (per-tensor k_scale or
+# v_scale, the vLLM page's fp8 cache scales), the division done in float32,
+# clamped to +-448, rounded to nearest with ties to even.
+
+
+def fp8_e4m3fn_encode(y: np.ndarray) -> np.ndarray:
+    """float32 values -> e4m3fn codes (uint8).
+
+    From the format definition alone: each value is clamped to +-448 (the
+    largest finite magnitude), then takes the code of the same sign whose
+    value is nearest, an exact tie going to the code with an even mantissa
+    (its lowest bit clear); a negative value that rounds to zero keeps its
+    sign (code 0x80).  NaN becomes the NaN code of its sign (0x7F / 0xFF).
+    """
+    tab = fp8_e4m3fn_table()
+    y32 = np.asarray(y, dtype=np.float32)
+    flat = y32.reshape(-1)
+    neg = np.signbit(flat)
+    mag = np.abs(flat.astype(np.float64))
+    nan = np.isnan(mag)
+    mag = np.minimum(np.where(nan, 0.0, mag), 448.0)
+    codes = np.arange(0x7F)                  # finite non-negative codes 0x00..0x7E
+    vals = tab[codes]                        # ascending magnitudes
+    dist = np.abs(mag[:, None] - vals[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    cand = dist == best                      # one or two neighbouring codes
+    even = cand & ((codes[None, :] & 1) == 0)
+    pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+    out = codes[pick].astype(np.uint8)
+    out = np.where(nan, np.uint8(0x7F), out)
+    out = np.where(neg, out | np.uint8(0x80), out).astype(np.uint8)
+    return out.reshape(y32.shape)
+
+
+def store_values(src: np.ndarray, src_dtype: str, pool_dtype: str, scale: float = 1.0):
+    """New values in their source representation (bf16 bits, f32) -> the
+    pool's stored representation."""
+    if pool_dtype == src_dtype:
+        return np.array(src, copy=True)
+    if pool_dtype == "fp8" and src_dtype == "bf16":
+        x32 = decode(src, "bf16").astype(np.float32)   # exact
+        y32 = x32 / np.float32(scale)                  # IEEE float32 division
+        return fp8_e4m3fn_encode(y32)
+    raise ValueError((src_dtype, pool_dtype))
+
+
+def append_kv(k_pool, v_pool, idx_k_pool, k_new, v_new, idx_k_new, slots, *,
+              kv_src: str, kv_dtype: str, idx_dtype: str, k_scale: float = 1.0,
+              v_scale: float = 1.0):
+    """Pools (stored arrays, [P, H, 128, D]) with token t's rows written at
+    slot slots[t]; returns new arrays, the inputs are left unchanged.
+    k_new / v_new [T, Hkv, D] and idx_k_new [T, Hidx, Di] are given in their
+    source representation (kv_src: bf16 bits or f32; index keys already in
+    idx_dtype)."""
+    k_pool, v_pool, idx_k_pool = (np.array(a, copy=True) for a in (k_pool, v_pool, idx_k_pool))
+    P = k_pool.shape[0]
+    for t, s in enumerate(np.asarray(slots, dtype=np.int64)):
+        if s < 0 or s >= P * BLOCK:
+            continue
+        page, off = divmod(int(s), BLOCK)
+        k_pool[page, :, off, :] = store_values(k_new[t], kv_src, kv_dtype, k_scale)
+        v_pool[page, :, off, :] = store_values(v_new[t], kv_src, kv_dtype, v_scale)
+        idx_k_pool[page, :, off, :] = store_values(idx_k_new[t], idx_dtype, idx_dtype)
+    return k_pool, v_pool, idx_k_pool

@@ -403,3 +403,92 @@ def test_selection_structure_on_random_case():
             F = oracle.forced_blocks(nb, 1, 2)
             assert set(F) <= set(S)
             assert len(S) == min(nb, len(F) + 3)
+
+
+# ---------------------------------------------------------------- paged append
+
+def test_fp8_encode_matches_torch_cast():
+    """The oracle's e4m3fn encoder (nearest code, ties to even, written from the
+    format) against torch's float32 -> float8_e4m3fn cast on the CPU, over
+    normals, subnormals, values past the largest finite one (clamped first:
+    the stored code saturates) and exact midpoints between neighbouring codes."""
+    rng = np.random.default_rng(7)
+    n = 30000
+    y = (rng.standard_normal(n) * np.exp(rng.uniform(-14.0, 8.0, n))).astype(np.float32)
+    tab = oracle.fp8_e4m3fn_table()
+    fin = tab[:0x7F]
+    mids = ((fin[:-1] + fin[1:]) / 2.0).astype(np.float32)   # exact in float32
+    y = np.concatenate([y, mids, -mids, np.float32([0.0, -0.0, 448.0, -448.0, 1e30, -1e30])])
+    mine = oracle.fp8_e4m3fn_encode(y)
+    ref = torch.from_numpy(np.clip(y, -448.0, 448.0)).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(mine, ref.numpy())
+
+
+def test_fp8_encode_round_trip_ties_and_saturation():
+    tab = oracle.fp8_e4m3fn_table()
+    codes = np.array([c for c in range(256) if not math.isnan(tab[c])], dtype=np.int64)
+    # every finite code is its own nearest value (the -0 code keeps its sign)
+    assert np.array_equal(oracle.fp8_e4m3fn_encode(tab[codes].astype(np.float32)), codes)
+    # a value halfway between two neighbouring codes takes the even one
+    for c in range(0x7E):
+        mid = np.float32((tab[c] + tab[c + 1]) / 2.0)
+        want = c if c % 2 == 0 else c + 1
+        assert oracle.fp8_e4m3fn_encode(np.float32([mid]))[0] == want
+        assert oracle.fp8_e4m3fn_encode(np.float32([-mid]))[0] == want | 0x80
+    # just above / below a midpoint goes to the nearer code
+    m = np.float32((tab[0x31] + tab[0x32]) / 2.0)
+    assert oracle.fp8_e4m3fn_encode(np.nextafter(m, np.float32(10.0), dtype=np.float32)[None])[0] == 0x32
+    assert oracle.fp8_e4m3fn_encode(np.nextafter(m, np.float32(0.0), dtype=np.float32)[None])[0] == 0x31
+    # saturation at the largest finite magnitude, 448 = 0x7E
+    assert list(oracle.fp8_e4m3fn_encode(np.float32([500.0, 1e38, -465.0]))) == [0x7E, 0x7E, 0xFE]
+    # a negative value below half the smallest subnormal rounds to -0
+    assert oracle.fp8_e4m3fn_encode(np.float32([-2.0 ** -11]))[0] == 0x80
+    assert oracle.fp8_e4m3fn_encode(np.float32([2.0 ** -11]))[0] == 0x00
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f32", "fp8"])
+def test_append_kv_oracle(kv):
+    """append_kv writes token t's rows at page slot//128, offset slot%128 of
+    every head, leaves all other rows untouched and skips slots outside the
+    pool; an fp8 pool holds the code of x / scale (bf16 x, float32 division),
+    which decodes back to x when x / scale is an e4m3 value."""
+    rng = np.random.default_rng(11)
+    P, Hkv, Hidx, D, Di, T = 5, 2, 1, 8, 4, 7
+    src = "f32" if kv == "f32" else "bf16"
+
+    def rand_src(shape, dt):
+        x = rng.standard_normal(shape).astype(np.float32)
+        return x if dt == "f32" else (x.view(np.uint32) >> 16).astype(np.uint16)
+
+    pool_dt = {"bf16": np.uint16, "f32": np.float32, "fp8": np.uint8}[kv]
+    k_pool = rng.integers(0, 2 ** 7, (P, Hkv, 128, D)).astype(pool_dt)
+    v_pool = rng.integers(0, 2 ** 7, (P, Hkv, 128, D)).astype(pool_dt)
+    ik_pool = rand_src((P, Hidx, 128, Di), "bf16")
+    k_new, v_new = rand_src((T, Hkv, D), src), rand_src((T, Hkv, D), src)
+    ik_new = rand_src((T, Hidx, Di), "bf16")
+    slots = np.array([3, 128 * 2 + 127, -1, 128 * 4, P * 128, 77, 128 + 5], dtype=np.int64)
+    ks, vs = 0.25, 0.125
+    k2, v2, ik2 = oracle.append_kv(k_pool, v_pool, ik_pool, k_new, v_new, ik_new, slots,
+                                   kv_src=src, kv_dtype=kv, idx_dtype="bf16", k_scale=ks,
+                                   v_scale=vs)
+    written = np.zeros((P, 128), dtype=bool)
+    for t, s in enumerate(slots):
+        if 0 <= s < P * 128:
+            page, off = divmod(int(s), 128)
+            written[page, off] = True
+            assert np.array_equal(ik2[page, :, off], ik_new[t])
+            if kv == "fp8":
+                for pool, new, sc in ((k2, k_new, ks), (v2, v_new, vs)):
+                    want = torch.from_numpy(
+                        (oracle.decode(new[t], "bf16").astype(np.float32) / np.float32(sc))
+                        .clip(-448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+                    assert np.array_equal(pool[page, :, off], want)
+            else:
+                assert np.array_equal(k2[page, :, off], k_new[t])
+                assert np.array_equal(v2[page, :, off], v_new[t])
+    for old, new in ((k_pool, k2), (v_pool, v2), (ik_pool, ik2)):
+        assert np.array_equal(old.transpose(0, 2, 1, 3)[~written], new.transpose(0, 2, 1, 3)[~written])
+    # e4m3 values times a power-of-two scale come back exactly
+    x = oracle.fp8_e4m3fn_table()[[0x01, 0x22, 0x38, 0x5C, 0xB3, 0xFE]].astype(np.float32) / 16
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.decode(oracle.store_values(xb, "bf16", "fp8", 1 / 16), "fp8", 1 / 16), x)
