@@ -2,7 +2,8 @@
 
 Python binding of libmsa.so (C ABI in include/msa.h): every step of the
 path (block scoring, top-k selection with init/local forcing, split-K
-attention over the selected blocks, log-sum-exp combine, fp8 dequantisation)
+attention over the selected blocks, log-sum-exp combine, fp8 dequantisation,
+the paged append of new tokens)
 runs in the library's gfx950 kernels; this package only marshals arguments.
 """
 
@@ -10,6 +11,7 @@ from ._lib import MsaError, load  # noqa: F401
 from .api import (  # noqa: F401
     MsaConfig,
     alloc_workspace,
+    append_kv,
     block_score,
     blocks_from_tokens,
     decode_workspace_size,

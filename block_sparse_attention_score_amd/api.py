@@ -235,6 +235,25 @@ def sparse_prefill(cfg: MsaConfig, q, idx_q, k_pool, v_pool, idx_k_pool, block_t
     return out
 
 
+def append_kv(cfg: MsaConfig, k_new, v_new, idx_k_new, slot_mapping, k_pool, v_pool,
+              idx_k_pool, stream=None):
+    """Write token t's K, V (k_new, v_new [T, Hkv, D]) and index keys
+    (idx_k_new [T, Hidx, Di]) into the pools at slot slot_mapping[t] (int64;
+    page s // 128, offset s % 128; slots outside the pool are skipped), in
+    place.  fp8 pools (uint8) receive the e4m3 codes of x / k_scale (v_scale)."""
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    T = slot_mapping.shape[0]
+    for t, rows in ((k_new, cfg.num_kv_heads), (v_new, cfg.num_kv_heads),
+                    (idx_k_new, cfg.num_idx_heads)):
+        if t.shape[0] != T or t.shape[1] != rows:
+            raise ValueError("new rows must be [T, heads, dim] with T = len(slot_mapping)")
+    p = cfg.params()
+    check(load().msa_append_kv(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(idx_k_new),
+                               _ptr(slot_mapping), T, _ptr(k_pool), _ptr(v_pool),
+                               _ptr(idx_k_pool), k_pool.shape[0], _stream(stream)))
+
+
 def fp8_dequant(codes: torch.Tensor, scale: float = 1.0, out=None, stream=None):
     """fp8-e4m3 codes (uint8) -> float32 values times scale, as the loaders do it."""
     if codes.dtype not in (torch.uint8, torch.float8_e4m3fn):

@@ -490,6 +490,41 @@ msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q, const 
   return st == MSA_OK ? ok() : st;
 }
 
+msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new, const void* v_new,
+                           const void* idx_k_new, const int64_t* slot_mapping,
+                           int32_t num_tokens, void* k_pool, void* v_pool, void* idx_k_pool,
+                           int64_t num_pages, void* stream) {
+  msa_status_t st = check_params(params);
+  if (st != MSA_OK) return st;
+  if (!k_new || !v_new || !idx_k_new || !slot_mapping || !k_pool || !v_pool || !idx_k_pool)
+    return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (num_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "num_tokens=%d < 0", num_tokens);
+  if (num_tokens > 65535)
+    return fail(MSA_ERR_UNSUPPORTED, "num_tokens=%d above 65535 per call", num_tokens);
+  if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
+  if (num_tokens == 0) return ok();
+  msa::AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.idx_k_new = idx_k_new;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.idx_k_pool = idx_k_pool;
+  a.num_pages = num_pages;
+  a.hkv = params->num_kv_heads;
+  a.hidx = params->num_idx_heads;
+  a.head_dim = params->head_dim;
+  a.idx_dim = params->idx_dim;
+  a.k_scale = params->kv_dtype == MSA_FP8_E4M3 ? params->k_scale : 1.f;
+  a.v_scale = params->kv_dtype == MSA_FP8_E4M3 ? params->v_scale : 1.f;
+  st = hip_status(msa::launch_append(a, params->kv_dtype, params->idx_dtype,
+                                     static_cast<hipStream_t>(stream)),
+                  "append launch");
+  return st == MSA_OK ? ok() : st;
+}
+
 msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const void* idx_q,
                                 const void* k_pool, const void* v_pool,
                                 const void* idx_k_pool, int64_t num_pages,

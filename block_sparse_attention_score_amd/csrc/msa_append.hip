@@ -1,0 +1,134 @@
+// Paged append: the new tokens' K, V and index keys written into the pools
+// at their token slots (the sglang page minimax_sparse_backend.py stores the
+// new tokens into its pool at out_cache_loc before it attends; slot s is
+// page s / 128, offset s % 128 of the head-major pages here).  fp8 pools
+// receive the e4m3 code of x / scale (per-tensor k_scale / v_scale, the vLLM
+// page's fp8 cache scales): float32 division, clamp to +-448, round to
+// nearest even by the gfx950 conversion instruction.
+//
+// One thread moves 8 consecutive elements of one row (16-byte bf16 loads);
+// a token's rows (Hkv K rows, Hkv V rows, Hidx index rows) are spread over
+// the x dimension of the grid, tokens over y.  Memory-bound and tiny: one
+// decode step appends B tokens.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+template <class T>
+struct Pack8;
+template <>
+struct Pack8<BF16> {
+  uint4 v;
+};
+template <>
+struct Pack8<F32> {
+  float4 a, b;
+};
+template <>
+struct Pack8<FP8> {
+  uint2 v;
+};
+
+__device__ __forceinline__ void load8_plain(const BF16*, const void* p, int64_t i, float (&x)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + i);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(w[k] << 16);
+    x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8_plain(const F32*, const void* p, int64_t i, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+  const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// Same storage type: the bytes are copied.
+__device__ __forceinline__ void copy8(const BF16*, const void* s, int64_t si, void* d, int64_t di) {
+  *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(d) + di) =
+      *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(s) + si);
+}
+__device__ __forceinline__ void copy8(const F32*, const void* s, int64_t si, void* d, int64_t di) {
+  const float4* sp = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(s) + si);
+  float4* dp = reinterpret_cast<float4*>(reinterpret_cast<float*>(d) + di);
+  dp[0] = sp[0];
+  dp[1] = sp[1];
+}
+
+// e4m3 code of x / scale: float32 division (correctly rounded), clamp to the
+// largest finite magnitude (NaN passes), round to nearest even.
+__device__ __forceinline__ float fp8_prescale(float x, float scale) {
+  const float y = x / scale;
+  return y > 448.f ? 448.f : (y < -448.f ? -448.f : y);
+}
+__device__ __forceinline__ uint2 quant8_fp8(const float (&x)[8], float scale) {
+  float y[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = fp8_prescale(x[k], scale);
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+  return uint2{static_cast<uint32_t>(w0), static_cast<uint32_t>(w1)};
+}
+
+// KS: storage of the new K/V rows; KP: of the K/V pools; IT: of the index
+// keys (new rows and pool alike).
+template <class KS, class KP, class IT>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int t = blockIdx.y;
+  const int64_t slot = a.slots[t];
+  if (slot < 0 || slot >= a.num_pages * kBlock) return;
+  const int64_t page = slot / kBlock;
+  const int off = static_cast<int>(slot - page * kBlock);
+  const int vd = a.head_dim / 8;   // 8-element vectors per K/V row
+  const int vi = a.idx_dim / 8;    // per index row
+  const int n_kv = a.hkv * vd;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < 2 * n_kv) {
+    const bool is_v = i >= n_kv;
+    const int r = is_v ? i - n_kv : i;
+    const int h = r / vd;
+    const int c = r - h * vd;
+    const void* src = is_v ? a.v_new : a.k_new;
+    void* pool = is_v ? a.v_pool : a.k_pool;
+    const int64_t si = (static_cast<int64_t>(t) * a.hkv + h) * a.head_dim + c * 8;
+    const int64_t di = ((page * a.hkv + h) * kBlock + off) * a.head_dim + c * 8;
+    if constexpr (__is_same(KP, FP8)) {
+      float x[8];
+      load8_plain(static_cast<const KS*>(nullptr), src, si, x);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(pool) + di) =
+          quant8_fp8(x, is_v ? a.v_scale : a.k_scale);
+    } else {
+      copy8(static_cast<const KS*>(nullptr), src, si, pool, di);
+    }
+  } else if (i < 2 * n_kv + a.hidx * vi) {
+    const int r = i - 2 * n_kv;
+    const int h = r / vi;
+    const int c = r - h * vi;
+    const int64_t si = (static_cast<int64_t>(t) * a.hidx + h) * a.idx_dim + c * 8;
+    const int64_t di = ((page * a.hidx + h) * kBlock + off) * a.idx_dim + c * 8;
+    copy8(static_cast<const IT*>(nullptr), a.idx_k_new, si, a.idx_k_pool, di);
+  }
+}
+
+template <class KS, class KP>
+static void launch_append_i(const AppendArgs& a, int idx_dtype, dim3 grid, hipStream_t s) {
+  if (idx_dtype == 1) append_kernel<KS, KP, F32><<<grid, 256, 0, s>>>(a);
+  else append_kernel<KS, KP, BF16><<<grid, 256, 0, s>>>(a);
+}
+
+hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  const int per_token = 2 * a.hkv * (a.head_dim / 8) + a.hidx * (a.idx_dim / 8);
+  const dim3 grid((per_token + 255) / 256, a.num_tokens);
+  if (kv_dtype == 0) launch_append_i<BF16, BF16>(a, idx_dtype, grid, s);
+  else if (kv_dtype == 2) launch_append_i<BF16, FP8>(a, idx_dtype, grid, s);
+  else launch_append_i<F32, F32>(a, idx_dtype, grid, s);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -91,6 +91,21 @@ struct AttendArgs {
   uint32_t* tickets;         // [B * Hkv], zero on entry
 };
 
+// Paged append of new tokens (k_new/v_new [T, Hkv, D], idx_k_new [T, Hidx, Di]).
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const void* idx_k_new;
+  const int64_t* slots;      // [T] token slots; outside [0, num_pages * 128): skipped
+  int32_t num_tokens;
+  void* k_pool;              // [P, Hkv, 128, D]
+  void* v_pool;
+  void* idx_k_pool;          // [P, Hidx, 128, Di]
+  int64_t num_pages;
+  int32_t hkv, hidx, head_dim, idx_dim;
+  float k_scale, v_scale;    // fp8 pools only
+};
+
 // One prefill attention tile: up to kPrefillTileRows query rows of one k2q
 // list against its key block, resolved by the planning kernel.
 struct Tile {
@@ -155,6 +170,7 @@ hipError_t launch_decode_attend(const AttendArgs& a, int q_dtype, int kv_dtype,
 hipError_t launch_prefill_k2q(const PrefillAttnArgs& a, hipStream_t s);
 hipError_t launch_prefill_attend(const PrefillAttnArgs& a, int kv_dtype, int group,
                                  hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipStream_t s);
 hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale,
                               hipStream_t s);
 

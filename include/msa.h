@@ -202,6 +202,26 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q,
                                 size_t ws_bytes, void* stream);
 
 /*
+ * Paged append, the step before the path: the sglang page's backend writes
+ * the new tokens' K, V and index keys into its pool at out_cache_loc before
+ * it attends (minimax_sparse_backend.py, forward_decode / forward_extend).
+ * Token t's rows go to slot slot_mapping[t]: page s / 128, offset s % 128, of
+ * every head.  Slots outside [0, num_pages * 128) (e.g. -1 padding) are
+ * skipped; slots must be distinct (with a repeated slot, which token lands
+ * there is unspecified).
+ *   k_new, v_new [T, Hkv, D]: bf16 for bf16 and fp8 pools, f32 for f32 pools
+ *                (q_dtype); idx_k_new [T, Hidx, Di] in idx_dtype.
+ *   fp8 pools store e4m3fn(RNE(clamp(x / k_scale, +-448))) (v_scale for V;
+ *   the division in float32).
+ * num_tokens <= 65535 per call.  Nothing else is read or written.
+ */
+msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new,
+                           const void* v_new, const void* idx_k_new,
+                           const int64_t* slot_mapping, int32_t num_tokens,
+                           void* k_pool, void* v_pool, void* idx_k_pool,
+                           int64_t num_pages, void* stream);
+
+/*
  * fp8-e4m3 dequantisation exactly as the attention loaders do it (sglang
  * page: the sparse path dequantises an fp8 main KV cache on load):
  * out[i] = value(in[i]) * scale for n codes.
