@@ -34,7 +34,7 @@ import torch
 BLOCK = 128
 PAGE_CHUNK = 256
 
-# The five workloads the library is measured and checked on, by shape.
+# The workloads the library is measured and checked on, by shape.
 WORKLOADS = {
     "decode_b2_l2048": dict(
         kind="decode", B=2, seq_lens=("fixed", 2048), Hq=8, Hkv=1, Hidx=1,
@@ -53,9 +53,13 @@ WORKLOADS = {
         kind="decode", B=32, seq_lens=("fixed", 65536), Hq=16, Hkv=2, Hidx=2,
         D=128, Di=128, topk=32, init=1, local=2, q="bf16", kv="fp8", idx="bf16",
         k_scale=1.0 / 16, v_scale=1.0 / 16),
+    # multi-token decode (speculative verification): 4 new tokens per sequence
+    "verify_b32_q4_l32k": dict(
+        kind="prefill", B=32, n_new=4, prefix=32764, Hq=16, Hkv=2, Hidx=2,
+        D=128, Di=128, topk=16, init=1, local=2, q="bf16", kv="bf16", idx="bf16"),
 }
 
-# Seeds of the five workloads, in the order above.
+# Seeds of the workloads, in the order above.
 WORKLOAD_SEEDS = {name: 1001 + i for i, name in enumerate(WORKLOADS)}
 
 _TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}

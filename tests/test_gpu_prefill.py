@@ -92,6 +92,49 @@ def test_prefill_small(msa, name):
     print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
 
 
+# Multi-token decode (speculative verification): a few new tokens per
+# sequence over long contexts, causal among themselves, each with its own
+# selection -- the prefill call with short chunks.
+VERIFY = {
+    "q4_long": _spec([4] * 6, [30000, 999, 5000, 12000, 127, 70000], Hq=16, Hkv=2, Hidx=2,
+                     topk=16),
+    "ragged_q": _spec([1, 2, 3, 5, 8], [20000, 4000, 300, 9000, 130], Hq=8, Hkv=2, Hidx=1,
+                      topk=8),
+    "fp8_q3": _spec([3, 3, 3], [40000, 7000, 16000], Hq=16, Hkv=2, Hidx=2, kv="fp8", topk=32),
+}
+
+
+@pytest.mark.parametrize("name", list(VERIFY))
+def test_multi_token_decode(msa, name):
+    spec = VERIFY[name]
+    seed = 900 + sorted(VERIFY).index(name)
+    print(f"[verify] {name} seed={seed}", flush=True)
+    case = generate(spec, seed, device="cuda")
+    g = _run(msa, case, spec)
+    err, nband = _compare(host_view(case), g, spec, np.arange(case.T))
+    print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
+
+
+def test_single_token_chunks_match_decode(msa):
+    """A prefill of one new token per sequence is a decode step: the same
+    selection, bit for bit, and outputs that agree within the parity bounds
+    (the two paths split the keys differently)."""
+    spec = _spec([1] * 5, [33000, 4095, 128, 9000, 1], Hq=16, Hkv=2, Hidx=2, topk=16)
+    print("[verify_vs_decode] seed=950", flush=True)
+    case = generate(spec, 950, device="cuda")
+    g = _run(msa, case, spec)
+    cfg = msa.MsaConfig.from_spec(spec)
+    out_d, lse_d, sel_d, cnt_d = msa.sparse_decode(
+        cfg, case.q, case.idx_q, case.k_pool, case.v_pool, case.idx_k_pool, case.block_table,
+        case.seq_lens, return_selection=True)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_d, g["sel"]) and torch.equal(cnt_d, g["cnt"])
+    d = (out_d.float() - g["out"].float()).abs()
+    assert d.max().item() <= parity.BF16_MAX and d.mean().item() <= parity.BF16_MEAN
+    err, _ = _compare(host_view(case), dict(g, out=out_d, lse=lse_d), spec, np.arange(case.T))
+    print(f"  decode vs oracle: max {err[0]:.3g} mean {err[1]:.3g}", flush=True)
+
+
 def test_prefill_full_size_sampled(msa):
     """The full chunked-prefill workload (4 x 4096 new tokens over 16384); the
     oracle checks a sample of tokens from every sequence, including each
