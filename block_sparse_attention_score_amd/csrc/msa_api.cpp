@@ -144,8 +144,39 @@ DecodeLayout decode_layout(const msa_params_t& p, int32_t B, int32_t MB) {
 // Prefill workspace: scores, selection, split partials and tickets per token.
 // Key-major prefill attention (k2q lists) serves bf16 queries over bf16 or
 // fp8 pools; f32 runs the per-token split-K attention.
-bool prefill_key_major(const msa_params_t& p) {
-  return p.q_dtype == MSA_BF16 && (p.kv_dtype == MSA_BF16 || p.kv_dtype == MSA_FP8_E4M3);
+// Short chunks (multi-token decode, e.g. speculative verification: at most
+// kShortChunk new tokens per sequence on average) are scored by the page scan
+// with several queries per pass and attend per token with split-K; the
+// key-major lists and tiles pay off only for long chunks.  The choice depends
+// on shapes only, so workspace sizes stay a function of them.
+constexpr int kShortChunk = 8;
+bool short_chunks(int32_t B, int32_t T) { return int64_t(T) <= int64_t(kShortChunk) * B; }
+
+bool prefill_key_major(const msa_params_t& p, int32_t B, int32_t T) {
+  return !short_chunks(B, T) && p.q_dtype == MSA_BF16 &&
+         (p.kv_dtype == MSA_BF16 || p.kv_dtype == MSA_FP8_E4M3);
+}
+
+// Index scan of the short-chunk path (all queries of a sequence per pass).
+msa::ScoreArgs multi_score_args(const msa_params_t& p, const void* idx_q, const void* idx_k_pool,
+                                int64_t num_pages, const int32_t* block_table,
+                                int32_t max_blocks, const int32_t* seq_lens,
+                                const int32_t* cu_seqlens_q, int32_t num_seqs, float* scores) {
+  msa::ScoreArgs a{};
+  a.idx_q = idx_q;
+  a.idx_k = idx_k_pool;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.num_seqs = num_seqs;
+  a.hidx = p.num_idx_heads;
+  a.pages_per_item = kPagesPerItem;
+  a.chunks_per_pair = (max_blocks + kPagesPerItem - 1) / kPagesPerItem;
+  a.scores = scores;
+  a.fill_tail = 0;
+  return a;
 }
 
 struct PrefillLayout {
@@ -169,7 +200,7 @@ PrefillLayout prefill_layout(const msa_params_t& p, int32_t B, int32_t T, int32_
   l.scores = take(sizeof(float) * size_t(T) * p.num_idx_heads * MB);
   l.sel = take(sizeof(int32_t) * size_t(T) * p.num_idx_heads * kmax);
   l.cnt = take(sizeof(int32_t) * size_t(T) * p.num_idx_heads);
-  if (prefill_key_major(p)) {
+  if (prefill_key_major(p, B, T)) {
     const size_t lists = size_t(B) * p.num_idx_heads * MB;
     const size_t entries = size_t(T) * p.num_idx_heads * kmax;
     l.tq = msa::kPrefillTileRows / G;
@@ -360,6 +391,13 @@ msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
                                                      max_blocks, -INFINITY, s),
                     "score fill launch");
     if (st != MSA_OK) return st;
+    if (short_chunks(num_seqs, num_q_tokens)) {
+      const msa::ScoreArgs ma =
+          multi_score_args(*params, idx_q, idx_k_pool, num_pages, block_table, max_blocks,
+                           seq_lens, cu_seqlens_q, num_seqs, scores);
+      st = hip_status(msa::launch_multi_score(ma, params->idx_dim, s), "chunk scan launch");
+      return st == MSA_OK ? ok() : st;
+    }
     const msa::PrefillScoreArgs pa =
         prefill_score_args(*params, idx_q, idx_k_pool, num_pages, block_table, max_blocks,
                            seq_lens, cu_seqlens_q, num_seqs, num_q_tokens, scores);
@@ -559,7 +597,7 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
   int32_t* cnt = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + l.cnt);
   float* scores = reinterpret_cast<float*>(w + l.scores);
 
-  const bool key_major = prefill_key_major(p);
+  const bool key_major = prefill_key_major(p, num_seqs, num_q_tokens);
   if (key_major) {
     st = hip_status(msa::launch_fill_u32(reinterpret_cast<uint32_t*>(w + l.counts),
                                          2 * int64_t(num_seqs) * p.num_idx_heads * max_blocks,
@@ -572,11 +610,19 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
                     "ticket reset launch");
     if (st != MSA_OK) return st;
   }
-  // 1. scores (causal GEMM, block max)
-  const msa::PrefillScoreArgs pa =
-      prefill_score_args(p, idx_q, idx_k_pool, num_pages, block_table, max_blocks, seq_lens,
-                         cu_seqlens_q, num_seqs, num_q_tokens, scores);
-  st = hip_status(msa::launch_prefill_score(pa, p.idx_dim, s), "prefill score launch");
+  // 1. scores (short chunks: page scan, several queries per pass; long
+  //    chunks: causal GEMM with a block-max epilogue)
+  if (short_chunks(num_seqs, num_q_tokens)) {
+    const msa::ScoreArgs ma = multi_score_args(p, idx_q, idx_k_pool, num_pages, block_table,
+                                               max_blocks, seq_lens, cu_seqlens_q, num_seqs,
+                                               scores);
+    st = hip_status(msa::launch_multi_score(ma, p.idx_dim, s), "chunk scan launch");
+  } else {
+    const msa::PrefillScoreArgs pa =
+        prefill_score_args(p, idx_q, idx_k_pool, num_pages, block_table, max_blocks, seq_lens,
+                           cu_seqlens_q, num_seqs, num_q_tokens, scores);
+    st = hip_status(msa::launch_prefill_score(pa, p.idx_dim, s), "prefill score launch");
+  }
   if (st != MSA_OK) return st;
   // 2. per-token selection
   const msa::SelectArgs sa = select_args(p, scores, max_blocks, seq_lens, cu_seqlens_q, num_seqs,

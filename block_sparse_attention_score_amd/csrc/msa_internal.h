@@ -23,6 +23,9 @@ struct ScoreArgs {
   // words zeroed by workgroup 0 (hand-off counters of a later kernel), or nullptr
   uint32_t* zero_words;
   int32_t zero_count;
+  // short chunks (several queries per sequence): query rows of sequence b are
+  // cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1; nullptr for decode
+  const int32_t* cu_seqlens_q;
 };
 
 // Prefill index scoring (causal GEMM with a block-max epilogue).
@@ -160,6 +163,7 @@ struct PrefillAttnArgs {
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
 hipError_t launch_decode_score(const ScoreArgs& a, int idx_dtype, int idx_dim,
                                hipStream_t s);
+hipError_t launch_multi_score(const ScoreArgs& a, int idx_dim, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_prefill_score(const PrefillScoreArgs& a, int idx_dim, hipStream_t s);
 bool select_wave_fits(int max_blocks);

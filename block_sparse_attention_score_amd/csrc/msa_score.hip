@@ -14,6 +14,14 @@ __global__ __launch_bounds__(kWgThreads) void decode_score_kernel(ScoreArgs a) {
   score_chunk<IT, DI>(a, pair, blockIdx.x - pair * a.chunks_per_pair);
 }
 
+// Short chunks: one workgroup per (pair, chunk), every query of the pair's
+// sequence.
+template <class IT, int DI>
+__global__ __launch_bounds__(kWgThreads) void multi_score_kernel(ScoreArgs a) {
+  const int pair = blockIdx.x / a.chunks_per_pair;
+  score_chunk_multi<IT, DI, 4>(a, pair, blockIdx.x - pair * a.chunks_per_pair);
+}
+
 // One workgroup per (query token, index head) row.
 template <int MAXPER>
 __global__ __launch_bounds__(kWgThreads) void select_kernel(SelectArgs a) {
@@ -94,6 +102,14 @@ hipError_t launch_decode_score(const ScoreArgs& a, int idx_dtype, int idx_dim,
   } else {
     if (f32) launch_score_t<F32, 64>(a, s); else launch_score_t<BF16, 64>(a, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_multi_score(const ScoreArgs& a, int idx_dim, hipStream_t s) {
+  const int grid = a.num_seqs * a.hidx * a.chunks_per_pair;
+  if (grid == 0) return hipSuccess;
+  if (idx_dim == 128) multi_score_kernel<BF16, 128><<<grid, kWgThreads, 0, s>>>(a);
+  else multi_score_kernel<BF16, 64><<<grid, kWgThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

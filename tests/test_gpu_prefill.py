@@ -101,6 +101,9 @@ VERIFY = {
     "ragged_q": _spec([1, 2, 3, 5, 8], [20000, 4000, 300, 9000, 130], Hq=8, Hkv=2, Hidx=1,
                       topk=8),
     "fp8_q3": _spec([3, 3, 3], [40000, 7000, 16000], Hq=16, Hkv=2, Hidx=2, kv="fp8", topk=32),
+    # two query groups per scan pass, an empty chunk, a row of more than 1024 blocks
+    "groups_empty_long": _spec([7, 0, 9, 1], [3000, 500, 140000, 20], Hq=16, Hkv=1, Hidx=1,
+                               Di=64, topk=8),
 }
 
 
