@@ -319,6 +319,8 @@ def main():
     spec = workload(args.workload)
     if spec["kind"] == "prefill":
         return bench_prefill(args, spec)
+    if spec["kind"] == "append":
+        return bench_append(args, spec)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     case = generate(spec, WORKLOAD_SEEDS[args.workload], device=dev)
@@ -481,6 +483,9 @@ def bench_prefill(args, spec):
                                                    cu_seqlens_q=case.cu_seqlens_q),
                          args.steps).mean())
     attn_ms = max(ms - score_ms - sel_ms, 1e-6)
+    # short chunks (at most 8 new tokens per sequence on average) take the
+    # page-scan path: HBM-bound like decode
+    short = T <= 8 * B
     peak = 2500.0
     score_tf = f_score / (score_ms * 1e-3) / 1e12
     attn_tf = f_attn / (attn_ms * 1e-3) / 1e12
@@ -492,8 +497,18 @@ def bench_prefill(args, spec):
            {"kernel": "prefill_score_kernel (causal index-score GEMM)", "bound": "mfma",
             "achieved": score_tf, "peak": peak, "unit": "TFLOP/s", "frac": score_tf / peak,
             "traffic": None, "flops_per_launch": f_score, "ms_per_launch": score_ms}
+    if short:
+        idx_b, kv_b, small_b = chunk_touched_bytes(spec, lens, cu, sel.cpu().numpy(),
+                                                   cnt.cpu().numpy())
+        scan_b = idx_b + int(T * cfg.num_idx_heads * cfg.idx_dim * 2 + 4 * (B * MB))
+        roof = {"kernel": "multi_score_kernel (index-key scan, four queries per pass)",
+                "bound": "hbm", "achieved": scan_b / (score_ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": scan_b / (score_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                "bytes_per_launch": scan_b, "ms_per_launch": score_ms}
     res = {
-        "metric": "chunked-prefill tokens/sec at 1 MI355X",
+        "metric": ("multi-token decode tokens/sec + achieved HBM GB/s (touched bytes) at 1 "
+                   "MI355X") if short else "chunked-prefill tokens/sec at 1 MI355X",
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -517,9 +532,98 @@ def bench_prefill(args, spec):
         "roofline": roof,
         "device": torch.cuda.get_device_name(dev),
     }
+    if short:
+        total_b = idx_b + kv_b + small_b
+        res["hbm_gbps"] = total_b / (ms * 1e-3) / 1e9
+        res["hbm_frac"] = res["hbm_gbps"] / HBM_PEAK_GBS
+        res["touched_bytes"] = {"idx_keys": idx_b, "selected_kv_union": kv_b, "small": small_b}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(case, spec, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def bench_append(args, spec):
+    """Paged append (msa_append_kv): T new tokens' K, V and index keys into
+    the pools at seeded random slots, GB/s on the bytes it must move."""
+    import torch
+
+    import block_sparse_attention_score_amd as msa
+    from synth import WORKLOAD_SEEDS
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device="cpu").manual_seed(WORKLOAD_SEEDS[args.workload])
+    T, Hkv, Hidx, D, Di = spec["T"], spec["Hkv"], spec["Hidx"], spec["D"], spec["Di"]
+    P = (spec["pool_tokens"] + 127) // 128
+    kv = spec["kv"]
+    pool_dt = torch.uint8 if kv == "fp8" else torch.bfloat16
+    k_pool = torch.zeros((P, Hkv, 128, D), dtype=pool_dt, device=dev)
+    v_pool = torch.zeros_like(k_pool)
+    ik_pool = torch.zeros((P, Hidx, 128, Di), dtype=torch.bfloat16, device=dev)
+    k_new = torch.randn((T, Hkv, D), generator=g).to(torch.bfloat16).to(dev)
+    v_new = torch.randn((T, Hkv, D), generator=g).to(torch.bfloat16).to(dev)
+    ik_new = torch.randn((T, Hidx, Di), generator=g).to(torch.bfloat16).to(dev)
+    slots = torch.randperm(P * 128, generator=g)[:T].to(torch.int64).to(dev)
+    cfg = msa.MsaConfig.from_spec(spec)
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+
+    def step():
+        msa.append_kv(cfg, k_new, v_new, ik_new, slots, k_pool, v_pool, ik_pool)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        flush.fill_(i)
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ekv = elem_bytes(kv)
+    moved = T * (2 * Hkv * D * 2 + Hidx * Di * 2 + 8) + T * (2 * Hkv * D * ekv + Hidx * Di * 2)
+    gbps = moved / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "paged KV append tokens/sec + achieved HBM GB/s at 1 MI355X",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": kv, "data": "synthetic",
+        "config": {"workload": args.workload, "new_tokens": T, "pool_pages": P,
+                   "kv_heads": Hkv, "idx_heads": Hidx, "head_dim": D, "idx_dim": Di,
+                   "kv_dtype": kv, "page": 128, "parallelism": "none"},
+        "wall_s_timed_region": t_wall,
+        "roofline": {"kernel": "append_kernel", "bound": "hbm", "achieved": gbps,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_launch": moved, "ms_per_launch": ms},
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def chunk_touched_bytes(spec, seq_lens, cu, sel, cnt):
+    """Algorithmic bytes of a short-chunk (multi-token decode) step: the index
+    keys of every sequence once, the K/V of the union of its tokens' selected
+    blocks (valid tokens), the queries, outputs, tables and selections."""
+    Hq, Hkv, Hidx, D, Di = spec["Hq"], spec["Hkv"], spec["Hidx"], spec["D"], spec["Di"]
+    ekv = elem_bytes(spec["kv"])
+    gpi = Hkv // Hidx
+    idx_b = kv_b = 0
+    for b, L in enumerate(seq_lens.astype(np.int64)):
+        idx_b += int(Hidx * L * Di * 2)
+        for g in range(Hkv):
+            blocks = set()
+            for t in range(int(cu[b]), int(cu[b + 1])):
+                blocks.update(int(j) for j in sel[t, g // gpi, : cnt[t, g // gpi]])
+            kv_b += sum(min(128, int(L) - 128 * j) for j in blocks) * D * 2 * ekv
+    T = int(cu[-1])
+    nb = (seq_lens.astype(np.int64) + 127) // 128
+    small = int(T * Hq * D * 2 * 2 + T * Hidx * Di * 2 + 4 * (nb.sum() + Hkv * cnt.sum()))
+    return idx_b, kv_b, small
 
 
 def cpu_baseline_prefill(case, spec, seconds):
