@@ -78,12 +78,36 @@ def fp8_e4m3fn_table() -> np.ndarray:
     return tab
 
 
+def fp8_e5m2_table() -> np.ndarray:
+    """Values of the 256 OCP FP8 E5M2 codes.
+
+    Layout s.eeeee.mm, exponent bias 15; exponent field 0 encodes subnormals
+    m/4 * 2^-14; exponent field 31 encodes +-inf (m = 0) and NaN (m != 0), as
+    in IEEE binary16, of which E5M2 is the top byte.  The sglang page keeps
+    fp8 main caches in this format, as in E4M3, on its sparse path that
+    dequantises on load.
+    """
+    tab = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 2) & 0x1F
+        m = code & 0x3
+        if e == 0x1F:
+            tab[code] = sign * math.inf if m == 0 else math.nan
+        elif e == 0:
+            tab[code] = sign * (m / 4.0) * 2.0 ** (1 - 15)
+        else:
+            tab[code] = sign * (1.0 + m / 4.0) * 2.0 ** (e - 15)
+    return tab
+
+
 _FP8_TABLE = None
+_E5M2_TABLE = None
 
 
 def decode(arr: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
     """Stored representation -> float64 values (times ``scale`` for fp8)."""
-    global _FP8_TABLE
+    global _FP8_TABLE, _E5M2_TABLE
     if dtype == "bf16":
         return bf16_bits_to_f64(arr)
     if dtype == "f32":
@@ -92,6 +116,10 @@ def decode(arr: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
         if _FP8_TABLE is None:
             _FP8_TABLE = fp8_e4m3fn_table()
         return _FP8_TABLE[np.asarray(arr, dtype=np.uint8)] * float(scale)
+    if dtype == "fp8_e5m2":
+        if _E5M2_TABLE is None:
+            _E5M2_TABLE = fp8_e5m2_table()
+        return _E5M2_TABLE[np.asarray(arr, dtype=np.uint8)] * float(scale)
     raise ValueError(dtype)
 
 
@@ -351,14 +379,27 @@ def fp8_e4m3fn_encode(y: np.ndarray) -> np.ndarray:
     (its lowest bit clear); a negative value that rounds to zero keeps its
     sign (code 0x80).  NaN becomes the NaN code of its sign (0x7F / 0xFF).
     """
-    tab = fp8_e4m3fn_table()
+    return _encode_nearest(y, fp8_e4m3fn_table(), 0x7F, 0x7F)
+
+
+def fp8_e5m2_encode(y: np.ndarray) -> np.ndarray:
+    """float32 values -> e5m2 codes (uint8): the same rule as the e4m3
+    encoder over the E5M2 codes: clamp to +-57344 (the largest finite
+    magnitude, so the stored code saturates instead of becoming inf), nearest
+    code of the same sign, ties to the even mantissa; NaN -> 0x7F / 0xFF."""
+    return _encode_nearest(y, fp8_e5m2_table(), 0x7C, 0x7F)
+
+
+def _encode_nearest(y, tab, n_finite: int, nan_code: int) -> np.ndarray:
+    """Codes 0..n_finite-1 are the finite non-negative ones, ascending."""
+    top = float(tab[n_finite - 1])
     y32 = np.asarray(y, dtype=np.float32)
     flat = y32.reshape(-1)
     neg = np.signbit(flat)
     mag = np.abs(flat.astype(np.float64))
     nan = np.isnan(mag)
-    mag = np.minimum(np.where(nan, 0.0, mag), 448.0)
-    codes = np.arange(0x7F)                  # finite non-negative codes 0x00..0x7E
+    mag = np.minimum(np.where(nan, 0.0, mag), top)
+    codes = np.arange(n_finite)              # finite non-negative codes
     vals = tab[codes]                        # ascending magnitudes
     dist = np.abs(mag[:, None] - vals[None, :])
     best = dist.min(axis=1, keepdims=True)
@@ -366,7 +407,7 @@ def fp8_e4m3fn_encode(y: np.ndarray) -> np.ndarray:
     even = cand & ((codes[None, :] & 1) == 0)
     pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
     out = codes[pick].astype(np.uint8)
-    out = np.where(nan, np.uint8(0x7F), out)
+    out = np.where(nan, np.uint8(nan_code), out)
     out = np.where(neg, out | np.uint8(0x80), out).astype(np.uint8)
     return out.reshape(y32.shape)
 
@@ -376,10 +417,10 @@ def store_values(src: np.ndarray, src_dtype: str, pool_dtype: str, scale: float 
     pool's stored representation."""
     if pool_dtype == src_dtype:
         return np.array(src, copy=True)
-    if pool_dtype == "fp8" and src_dtype == "bf16":
+    if pool_dtype in ("fp8", "fp8_e5m2") and src_dtype == "bf16":
         x32 = decode(src, "bf16").astype(np.float32)   # exact
         y32 = x32 / np.float32(scale)                  # IEEE float32 division
-        return fp8_e4m3fn_encode(y32)
+        return fp8_e4m3fn_encode(y32) if pool_dtype == "fp8" else fp8_e5m2_encode(y32)
     raise ValueError((src_dtype, pool_dtype))
 
 

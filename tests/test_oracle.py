@@ -446,7 +446,7 @@ def test_fp8_encode_round_trip_ties_and_saturation():
     assert oracle.fp8_e4m3fn_encode(np.float32([2.0 ** -11]))[0] == 0x00
 
 
-@pytest.mark.parametrize("kv", ["bf16", "f32", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "f32", "fp8", "fp8_e5m2"])
 def test_append_kv_oracle(kv):
     """append_kv writes token t's rows at page slot//128, offset slot%128 of
     every head, leaves all other rows untouched and skips slots outside the
@@ -460,7 +460,7 @@ def test_append_kv_oracle(kv):
         x = rng.standard_normal(shape).astype(np.float32)
         return x if dt == "f32" else (x.view(np.uint32) >> 16).astype(np.uint16)
 
-    pool_dt = {"bf16": np.uint16, "f32": np.float32, "fp8": np.uint8}[kv]
+    pool_dt = {"bf16": np.uint16, "f32": np.float32, "fp8": np.uint8, "fp8_e5m2": np.uint8}[kv]
     k_pool = rng.integers(0, 2 ** 7, (P, Hkv, 128, D)).astype(pool_dt)
     v_pool = rng.integers(0, 2 ** 7, (P, Hkv, 128, D)).astype(pool_dt)
     ik_pool = rand_src((P, Hidx, 128, Di), "bf16")
@@ -477,11 +477,13 @@ def test_append_kv_oracle(kv):
             page, off = divmod(int(s), 128)
             written[page, off] = True
             assert np.array_equal(ik2[page, :, off], ik_new[t])
-            if kv == "fp8":
+            if kv.startswith("fp8"):
+                tdt, top = ((torch.float8_e4m3fn, 448.0) if kv == "fp8"
+                            else (torch.float8_e5m2, 57344.0))
                 for pool, new, sc in ((k2, k_new, ks), (v2, v_new, vs)):
                     want = torch.from_numpy(
                         (oracle.decode(new[t], "bf16").astype(np.float32) / np.float32(sc))
-                        .clip(-448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+                        .clip(-top, top)).to(tdt).view(torch.uint8).numpy()
                     assert np.array_equal(pool[page, :, off], want)
             else:
                 assert np.array_equal(k2[page, :, off], k_new[t])
@@ -492,3 +494,32 @@ def test_append_kv_oracle(kv):
     x = oracle.fp8_e4m3fn_table()[[0x01, 0x22, 0x38, 0x5C, 0xB3, 0xFE]].astype(np.float32) / 16
     xb = (x.view(np.uint32) >> 16).astype(np.uint16)
     assert np.array_equal(oracle.decode(oracle.store_values(xb, "bf16", "fp8", 1 / 16), "fp8", 1 / 16), x)
+
+
+def test_fp8_e5m2_table_matches_torch_all_codes():
+    """The E5M2 table (from the format definition) against torch's
+    float8_e5m2 -> float32 cast of all 256 codes, NaN codes included."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e5m2).to(torch.float32).double().numpy()
+    mine = oracle.fp8_e5m2_table()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(mine[fin], ref[fin])
+    # hand values: 1.0, the largest finite, the smallest subnormal, infinities
+    assert mine[0x3C] == 1.0 and mine[0x7B] == 57344.0 and mine[0x01] == 2.0 ** -16
+    assert mine[0x7C] == math.inf and mine[0xFC] == -math.inf
+
+
+def test_fp8_e5m2_encode_matches_torch_cast():
+    rng = np.random.default_rng(9)
+    n = 30000
+    y = (rng.standard_normal(n) * np.exp(rng.uniform(-20.0, 13.0, n))).astype(np.float32)
+    tab = oracle.fp8_e5m2_table()
+    fin = tab[:0x7C]
+    mids = ((fin[:-1] + fin[1:]) / 2.0).astype(np.float32)
+    y = np.concatenate([y, mids, -mids, np.float32([0.0, -0.0, 57344.0, 1e30, -1e30])])
+    mine = oracle.fp8_e5m2_encode(y)
+    ref = torch.from_numpy(np.clip(y, -57344.0, 57344.0)).to(torch.float8_e5m2).view(torch.uint8)
+    assert np.array_equal(mine, ref.numpy())
+    codes = np.array([c for c in range(256) if np.isfinite(tab[c])], dtype=np.int64)
+    assert np.array_equal(oracle.fp8_e5m2_encode(tab[codes].astype(np.float32)), codes)
