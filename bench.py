@@ -52,7 +52,7 @@ def parse():
 
 
 def elem_bytes(dt: str) -> int:
-    return {"bf16": 2, "f32": 4, "fp8": 1}[dt]
+    return {"bf16": 2, "f32": 4, "fp8": 1, "fp8_e5m2": 1}[dt]
 
 
 def step_bytes(spec, seq_lens, sel, cnt):
@@ -556,7 +556,7 @@ def bench_append(args, spec):
     T, Hkv, Hidx, D, Di = spec["T"], spec["Hkv"], spec["Hidx"], spec["D"], spec["Di"]
     P = (spec["pool_tokens"] + 127) // 128
     kv = spec["kv"]
-    pool_dt = torch.uint8 if kv == "fp8" else torch.bfloat16
+    pool_dt = torch.uint8 if kv.startswith("fp8") else torch.bfloat16
     k_pool = torch.zeros((P, Hkv, 128, D), dtype=pool_dt, device=dev)
     v_pool = torch.zeros_like(k_pool)
     ik_pool = torch.zeros((P, Hidx, 128, Di), dtype=torch.bfloat16, device=dev)

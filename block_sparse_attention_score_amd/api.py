@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import MSA_BF16, MSA_F32, MSA_FP8_E4M3, Params, check, load
+from ._lib import MSA_BF16, MSA_F32, MSA_FP8_E4M3, MSA_FP8_E5M2, Params, check, load
 
 BLOCK = 128
 
@@ -46,7 +46,8 @@ class MsaConfig:
         return self.topk + self.init_blocks + self.local_blocks
 
     def params(self) -> Params:
-        code = {"bf16": MSA_BF16, "f32": MSA_F32, "fp8": MSA_FP8_E4M3}
+        code = {"bf16": MSA_BF16, "f32": MSA_F32, "fp8": MSA_FP8_E4M3,
+                "fp8_e5m2": MSA_FP8_E5M2}
         return Params(self.num_q_heads, self.num_kv_heads, self.num_idx_heads, self.head_dim,
                       self.idx_dim, self.block_size, self.topk, self.init_blocks,
                       self.local_blocks, self.softmax_scale, code[self.q_dtype],

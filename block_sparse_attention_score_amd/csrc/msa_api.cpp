@@ -37,6 +37,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int kmax_of(const msa_params_t& p) { return p.topk + p.init_blocks + p.local_blocks; }
 int group_of(const msa_params_t& p) { return p.num_q_heads / p.num_kv_heads; }
 
+bool is_fp8(int dtype) { return dtype == MSA_FP8_E4M3 || dtype == MSA_FP8_E5M2; }
+
 msa_status_t check_params(const msa_params_t* p) {
   if (p == nullptr) return fail(MSA_ERR_INVALID_ARG, "params is NULL");
   if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_idx_heads <= 0)
@@ -68,13 +70,14 @@ msa_status_t check_params(const msa_params_t* p) {
     return fail(MSA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
   const bool qkv_ok = (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_BF16) ||
                       (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_FP8_E4M3) ||
+                      (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_FP8_E5M2) ||
                       (p->q_dtype == MSA_F32 && p->kv_dtype == MSA_F32);
   if (!qkv_ok)
     return fail(MSA_ERR_UNSUPPORTED, "(q_dtype=%d, kv_dtype=%d) not supported", p->q_dtype,
                 p->kv_dtype);
   if (p->idx_dtype != MSA_BF16 && p->idx_dtype != MSA_F32)
     return fail(MSA_ERR_UNSUPPORTED, "idx_dtype=%d not supported", p->idx_dtype);
-  if (p->kv_dtype == MSA_FP8_E4M3 &&
+  if (is_fp8(p->kv_dtype) &&
       (!std::isfinite(p->k_scale) || !std::isfinite(p->v_scale) || p->k_scale <= 0.f ||
        p->v_scale <= 0.f))
     return fail(MSA_ERR_INVALID_ARG, "fp8 k_scale/v_scale must be finite and > 0");
@@ -154,7 +157,7 @@ bool short_chunks(int32_t B, int32_t T) { return int64_t(T) <= int64_t(kShortChu
 
 bool prefill_key_major(const msa_params_t& p, int32_t B, int32_t T) {
   return !short_chunks(B, T) && p.q_dtype == MSA_BF16 &&
-         (p.kv_dtype == MSA_BF16 || p.kv_dtype == MSA_FP8_E4M3);
+         (p.kv_dtype == MSA_BF16 || is_fp8(p.kv_dtype));
 }
 
 // Index scan of the short-chunk path (all queries of a sequence per pass).
@@ -316,9 +319,9 @@ msa::AttendArgs attend_args(const msa_params_t& p, const void* q, const void* k_
   a.hidx = p.num_idx_heads;
   a.bps = l.bps;
   a.nsplit_max = l.nsplit_max;
-  const float ks = p.kv_dtype == MSA_FP8_E4M3 ? p.k_scale : 1.f;
+  const float ks = is_fp8(p.kv_dtype) ? p.k_scale : 1.f;
   a.qk_scale_log2 = softmax_scale_of(p) * ks * 1.4426950408889634f;
-  a.v_scale = p.kv_dtype == MSA_FP8_E4M3 ? p.v_scale : 1.f;
+  a.v_scale = is_fp8(p.kv_dtype) ? p.v_scale : 1.f;
   a.out = out;
   a.lse_out = lse_out;
   a.part_o = reinterpret_cast<float*>(w + l.part_o);
@@ -555,8 +558,8 @@ msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new, const 
   a.hidx = params->num_idx_heads;
   a.head_dim = params->head_dim;
   a.idx_dim = params->idx_dim;
-  a.k_scale = params->kv_dtype == MSA_FP8_E4M3 ? params->k_scale : 1.f;
-  a.v_scale = params->kv_dtype == MSA_FP8_E4M3 ? params->v_scale : 1.f;
+  a.k_scale = is_fp8(params->kv_dtype) ? params->k_scale : 1.f;
+  a.v_scale = is_fp8(params->kv_dtype) ? params->v_scale : 1.f;
   st = hip_status(msa::launch_append(a, params->kv_dtype, params->idx_dtype,
                                      static_cast<hipStream_t>(stream)),
                   "append launch");
@@ -655,9 +658,9 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
     ka.items = reinterpret_cast<msa::Tile*>(w + l.items);
     ka.n_items = reinterpret_cast<int32_t*>(w + l.n_items);
     ka.max_items = l.max_items;
-    const float ks = p.kv_dtype == MSA_FP8_E4M3 ? p.k_scale : 1.f;
+    const float ks = is_fp8(p.kv_dtype) ? p.k_scale : 1.f;
     ka.qk_scale_log2 = softmax_scale_of(p) * ks * 1.4426950408889634f;
-    ka.v_scale = p.kv_dtype == MSA_FP8_E4M3 ? p.v_scale : 1.f;
+    ka.v_scale = is_fp8(p.kv_dtype) ? p.v_scale : 1.f;
     ka.part_o = reinterpret_cast<uint16_t*>(w + l.part_o);
     ka.part_lse = reinterpret_cast<float*>(w + l.part_lse);
     ka.sink_o = reinterpret_cast<uint16_t*>(w + l.sink);
@@ -688,9 +691,9 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
   aa.hidx = p.num_idx_heads;
   aa.bps = l.bps;
   aa.nsplit_max = l.nsplit_max;
-  const float ks = p.kv_dtype == MSA_FP8_E4M3 ? p.k_scale : 1.f;
+  const float ks = is_fp8(p.kv_dtype) ? p.k_scale : 1.f;
   aa.qk_scale_log2 = softmax_scale_of(p) * ks * 1.4426950408889634f;
-  aa.v_scale = p.kv_dtype == MSA_FP8_E4M3 ? p.v_scale : 1.f;
+  aa.v_scale = is_fp8(p.kv_dtype) ? p.v_scale : 1.f;
   aa.out = out;
   aa.lse_out = lse_out;
   aa.part_o = reinterpret_cast<float*>(w + l.part_o);

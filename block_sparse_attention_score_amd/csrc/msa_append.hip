@@ -2,9 +2,10 @@
 // at their token slots (the sglang page minimax_sparse_backend.py stores the
 // new tokens into its pool at out_cache_loc before it attends; slot s is
 // page s / 128, offset s % 128 of the head-major pages here).  fp8 pools
-// receive the e4m3 code of x / scale (per-tensor k_scale / v_scale, the vLLM
-// page's fp8 cache scales): float32 division, clamp to +-448, round to
-// nearest even by the gfx950 conversion instruction.
+// receive the e4m3 (or e5m2) code of x / scale (per-tensor k_scale / v_scale,
+// the vLLM page's fp8 cache scales): float32 division, clamp to the format's
+// largest finite value (448 / 57344), round to nearest even by the gfx950
+// conversion instruction.
 //
 // One thread moves 8 consecutive elements of one row (16-byte bf16 loads);
 // a token's rows (Hkv K rows, Hkv V rows, Hidx index rows) are spread over
@@ -64,7 +65,7 @@ __device__ __forceinline__ float fp8_prescale(float x, float scale) {
   const float y = x / scale;
   return y > 448.f ? 448.f : (y < -448.f ? -448.f : y);
 }
-__device__ __forceinline__ uint2 quant8_fp8(const float (&x)[8], float scale) {
+__device__ __forceinline__ uint2 quant8(const FP8*, const float (&x)[8], float scale) {
   float y[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) y[k] = fp8_prescale(x[k], scale);
@@ -72,6 +73,21 @@ __device__ __forceinline__ uint2 quant8_fp8(const float (&x)[8], float scale) {
   w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
   int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
   w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+  return uint2{static_cast<uint32_t>(w0), static_cast<uint32_t>(w1)};
+}
+// e5m2: clamp to its largest finite magnitude, 57344 (the code saturates
+// rather than becoming inf), then round to nearest even.
+__device__ __forceinline__ uint2 quant8(const BF8*, const float (&x)[8], float scale) {
+  float y[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float v = x[k] / scale;
+    y[k] = v > 57344.f ? 57344.f : (v < -57344.f ? -57344.f : v);
+  }
+  int w0 = __builtin_amdgcn_cvt_pk_bf8_f32(y[0], y[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_bf8_f32(y[2], y[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_bf8_f32(y[4], y[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_bf8_f32(y[6], y[7], w1, true);
   return uint2{static_cast<uint32_t>(w0), static_cast<uint32_t>(w1)};
 }
 
@@ -97,11 +113,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     void* pool = is_v ? a.v_pool : a.k_pool;
     const int64_t si = (static_cast<int64_t>(t) * a.hkv + h) * a.head_dim + c * 8;
     const int64_t di = ((page * a.hkv + h) * kBlock + off) * a.head_dim + c * 8;
-    if constexpr (__is_same(KP, FP8)) {
+    if constexpr (__is_same(KP, FP8) || __is_same(KP, BF8)) {
       float x[8];
       load8_plain(static_cast<const KS*>(nullptr), src, si, x);
       *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(pool) + di) =
-          quant8_fp8(x, is_v ? a.v_scale : a.k_scale);
+          quant8(static_cast<const KP*>(nullptr), x, is_v ? a.v_scale : a.k_scale);
     } else {
       copy8(static_cast<const KS*>(nullptr), src, si, pool, di);
     }
@@ -127,6 +143,7 @@ hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipSt
   const dim3 grid((per_token + 255) / 256, a.num_tokens);
   if (kv_dtype == 0) launch_append_i<BF16, BF16>(a, idx_dtype, grid, s);
   else if (kv_dtype == 2) launch_append_i<BF16, FP8>(a, idx_dtype, grid, s);
+  else if (kv_dtype == 3) launch_append_i<BF16, BF8>(a, idx_dtype, grid, s);
   else launch_append_i<F32, F32>(a, idx_dtype, grid, s);
   return hipGetLastError();
 }

@@ -106,6 +106,10 @@ struct Row<FP8> {
   Raw8<FP8> c[4];
 };
 template <>
+struct Row<BF8> {
+  Raw8<BF8> c[4];
+};
+template <>
 struct Row<F32> {
   f32x4v_t c[8];
 };
@@ -119,6 +123,11 @@ __device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, 
 #pragma unroll
   for (int c = 0; c < 4; ++c)
     r.c[c] = load_raw(static_cast<const FP8*>(nullptr), pool, row0 + 32 * c + 8 * q);
+}
+__device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, Row<BF8>& r) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    r.c[c] = load_raw(static_cast<const BF8*>(nullptr), pool, row0 + 32 * c + 8 * q);
 }
 __device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, Row<F32>& r) {
 #pragma unroll
@@ -147,6 +156,10 @@ __device__ __forceinline__ bf16x8_t fp8_to_bf16x8(const Raw8<FP8>& r) {
 }
 __device__ __forceinline__ bf16x8_t as_bf16(const bf16x8_t& v) { return v; }
 __device__ __forceinline__ bf16x8_t as_bf16(const Raw8<FP8>& v) { return fp8_to_bf16x8(v); }
+__device__ __forceinline__ bf16x8_t fp8_to_bf16x8(const Raw8<BF8>& r) {
+  return bf8x8_to_bf16x8(r.v.x, r.v.y);
+}
+__device__ __forceinline__ bf16x8_t as_bf16(const Raw8<BF8>& v) { return fp8_to_bf16x8(v); }
 
 // S^T tile (16 tokens x 16 heads): lane holds S^T[4q + r][lane % 16].
 __device__ __forceinline__ f32x4_t st_tile(const QFrag<BF16>& qf, const Row<BF16>& k) {
@@ -155,7 +168,8 @@ __device__ __forceinline__ f32x4_t st_tile(const QFrag<BF16>& qf, const Row<BF16
   for (int c = 0; c < 4; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k.c[c], qf.a[c], acc, 0, 0, 0);
   return acc;
 }
-__device__ __forceinline__ f32x4_t st_tile(const QFrag<BF16>& qf, const Row<FP8>& k) {
+template <class K8>
+__device__ __forceinline__ f32x4_t st_tile(const QFrag<BF16>& qf, const Row<K8>& k) {
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < 4; ++c)
@@ -182,7 +196,8 @@ __device__ __forceinline__ f32x4_t vt_tile(const Row<BF16>& v, int m, const bf16
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(v.c[m >> 1], sel[m & 1], f32x4_t{0.f, 0.f, 0.f, 0.f},
                                                  0, 0, 0);
 }
-__device__ __forceinline__ f32x4_t vt_tile(const Row<FP8>& v, int m, const bf16x8_t (&sel)[2]) {
+template <class K8>
+__device__ __forceinline__ f32x4_t vt_tile(const Row<K8>& v, int m, const bf16x8_t (&sel)[2]) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8_to_bf16x8(v.c[m >> 1]), sel[m & 1],
                                                  f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 }

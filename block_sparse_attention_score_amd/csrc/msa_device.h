@@ -18,7 +18,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // Storage tags.
 struct BF16 {};
 struct F32 {};
-struct FP8 {};
+struct FP8 {};   // OCP fp8 E4M3 ("e4m3fn") codes
+struct BF8 {};   // OCP fp8 E5M2 codes
 
 // ---------------------------------------------------------------- loads
 
@@ -36,6 +37,10 @@ struct Raw8<F32> {
 };
 template <>
 struct Raw8<FP8> {
+  uint2 v;
+};
+template <>
+struct Raw8<BF8> {
   uint2 v;
 };
 
@@ -92,6 +97,21 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* x) {
 __device__ __forceinline__ void unpack(const Raw8<FP8>& r, float (&x)[8]) {
   fp8x4_to_f32(r.v.x, x);
   fp8x4_to_f32(r.v.y, x + 4);
+}
+__device__ __forceinline__ Raw8<BF8> load_raw(const BF8*, const void* base, int64_t idx) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(
+      reinterpret_cast<const uint8_t*>(base) + idx));
+  return {uint2{v.x, v.y}};
+}
+// OCP e5m2 codes -> float (gfx950 conversion, two codes per instruction).
+__device__ __forceinline__ void bf8x4_to_f32(uint32_t w, float* x) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), true);
+  x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
+}
+__device__ __forceinline__ void unpack(const Raw8<BF8>& r, float (&x)[8]) {
+  bf8x4_to_f32(r.v.x, x);
+  bf8x4_to_f32(r.v.y, x + 4);
 }
 
 template <class T>
@@ -153,6 +173,17 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
   const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
   const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight fp8-e5m2 codes to bf16, exactly (every e5m2 value, subnormals and
+// infinities included, is a bf16 value): the gfx950 packed conversion.
+__device__ __forceinline__ bf16x8_t bf8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, 1.0f, true);
   return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 

@@ -91,6 +91,10 @@ template <>
 struct RawOf<FP8> {
   typedef uint8_t elem;
 };
+template <>
+struct RawOf<BF8> {
+  typedef uint8_t elem;
+};
 // Eight elements at byte offset voff + soff of a run, as bf16.
 __device__ __forceinline__ bf16x8_t load8_buf(const BF16*, __amdgpu_buffer_rsrc_t r, uint32_t voff,
                                               uint32_t soff) {
@@ -100,6 +104,11 @@ __device__ __forceinline__ bf16x8_t load8_buf(const FP8*, __amdgpu_buffer_rsrc_t
                                               uint32_t soff) {
   const auto raw = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
   return fp8x8_to_bf16x8(raw[0], raw[1]);
+}
+__device__ __forceinline__ bf16x8_t load8_buf(const BF8*, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
+  const auto raw = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return bf8x8_to_bf16x8(raw[0], raw[1]);
 }
 
 // Clears v unless keep, without a branch.
@@ -712,6 +721,7 @@ hipError_t launch_prefill_attend(const PrefillAttnArgs& a, int kv_dtype, int gro
   if (a.max_items > 0) {
     if (kv_dtype == 0) ok = launch_pf_attend_g<BF16>(a, group, s);
     else if (kv_dtype == 2) ok = launch_pf_attend_g<FP8>(a, group, s);
+    else if (kv_dtype == 3) ok = launch_pf_attend_g<BF8>(a, group, s);
     if (!ok) return hipErrorInvalidValue;
   }
   // 16 / G (token, kv head) units per combine workgroup

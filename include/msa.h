@@ -78,7 +78,10 @@ typedef enum {
 typedef enum {
   MSA_BF16 = 0,
   MSA_F32 = 1,
-  MSA_FP8_E4M3 = 2 /* OCP e4m3 ("e4m3fn"): bias 7, no inf, S.1111.111 = NaN */
+  MSA_FP8_E4M3 = 2, /* OCP e4m3 ("e4m3fn"): bias 7, no inf, S.1111.111 = NaN */
+  MSA_FP8_E5M2 = 3  /* OCP e5m2: bias 15, S.11111.00 = inf, other S.11111.xx NaN
+                       (the sglang page keeps fp8 main caches of either format
+                       on its sparse path that dequantises on load) */
 } msa_dtype_t;
 
 /*
@@ -88,7 +91,8 @@ typedef enum {
  *   block_size == 128 (page size == block size), head_dim == 128,
  *   idx_dim in {64, 128}, topk in {4, 8, 16, 32}, 0 <= init, local <= 64,
  *   Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8, 16}, Hkv % Hidx == 0,
- *   (q_dtype, kv_dtype) in {(bf16, bf16), (bf16, fp8_e4m3), (f32, f32)},
+ *   (q_dtype, kv_dtype) in {(bf16, bf16), (bf16, fp8_e4m3), (bf16, fp8_e5m2),
+ *   (f32, f32)},
  *   idx_dtype in {bf16, f32} (idx_q and idx_k share it).
  */
 typedef struct {
@@ -212,7 +216,7 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q,
  *   k_new, v_new [T, Hkv, D]: bf16 for bf16 and fp8 pools, f32 for f32 pools
  *                (q_dtype); idx_k_new [T, Hidx, Di] in idx_dtype.
  *   fp8 pools store e4m3fn(RNE(clamp(x / k_scale, +-448))) (v_scale for V;
- *   the division in float32).
+ *   the division in float32); e5m2 pools the same with +-57344.
  * num_tokens <= 65535 per call.  Nothing else is read or written.
  */
 msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new,

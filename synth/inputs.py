@@ -57,6 +57,11 @@ WORKLOADS = {
     "verify_b32_q4_l32k": dict(
         kind="prefill", B=32, n_new=4, prefix=32764, Hq=16, Hkv=2, Hidx=2,
         D=128, Di=128, topk=16, init=1, local=2, q="bf16", kv="bf16", idx="bf16"),
+    # fp8-e5m2 K/V pools (the other fp8 cache format of the sglang page)
+    "decode_e5m2_b32_l64k": dict(
+        kind="decode", B=32, seq_lens=("fixed", 65536), Hq=16, Hkv=2, Hidx=2,
+        D=128, Di=128, topk=32, init=1, local=2, q="bf16", kv="fp8_e5m2", idx="bf16",
+        k_scale=1.0 / 16, v_scale=1.0 / 16),
     # paged append of a 4 x 4096-token chunk into pools of 4 x 20480 tokens
     # (the step before the path; slots in a seeded random order)
     "append_4x4096": dict(
@@ -71,7 +76,8 @@ WORKLOADS = {
 # Seeds of the workloads, in the order above.
 WORKLOAD_SEEDS = {name: 1001 + i for i, name in enumerate(WORKLOADS)}
 
-_TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn}
+_TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn,
+             "fp8_e5m2": torch.float8_e5m2}
 _POISON_KV = {"bf16": float("nan"), "f32": float("nan")}
 FP8_NAN_BYTE = 0x7F
 IDX_POISON = 1.0e4
@@ -141,11 +147,14 @@ def _quantise(x: torch.Tensor, dtype: str, scale: float) -> torch.Tensor:
     if dtype == "fp8":
         y = (x / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
         return y.view(torch.uint8)
+    if dtype == "fp8_e5m2":
+        y = (x / scale).clamp_(-57344.0, 57344.0).to(torch.float8_e5m2)
+        return y.view(torch.uint8)
     return x.to(_TORCH_DT[dtype])
 
 
 def _draw_pool(P, H, Dm, dtype, scale, g, device) -> torch.Tensor:
-    out_dt = torch.uint8 if dtype == "fp8" else _TORCH_DT[dtype]
+    out_dt = torch.uint8 if dtype.startswith("fp8") else _TORCH_DT[dtype]
     pool = torch.empty((P, H, BLOCK, Dm), dtype=out_dt, device=device)
     for p0 in range(0, P, PAGE_CHUNK):
         p1 = min(P, p0 + PAGE_CHUNK)
@@ -160,8 +169,8 @@ def _poison(pool: torch.Tensor, valid: torch.Tensor, dtype: str, value: float):
     tok = torch.arange(BLOCK, device=pool.device)
     bad = tok[None, :] >= valid.to(pool.device)[:, None]          # [P,128]
     bad = bad[:, None, :, None].expand(pool.shape)
-    if dtype == "fp8":
-        pool.masked_fill_(bad, FP8_NAN_BYTE)
+    if dtype.startswith("fp8"):
+        pool.masked_fill_(bad, FP8_NAN_BYTE)   # NaN in e4m3 and in e5m2
     else:
         pool.masked_fill_(bad, value)
 

@@ -35,6 +35,8 @@ CASES = {
     "f32": ("f32", "f32", 2, 1, 128, 1.0, 1.0),
     "fp8": ("fp8", "bf16", 2, 2, 128, 1 / 16, 1 / 16),
     "fp8_odd_scales": ("fp8", "bf16", 1, 1, 64, 0.37, 0.11),
+    "fp8_e5m2": ("fp8_e5m2", "bf16", 2, 2, 128, 1 / 16, 1 / 16),
+    "fp8_e5m2_odd_scales": ("fp8_e5m2", "bf16", 1, 1, 64, 0.37, 0.011),
 }
 
 
@@ -51,11 +53,12 @@ def test_append_matches_oracle_bytes(msa, name):
         # N(0,1), with some rows far outside e4m3's range and some tiny
         x = torch.randn(shape, generator=g)
         x[::7] *= 300.0
+        x[5::13] *= 3e4          # past e5m2's largest finite value once scaled
         x[3::11] *= 1e-4
         return x.to(dt)
 
     def pool(shape, dt):
-        if dt == "fp8":
+        if dt.startswith("fp8"):
             return torch.randint(0, 256, shape, generator=g, dtype=torch.uint8)
         return torch.randn(shape, generator=g).to(src_dt if dt != "idx" else idx_dt)
 
@@ -64,7 +67,7 @@ def test_append_matches_oracle_bytes(msa, name):
     ik_pool = pool((P, Hidx, 128, Di), "idx")
     k_new, v_new = new_rows((T, Hkv, D), src_dt), new_rows((T, Hkv, D), src_dt)
     # exact ties of e4m3 rounding in the fp8 cases: midpoints of neighbouring codes times scale
-    tab = oracle.fp8_e4m3fn_table()
+    tab = oracle.fp8_e5m2_table() if kv == "fp8_e5m2" else oracle.fp8_e4m3fn_table()
     mids = torch.tensor((tab[0x10:0x20] + tab[0x11:0x21]) / 2.0, dtype=torch.float32)
     k_new[0, 0, :16] = (mids * ks).to(src_dt)
     ik_new = new_rows((T, Hidx, Di), idx_dt)

@@ -31,7 +31,7 @@ def _spec(B, lens, Hq=8, Hkv=2, Hidx=1, Di=128, topk=4, init=1, local=2, q="bf16
           kv="bf16", idx="bf16", scale=None):
     s = dict(kind="decode", B=B, seq_lens=list(lens), Hq=Hq, Hkv=Hkv, Hidx=Hidx, D=128, Di=Di,
              topk=topk, init=init, local=local, q=q, kv=kv, idx=idx)
-    if kv == "fp8":
+    if kv.startswith("fp8"):
         s.update(k_scale=1.0 / 16 if scale is None else scale[0],
                  v_scale=1.0 / 16 if scale is None else scale[1])
     return s
@@ -266,5 +266,24 @@ def test_decode_maximum_sizes(msa):
     print("[decode_max] seed=31", flush=True)
     case, cfg, g = _run(msa, spec, 31)
     assert case.max_blocks == 8192
+    err, nband = _compare(host_view(case), g, spec)
+    print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
+
+
+E5M2 = {
+    "e5m2_small": _spec(3, [3000, 7000, 12345], Hq=16, Hkv=2, Hidx=2, kv="fp8_e5m2", topk=8),
+    "e5m2_odd_scales_long": _spec(2, [40000, 150000], Hq=8, Hkv=1, Hidx=1, kv="fp8_e5m2",
+                                  topk=16, scale=(0.37, 0.11)),
+}
+
+
+@pytest.mark.parametrize("name", list(E5M2))
+def test_decode_e5m2(msa, name):
+    """fp8-e5m2 K/V pools (the sglang page's other fp8 cache format), dequantised
+    on load; the second case has a row of more than 1024 blocks."""
+    spec = E5M2[name]
+    seed = 700 + sorted(E5M2).index(name)
+    print(f"[decode_e5m2] {name} seed={seed}", flush=True)
+    case, cfg, g = _run(msa, spec, seed)
     err, nband = _compare(host_view(case), g, spec)
     print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)

@@ -27,7 +27,7 @@ def _spec(n_new, prefix, Hq=8, Hkv=2, Hidx=2, Di=128, topk=4, init=1, local=2, q
     s = dict(kind="prefill", B=len(n_new), n_new=list(n_new), prefix=list(prefix), Hq=Hq,
              Hkv=Hkv, Hidx=Hidx, D=128, Di=Di, topk=topk, init=init, local=local, q=q, kv=kv,
              idx="bf16")
-    if kv == "fp8":
+    if kv.startswith("fp8"):
         s.update(k_scale=1.0 / 16, v_scale=1.0 / 16)
     return s
 
@@ -177,6 +177,24 @@ def test_prefill_maximum_sizes(msa):
     print("[prefill_max] seed=41", flush=True)
     case = generate(spec, 41, device="cuda")
     assert case.max_blocks == 8192
+    g = _run(msa, case, spec)
+    err, nband = _compare(host_view(case), g, spec, np.arange(case.T))
+    print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
+
+
+E5M2 = {
+    "key_major": _spec([260, 100], [4000, 1500], Hq=16, Hkv=2, Hidx=2, kv="fp8_e5m2", topk=8),
+    "short_chunks": _spec([3, 4, 1], [40000, 7000, 16000], Hq=16, Hkv=2, Hidx=2,
+                          kv="fp8_e5m2", topk=32),
+}
+
+
+@pytest.mark.parametrize("name", list(E5M2))
+def test_prefill_e5m2(msa, name):
+    spec = E5M2[name]
+    seed = 960 + sorted(E5M2).index(name)
+    print(f"[prefill_e5m2] {name} seed={seed}", flush=True)
+    case = generate(spec, seed, device="cuda")
     g = _run(msa, case, spec)
     err, nband = _compare(host_view(case), g, spec, np.arange(case.T))
     print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
