@@ -57,11 +57,6 @@ WORKLOADS = {
     "verify_b32_q4_l32k": dict(
         kind="prefill", B=32, n_new=4, prefix=32764, Hq=16, Hkv=2, Hidx=2,
         D=128, Di=128, topk=16, init=1, local=2, q="bf16", kv="bf16", idx="bf16"),
-    # fp8-e5m2 K/V pools (the other fp8 cache format of the sglang page)
-    "decode_e5m2_b32_l64k": dict(
-        kind="decode", B=32, seq_lens=("fixed", 65536), Hq=16, Hkv=2, Hidx=2,
-        D=128, Di=128, topk=32, init=1, local=2, q="bf16", kv="fp8_e5m2", idx="bf16",
-        k_scale=1.0 / 16, v_scale=1.0 / 16),
     # paged append of a 4 x 4096-token chunk into pools of 4 x 20480 tokens
     # (the step before the path; slots in a seeded random order)
     "append_4x4096": dict(
@@ -70,6 +65,11 @@ WORKLOADS = {
     "append_fp8_4x4096": dict(
         kind="append", T=16384, pool_tokens=4 * 20480, Hq=16, Hkv=2, Hidx=2, D=128,
         Di=128, topk=16, init=1, local=2, q="bf16", kv="fp8", idx="bf16",
+        k_scale=1.0 / 16, v_scale=1.0 / 16),
+    # fp8-e5m2 K/V pools (the other fp8 cache format of the sglang page)
+    "decode_e5m2_b32_l64k": dict(
+        kind="decode", B=32, seq_lens=("fixed", 65536), Hq=16, Hkv=2, Hidx=2,
+        D=128, Di=128, topk=32, init=1, local=2, q="bf16", kv="fp8_e5m2", idx="bf16",
         k_scale=1.0 / 16, v_scale=1.0 / 16),
 }
 
