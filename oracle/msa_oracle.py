@@ -234,14 +234,21 @@ def forced_blocks(nb: int, init: int, local: int) -> list:
     return sorted(f)
 
 
-def select_for_query(scores: np.ndarray, nb: int, topk: int, init: int, local: int) -> list:
+def select_for_query(scores: np.ndarray, nb: int, topk: int, init: int, local: int,
+                     forced_in_budget: bool = False) -> list:
     """S = forced blocks plus the top-k of the others by (score desc, index asc),
-    returned in ascending block order."""
+    returned in ascending block order.
+
+    ``forced_in_budget`` is the other reading of the budget (the sglang page
+    sizes its dense fallback over the selected blocks for topk_blocks *
+    block_size_k tokens): the forced blocks count against topk, so only
+    max(topk - |F|, 0) others join them."""
     forced = forced_blocks(nb, init, local)
     fset = set(forced)
     cand = [j for j in range(nb) if j not in fset]
     cand.sort(key=lambda j: (-float(scores[j]), j))
-    chosen = cand[: min(topk, len(cand))]
+    k = max(topk - len(forced), 0) if forced_in_budget else topk
+    chosen = cand[: min(k, len(cand))]
     return sorted(fset.union(chosen))
 
 
@@ -259,7 +266,8 @@ def select(inp: dict, scores: np.ndarray):
     for t, (b, p) in enumerate(pos):
         nb = num_visible_blocks(p)
         for h in range(Hidx):
-            s = select_for_query(scores[t, h], nb, inp["topk"], inp["init"], inp["local"])
+            s = select_for_query(scores[t, h], nb, inp["topk"], inp["init"], inp["local"],
+                                 bool(inp.get("forced_in_budget", False)))
             sel[t, h, : len(s)] = s
             cnt[t, h] = len(s)
     return sel, cnt

@@ -523,3 +523,27 @@ def test_fp8_e5m2_encode_matches_torch_cast():
     assert np.array_equal(mine, ref.numpy())
     codes = np.array([c for c in range(256) if np.isfinite(tab[c])], dtype=np.int64)
     assert np.array_equal(oracle.fp8_e5m2_encode(tab[codes].astype(np.float32)), codes)
+
+
+@pytest.mark.parametrize("nb,init,local,topk", [(7, 1, 2, 4), (9, 0, 0, 3), (8, 2, 1, 4),
+                                                (6, 1, 2, 8), (10, 2, 3, 4), (12, 3, 3, 4)])
+def test_selection_forced_in_budget_brute_force(nb, init, local, topk):
+    """The budget variant: S holds every forced block and the best
+    max(topk - |F|, 0) others, checked against every subset of that size;
+    |S| = min(nb, max(topk, |F|))."""
+    rng = np.random.default_rng(nb * 31 + topk)
+    for trial in range(30):
+        s = rng.integers(-3, 4, size=nb).astype(np.float64)
+        S = oracle.select_for_query(s, nb, topk, init, local, forced_in_budget=True)
+        F = set(range(min(init, nb))) | set(range(max(0, nb - local), nb))
+        C = [j for j in range(nb) if j not in F]
+        k = min(max(topk - len(F), 0), len(C))
+
+        def beats(a, b):
+            return s[a] > s[b] or (s[a] == s[b] and a < b)
+
+        winners = [set(T) for T in itertools.combinations(C, k)
+                   if all(beats(a, b) for a in T for b in C if b not in T)]
+        assert len(winners) == 1
+        assert S == sorted(F | winners[0])
+        assert len(S) == min(nb, max(topk, len(F)))
