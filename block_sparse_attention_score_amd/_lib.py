@@ -39,6 +39,7 @@ class Params(ctypes.Structure):
         ("idx_dtype", ctypes.c_int32),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("forced_in_budget", ctypes.c_int32),
     ]
 
 

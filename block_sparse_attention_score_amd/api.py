@@ -40,6 +40,7 @@ class MsaConfig:
     k_scale: float = 1.0
     v_scale: float = 1.0
     block_size: int = BLOCK
+    forced_in_budget: bool = False  # forced blocks count inside topk
 
     @property
     def kmax(self) -> int:
@@ -51,7 +52,8 @@ class MsaConfig:
         return Params(self.num_q_heads, self.num_kv_heads, self.num_idx_heads, self.head_dim,
                       self.idx_dim, self.block_size, self.topk, self.init_blocks,
                       self.local_blocks, self.softmax_scale, code[self.q_dtype],
-                      code[self.kv_dtype], code[self.idx_dtype], self.k_scale, self.v_scale)
+                      code[self.kv_dtype], code[self.idx_dtype], self.k_scale, self.v_scale,
+                      int(self.forced_in_budget))
 
     @staticmethod
     def from_spec(spec: dict) -> "MsaConfig":
@@ -61,7 +63,8 @@ class MsaConfig:
                          local_blocks=spec["local"], q_dtype=spec.get("q", "bf16"),
                          kv_dtype=spec.get("kv", "bf16"), idx_dtype=spec.get("idx", "bf16"),
                          k_scale=float(spec.get("k_scale", 1.0)),
-                         v_scale=float(spec.get("v_scale", 1.0)))
+                         v_scale=float(spec.get("v_scale", 1.0)),
+                         forced_in_budget=bool(spec.get("forced_in_budget", False)))
 
 
 def blocks_from_tokens(init_tokens: int, local_tokens: int, block_size: int = BLOCK):

@@ -64,6 +64,8 @@ msa_status_t check_params(const msa_params_t* p) {
     return fail(MSA_ERR_UNSUPPORTED, "topk=%d not in {4,8,16,32}", p->topk);
   if (p->init_blocks < 0 || p->local_blocks < 0)
     return fail(MSA_ERR_INVALID_ARG, "negative init/local block count");
+  if (p->forced_in_budget != 0 && p->forced_in_budget != 1)
+    return fail(MSA_ERR_INVALID_ARG, "forced_in_budget=%d (0 or 1)", p->forced_in_budget);
   if (p->init_blocks > 64 || p->local_blocks > 64)
     return fail(MSA_ERR_UNSUPPORTED, "init/local block counts above 64");
   if (!std::isfinite(p->softmax_scale) || p->softmax_scale < 0.f)
@@ -270,6 +272,7 @@ msa::SelectArgs select_args(const msa_params_t& p, const float* scores, int32_t 
   a.init = p.init_blocks;
   a.local = p.local_blocks;
   a.kmax = kmax_of(p);
+  a.forced_in_budget = p.forced_in_budget;
   a.sel = sel;
   a.cnt = cnt;
   return a;
@@ -315,6 +318,7 @@ msa::AttendArgs attend_args(const msa_params_t& p, const void* q, const void* k_
   a.sel = sel;
   a.cnt = cnt;
   a.kmax = kmax_of(p);
+  a.forced_in_budget = p.forced_in_budget;
   a.hkv = p.num_kv_heads;
   a.hidx = p.num_idx_heads;
   a.bps = l.bps;
@@ -687,6 +691,7 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
   aa.sel = sel;
   aa.cnt = cnt;
   aa.kmax = kmax_of(p);
+  aa.forced_in_budget = p.forced_in_budget;
   aa.hkv = p.num_kv_heads;
   aa.hidx = p.num_idx_heads;
   aa.bps = l.bps;

@@ -303,9 +303,10 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   // them alone (init and local blocks plus min(topk, rest)).
   const int nb_vis = p >= 0 ? min(p / kBlock + 1, a.max_blocks) : 0;
   int count;
+  const int topk_row = topk_beside_forced(a.topk, nb_vis, a.init, a.local, a.forced_in_budget);
   if (self_select) {
     const int nf = forced_count(nb_vis, a.init, a.local);
-    count = nf + min(a.topk, nb_vis - nf);
+    count = nf + min(topk_row, nb_vis - nf);
   } else {
     const int cnt_raw = a.cnt[sel_row];
     count = p >= 0 ? min(max(cnt_raw, 0), a.kmax) : 0;
@@ -357,11 +358,12 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
     // One wave selects rows of up to 1024 blocks; longer rows take the
     // workgroup radix select.
     if (nb_vis <= 256) {
-      if (w == 0) select_wave<4>(srow, nb_vis, a.topk, a.init, a.local, emit);
+      if (w == 0) select_wave<4>(srow, nb_vis, topk_row, a.init, a.local, emit);
     } else if (nb_vis <= 1024) {
-      if (w == 0) select_wave<16>(srow, nb_vis, a.topk, a.init, a.local, emit);
+      if (w == 0) select_wave<16>(srow, nb_vis, topk_row, a.init, a.local, emit);
     } else {
-      select_core<div_up(8192, kThreads), kThreads>(srow, nb_vis, a.topk, a.init, a.local, S.sl, emit);
+      select_core<div_up(8192, kThreads), kThreads>(srow, nb_vis, topk_row, a.init, a.local, S.sl,
+                                                     emit);
     }
     if (sel_writer) {
       for (int i = count + tid; i < a.kmax; i += kThreads) so[i] = -1;

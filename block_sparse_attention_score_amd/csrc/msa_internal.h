@@ -55,6 +55,7 @@ struct SelectArgs {
   int32_t num_tokens;
   int32_t hidx;
   int32_t topk, init, local, kmax;
+  int32_t forced_in_budget;  // forced blocks count inside topk
   int32_t* sel;
   int32_t* cnt;
 };
@@ -79,6 +80,7 @@ struct AttendArgs {
   // selection to sel_out/cnt_out when they are set.
   const float* scores;       // [B, Hidx, max_blocks] or nullptr
   int32_t topk, init, local;
+  int32_t forced_in_budget;  // forced blocks count inside topk
   int32_t* sel_out;          // [B, Hidx, kmax] or nullptr
   int32_t* cnt_out;          // [B, Hidx] or nullptr
   int32_t kmax;

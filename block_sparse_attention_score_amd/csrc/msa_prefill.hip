@@ -240,7 +240,9 @@ __global__ __launch_bounds__(kWgThreads) void select_wave_kernel(SelectArgs a) {
   const int nb = p >= 0 ? min(p / kBlock + 1, a.max_blocks) : 0;
   int32_t* sel = a.sel + static_cast<int64_t>(row) * a.kmax;
   const int total = select_wave<E>(a.scores + static_cast<int64_t>(row) * a.max_blocks, nb,
-                                   a.topk, a.init, a.local,
+                                   topk_beside_forced(a.topk, nb, a.init, a.local,
+                                                      a.forced_in_budget),
+                                   a.init, a.local,
                                    [&](int pos, int j) { sel[pos] = j; });
   for (int i = total + lane; i < a.kmax; i += kWave) sel[i] = -1;
   if (lane == 0) a.cnt[row] = total;

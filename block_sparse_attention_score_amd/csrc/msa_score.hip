@@ -43,7 +43,8 @@ __global__ __launch_bounds__(kWgThreads) void select_kernel(SelectArgs a) {
     p = a.seq_lens[b] - n + (t - a.cu_seqlens_q[b]);
   }
   const int nb = p >= 0 ? min(p / kBlock + 1, a.max_blocks) : 0;
-  select_row<MAXPER>(a.scores + static_cast<int64_t>(rowi) * a.max_blocks, nb, a.topk,
+  select_row<MAXPER>(a.scores + static_cast<int64_t>(rowi) * a.max_blocks, nb,
+                     topk_beside_forced(a.topk, nb, a.init, a.local, a.forced_in_budget),
                      a.init, a.local, a.kmax, a.sel + static_cast<int64_t>(rowi) * a.kmax,
                      a.cnt + rowi, sl);
 }

@@ -33,6 +33,14 @@ __device__ __forceinline__ int forced_count(int nb, int init, int local) {
   return a + (nb - lo) - max(0, a - lo);
 }
 
+// Candidates to take beside the forced blocks of a row of nb visible blocks:
+// topk, or, when the forced blocks count inside the budget, what is left of
+// it (max(topk - |F|, 0)).  The selection routines below take this count.
+__device__ __forceinline__ int topk_beside_forced(int topk, int nb, int init, int local,
+                                                  int forced_in_budget) {
+  return forced_in_budget ? max(topk - forced_count(nb, init, local), 0) : topk;
+}
+
 // s: nb scores of one (query, index head) row.  MAXPER >= ceil(nb / NT).
 // Must be called by all NT (256 .. 1024) threads of the workgroup.  Calls
 // emit(pos, j) for every selected block j, pos being its slot in ascending
@@ -72,7 +80,11 @@ __device__ int select_core(const float* __restrict__ s, int nb, int topk, int in
 
   uint32_t T = 0u;
   int need = 0;
-  if (!take_all) {
+  if (!take_all && keff == 0) {
+    // no candidate joins the forced blocks: no key lies above T = max, none
+    // of those equal to it is needed
+    T = 0xFFFFFFFFu;
+  } else if (!take_all) {
     uint32_t prefix = 0u;
     need = keff;
     for (int pass = 0; pass < 4; ++pass) {
@@ -181,7 +193,9 @@ __device__ int select_wave(const float* __restrict__ s, int nb, int topk, int in
   auto count = [](bool x) { return __popcll(__builtin_amdgcn_ballot_w64(x)); };
   uint32_t T = 0u;
   int need = 0;
-  if (!take_all) {
+  if (!take_all && keff == 0) {
+    T = 0xFFFFFFFFu;  // no candidate joins the forced blocks
+  } else if (!take_all) {
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t c = T | (1u << bit);
       int n = 0;

@@ -13,7 +13,8 @@
  *                q_idx[h] . k_idx[t, h]  (blocks >= nb(p) score -inf);
  *   2. select -- S = {init blocks 0..init-1} U {local blocks nb-local..nb-1}
  *                U top-k of the remaining blocks by (score desc, block asc),
- *                listed ascending, |S| = min(nb, |F| + topk);
+ *                listed ascending, |S| = min(nb, |F| + topk) (or, with
+ *                forced_in_budget, top-max(topk - |F|, 0) of the others);
  *   3. attend -- exact softmax attention of each q head over the tokens
  *                t <= p of the blocks in S of its index head, split along the
  *                selected-block axis and merged with a log-sum-exp combine.
@@ -111,6 +112,12 @@ typedef struct {
   int32_t idx_dtype;     /* msa_dtype_t */
   float k_scale;         /* fp8 only: k = code value * k_scale            */
   float v_scale;         /* fp8 only: v = code value * v_scale            */
+  int32_t forced_in_budget; /* 0: S = F U top-k of the rest (|S| = min(nb,
+                            |F| + topk)); 1: the forced blocks count inside
+                            the budget, S = F U top-max(topk - |F|, 0) of the
+                            rest (|S| = min(nb, max(topk, |F|))), the reading
+                            under which the sglang page sizes its dense
+                            fallback for topk_blocks * block_size_k tokens */
 } msa_params_t;
 
 /* Library version, (major << 16) | minor. */

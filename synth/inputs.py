@@ -285,5 +285,6 @@ def host_view(case: Case, pages: Optional[np.ndarray] = None) -> dict:
         idx_dtype=spec.get("idx", "bf16"),
         k_scale=case.k_scale, v_scale=case.v_scale,
         topk=spec["topk"], init=spec["init"], local=spec["local"],
+        forced_in_budget=bool(spec.get("forced_in_budget", False)),
         Hq=spec["Hq"], Hkv=spec["Hkv"], Hidx=spec["Hidx"],
     )

@@ -41,8 +41,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_params_struct_layout_matches_header():
-    # 13 int32/float fields + 2 floats, no padding
-    assert ctypes.sizeof(_lib.Params) == 15 * 4
+    # 14 int32 / float fields + 2 floats, no padding
+    assert ctypes.sizeof(_lib.Params) == 16 * 4
 
 
 def base_cfg(**kw):
@@ -73,6 +73,7 @@ BAD_PARAMS = [
     (dict(init_blocks=-1), _lib.MSA_ERR_INVALID_ARG),
     (dict(local_blocks=65), _lib.MSA_ERR_UNSUPPORTED),
     (dict(softmax_scale=float("nan")), _lib.MSA_ERR_INVALID_ARG),
+    (dict(forced_in_budget=2), _lib.MSA_ERR_INVALID_ARG),
     (dict(q_dtype="fp8", kv_dtype="fp8"), _lib.MSA_ERR_UNSUPPORTED),
     (dict(q_dtype="f32", kv_dtype="bf16"), _lib.MSA_ERR_UNSUPPORTED),
     (dict(idx_dtype="fp8"), _lib.MSA_ERR_UNSUPPORTED),

@@ -287,3 +287,30 @@ def test_decode_e5m2(msa, name):
     case, cfg, g = _run(msa, spec, seed)
     err, nband = _compare(host_view(case), g, spec)
     print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
+
+
+BUDGET = {
+    "budget_g8": dict(_spec(3, [5000, 30000, 700], Hq=16, Hkv=2, Hidx=2, topk=16),
+                      forced_in_budget=True),
+    # |F| = 6 > topk = 4: the selection is the forced blocks alone; the long row
+    # takes the workgroup radix select
+    "budget_forced_exceed": dict(_spec(2, [9000, 140000], Hq=8, Hkv=1, Hidx=1, topk=4, init=3,
+                                       local=3), forced_in_budget=True),
+}
+
+
+@pytest.mark.parametrize("name", list(BUDGET))
+def test_decode_forced_in_budget(msa, name):
+    """The other reading of the budget: forced blocks count inside topk."""
+    spec = BUDGET[name]
+    seed = 720 + sorted(BUDGET).index(name)
+    print(f"[decode_budget] {name} seed={seed}", flush=True)
+    case, cfg, g = _run(msa, spec, seed)
+    assert cfg.forced_in_budget
+    err, nband = _compare(host_view(case), g, spec)
+    lens = case.seq_lens.cpu().numpy()
+    nb = (lens + 127) // 128
+    F = np.array([len(oracle.forced_blocks(int(n), spec["init"], spec["local"])) for n in nb])
+    want = np.minimum(nb, np.maximum(spec["topk"], F))
+    assert (parity.to_np(g["cnt"]) == want[:, None]).all()
+    print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)

@@ -198,3 +198,22 @@ def test_prefill_e5m2(msa, name):
     g = _run(msa, case, spec)
     err, nband = _compare(host_view(case), g, spec, np.arange(case.T))
     print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
+
+
+BUDGET = {
+    "key_major": dict(_spec([300, 200], [5000, 2000], topk=8, init=2, local=2),
+                      forced_in_budget=True),
+    "short_forced_exceed": dict(_spec([4, 4, 2], [20000, 3000, 140000], Hq=8, Hkv=1, Hidx=1,
+                                      topk=4, init=3, local=3), forced_in_budget=True),
+}
+
+
+@pytest.mark.parametrize("name", list(BUDGET))
+def test_prefill_forced_in_budget(msa, name):
+    spec = BUDGET[name]
+    seed = 980 + sorted(BUDGET).index(name)
+    print(f"[prefill_budget] {name} seed={seed}", flush=True)
+    case = generate(spec, seed, device="cuda")
+    g = _run(msa, case, spec)
+    err, nband = _compare(host_view(case), g, spec, np.arange(case.T))
+    print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
