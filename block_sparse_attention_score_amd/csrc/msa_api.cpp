@@ -544,8 +544,6 @@ msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new, const 
   if (!k_new || !v_new || !idx_k_new || !slot_mapping || !k_pool || !v_pool || !idx_k_pool)
     return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (num_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "num_tokens=%d < 0", num_tokens);
-  if (num_tokens > 65535)
-    return fail(MSA_ERR_UNSUPPORTED, "num_tokens=%d above 65535 per call", num_tokens);
   if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
   if (num_tokens == 0) return ok();
   msa::AppendArgs a{};

@@ -8,8 +8,8 @@
 // conversion instruction.
 //
 // One thread moves 8 consecutive elements of one row (16-byte bf16 loads);
-// a token's rows (Hkv K rows, Hkv V rows, Hidx index rows) are spread over
-// the x dimension of the grid, tokens over y.  Memory-bound and tiny: one
+// tokens are spread over the x dimension of the grid, a token's rows (Hkv K
+// rows, Hkv V rows, Hidx index rows) over y.  Memory-bound and tiny: one
 // decode step appends B tokens.
 #include "msa_device.h"
 #include "msa_internal.h"
@@ -95,7 +95,7 @@ __device__ __forceinline__ uint2 quant8(const BF8*, const float (&x)[8], float s
 // keys (new rows and pool alike).
 template <class KS, class KP, class IT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  const int t = blockIdx.y;
+  const int t = blockIdx.x;
   const int64_t slot = a.slots[t];
   if (slot < 0 || slot >= a.num_pages * kBlock) return;
   const int64_t page = slot / kBlock;
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int vd = a.head_dim / 8;   // 8-element vectors per K/V row
   const int vi = a.idx_dim / 8;    // per index row
   const int n_kv = a.hkv * vd;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.y * blockDim.x + threadIdx.x;
   if (i < 2 * n_kv) {
     const bool is_v = i >= n_kv;
     const int r = is_v ? i - n_kv : i;
@@ -140,7 +140,7 @@ static void launch_append_i(const AppendArgs& a, int idx_dtype, dim3 grid, hipSt
 hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   const int per_token = 2 * a.hkv * (a.head_dim / 8) + a.hidx * (a.idx_dim / 8);
-  const dim3 grid((per_token + 255) / 256, a.num_tokens);
+  const dim3 grid(a.num_tokens, (per_token + 255) / 256);
   if (kv_dtype == 0) launch_append_i<BF16, BF16>(a, idx_dtype, grid, s);
   else if (kv_dtype == 2) launch_append_i<BF16, FP8>(a, idx_dtype, grid, s);
   else if (kv_dtype == 3) launch_append_i<BF16, BF8>(a, idx_dtype, grid, s);

@@ -198,6 +198,11 @@ msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q,
  * Steps 1-3 for chunked prefill: num_q_tokens new tokens laid out by
  * cu_seqlens_q [B+1], each attending causally to its sequence's tokens
  * t <= p through its own selection.  Outputs as for decode, per token.
+ * Short chunks (num_q_tokens <= 8 * num_seqs, e.g. multi-token decode for
+ * speculative verification) are scored by a page scan over several queries
+ * per pass and attend per token with split-K; longer chunks take the causal
+ * index GEMM and key-major tiles over per-block token lists.  The choice
+ * follows from the shapes alone, like the workspace size.
  * Needs bf16 index keys and num_q_tokens < 2^23 (MSA_ERR_UNSUPPORTED
  * otherwise).  ws: msa_prefill_workspace_size() bytes.
  */
@@ -224,7 +229,7 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q,
  *                (q_dtype); idx_k_new [T, Hidx, Di] in idx_dtype.
  *   fp8 pools store e4m3fn(RNE(clamp(x / k_scale, +-448))) (v_scale for V;
  *   the division in float32); e5m2 pools the same with +-57344.
- * num_tokens <= 65535 per call.  Nothing else is read or written.
+ * Nothing else is read or written.
  */
 msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new,
                            const void* v_new, const void* idx_k_new,

@@ -140,3 +140,25 @@ def test_append_then_decode(msa, kv):
                            spec["init"], spec["local"])
     ora_out, _ = oracle.attend(ref_inp, gsel, gcnt)
     parity.check_output(parity.to_np(out), ora_out, False)
+
+
+def test_append_more_tokens_than_one_grid_row(msa):
+    """70000 tokens in one call (tokens lie on the grid's x dimension)."""
+    print("[append_many] 70000 tokens", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(12)
+    P, T, Hkv, Hidx, Di = 600, 70000, 2, 1, 64
+    pools = [torch.randn((P, Hkv, 128, 128), generator=g).to(torch.bfloat16),
+             torch.randn((P, Hkv, 128, 128), generator=g).to(torch.bfloat16),
+             torch.randn((P, Hidx, 128, Di), generator=g).to(torch.bfloat16)]
+    new = [torch.randn((T, Hkv, 128), generator=g).to(torch.bfloat16),
+           torch.randn((T, Hkv, 128), generator=g).to(torch.bfloat16),
+           torch.randn((T, Hidx, Di), generator=g).to(torch.bfloat16)]
+    slots = torch.randperm(P * 128, generator=g)[:T].to(torch.int64)
+    cfg = msa.MsaConfig(num_q_heads=8, num_kv_heads=Hkv, num_idx_heads=Hidx, idx_dim=Di)
+    dev_pools = [t.cuda() for t in pools]
+    msa.append_kv(cfg, *[t.cuda() for t in new], slots.cuda(), *dev_pools)
+    torch.cuda.synchronize()
+    want = oracle.append_kv(*[_bits(t) for t in pools], *[_bits(t) for t in new], slots.numpy(),
+                            kv_src="bf16", kv_dtype="bf16", idx_dtype="bf16")
+    for got, ref in zip(dev_pools, want):
+        assert np.array_equal(_bits(got), ref)
