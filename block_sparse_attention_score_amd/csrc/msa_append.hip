@@ -7,9 +7,10 @@
 // largest finite value (448 / 57344), round to nearest even by the gfx950
 // conversion instruction.
 //
-// One thread moves 8 consecutive elements of one row (16-byte bf16 loads);
-// tokens are spread over the x dimension of the grid, a token's rows (Hkv K
-// rows, Hkv V rows, Hidx index rows) over y.  Memory-bound and tiny: one
+// One thread moves 8 consecutive elements of one row (16-byte bf16 loads):
+// the grid is flat over (token, 8-element vector of the token's Hkv K rows,
+// Hkv V rows and Hidx index rows), so consecutive threads write consecutive
+// 16-byte pieces of a row and no thread idles.  Memory-bound and tiny: one
 // decode step appends B tokens.
 #include "msa_device.h"
 #include "msa_internal.h"
@@ -95,15 +96,18 @@ __device__ __forceinline__ uint2 quant8(const BF8*, const float (&x)[8], float s
 // keys (new rows and pool alike).
 template <class KS, class KP, class IT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  const int t = blockIdx.x;
+  const int vd = a.head_dim / 8;   // 8-element vectors per K/V row
+  const int vi = a.idx_dim / 8;    // per index row
+  const int n_kv = a.hkv * vd;
+  const int per_token = 2 * n_kv + a.hidx * vi;
+  const int64_t gi = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gi >= static_cast<int64_t>(a.num_tokens) * per_token) return;
+  const int t = static_cast<int>(gi / per_token);
+  const int i = static_cast<int>(gi - static_cast<int64_t>(t) * per_token);
   const int64_t slot = a.slots[t];
   if (slot < 0 || slot >= a.num_pages * kBlock) return;
   const int64_t page = slot / kBlock;
   const int off = static_cast<int>(slot - page * kBlock);
-  const int vd = a.head_dim / 8;   // 8-element vectors per K/V row
-  const int vi = a.idx_dim / 8;    // per index row
-  const int n_kv = a.hkv * vd;
-  const int i = blockIdx.y * blockDim.x + threadIdx.x;
   if (i < 2 * n_kv) {
     const bool is_v = i >= n_kv;
     const int r = is_v ? i - n_kv : i;
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     } else {
       copy8(static_cast<const KS*>(nullptr), src, si, pool, di);
     }
-  } else if (i < 2 * n_kv + a.hidx * vi) {
+  } else {
     const int r = i - 2 * n_kv;
     const int h = r / vi;
     const int c = r - h * vi;
@@ -139,8 +143,10 @@ static void launch_append_i(const AppendArgs& a, int idx_dtype, dim3 grid, hipSt
 
 hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  const int per_token = 2 * a.hkv * (a.head_dim / 8) + a.hidx * (a.idx_dim / 8);
-  const dim3 grid(a.num_tokens, (per_token + 255) / 256);
+  const int64_t per_token = 2 * a.hkv * (a.head_dim / 8) + a.hidx * (a.idx_dim / 8);
+  const int64_t blocks = (static_cast<int64_t>(a.num_tokens) * per_token + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks));
   if (kv_dtype == 0) launch_append_i<BF16, BF16>(a, idx_dtype, grid, s);
   else if (kv_dtype == 2) launch_append_i<BF16, FP8>(a, idx_dtype, grid, s);
   else if (kv_dtype == 3) launch_append_i<BF16, BF8>(a, idx_dtype, grid, s);
