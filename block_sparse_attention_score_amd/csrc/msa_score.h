@@ -11,16 +11,69 @@
 // pages), read with non-temporal 16-byte loads, 32 per lane in flight: Di/8
 // lanes cover one token row, so a wave instruction reads 64/(Di/8) full rows.
 // Every lane keeps the 8 query elements of its column slice in registers,
-// forms an 8-term partial dot product, the row is summed across its lanes
-// with DPP, tokens past the query are masked by select (never by
-// multiplying, so stale bytes cannot leak), and the wave reduces the block
-// max.
+// forms an 8-term partial dot product (bf16 pairs on v_dot2c_f32_bf16), the
+// row is summed across its lanes with DPP, tokens past the query are masked
+// by select (never by multiplying, so stale bytes cannot leak), and the wave
+// reduces the block max.
 #pragma once
 
 #include "msa_device.h"
 #include "msa_internal.h"
 
 namespace msa {
+
+// The slice of the index query a lane dots with its 8 keys.  bf16 keys feed
+// the query's bf16 pairs and their own straight into v_dot2c_f32_bf16 (two
+// products and the running sum per instruction, no unpacking); f32 keys are
+// unpacked and chained with fmaf.  Every scan sums in the same order, so the
+// decode scan and the short-chunk scan give the same bits for one query.
+template <class IT>
+struct QSlice;
+template <>
+struct QSlice<BF16> {
+  uint32_t w[4];
+};
+template <>
+struct QSlice<F32> {
+  float v[8];
+};
+
+__device__ __forceinline__ void load_qslice(const BF16* tag, const void* q, int64_t idx,
+                                            QSlice<BF16>& s) {
+  const Raw8<BF16> r = load_raw(tag, q, idx);
+  s.w[0] = r.v.x; s.w[1] = r.v.y; s.w[2] = r.v.z; s.w[3] = r.v.w;
+}
+__device__ __forceinline__ void load_qslice(const F32* tag, const void* q, int64_t idx,
+                                            QSlice<F32>& s) {
+  load8(tag, q, idx, s.v);
+}
+__device__ __forceinline__ void zero_qslice(QSlice<BF16>& s) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s.w[k] = 0u;
+}
+__device__ __forceinline__ void zero_qslice(QSlice<F32>& s) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s.v[k] = 0.f;
+}
+
+__device__ __forceinline__ float dot8(const QSlice<BF16>& q, const Raw8<BF16>& k) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const uint32_t kw[4] = {k.v.x, k.v.y, k.v.z, k.v.w};
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w[i]),
+                                        __builtin_bit_cast(bf16x2_t, kw[i]), d, false);
+  return d;
+}
+__device__ __forceinline__ float dot8(const QSlice<F32>& q, const Raw8<F32>& k) {
+  float x[8];
+  unpack(k, x);
+  float d = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) d = fmaf(q.v[e], x[e], d);
+  return d;
+}
 
 template <class IT, int DI>
 __device__ void score_chunk(const ScoreArgs& a, int pair, int chunk) {
@@ -50,8 +103,8 @@ __device__ void score_chunk(const ScoreArgs& a, int pair, int chunk) {
   const int col = lane % LPR;
   const IT* tag = nullptr;
 
-  float qv[8];
-  load8(tag, a.idx_q, (static_cast<int64_t>(b) * a.hidx + h) * DI + col * 8, qv);
+  QSlice<IT> qs;
+  load_qslice(tag, a.idx_q, (static_cast<int64_t>(b) * a.hidx + h) * DI + col * 8, qs);
 
   const int p = L - 1;
   const int j0 = chunk * a.pages_per_item;
@@ -69,14 +122,13 @@ __device__ void score_chunk(const ScoreArgs& a, int pair, int chunk) {
 #pragma unroll
         for (int i = 0; i < BATCH; ++i)
           raw[i] = load_raw(tag, a.idx_k, base + static_cast<int64_t>((i0 + i) * RPL) * DI);
+        // the whole batch is in flight before the first dot product (the
+        // scheduler would otherwise interleave loads and dot products and
+        // keep about ten loads in flight)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
-          float x[8];
-          unpack(raw[i], x);
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) d = fmaf(qv[e], x[e], d);
-          d = group_sum<LPR>(d);
+          const float d = group_sum<LPR>(dot8(qs, raw[i]));
           const int t = (i0 + i) * RPL + row;
           m = fmaxf(m, t < nvalid ? d : -INFINITY);
         }
@@ -127,17 +179,17 @@ __device__ void score_chunk_multi(const ScoreArgs& a, int pair, int chunk) {
   const int j1 = min(nb, j0 + a.pages_per_item);
 
   for (int q0 = 0; q0 < n; q0 += QG) {
-    float qv[QG][8];
+    QSlice<IT> qs[QG];
     int pq[QG];  // position of each query of the group (-1: past the chunk)
 #pragma unroll
     for (int qi = 0; qi < QG; ++qi) {
       const int i = q0 + qi;
       if (i < n) {
-        load8(tag, a.idx_q, (static_cast<int64_t>(c0 + i) * a.hidx + h) * DI + col * 8, qv[qi]);
+        load_qslice(tag, a.idx_q, (static_cast<int64_t>(c0 + i) * a.hidx + h) * DI + col * 8,
+                    qs[qi]);
         pq[qi] = L - n + i;
       } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[qi][e] = 0.f;
+        zero_qslice(qs[qi]);
         pq[qi] = -1;
       }
     }
@@ -155,17 +207,14 @@ __device__ void score_chunk_multi(const ScoreArgs& a, int pair, int chunk) {
 #pragma unroll
           for (int i = 0; i < BATCH; ++i)
             raw[i] = load_raw(tag, a.idx_k, base + static_cast<int64_t>((i0 + i) * RPL) * DI);
+          // (no scheduling barrier here: with four queries' dot products per
+          // load, interleaving loads and compute measured faster)
 #pragma unroll
           for (int i = 0; i < BATCH; ++i) {
-            float x[8];
-            unpack(raw[i], x);
             const int t = j * kBlock + (i0 + i) * RPL + row;  // token position
 #pragma unroll
             for (int qi = 0; qi < QG; ++qi) {
-              float d = 0.f;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) d = fmaf(qv[qi][e], x[e], d);
-              d = group_sum<LPR>(d);
+              const float d = group_sum<LPR>(dot8(qs[qi], raw[i]));
               m[qi] = fmaxf(m[qi], t <= pq[qi] ? d : -INFINITY);
             }
           }
