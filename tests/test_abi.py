@@ -162,3 +162,43 @@ def test_prefill_workspace_and_token_limit():
     assert lib.msa_prefill_workspace_size(ctypes.byref(p), B, (1 << 23) - 1, MB) > 0
     assert lib.msa_prefill_workspace_size(ctypes.byref(p), B, 1 << 23, MB) == 0
     assert "num_q_tokens" in lib.msa_last_error().decode()
+
+
+def append_call(cfg, num_tokens=8, num_pages=16, **ptrs):
+    p = cfg.params()
+    args = dict(k_new=FAKE, v_new=FAKE, idx_k_new=FAKE, slots=FAKE, k_pool=FAKE, v_pool=FAKE,
+                idx_k_pool=FAKE)
+    args.update(ptrs)
+    return msa.load().msa_append_kv(ctypes.byref(p), args["k_new"], args["v_new"],
+                                    args["idx_k_new"], args["slots"], num_tokens,
+                                    args["k_pool"], args["v_pool"], args["idx_k_pool"],
+                                    num_pages, None)
+
+
+def test_append_validation_before_launch():
+    """msa_append_kv rejects bad arguments before it enqueues anything (the
+    fake pointers are never dereferenced)."""
+    lib = msa.load()
+    for name in ("k_new", "v_new", "idx_k_new", "slots", "k_pool", "v_pool", "idx_k_pool"):
+        assert append_call(base_cfg(), **{name: None}) == _lib.MSA_ERR_INVALID_ARG, name
+        assert "NULL" in lib.msa_last_error().decode()
+    assert append_call(base_cfg(), num_tokens=-1) == _lib.MSA_ERR_INVALID_ARG
+    assert append_call(base_cfg(), num_pages=0) == _lib.MSA_ERR_INVALID_ARG
+    assert append_call(base_cfg(kv_dtype="fp8", k_scale=0.0)) == _lib.MSA_ERR_INVALID_ARG
+    assert append_call(base_cfg(kv_dtype="fp8_e5m2", v_scale=float("inf"))) == \
+        _lib.MSA_ERR_INVALID_ARG
+    assert append_call(base_cfg(q_dtype="f32", kv_dtype="fp8_e5m2")) == _lib.MSA_ERR_UNSUPPORTED
+    # nothing to do: success without touching memory
+    assert append_call(base_cfg(), num_tokens=0) == _lib.MSA_OK
+
+
+def test_prefill_workspace_follows_the_chunk_path():
+    """Short chunks (T <= 8 B) keep per-token split-K partials, long chunks the
+    key-major lists and bf16 partials; the size is a function of the shapes."""
+    cfg = base_cfg()
+    lib = msa.load()
+    p = cfg.params()
+    short = lib.msa_prefill_workspace_size(ctypes.byref(p), 32, 8 * 32, 256)
+    long_ = lib.msa_prefill_workspace_size(ctypes.byref(p), 32, 8 * 32 + 1, 256)
+    assert short > 0 and long_ > 0 and long_ != short
+    assert lib.msa_prefill_workspace_size(ctypes.byref(p), 32, 8 * 32, 256) == short
