@@ -314,3 +314,33 @@ def test_decode_forced_in_budget(msa, name):
     want = np.minimum(nb, np.maximum(spec["topk"], F))
     assert (parity.to_np(g["cnt"]) == want[:, None]).all()
     print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
+
+
+def test_sparse_equals_dense_over_compacted_table(msa):
+    """The library's sparse decode against its own decode over a page table
+    compacted to the selected blocks, where every block is selected (the
+    sglang page's dense-sparse form): the same attention, summed in another
+    order, so within the parity bounds of each other and of the oracle."""
+    spec = _spec(4, [33000, 5000, 129, 20000], Hq=16, Hkv=2, Hidx=1, topk=16)
+    print("[compacted] seed=731", flush=True)
+    case, cfg, g = _run(msa, spec, 731)
+    _compare(host_view(case), g, spec)
+    sel, cnt = parity.to_np(g["sel"]), parity.to_np(g["cnt"])
+    lens = case.seq_lens.cpu().numpy()
+    bt = case.block_table.cpu().numpy()
+    K = sel.shape[2]
+    bt_c = np.full((case.B, K), -1, dtype=np.int32)
+    lens_c = np.zeros(case.B, dtype=np.int32)
+    for b in range(case.B):
+        c = int(cnt[b, 0])
+        bt_c[b, :c] = bt[b, sel[b, 0, :c]]
+        nb = (int(lens[b]) + 127) // 128
+        assert sel[b, 0, c - 1] == nb - 1
+        lens_c[b] = 128 * (c - 1) + (int(lens[b]) - 128 * (nb - 1))
+    dense_cfg = msa.MsaConfig.from_spec(dict(spec, topk=32))  # every compacted block is kept
+    out_c = msa.sparse_decode(dense_cfg, case.q, case.idx_q, case.k_pool, case.v_pool,
+                              case.idx_k_pool, torch.from_numpy(bt_c).cuda(),
+                              torch.from_numpy(lens_c).cuda())
+    torch.cuda.synchronize()
+    d = (out_c.float() - g["out"].float()).abs()
+    assert d.max().item() <= parity.BF16_MAX and d.mean().item() <= parity.BF16_MEAN

@@ -296,6 +296,37 @@ def test_dense_equivalence_with_explicit_scale():
     assert np.allclose(res["out"], dense, rtol=1e-11, atol=1e-12)
 
 
+def _compacted(inp, sel, cnt):
+    """The sglang page's dense-sparse form: a page table holding only each
+    sequence's selected blocks, in order, and the length that covers them
+    (every selected block is full but the last, the query's own)."""
+    B, K = sel.shape[0], sel.shape[2]
+    bt = np.full((B, K), -1, dtype=np.int32)
+    lens = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        c = int(cnt[b, 0])
+        blocks = sel[b, 0, :c]
+        bt[b, :c] = inp["block_table"][b, blocks]
+        L = int(inp["seq_lens"][b])
+        nb = (L + 127) // 128
+        assert blocks[-1] == nb - 1
+        lens[b] = 128 * (c - 1) + (L - 128 * (nb - 1))
+    return dict(inp, block_table=bt, seq_lens=lens)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_sparse_equals_dense_over_compacted_table(kv):
+    """Sparse decode over the selection equals dense causal attention (torch
+    SDPA, float64) over a page table compacted to the selected blocks, the
+    equivalence the sglang page's dense-sparse decode relies on."""
+    inp = _tiny_case(21, lens=(1500, 700, 129), B=3, Hq=4, Hkv=2, Hidx=1, D=16, Di=8, topk=2,
+                     init=1, local=2, kv=kv)
+    res = oracle.sparse_attention(inp)
+    assert (res["count"] < (np.asarray(inp["seq_lens"]) + 127) // 128).any()  # really sparse
+    dense = _dense_sdpa(_compacted(inp, res["sel"], res["count"]))
+    assert np.allclose(res["out"], dense, rtol=1e-11, atol=1e-12)
+
+
 # ----------------------------------------------------------- invariances
 
 def test_softmax_weights_sum_to_one():
