@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "msa.h"
@@ -27,6 +28,26 @@ msa_status_t fail(msa_status_t st, const char* fmt, ...) {
 msa_status_t ok() {
   g_err[0] = '\0';
   return MSA_OK;
+}
+
+// MSA_LOG=1 in the environment: one line per entry-point call on stderr with
+// the launch configuration it chose (the variable is read once).
+bool log_on() {
+  static const bool on = [] {
+    const char* v = std::getenv("MSA_LOG");
+    return v != nullptr && v[0] == '1';
+  }();
+  return on;
+}
+
+void log_line(const char* fmt, ...) {
+  if (!log_on()) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[msa] %s\n", buf);
 }
 
 constexpr int kMaxBlocksLimit = 8192;  // 1M tokens per sequence
@@ -468,6 +489,10 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const 
   const msa_params_t& p = *params;
   const DecodeLayout l = decode_layout(p, num_seqs, max_blocks);
   if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
+  log_line("msa_sparse_decode: B=%d max_blocks=%d scan grid %d (%d pages per item), attention "
+           "grid %d x %d x %d (%d blocks per split), G=%d", num_seqs, max_blocks,
+           num_seqs * p.num_idx_heads * ((max_blocks + kPagesPerItem - 1) / kPagesPerItem),
+           kPagesPerItem, l.nsplit_max, p.num_kv_heads, num_seqs, l.bps, group_of(p));
   if (num_seqs == 0) return ok();
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
@@ -519,6 +544,8 @@ msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q, const 
   if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
   const DecodeLayout l = decode_layout(*params, num_seqs, max_blocks);
   if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
+  log_line("msa_sparse_attend: B=%d attention grid %d x %d x %d (%d blocks per split)", num_seqs,
+           l.nsplit_max, params->num_kv_heads, num_seqs, l.bps);
   if (num_seqs == 0) return ok();
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
@@ -545,6 +572,8 @@ msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new, const 
     return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (num_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "num_tokens=%d < 0", num_tokens);
   if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
+  log_line("msa_append_kv: T=%d into %lld pages (kv dtype %d)", num_tokens,
+           (long long)num_pages, params->kv_dtype);
   if (num_tokens == 0) return ok();
   msa::AppendArgs a{};
   a.k_new = k_new;
@@ -595,6 +624,15 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
                 kMaxPrefillTokens - 1);
   const PrefillLayout l = prefill_layout(p, num_seqs, num_q_tokens, max_blocks);
   if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
+  if (short_chunks(num_seqs, num_q_tokens))
+    log_line("msa_sparse_prefill: B=%d T=%d short chunks: scan with four queries per pass, "
+             "per-token split-K (%d blocks per split)", num_seqs, num_q_tokens, l.bps);
+  else if (prefill_key_major(p, num_seqs, num_q_tokens))
+    log_line("msa_sparse_prefill: B=%d T=%d key-major: %d tokens per tile, at most %d tiles",
+             num_seqs, num_q_tokens, l.tq, l.max_items);
+  else
+    log_line("msa_sparse_prefill: B=%d T=%d per-token split-K (%d blocks per split)", num_seqs,
+             num_q_tokens, l.bps);
   if (num_seqs == 0 || num_q_tokens == 0) return ok();
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);

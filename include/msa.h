@@ -57,6 +57,8 @@
  *  - Workspaces are plain device memory of msa_*_workspace_size() bytes,
  *    256-byte aligned; their contents on entry do not matter.  Calls that
  *    share a workspace must be ordered on one stream.
+ *  - MSA_LOG=1 in the environment: every call prints the launch configuration
+ *    it chose (grids, blocks per split, prefill path) on stderr.
  */
 #ifndef MSA_H
 #define MSA_H

@@ -202,3 +202,26 @@ def test_prefill_workspace_follows_the_chunk_path():
     long_ = lib.msa_prefill_workspace_size(ctypes.byref(p), 32, 8 * 32 + 1, 256)
     assert short > 0 and long_ > 0 and long_ != short
     assert lib.msa_prefill_workspace_size(ctypes.byref(p), 32, 8 * 32, 256) == short
+
+
+def test_msa_log_prints_the_launch_configuration():
+    """MSA_LOG=1 makes every call print its launch configuration on stderr
+    (read once per process, so this runs in a child process; the calls below
+    have nothing to launch)."""
+    import subprocess
+    import sys
+    code = (
+        "import ctypes, block_sparse_attention_score_amd as msa\n"
+        "from block_sparse_attention_score_amd import _lib\n"
+        "cfg = msa.MsaConfig(num_q_heads=16, num_kv_heads=2, num_idx_heads=2)\n"
+        "p = cfg.params(); F = ctypes.c_void_p(1 << 20)\n"
+        "lib = msa.load()\n"
+        "assert lib.msa_append_kv(ctypes.byref(p), F, F, F, F, 0, F, F, F, 16, None) == 0\n"
+        "assert lib.msa_sparse_decode(ctypes.byref(p), F, F, F, F, F, 64, F, 16, F, 0, F, None,"
+        " None, None, ctypes.c_void_p(1 << 20), 1 << 20, None) == 0\n")
+    env = dict(os.environ, MSA_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=120, cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr
+    assert "[msa] msa_append_kv: T=0" in r.stderr
+    assert "[msa] msa_sparse_decode: B=0" in r.stderr
