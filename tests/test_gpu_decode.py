@@ -344,3 +344,17 @@ def test_sparse_equals_dense_over_compacted_table(msa):
     torch.cuda.synchronize()
     d = (out_c.float() - g["out"].float()).abs()
     assert d.max().item() <= parity.BF16_MAX and d.mean().item() <= parity.BF16_MEAN
+
+
+def test_decode_all_sequences_empty(msa):
+    """Every sequence of the batch has length 0: zeros, lse -inf, empty selections."""
+    spec = _spec(3, [0, 0, 0], Hq=16, Hkv=2, Hidx=2, topk=8)
+    print("[decode_empty] seed=741", flush=True)
+    case = generate(spec, 741, device="cuda", max_blocks=4)
+    cfg = msa.MsaConfig.from_spec(spec)
+    out, lse, sel, cnt = msa.sparse_decode(cfg, case.q, case.idx_q, case.k_pool, case.v_pool,
+                                           case.idx_k_pool, case.block_table, case.seq_lens,
+                                           return_selection=True)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all() and torch.isneginf(lse).all()
+    assert (cnt == 0).all() and (sel == -1).all()

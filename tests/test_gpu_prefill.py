@@ -217,3 +217,14 @@ def test_prefill_forced_in_budget(msa, name):
     g = _run(msa, case, spec)
     err, nband = _compare(host_view(case), g, spec, np.arange(case.T))
     print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
+
+
+def test_short_chunks_with_empty_sequences(msa):
+    """Short chunks where some sequences have no tokens at all (length 0, no new
+    tokens) and some chunks are empty."""
+    spec = _spec([2, 0, 3, 0], [5000, 0, 300, 0], Hq=8, Hkv=2, Hidx=2, topk=8)
+    print("[short_empty] seed=990", flush=True)
+    case = generate(spec, 990, device="cuda")
+    g = _run(msa, case, spec)
+    err, nband = _compare(host_view(case), g, spec, np.arange(case.T))
+    print(f"  max {err[0]:.3g} mean {err[1]:.3g}", flush=True)
