@@ -74,6 +74,7 @@ SIGNATURES = {
                                   _P, _P, _P, _P, _P, _SZ, _P]),
     "msa_append_kv": (_I32, [_PP, _P, _P, _P, _P, _I32, _P, _P, _P, _I64, _P]),
     "msa_fp8_e4m3_dequant": (_I32, [_P, _P, _I64, _F, _P]),
+    "msa_fp8_dequant": (_I32, [_P, _P, _I64, _F, _I32, _P]),
 }
 
 _lib = None

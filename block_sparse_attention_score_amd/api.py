@@ -258,14 +258,17 @@ def append_kv(cfg: MsaConfig, k_new, v_new, idx_k_new, slot_mapping, k_pool, v_p
                                _ptr(idx_k_pool), k_pool.shape[0], _stream(stream)))
 
 
-def fp8_dequant(codes: torch.Tensor, scale: float = 1.0, out=None, stream=None):
-    """fp8-e4m3 codes (uint8) -> float32 values times scale, as the loaders do it."""
-    if codes.dtype not in (torch.uint8, torch.float8_e4m3fn):
-        raise ValueError("codes must be uint8 or float8_e4m3fn")
+def fp8_dequant(codes: torch.Tensor, scale: float = 1.0, out=None, fmt: str = "fp8",
+                stream=None):
+    """fp8 codes (uint8; fmt "fp8" = e4m3, "fp8_e5m2") -> float32 values times
+    scale, as the loaders do it."""
+    if codes.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2):
+        raise ValueError("codes must be uint8, float8_e4m3fn or float8_e5m2")
     if out is None:
         out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
-    check(load().msa_fp8_e4m3_dequant(_ptr(codes), _ptr(out), codes.numel(), float(scale),
-                                      _stream(stream)))
+    code = {"fp8": MSA_FP8_E4M3, "fp8_e5m2": MSA_FP8_E5M2}[fmt]
+    check(load().msa_fp8_dequant(_ptr(codes), _ptr(out), codes.numel(), float(scale), code,
+                                 _stream(stream)))
     return out
 
 

@@ -745,15 +745,22 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
   return st == MSA_OK ? ok() : st;
 }
 
-msa_status_t msa_fp8_e4m3_dequant(const uint8_t* in, float* out, int64_t n, float scale,
-                                  void* stream) {
+msa_status_t msa_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale,
+                             int32_t dtype, void* stream) {
   if (n < 0) return fail(MSA_ERR_INVALID_ARG, "n=%lld < 0", (long long)n);
   if (n > 0 && (!in || !out)) return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!std::isfinite(scale)) return fail(MSA_ERR_INVALID_ARG, "scale must be finite");
+  if (!is_fp8(dtype)) return fail(MSA_ERR_UNSUPPORTED, "dtype=%d is not an fp8 format", dtype);
   const msa_status_t st = hip_status(
-      msa::launch_fp8_dequant(in, out, n, scale, static_cast<hipStream_t>(stream)),
+      msa::launch_fp8_dequant(in, out, n, scale, dtype == MSA_FP8_E5M2,
+                              static_cast<hipStream_t>(stream)),
       "fp8 dequant launch");
   return st == MSA_OK ? ok() : st;
+}
+
+msa_status_t msa_fp8_e4m3_dequant(const uint8_t* in, float* out, int64_t n, float scale,
+                                  void* stream) {
+  return msa_fp8_dequant(in, out, n, scale, MSA_FP8_E4M3, stream);
 }
 
 }  // extern "C"

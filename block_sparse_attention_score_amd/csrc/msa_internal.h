@@ -177,7 +177,7 @@ hipError_t launch_prefill_k2q(const PrefillAttnArgs& a, hipStream_t s);
 hipError_t launch_prefill_attend(const PrefillAttnArgs& a, int kv_dtype, int group,
                                  hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipStream_t s);
-hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale,
+hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale, bool e5m2,
                               hipStream_t s);
 
 }  // namespace msa

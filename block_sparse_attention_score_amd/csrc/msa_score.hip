@@ -61,14 +61,17 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t value) {
     p[i] = value;
 }
 
+// fp8 codes -> float32, through the same packed conversions to bf16 the
+// attention loaders use (exact for both formats), widened exactly to float32
+// and multiplied by the scale.
+template <class K8>
 __global__ void fp8_dequant_kernel(const uint8_t* in, float* out, int64_t n, float scale) {
-  const int64_t i = (blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x) * 4;
+  const int64_t i = (blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x) * 8;
   if (i >= n) return;
-  uint32_t w = 0;
-  for (int k = 0; k < 4 && i + k < n; ++k) w |= static_cast<uint32_t>(in[i + k]) << (8 * k);
-  float x[4];
-  fp8x4_to_f32(w, x);
-  for (int k = 0; k < 4 && i + k < n; ++k) out[i + k] = x[k] * scale;
+  uint32_t w[2] = {0u, 0u};
+  for (int k = 0; k < 8 && i + k < n; ++k) w[k / 4] |= static_cast<uint32_t>(in[i + k]) << (8 * (k % 4));
+  const bf16x8_t v = __is_same(K8, BF8) ? bf8x8_to_bf16x8(w[0], w[1]) : fp8x8_to_bf16x8(w[0], w[1]);
+  for (int k = 0; k < 8 && i + k < n; ++k) out[i + k] = static_cast<float>(v[k]) * scale;
 }
 
 // ------------------------------------------------------------- launchers
@@ -124,11 +127,16 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale,
+hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale, bool e5m2,
                               hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  const int64_t threads = (n + 3) / 4;
-  fp8_dequant_kernel<<<static_cast<int>((threads + 255) / 256), 256, 0, s>>>(in, out, n, scale);
+  const int64_t threads = (n + 7) / 8;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (e5m2)
+    fp8_dequant_kernel<BF8><<<static_cast<unsigned>(blocks), 256, 0, s>>>(in, out, n, scale);
+  else
+    fp8_dequant_kernel<FP8><<<static_cast<unsigned>(blocks), 256, 0, s>>>(in, out, n, scale);
   return hipGetLastError();
 }
 

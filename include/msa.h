@@ -247,6 +247,15 @@ msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new,
 msa_status_t msa_fp8_e4m3_dequant(const uint8_t* in, float* out, int64_t n,
                                   float scale, void* stream);
 
+/*
+ * The same for either fp8 format of the K/V pools (dtype MSA_FP8_E4M3 or
+ * MSA_FP8_E5M2; e5m2 infinities stay infinite, NaN codes give NaN):
+ * out[i] = value(in[i]) * scale, through the loaders' bf16 conversion.
+ * MSA_ERR_UNSUPPORTED for any other dtype.
+ */
+msa_status_t msa_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale,
+                             int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for need in ("msa_block_score", "msa_select_blocks", "msa_sparse_decode",
                  "msa_sparse_attend", "msa_sparse_prefill", "msa_decode_workspace_size",
-                 "msa_prefill_workspace_size", "msa_fp8_e4m3_dequant", "msa_append_kv",
+                 "msa_prefill_workspace_size", "msa_fp8_e4m3_dequant", "msa_fp8_dequant",
+                 "msa_append_kv",
                  "msa_status_string",
                  "msa_last_error", "msa_version"):
         assert need in names

@@ -104,15 +104,21 @@ def _compare(inp, g, spec, rows=None):
     return err, nband
 
 
-def test_fp8_dequant_all_codes(msa):
-    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).cuda()
-    for scale in (1.0, 1.0 / 16, 0.37):
-        got = msa.fp8_dequant(codes, scale).cpu().numpy().astype(np.float64)
-        ref = oracle.fp8_e4m3fn_table() * np.float32(scale).astype(np.float64)
-        ref = ref.astype(np.float32).astype(np.float64)   # the loader multiplies in fp32
-        nan = np.isnan(ref)
-        assert np.array_equal(np.isnan(got), nan)
-        assert np.array_equal(got[~nan], ref[~nan])
+@pytest.mark.parametrize("fmt", ["fp8", "fp8_e5m2"])
+def test_fp8_dequant_all_codes(msa, fmt):
+    """The loaders' conversion of all 256 codes (and a ragged count of 251)
+    against the oracle's tables from the format definitions."""
+    table = oracle.fp8_e4m3fn_table() if fmt == "fp8" else oracle.fp8_e5m2_table()
+    for n in (256, 251):
+        codes = torch.arange(n, dtype=torch.int32).to(torch.uint8).cuda()
+        for scale in (1.0, 1.0 / 16, 0.37):
+            got = msa.fp8_dequant(codes, scale, fmt=fmt).cpu().numpy().astype(np.float64)
+            with np.errstate(invalid="ignore"):
+                ref = table[:n] * np.float32(scale).astype(np.float64)
+            ref = ref.astype(np.float32).astype(np.float64)   # the loader multiplies in fp32
+            nan = np.isnan(ref)
+            assert np.array_equal(np.isnan(got), nan)
+            assert np.array_equal(got[~nan], ref[~nan])
 
 
 @pytest.mark.parametrize("name", list(SMALL))
