@@ -207,7 +207,7 @@ msa::ScoreArgs multi_score_args(const msa_params_t& p, const void* idx_q, const 
 
 struct PrefillLayout {
   size_t scores, sel, cnt, part_o, part_lse, tickets;
-  size_t counts, cursor, tok_off, csr, items, n_items, sink;  // key-major only
+  size_t counts, cursor, tok_off, tile_off, csr, items, n_items, sink;  // key-major only
   size_t total;
   int bps, nsplit_max;
   int tq, max_items;  // key-major only
@@ -234,6 +234,7 @@ PrefillLayout prefill_layout(const msa_params_t& p, int32_t B, int32_t T, int32_
     l.counts = take(sizeof(int32_t) * 2 * lists);  // counts, then cursor
     l.cursor = l.counts + sizeof(int32_t) * lists;
     l.tok_off = take(sizeof(int32_t) * lists);
+    l.tile_off = take(sizeof(int32_t) * lists);
     l.csr = take(sizeof(int32_t) * entries);
     l.items = take(sizeof(msa::Tile) * size_t(l.max_items));
     l.n_items = take(sizeof(int32_t));
@@ -694,6 +695,7 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
     ka.counts = reinterpret_cast<int32_t*>(w + l.counts);
     ka.cursor = reinterpret_cast<int32_t*>(w + l.cursor);
     ka.tok_off = reinterpret_cast<int32_t*>(w + l.tok_off);
+    ka.tile_off = reinterpret_cast<int32_t*>(w + l.tile_off);
     ka.csr = reinterpret_cast<int32_t*>(w + l.csr);
     ka.items = reinterpret_cast<msa::Tile*>(w + l.items);
     ka.n_items = reinterpret_cast<int32_t*>(w + l.n_items);

@@ -146,6 +146,7 @@ struct PrefillAttnArgs {
   int32_t* counts;           // [B * Hidx * max_blocks]
   int32_t* cursor;           // [B * Hidx * max_blocks]
   int32_t* tok_off;          // [B * Hidx * max_blocks] list offsets
+  int32_t* tile_off;         // [B * Hidx * max_blocks] first work tile of each list
   int32_t* csr;              // [T * Hidx * kmax] entries token << 8 | slot
   struct Tile* items;        // [max_items] resolved work tiles
   int32_t* n_items;          // [1]

@@ -182,80 +182,30 @@ __global__ __launch_bounds__(kWgThreads) void k2q_count_kernel(PrefillAttnArgs a
 }
 
 // One workgroup: exclusive scans of the counts (list offsets) and of the
-// tiles per list (work-item offsets), then the work tiles themselves, with
-// the page, the sequence bounds and the pool offset already resolved.  Lists
-// go in rounds of 1024, one per thread; each thread leaves its list's
-// offsets and resolved fields in LDS and marks, in an LDS map, which of the
-// round's tiles are its list's (in windows of kTileWin tiles); then the whole
-// workgroup writes the tiles, consecutive threads consecutive records, so
-// that the stores of a wave fill whole cache lines.
-constexpr int kTileWin = 8192;
+// tiles per list (work-tile offsets), lists in rounds of 1024, one per
+// thread; the fill kernel writes the tiles themselves.
 __global__ __launch_bounds__(1024) void k2q_scan_kernel(PrefillAttnArgs a, int n) {
   __shared__ int wsum[16];
   __shared__ int carry[2];
-  __shared__ int l_et[1024], l_ec[1024], l_c[1024], l_p0[1024], l_nvalid[1024];
-  __shared__ int64_t l_head0[1024];
-  __shared__ uint16_t tile_list[kTileWin];  // round list index of each tile of the window
   const int tid = threadIdx.x;
   if (tid == 0) carry[0] = carry[1] = 0;
   __syncthreads();
   for (int base = 0; base < n; base += 1024) {
     const int i = base + tid;
-    const int ic = min(i, n - 1);  // clamped: every load is in bounds
-    const int c = i < n ? a.counts[ic] : 0;
-    const int j = ic % a.max_blocks;
-    const int h = (ic / a.max_blocks) % a.hidx;
-    const int b = ic / a.max_blocks / a.hidx;
-    const int L = a.seq_lens[b];
-    const int cuA = a.cu_seqlens_q[b];
-    const int cuB = a.cu_seqlens_q[b + 1];
-    const int page = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
+    const int c = i < n ? a.counts[i] : 0;
     const int nt = (c + a.tq - 1) / a.tq;
     const int c0 = carry[0], t0 = carry[1];
     const int incl_c = block_incl_scan(c, wsum);
     const int incl_t = block_incl_scan(nt, wsum);
-    const int ec = c0 + incl_c - c;
-    const int et = t0 + incl_t - nt;
-    if (i < n) a.tok_off[i] = ec;
-    const bool page_ok = page >= 0 && page < a.num_pages;
-    l_et[tid] = et;
-    l_ec[tid] = ec;
-    l_c[tid] = c;
-    l_p0[tid] = L - (cuB - cuA) - cuA;
-    // keys at or past the sequence end hold stale bytes: staged as zeros
-    l_nvalid[tid] = page_ok ? max(0, min(kBlock, L - j * kBlock)) : 0;
-    l_head0[tid] = (static_cast<int64_t>(page_ok ? page : 0) * a.hkv + h * (a.hkv / a.hidx)) *
-                   kBlock * 128;
-    if (tid == 1023) {
+    if (i < n) {
+      a.tok_off[i] = c0 + incl_c - c;
+      a.tile_off[i] = t0 + incl_t - nt;
+    }
+    if (tid == 1023) {  // (every thread read the carry before the scans' barriers)
       carry[0] = c0 + incl_c;
       carry[1] = t0 + incl_t;
     }
     __syncthreads();
-    // the round's tiles [t0, t1), window by window
-    const int t1 = min(carry[1], a.max_items);
-    const int lists = min(1024, n - base);
-    for (int w0 = t0; w0 < t1; w0 += kTileWin) {
-      const int w1 = min(w0 + kTileWin, t1);
-      if (tid < lists)
-        for (int q = max(et, w0); q < min(et + nt, w1); ++q) tile_list[q - w0] = tid;
-      __syncthreads();
-      for (int q = w0 + tid; q < w1; q += 1024) {
-        const int lo = tile_list[q - w0];
-        const int k = q - l_et[lo];
-        const int il = base + lo;
-        Tile m;
-        m.j = il % a.max_blocks;
-        m.g0 = ((il / a.max_blocks) % a.hidx) * (a.hkv / a.hidx);
-        m.p0 = l_p0[lo];
-        m.nvalid = l_nvalid[lo];
-        m.head0 = l_head0[lo];
-        m.c0 = l_ec[lo] + k * a.tq;
-        m.ntok = min(a.tq, l_c[lo] - k * a.tq);
-        a.items[q] = m;
-      }
-      __syncthreads();  // the window's map is read
-    }
-    __syncthreads();  // the round's LDS fields are read; the carry is final
   }
   if (tid == 0) *a.n_items = min(carry[1], a.max_items);
 }
@@ -292,6 +242,36 @@ __global__ __launch_bounds__(kWgThreads) void k2q_fill_kernel(PrefillAttnArgs a)
     const int j = a.sel[static_cast<int64_t>(row) * a.kmax + s];
     if (j < 0 || j >= a.max_blocks) continue;
     a.csr[atomicAdd(&hist[j], 1)] = (t << 8) | s;
+  }
+
+  // The work tiles of the lists j = blockIdx.x, blockIdx.x + nact, ... of
+  // (b, h), nact being the sequence's active chunks: one tile per thread,
+  // with the page, the sequence bounds and the pool offset resolved, so that
+  // consecutive threads store consecutive records.
+  const int nact = (n_b + kWgThreads - 1) / kWgThreads;
+  const int L = a.seq_lens[b];
+  const int p0 = L - n_b - cu0;
+  const int g0 = h * (a.hkv / a.hidx);
+  for (int j = blockIdx.x; j < a.max_blocks; j += nact) {
+    const int c = a.counts[bh0 + j];
+    if (c == 0) continue;
+    const int et = a.tile_off[bh0 + j];
+    const int ec = a.tok_off[bh0 + j];
+    const int nt = (c + a.tq - 1) / a.tq;
+    const int page = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
+    const bool page_ok = page >= 0 && page < a.num_pages;
+    for (int k = tid; k < nt && et + k < a.max_items; k += kWgThreads) {
+      Tile m;
+      m.c0 = ec + k * a.tq;
+      m.ntok = min(a.tq, c - k * a.tq);
+      m.j = j;
+      // keys at or past the sequence end hold stale bytes: staged as zeros
+      m.nvalid = page_ok ? max(0, min(kBlock, L - j * kBlock)) : 0;
+      m.p0 = p0;
+      m.g0 = g0;
+      m.head0 = (static_cast<int64_t>(page_ok ? page : 0) * a.hkv + g0) * kBlock * 128;
+      a.items[et + k] = m;
+    }
   }
 }
 
