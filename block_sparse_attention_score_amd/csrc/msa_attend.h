@@ -8,9 +8,11 @@
 // selected blocks c*bps .. of the index head that serves g, for all G query
 // heads of g at once (the GQA group shares every K/V byte it loads).
 //
-// The split's selected blocks are cut into 64-token chunks (32 for f32
-// caches) that the workgroup's waves take round-robin, each wave with its own
-// online softmax; per chunk:
+// The split's selected blocks are cut into 32-token chunks that the
+// workgroup's waves take round-robin, each wave with its own online softmax
+// (at five blocks per split no wave streams more than three chunks, where
+// 64-token chunks would give two waves of eight a second 64-token chunk);
+// per chunk:
 //  * S^T = K q^T on the matrix cores: K rows are read straight from the page
 //    into the A operand (16 tokens x 32 dims per instruction, 64 contiguous
 //    bytes per token), q^T (G heads, zero-padded to 16 columns) is the B
@@ -387,7 +389,7 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   // of W still spreads evenly), with its own online softmax; no barrier until
   // the final merge.
   constexpr bool kF32 = __is_same(KT, F32);
-  constexpr int TILES = kF32 ? 2 : 4;           // tiles per chunk
+  constexpr int TILES = 2;                      // tiles per chunk
   constexpr int CPB = 8 / TILES;                // chunks per 128-token block
   const int nchunk = nblk * CPB > w ? (nblk * CPB - w + W - 1) / W : 0;
 
