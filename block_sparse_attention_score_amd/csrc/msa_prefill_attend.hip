@@ -245,14 +245,16 @@ __global__ __launch_bounds__(kWgThreads) void k2q_fill_kernel(PrefillAttnArgs a)
   }
 
   // The work tiles of the lists j = blockIdx.x, blockIdx.x + nact, ... of
-  // (b, h), nact being the sequence's active chunks: one tile per thread,
-  // with the page, the sequence bounds and the pool offset resolved, so that
-  // consecutive threads store consecutive records.
+  // (b, h), nact being the sequence's active chunks, dealt to the waves; one
+  // tile per lane, with the page, the sequence bounds and the pool offset
+  // resolved, so that consecutive lanes store consecutive records.
+  constexpr int kWaves = kWgThreads / kWave;
   const int nact = (n_b + kWgThreads - 1) / kWgThreads;
+  const int lane = tid & (kWave - 1);
   const int L = a.seq_lens[b];
   const int p0 = L - n_b - cu0;
   const int g0 = h * (a.hkv / a.hidx);
-  for (int j = blockIdx.x; j < a.max_blocks; j += nact) {
+  for (int j = blockIdx.x + nact * (tid / kWave); j < a.max_blocks; j += nact * kWaves) {
     const int c = a.counts[bh0 + j];
     if (c == 0) continue;
     const int et = a.tile_off[bh0 + j];
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(kWgThreads) void k2q_fill_kernel(PrefillAttnArgs a)
     const int nt = (c + a.tq - 1) / a.tq;
     const int page = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
     const bool page_ok = page >= 0 && page < a.num_pages;
-    for (int k = tid; k < nt && et + k < a.max_items; k += kWgThreads) {
+    for (int k = lane; k < nt && et + k < a.max_items; k += kWave) {
       Tile m;
       m.c0 = ec + k * a.tq;
       m.ntok = min(a.tq, c - k * a.tq);
