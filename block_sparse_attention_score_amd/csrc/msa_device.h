@@ -260,8 +260,9 @@ __device__ __forceinline__ uint32_t score_key(float x) {
 
 // ------------------------------------------------------- block scans
 
-// Inclusive prefix sum over the 256 threads of a workgroup.  `wsum` is LDS
-// scratch of 4 ints.  Contains barriers: every thread must call it.
+// Inclusive prefix sum over the threads of a workgroup (up to 1024).  `wsum`
+// is LDS scratch of one int per wave.  Contains barriers: every thread must
+// call it.
 __device__ __forceinline__ int block_incl_scan(int v, int* wsum) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;

@@ -112,7 +112,8 @@ struct AppendArgs {
 };
 
 // One prefill attention tile: up to kPrefillTileRows query rows of one k2q
-// list against its key block, resolved by the planning kernel.
+// list against its key block, with page and bounds resolved by the kernel
+// that fills the lists.
 struct Tile {
   int32_t c0;      // first list entry of the tile
   int32_t ntok;    // tokens in the tile
