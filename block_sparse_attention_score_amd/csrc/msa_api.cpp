@@ -464,7 +464,9 @@ msa_status_t msa_select_blocks(const msa_params_t* params, const float* scores,
     return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
   const int32_t T = cu_seqlens_q == nullptr ? num_seqs : num_q_tokens;
   if (T < 0) return fail(MSA_ERR_INVALID_ARG, "num_q_tokens=%d < 0", T);
-  if (T == 0) return ok();
+  // (no sequences: nothing to select, as in msa_sparse_prefill; the kernel
+  // reads at least one sequence's offsets)
+  if (T == 0 || num_seqs == 0) return ok();
   const msa::SelectArgs a = select_args(*params, scores, max_blocks, seq_lens, cu_seqlens_q,
                                         num_seqs, T, sel_blocks, sel_count);
   st = hip_status(launch_selection(a, static_cast<hipStream_t>(stream)), "select launch");

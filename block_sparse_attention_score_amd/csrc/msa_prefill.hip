@@ -226,9 +226,25 @@ __global__ __launch_bounds__(kWgThreads) void select_wave_kernel(SelectArgs a) {
   const int row = blockIdx.x * (kWgThreads / kWave) + threadIdx.x / kWave;
   if (row >= a.num_tokens * a.hidx) return;
   const int t = row / a.hidx;
+  // The row's scores are fetched first (their address does not depend on the
+  // position), so their loads overlap the position lookup.
+  float v[E];
+  load_row_scores<E>(a.scores + static_cast<int64_t>(row) * a.max_blocks, a.max_blocks, v);
   int p;
   if (a.cu_seqlens_q == nullptr) {
     p = a.seq_lens[t] - 1;
+  } else if (a.num_seqs <= kWave) {
+    // lane b reads sequence b's bounds and length in one round trip; token t
+    // belongs to the last sequence whose first token is at or before t (the
+    // offsets never decrease, so those lanes are a prefix of the wave)
+    const int bl = min(lane, a.num_seqs - 1);
+    const int cu_l = a.cu_seqlens_q[bl];
+    const int cu_n = a.cu_seqlens_q[bl + 1];
+    const int len = a.seq_lens[bl];
+    const int b = max(__popcll(__builtin_amdgcn_ballot_w64(lane < a.num_seqs && cu_l <= t)) - 1, 0);
+    const int first = __builtin_amdgcn_readlane(cu_l, b);
+    p = __builtin_amdgcn_readlane(len, b) - (__builtin_amdgcn_readlane(cu_n, b) - first) +
+        (t - first);
   } else {
     int lo = 0, hi = a.num_seqs;
     while (hi - lo > 1) {
@@ -239,11 +255,11 @@ __global__ __launch_bounds__(kWgThreads) void select_wave_kernel(SelectArgs a) {
   }
   const int nb = p >= 0 ? min(p / kBlock + 1, a.max_blocks) : 0;
   int32_t* sel = a.sel + static_cast<int64_t>(row) * a.kmax;
-  const int total = select_wave<E>(a.scores + static_cast<int64_t>(row) * a.max_blocks, nb,
-                                   topk_beside_forced(a.topk, nb, a.init, a.local,
-                                                      a.forced_in_budget),
-                                   a.init, a.local,
-                                   [&](int pos, int j) { sel[pos] = j; });
+  const int total = select_wave_loaded<E>(v, nb,
+                                          topk_beside_forced(a.topk, nb, a.init, a.local,
+                                                             a.forced_in_budget),
+                                          a.init, a.local,
+                                          [&](int pos, int j) { sel[pos] = j; });
   for (int i = total + lane; i < a.kmax; i += kWave) sel[i] = -1;
   if (lane == 0) a.cnt[row] = total;
 }

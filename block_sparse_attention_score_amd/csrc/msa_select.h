@@ -165,9 +165,19 @@ __device__ int select_core(const float* __restrict__ s, int nb, int topk, int in
 // (ranks from ballot prefix counts), which is the lower-index tie rule.
 // Output slots come from the same prefix counts, so the list is ascending.
 // Calls emit(pos, j) from the lane owning block j; returns the selection size.
+// select_wave_loaded takes the row already in registers: v[e] holds block
+// lane + 64 e for every such block below nb (other slots are ignored).
+template <int E>
+__device__ __forceinline__ void load_row_scores(const float* __restrict__ s, int n,
+                                                float (&v)[E]) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = s[min(lane + kWave * e, max(n - 1, 0))];
+}
+
 template <int E, class Emit>
-__device__ int select_wave(const float* __restrict__ s, int nb, int topk, int init, int local,
-                           Emit emit) {
+__device__ int select_wave_loaded(const float (&v)[E], int nb, int topk, int init, int local,
+                                  Emit emit) {
   const int lane = threadIdx.x & (kWave - 1);
   const int lo_init = min(init, nb);
   const int hi_local = max(0, nb - local);
@@ -178,9 +188,6 @@ __device__ int select_wave(const float* __restrict__ s, int nb, int topk, int in
 
   uint32_t key[E];
   bool cand[E], valid[E];
-  float v[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) v[e] = s[min(lane + kWave * e, max(nb - 1, 0))];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = lane + kWave * e;
@@ -230,6 +237,14 @@ __device__ int select_wave(const float* __restrict__ s, int nb, int topk, int in
     pos_before += __popcll(pm);
   }
   return nforced + keff;
+}
+
+template <int E, class Emit>
+__device__ int select_wave(const float* __restrict__ s, int nb, int topk, int init, int local,
+                           Emit emit) {
+  float v[E];
+  load_row_scores<E>(s, nb, v);
+  return select_wave_loaded<E>(v, nb, topk, init, local, emit);
 }
 
 // select_core writing the selection to sel[0..kmax) (-1 padded) and its size

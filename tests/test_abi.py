@@ -226,3 +226,12 @@ def test_msa_log_prints_the_launch_configuration():
     assert r.returncode == 0, r.stderr
     assert "[msa] msa_append_kv: T=0" in r.stderr
     assert "[msa] msa_sparse_decode: B=0" in r.stderr
+
+
+def test_select_without_sequences_enqueues_nothing():
+    """Token rows with no sequence to own them: nothing to select, and no
+    kernel reads the one-entry offsets (the fake pointers are never used)."""
+    p = base_cfg().params()
+    lib = msa.load()
+    assert lib.msa_select_blocks(ctypes.byref(p), FAKE, 16, FAKE, FAKE, 0, 5, FAKE, FAKE,
+                                 None) == _lib.MSA_OK

@@ -118,6 +118,31 @@ def test_multi_token_decode(msa, name):
     print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
 
 
+# Batches of more than a wave's worth of sequences: the per-token selection
+# finds a token's sequence by a search over the offsets instead of one ballot
+# (64 sequences is the last batch on the ballot path).  Lengths and new-token
+# counts cycle through patterns that include empty sequences and chunks.
+MANY_SEQS = {
+    "short_70": _spec([i % 4 for i in range(70)], [(i * 997) % 3000 for i in range(70)],
+                      Hq=8, Hkv=1, Hidx=1, topk=4),
+    "short_64": _spec([1 + i % 3 for i in range(64)], [(i * 331) % 2000 for i in range(64)],
+                      Hq=8, Hkv=1, Hidx=1, topk=4),
+    "key_major_66": _spec([20 + i % 7 for i in range(66)], [(i * 53) % 700 for i in range(66)],
+                          Hq=8, Hkv=2, Hidx=2, topk=4),
+}
+
+
+@pytest.mark.parametrize("name", list(MANY_SEQS))
+def test_many_sequences(msa, name):
+    spec = MANY_SEQS[name]
+    seed = 960 + list(MANY_SEQS).index(name)
+    print(f"[many_seqs] {name} seed={seed}", flush=True)
+    case = generate(spec, seed, device="cuda")
+    g = _run(msa, case, spec)
+    err, nband = _compare(host_view(case), g, spec, np.arange(case.T))
+    print(f"  T={case.T} max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
+
+
 def test_single_token_chunks_match_decode(msa):
     """A prefill of one new token per sequence is a decode step: the same
     selection, bit for bit, and outputs that agree within the parity bounds
