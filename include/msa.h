@@ -155,8 +155,10 @@ msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
 /*
  * Step 2 (select).  From scores[T, Hidx, max_blocks] writes
  * sel_blocks[T, Hidx, Kmax] and sel_count[T, Hidx].  Only the first nb(p)
- * scores of each row are read.  Deterministic: equal scores (+0 and -0 are
- * equal) go to the lower block index.
+ * scores of each row affect the result (the rest of the row may hold
+ * anything).  Deterministic: equal scores (+0 and -0 are equal) go to the
+ * lower block index.  With cu_seqlens_q given and num_seqs == 0 there is
+ * nothing to select: returns MSA_OK and enqueues nothing.
  */
 msa_status_t msa_select_blocks(const msa_params_t* params,
                                const float* scores, int32_t max_blocks,
