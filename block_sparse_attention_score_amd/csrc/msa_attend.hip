@@ -8,18 +8,28 @@ namespace msa {
 // aims at that), two waves per SIMD stream blocks.
 constexpr int kAttendWaves = 8;
 
+// Workgroup i runs on XCD i % 8; each XCD takes a contiguous run of
+// (token, kv head, split) units (`per` of them), so the splits of a row and
+// the neighbouring tokens of a sequence share one L2.
 template <class QT, class KT, int G>
-__global__ __launch_bounds__(kWave * kAttendWaves, 1) void decode_attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kWave * kAttendWaves, 1) void decode_attend_kernel(AttendArgs a,
+                                                                                int per) {
   __shared__ AttendLds<G, kAttendWaves> lds;
-  attend_split<QT, KT, G, kAttendWaves>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+  const int u = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
+  const int per_tok = a.nsplit_max * a.hkv;
+  if (u >= per_tok * a.num_tokens) return;
+  const int t = u / per_tok;
+  const int r = u - t * per_tok;
+  attend_split<QT, KT, G, kAttendWaves>(a, r % a.nsplit_max, r / a.nsplit_max, t, lds);
 }
 
 // ------------------------------------------------------------ launcher
 
 template <class QT, class KT, int G>
 static void launch_attend_t(const AttendArgs& a, hipStream_t s) {
-  const dim3 grid(a.nsplit_max, a.hkv, a.num_tokens);
-  decode_attend_kernel<QT, KT, G><<<grid, kWave * kAttendWaves, 0, s>>>(a);
+  const int units = a.nsplit_max * a.hkv * a.num_tokens;
+  const int per = (units + 7) / 8;
+  decode_attend_kernel<QT, KT, G><<<8 * per, kWave * kAttendWaves, 0, s>>>(a, per);
 }
 
 template <class QT, class KT>
