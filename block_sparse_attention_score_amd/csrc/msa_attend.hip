@@ -47,6 +47,9 @@ static bool launch_attend_g(const AttendArgs& a, int group, hipStream_t s) {
 hipError_t launch_decode_attend(const AttendArgs& a, int q_dtype, int kv_dtype, int group,
                                 hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
+  // the 1-D grid holds all units rounded up to a multiple of 8, in 32 bits
+  if (int64_t(a.nsplit_max) * a.hkv * a.num_tokens > int64_t(0x7fffffff) - 7)
+    return hipErrorInvalidValue;
   bool ok = false;
   if (q_dtype == 0 && kv_dtype == 0) ok = launch_attend_g<BF16, BF16>(a, group, s);
   else if (q_dtype == 0 && kv_dtype == 2) ok = launch_attend_g<BF16, FP8>(a, group, s);
