@@ -130,7 +130,19 @@ def _tiny_case(seed, B=2, lens=(300, 77), Hq=4, Hkv=2, Hidx=1, D=8, Di=8, topk=2
     if prefill_new is not None:
         spec.update(kind="prefill", n_new=list(prefill_new),
                     prefix=[L - n for L, n in zip(lens, prefill_new)])
-    return host_view(generate(spec, seed))
+    inp = host_view(generate(spec, seed))
+    inp["_pos"] = _spec_positions(spec)
+    return inp
+
+
+def _spec_positions(spec):
+    """(sequence, position) of every query row, written from the case's own
+    description and not from the oracle: decode queries sit at seq_len - 1;
+    a prefill chunk's i-th new token sits at prefix + i (the new tokens follow
+    the prefix the sglang page hands over beside cu_seqlens in forward_extend)."""
+    if spec["kind"] == "decode":
+        return [(b, L - 1) for b, L in enumerate(spec["seq_lens"])]
+    return [(b, spec["prefix"][b] + i) for b in range(spec["B"]) for i in range(spec["n_new"][b])]
 
 
 def _py_value(raw, dtype, scale=1.0):
@@ -143,10 +155,25 @@ def _py_value(raw, dtype, scale=1.0):
     return float(raw)
 
 
+class _RowCache:
+    """Stored rows decoded one scalar at a time (``_py_value``), each once."""
+
+    def __init__(self, pool, dtype, scale=1.0):
+        self.pool, self.dtype, self.scale, self.rows = pool, dtype, scale, {}
+
+    def __call__(self, page, h, s):
+        key = (page, h, s)
+        if key not in self.rows:
+            self.rows[key] = [_py_value(x, self.dtype, self.scale) for x in self.pool[page, h, s]]
+        return self.rows[key]
+
+
 def _py_scores(inp):
-    """Block scores with explicit loops over blocks and tokens."""
+    """Block scores with explicit loops over blocks and tokens; query
+    positions from the case description (``_spec_positions``)."""
     out = {}
-    for t, (b, p) in enumerate(oracle.query_positions(inp["seq_lens"], inp["cu_seqlens_q"])):
+    ikc = _RowCache(inp["idx_k_pool"], "bf16")
+    for t, (b, p) in enumerate(inp["_pos"]):
         for h in range(inp["Hidx"]):
             iq = [_py_value(x, "bf16") for x in inp["idx_q"][t, h]]
             row = []
@@ -157,7 +184,7 @@ def _py_scores(inp):
                 for s in range(128):
                     if j * 128 + s > p:
                         break
-                    ik = [_py_value(x, "bf16") for x in inp["idx_k_pool"][page, h, s]]
+                    ik = ikc(page, h, s)
                     best = max(best, sum(a * c for a, c in zip(iq, ik)))
                 row.append(best)
                 j += 1
@@ -178,8 +205,7 @@ def test_scores_brute_force(seed):
 def test_batched_scores_equal_per_query_definition():
     inp = _tiny_case(5, lens=(700, 260), prefill_new=(40, 260))
     sc = oracle.block_scores(inp)
-    pos = oracle.query_positions(inp["seq_lens"], inp["cu_seqlens_q"])
-    for t, (b, p) in enumerate(pos):
+    for t, (b, p) in enumerate(inp["_pos"]):
         for h in range(inp["Hidx"]):
             ik = oracle.decode(inp["idx_k_pool"][inp["block_table"][b, : (p // 128 + 1)], h]
                                .reshape(-1, inp["idx_k_pool"].shape[-1]), "bf16")
@@ -210,11 +236,14 @@ def test_selection_brute_force(nb, init, local, topk):
 
 
 def _py_attend(inp, sel, cnt, scale):
-    """Attention with explicit loops over heads and tokens."""
+    """Attention with explicit loops over heads and tokens; query positions
+    from the case description."""
     Hq, Hkv, Hidx = inp["Hq"], inp["Hkv"], inp["Hidx"]
     G = Hq // Hkv
     outs = {}
-    for t, (b, p) in enumerate(oracle.query_positions(inp["seq_lens"], inp["cu_seqlens_q"])):
+    kc = _RowCache(inp["k_pool"], inp["kv_dtype"], inp["k_scale"])
+    vc = _RowCache(inp["v_pool"], inp["kv_dtype"], inp["v_scale"])
+    for t, (b, p) in enumerate(inp["_pos"]):
         for hq in range(Hq):
             g = hq // G
             h = g // (Hkv // Hidx)
@@ -225,8 +254,8 @@ def _py_attend(inp, sel, cnt, scale):
                 for s in range(128):
                     if j * 128 + s > p:
                         break
-                    k = [_py_value(x, inp["kv_dtype"], inp["k_scale"]) for x in inp["k_pool"][page, g, s]]
-                    v = [_py_value(x, inp["kv_dtype"], inp["v_scale"]) for x in inp["v_pool"][page, g, s]]
+                    k = kc(page, g, s)
+                    v = vc(page, g, s)
                     zs.append(scale * sum(a * c for a, c in zip(q, k)))
                     vs.append(v)
             m = max(zs)
@@ -247,15 +276,113 @@ def test_attention_brute_force(kv):
         assert abs(res["lse"][t, hq] - l) < 1e-12
 
 
+# ------------------------------------------- prefill query positions
+
+def _prefill_tiny(seed=5, lens=(700, 260), new=(40, 100), **kw):
+    return _tiny_case(seed, lens=lens, prefill_new=new, **kw)
+
+
+def _check_prefill_scores_brute_force():
+    inp = _prefill_tiny(Hidx=2, Hkv=2)
+    sc = oracle.block_scores(inp)
+    ref = _py_scores(inp)
+    for (t, h), row in ref.items():
+        assert np.allclose(sc[t, h, : len(row)], row, rtol=1e-13, atol=1e-13), (t, h)
+        assert np.all(np.isneginf(sc[t, h, len(row):])), (t, h)
+
+
+def _check_prefill_attention_brute_force():
+    inp = _prefill_tiny(Hq=2, Hkv=1, Hidx=1, topk=1)
+    res = oracle.sparse_attention(inp)
+    ref = _py_attend(inp, res["sel"], res["count"], 1.0 / math.sqrt(8))
+    for (t, hq), (o, l) in ref.items():
+        assert np.allclose(res["out"][t, hq], o, rtol=1e-12, atol=1e-12), (t, hq)
+        assert abs(res["lse"][t, hq] - l) < 1e-12, (t, hq)
+
+
+def _check_prefill_equals_full_sequence_causal_sdpa():
+    """A chunk of the sequence's last n tokens, every block selected, equals
+    the last n rows of plain causal attention over the whole sequence
+    (torch SDPA, is_causal=True on the square L x L problem, float64), whose
+    other query rows are filler: no position enters this check."""
+    lens, new = (600, 300), (600, 77)
+    inp = _prefill_tiny(seed=13, lens=lens, new=new, Hq=4, Hkv=2, Hidx=1, D=16, Di=8, topk=8)
+    res = oracle.sparse_attention(inp)
+    q = torch.from_numpy(oracle.decode(inp["q"], "bf16"))
+    rng = torch.Generator().manual_seed(4)
+    row = 0
+    for b, (L, n) in enumerate(zip(lens, new)):
+        nbk = (L + 127) // 128
+        pages = inp["block_table"][b, :nbk].astype(np.int64)
+        k = torch.from_numpy(oracle.decode(inp["k_pool"][pages], "bf16"))
+        v = torch.from_numpy(oracle.decode(inp["v_pool"][pages], "bf16"))
+        k = k.permute(1, 0, 2, 3).reshape(2, nbk * 128, 16)[:, :L].repeat_interleave(2, dim=0)
+        v = v.permute(1, 0, 2, 3).reshape(2, nbk * 128, 16)[:, :L].repeat_interleave(2, dim=0)
+        qf = torch.randn(4, L, 16, generator=rng, dtype=torch.float64)
+        qf[:, L - n:] = q[row:row + n].permute(1, 0, 2)
+        o = torch.nn.functional.scaled_dot_product_attention(qf, k, v, is_causal=True)
+        assert np.allclose(res["out"][row:row + n], o[:, L - n:].permute(1, 0, 2).numpy(),
+                           rtol=1e-11, atol=1e-12), b
+        row += n
+
+
+def test_prefill_scores_brute_force():
+    """Per-query causal block maxima of a prefill chunk (two sequences, one
+    partly new, one all new) by explicit loops at the positions prefix + i."""
+    _check_prefill_scores_brute_force()
+
+
+def test_prefill_attention_brute_force():
+    _check_prefill_attention_brute_force()
+
+
+def test_prefill_equals_full_sequence_causal_sdpa():
+    _check_prefill_equals_full_sequence_causal_sdpa()
+
+
+def test_prefill_positions_golden():
+    """Hand-written positions for a ragged cu_seqlens_q with an empty chunk
+    (tests/golden/prefill_positions.json), and the blocks each query scores."""
+    with open(os.path.join(GOLDEN, "prefill_positions.json")) as f:
+        g = json.load(f)
+    sl, cu = np.array(g["seq_lens"]), np.array(g["cu_seqlens_q"])
+    assert oracle.query_positions(sl, cu) == [tuple(x) for x in g["expected"]]
+    n_new = [int(cu[b + 1] - cu[b]) for b in range(len(sl))]
+    inp = _tiny_case(3, B=len(sl), lens=tuple(int(x) for x in sl), prefill_new=n_new, topk=2)
+    sc = oracle.block_scores(inp)
+    for t, nb in enumerate(g["nb"]):
+        assert np.isfinite(sc[t, 0, :nb]).all() and np.isneginf(sc[t, 0, nb:]).all(), t
+
+
+@pytest.mark.parametrize("shift", [-1, 1])
+def test_position_pins_catch_an_off_by_one(monkeypatch, shift):
+    """A prefill position map off by one (p = L - n + i +- 1), planted in the
+    oracle on the CPU, fails every prefill position pin above."""
+    good = oracle.msa_oracle.query_positions
+
+    def shifted(seq_lens, cu_seqlens_q, positions=None):
+        pos = good(seq_lens, cu_seqlens_q, positions)
+        if cu_seqlens_q is None or positions is not None:
+            return pos
+        return [(b, p + shift) for b, p in pos]
+
+    monkeypatch.setattr(oracle.msa_oracle, "query_positions", shifted)
+    for check in (_check_prefill_scores_brute_force, _check_prefill_attention_brute_force,
+                  _check_prefill_equals_full_sequence_causal_sdpa):
+        with pytest.raises((AssertionError, IndexError, ValueError)):
+            check()
+
+
 # ------------------------------------------ dense equivalence (library pin)
 
 def _dense_sdpa(inp, scale=None):
-    """All visible tokens, via torch SDPA in float64 with an explicit causal mask."""
+    """All visible tokens, via torch SDPA in float64 with an explicit causal
+    mask at the query positions of the case description."""
     q = torch.from_numpy(oracle.decode(inp["q"], inp["q_dtype"]))
     T, Hq, D = q.shape
     G = Hq // inp["Hkv"]
     out = torch.zeros(T, Hq, D, dtype=torch.float64)
-    pos = oracle.query_positions(inp["seq_lens"], inp["cu_seqlens_q"])
+    pos = inp["_pos"]
     for b in range(len(inp["seq_lens"])):
         L = int(inp["seq_lens"][b])
         toks = [t for t, (bb, _) in enumerate(pos) if bb == b]
@@ -311,7 +438,7 @@ def _compacted(inp, sel, cnt):
         nb = (L + 127) // 128
         assert blocks[-1] == nb - 1
         lens[b] = 128 * (c - 1) + (L - 128 * (nb - 1))
-    return dict(inp, block_table=bt, seq_lens=lens)
+    return dict(inp, block_table=bt, seq_lens=lens, _pos=[(b, int(n) - 1) for b, n in enumerate(lens)])
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
@@ -371,7 +498,7 @@ def test_zero_query_gives_mean_of_selected_values():
     inp = _tiny_case(32, lens=(800, 260), Hq=2, Hkv=1, Hidx=1, topk=2)
     inp["q"] = np.zeros_like(inp["q"])
     res = oracle.sparse_attention(inp)
-    for t, (b, p) in enumerate(oracle.query_positions(inp["seq_lens"], None)):
+    for t, (b, p) in enumerate(inp["_pos"]):
         S = res["sel"][t, 0, : res["count"][t, 0]]
         rows = []
         for j in S:
@@ -426,7 +553,7 @@ def test_selection_structure_on_random_case():
     inp = _tiny_case(41, lens=(3000, 2000), Hq=4, Hkv=2, Hidx=2, D=8, Di=8, topk=3,
                      init=1, local=2)
     res = oracle.sparse_attention(inp)
-    for t, (b, p) in enumerate(oracle.query_positions(inp["seq_lens"], None)):
+    for t, (b, p) in enumerate(inp["_pos"]):
         nb = p // 128 + 1
         for h in range(2):
             S = list(res["sel"][t, h, : res["count"][t, h]])
