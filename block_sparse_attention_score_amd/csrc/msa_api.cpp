@@ -319,6 +319,32 @@ msa_status_t hip_status(hipError_t e, const char* what) {
   return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Launch-size limits, checked before a call enqueues anything: a dispatch
+// holds each grid dimension as a 32-bit count of work-items, and the
+// launchers count workgroups in int.
+msa_status_t check_grid(int64_t workgroups, int threads, const char* what) {
+  if (workgroups > 0x7fffffffLL || workgroups * threads > 0xffffffffLL)
+    return fail(MSA_ERR_UNSUPPORTED,
+                "%s: %lld workgroups of %d threads exceed a grid's 32-bit work-item count",
+                what, (long long)workgroups, threads);
+  return MSA_OK;
+}
+
+constexpr int kScanThreads = 256;     // decode and short-chunk scans, selection, combine
+constexpr int kAttendThreads = 512;   // decode attention: eight waves
+int64_t scan_workgroups(int32_t B, int hidx, int32_t MB) {
+  return int64_t(B) * hidx * ((MB + kPagesPerItem - 1) / kPagesPerItem);
+}
+// the attention grid holds every (token, kv head, split) unit, rounded up to
+// one run per XCD
+int64_t attend_workgroups(int nsplit, int hkv, int32_t T) {
+  return (int64_t(nsplit) * hkv * T + 7) / 8 * 8;
+}
+int64_t select_workgroups(int32_t T, int hidx, int32_t MB) {
+  const int64_t rows = int64_t(T) * hidx;
+  return msa::select_wave_fits(MB) ? (rows + 3) / 4 : rows;
+}
+
 // Arguments of the split-K attention (decode).
 msa::AttendArgs attend_args(const msa_params_t& p, const void* q, const void* k_pool,
                             const void* v_pool, int64_t num_pages, const int32_t* block_table,
@@ -354,6 +380,72 @@ msa::AttendArgs attend_args(const msa_params_t& p, const void* q, const void* k_
   a.part_lse = reinterpret_cast<float*>(w + l.part_lse);
   a.tickets = reinterpret_cast<uint32_t*>(w + l.tickets);
   return a;
+}
+
+// Decode with the caller's workspace.  Everything is validated before the
+// first launch.
+msa_status_t sparse_decode_impl(const msa_params_t* params, const void* q, const void* idx_q,
+                                const void* k_pool, const void* v_pool, const void* idx_k_pool,
+                                int64_t num_pages, const int32_t* block_table,
+                                int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs,
+                                void* out, float* lse_out, int32_t* sel_blocks_out,
+                                int32_t* sel_count_out, void* ws, size_t ws_bytes,
+                                void* stream) {
+  msa_status_t st = check_params(params);
+  if (st != MSA_OK) return st;
+  if ((st = check_shape(num_seqs, max_blocks)) != MSA_OK) return st;
+  if (!q || !idx_q || !k_pool || !v_pool || !idx_k_pool || !block_table || !seq_lens || !out)
+    return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if ((sel_blocks_out == nullptr) != (sel_count_out == nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "sel_blocks_out and sel_count_out go together");
+  if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
+  const msa_params_t& p = *params;
+  const DecodeLayout l = decode_layout(p, num_seqs, max_blocks);
+  if ((st = check_grid(scan_workgroups(num_seqs, p.num_idx_heads, max_blocks), kScanThreads,
+                       "index scan")) != MSA_OK ||
+      (st = check_grid(attend_workgroups(l.nsplit_max, p.num_kv_heads, num_seqs),
+                       kAttendThreads, "decode attention")) != MSA_OK)
+    return st;
+  if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
+  log_line("msa_sparse_decode: B=%d max_blocks=%d scan grid %d (%d pages per item), attention "
+           "grid %d x %d x %d (%d blocks per split), G=%d", num_seqs, max_blocks,
+           num_seqs * p.num_idx_heads * ((max_blocks + kPagesPerItem - 1) / kPagesPerItem),
+           kPagesPerItem, l.nsplit_max, p.num_kv_heads, num_seqs, l.bps, group_of(p));
+  if (num_seqs == 0) return ok();
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+
+  // 1. scores of every visible block; workgroup 0 also zeroes the split
+  //    tickets of step 2
+  msa::ScoreArgs a{};
+  a.idx_q = idx_q;
+  a.idx_k = idx_k_pool;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.num_seqs = num_seqs;
+  a.hidx = p.num_idx_heads;
+  a.pages_per_item = kPagesPerItem;
+  a.chunks_per_pair = (max_blocks + kPagesPerItem - 1) / kPagesPerItem;
+  a.scores = reinterpret_cast<float*>(w + l.scores);
+  a.fill_tail = 0;
+  a.zero_words = reinterpret_cast<uint32_t*>(w + l.tickets);
+  a.zero_count = num_seqs * p.num_kv_heads;
+  st = hip_status(msa::launch_decode_score(a, p.idx_dtype, p.idx_dim, s), "score launch");
+  if (st != MSA_OK) return st;
+  // 2. selection inside each attention workgroup, split-K attention, combine
+  msa::AttendArgs aa = attend_args(p, q, k_pool, v_pool, num_pages, block_table, max_blocks,
+                                   seq_lens, num_seqs, nullptr, nullptr, out, lse_out, ws, l);
+  aa.scores = a.scores;
+  aa.topk = p.topk;
+  aa.init = p.init_blocks;
+  aa.local = p.local_blocks;
+  aa.sel_out = sel_blocks_out;
+  aa.cnt_out = sel_count_out;
+  st = hip_status(msa::launch_decode_attend(aa, p.q_dtype, p.kv_dtype, group_of(p), s),
+                  "attention launch");
+  return st == MSA_OK ? ok() : st;
 }
 
 }  // namespace
@@ -415,6 +507,16 @@ msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
     if (params->idx_dtype != MSA_BF16)
       return fail(MSA_ERR_UNSUPPORTED, "prefill scoring needs bf16 index keys");
     if (num_q_tokens == 0) return ok();
+    if (short_chunks(num_seqs, num_q_tokens)) {
+      st = check_grid(scan_workgroups(num_seqs, params->num_idx_heads, max_blocks), kScanThreads,
+                      "chunk scan");
+    } else {
+      const int64_t tiles = (int64_t(num_q_tokens) + 255) / 256;
+      st = check_grid(int64_t(num_seqs) * tiles * params->num_idx_heads *
+                          ((max_blocks + kPrefillBlocksPerChunk - 1) / kPrefillBlocksPerChunk),
+                      kScanThreads, "prefill scoring");
+    }
+    if (st != MSA_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     st = hip_status(msa::launch_fill_f32(scores, int64_t(num_q_tokens) * params->num_idx_heads *
                                                      max_blocks, -INFINITY, s),
@@ -433,6 +535,9 @@ msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
     st = hip_status(msa::launch_prefill_score(pa, params->idx_dim, s), "prefill score launch");
     return st == MSA_OK ? ok() : st;
   }
+  if ((st = check_grid(scan_workgroups(num_seqs, params->num_idx_heads, max_blocks),
+                       kScanThreads, "index scan")) != MSA_OK)
+    return st;
   msa::ScoreArgs a{};
   a.idx_q = idx_q;
   a.idx_k = idx_k_pool;
@@ -467,6 +572,9 @@ msa_status_t msa_select_blocks(const msa_params_t* params, const float* scores,
   // (no sequences: nothing to select, as in msa_sparse_prefill; the kernel
   // reads at least one sequence's offsets)
   if (T == 0 || num_seqs == 0) return ok();
+  if ((st = check_grid(select_workgroups(T, params->num_idx_heads, max_blocks), kScanThreads,
+                       "selection")) != MSA_OK)
+    return st;
   const msa::SelectArgs a = select_args(*params, scores, max_blocks, seq_lens, cu_seqlens_q,
                                         num_seqs, T, sel_blocks, sel_count);
   st = hip_status(launch_selection(a, static_cast<hipStream_t>(stream)), "select launch");
@@ -481,56 +589,9 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const 
                                float* lse_out, int32_t* sel_blocks_out,
                                int32_t* sel_count_out, void* ws, size_t ws_bytes,
                                void* stream) {
-  msa_status_t st = check_params(params);
-  if (st != MSA_OK) return st;
-  if ((st = check_shape(num_seqs, max_blocks)) != MSA_OK) return st;
-  if (!q || !idx_q || !k_pool || !v_pool || !idx_k_pool || !block_table || !seq_lens || !out)
-    return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
-  if ((sel_blocks_out == nullptr) != (sel_count_out == nullptr))
-    return fail(MSA_ERR_INVALID_ARG, "sel_blocks_out and sel_count_out go together");
-  if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
-  const msa_params_t& p = *params;
-  const DecodeLayout l = decode_layout(p, num_seqs, max_blocks);
-  if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
-  log_line("msa_sparse_decode: B=%d max_blocks=%d scan grid %d (%d pages per item), attention "
-           "grid %d x %d x %d (%d blocks per split), G=%d", num_seqs, max_blocks,
-           num_seqs * p.num_idx_heads * ((max_blocks + kPagesPerItem - 1) / kPagesPerItem),
-           kPagesPerItem, l.nsplit_max, p.num_kv_heads, num_seqs, l.bps, group_of(p));
-  if (num_seqs == 0) return ok();
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(ws);
-
-  // 1. scores of every visible block; workgroup 0 also zeroes the split
-  //    tickets of step 2
-  msa::ScoreArgs a{};
-  a.idx_q = idx_q;
-  a.idx_k = idx_k_pool;
-  a.num_pages = num_pages;
-  a.block_table = block_table;
-  a.max_blocks = max_blocks;
-  a.seq_lens = seq_lens;
-  a.num_seqs = num_seqs;
-  a.hidx = p.num_idx_heads;
-  a.pages_per_item = kPagesPerItem;
-  a.chunks_per_pair = (max_blocks + kPagesPerItem - 1) / kPagesPerItem;
-  a.scores = reinterpret_cast<float*>(w + l.scores);
-  a.fill_tail = 0;
-  a.zero_words = reinterpret_cast<uint32_t*>(w + l.tickets);
-  a.zero_count = num_seqs * p.num_kv_heads;
-  st = hip_status(msa::launch_decode_score(a, p.idx_dtype, p.idx_dim, s), "score launch");
-  if (st != MSA_OK) return st;
-  // 2. selection inside each attention workgroup, split-K attention, combine
-  msa::AttendArgs aa = attend_args(p, q, k_pool, v_pool, num_pages, block_table, max_blocks,
-                                   seq_lens, num_seqs, nullptr, nullptr, out, lse_out, ws, l);
-  aa.scores = a.scores;
-  aa.topk = p.topk;
-  aa.init = p.init_blocks;
-  aa.local = p.local_blocks;
-  aa.sel_out = sel_blocks_out;
-  aa.cnt_out = sel_count_out;
-  st = hip_status(msa::launch_decode_attend(aa, p.q_dtype, p.kv_dtype, group_of(p), s),
-                  "attention launch");
-  return st == MSA_OK ? ok() : st;
+  return sparse_decode_impl(params, q, idx_q, k_pool, v_pool, idx_k_pool, num_pages, block_table,
+                            max_blocks, seq_lens, num_seqs, out, lse_out, sel_blocks_out,
+                            sel_count_out, ws, ws_bytes, stream);
 }
 
 msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q, const void* k_pool,
@@ -546,6 +607,9 @@ msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q, const 
     return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
   const DecodeLayout l = decode_layout(*params, num_seqs, max_blocks);
+  if ((st = check_grid(attend_workgroups(l.nsplit_max, params->num_kv_heads, num_seqs),
+                       kAttendThreads, "decode attention")) != MSA_OK)
+    return st;
   if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
   log_line("msa_sparse_attend: B=%d attention grid %d x %d x %d (%d blocks per split)", num_seqs,
            l.nsplit_max, params->num_kv_heads, num_seqs, l.bps);
@@ -575,6 +639,13 @@ msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new, const 
     return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (num_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "num_tokens=%d < 0", num_tokens);
   if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
+  {
+    const int64_t per_token = 2 * int64_t(params->num_kv_heads) * (params->head_dim / 8) +
+                              int64_t(params->num_idx_heads) * (params->idx_dim / 8);
+    if ((st = check_grid((int64_t(num_tokens) * per_token + 255) / 256, 256, "append")) !=
+        MSA_OK)
+      return st;
+  }
   log_line("msa_append_kv: T=%d into %lld pages (kv dtype %d)", num_tokens,
            (long long)num_pages, params->kv_dtype);
   if (num_tokens == 0) return ok();
@@ -626,6 +697,32 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
     return fail(MSA_ERR_UNSUPPORTED, "num_q_tokens=%d above %d", num_q_tokens,
                 kMaxPrefillTokens - 1);
   const PrefillLayout l = prefill_layout(p, num_seqs, num_q_tokens, max_blocks);
+  if (short_chunks(num_seqs, num_q_tokens)) {
+    st = check_grid(scan_workgroups(num_seqs, p.num_idx_heads, max_blocks), kScanThreads,
+                    "chunk scan");
+  } else {
+    const int64_t tiles = (int64_t(num_q_tokens) + 255) / 256;
+    st = check_grid(int64_t(num_seqs) * tiles * p.num_idx_heads *
+                        ((max_blocks + kPrefillBlocksPerChunk - 1) / kPrefillBlocksPerChunk),
+                    kScanThreads, "prefill scoring");
+  }
+  if (st != MSA_OK) return st;
+  if ((st = check_grid(select_workgroups(num_q_tokens, p.num_idx_heads, max_blocks),
+                       kScanThreads, "selection")) != MSA_OK)
+    return st;
+  if (prefill_key_major(p, num_seqs, num_q_tokens)) {
+    // list kernels: one grid row per sequence; combine: 16 / G units per workgroup
+    if (num_seqs > 65535)
+      return fail(MSA_ERR_UNSUPPORTED, "num_seqs=%d above 65535 for a long prefill chunk",
+                  num_seqs);
+    const int per = 16 / group_of(p);
+    if ((st = check_grid((int64_t(num_q_tokens) * p.num_kv_heads + per - 1) / per,
+                         kScanThreads, "prefill combine")) != MSA_OK)
+      return st;
+  } else if ((st = check_grid(attend_workgroups(l.nsplit_max, p.num_kv_heads, num_q_tokens),
+                              kAttendThreads, "per-token attention")) != MSA_OK) {
+    return st;
+  }
   if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
   if (short_chunks(num_seqs, num_q_tokens))
     log_line("msa_sparse_prefill: B=%d T=%d short chunks: scan with four queries per pass, "
@@ -755,7 +852,9 @@ msa_status_t msa_fp8_dequant(const uint8_t* in, float* out, int64_t n, float sca
   if (n > 0 && (!in || !out)) return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!std::isfinite(scale)) return fail(MSA_ERR_INVALID_ARG, "scale must be finite");
   if (!is_fp8(dtype)) return fail(MSA_ERR_UNSUPPORTED, "dtype=%d is not an fp8 format", dtype);
-  const msa_status_t st = hip_status(
+  msa_status_t st = check_grid((n / 8 + 1 + 255) / 256, 256, "fp8 dequant");
+  if (st != MSA_OK) return st;
+  st = hip_status(
       msa::launch_fp8_dequant(in, out, n, scale, dtype == MSA_FP8_E5M2,
                               static_cast<hipStream_t>(stream)),
       "fp8 dequant launch");

@@ -235,3 +235,26 @@ def test_select_without_sequences_enqueues_nothing():
     lib = msa.load()
     assert lib.msa_select_blocks(ctypes.byref(p), FAKE, 16, FAKE, FAKE, 0, 5, FAKE, FAKE,
                                  None) == _lib.MSA_OK
+
+
+def test_launch_sizes_past_the_grid_range_are_refused():
+    """A launch whose grid would exceed a dispatch's 32-bit work-item count is
+    refused on the host before anything is enqueued (fake pointers, never
+    dereferenced): the decode attention grid (512 threads per workgroup), the
+    append grid and the fp8 dequantisation grid."""
+    lib = msa.load()
+    # 5M sequences x 2 kv heads x 1 split = 10M attention workgroups
+    assert decode_call(base_cfg(), num_seqs=5_000_000, max_blocks=8) == _lib.MSA_ERR_UNSUPPORTED
+    assert "32-bit" in lib.msa_last_error().decode()
+    p = base_cfg().params()
+    assert lib.msa_sparse_attend(ctypes.byref(p), FAKE, FAKE, FAKE, 64, FAKE, 8, FAKE,
+                                 5_000_000, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                                 None) == _lib.MSA_ERR_UNSUPPORTED
+    # 50M tokens x 96 sixteen-byte pieces each
+    assert append_call(base_cfg(), num_tokens=50_000_000) == _lib.MSA_ERR_UNSUPPORTED
+    assert lib.msa_fp8_dequant(FAKE, FAKE, 1 << 36, 1.0, _lib.MSA_FP8_E4M3,
+                               None) == _lib.MSA_ERR_UNSUPPORTED
+    # a long prefill chunk over more sequences than the list kernels' grid rows
+    assert lib.msa_sparse_prefill(ctypes.byref(p), *([FAKE] * 5), 64, FAKE, 8, FAKE, FAKE,
+                                  70000, 600000, FAKE, None, None, None, FAKE, 1 << 40,
+                                  None) == _lib.MSA_ERR_UNSUPPORTED
