@@ -20,6 +20,7 @@ from .api import (  # noqa: F401
     select_blocks,
     sparse_attend,
     sparse_decode,
+    sparse_decode_noalloc,
     sparse_prefill,
     version,
 )

@@ -68,6 +68,8 @@ SIGNATURES = {
     "msa_select_blocks": (_I32, [_PP, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P]),
     "msa_sparse_decode": (_I32, [_PP, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _P, _P,
                                  _P, _P, _P, _SZ, _P]),
+    "msa_sparse_decode_noalloc": (_I32, [_PP, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32,
+                                         _P, _P, _P, _P, _P]),
     "msa_sparse_attend": (_I32, [_PP, _P, _P, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P,
                                  _P, _SZ, _P]),
     "msa_sparse_prefill": (_I32, [_PP, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32,

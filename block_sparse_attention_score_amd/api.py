@@ -188,6 +188,22 @@ def sparse_decode(cfg: MsaConfig, q, idx_q, k_pool, v_pool, idx_k_pool, block_ta
     return out
 
 
+def sparse_decode_noalloc(cfg: MsaConfig, q, idx_q, k_pool, v_pool, idx_k_pool, block_table,
+                          seq_lens, out, lse=None, sel_blocks=None, sel_count=None,
+                          stream=None):
+    """msa_sparse_decode_noalloc: decode into the caller's ``out`` (and the
+    optional lse / selection outputs) with the library's own per-GPU scratch
+    as the workspace; nothing is allocated, here or in the library."""
+    _check_i32(block_table, seq_lens)
+    B, MB = block_table.shape
+    p = cfg.params()
+    check(load().msa_sparse_decode_noalloc(
+        ctypes.byref(p), _ptr(q), _ptr(idx_q), _ptr(k_pool), _ptr(v_pool), _ptr(idx_k_pool),
+        k_pool.shape[0], _ptr(block_table), MB, _ptr(seq_lens), B, _ptr(out), _ptr(lse),
+        _ptr(sel_blocks), _ptr(sel_count), _stream(stream)))
+    return out
+
+
 def sparse_attend(cfg: MsaConfig, q, k_pool, v_pool, block_table, seq_lens, sel_blocks,
                   sel_count, out=None, lse=None, workspace=None, stream=None):
     """Step 3 alone (decode) over a given selection.  Returns (out, lse)."""

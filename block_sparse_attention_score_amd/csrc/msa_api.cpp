@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "msa.h"
 #include "msa_internal.h"
@@ -382,15 +383,44 @@ msa::AttendArgs attend_args(const msa_params_t& p, const void* q, const void* k_
   return a;
 }
 
-// Decode with the caller's workspace.  Everything is validated before the
-// first launch.
+// Scratch of msa_sparse_decode_noalloc: the decode workspace of callers that
+// cannot allocate.  One copy per GPU, held until the process ends.  Host code
+// never uses the array's name as an address: each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+msa_status_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  msa_status_t st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != MSA_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MSA_ERR_UNSUPPORTED, "device %d: scratch is kept for devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    st = hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress");
+    if (st != MSA_OK) return st;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
+// Decode with the caller's workspace, or (use_scratch) with this device's
+// scratch.  Everything is validated before the first launch.
 msa_status_t sparse_decode_impl(const msa_params_t* params, const void* q, const void* idx_q,
                                 const void* k_pool, const void* v_pool, const void* idx_k_pool,
                                 int64_t num_pages, const int32_t* block_table,
                                 int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs,
                                 void* out, float* lse_out, int32_t* sel_blocks_out,
                                 int32_t* sel_count_out, void* ws, size_t ws_bytes,
-                                void* stream) {
+                                bool use_scratch, void* stream) {
   msa_status_t st = check_params(params);
   if (st != MSA_OK) return st;
   if ((st = check_shape(num_seqs, max_blocks)) != MSA_OK) return st;
@@ -406,9 +436,19 @@ msa_status_t sparse_decode_impl(const msa_params_t* params, const void* q, const
       (st = check_grid(attend_workgroups(l.nsplit_max, p.num_kv_heads, num_seqs),
                        kAttendThreads, "decode attention")) != MSA_OK)
     return st;
+  if (use_scratch) {
+    if (l.total > kScratchBytes)
+      return fail(MSA_ERR_UNSUPPORTED,
+                  "B=%d with max_blocks=%d needs %zu bytes of decode scratch; the library holds "
+                  "%zu (use msa_sparse_decode with a workspace)",
+                  num_seqs, max_blocks, l.total, kScratchBytes);
+    if ((st = scratch_of_current_device(&ws)) != MSA_OK) return st;
+    ws_bytes = kScratchBytes;
+  }
   if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
-  log_line("msa_sparse_decode: B=%d max_blocks=%d scan grid %d (%d pages per item), attention "
-           "grid %d x %d x %d (%d blocks per split), G=%d", num_seqs, max_blocks,
+  log_line("msa_sparse_decode%s: B=%d max_blocks=%d scan grid %d (%d pages per item), attention "
+           "grid %d x %d x %d (%d blocks per split), G=%d", use_scratch ? "_noalloc" : "",
+           num_seqs, max_blocks,
            num_seqs * p.num_idx_heads * ((max_blocks + kPagesPerItem - 1) / kPagesPerItem),
            kPagesPerItem, l.nsplit_max, p.num_kv_heads, num_seqs, l.bps, group_of(p));
   if (num_seqs == 0) return ok();
@@ -591,7 +631,20 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const 
                                void* stream) {
   return sparse_decode_impl(params, q, idx_q, k_pool, v_pool, idx_k_pool, num_pages, block_table,
                             max_blocks, seq_lens, num_seqs, out, lse_out, sel_blocks_out,
-                            sel_count_out, ws, ws_bytes, stream);
+                            sel_count_out, ws, ws_bytes, false, stream);
+}
+
+msa_status_t msa_sparse_decode_noalloc(const msa_params_t* params, const void* q,
+                                       const void* idx_q, const void* k_pool,
+                                       const void* v_pool, const void* idx_k_pool,
+                                       int64_t num_pages, const int32_t* block_table,
+                                       int32_t max_blocks, const int32_t* seq_lens,
+                                       int32_t num_seqs, void* out, float* lse_out,
+                                       int32_t* sel_blocks_out, int32_t* sel_count_out,
+                                       void* stream) {
+  return sparse_decode_impl(params, q, idx_q, k_pool, v_pool, idx_k_pool, num_pages, block_table,
+                            max_blocks, seq_lens, num_seqs, out, lse_out, sel_blocks_out,
+                            sel_count_out, nullptr, 0, true, stream);
 }
 
 msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q, const void* k_pool,

@@ -185,6 +185,29 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q,
                                size_t ws_bytes, void* stream);
 
 /*
+ * msa_sparse_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops that
+ * must not call the allocator, harnesses that forbid it.  Same arguments,
+ * results and kernels as msa_sparse_decode; the workspace is a scratch area
+ * the library keeps in each GPU's memory (16 MiB per GPU, held until the
+ * process ends; its address is looked up once per device, on the first call
+ * with that device current).  The stream must belong to the current device.
+ * Calls whose decode workspace (msa_decode_workspace_size()) exceeds 16 MiB
+ * return MSA_ERR_UNSUPPORTED and enqueue nothing.  No call allocates or frees
+ * memory.  Every call on one GPU shares that GPU's scratch: calls that may
+ * overlap on one GPU (different streams without ordering) race and must not
+ * be issued; each call clears what it needs cleared inside its own kernels.
+ */
+msa_status_t msa_sparse_decode_noalloc(const msa_params_t* params, const void* q,
+                                       const void* idx_q, const void* k_pool,
+                                       const void* v_pool, const void* idx_k_pool,
+                                       int64_t num_pages, const int32_t* block_table,
+                                       int32_t max_blocks, const int32_t* seq_lens,
+                                       int32_t num_seqs, void* out, float* lse_out,
+                                       int32_t* sel_blocks_out, int32_t* sel_count_out,
+                                       void* stream);
+
+/*
  * Step 3 alone (decode): attention over a given selection sel_blocks
  * [B, Hidx, Kmax] / sel_count [B, Hidx] (ascending block ids < nb).  Same
  * outputs and workspace as msa_sparse_decode.

@@ -258,3 +258,25 @@ def test_launch_sizes_past_the_grid_range_are_refused():
     assert lib.msa_sparse_prefill(ctypes.byref(p), *([FAKE] * 5), 64, FAKE, 8, FAKE, FAKE,
                                   70000, 600000, FAKE, None, None, None, FAKE, 1 << 40,
                                   None) == _lib.MSA_ERR_UNSUPPORTED
+
+
+def noalloc_call(cfg, num_seqs=4, max_blocks=16, q=FAKE):
+    p = cfg.params()
+    return msa.load().msa_sparse_decode_noalloc(
+        ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, 64, FAKE, max_blocks, FAKE, num_seqs,
+        FAKE, None, None, None, None)
+
+
+def test_noalloc_decode_validates_before_touching_the_device():
+    """The no-allocation decode checks its arguments and its scratch limit
+    (16 MiB) on the host first; none of these calls reaches HIP."""
+    lib = msa.load()
+    assert noalloc_call(base_cfg(topk=5)) == _lib.MSA_ERR_UNSUPPORTED
+    assert noalloc_call(base_cfg(), q=None) == _lib.MSA_ERR_INVALID_ARG
+    assert noalloc_call(base_cfg(), max_blocks=0) == _lib.MSA_ERR_INVALID_ARG
+    # 4096 sequences x 2 index heads x 8192 blocks of scores alone = 256 MiB
+    need = msa.decode_workspace_size(base_cfg(), 4096, 8192)
+    assert need > 16 << 20
+    assert noalloc_call(base_cfg(), num_seqs=4096, max_blocks=8192) == _lib.MSA_ERR_UNSUPPORTED
+    err = lib.msa_last_error().decode()
+    assert "scratch" in err and str(need) in err
