@@ -1,16 +1,23 @@
 """Benchmark of block-sparse attention on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-configs]
+                    [--no-cpu-baseline]
 
-Default workload: decode, batch 32 x 32768 tokens (the headline metric).
-``--workload prefill_4x4096_p16k`` measures chunked prefill instead (tokens/s,
-MFMA roofline of its dominant kernel).
+Default: decode of 64 sequences with lengths drawn uniformly from 4096 to
+131072 tokens (the largest decode workload on one GPU) is the headline line;
+the four other workloads of the method's configurations are measured after it
+in the same run and reported under "configs": decode 2 x 2048, decode
+32 x 32768, fp8-e4m3 decode 32 x 65536 and chunked prefill 4 x 4096 over a
+16384-token prefix.  ``--workload NAME`` makes NAME the headline (prefill and
+append workloads report tokens/s); ``--no-configs`` measures the headline
+alone (profiling runs).
 
 A decode step is one msa_sparse_decode call (score every block of the index keys,
 select, split-K attend over the selected blocks, combine) over one batch of
-synthetic inputs already resident in HBM.  Before every timed step a 1 GiB
-buffer is overwritten so that no input is served from the L2 or the 256 MB
-Infinity Cache; HIP events on the library's stream bracket each step.
+synthetic inputs already resident in HBM; a prefill step is one
+msa_sparse_prefill call.  Before every timed step a 1 GiB buffer is
+overwritten so that no input is served from the L2 or the 256 MB Infinity
+Cache; HIP events on the library's stream bracket each step.
 
 Prints ONE JSON line: queries/s (value), achieved HBM GB/s on the touched
 bytes of the step, the roofline of the dominant kernel (the index-key scan,
@@ -30,7 +37,11 @@ import numpy as np
 
 METRIC = "sparse-decode queries/sec + achieved HBM GB/s (touched bytes) at 1 MI355X"
 HBM_PEAK_GBS = 8000.0
-DEFAULT_WORKLOAD = "decode_b32_l32k"
+DEFAULT_WORKLOAD = "decode_b64_lvar"
+# the other workloads of the method's configurations, reported beside the headline
+SUB_CONFIGS = ["decode_b2_l2048", "decode_b32_l32k", "decode_fp8_b32_l64k",
+               "prefill_4x4096_p16k"]
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 FLUSH_BYTES = 1 << 30
 
 
@@ -41,13 +52,16 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure the headline workload only")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a read+write kernel over 1 GiB (HBM counter calibration)")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("SCAN_RD", "SCAN_WR", "COPY_RD",
                                                           "COPY_WR"),
-                    help="rocprofv3 --pmc output folders -> profiles/ HBM traffic summary")
+                    help="rocprofv3 --pmc output folders -> profiles/ HBM traffic summary "
+                         "of the --workload decode scan")
     return ap.parse_args()
 
 
@@ -170,8 +184,11 @@ def cpu_baseline(case, spec, seconds):
 TRAFFIC_RD = ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_128B_sum", "TCC_EA0_RDREQ_32B_sum",
               "TCC_BUBBLE_sum"]
 TRAFFIC_WR = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum"]
-TRAFFIC_JSON = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "decode_b32_l32k_scan_hbm_traffic.json")
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+
+
+def traffic_json(workload_name: str) -> str:
+    return os.path.join(PROFILES, f"{workload_name}_scan_hbm_traffic.json")
 COPY_PROBE_BYTES = 1 << 30
 SCAN_SOURCES = ["msa_score.h", "msa_score.hip", "msa_device.h", "msa_internal.h"]
 
@@ -231,8 +248,12 @@ def _write_bytes(c):
     return 64 * w64 + 32 * (wr - w64)
 
 
-def traffic_summary(scan_rd, scan_wr, copy_rd, copy_wr):
-    """Write the scan's calibrated HBM traffic to profiles/ (JSON for bench.py, Markdown for readers)."""
+def traffic_summary(name, scan_rd, scan_wr, copy_rd, copy_wr):
+    """Write the scan's calibrated HBM traffic of decode workload ``name`` to
+    profiles/ (JSON for bench.py, Markdown for readers)."""
+    from synth import WORKLOAD_SEEDS, workload
+    from synth.inputs import _draw_seq_lens
+
     med = lambda xs: float(np.median(xs))
     s_rd = _counters(scan_rd, "decode_score_kernel")
     s_wr = _counters(scan_wr, "decode_score_kernel")
@@ -243,31 +264,37 @@ def traffic_summary(scan_rd, scan_wr, copy_rd, copy_wr):
     rd = med([_read_bytes(c) for c in s_rd]) * f_rd
     wr = med([_write_bytes(c) for c in s_wr]) * f_wr
     stock = med([_fetch_size_bytes(c) for c in s_rd])
-    res = {"kernel": "decode_score_kernel", "workload": DEFAULT_WORKLOAD,
+    spec = workload(name)
+    lens = _draw_seq_lens(spec, WORKLOAD_SEEDS[name]).numpy().astype(np.int64)
+    alg = score_kernel_bytes(spec, lens, int(((lens + 127) // 128).max()))
+    res = {"kernel": "decode_score_kernel", "workload": name,
            "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
-           "traffic_bytes_per_launch": rd + wr, "copy_factor_read": f_rd,
-           "copy_factor_write": f_wr, "stock_fetch_size_bytes": stock,
+           "traffic_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": alg,
+           "copy_factor_read": f_rd, "copy_factor_write": f_wr, "stock_fetch_size_bytes": stock,
            "dispatches": [len(s_rd), len(s_wr)], "source_sha256": scan_source_hash()}
-    with open(TRAFFIC_JSON, "w") as f:
+    path = traffic_json(name)
+    with open(path, "w") as f:
         json.dump(res, f, indent=1)
-    md = TRAFFIC_JSON[:-5] + ".md"
-    with open(md, "w") as f:
+    lens_txt = (f"L = {lens[0]}" if (lens == lens[0]).all()
+                else f"L from {lens.min()} to {lens.max()}, mean {lens.mean():.0f}")
+    with open(path[:-5] + ".md", "w") as f:
         f.write(
-            "# HBM traffic of the decode index scan, decode_b32_l32k (B=32, L=32768, 2 index heads, Di=128)\n\n"
+            f"# HBM traffic of the decode index scan, {name} (B={spec['B']}, {lens_txt}, "
+            f"{spec['Hidx']} index heads, Di={spec['Di']})\n\n"
             "Commands (run from the repository root on one MI355X; each pass alone):\n\n"
             "    cd /tmp && export TMPDIR=/tmp\n"
-            f"    rocprofv3 --pmc {' '.join(TRAFFIC_RD)} --output-format csv -d <scan_rd> -- python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline\n"
-            f"    rocprofv3 --pmc {' '.join(TRAFFIC_WR)} --output-format csv -d <scan_wr> -- python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline\n"
+            f"    rocprofv3 --pmc {' '.join(TRAFFIC_RD)} --output-format csv -d <scan_rd> -- python3 <repo>/bench.py --workload {name} --no-configs --steps 3 --warmup 1 --no-cpu-baseline\n"
+            f"    rocprofv3 --pmc {' '.join(TRAFFIC_WR)} --output-format csv -d <scan_wr> -- python3 <repo>/bench.py --workload {name} --no-configs --steps 3 --warmup 1 --no-cpu-baseline\n"
             f"    rocprofv3 --pmc {' '.join(TRAFFIC_RD)} --output-format csv -d <copy_rd> -- python3 <repo>/bench.py --copy-probe\n"
             f"    rocprofv3 --pmc {' '.join(TRAFFIC_WR)} --output-format csv -d <copy_wr> -- python3 <repo>/bench.py --copy-probe\n"
-            "    python3 bench.py --traffic-summary <scan_rd> <scan_wr> <copy_rd> <copy_wr>\n\n"
+            f"    python3 bench.py --workload {name} --traffic-summary <scan_rd> <scan_wr> <copy_rd> <copy_wr>\n\n"
             "Bytes per launch are 128 x RDREQ_128B + 64 x (RDREQ - RDREQ_128B - RDREQ_32B) + 32 x RDREQ_32B\n"
             "(reads) and 64 x WRREQ_64B + 32 x (WRREQ - WRREQ_64B) (writes), medians over the dispatches,\n"
             "scaled by the copy probe (1 GiB read and written by one elementwise kernel).\n\n"
             "| quantity | value |\n|---|---|\n"
             f"| scan reads per launch | {rd / 1e6:.1f} MB |\n"
             f"| scan writes per launch | {wr / 1e6:.3f} MB |\n"
-            f"| algorithmic bytes per launch | {score_kernel_bytes_default() / 1e6:.1f} MB |\n"
+            f"| algorithmic bytes per launch | {alg / 1e6:.1f} MB |\n"
             f"| copy-probe factor, reads / writes | {f_rd:.3f} / {f_wr:.3f} |\n"
             f"| stock FETCH_SIZE expression for the scan | {stock / 1e6:.1f} MB |\n"
             f"| dispatches (read pass, write pass) | {len(s_rd)}, {len(s_wr)} |\n"
@@ -275,22 +302,11 @@ def traffic_summary(scan_rd, scan_wr, copy_rd, copy_wr):
     print(json.dumps(res))
 
 
-def score_kernel_bytes_default():
-    """Algorithmic bytes of one scan launch of the default workload (every
-    sequence at its fixed length)."""
-    from synth import workload
-    spec = workload(DEFAULT_WORKLOAD)
-    kind, length = spec["seq_lens"]
-    assert kind == "fixed"
-    lens = np.full(spec["B"], length, dtype=np.int64)
-    return score_kernel_bytes(spec, lens, int((length + 127) // 128))
-
-
-def measured_traffic():
-    """The calibrated scan traffic per launch, while the scan's sources are the
-    ones it was measured on; else None."""
+def measured_traffic(name):
+    """The calibrated scan traffic per launch of decode workload ``name``,
+    while the scan's sources are the ones it was measured on; else None."""
     try:
-        with open(TRAFFIC_JSON) as f:
+        with open(traffic_json(name)) as f:
             t = json.load(f)
     except OSError:
         return None
@@ -299,10 +315,41 @@ def measured_traffic():
     return t["traffic_bytes_per_launch"]
 
 
+def device_info(dev):
+    import torch
+    props = torch.cuda.get_device_properties(dev)
+    return {"device": torch.cuda.get_device_name(dev),
+            "device_arch": getattr(props, "gcnArchName", "unknown")}
+
+
+def timed_steps(fn, n, flush, stream):
+    """n calls of fn, each after a 1 GiB overwrite, HIP events on ``stream``
+    around each call; returns the per-call times in ms."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for i in range(n):
+        flush.fill_(i)
+        evs[i][0].record(stream)
+        fn()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def sub_entry(res):
+    """What a workload measured beside the headline reports."""
+    keep = ("value", "unit", "ms_per_step", "ms_per_step_median", "hbm_gbps", "hbm_frac",
+            "touched_bytes", "stages_ms", "mfma_tflops", "mfma_frac", "flops", "roofline")
+    out = {k: res[k] for k in keep if k in res}
+    out["config"] = res["config"]
+    return out
+
+
 def main():
     args = parse()
     if args.traffic_summary:
-        return traffic_summary(*args.traffic_summary)
+        return traffic_summary(args.workload, *args.traffic_summary)
     if args.copy_probe:
         return copy_probe()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -313,17 +360,34 @@ def main():
 
     import torch
 
+    from synth import workload
+
+    measure = {"decode": measure_decode, "prefill": measure_prefill, "append": measure_append}
+    spec = workload(args.workload)
+    res = measure[spec["kind"]](args, args.workload, headline=True)
+    if not args.no_configs and args.workload == DEFAULT_WORKLOAD:
+        res["configs"] = {}
+        for name in SUB_CONFIGS:
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            sub = measure[workload(name)["kind"]](args, name, headline=False)
+            res["configs"][name] = sub_entry(sub)
+            torch.cuda.empty_cache()
+    print(json.dumps(res), flush=True)
+
+
+def measure_decode(args, name, headline):
+    """One decode workload: step time over K cold-cache steps, touched bytes,
+    the standalone index scan (the dominant kernel); on the headline also the
+    warm step and the oracle on the host cores."""
+    import torch
+
     import block_sparse_attention_score_amd as msa
     from synth import WORKLOAD_SEEDS, generate, workload
 
-    spec = workload(args.workload)
-    if spec["kind"] == "prefill":
-        return bench_prefill(args, spec)
-    if spec["kind"] == "append":
-        return bench_append(args, spec)
+    spec = workload(name)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    case = generate(spec, WORKLOAD_SEEDS[args.workload], device=dev)
+    case = generate(spec, WORKLOAD_SEEDS[name], device=dev)
     cfg = msa.MsaConfig.from_spec(spec)
     B, MB = case.B, case.max_blocks
     ws = msa.alloc_workspace(msa.decode_workspace_size(cfg, B, MB), dev)
@@ -349,41 +413,18 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region: K steps, cold caches, events on the library's stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    for i in range(args.steps):
-        flush.fill_(i)
-        evs[i][0].record(stream)
-        step()
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
+    step_ms = timed_steps(step, args.steps, flush, stream)
     t_wall = time.perf_counter() - t_wall0
-    step_ms = np.array([a.elapsed_time(b) for a, b in evs])
     ms = float(step_ms.mean())
-
-    # ---- warm back-to-back steps (context only)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    warm_ms = e0.elapsed_time(e1) / args.steps
 
     # ---- dominant kernel: the index-key scan, standalone, cold caches
     scores = torch.empty((B, cfg.num_idx_heads, MB), dtype=torch.float32, device=dev)
-    kevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(args.steps)]
-    for i in range(args.steps):
-        flush.fill_(i)
-        kevs[i][0].record(stream)
-        msa.block_score(cfg, case.idx_q, case.idx_k_pool, case.block_table, case.seq_lens,
-                        scores=scores)
-        kevs[i][1].record(stream)
-    torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in kevs]))
+    k_ms = float(timed_steps(lambda: msa.block_score(cfg, case.idx_q, case.idx_k_pool,
+                                                     case.block_table, case.seq_lens,
+                                                     scores=scores),
+                             args.steps, flush, stream).mean())
     k_bytes = score_kernel_bytes(spec, lens, MB)
     k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
 
@@ -400,7 +441,7 @@ def main():
         "vs_baseline": None,
         "dtype": spec["kv"] if spec["kv"] != "bf16" else "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": B, "seq_lens": spec["seq_lens"],
+        "config": {"workload": name, "batch": B, "seq_lens": spec["seq_lens"],
                    "q_heads": spec["Hq"], "kv_heads": spec["Hkv"], "idx_heads": spec["Hidx"],
                    "head_dim": spec["D"], "idx_dim": spec["Di"], "topk": spec["topk"],
                    "init": spec["init"], "local": spec["local"], "kv_dtype": spec["kv"],
@@ -409,32 +450,40 @@ def main():
         "hbm_frac": total_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "touched_bytes": {"idx_keys": idx_b, "selected_kv": kv_b, "small": small_b},
         "ms_per_step_median": float(np.median(step_ms)),
-        "ms_per_step_warm": warm_ms,
         "wall_s_timed_region": t_wall,
         "roofline": {"kernel": "decode_score_kernel (index-key scan)", "bound": "hbm",
                      "achieved": k_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": k_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic() if args.workload == DEFAULT_WORKLOAD else None,
+                     "frac": k_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(name),
                      "bytes_per_launch": k_bytes, "ms_per_launch": k_ms},
-        "device": torch.cuda.get_device_name(dev),
+        **device_info(dev),
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, spec, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+    if headline:
+        # warm back-to-back steps (context only)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["ms_per_step_warm"] = e0.elapsed_time(e1) / args.steps
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline(case, spec, args.cpu_seconds)
+    return res
 
 
-def bench_prefill(args, spec):
+def measure_prefill(args, name, headline):
     """Chunked prefill: tokens/s of msa_sparse_prefill, with the index-score
     GEMM and the selection timed standalone on the same inputs (attention is
     the remainder of the step)."""
     import torch
 
     import block_sparse_attention_score_amd as msa
-    from synth import WORKLOAD_SEEDS, generate
+    from synth import WORKLOAD_SEEDS, generate, workload
 
+    spec = workload(name)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    case = generate(spec, WORKLOAD_SEEDS[args.workload], device=dev)
+    case = generate(spec, WORKLOAD_SEEDS[name], device=dev)
     cfg = msa.MsaConfig.from_spec(spec)
     B, MB, T = case.B, case.max_blocks, case.T
     ws = msa.alloc_workspace(msa.prefill_workspace_size(cfg, B, T, MB), dev)
@@ -457,15 +506,7 @@ def bench_prefill(args, spec):
     f_score, f_attn = prefill_flops(spec, lens, cu, valid)
 
     def timed(fn, n):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n)]
-        for i in range(n):
-            flush.fill_(i)
-            evs[i][0].record(stream)
-            fn()
-            evs[i][1].record(stream)
-        torch.cuda.synchronize()
-        return np.array([a.elapsed_time(b) for a, b in evs])
+        return timed_steps(fn, n, flush, stream)
 
     for _ in range(args.warmup):
         step()
@@ -486,7 +527,7 @@ def bench_prefill(args, spec):
     # short chunks (at most 8 new tokens per sequence on average) take the
     # page-scan path: HBM-bound like decode
     short = T <= 8 * B
-    peak = 2500.0
+    peak = MFMA_BF16_PEAK_TFLOPS
     score_tf = f_score / (score_ms * 1e-3) / 1e12
     attn_tf = f_attn / (attn_ms * 1e-3) / 1e12
     dominant = "attention" if attn_ms >= score_ms else "score"
@@ -520,39 +561,44 @@ def bench_prefill(args, spec):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": B, "new_tokens": spec["n_new"],
+        "config": {"workload": name, "batch": B, "new_tokens": spec["n_new"],
                    "prefix": spec["prefix"], "q_heads": spec["Hq"], "kv_heads": spec["Hkv"],
                    "idx_heads": spec["Hidx"], "head_dim": spec["D"], "idx_dim": spec["Di"],
                    "topk": spec["topk"], "init": spec["init"], "local": spec["local"],
                    "page": 128, "parallelism": "none"},
         "stages_ms": {"score_gemm": score_ms, "select": sel_ms, "attention": attn_ms},
-        "mfma_tflops": {"score_gemm": score_tf, "attention": attn_tf},
+        "mfma_tflops": {"score_gemm": score_tf, "attention": attn_tf,
+                        "step": (f_score + f_attn) / (ms * 1e-3) / 1e12},
+        "mfma_frac": {"score_gemm": score_tf / peak, "attention": attn_tf / peak,
+                      "step": (f_score + f_attn) / (ms * 1e-3) / 1e12 / peak},
         "flops": {"score_gemm": f_score, "attention": f_attn},
+        "ms_per_step_median": float(np.median(step_ms)),
         "wall_s_timed_region": t_wall,
         "roofline": roof,
-        "device": torch.cuda.get_device_name(dev),
+        **device_info(dev),
     }
     if short:
         total_b = idx_b + kv_b + small_b
         res["hbm_gbps"] = total_b / (ms * 1e-3) / 1e9
         res["hbm_frac"] = res["hbm_gbps"] / HBM_PEAK_GBS
         res["touched_bytes"] = {"idx_keys": idx_b, "selected_kv_union": kv_b, "small": small_b}
-    if not args.no_cpu_baseline:
+    if headline and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(case, spec, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
+    return res
 
 
-def bench_append(args, spec):
+def measure_append(args, name, headline):
     """Paged append (msa_append_kv): T new tokens' K, V and index keys into
     the pools at seeded random slots, GB/s on the bytes it must move."""
     import torch
 
     import block_sparse_attention_score_amd as msa
-    from synth import WORKLOAD_SEEDS
+    from synth import WORKLOAD_SEEDS, workload
 
+    spec = workload(name)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    g = torch.Generator(device="cpu").manual_seed(WORKLOAD_SEEDS[args.workload])
+    g = torch.Generator(device="cpu").manual_seed(WORKLOAD_SEEDS[name])
     T, Hkv, Hidx, D, Di = spec["T"], spec["Hkv"], spec["Hidx"], spec["D"], spec["Di"]
     P = (spec["pool_tokens"] + 127) // 128
     kv = spec["kv"]
@@ -593,16 +639,16 @@ def bench_append(args, spec):
         "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": kv, "data": "synthetic",
-        "config": {"workload": args.workload, "new_tokens": T, "pool_pages": P,
+        "config": {"workload": name, "new_tokens": T, "pool_pages": P,
                    "kv_heads": Hkv, "idx_heads": Hidx, "head_dim": D, "idx_dim": Di,
                    "kv_dtype": kv, "page": 128, "parallelism": "none"},
         "wall_s_timed_region": t_wall,
         "roofline": {"kernel": "append_kernel", "bound": "hbm", "achieved": gbps,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBS,
                      "traffic": None, "bytes_per_launch": moved, "ms_per_launch": ms},
-        "device": torch.cuda.get_device_name(dev),
+        **device_info(dev),
     }
-    print(json.dumps(res), flush=True)
+    return res
 
 
 def chunk_touched_bytes(spec, seq_lens, cu, sel, cnt):

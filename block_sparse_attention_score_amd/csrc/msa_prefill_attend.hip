@@ -3,10 +3,11 @@
 // Selection is per query token (sglang page minimax_sparse_backend.py,
 // MiniMaxSparseAttnBackend.__init__: one query per selection block), so in a
 // prefill chunk every key block j of a sequence is attended by the tokens
-// that selected it.  The SM100 prefill page (minimax_sparse.py,
-// minimax_sparse_prefill) builds, per (sequence, head, key block), the list of
-// those tokens and runs key-major attention tiles over it; this file does the
-// same on gfx950:
+// that selected it.  The vLLM page sparse_attention_msa.py (its module
+// docstring, and the prefill part of MiniMaxM3SparseMSAImpl.forward:
+// build_k2q_csr, then sparse_atten_func) builds, per (sequence, head, key
+// block), the list of those tokens and runs key-major attention tiles over it;
+// this file does the same on gfx950:
 //   1. k2q CSR: count the selecting tokens of every (b, index head, j), scan
 //      the counts into list offsets and 256-row work tiles, fill the lists;
 //   2. per tile: up to 256 query rows (tokens x GQA heads of one kv head,

@@ -139,7 +139,14 @@ size_t msa_prefill_workspace_size(const msa_params_t* params, int32_t num_seqs,
                                   int32_t num_q_tokens, int32_t max_blocks);
 
 /*
- * Step 1 (score).  Writes scores[T, Hidx, max_blocks] (float32; -inf for
+ * Step 1 (score).  Defined by the sglang page minimax_sparse_backend.py:
+ * MiniMaxSparseAttnBackend.__init__ reads the sparse index dim, block_size_k
+ * (128) and the score type, and forward_decode hands the index query idx_q
+ * and the index-key cache to minimax_sparse_decode, which scores every key
+ * block for each query; the score of a block is the maximum over its tokens
+ * up to the query of q_idx . k_idx (the page leaves the score type open; this
+ * is the reading taken).
+ * Writes scores[T, Hidx, max_blocks] (float32; -inf for
  * blocks past each query).  cu_seqlens_q == NULL: decode, T = num_seqs, one
  * query per sequence at position seq_len - 1.  Otherwise T = num_q_tokens
  * query tokens laid out by cu_seqlens_q.  Accumulation is float32.
@@ -153,7 +160,13 @@ msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
                              void* stream);
 
 /*
- * Step 2 (select).  From scores[T, Hidx, max_blocks] writes
+ * Step 2 (select).  Defined by the sglang page minimax_sparse_backend.py,
+ * MiniMaxSparseAttnBackend.__init__: one selection per query token
+ * (block_size_q = 1) of the init, local and top-k key blocks, which
+ * forward_decode / forward_extend pass to the sparse ops; the vLLM page
+ * sparse_attention_msa.py (MiniMaxM3SparseMSAImpl.forward) consumes such a
+ * selection as a token-major [total_q, H, MK] index buffer.
+ * From scores[T, Hidx, max_blocks] writes
  * sel_blocks[T, Hidx, Kmax] and sel_count[T, Hidx].  Only the first nb(p)
  * scores of each row affect the result (the rest of the row may hold
  * anything).  Deterministic: equal scores (+0 and -0 are equal) go to the
@@ -168,7 +181,11 @@ msa_status_t msa_select_blocks(const msa_params_t* params,
                                int32_t* sel_count, void* stream);
 
 /*
- * Steps 1-3 for decode (one query per sequence): score, select, split-K
+ * Steps 1-3 for decode.  Defined by the sglang page minimax_sparse_backend.py,
+ * forward_decode (the minimax_sparse_decode call: one query per sequence over
+ * the paged cache, block table and seq_lens), attending as the vLLM page's
+ * module docstring describes its decode: split-K over the selected blocks.
+ * One query per sequence: score, select, split-K
  * attention over the selected blocks and log-sum-exp combine.  out [B, Hq, D]
  * in q_dtype.  lse_out, sel_blocks_out and sel_count_out may be NULL; when
  * given they receive the per-head lse and the selection.  ws: a workspace of
@@ -208,7 +225,11 @@ msa_status_t msa_sparse_decode_noalloc(const msa_params_t* params, const void* q
                                        void* stream);
 
 /*
- * Step 3 alone (decode): attention over a given selection sel_blocks
+ * Step 3 alone (decode).  Defined by the vLLM page sparse_attention_msa.py,
+ * MiniMaxM3SparseMSAImpl.forward, decode part: split-K attention of the
+ * decode queries over the blocks an indexer selected, through the block
+ * table and seq_lens, with the fp8 k_scale / v_scale.
+ * Attention over a given selection sel_blocks
  * [B, Hidx, Kmax] / sel_count [B, Hidx] (ascending block ids < nb).  Same
  * outputs and workspace as msa_sparse_decode.
  */
@@ -222,7 +243,13 @@ msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q,
                                void* stream);
 
 /*
- * Steps 1-3 for chunked prefill: num_q_tokens new tokens laid out by
+ * Steps 1-3 for chunked prefill.  Defined by the vLLM page
+ * sparse_attention_msa.py, MiniMaxM3SparseMSAImpl.forward, prefill part
+ * (per-block query lists from build_k2q_csr, then causal attention over the
+ * selected 128-token blocks, causal=True, blk_kv = 128) and the sglang page's
+ * forward_extend (cu_seqlens from the extend lengths, prefix lengths beside
+ * seq_lens).
+ * num_q_tokens new tokens laid out by
  * cu_seqlens_q [B+1], each attending causally to its sequence's tokens
  * t <= p through its own selection.  Outputs as for decode, per token.
  * Short chunks (num_q_tokens <= 8 * num_seqs, e.g. multi-token decode for

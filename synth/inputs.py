@@ -12,9 +12,11 @@ Recipe (applies to every workload below):
 * Poison: spare pages and the token slots past ``seq_len`` in every
   sequence's last page hold NaN in K/V (bf16 0x7FC0, f32 NaN, fp8 0x7F) and
   +1e4 in index-K, so that any read of an invalid slot shows up in results.
-* Draw order on one ``torch.Generator`` seeded with ``seed``: seq_lens,
-  permutation, q, idx_q, K, V, idx_K; pools are drawn in chunks of 256 pages.
-  The generator lives on ``device``, so CPU and GPU draws differ; every
+* Sequence lengths drawn at random come from a CPU ``torch.Generator``
+  seeded with ``seed``, so they are the same whichever device generates the
+  case.  Everything else is drawn, in the order permutation, q, idx_q, K, V,
+  idx_K, from one generator on ``device`` seeded with ``seed``; pools are
+  drawn in chunks of 256 pages.  CPU and GPU draws of those differ; every
   consumer gets the bytes of one draw.
 
 Decode: one query per sequence at position ``seq_len - 1``.  Prefill: the
@@ -125,7 +127,7 @@ class Case:
         return Case(**f)
 
 
-def _draw_seq_lens(spec, g, device) -> torch.Tensor:
+def _draw_seq_lens(spec, seed) -> torch.Tensor:
     B = spec["B"]
     if spec["kind"] == "prefill":
         n_new = spec["n_new"]
@@ -138,8 +140,9 @@ def _draw_seq_lens(spec, g, device) -> torch.Tensor:
         return torch.full((B,), int(sl[1]), dtype=torch.int32)
     if isinstance(sl, (list, tuple)) and sl and sl[0] == "uniform":
         lo, hi = int(sl[1]), int(sl[2])
-        r = torch.randint(lo, hi + 1, (B,), generator=g, device=device)
-        return r.to(torch.int32).cpu()
+        g = torch.Generator(device="cpu")
+        g.manual_seed(int(seed))
+        return torch.randint(lo, hi + 1, (B,), generator=g).to(torch.int32)
     return torch.tensor(list(sl), dtype=torch.int32)
 
 
@@ -188,7 +191,7 @@ def generate(spec: dict, seed: int, device="cpu", max_blocks: Optional[int] = No
     v_scale = float(spec.get("v_scale", 1.0))
 
     # 1. sequence lengths
-    seq_lens = _draw_seq_lens(spec, g, device)
+    seq_lens = _draw_seq_lens(spec, seed)
     nb = [(int(L) + BLOCK - 1) // BLOCK for L in seq_lens.tolist()]
     used = sum(nb)
     spare = spare_pages if spare_pages is not None else max(8, math.ceil(used / 100))

@@ -213,30 +213,41 @@ def test_planted_selection_exact(msa, case):
 FULL = ["decode_b32_l32k", "decode_b64_lvar", "decode_fp8_b32_l64k"]
 
 
+def _sub_input(case, rows):
+    """Host copy of sequences ``rows`` only (their pages, queries, tables and
+    lengths), so the oracle scores nothing else."""
+    bt = case.block_table.cpu().numpy()
+    pages = np.unique(bt[rows].reshape(-1))
+    inp = host_view(case, pages=pages[pages >= 0])
+    for key in ("q", "idx_q", "block_table", "seq_lens"):
+        inp[key] = inp[key][rows]
+    return inp
+
+
 @pytest.mark.parametrize("name", FULL)
-def test_decode_full_size_sampled(msa, name):
+def test_decode_full_size(msa, name):
     """The full workload in the launch configuration the benchmark times; the
-    oracle checks a sample of sequences (all their heads and blocks)."""
+    oracle checks every sequence (all heads and blocks), eight at a time."""
     spec = workload(name)
     seed = WORKLOAD_SEEDS[name]
     print(f"[decode_full] {name} seed={seed}", flush=True)
     case, cfg, g = _run(msa, spec, seed)
     B = case.B
-    rng = np.random.default_rng(seed)
-    lens = case.seq_lens.cpu().numpy()
-    rows = sorted(set([int(np.argmax(lens)), int(np.argmin(lens))] +
-                      [int(x) for x in rng.choice(B, size=2, replace=False)]))
-    pages = np.unique(np.concatenate([case.block_table.cpu().numpy()[b] for b in rows]))
-    pages = pages[pages >= 0]
-    inp = host_view(case, pages=pages)
-    err, nband = _compare(inp, g, spec, rows=rows)
-    print(f"  rows {rows} max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
-    # every row: well-formed selections and finite outputs
+    worst = [0.0, 0.0]
+    nband = 0
+    for r0 in range(0, B, 8):
+        rows = list(range(r0, min(B, r0 + 8)))
+        sub = {k: (v[rows] if k in ("out", "lse", "sel", "cnt", "scores", "sel2", "cnt2",
+                                    "out3", "lse3") else v) for k, v in g.items()}
+        err, nb_ = _compare(_sub_input(case, rows), sub, spec)
+        worst = [max(worst[0], err[0]), max(worst[1], err[1])]
+        nband += nb_
+    print(f"  all {B} sequences: max {worst[0]:.3g} worst mean {worst[1]:.3g} "
+          f"band-rows {nband}", flush=True)
     cnt = parity.to_np(g["cnt"])
     kmax = spec["topk"] + spec["init"] + spec["local"]
-    nb = (lens + 127) // 128
+    nb = (case.seq_lens.cpu().numpy() + 127) // 128
     assert (cnt == np.minimum(nb, kmax)[:, None]).all()
-    assert torch.isfinite(g["out"].float()).all()
 
 
 def test_decode_repeats_match_composition(msa):
