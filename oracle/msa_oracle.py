@@ -434,13 +434,16 @@ def store_values(src: np.ndarray, src_dtype: str, pool_dtype: str, scale: float 
 
 def append_kv(k_pool, v_pool, idx_k_pool, k_new, v_new, idx_k_new, slots, *,
               kv_src: str, kv_dtype: str, idx_dtype: str, k_scale: float = 1.0,
-              v_scale: float = 1.0):
+              v_scale: float = 1.0, idx_v_pool=None, idx_v_new=None):
     """Pools (stored arrays, [P, H, 128, D]) with token t's rows written at
     slot slots[t]; returns new arrays, the inputs are left unchanged.
     k_new / v_new [T, Hkv, D] and idx_k_new [T, Hidx, Di] are given in their
     source representation (kv_src: bf16 bits or f32; index keys already in
-    idx_dtype)."""
+    idx_dtype).  With an index-value pool, idx_v_new [T, Hidx, Di] (idx_dtype)
+    is stored beside the index keys and the new pool is returned fourth."""
     k_pool, v_pool, idx_k_pool = (np.array(a, copy=True) for a in (k_pool, v_pool, idx_k_pool))
+    if idx_v_pool is not None:
+        idx_v_pool = np.array(idx_v_pool, copy=True)
     P = k_pool.shape[0]
     for t, s in enumerate(np.asarray(slots, dtype=np.int64)):
         if s < 0 or s >= P * BLOCK:
@@ -449,4 +452,47 @@ def append_kv(k_pool, v_pool, idx_k_pool, k_new, v_new, idx_k_new, slots, *,
         k_pool[page, :, off, :] = store_values(k_new[t], kv_src, kv_dtype, k_scale)
         v_pool[page, :, off, :] = store_values(v_new[t], kv_src, kv_dtype, v_scale)
         idx_k_pool[page, :, off, :] = store_values(idx_k_new[t], idx_dtype, idx_dtype)
+        if idx_v_pool is not None:
+            idx_v_pool[page, :, off, :] = store_values(idx_v_new[t], idx_dtype, idx_dtype)
+    if idx_v_pool is not None:
+        return k_pool, v_pool, idx_k_pool, idx_v_pool
     return k_pool, v_pool, idx_k_pool
+
+
+# --------------------------------------------------------------------------
+# Index-value branch
+# --------------------------------------------------------------------------
+#
+# The sglang page's backend keeps an index-value cache beside the index keys
+# (set_fused_kv_index_buffer stores idx_v unless the layer is listed in
+# disable_value_layer_ids), hands both caches to the sparse ops with
+# disable_index_value, and gets back an index output idx_o of
+# num_idx_heads * sparse_index_dim values per token next to the attention
+# output.  What the ops compute is not on the pages.  Reading taken here: per
+# index head, plain softmax attention of the index query over the index keys
+# and index values of every token the query can see (t <= p, all blocks: the
+# index branch already scores every block), with the usual scale
+# 1/sqrt(idx_dim).
+
+
+def index_value_attention(inp: dict, scale: Optional[float] = None):
+    """idx_out [T, Hidx, Di] and its lse [T, Hidx] (natural log of the scaled
+    logits); an index query with no visible token gives zeros and -inf."""
+    iq_all = decode(inp["idx_q"], inp["idx_dtype"])
+    T, Hidx, Di = iq_all.shape
+    sc = (1.0 / math.sqrt(Di)) if not scale else float(scale)
+    out = np.zeros((T, Hidx, Di))
+    lse = np.full((T, Hidx), -np.inf)
+    pos = query_positions(inp["seq_lens"], inp.get("cu_seqlens_q"), inp.get("positions"))
+    for t, (b, p) in enumerate(pos):
+        if p < 0:
+            continue
+        for h in range(Hidx):
+            k = decode(_gather_rows_raw(inp["idx_k_pool"], inp["block_table"][b], h, p + 1),
+                       inp["idx_dtype"])
+            v = decode(_gather_rows_raw(inp["idx_v_pool"], inp["block_table"][b], h, p + 1),
+                       inp["idx_dtype"])
+            o, l = softmax_attention(iq_all[t, h][None, :], k, v, sc)
+            out[t, h] = o[0]
+            lse[t, h] = l[0]
+    return out, lse

@@ -15,8 +15,9 @@ Recipe (applies to every workload below):
 * Sequence lengths drawn at random come from a CPU ``torch.Generator``
   seeded with ``seed``, so they are the same whichever device generates the
   case.  Everything else is drawn, in the order permutation, q, idx_q, K, V,
-  idx_K, from one generator on ``device`` seeded with ``seed``; pools are
-  drawn in chunks of 256 pages.  CPU and GPU draws of those differ; every
+  idx_K (then idx_V, for workloads with the index-value branch), from one
+  generator on ``device`` seeded with ``seed``; pools are drawn in chunks of
+  256 pages.  CPU and GPU draws of those differ; every
   consumer gets the bytes of one draw.
 
 Decode: one query per sequence at position ``seq_len - 1``.  Prefill: the
@@ -106,6 +107,7 @@ class Case:
     num_pages: int
     k_scale: float = 1.0
     v_scale: float = 1.0
+    idx_v_pool: Optional[torch.Tensor] = None  # [P, Hidx, 128, Di] (index-value branch)
 
     @property
     def B(self) -> int:
@@ -234,17 +236,20 @@ def generate(spec: dict, seed: int, device="cpu", max_blocks: Optional[int] = No
     k_pool = _draw_pool(P, Hkv, D, kvd, k_scale, g, device)
     v_pool = _draw_pool(P, Hkv, D, kvd, v_scale, g, device)
     idx_k_pool = _draw_pool(P, Hidx, Di, idd, 1.0, g, device)
+    idx_v_pool = _draw_pool(P, Hidx, Di, idd, 1.0, g, device) if spec.get("idx_value") else None
 
     if poison:
         _poison(k_pool, valid, kvd, _POISON_KV.get(kvd, 0.0))
         _poison(v_pool, valid, kvd, _POISON_KV.get(kvd, 0.0))
         _poison(idx_k_pool, valid, idd, IDX_POISON)
+        if idx_v_pool is not None:
+            _poison(idx_v_pool, valid, idd, _POISON_KV.get(idd, 0.0))
 
     return Case(spec=dict(spec), seq_lens=seq_lens.to(device),
                 cu_seqlens_q=None if cu is None else cu.to(device),
                 block_table=bt.to(device), q=q, idx_q=idx_q, k_pool=k_pool,
                 v_pool=v_pool, idx_k_pool=idx_k_pool, num_pages=P,
-                k_scale=k_scale, v_scale=v_scale)
+                k_scale=k_scale, v_scale=v_scale, idx_v_pool=idx_v_pool)
 
 
 def _bits(t: torch.Tensor) -> np.ndarray:
@@ -282,6 +287,7 @@ def host_view(case: Case, pages: Optional[np.ndarray] = None) -> dict:
         q=_bits(case.q), idx_q=_bits(case.idx_q),
         k_pool=pool(case.k_pool), v_pool=pool(case.v_pool),
         idx_k_pool=pool(case.idx_k_pool),
+        idx_v_pool=None if case.idx_v_pool is None else pool(case.idx_v_pool),
         block_table=_bits(case.block_table), seq_lens=_bits(case.seq_lens),
         cu_seqlens_q=None if case.cu_seqlens_q is None else _bits(case.cu_seqlens_q),
         q_dtype=spec.get("q", "bf16"), kv_dtype=spec.get("kv", "bf16"),

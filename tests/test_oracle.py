@@ -122,11 +122,11 @@ def test_planted_scores_and_selection(case):
 # ---------------------------------------------------- brute force, tiny
 
 def _tiny_case(seed, B=2, lens=(300, 77), Hq=4, Hkv=2, Hidx=1, D=8, Di=8, topk=2,
-               init=1, local=1, kv="bf16", prefill_new=None):
+               init=1, local=1, kv="bf16", prefill_new=None, idx_value=False):
     spec = dict(kind="decode", B=B, seq_lens=list(lens), Hq=Hq, Hkv=Hkv, Hidx=Hidx,
                 D=D, Di=Di, topk=topk, init=init, local=local, q="bf16", kv=kv,
                 idx="bf16", k_scale=0.5 if kv == "fp8" else 1.0,
-                v_scale=0.25 if kv == "fp8" else 1.0)
+                v_scale=0.25 if kv == "fp8" else 1.0, idx_value=idx_value)
     if prefill_new is not None:
         spec.update(kind="prefill", n_new=list(prefill_new),
                     prefix=[L - n for L, n in zip(lens, prefill_new)])
@@ -705,3 +705,99 @@ def test_selection_forced_in_budget_brute_force(nb, init, local, topk):
         assert len(winners) == 1
         assert S == sorted(F | winners[0])
         assert len(S) == min(nb, max(topk, len(F)))
+
+
+# ------------------------------------------------------ index-value branch
+
+def _py_index_value(inp, scale):
+    """Index-value attention with explicit loops over heads and tokens, at the
+    positions of the case description."""
+    ikc = _RowCache(inp["idx_k_pool"], "bf16")
+    ivc = _RowCache(inp["idx_v_pool"], "bf16")
+    outs = {}
+    for t, (b, p) in enumerate(inp["_pos"]):
+        for h in range(inp["Hidx"]):
+            q = [_py_value(x, "bf16") for x in inp["idx_q"][t, h]]
+            zs, vs = [], []
+            for tok in range(p + 1):
+                page = int(inp["block_table"][b, tok // 128])
+                k = ikc(page, h, tok % 128)
+                zs.append(scale * sum(a * c for a, c in zip(q, k)))
+                vs.append(ivc(page, h, tok % 128))
+            m = max(zs)
+            e = [math.exp(z - m) for z in zs]
+            tot = sum(e)
+            outs[(t, h)] = ([sum(e[i] * vs[i][d] for i in range(len(e))) / tot
+                             for d in range(len(q))], m + math.log(tot))
+    return outs
+
+
+@pytest.mark.parametrize("prefill", [None, (40, 100)])
+def test_index_value_brute_force(prefill):
+    inp = _tiny_case(51, lens=(700, 260), Hq=4, Hkv=2, Hidx=2, prefill_new=prefill,
+                     idx_value=True)
+    out, lse = oracle.index_value_attention(inp)
+    ref = _py_index_value(inp, 1.0 / math.sqrt(8))
+    for (t, h), (o, l) in ref.items():
+        assert np.allclose(out[t, h], o, rtol=1e-12, atol=1e-12), (t, h)
+        assert abs(lse[t, h] - l) < 1e-12, (t, h)
+
+
+def test_index_value_equals_causal_sdpa():
+    """Every index head of a chunk of the last n tokens (and of decode) against
+    torch SDPA, is_causal=True over the whole sequence in float64, whose other
+    query rows are filler: no position enters the check."""
+    lens, new = (900, 300), (900, 64)
+    inp = _tiny_case(52, lens=lens, Hq=4, Hkv=2, Hidx=2, Di=16, prefill_new=new,
+                     idx_value=True)
+    out, _ = oracle.index_value_attention(inp)
+    iq = torch.from_numpy(oracle.decode(inp["idx_q"], "bf16"))
+    rng = torch.Generator().manual_seed(5)
+    row = 0
+    for b, (L, n) in enumerate(zip(lens, new)):
+        nbk = (L + 127) // 128
+        pages = inp["block_table"][b, :nbk].astype(np.int64)
+        k = torch.from_numpy(oracle.decode(inp["idx_k_pool"][pages], "bf16"))
+        v = torch.from_numpy(oracle.decode(inp["idx_v_pool"][pages], "bf16"))
+        k = k.permute(1, 0, 2, 3).reshape(2, nbk * 128, 16)[:, :L]
+        v = v.permute(1, 0, 2, 3).reshape(2, nbk * 128, 16)[:, :L]
+        qf = torch.randn(2, L, 16, generator=rng, dtype=torch.float64)
+        qf[:, L - n:] = iq[row:row + n].permute(1, 0, 2)
+        o = torch.nn.functional.scaled_dot_product_attention(qf, k, v, is_causal=True)
+        assert np.allclose(out[row:row + n], o[:, L - n:].permute(1, 0, 2).numpy(),
+                           rtol=1e-11, atol=1e-12), b
+        row += n
+
+
+def test_index_value_closed_forms():
+    inp = _tiny_case(53, lens=(500, 1, 129), B=3, Hidx=1, idx_value=True)
+    # a zero index query weighs every visible token equally
+    inp["idx_q"] = np.zeros_like(inp["idx_q"])
+    out, lse = oracle.index_value_attention(inp)
+    for t, (b, p) in enumerate(inp["_pos"]):
+        pages = inp["block_table"][b, : p // 128 + 1].astype(np.int64)
+        rows = oracle.decode(inp["idx_v_pool"][pages, 0].reshape(-1, 8)[: p + 1], "bf16")
+        assert np.allclose(out[t, 0], rows.mean(axis=0), rtol=1e-13, atol=1e-14)
+        assert abs(lse[t, 0] - math.log(p + 1)) < 1e-13
+    # a single visible token returns its value; constant values return the constant
+    page = inp["block_table"][1, 0]
+    assert np.array_equal(out[1, 0], oracle.decode(inp["idx_v_pool"][page, 0, 0], "bf16"))
+    inp["idx_v_pool"] = np.full_like(inp["idx_v_pool"], _bf16_bits([-1.25])[0])
+    out, _ = oracle.index_value_attention(inp)
+    assert np.all(np.abs(out - (-1.25)) < 1e-14)
+
+
+def test_index_value_empty_sequence_and_append():
+    inp = _tiny_case(54, lens=(0, 300), Hidx=1, idx_value=True)
+    out, lse = oracle.index_value_attention(inp)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    # the append stores index values beside the index keys
+    rng = np.random.default_rng(3)
+    P = 3
+    pools = [rng.integers(0, 1 << 14, (P, 1, 128, 8)).astype(np.uint16) for _ in range(4)]
+    new = [rng.integers(0, 1 << 14, (2, 1, 8)).astype(np.uint16) for _ in range(4)]
+    res = oracle.append_kv(*pools[:3], *new[:3], np.array([130, 5]), kv_src="bf16",
+                           kv_dtype="bf16", idx_dtype="bf16", idx_v_pool=pools[3],
+                           idx_v_new=new[3])
+    assert len(res) == 4
+    assert np.array_equal(res[3][1, :, 2], new[3][0]) and np.array_equal(res[3][0, :, 5], new[3][1])
