@@ -86,6 +86,10 @@ def step_bytes(spec, seq_lens, sel, cnt):
                 valid = min(128, int(L[b]) - 128 * int(j))
                 kv += valid * D * 2 * ekv
     small = int(B * Hq * D * 2 * eq + B * Hidx * Di * eq + 4 * (nb.sum() + Hkv * cnt.sum()))
+    if spec.get("idx_value"):
+        # the index values of every visible token, and the index output
+        idx_keys *= 2
+        small += B * Hidx * Di * eq
     return idx_keys, kv, small
 
 
@@ -397,12 +401,14 @@ def measure_decode(args, name, headline):
 
     def step():
         msa.sparse_decode(cfg, case.q, case.idx_q, case.k_pool, case.v_pool, case.idx_k_pool,
-                          case.block_table, case.seq_lens, out=out, workspace=ws)
+                          case.block_table, case.seq_lens, out=out, workspace=ws,
+                          idx_v_pool=case.idx_v_pool)
 
     # selection of this batch, for the touched-bytes count
     _, _, sel, cnt = msa.sparse_decode(cfg, case.q, case.idx_q, case.k_pool, case.v_pool,
                                        case.idx_k_pool, case.block_table, case.seq_lens,
-                                       workspace=ws, return_selection=True)
+                                       workspace=ws, return_selection=True,
+                                       idx_v_pool=case.idx_v_pool)[:4]
     torch.cuda.synchronize()
     lens = case.seq_lens.cpu().numpy()
     idx_b, kv_b, small_b = step_bytes(spec, lens, sel.cpu().numpy(), cnt.cpu().numpy())
@@ -494,16 +500,20 @@ def measure_prefill(args, name, headline):
     def step():
         msa.sparse_prefill(cfg, case.q, case.idx_q, case.k_pool, case.v_pool, case.idx_k_pool,
                            case.block_table, case.seq_lens, case.cu_seqlens_q, out=out,
-                           workspace=ws)
+                           workspace=ws, idx_v_pool=case.idx_v_pool)
 
     _, _, sel, cnt = msa.sparse_prefill(cfg, case.q, case.idx_q, case.k_pool, case.v_pool,
                                         case.idx_k_pool, case.block_table, case.seq_lens,
-                                        case.cu_seqlens_q, workspace=ws, return_selection=True)
+                                        case.cu_seqlens_q, workspace=ws, return_selection=True,
+                                        idx_v_pool=case.idx_v_pool)[:4]
     torch.cuda.synchronize()
     lens = case.seq_lens.cpu().numpy()
     cu = case.cu_seqlens_q.cpu().numpy()
     valid = selected_valid_tokens(lens, cu, sel.cpu().numpy(), cnt.cpu().numpy())
     f_score, f_attn = prefill_flops(spec, lens, cu, valid)
+    # index-value branch: q.k over the same (query, visible token) pairs as
+    # the scoring, and p.v over them again
+    f_iv = 2 * f_score if spec.get("idx_value") else 0
 
     def timed(fn, n):
         return timed_steps(fn, n, flush, stream)
@@ -568,10 +578,10 @@ def measure_prefill(args, name, headline):
                    "page": 128, "parallelism": "none"},
         "stages_ms": {"score_gemm": score_ms, "select": sel_ms, "attention": attn_ms},
         "mfma_tflops": {"score_gemm": score_tf, "attention": attn_tf,
-                        "step": (f_score + f_attn) / (ms * 1e-3) / 1e12},
+                        "step": (f_score + f_attn + f_iv) / (ms * 1e-3) / 1e12},
         "mfma_frac": {"score_gemm": score_tf / peak, "attention": attn_tf / peak,
-                      "step": (f_score + f_attn) / (ms * 1e-3) / 1e12 / peak},
-        "flops": {"score_gemm": f_score, "attention": f_attn},
+                      "step": (f_score + f_attn + f_iv) / (ms * 1e-3) / 1e12 / peak},
+        "flops": {"score_gemm": f_score, "attention": f_attn, "index_value": f_iv},
         "ms_per_step_median": float(np.median(step_ms)),
         "wall_s_timed_region": t_wall,
         "roofline": roof,

@@ -40,6 +40,7 @@ class Params(ctypes.Structure):
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
         ("forced_in_budget", ctypes.c_int32),
+        ("index_value", ctypes.c_int32),
     ]
 
 
@@ -66,15 +67,15 @@ SIGNATURES = {
     "msa_prefill_workspace_size": (_SZ, [_PP, _I32, _I32, _I32]),
     "msa_block_score": (_I32, [_PP, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _P, _P]),
     "msa_select_blocks": (_I32, [_PP, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P]),
-    "msa_sparse_decode": (_I32, [_PP, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _P, _P,
-                                 _P, _P, _P, _SZ, _P]),
-    "msa_sparse_decode_noalloc": (_I32, [_PP, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32,
-                                         _P, _P, _P, _P, _P]),
+    "msa_sparse_decode": (_I32, [_PP, _P, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32, _P,
+                                 _P, _P, _P, _P, _P, _SZ, _P]),
+    "msa_sparse_decode_noalloc": (_I32, [_PP, _P, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _I32,
+                                         _P, _P, _P, _P, _P, _P]),
     "msa_sparse_attend": (_I32, [_PP, _P, _P, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P,
                                  _P, _SZ, _P]),
-    "msa_sparse_prefill": (_I32, [_PP, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32, _I32,
-                                  _P, _P, _P, _P, _P, _SZ, _P]),
-    "msa_append_kv": (_I32, [_PP, _P, _P, _P, _P, _I32, _P, _P, _P, _I64, _P]),
+    "msa_sparse_prefill": (_I32, [_PP, _P, _P, _P, _P, _P, _P, _I64, _P, _I32, _P, _P, _I32,
+                                  _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "msa_append_kv": (_I32, [_PP, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _I64, _P]),
     "msa_fp8_e4m3_dequant": (_I32, [_P, _P, _I64, _F, _P]),
     "msa_fp8_dequant": (_I32, [_P, _P, _I64, _F, _I32, _P]),
 }

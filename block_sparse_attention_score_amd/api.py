@@ -41,6 +41,7 @@ class MsaConfig:
     v_scale: float = 1.0
     block_size: int = BLOCK
     forced_in_budget: bool = False  # forced blocks count inside topk
+    index_value: bool = False       # the index-value branch (idx_v pool, idx_out)
 
     @property
     def kmax(self) -> int:
@@ -53,7 +54,7 @@ class MsaConfig:
                       self.idx_dim, self.block_size, self.topk, self.init_blocks,
                       self.local_blocks, self.softmax_scale, code[self.q_dtype],
                       code[self.kv_dtype], code[self.idx_dtype], self.k_scale, self.v_scale,
-                      int(self.forced_in_budget))
+                      int(self.forced_in_budget), int(self.index_value))
 
     @staticmethod
     def from_spec(spec: dict) -> "MsaConfig":
@@ -64,7 +65,8 @@ class MsaConfig:
                          kv_dtype=spec.get("kv", "bf16"), idx_dtype=spec.get("idx", "bf16"),
                          k_scale=float(spec.get("k_scale", 1.0)),
                          v_scale=float(spec.get("v_scale", 1.0)),
-                         forced_in_budget=bool(spec.get("forced_in_budget", False)))
+                         forced_in_budget=bool(spec.get("forced_in_budget", False)),
+                         index_value=bool(spec.get("idx_value", False)))
 
 
 def blocks_from_tokens(init_tokens: int, local_tokens: int, block_size: int = BLOCK):
@@ -157,16 +159,29 @@ def select_blocks(cfg: MsaConfig, scores, seq_lens, cu_seqlens_q=None, sel_block
     return sel_blocks, sel_count
 
 
+def _idx_out(cfg: MsaConfig, q, idx_q, idx_out):
+    if not cfg.index_value:
+        return None
+    if idx_out is None:
+        idx_out = torch.empty((idx_q.shape[0], cfg.num_idx_heads, cfg.idx_dim), dtype=q.dtype,
+                              device=q.device)
+    return idx_out
+
+
 def sparse_decode(cfg: MsaConfig, q, idx_q, k_pool, v_pool, idx_k_pool, block_table,
                   seq_lens, out=None, lse=None, sel_blocks=None, sel_count=None,
-                  workspace=None, return_selection=False, stream=None):
+                  workspace=None, return_selection=False, stream=None, idx_v_pool=None,
+                  idx_out=None):
     """Steps 1-3 for decode (one query per sequence).  Returns out [B, Hq, D]
-    (and lse [B, Hq], sel_blocks, sel_count when asked for)."""
+    (and lse [B, Hq], sel_blocks, sel_count when asked for); with
+    cfg.index_value, idx_out [B, Hidx, Di] (the index-value branch over
+    idx_v_pool) comes last."""
     _check_i32(block_table, seq_lens)
     B, MB = block_table.shape
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
+    idx_out = _idx_out(cfg, q, idx_q, idx_out)
     if return_selection:
         if lse is None:
             lse = torch.empty((B, cfg.num_q_heads), dtype=torch.float32, device=dev)
@@ -180,17 +195,18 @@ def sparse_decode(cfg: MsaConfig, q, idx_q, k_pool, v_pool, idx_k_pool, block_ta
     p = cfg.params()
     check(load().msa_sparse_decode(
         ctypes.byref(p), _ptr(q), _ptr(idx_q), _ptr(k_pool), _ptr(v_pool), _ptr(idx_k_pool),
-        k_pool.shape[0], _ptr(block_table), MB, _ptr(seq_lens), B, _ptr(out), _ptr(lse),
-        _ptr(sel_blocks), _ptr(sel_count), _ptr(workspace), workspace.numel(),
-        _stream(stream)))
-    if return_selection:
-        return out, lse, sel_blocks, sel_count
-    return out
+        _ptr(idx_v_pool), k_pool.shape[0], _ptr(block_table), MB, _ptr(seq_lens), B, _ptr(out),
+        _ptr(idx_out), _ptr(lse), _ptr(sel_blocks), _ptr(sel_count), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    res = (out, lse, sel_blocks, sel_count) if return_selection else (out,)
+    if cfg.index_value:
+        res = res + (idx_out,)
+    return res if len(res) > 1 else res[0]
 
 
 def sparse_decode_noalloc(cfg: MsaConfig, q, idx_q, k_pool, v_pool, idx_k_pool, block_table,
                           seq_lens, out, lse=None, sel_blocks=None, sel_count=None,
-                          stream=None):
+                          stream=None, idx_v_pool=None, idx_out=None):
     """msa_sparse_decode_noalloc: decode into the caller's ``out`` (and the
     optional lse / selection outputs) with the library's own per-GPU scratch
     as the workspace; nothing is allocated, here or in the library."""
@@ -199,8 +215,8 @@ def sparse_decode_noalloc(cfg: MsaConfig, q, idx_q, k_pool, v_pool, idx_k_pool, 
     p = cfg.params()
     check(load().msa_sparse_decode_noalloc(
         ctypes.byref(p), _ptr(q), _ptr(idx_q), _ptr(k_pool), _ptr(v_pool), _ptr(idx_k_pool),
-        k_pool.shape[0], _ptr(block_table), MB, _ptr(seq_lens), B, _ptr(out), _ptr(lse),
-        _ptr(sel_blocks), _ptr(sel_count), _stream(stream)))
+        _ptr(idx_v_pool), k_pool.shape[0], _ptr(block_table), MB, _ptr(seq_lens), B, _ptr(out),
+        _ptr(idx_out), _ptr(lse), _ptr(sel_blocks), _ptr(sel_count), _stream(stream)))
     return out
 
 
@@ -226,14 +242,17 @@ def sparse_attend(cfg: MsaConfig, q, k_pool, v_pool, block_table, seq_lens, sel_
 
 def sparse_prefill(cfg: MsaConfig, q, idx_q, k_pool, v_pool, idx_k_pool, block_table,
                    seq_lens, cu_seqlens_q, out=None, lse=None, sel_blocks=None,
-                   sel_count=None, workspace=None, return_selection=False, stream=None):
-    """Steps 1-3 for chunked prefill (query tokens laid out by cu_seqlens_q)."""
+                   sel_count=None, workspace=None, return_selection=False, stream=None,
+                   idx_v_pool=None, idx_out=None):
+    """Steps 1-3 for chunked prefill (query tokens laid out by cu_seqlens_q);
+    with cfg.index_value, idx_out [T, Hidx, Di] comes last."""
     _check_i32(block_table, seq_lens, cu_seqlens_q)
     B, MB = block_table.shape
     T = q.shape[0]
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
+    idx_out = _idx_out(cfg, q, idx_q, idx_out)
     if return_selection:
         if lse is None:
             lse = torch.empty((T, cfg.num_q_heads), dtype=torch.float32, device=dev)
@@ -247,16 +266,17 @@ def sparse_prefill(cfg: MsaConfig, q, idx_q, k_pool, v_pool, idx_k_pool, block_t
     p = cfg.params()
     check(load().msa_sparse_prefill(
         ctypes.byref(p), _ptr(q), _ptr(idx_q), _ptr(k_pool), _ptr(v_pool), _ptr(idx_k_pool),
-        k_pool.shape[0], _ptr(block_table), MB, _ptr(seq_lens), _ptr(cu_seqlens_q), B, T,
-        _ptr(out), _ptr(lse), _ptr(sel_blocks), _ptr(sel_count), _ptr(workspace),
-        workspace.numel(), _stream(stream)))
-    if return_selection:
-        return out, lse, sel_blocks, sel_count
-    return out
+        _ptr(idx_v_pool), k_pool.shape[0], _ptr(block_table), MB, _ptr(seq_lens),
+        _ptr(cu_seqlens_q), B, T, _ptr(out), _ptr(idx_out), _ptr(lse), _ptr(sel_blocks),
+        _ptr(sel_count), _ptr(workspace), workspace.numel(), _stream(stream)))
+    res = (out, lse, sel_blocks, sel_count) if return_selection else (out,)
+    if cfg.index_value:
+        res = res + (idx_out,)
+    return res if len(res) > 1 else res[0]
 
 
 def append_kv(cfg: MsaConfig, k_new, v_new, idx_k_new, slot_mapping, k_pool, v_pool,
-              idx_k_pool, stream=None):
+              idx_k_pool, stream=None, idx_v_new=None, idx_v_pool=None):
     """Write token t's K, V (k_new, v_new [T, Hkv, D]) and index keys
     (idx_k_new [T, Hidx, Di]) into the pools at slot slot_mapping[t] (int64;
     page s // 128, offset s % 128; slots outside the pool are skipped), in
@@ -270,8 +290,9 @@ def append_kv(cfg: MsaConfig, k_new, v_new, idx_k_new, slot_mapping, k_pool, v_p
             raise ValueError("new rows must be [T, heads, dim] with T = len(slot_mapping)")
     p = cfg.params()
     check(load().msa_append_kv(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(idx_k_new),
-                               _ptr(slot_mapping), T, _ptr(k_pool), _ptr(v_pool),
-                               _ptr(idx_k_pool), k_pool.shape[0], _stream(stream)))
+                               _ptr(idx_v_new), _ptr(slot_mapping), T, _ptr(k_pool),
+                               _ptr(v_pool), _ptr(idx_k_pool), _ptr(idx_v_pool),
+                               k_pool.shape[0], _stream(stream)))
 
 
 def fp8_dequant(codes: torch.Tensor, scale: float = 1.0, out=None, fmt: str = "fp8",

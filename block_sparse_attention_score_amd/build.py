@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
-SOURCES = ["msa_api.cpp", "msa_score.hip", "msa_attend.hip", "msa_append.hip", "msa_prefill.hip", "msa_prefill_attend.hip"]
+SOURCES = ["msa_api.cpp", "msa_score.hip", "msa_attend.hip", "msa_append.hip", "msa_prefill.hip",
+           "msa_prefill_attend.hip", "msa_prefill_value.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -88,6 +88,8 @@ msa_status_t check_params(const msa_params_t* p) {
     return fail(MSA_ERR_INVALID_ARG, "negative init/local block count");
   if (p->forced_in_budget != 0 && p->forced_in_budget != 1)
     return fail(MSA_ERR_INVALID_ARG, "forced_in_budget=%d (0 or 1)", p->forced_in_budget);
+  if (p->index_value != 0 && p->index_value != 1)
+    return fail(MSA_ERR_INVALID_ARG, "index_value=%d (0 or 1)", p->index_value);
   if (p->init_blocks > 64 || p->local_blocks > 64)
     return fail(MSA_ERR_UNSUPPORTED, "init/local block counts above 64");
   if (!std::isfinite(p->softmax_scale) || p->softmax_scale < 0.f)
@@ -141,10 +143,13 @@ int blocks_per_split(const msa_params_t& p, int32_t num_units) {
 constexpr int kPagesPerItem = 8;
 // Prefill list entries pack a token index above an 8-bit selection slot.
 constexpr int kMaxPrefillTokens = 1 << 23;
+// Blocks of keys per prefill scoring (and index-value) workgroup.
+constexpr int kPrefillBlocksPerChunk = 16;
 
-// Decode workspace: block scores, split partials and the split tickets.
+// Decode workspace: block scores, split partials and the split tickets (and,
+// with the index-value branch, the scan's per-chunk value partials).
 struct DecodeLayout {
-  size_t scores, part_o, part_lse, tickets, total;
+  size_t scores, part_o, part_lse, tickets, iv_part, total;
   int bps, nsplit_max;
 };
 
@@ -164,6 +169,9 @@ DecodeLayout decode_layout(const msa_params_t& p, int32_t B, int32_t MB) {
   l.part_o = take(sizeof(float) * size_t(B) * p.num_kv_heads * l.nsplit_max * G * p.head_dim);
   l.part_lse = take(sizeof(float) * size_t(B) * p.num_kv_heads * l.nsplit_max * G);
   l.tickets = take(sizeof(uint32_t) * size_t(B) * p.num_kv_heads);
+  if (p.index_value)
+    l.iv_part = take(sizeof(float) * size_t(B) * p.num_idx_heads *
+                     ((MB + kPagesPerItem - 1) / kPagesPerItem) * (p.idx_dim + 2));
   l.total = off;
   return l;
 }
@@ -208,6 +216,7 @@ msa::ScoreArgs multi_score_args(const msa_params_t& p, const void* idx_q, const 
 
 struct PrefillLayout {
   size_t scores, sel, cnt, part_o, part_lse, tickets;
+  size_t iv_o, iv_lse;  // index-value branch: partials per (token, index head, key run)
   size_t counts, cursor, tok_off, tile_off, csr, items, n_items, sink;  // key-major only
   size_t total;
   int bps, nsplit_max;
@@ -251,12 +260,15 @@ PrefillLayout prefill_layout(const msa_params_t& p, int32_t B, int32_t T, int32_
     l.part_lse = take(sizeof(float) * parts);
     l.tickets = take(sizeof(uint32_t) * size_t(T) * p.num_kv_heads);
   }
+  if (p.index_value) {
+    const size_t runs = size_t(T) * p.num_idx_heads *
+                        ((MB + kPrefillBlocksPerChunk - 1) / kPrefillBlocksPerChunk);
+    l.iv_o = take(sizeof(float) * runs * p.idx_dim);
+    l.iv_lse = take(sizeof(float) * runs);
+  }
   l.total = off;
   return l;
 }
-
-// Blocks of keys per prefill scoring workgroup.
-constexpr int kPrefillBlocksPerChunk = 16;
 
 msa::PrefillScoreArgs prefill_score_args(const msa_params_t& p, const void* idx_q,
                                          const void* idx_k_pool, int64_t num_pages,
@@ -312,6 +324,16 @@ msa_status_t check_ws(const void* ws, size_t ws_bytes, size_t need) {
     return fail(MSA_ERR_WORKSPACE, "workspace not %zu-byte aligned", kAlign);
   if (ws_bytes < need)
     return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  return MSA_OK;
+}
+
+// The index-value pointers go with params->index_value: all given when it is
+// on, none when it is off.
+msa_status_t check_iv(const msa_params_t& p, const void* a, const void* b, const char* names) {
+  if (p.index_value && (a == nullptr || b == nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "index_value=1 needs %s", names);
+  if (!p.index_value && (a != nullptr || b != nullptr))
+    return fail(MSA_ERR_INVALID_ARG, "%s given with index_value=0", names);
   return MSA_OK;
 }
 
@@ -416,9 +438,10 @@ msa_status_t scratch_of_current_device(void** out) {
 // scratch.  Everything is validated before the first launch.
 msa_status_t sparse_decode_impl(const msa_params_t* params, const void* q, const void* idx_q,
                                 const void* k_pool, const void* v_pool, const void* idx_k_pool,
-                                int64_t num_pages, const int32_t* block_table,
-                                int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs,
-                                void* out, float* lse_out, int32_t* sel_blocks_out,
+                                const void* idx_v_pool, int64_t num_pages,
+                                const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* seq_lens, int32_t num_seqs, void* out,
+                                void* idx_out, float* lse_out, int32_t* sel_blocks_out,
                                 int32_t* sel_count_out, void* ws, size_t ws_bytes,
                                 bool use_scratch, void* stream) {
   msa_status_t st = check_params(params);
@@ -429,6 +452,7 @@ msa_status_t sparse_decode_impl(const msa_params_t* params, const void* q, const
   if ((sel_blocks_out == nullptr) != (sel_count_out == nullptr))
     return fail(MSA_ERR_INVALID_ARG, "sel_blocks_out and sel_count_out go together");
   if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
+  if ((st = check_iv(*params, idx_v_pool, idx_out, "idx_v_pool and idx_out")) != MSA_OK) return st;
   const msa_params_t& p = *params;
   const DecodeLayout l = decode_layout(p, num_seqs, max_blocks);
   if ((st = check_grid(scan_workgroups(num_seqs, p.num_idx_heads, max_blocks), kScanThreads,
@@ -472,6 +496,11 @@ msa_status_t sparse_decode_impl(const msa_params_t* params, const void* q, const
   a.fill_tail = 0;
   a.zero_words = reinterpret_cast<uint32_t*>(w + l.tickets);
   a.zero_count = num_seqs * p.num_kv_heads;
+  if (p.index_value) {
+    a.idx_v = idx_v_pool;
+    a.iv_part = reinterpret_cast<float*>(w + l.iv_part);
+    a.iv_scale_log2 = 1.4426950408889634f / std::sqrt(float(p.idx_dim));
+  }
   st = hip_status(msa::launch_decode_score(a, p.idx_dtype, p.idx_dim, s), "score launch");
   if (st != MSA_OK) return st;
   // 2. selection inside each attention workgroup, split-K attention, combine
@@ -483,6 +512,13 @@ msa_status_t sparse_decode_impl(const msa_params_t* params, const void* q, const
   aa.local = p.local_blocks;
   aa.sel_out = sel_blocks_out;
   aa.cnt_out = sel_count_out;
+  if (p.index_value) {
+    aa.iv_part = a.iv_part;
+    aa.idx_out = idx_out;
+    aa.iv_chunks = a.chunks_per_pair;
+    aa.iv_pages = kPagesPerItem;
+    aa.idx_dim = p.idx_dim;
+  }
   st = hip_status(msa::launch_decode_attend(aa, p.q_dtype, p.kv_dtype, group_of(p), s),
                   "attention launch");
   return st == MSA_OK ? ok() : st;
@@ -623,28 +659,28 @@ msa_status_t msa_select_blocks(const msa_params_t* params, const float* scores,
 
 msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q, const void* idx_q,
                                const void* k_pool, const void* v_pool,
-                               const void* idx_k_pool, int64_t num_pages,
-                               const int32_t* block_table, int32_t max_blocks,
-                               const int32_t* seq_lens, int32_t num_seqs, void* out,
-                               float* lse_out, int32_t* sel_blocks_out,
-                               int32_t* sel_count_out, void* ws, size_t ws_bytes,
-                               void* stream) {
-  return sparse_decode_impl(params, q, idx_q, k_pool, v_pool, idx_k_pool, num_pages, block_table,
-                            max_blocks, seq_lens, num_seqs, out, lse_out, sel_blocks_out,
-                            sel_count_out, ws, ws_bytes, false, stream);
+                               const void* idx_k_pool, const void* idx_v_pool,
+                               int64_t num_pages, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seq_lens, int32_t num_seqs,
+                               void* out, void* idx_out, float* lse_out,
+                               int32_t* sel_blocks_out, int32_t* sel_count_out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return sparse_decode_impl(params, q, idx_q, k_pool, v_pool, idx_k_pool, idx_v_pool, num_pages,
+                            block_table, max_blocks, seq_lens, num_seqs, out, idx_out, lse_out,
+                            sel_blocks_out, sel_count_out, ws, ws_bytes, false, stream);
 }
 
 msa_status_t msa_sparse_decode_noalloc(const msa_params_t* params, const void* q,
                                        const void* idx_q, const void* k_pool,
                                        const void* v_pool, const void* idx_k_pool,
-                                       int64_t num_pages, const int32_t* block_table,
-                                       int32_t max_blocks, const int32_t* seq_lens,
-                                       int32_t num_seqs, void* out, float* lse_out,
-                                       int32_t* sel_blocks_out, int32_t* sel_count_out,
-                                       void* stream) {
-  return sparse_decode_impl(params, q, idx_q, k_pool, v_pool, idx_k_pool, num_pages, block_table,
-                            max_blocks, seq_lens, num_seqs, out, lse_out, sel_blocks_out,
-                            sel_count_out, nullptr, 0, true, stream);
+                                       const void* idx_v_pool, int64_t num_pages,
+                                       const int32_t* block_table, int32_t max_blocks,
+                                       const int32_t* seq_lens, int32_t num_seqs, void* out,
+                                       void* idx_out, float* lse_out, int32_t* sel_blocks_out,
+                                       int32_t* sel_count_out, void* stream) {
+  return sparse_decode_impl(params, q, idx_q, k_pool, v_pool, idx_k_pool, idx_v_pool, num_pages,
+                            block_table, max_blocks, seq_lens, num_seqs, out, idx_out, lse_out,
+                            sel_blocks_out, sel_count_out, nullptr, 0, true, stream);
 }
 
 msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q, const void* k_pool,
@@ -683,18 +719,22 @@ msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q, const 
 }
 
 msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new, const void* v_new,
-                           const void* idx_k_new, const int64_t* slot_mapping,
-                           int32_t num_tokens, void* k_pool, void* v_pool, void* idx_k_pool,
-                           int64_t num_pages, void* stream) {
+                           const void* idx_k_new, const void* idx_v_new,
+                           const int64_t* slot_mapping, int32_t num_tokens, void* k_pool,
+                           void* v_pool, void* idx_k_pool, void* idx_v_pool, int64_t num_pages,
+                           void* stream) {
   msa_status_t st = check_params(params);
   if (st != MSA_OK) return st;
   if (!k_new || !v_new || !idx_k_new || !slot_mapping || !k_pool || !v_pool || !idx_k_pool)
     return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if ((st = check_iv(*params, idx_v_new, idx_v_pool, "idx_v_new and idx_v_pool")) != MSA_OK)
+    return st;
   if (num_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "num_tokens=%d < 0", num_tokens);
   if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
   {
     const int64_t per_token = 2 * int64_t(params->num_kv_heads) * (params->head_dim / 8) +
-                              int64_t(params->num_idx_heads) * (params->idx_dim / 8);
+                              (params->index_value ? 2 : 1) * int64_t(params->num_idx_heads) *
+                                  (params->idx_dim / 8);
     if ((st = check_grid((int64_t(num_tokens) * per_token + 255) / 256, 256, "append")) !=
         MSA_OK)
       return st;
@@ -711,6 +751,8 @@ msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new, const 
   a.k_pool = k_pool;
   a.v_pool = v_pool;
   a.idx_k_pool = idx_k_pool;
+  a.idx_v_new = idx_v_new;
+  a.idx_v_pool = idx_v_pool;
   a.num_pages = num_pages;
   a.hkv = params->num_kv_heads;
   a.hidx = params->num_idx_heads;
@@ -726,13 +768,13 @@ msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new, const 
 
 msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const void* idx_q,
                                 const void* k_pool, const void* v_pool,
-                                const void* idx_k_pool, int64_t num_pages,
-                                const int32_t* block_table, int32_t max_blocks,
-                                const int32_t* seq_lens, const int32_t* cu_seqlens_q,
-                                int32_t num_seqs, int32_t num_q_tokens, void* out,
-                                float* lse_out, int32_t* sel_blocks_out,
-                                int32_t* sel_count_out, void* ws, size_t ws_bytes,
-                                void* stream) {
+                                const void* idx_k_pool, const void* idx_v_pool,
+                                int64_t num_pages, const int32_t* block_table,
+                                int32_t max_blocks, const int32_t* seq_lens,
+                                const int32_t* cu_seqlens_q, int32_t num_seqs,
+                                int32_t num_q_tokens, void* out, void* idx_out, float* lse_out,
+                                int32_t* sel_blocks_out, int32_t* sel_count_out, void* ws,
+                                size_t ws_bytes, void* stream) {
   msa_status_t st = check_params(params);
   if (st != MSA_OK) return st;
   if ((st = check_shape(num_seqs, max_blocks)) != MSA_OK) return st;
@@ -743,6 +785,7 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
     return fail(MSA_ERR_INVALID_ARG, "sel_blocks_out and sel_count_out go together");
   if (num_pages < 1) return fail(MSA_ERR_INVALID_ARG, "num_pages=%lld < 1", (long long)num_pages);
   if (num_q_tokens < 0) return fail(MSA_ERR_INVALID_ARG, "num_q_tokens=%d < 0", num_q_tokens);
+  if ((st = check_iv(*params, idx_v_pool, idx_out, "idx_v_pool and idx_out")) != MSA_OK) return st;
   const msa_params_t& p = *params;
   if (p.idx_dtype != MSA_BF16)
     return fail(MSA_ERR_UNSUPPORTED, "prefill scoring needs bf16 index keys");
@@ -776,6 +819,13 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
                               kAttendThreads, "per-token attention")) != MSA_OK) {
     return st;
   }
+  if (p.index_value) {
+    const int64_t tiles = (int64_t(num_q_tokens) + 255) / 256;
+    if ((st = check_grid(int64_t(num_seqs) * tiles * p.num_idx_heads *
+                             ((max_blocks + kPrefillBlocksPerChunk - 1) / kPrefillBlocksPerChunk),
+                         kAttendThreads, "index-value attention")) != MSA_OK)
+      return st;
+  }
   if ((st = check_ws(ws, ws_bytes, l.total)) != MSA_OK) return st;
   if (short_chunks(num_seqs, num_q_tokens))
     log_line("msa_sparse_prefill: B=%d T=%d short chunks: scan with four queries per pass, "
@@ -792,6 +842,32 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
   int32_t* sel = sel_blocks_out ? sel_blocks_out : reinterpret_cast<int32_t*>(w + l.sel);
   int32_t* cnt = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + l.cnt);
   float* scores = reinterpret_cast<float*>(w + l.scores);
+
+  // index-value branch: its own kernels, independent of the selection
+  if (p.index_value) {
+    msa::PrefillValueArgs va{};
+    va.idx_q = idx_q;
+    va.idx_k = idx_k_pool;
+    va.idx_v = idx_v_pool;
+    va.num_pages = num_pages;
+    va.block_table = block_table;
+    va.max_blocks = max_blocks;
+    va.seq_lens = seq_lens;
+    va.cu_seqlens_q = cu_seqlens_q;
+    va.num_seqs = num_seqs;
+    va.num_tokens = num_q_tokens;
+    va.hidx = p.num_idx_heads;
+    va.max_tiles = (num_q_tokens + 255) / 256;
+    va.blocks_per_chunk = kPrefillBlocksPerChunk;
+    va.kchunks = (max_blocks + kPrefillBlocksPerChunk - 1) / kPrefillBlocksPerChunk;
+    va.scale_log2 = 1.4426950408889634f / std::sqrt(float(p.idx_dim));
+    va.part_o = reinterpret_cast<float*>(w + l.iv_o);
+    va.part_lse = reinterpret_cast<float*>(w + l.iv_lse);
+    va.idx_out = idx_out;
+    va.out_f32 = p.q_dtype == MSA_F32;
+    st = hip_status(msa::launch_prefill_value(va, p.idx_dim, s), "index-value launch");
+    if (st != MSA_OK) return st;
+  }
 
   const bool key_major = prefill_key_major(p, num_seqs, num_q_tokens);
   if (key_major) {

@@ -1,5 +1,6 @@
-// Paged append: the new tokens' K, V and index keys written into the pools
-// at their token slots (the sglang page minimax_sparse_backend.py stores the
+// Paged append: the new tokens' K, V and index keys (and, with the
+// index-value branch, index values) written into the pools at their token
+// slots (the sglang page minimax_sparse_backend.py stores the
 // new tokens into its pool at out_cache_loc before it attends; slot s is
 // page s / 128, offset s % 128 of the head-major pages here).  fp8 pools
 // receive the e4m3 (or e5m2) code of x / scale (per-tensor k_scale / v_scale,
@@ -99,7 +100,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int vd = a.head_dim / 8;   // 8-element vectors per K/V row
   const int vi = a.idx_dim / 8;    // per index row
   const int n_kv = a.hkv * vd;
-  const int per_token = 2 * n_kv + a.hidx * vi;
+  const int n_iv = a.idx_v_pool != nullptr ? a.hidx * vi : 0;  // index-value pieces
+  const int per_token = 2 * n_kv + a.hidx * vi + n_iv;
   const int64_t gi = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (gi >= static_cast<int64_t>(a.num_tokens) * per_token) return;
   const int t = static_cast<int>(gi / per_token);
@@ -126,12 +128,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       copy8(static_cast<const KS*>(nullptr), src, si, pool, di);
     }
   } else {
-    const int r = i - 2 * n_kv;
+    // index keys, then (index-value branch) index values
+    int r = i - 2 * n_kv;
+    const bool is_iv = r >= a.hidx * vi;
+    if (is_iv) r -= a.hidx * vi;
     const int h = r / vi;
     const int c = r - h * vi;
     const int64_t si = (static_cast<int64_t>(t) * a.hidx + h) * a.idx_dim + c * 8;
     const int64_t di = ((page * a.hidx + h) * kBlock + off) * a.idx_dim + c * 8;
-    copy8(static_cast<const IT*>(nullptr), a.idx_k_new, si, a.idx_k_pool, di);
+    copy8(static_cast<const IT*>(nullptr), is_iv ? a.idx_v_new : a.idx_k_new, si,
+          is_iv ? a.idx_v_pool : a.idx_k_pool, di);
   }
 }
 
@@ -143,7 +149,8 @@ static void launch_append_i(const AppendArgs& a, int idx_dtype, dim3 grid, hipSt
 
 hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  const int64_t per_token = 2 * a.hkv * (a.head_dim / 8) + a.hidx * (a.idx_dim / 8);
+  const int64_t per_token = 2 * a.hkv * (a.head_dim / 8) +
+                            (a.idx_v_pool != nullptr ? 2 : 1) * a.hidx * (a.idx_dim / 8);
   const int64_t blocks = (static_cast<int64_t>(a.num_tokens) * per_token + 255) / 256;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));

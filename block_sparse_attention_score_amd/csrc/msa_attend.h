@@ -325,6 +325,29 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   const QT* qtag = nullptr;
   const KT* ktag = nullptr;
 
+  // Index-value branch (decode): split 0 of the first kv head of each index
+  // head merges the scan's chunk partials of its row into idx_out,
+  //   out = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c,
+  // zeros for a row with nothing visible.
+  if (a.iv_part != nullptr && split == 0 && g % (a.hkv / a.hidx) == 0) {
+    const int di = a.idx_dim;
+    const int nch = div_up(nb_vis, a.iv_pages);
+    const float* part = a.iv_part + static_cast<int64_t>(sel_row) * a.iv_chunks * (di + 2);
+    for (int d = tid; d < di; d += kThreads) {
+      float M = -INFINITY;
+      for (int c = 0; c < nch; ++c) M = fmaxf(M, part[c * (di + 2) + di]);
+      float lsum = 0.f, o = 0.f;
+      if (M != -INFINITY) {
+        for (int c = 0; c < nch; ++c) {
+          const float* pc = part + c * (di + 2);
+          const float wgt = __builtin_amdgcn_exp2f(pc[di] - M);
+          lsum = fmaf(wgt, pc[di + 1], lsum);
+          o = fmaf(wgt, pc[d], o);
+        }
+      }
+      store_out(qtag, a.idx_out, static_cast<int64_t>(sel_row) * di + d, lsum > 0.f ? o / lsum : 0.f);
+    }
+  }
   if (sel_writer && count == 0) {
     for (int i = threadIdx.x; i < a.kmax; i += kThreads)
       a.sel_out[static_cast<int64_t>(sel_row) * a.kmax + i] = -1;

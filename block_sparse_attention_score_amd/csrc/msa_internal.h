@@ -26,6 +26,12 @@ struct ScoreArgs {
   // short chunks (several queries per sequence): query rows of sequence b are
   // cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1; nullptr for decode
   const int32_t* cu_seqlens_q;
+  // index-value branch (decode): index values [P, Hidx, 128, Di] and, per
+  // (pair, chunk), the chunk's partial: Di sums of p v, then the base-2 max
+  // m and the sum l of p = 2^(scaled logit - m); nullptr when off
+  const void* idx_v;
+  float* iv_part;            // [B * Hidx * chunks_per_pair, Di + 2]
+  float iv_scale_log2;       // log2(e) / sqrt(Di)
 };
 
 // Prefill index scoring (causal GEMM with a block-max epilogue).
@@ -94,6 +100,13 @@ struct AttendArgs {
   float* part_o;             // [B, Hkv, nsplit_max, G, D]
   float* part_lse;           // [B, Hkv, nsplit_max, G]
   uint32_t* tickets;         // [B * Hkv], zero on entry
+  // index-value branch (decode): the scan's per-chunk partials, merged by
+  // split 0 of the first kv head of each index head into idx_out [B, Hidx, Di]
+  const float* iv_part;      // [B * Hidx * iv_chunks, Di + 2] or nullptr
+  void* idx_out;             // q dtype
+  int32_t iv_chunks;         // chunks per (sequence, index head) of the scan
+  int32_t iv_pages;          // pages per scan chunk
+  int32_t idx_dim;
 };
 
 // Paged append of new tokens (k_new/v_new [T, Hkv, D], idx_k_new [T, Hidx, Di]).
@@ -106,6 +119,8 @@ struct AppendArgs {
   void* k_pool;              // [P, Hkv, 128, D]
   void* v_pool;
   void* idx_k_pool;          // [P, Hidx, 128, Di]
+  const void* idx_v_new;     // [T, Hidx, Di] or nullptr (index-value branch off)
+  void* idx_v_pool;          // [P, Hidx, 128, Di] or nullptr
   int64_t num_pages;
   int32_t hkv, hidx, head_dim, idx_dim;
   float k_scale, v_scale;    // fp8 pools only
@@ -122,6 +137,31 @@ struct Tile {
   int32_t p0;      // position of token t is p0 + t
   int32_t g0;      // first kv head of the list's index head
   int64_t head0;   // element offset of (page, kv head g0) in the K/V pools
+};
+
+// Prefill index-value branch: causal softmax attention of every new token's
+// index query over the index keys and values of its sequence, split over
+// chunks of key blocks (the scoring grid), then merged per token.
+struct PrefillValueArgs {
+  const void* idx_q;         // [T, Hidx, Di] bf16
+  const void* idx_k;         // [P, Hidx, 128, Di] bf16
+  const void* idx_v;         // [P, Hidx, 128, Di] bf16
+  int64_t num_pages;
+  const int32_t* block_table;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens_q;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t hidx;
+  int32_t max_tiles;         // 256-row query tiles of the longest possible sequence
+  int32_t blocks_per_chunk;  // key blocks per workgroup
+  int32_t kchunks;           // ceil(max_blocks / blocks_per_chunk)
+  float scale_log2;          // log2(e) / sqrt(Di)
+  float* part_o;             // [T, Hidx, kchunks, Di] normalised partial outputs
+  float* part_lse;           // [T, Hidx, kchunks] natural log
+  void* idx_out;             // [T, Hidx, Di] in the query dtype (bf16 or f32)
+  int32_t out_f32;           // 1: idx_out is float32
 };
 
 // Key-major prefill attention over the k2q lists (bf16 q; bf16 or fp8 K/V).
@@ -179,6 +219,7 @@ hipError_t launch_prefill_k2q(const PrefillAttnArgs& a, hipStream_t s);
 hipError_t launch_prefill_attend(const PrefillAttnArgs& a, int kv_dtype, int group,
                                  hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipStream_t s);
+hipError_t launch_prefill_value(const PrefillValueArgs& a, int idx_dim, hipStream_t s);
 hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale, bool e5m2,
                               hipStream_t s);
 

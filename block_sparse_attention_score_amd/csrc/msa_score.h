@@ -139,6 +139,169 @@ __device__ void score_chunk(const ScoreArgs& a, int pair, int chunk) {
   }
 }
 
+// Index-value branch, decode: one pass over the chunk's index keys yields its
+// block scores (as score_chunk) and its share of the index-value attention
+// (the sglang page hands the index-value cache to the decode op beside the
+// index keys; the attention of the index query over every visible token's
+// index key and value is the reading taken).  The logits are the block-score
+// dots times 1/sqrt(Di); each lane keeps an online softmax (base 2) over the
+// token rows it loads and the weighted sum of their values on its 8 dims; the
+// rows of a wave, then the four waves, are merged, and the chunk's partial
+// (Di sums, max, sum) goes to iv_part.  Value rows past the query are cleared
+// before use (stale bytes may be NaN).  K and V loads go out 16 + 16 at a
+// time per lane.
+template <int DI>
+struct IvLds {
+  float m[4];
+  float l[4];
+  float o[4][DI];
+};
+
+__device__ __forceinline__ void clear_raw(Raw8<BF16>& r, bool keep) {
+  const uint32_t k = keep ? 0xffffffffu : 0u;
+  r.v.x &= k; r.v.y &= k; r.v.z &= k; r.v.w &= k;
+}
+__device__ __forceinline__ void clear_raw(Raw8<F32>& r, bool keep) {
+  const uint32_t k = keep ? 0xffffffffu : 0u;
+  r.a = make_float4(__uint_as_float(__float_as_uint(r.a.x) & k), __uint_as_float(__float_as_uint(r.a.y) & k),
+                    __uint_as_float(__float_as_uint(r.a.z) & k), __uint_as_float(__float_as_uint(r.a.w) & k));
+  r.b = make_float4(__uint_as_float(__float_as_uint(r.b.x) & k), __uint_as_float(__float_as_uint(r.b.y) & k),
+                    __uint_as_float(__float_as_uint(r.b.z) & k), __uint_as_float(__float_as_uint(r.b.w) & k));
+}
+
+// (m, l, o) of two disjoint token sets merged into the first (base 2).
+__device__ __forceinline__ void iv_merge(float& m, float& l, float (&o)[8], float m2, float l2,
+                                         const float (&o2)[8]) {
+  const float M = fmaxf(m, m2);
+  const float mu = M == -INFINITY ? 0.f : M;
+  const float a1 = __builtin_amdgcn_exp2f(m - mu);
+  const float a2 = __builtin_amdgcn_exp2f(m2 - mu);
+  l = l * a1 + l2 * a2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = o[e] * a1 + o2[e] * a2;
+  m = M;
+}
+
+template <class IT, int DI>
+__device__ void score_value_chunk(const ScoreArgs& a, int pair, int chunk, IvLds<DI>& S) {
+  constexpr int LPR = DI / 8;          // lanes per token row
+  constexpr int RPL = kWave / LPR;     // token rows per wave load
+  constexpr int NLOAD = kBlock / RPL;  // loads per page per lane
+  constexpr int BATCH = 16 < NLOAD ? 16 : NLOAD;
+  static_assert(NLOAD % BATCH == 0, "batch must divide the page");
+
+  const int b = pair / a.hidx;
+  const int h = pair - b * a.hidx;
+  const int L = a.seq_lens[b];
+  const int nb = L > 0 ? min((L - 1) / kBlock + 1, a.max_blocks) : 0;
+  const int nchunks = div_up(nb, a.pages_per_item);
+  float* srow = a.scores + static_cast<int64_t>(pair) * a.max_blocks;
+
+  if (a.fill_tail && chunk == 0)
+    for (int j = nb + threadIdx.x; j < a.max_blocks; j += kWgThreads) srow[j] = -INFINITY;
+  if (chunk >= nchunks) return;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int row = lane / LPR;
+  const int col = lane % LPR;
+  const IT* tag = nullptr;
+
+  QSlice<IT> qs;
+  load_qslice(tag, a.idx_q, (static_cast<int64_t>(b) * a.hidx + h) * DI + col * 8, qs);
+
+  const int p = L - 1;
+  const int j0 = chunk * a.pages_per_item;
+  const int j1 = min(nb, j0 + a.pages_per_item);
+  float om = -INFINITY, ol = 0.f;
+  float oacc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) oacc[e] = 0.f;
+  for (int j = j0 + w; j < j1; j += kWgThreads / kWave) {
+    const int page = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
+    float m = -INFINITY;
+    if (page >= 0 && page < a.num_pages) {
+      const int nvalid = min(kBlock, p + 1 - j * kBlock);
+      const int64_t base =
+          (static_cast<int64_t>(page) * a.hidx + h) * kBlock * DI + row * DI + col * 8;
+#pragma unroll
+      for (int i0 = 0; i0 < NLOAD; i0 += BATCH) {
+        Raw8<IT> rk[BATCH], rv[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i)
+          rk[i] = load_raw(tag, a.idx_k, base + static_cast<int64_t>((i0 + i) * RPL) * DI);
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i)
+          rv[i] = load_raw(tag, a.idx_v, base + static_cast<int64_t>((i0 + i) * RPL) * DI);
+        float sc[BATCH];
+        float mb = om;
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          const float d = group_sum<LPR>(dot8(qs, rk[i]));
+          const bool ok = (i0 + i) * RPL + row < nvalid;
+          m = fmaxf(m, ok ? d : -INFINITY);
+          sc[i] = ok ? d * a.iv_scale_log2 : -INFINITY;
+          mb = fmaxf(mb, sc[i]);
+        }
+        // online softmax over this lane's rows: rescale by the new maximum
+        const float mu = mb == -INFINITY ? 0.f : mb;
+        const float alpha = __builtin_amdgcn_exp2f(om - mu);
+        ol *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[e] *= alpha;
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          const float pr = __builtin_amdgcn_exp2f(sc[i] - mu);
+          ol += pr;
+          clear_raw(rv[i], (i0 + i) * RPL + row < nvalid);
+          float v[8];
+          unpack(rv[i], v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) oacc[e] = fmaf(pr, v[e], oacc[e]);
+        }
+        om = mb;
+      }
+      m = wave_max(m);
+    }
+    if (lane == 0) srow[j] = m;
+  }
+
+  // rows of the wave (lanes col, col + LPR, ...), then the four waves
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) {
+    float o2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(oacc[e], off);
+    const float m2 = __shfl_xor(om, off);
+    const float l2 = __shfl_xor(ol, off);
+    iv_merge(om, ol, oacc, m2, l2, o2);
+  }
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) S.o[w][col * 8 + e] = oacc[e];
+    if (lane == 0) {
+      S.m[w] = om;
+      S.l[w] = ol;
+    }
+  }
+  __syncthreads();
+  float* part = a.iv_part + (static_cast<int64_t>(pair) * a.chunks_per_pair + chunk) * (DI + 2);
+  const int tid = threadIdx.x;
+  if (tid < DI + 2) {
+    float M = S.m[0];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, S.m[ww]);
+    const float mu = M == -INFINITY ? 0.f : M;
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float sw = __builtin_amdgcn_exp2f(S.m[ww] - mu);
+      v += sw * (tid < DI ? S.o[ww][tid] : S.l[ww]);
+    }
+    part[tid] = tid < DI ? v : (tid == DI ? M : v);
+  }
+}
+
 // Short chunks: the n newest tokens of a sequence (positions L - n + i) are
 // scored in one pass over the sequence's pages, QG queries at a time: each
 // token row of a page is dotted with every query of the group and masked by

@@ -14,6 +14,16 @@ __global__ __launch_bounds__(kWgThreads) void decode_score_kernel(ScoreArgs a) {
   score_chunk<IT, DI>(a, pair, blockIdx.x - pair * a.chunks_per_pair);
 }
 
+// The same grid with the index-value branch on: scores and value partials.
+template <class IT, int DI>
+__global__ __launch_bounds__(kWgThreads) void decode_score_value_kernel(ScoreArgs a) {
+  __shared__ IvLds<DI> lds;
+  if (blockIdx.x == 0 && a.zero_words != nullptr)
+    for (int i = threadIdx.x; i < a.zero_count; i += kWgThreads) a.zero_words[i] = 0u;
+  const int pair = blockIdx.x / a.chunks_per_pair;
+  score_value_chunk<IT, DI>(a, pair, blockIdx.x - pair * a.chunks_per_pair, lds);
+}
+
 // Short chunks: one workgroup per (pair, chunk), every query of the pair's
 // sequence.
 template <class IT, int DI>
@@ -94,7 +104,10 @@ hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s) {
 template <class IT, int DI>
 static void launch_score_t(const ScoreArgs& a, hipStream_t s) {
   const int grid = a.num_seqs * a.hidx * a.chunks_per_pair;
-  decode_score_kernel<IT, DI><<<grid, kWgThreads, 0, s>>>(a);
+  if (a.idx_v != nullptr)
+    decode_score_value_kernel<IT, DI><<<grid, kWgThreads, 0, s>>>(a);
+  else
+    decode_score_kernel<IT, DI><<<grid, kWgThreads, 0, s>>>(a);
 }
 
 hipError_t launch_decode_score(const ScoreArgs& a, int idx_dtype, int idx_dim,

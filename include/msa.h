@@ -33,10 +33,18 @@
  *              rows cu[b]..cu[b+1]-1 and are the sequence's LAST tokens, at
  *              positions seq_lens[b] - n_b + i
  *   scores     [T, Hidx, max_blocks] float32
+ *   idx_v_pool [P, Hidx, 128, Di]   idx_dtype (index-value branch only)
  *   sel_blocks [T, Hidx, Kmax] int32, Kmax = topk + init + local, ascending,
  *              -1 padded;  sel_count [T, Hidx] int32
  *   out        [T, Hq, D] q_dtype;  lse [T, Hq] float32 (natural log, of the
  *              scaled logits; -inf and out = 0 for a query with no tokens)
+ *   idx_out    [T, Hidx, Di] q_dtype (index-value branch): per index head,
+ *              softmax attention of the index query over the index keys and
+ *              index values of every token t <= p, logits q_idx . k_idx /
+ *              sqrt(Di); zeros for a query with no tokens.  The sglang page
+ *              returns such an index output (idx_o, num_idx_heads *
+ *              sparse_index_dim per token) beside the attention output; what
+ *              its ops compute is not on the page, this is the reading taken.
  *
  * Head maps: q head hq reads kv head g = hq / (Hq/Hkv); kv head g uses index
  * head h = g / (Hkv/Hidx).
@@ -120,6 +128,11 @@ typedef struct {
                             rest (|S| = min(nb, max(topk, |F|))), the reading
                             under which the sglang page sizes its dense
                             fallback for topk_blocks * block_size_k tokens */
+  int32_t index_value;   /* 1: the index-value branch is on: decode and
+                            prefill also take the index-value pool and write
+                            idx_out, the append stores index values; 0: off
+                            (the sglang page's disable_index_value), those
+                            pointers must be NULL */
 } msa_params_t;
 
 /* Library version, (major << 16) | minor. */
@@ -188,15 +201,19 @@ msa_status_t msa_select_blocks(const msa_params_t* params,
  * One query per sequence: score, select, split-K
  * attention over the selected blocks and log-sum-exp combine.  out [B, Hq, D]
  * in q_dtype.  lse_out, sel_blocks_out and sel_count_out may be NULL; when
- * given they receive the per-head lse and the selection.  ws: a workspace of
+ * given they receive the per-head lse and the selection.  With
+ * params->index_value, the index scan also reads idx_v_pool and the
+ * index-value output goes to idx_out [B, Hidx, Di] (one pass over the index
+ * keys serves both); otherwise both must be NULL.  ws: a workspace of
  * msa_decode_workspace_size() bytes.
  */
 msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q,
                                const void* idx_q, const void* k_pool,
                                const void* v_pool, const void* idx_k_pool,
-                               int64_t num_pages, const int32_t* block_table,
-                               int32_t max_blocks, const int32_t* seq_lens,
-                               int32_t num_seqs, void* out, float* lse_out,
+                               const void* idx_v_pool, int64_t num_pages,
+                               const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* seq_lens, int32_t num_seqs,
+                               void* out, void* idx_out, float* lse_out,
                                int32_t* sel_blocks_out,
                                int32_t* sel_count_out, void* ws,
                                size_t ws_bytes, void* stream);
@@ -218,9 +235,10 @@ msa_status_t msa_sparse_decode(const msa_params_t* params, const void* q,
 msa_status_t msa_sparse_decode_noalloc(const msa_params_t* params, const void* q,
                                        const void* idx_q, const void* k_pool,
                                        const void* v_pool, const void* idx_k_pool,
-                                       int64_t num_pages, const int32_t* block_table,
-                                       int32_t max_blocks, const int32_t* seq_lens,
-                                       int32_t num_seqs, void* out, float* lse_out,
+                                       const void* idx_v_pool, int64_t num_pages,
+                                       const int32_t* block_table, int32_t max_blocks,
+                                       const int32_t* seq_lens, int32_t num_seqs,
+                                       void* out, void* idx_out, float* lse_out,
                                        int32_t* sel_blocks_out, int32_t* sel_count_out,
                                        void* stream);
 
@@ -258,15 +276,20 @@ msa_status_t msa_sparse_attend(const msa_params_t* params, const void* q,
  * index GEMM and key-major tiles over per-block token lists.  The choice
  * follows from the shapes alone, like the workspace size.
  * Needs bf16 index keys and num_q_tokens < 2^23 (MSA_ERR_UNSUPPORTED
- * otherwise).  ws: msa_prefill_workspace_size() bytes.
+ * otherwise).  With params->index_value, idx_out [T, Hidx, Di] receives the
+ * index-value branch (causal attention over the index keys and values, split
+ * over runs of key blocks as the index scoring is, on the matrix cores);
+ * otherwise idx_v_pool and idx_out must be NULL.
+ * ws: msa_prefill_workspace_size() bytes.
  */
 msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q,
                                 const void* idx_q, const void* k_pool,
                                 const void* v_pool, const void* idx_k_pool,
-                                int64_t num_pages, const int32_t* block_table,
-                                int32_t max_blocks, const int32_t* seq_lens,
+                                const void* idx_v_pool, int64_t num_pages,
+                                const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* seq_lens,
                                 const int32_t* cu_seqlens_q, int32_t num_seqs,
-                                int32_t num_q_tokens, void* out,
+                                int32_t num_q_tokens, void* out, void* idx_out,
                                 float* lse_out, int32_t* sel_blocks_out,
                                 int32_t* sel_count_out, void* ws,
                                 size_t ws_bytes, void* stream);
@@ -283,13 +306,17 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q,
  *                (q_dtype); idx_k_new [T, Hidx, Di] in idx_dtype.
  *   fp8 pools store e4m3fn(RNE(clamp(x / k_scale, +-448))) (v_scale for V;
  *   the division in float32); e5m2 pools the same with +-57344.
+ *   With params->index_value, idx_v_new [T, Hidx, Di] (idx_dtype) goes to
+ *   idx_v_pool beside the index keys (the page stores idx_v unless the layer
+ *   disables the value branch); otherwise both must be NULL.
  * Nothing else is read or written.
  */
 msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new,
                            const void* v_new, const void* idx_k_new,
-                           const int64_t* slot_mapping, int32_t num_tokens,
-                           void* k_pool, void* v_pool, void* idx_k_pool,
-                           int64_t num_pages, void* stream);
+                           const void* idx_v_new, const int64_t* slot_mapping,
+                           int32_t num_tokens, void* k_pool, void* v_pool,
+                           void* idx_k_pool, void* idx_v_pool, int64_t num_pages,
+                           void* stream);
 
 /*
  * fp8-e4m3 dequantisation exactly as the attention loaders do it (sglang

@@ -74,6 +74,15 @@ WORKLOADS = {
         kind="decode", B=32, seq_lens=("fixed", 65536), Hq=16, Hkv=2, Hidx=2,
         D=128, Di=128, topk=32, init=1, local=2, q="bf16", kv="fp8_e5m2", idx="bf16",
         k_scale=1.0 / 16, v_scale=1.0 / 16),
+    # the index-value branch on (an index-value pool beside the index keys)
+    "decode_iv_b32_l32k": dict(
+        kind="decode", B=32, seq_lens=("fixed", 32768), Hq=16, Hkv=2, Hidx=2,
+        D=128, Di=128, topk=16, init=1, local=2, q="bf16", kv="bf16", idx="bf16",
+        idx_value=True),
+    "prefill_iv_4x4096_p16k": dict(
+        kind="prefill", B=4, n_new=4096, prefix=16384, Hq=16, Hkv=2, Hidx=2,
+        D=128, Di=128, topk=16, init=1, local=2, q="bf16", kv="bf16", idx="bf16",
+        idx_value=True),
 }
 
 # Seeds of the workloads, in the order above.

@@ -42,8 +42,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_params_struct_layout_matches_header():
-    # 14 int32 / float fields + 2 floats, no padding
-    assert ctypes.sizeof(_lib.Params) == 16 * 4
+    # 17 four-byte int32 / float fields, no padding
+    assert ctypes.sizeof(_lib.Params) == 17 * 4
 
 
 def base_cfg(**kw):
@@ -57,8 +57,8 @@ def decode_call(cfg, num_seqs=4, max_blocks=16, ws=FAKE, ws_bytes=1 << 30, q=FAK
                 num_pages=64):
     p = cfg.params()
     return msa.load().msa_sparse_decode(
-        ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, num_pages, FAKE, max_blocks, FAKE, num_seqs,
-        FAKE, None, None, None, ws, ws_bytes, None)
+        ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, None, num_pages, FAKE, max_blocks, FAKE,
+        num_seqs, FAKE, None, None, None, None, ws, ws_bytes, None)
 
 
 BAD_PARAMS = [
@@ -92,8 +92,8 @@ def test_bad_params_rejected(kw, code):
 
 def test_null_params_and_pointers():
     lib = msa.load()
-    assert lib.msa_sparse_decode(None, *([FAKE] * 5), 64, FAKE, 16, FAKE, 4, FAKE, None, None,
-                                 None, FAKE, 1 << 20, None) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_sparse_decode(None, *([FAKE] * 5), None, 64, FAKE, 16, FAKE, 4, FAKE, None,
+                                 None, None, None, FAKE, 1 << 20, None) == _lib.MSA_ERR_INVALID_ARG
     assert decode_call(base_cfg(), q=None) == _lib.MSA_ERR_INVALID_ARG
     assert "NULL" in lib.msa_last_error().decode()
 
@@ -128,8 +128,8 @@ def test_selection_pairing_required():
     cfg = base_cfg()
     p = cfg.params()
     st = msa.load().msa_sparse_decode(
-        ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 16, FAKE, 4, FAKE, None,
-        FAKE, None, FAKE, 1 << 30, None)
+        ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, FAKE, 16, FAKE, 4, FAKE, None,
+        None, FAKE, None, FAKE, 1 << 30, None)
     assert st == _lib.MSA_ERR_INVALID_ARG
 
 
@@ -168,12 +168,12 @@ def test_prefill_workspace_and_token_limit():
 def append_call(cfg, num_tokens=8, num_pages=16, **ptrs):
     p = cfg.params()
     args = dict(k_new=FAKE, v_new=FAKE, idx_k_new=FAKE, slots=FAKE, k_pool=FAKE, v_pool=FAKE,
-                idx_k_pool=FAKE)
+                idx_k_pool=FAKE, idx_v_new=None, idx_v_pool=None)
     args.update(ptrs)
     return msa.load().msa_append_kv(ctypes.byref(p), args["k_new"], args["v_new"],
-                                    args["idx_k_new"], args["slots"], num_tokens,
-                                    args["k_pool"], args["v_pool"], args["idx_k_pool"],
-                                    num_pages, None)
+                                    args["idx_k_new"], args["idx_v_new"], args["slots"],
+                                    num_tokens, args["k_pool"], args["v_pool"],
+                                    args["idx_k_pool"], args["idx_v_pool"], num_pages, None)
 
 
 def test_append_validation_before_launch():
@@ -217,9 +217,10 @@ def test_msa_log_prints_the_launch_configuration():
         "cfg = msa.MsaConfig(num_q_heads=16, num_kv_heads=2, num_idx_heads=2)\n"
         "p = cfg.params(); F = ctypes.c_void_p(1 << 20)\n"
         "lib = msa.load()\n"
-        "assert lib.msa_append_kv(ctypes.byref(p), F, F, F, F, 0, F, F, F, 16, None) == 0\n"
-        "assert lib.msa_sparse_decode(ctypes.byref(p), F, F, F, F, F, 64, F, 16, F, 0, F, None,"
-        " None, None, ctypes.c_void_p(1 << 20), 1 << 20, None) == 0\n")
+        "assert lib.msa_append_kv(ctypes.byref(p), F, F, F, None, F, 0, F, F, F, None, 16,"
+        " None) == 0\n"
+        "assert lib.msa_sparse_decode(ctypes.byref(p), F, F, F, F, F, None, 64, F, 16, F, 0, F,"
+        " None, None, None, None, ctypes.c_void_p(1 << 20), 1 << 20, None) == 0\n")
     env = dict(os.environ, MSA_LOG="1")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
                        timeout=120, cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
@@ -255,16 +256,16 @@ def test_launch_sizes_past_the_grid_range_are_refused():
     assert lib.msa_fp8_dequant(FAKE, FAKE, 1 << 36, 1.0, _lib.MSA_FP8_E4M3,
                                None) == _lib.MSA_ERR_UNSUPPORTED
     # a long prefill chunk over more sequences than the list kernels' grid rows
-    assert lib.msa_sparse_prefill(ctypes.byref(p), *([FAKE] * 5), 64, FAKE, 8, FAKE, FAKE,
-                                  70000, 600000, FAKE, None, None, None, FAKE, 1 << 40,
+    assert lib.msa_sparse_prefill(ctypes.byref(p), *([FAKE] * 5), None, 64, FAKE, 8, FAKE, FAKE,
+                                  70000, 600000, FAKE, None, None, None, None, FAKE, 1 << 40,
                                   None) == _lib.MSA_ERR_UNSUPPORTED
 
 
 def noalloc_call(cfg, num_seqs=4, max_blocks=16, q=FAKE):
     p = cfg.params()
     return msa.load().msa_sparse_decode_noalloc(
-        ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, 64, FAKE, max_blocks, FAKE, num_seqs,
-        FAKE, None, None, None, None)
+        ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, None, 64, FAKE, max_blocks, FAKE, num_seqs,
+        FAKE, None, None, None, None, None)
 
 
 def test_noalloc_decode_validates_before_touching_the_device():
@@ -280,3 +281,26 @@ def test_noalloc_decode_validates_before_touching_the_device():
     assert noalloc_call(base_cfg(), num_seqs=4096, max_blocks=8192) == _lib.MSA_ERR_UNSUPPORTED
     err = lib.msa_last_error().decode()
     assert "scratch" in err and str(need) in err
+
+
+def test_index_value_pointers_follow_the_flag():
+    """idx_v_pool / idx_out (idx_v_new / idx_v_pool for the append) are given
+    exactly when params.index_value is set; checked before any launch."""
+    lib = msa.load()
+    on = base_cfg(index_value=True).params()
+    off = base_cfg().params()
+    args = lambda p, iv, io: (ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, iv, 64, FAKE, 16,
+                              FAKE, 4, FAKE, io, None, None, None, FAKE, 1 << 30, None)
+    assert lib.msa_sparse_decode(*args(on, None, None)) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_sparse_decode(*args(on, FAKE, None)) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_sparse_decode(*args(off, FAKE, FAKE)) == _lib.MSA_ERR_INVALID_ARG
+    assert "index_value" in lib.msa_last_error().decode()
+    assert append_call(base_cfg(index_value=True)) == _lib.MSA_ERR_INVALID_ARG
+    assert append_call(base_cfg(), idx_v_new=FAKE, idx_v_pool=FAKE) == _lib.MSA_ERR_INVALID_ARG
+    # the decode workspace grows by the scan's value partials
+    a = msa.decode_workspace_size(base_cfg(), 8, 256)
+    b = msa.decode_workspace_size(base_cfg(index_value=True), 8, 256)
+    assert b >= a + 8 * 2 * 32 * 130 * 4
+    bad = base_cfg().params()
+    bad.index_value = 2
+    assert lib.msa_decode_workspace_size(ctypes.byref(bad), 4, 16) == 0
