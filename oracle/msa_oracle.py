@@ -223,6 +223,17 @@ def _gather_rows_raw(pool: np.ndarray, bt_row: np.ndarray, head: int, n_tokens: 
     return rows[:n_tokens]
 
 
+def _gather_values(pool: np.ndarray, bt_row: np.ndarray, head: int, n_tokens: int, dtype: str,
+                   scale: float, D: int) -> np.ndarray:
+    """Values (float64) of rows 0..n_tokens-1 of one head of a sequence."""
+    if dtype == "mxfp4":
+        nbk = (n_tokens + BLOCK - 1) // BLOCK
+        pages = np.asarray(bt_row[:nbk], dtype=np.int64)
+        vals = mxfp4_decode_runs(pool[pages, head], D, scale)
+        return vals.reshape(nbk * BLOCK, D)[:n_tokens]
+    return decode(_gather_rows_raw(pool, bt_row, head, n_tokens), dtype, scale)
+
+
 # --------------------------------------------------------------------------
 # Step 2: forced blocks and top-k selection
 # --------------------------------------------------------------------------
@@ -325,10 +336,10 @@ def attend(inp: dict, sel: np.ndarray, cnt: np.ndarray, scale: Optional[float] =
         if L <= 0:
             continue
         for g in range(Hkv):
-            kr = decode(_gather_rows_raw(inp["k_pool"], inp["block_table"][b], g, L),
-                        inp["kv_dtype"], inp.get("k_scale", 1.0))
-            vr = decode(_gather_rows_raw(inp["v_pool"], inp["block_table"][b], g, L),
-                        inp["kv_dtype"], inp.get("v_scale", 1.0))
+            kr = _gather_values(inp["k_pool"], inp["block_table"][b], g, L, inp["kv_dtype"],
+                                inp.get("k_scale", 1.0), D)
+            vr = _gather_values(inp["v_pool"], inp["block_table"][b], g, L, inp["kv_dtype"],
+                                inp.get("v_scale", 1.0), D)
             h = g // gpi
             for t, p in items:
                 blocks = sel[t, h, : cnt[t, h]]
@@ -449,14 +460,29 @@ def append_kv(k_pool, v_pool, idx_k_pool, k_new, v_new, idx_k_new, slots, *,
         if s < 0 or s >= P * BLOCK:
             continue
         page, off = divmod(int(s), BLOCK)
-        k_pool[page, :, off, :] = store_values(k_new[t], kv_src, kv_dtype, k_scale)
-        v_pool[page, :, off, :] = store_values(v_new[t], kv_src, kv_dtype, v_scale)
+        if kv_dtype == "mxfp4":
+            for pool, new, sc in ((k_pool, k_new, k_scale), (v_pool, v_new, v_scale)):
+                _store_mxfp4_row(pool, page, off, new[t], kv_src, sc)
+        else:
+            k_pool[page, :, off, :] = store_values(k_new[t], kv_src, kv_dtype, k_scale)
+            v_pool[page, :, off, :] = store_values(v_new[t], kv_src, kv_dtype, v_scale)
         idx_k_pool[page, :, off, :] = store_values(idx_k_new[t], idx_dtype, idx_dtype)
         if idx_v_pool is not None:
             idx_v_pool[page, :, off, :] = store_values(idx_v_new[t], idx_dtype, idx_dtype)
     if idx_v_pool is not None:
         return k_pool, v_pool, idx_k_pool, idx_v_pool
     return k_pool, v_pool, idx_k_pool
+
+
+def _store_mxfp4_row(pool, page, off, new_row, src, scale):
+    """One token's rows [H, D] (bf16 bits) into an MX-fp4 pool: the float32
+    quotient x / scale encoded per group of 32 (mxfp4_encode_rows)."""
+    x32 = decode(new_row, src).astype(np.float32) / np.float32(scale)
+    codes, sc = mxfp4_encode_rows(x32)
+    D = new_row.shape[-1]
+    nc = BLOCK * D // 2
+    pool[page, :, off * D // 2:(off + 1) * D // 2] = codes
+    pool[page, :, nc + off * D // MXFP4_GROUP:nc + (off + 1) * D // MXFP4_GROUP] = sc
 
 
 # --------------------------------------------------------------------------
@@ -496,3 +522,97 @@ def index_value_attention(inp: dict, scale: Optional[float] = None):
             out[t, h] = o[0]
             lse[t, h] = l[0]
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# MX-fp4 K/V pools
+# --------------------------------------------------------------------------
+#
+# The vLLM page keeps 4-bit K/V caches with per-block scales in per-head
+# K/V slots (MiniMaxM3SparseMSANvfp4Backend).  The gfx950 counterpart taken
+# here is the OCP Microscaling MXFP4 format: E2M1 element codes, a shared
+# E8M0 scale per 32 consecutive elements.  Pool layout per (page, head): the
+# 128 x D / 2 code bytes (two codes per byte, element 2i in the low nibble),
+# then the 128 x D / 32 scale bytes; the per-tensor k_scale / v_scale
+# multiply on top.
+
+MXFP4_GROUP = 32
+
+
+def fp4_e2m1_table() -> np.ndarray:
+    """Values of the 16 OCP E2M1 codes: s.ee.m, exponent bias 1; exponent
+    field 0 encodes the subnormal m * 0.5; no infinities or NaN."""
+    tab = np.empty(16, dtype=np.float64)
+    for code in range(16):
+        sign = -1.0 if code & 0x8 else 1.0
+        e = (code >> 1) & 0x3
+        m = code & 0x1
+        tab[code] = sign * (m * 0.5 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1))
+    return tab
+
+
+def e8m0_table() -> np.ndarray:
+    """Values of the 256 E8M0 scale codes: 2^(code - 127); 0xFF is NaN."""
+    tab = np.array([2.0 ** (c - 127) for c in range(256)], dtype=np.float64)
+    tab[255] = math.nan
+    return tab
+
+
+def mxfp4_run_bytes(D: int) -> int:
+    return BLOCK * D // 2 + BLOCK * D // MXFP4_GROUP
+
+
+def mxfp4_decode_runs(runs: np.ndarray, D: int, scale: float = 1.0) -> np.ndarray:
+    """[..., run bytes] uint8 -> [..., 128, D] float64 values times scale."""
+    runs = np.asarray(runs, dtype=np.uint8)
+    nc = BLOCK * D // 2
+    codes = runs[..., :nc].reshape(runs.shape[:-1] + (BLOCK, D // 2))
+    sc = runs[..., nc:].reshape(runs.shape[:-1] + (BLOCK, D // MXFP4_GROUP))
+    tab = fp4_e2m1_table()
+    el = np.empty(runs.shape[:-1] + (BLOCK, D), dtype=np.float64)
+    el[..., 0::2] = tab[codes & 0xF]
+    el[..., 1::2] = tab[codes >> 4]
+    s = e8m0_table()[sc]
+    return el * np.repeat(s, MXFP4_GROUP, axis=-1) * float(scale)
+
+
+def fp4_e2m1_encode(y: np.ndarray) -> np.ndarray:
+    """Magnitudes to E2M1 codes: nearest of the eight values, an exact tie to
+    the even mantissa, clamped at 6; the sign is kept (-0 -> 0x8)."""
+    y = np.asarray(y, dtype=np.float64)
+    tab = fp4_e2m1_table()[:8]
+    mag = np.minimum(np.abs(np.where(np.isnan(y), 0.0, y)), 6.0)
+    dist = np.abs(mag[..., None] - tab)
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best
+    even = cand & ((np.arange(8) & 1) == 0)
+    pick = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    return (pick | np.where(np.signbit(y), 8, 0)).astype(np.uint8)
+
+
+def mxfp4_encode_rows(x32: np.ndarray):
+    """Rows [..., D] of float32 values -> (codes [..., D / 2], scale codes
+    [..., D / 32]) by the OCP rule: per group of 32, the shared exponent is
+    floor(log2(max |x|)) - 2 (2 being E2M1's largest exponent), clamped to the
+    E8M0 range (an all-zero group takes code 0), and every element is
+    encoded as x / 2^exponent; a group holding a NaN gets the NaN scale code."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    D = x.shape[-1]
+    g = x.reshape(x.shape[:-1] + (D // MXFP4_GROUP, MXFP4_GROUP))
+    nan = np.isnan(g).any(axis=-1)
+    amax = np.max(np.abs(np.where(np.isnan(g), 0.0, g)), axis=-1)
+    _, e = np.frexp(amax)                       # amax = f * 2^e, f in [0.5, 1)
+    k = np.where(amax > 0, e - 1 - 2, -127)
+    sc = np.clip(k + 127, 0, 254)
+    X = np.ldexp(1.0, (sc - 127).astype(np.int64))
+    codes = fp4_e2m1_encode(g / X[..., None]).reshape(x.shape)
+    codes = np.where(np.repeat(nan, MXFP4_GROUP, axis=-1), np.uint8(0), codes)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, np.where(nan, 255, sc).astype(np.uint8)
+
+
+def mxfp4_encode_run_rows(x32: np.ndarray):
+    """Convenience: [..., 128, D] float32 -> [..., run bytes] (codes, then scales)."""
+    codes, sc = mxfp4_encode_rows(x32)
+    lead = codes.shape[:-2]
+    return np.concatenate([codes.reshape(lead + (-1,)), sc.reshape(lead + (-1,))], axis=-1)

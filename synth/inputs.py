@@ -6,7 +6,12 @@ Recipe (applies to every workload below):
   K, V ``[P, Hkv, 128, D]`` and index-K ``[P, Hidx, 128, Di]``.
 * Values are float32 N(0,1) draws rounded to the storage type with
   round-to-nearest-even (bf16 / f32), or, for fp8-e4m3 pools, divided by the
-  per-tensor scale, clamped to +-448 and rounded to e4m3fn.
+  per-tensor scale, clamped to +-448 and rounded to e4m3fn.  MX-fp4 pools
+  (OCP E2M1 codes with an E8M0 scale per 32 elements) hold, per (page,
+  head), the 128 x D / 2 code bytes then the 128 x D / 32 scale bytes of the
+  draws divided by the per-tensor scale: per group of 32 the scale is
+  2^(floor(log2 max|x|) - 2) and each code the nearest E2M1 value of
+  x / scale (ties to the even code, clamped at 6).
 * Physical page ids come from a seeded permutation; ``P`` = pages used plus
   ``max(8, ceil(1%))`` spare pages.  Unused block-table entries are -1.
 * Poison: spare pages and the token slots past ``seq_len`` in every
@@ -90,7 +95,28 @@ WORKLOAD_SEEDS = {name: 1001 + i for i, name in enumerate(WORKLOADS)}
 
 _TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.float8_e4m3fn,
              "fp8_e5m2": torch.float8_e5m2}
-_POISON_KV = {"bf16": float("nan"), "f32": float("nan")}
+MX_GROUP = 32
+
+
+def mxfp4_run_bytes(D: int) -> int:
+    return BLOCK * D // 2 + BLOCK * D // MX_GROUP
+
+
+def _mxfp4_runs(y: torch.Tensor) -> torch.Tensor:
+    """[n, H, 128, D] float32 -> [n, H, run bytes] uint8 (codes, then scales)."""
+    n, H, T, D = y.shape
+    g = y.reshape(n, H, T, D // MX_GROUP, MX_GROUP)
+    amax = g.abs().amax(dim=-1)
+    _, e = torch.frexp(amax)
+    k = torch.where(amax > 0, e - 3, torch.full_like(e, -127))
+    sc = (k + 127).clamp(0, 254)
+    a = torch.ldexp(g, (127 - sc).unsqueeze(-1)).abs()
+    code = ((a > 0.25).to(torch.int32) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5)
+            + (a >= 3.5) + (a > 5.0))
+    code = (code | (torch.signbit(g).to(torch.int32) << 3)).reshape(n, H, T, D)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).to(torch.uint8)
+    return torch.cat([packed.reshape(n, H, -1), sc.to(torch.uint8).reshape(n, H, -1)], dim=-1)
+_POISON_KV = {"bf16": float("nan"), "f32": float("nan"), "mxfp4": 0.0}
 FP8_NAN_BYTE = 0x7F
 IDX_POISON = 1.0e4
 
@@ -168,13 +194,19 @@ def _quantise(x: torch.Tensor, dtype: str, scale: float) -> torch.Tensor:
 
 
 def _draw_pool(P, H, Dm, dtype, scale, g, device) -> torch.Tensor:
-    out_dt = torch.uint8 if dtype.startswith("fp8") else _TORCH_DT[dtype]
-    pool = torch.empty((P, H, BLOCK, Dm), dtype=out_dt, device=device)
+    if dtype == "mxfp4":
+        pool = torch.empty((P, H, mxfp4_run_bytes(Dm)), dtype=torch.uint8, device=device)
+    else:
+        out_dt = torch.uint8 if dtype.startswith("fp8") else _TORCH_DT[dtype]
+        pool = torch.empty((P, H, BLOCK, Dm), dtype=out_dt, device=device)
     for p0 in range(0, P, PAGE_CHUNK):
         p1 = min(P, p0 + PAGE_CHUNK)
         x = torch.randn((p1 - p0, H, BLOCK, Dm), generator=g, device=device,
                         dtype=torch.float32)
-        pool[p0:p1] = _quantise(x, dtype, scale)
+        if dtype == "mxfp4":
+            pool[p0:p1] = _mxfp4_runs(x / scale)
+        else:
+            pool[p0:p1] = _quantise(x, dtype, scale)
     return pool
 
 
@@ -182,6 +214,13 @@ def _poison(pool: torch.Tensor, valid: torch.Tensor, dtype: str, value: float):
     """Overwrite token slots ``t >= valid[page]`` of every page."""
     tok = torch.arange(BLOCK, device=pool.device)
     bad = tok[None, :] >= valid.to(pool.device)[:, None]          # [P,128]
+    if dtype == "mxfp4":
+        # the NaN scale code (0xFF) for every group of the slot
+        D = pool.shape[-1] // (BLOCK // 2 + BLOCK // MX_GROUP)   # run = 128 D / 2 + 128 D / 32
+        nsc = D // MX_GROUP
+        sc = pool[:, :, pool.shape[-1] - BLOCK * nsc:].view(pool.shape[0], pool.shape[1], BLOCK, nsc)
+        sc.masked_fill_(bad[:, None, :, None].expand(sc.shape), 0xFF)
+        return
     bad = bad[:, None, :, None].expand(pool.shape)
     if dtype.startswith("fp8"):
         pool.masked_fill_(bad, FP8_NAN_BYTE)   # NaN in e4m3 and in e5m2

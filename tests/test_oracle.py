@@ -801,3 +801,176 @@ def test_index_value_empty_sequence_and_append():
                            idx_v_new=new[3])
     assert len(res) == 4
     assert np.array_equal(res[3][1, :, 2], new[3][0]) and np.array_equal(res[3][0, :, 5], new[3][1])
+
+
+# ------------------------------------------------------------- MX-fp4 pools
+
+def test_e2m1_table_from_the_format():
+    """E2M1: the eight magnitudes the format definition gives (0, the
+    subnormal 0.5, then 1 .. 6), negated by the sign bit; each is exactly an
+    e4m3 value, and the e4m3 code with the same sign, exponent (rebiased from
+    1 to 7) and mantissa (shifted up two bits) holds it (e4m3 table pinned
+    against torch's cast above)."""
+    tab = oracle.fp4_e2m1_table()
+    assert list(tab[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(tab[8:]) == [-0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    assert math.copysign(1.0, tab[8]) == -1.0
+    e4 = oracle.fp8_e4m3fn_table()
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        if e == 0 and m == 1:
+            e4code = (s << 7) | 0x30            # 0.5 = 2^-1: e4m3 exponent field 6
+        elif e == 0:
+            e4code = s << 7
+        else:
+            e4code = (s << 7) | ((e - 1 + 7) << 3) | (m << 2)
+        assert tab[c] == e4[e4code], c
+    got = torch.from_numpy(tab).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(got, tab)
+
+
+def test_e8m0_table_matches_torch_all_codes():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    mine = oracle.e8m0_table()
+    assert np.isnan(mine[255]) and np.isnan(ref[255])
+    assert np.array_equal(mine[:255], ref[:255])
+
+
+def _brute_group(x):
+    """One group of 32 float32 values, brute force: the largest k with
+    2^k <= max|x| (by repeated doubling), scale 2^(k-2) (clamped to the E8M0
+    range), and per element the E2M1 code nearest to x / scale among all 16,
+    ties to the even code."""
+    amax = max(abs(float(v)) for v in x)
+    if amax == 0:
+        sc = 0
+    else:
+        k = 0
+        while 2.0 ** (k + 1) <= amax:
+            k += 1
+        while 2.0 ** k > amax:
+            k -= 1
+        sc = min(max(k - 2 + 127, 0), 254)
+    X = 2.0 ** (sc - 127)
+    tab = oracle.fp4_e2m1_table()
+    codes = []
+    for v in x:
+        y = min(max(float(v) / X, -6.0), 6.0)
+        d = [abs(y - tab[c]) for c in range(16)]
+        sign_ok = [c for c in range(16) if (c >= 8) == (math.copysign(1.0, y) < 0)]
+        best = min(d[c] for c in sign_ok)
+        cands = [c for c in sign_ok if d[c] == best]
+        even = [c for c in cands if c % 2 == 0]
+        codes.append((even or cands)[0])
+    return sc, codes
+
+
+def test_mxfp4_encoder_brute_force():
+    rng = np.random.default_rng(17)
+    groups = [rng.standard_normal(32).astype(np.float32) * np.float32(2.0 ** rng.integers(-6, 7))
+              for _ in range(40)]
+    tab = oracle.fp4_e2m1_table()
+    # exact midpoints between neighbouring codes, scaled: ties to the even code
+    mids = np.array([(tab[i] + tab[i + 1]) / 2 for i in range(7)] * 4 + [6.0] * 4, dtype=np.float32)
+    groups.append(mids)
+    groups.append(-mids)
+    groups.append(np.zeros(32, dtype=np.float32))
+    groups.append(np.array([7.9] + [0.01] * 31, dtype=np.float32))   # saturates at 6 * scale
+    x = np.stack(groups)
+    packed, sc = oracle.mxfp4_encode_rows(x)
+    for gi, grp in enumerate(groups):
+        want_sc, want_codes = _brute_group(grp)
+        assert sc[gi, 0] == want_sc, gi
+        got = [(packed[gi, i // 2] >> (4 * (i % 2))) & 0xF for i in range(32)]
+        assert got == want_codes, gi
+
+
+def test_mxfp4_run_layout_and_round_trip():
+    """Run layout (codes of token t at bytes t * D / 2 .., element 2i in the
+    low nibble; scales after all codes) and values of the form code * 2^k that
+    come back exactly."""
+    D = 64
+    rng = np.random.default_rng(5)
+    tab = oracle.fp4_e2m1_table()
+    codes = rng.integers(0, 16, (128, D))
+    codes[:, ::32] = 7                       # every group holds a 6: scale = its 2^k
+    k = rng.integers(-4, 5, (128, D // 32))
+    vals = (tab[codes] * np.repeat(2.0 ** k, 32, axis=1)).astype(np.float32)
+    run = oracle.mxfp4_encode_run_rows(vals[None])[0]
+    assert run.shape == (oracle.mxfp4_run_bytes(D),)
+    assert run[0] & 0xF == codes[0, 0] and run[0] >> 4 == codes[0, 1]
+    assert run[D // 2 * 5 + 3] >> 4 == codes[5, 7]
+    assert run[128 * D // 2 + 2 * 9 + 1] == k[9, 1] + 127
+    dec = oracle.mxfp4_decode_runs(run[None], D)[0]
+    assert np.array_equal(dec, vals.astype(np.float64))
+    # a NaN scale code decodes its group to NaN
+    bad = run.copy()
+    bad[128 * D // 2] = 0xFF
+    dec = oracle.mxfp4_decode_runs(bad[None], D)[0]
+    assert np.isnan(dec[0, :32]).all() and not np.isnan(dec[0, 32:]).any()
+
+
+def test_mxfp4_synthetic_pools_follow_the_encoder():
+    """The generator's MX-fp4 pools are the oracle encoder's bytes of the same
+    float draws (the generator holds its own vectorised copy of the rule)."""
+    from synth.inputs import _mxfp4_runs
+    g = torch.Generator().manual_seed(9)
+    x = torch.randn((3, 2, 128, 128), generator=g) * 1.7
+    mine = _mxfp4_runs(x).numpy()
+    ref = oracle.mxfp4_encode_run_rows(x.numpy())
+    assert np.array_equal(mine, ref)
+
+
+@pytest.mark.parametrize("prefill", [None, (100, 256)])
+def test_mxfp4_attention_dense_equivalence_and_brute_force(prefill):
+    inp = _tiny_case(61, lens=(1000, 600), Hq=6, Hkv=3, Hidx=1, D=64, Di=8, topk=8,
+                     kv="mxfp4", prefill_new=prefill)
+    res = oracle.sparse_attention(inp)
+    # dense causal SDPA over the decoded pools
+    q = torch.from_numpy(oracle.decode(inp["q"], "bf16"))
+    for b, L in enumerate(inp["seq_lens"]):
+        L = int(L)
+        nbk = (L + 127) // 128
+        pages = inp["block_table"][b, :nbk].astype(np.int64)
+        k = torch.from_numpy(oracle.mxfp4_decode_runs(inp["k_pool"][pages], 64))
+        v = torch.from_numpy(oracle.mxfp4_decode_runs(inp["v_pool"][pages], 64))
+        k = k.permute(1, 0, 2, 3).reshape(3, -1, 64)[:, :L].repeat_interleave(2, dim=0)
+        v = v.permute(1, 0, 2, 3).reshape(3, -1, 64)[:, :L].repeat_interleave(2, dim=0)
+        toks = [t for t, (bb, _) in enumerate(inp["_pos"]) if bb == b]
+        ps = torch.tensor([inp["_pos"][t][1] for t in toks])
+        mask = torch.arange(L)[None, :] <= ps[:, None]
+        o = torch.nn.functional.scaled_dot_product_attention(q[toks].permute(1, 0, 2), k, v,
+                                                             attn_mask=mask)
+        assert np.allclose(res["out"][toks], o.permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_mxfp4_append_oracle():
+    rng = np.random.default_rng(23)
+    P, H, D, T = 3, 2, 64, 4
+    run = oracle.mxfp4_run_bytes(D)
+    k_pool = rng.integers(0, 256, (P, H, run)).astype(np.uint8)
+    v_pool = rng.integers(0, 256, (P, H, run)).astype(np.uint8)
+    ik = np.zeros((P, 1, 128, 8), dtype=np.uint16)
+    xs = rng.standard_normal((T, H, D)).astype(np.float32)
+    bits = (xs.view(np.uint32) >> 16).astype(np.uint16)          # bf16 by truncation
+    new_ik = np.zeros((T, 1, 8), dtype=np.uint16)
+    slots = np.array([5, 130, -1, 383])
+    k2, v2, _ = oracle.append_kv(k_pool, v_pool, ik, bits, bits, new_ik, slots, kv_src="bf16",
+                                 kv_dtype="mxfp4", idx_dtype="bf16", k_scale=0.5, v_scale=2.0)
+    dk = oracle.mxfp4_decode_runs(k2, D, 0.5)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        page, off = divmod(int(s), 128)
+        x = oracle.decode(bits[t], "bf16")
+        err = np.abs(dk[page, :, off] - x)
+        # within one E2M1 step of the group's scale (times the tensor scale)
+        bound = np.repeat(np.abs(x).reshape(H, -1, 32).max(axis=-1), 32, axis=-1) / 2
+        assert (err <= bound + 1e-30).all()
+    changed = np.zeros((P, H, run), dtype=bool)
+    for s in slots[slots >= 0]:
+        page, off = divmod(int(s), 128)
+        changed[page, :, off * D // 2:(off + 1) * D // 2] = True
+        changed[page, :, 128 * D // 2 + off * 2:128 * D // 2 + off * 2 + 2] = True
+    assert np.array_equal(k2[~changed], k_pool[~changed])
