@@ -65,8 +65,9 @@ def parse():
     return ap.parse_args()
 
 
-def elem_bytes(dt: str) -> int:
-    return {"bf16": 2, "f32": 4, "fp8": 1, "fp8_e5m2": 1}[dt]
+def elem_bytes(dt: str) -> float:
+    # MX-fp4: half a byte per element plus one scale byte per 32
+    return {"bf16": 2, "f32": 4, "fp8": 1, "fp8_e5m2": 1, "mxfp4": 17 / 32}[dt]
 
 
 def step_bytes(spec, seq_lens, sel, cnt):
@@ -90,7 +91,7 @@ def step_bytes(spec, seq_lens, sel, cnt):
         # the index values of every visible token, and the index output
         idx_keys *= 2
         small += B * Hidx * Di * eq
-    return idx_keys, kv, small
+    return idx_keys, int(kv), small
 
 
 def score_kernel_bytes(spec, seq_lens, max_blocks):

@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import MSA_BF16, MSA_F32, MSA_FP8_E4M3, MSA_FP8_E5M2, Params, check, load
+from ._lib import MSA_BF16, MSA_F32, MSA_FP8_E4M3, MSA_FP8_E5M2, MSA_MXFP4, Params, check, load
 
 BLOCK = 128
 
@@ -49,7 +49,7 @@ class MsaConfig:
 
     def params(self) -> Params:
         code = {"bf16": MSA_BF16, "f32": MSA_F32, "fp8": MSA_FP8_E4M3,
-                "fp8_e5m2": MSA_FP8_E5M2}
+                "fp8_e5m2": MSA_FP8_E5M2, "mxfp4": MSA_MXFP4}
         return Params(self.num_q_heads, self.num_kv_heads, self.num_idx_heads, self.head_dim,
                       self.idx_dim, self.block_size, self.topk, self.init_blocks,
                       self.local_blocks, self.softmax_scale, code[self.q_dtype],
@@ -298,13 +298,18 @@ def append_kv(cfg: MsaConfig, k_new, v_new, idx_k_new, slot_mapping, k_pool, v_p
 def fp8_dequant(codes: torch.Tensor, scale: float = 1.0, out=None, fmt: str = "fp8",
                 stream=None):
     """fp8 codes (uint8; fmt "fp8" = e4m3, "fp8_e5m2") -> float32 values times
-    scale, as the loaders do it."""
+    scale, as the loaders do it.  fmt "mxfp4": ``codes`` holds n / 2 code bytes
+    then n / 32 scale bytes (17 n / 32 bytes), and n values come back."""
     if codes.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2):
         raise ValueError("codes must be uint8, float8_e4m3fn or float8_e5m2")
+    code = {"fp8": MSA_FP8_E4M3, "fp8_e5m2": MSA_FP8_E5M2, "mxfp4": MSA_MXFP4}[fmt]
+    n = codes.numel() if fmt != "mxfp4" else codes.numel() * 32 // 17
     if out is None:
-        out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
-    code = {"fp8": MSA_FP8_E4M3, "fp8_e5m2": MSA_FP8_E5M2}[fmt]
-    check(load().msa_fp8_dequant(_ptr(codes), _ptr(out), codes.numel(), float(scale), code,
+        shape = codes.shape if fmt != "mxfp4" else (n,)
+        out = torch.empty(shape, dtype=torch.float32, device=codes.device)
+    if out.numel() < n:
+        raise ValueError("out holds fewer values than the codes")
+    check(load().msa_fp8_dequant(_ptr(codes), _ptr(out), n, float(scale), code,
                                  _stream(stream)))
     return out
 

@@ -60,6 +60,8 @@ int kmax_of(const msa_params_t& p) { return p.topk + p.init_blocks + p.local_blo
 int group_of(const msa_params_t& p) { return p.num_q_heads / p.num_kv_heads; }
 
 bool is_fp8(int dtype) { return dtype == MSA_FP8_E4M3 || dtype == MSA_FP8_E5M2; }
+// K/V formats whose per-tensor k_scale / v_scale apply (fp8 codes, MX-fp4)
+bool scaled_kv(int dtype) { return is_fp8(dtype) || dtype == MSA_MXFP4; }
 
 msa_status_t check_params(const msa_params_t* p) {
   if (p == nullptr) return fail(MSA_ERR_INVALID_ARG, "params is NULL");
@@ -97,13 +99,14 @@ msa_status_t check_params(const msa_params_t* p) {
   const bool qkv_ok = (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_BF16) ||
                       (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_FP8_E4M3) ||
                       (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_FP8_E5M2) ||
+                      (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_MXFP4) ||
                       (p->q_dtype == MSA_F32 && p->kv_dtype == MSA_F32);
   if (!qkv_ok)
     return fail(MSA_ERR_UNSUPPORTED, "(q_dtype=%d, kv_dtype=%d) not supported", p->q_dtype,
                 p->kv_dtype);
   if (p->idx_dtype != MSA_BF16 && p->idx_dtype != MSA_F32)
     return fail(MSA_ERR_UNSUPPORTED, "idx_dtype=%d not supported", p->idx_dtype);
-  if (is_fp8(p->kv_dtype) &&
+  if (scaled_kv(p->kv_dtype) &&
       (!std::isfinite(p->k_scale) || !std::isfinite(p->v_scale) || p->k_scale <= 0.f ||
        p->v_scale <= 0.f))
     return fail(MSA_ERR_INVALID_ARG, "fp8 k_scale/v_scale must be finite and > 0");
@@ -189,7 +192,7 @@ bool short_chunks(int32_t B, int32_t T) { return int64_t(T) <= int64_t(kShortChu
 
 bool prefill_key_major(const msa_params_t& p, int32_t B, int32_t T) {
   return !short_chunks(B, T) && p.q_dtype == MSA_BF16 &&
-         (p.kv_dtype == MSA_BF16 || is_fp8(p.kv_dtype));
+         (p.kv_dtype == MSA_BF16 || scaled_kv(p.kv_dtype));
 }
 
 // Index scan of the short-chunk path (all queries of a sequence per pass).
@@ -394,9 +397,9 @@ msa::AttendArgs attend_args(const msa_params_t& p, const void* q, const void* k_
   a.hidx = p.num_idx_heads;
   a.bps = l.bps;
   a.nsplit_max = l.nsplit_max;
-  const float ks = is_fp8(p.kv_dtype) ? p.k_scale : 1.f;
+  const float ks = scaled_kv(p.kv_dtype) ? p.k_scale : 1.f;
   a.qk_scale_log2 = softmax_scale_of(p) * ks * 1.4426950408889634f;
-  a.v_scale = is_fp8(p.kv_dtype) ? p.v_scale : 1.f;
+  a.v_scale = scaled_kv(p.kv_dtype) ? p.v_scale : 1.f;
   a.out = out;
   a.lse_out = lse_out;
   a.part_o = reinterpret_cast<float*>(w + l.part_o);
@@ -758,8 +761,8 @@ msa_status_t msa_append_kv(const msa_params_t* params, const void* k_new, const 
   a.hidx = params->num_idx_heads;
   a.head_dim = params->head_dim;
   a.idx_dim = params->idx_dim;
-  a.k_scale = is_fp8(params->kv_dtype) ? params->k_scale : 1.f;
-  a.v_scale = is_fp8(params->kv_dtype) ? params->v_scale : 1.f;
+  a.k_scale = scaled_kv(params->kv_dtype) ? params->k_scale : 1.f;
+  a.v_scale = scaled_kv(params->kv_dtype) ? params->v_scale : 1.f;
   st = hip_status(msa::launch_append(a, params->kv_dtype, params->idx_dtype,
                                      static_cast<hipStream_t>(stream)),
                   "append launch");
@@ -928,9 +931,9 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
     ka.items = reinterpret_cast<msa::Tile*>(w + l.items);
     ka.n_items = reinterpret_cast<int32_t*>(w + l.n_items);
     ka.max_items = l.max_items;
-    const float ks = is_fp8(p.kv_dtype) ? p.k_scale : 1.f;
+    const float ks = scaled_kv(p.kv_dtype) ? p.k_scale : 1.f;
     ka.qk_scale_log2 = softmax_scale_of(p) * ks * 1.4426950408889634f;
-    ka.v_scale = is_fp8(p.kv_dtype) ? p.v_scale : 1.f;
+    ka.v_scale = scaled_kv(p.kv_dtype) ? p.v_scale : 1.f;
     ka.part_o = reinterpret_cast<uint16_t*>(w + l.part_o);
     ka.part_lse = reinterpret_cast<float*>(w + l.part_lse);
     ka.sink_o = reinterpret_cast<uint16_t*>(w + l.sink);
@@ -962,9 +965,9 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
   aa.hidx = p.num_idx_heads;
   aa.bps = l.bps;
   aa.nsplit_max = l.nsplit_max;
-  const float ks = is_fp8(p.kv_dtype) ? p.k_scale : 1.f;
+  const float ks = scaled_kv(p.kv_dtype) ? p.k_scale : 1.f;
   aa.qk_scale_log2 = softmax_scale_of(p) * ks * 1.4426950408889634f;
-  aa.v_scale = is_fp8(p.kv_dtype) ? p.v_scale : 1.f;
+  aa.v_scale = scaled_kv(p.kv_dtype) ? p.v_scale : 1.f;
   aa.out = out;
   aa.lse_out = lse_out;
   aa.part_o = reinterpret_cast<float*>(w + l.part_o);
@@ -980,12 +983,14 @@ msa_status_t msa_fp8_dequant(const uint8_t* in, float* out, int64_t n, float sca
   if (n < 0) return fail(MSA_ERR_INVALID_ARG, "n=%lld < 0", (long long)n);
   if (n > 0 && (!in || !out)) return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!std::isfinite(scale)) return fail(MSA_ERR_INVALID_ARG, "scale must be finite");
-  if (!is_fp8(dtype)) return fail(MSA_ERR_UNSUPPORTED, "dtype=%d is not an fp8 format", dtype);
+  if (!scaled_kv(dtype))
+    return fail(MSA_ERR_UNSUPPORTED, "dtype=%d is not an fp8 or MX-fp4 format", dtype);
+  if (dtype == MSA_MXFP4 && n % 32 != 0)
+    return fail(MSA_ERR_INVALID_ARG, "MX-fp4: n=%lld is not a multiple of 32", (long long)n);
   msa_status_t st = check_grid((n / 8 + 1 + 255) / 256, 256, "fp8 dequant");
   if (st != MSA_OK) return st;
   st = hip_status(
-      msa::launch_fp8_dequant(in, out, n, scale, dtype == MSA_FP8_E5M2,
-                              static_cast<hipStream_t>(stream)),
+      msa::launch_fp8_dequant(in, out, n, scale, dtype, static_cast<hipStream_t>(stream)),
       "fp8 dequant launch");
   return st == MSA_OK ? ok() : st;
 }

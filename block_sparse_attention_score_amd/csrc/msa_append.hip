@@ -93,11 +93,59 @@ __device__ __forceinline__ uint2 quant8(const BF8*, const float (&x)[8], float s
   return uint2{static_cast<uint32_t>(w0), static_cast<uint32_t>(w1)};
 }
 
+// E2M1 code of y (already divided by its group's power-of-two scale): the
+// nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 (clamped at 6), an exact tie going to
+// the even code; the sign is kept.  The count of midpoints below |y| is the
+// magnitude code, each midpoint compared so that a tie lands on the even
+// neighbour.
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float m = fabsf(y);
+  const uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) +
+                     (m >= 3.5f) + (m > 5.0f);
+  return c | (__float_as_uint(y) >> 31 << 3);
+}
+
+// One 32-element group of an MX-fp4 row: y = x / tensor scale (float32
+// division); the group's E8M0 scale is 2^(floor(log2 max|y|) - 2) (2 being
+// E2M1's largest exponent), clamped to the code range (an all-zero group
+// takes code 0); each element stores the E2M1 code of y / 2^(scale - 127);
+// a group holding a NaN stores the NaN scale code and zero codes.
+template <class KS>
+__device__ void quant_group_fp4(const void* src, int64_t si, float tscale, uint8_t* codes16,
+                                uint8_t* scale_byte) {
+  float y[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float x[8];
+    load8_plain(static_cast<const KS*>(nullptr), src, si + 8 * q, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[8 * q + e] = x[e] / tscale;
+  }
+  float amax = 0.f;
+  bool nan = false;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    nan |= y[e] != y[e];
+    amax = fmaxf(amax, fabsf(y[e]));
+  }
+  const int k = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 3 : -127;
+  const int sc = min(max(k + 127, 0), 254);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (!nan) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) w[e / 8] |= e2m1_code(ldexpf(y[e], 127 - sc)) << (4 * (e % 8));
+  }
+  *reinterpret_cast<uint4*>(codes16) = uint4{w[0], w[1], w[2], w[3]};
+  *scale_byte = static_cast<uint8_t>(nan ? 255 : sc);
+}
+
 // KS: storage of the new K/V rows; KP: of the K/V pools; IT: of the index
-// keys (new rows and pool alike).
+// keys (new rows and pool alike).  A K/V piece is 8 elements, or, for MX-fp4
+// pools, one 32-element scale group.
 template <class KS, class KP, class IT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  const int vd = a.head_dim / 8;   // 8-element vectors per K/V row
+  constexpr int kPiece = __is_same(KP, FP4) ? 32 : 8;
+  const int vd = a.head_dim / kPiece;   // pieces per K/V row
   const int vi = a.idx_dim / 8;    // per index row
   const int n_kv = a.hkv * vd;
   const int n_iv = a.idx_v_pool != nullptr ? a.hidx * vi : 0;  // index-value pieces
@@ -119,7 +167,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     void* pool = is_v ? a.v_pool : a.k_pool;
     const int64_t si = (static_cast<int64_t>(t) * a.hkv + h) * a.head_dim + c * 8;
     const int64_t di = ((page * a.hkv + h) * kBlock + off) * a.head_dim + c * 8;
-    if constexpr (__is_same(KP, FP8) || __is_same(KP, BF8)) {
+    if constexpr (__is_same(KP, FP4)) {
+      uint8_t* run = reinterpret_cast<uint8_t*>(pool) + (page * a.hkv + h) * kFp4Run;
+      quant_group_fp4<KS>(src, (static_cast<int64_t>(t) * a.hkv + h) * a.head_dim + c * 32,
+                          is_v ? a.v_scale : a.k_scale, run + off * 64 + c * 16,
+                          run + kFp4Codes + off * 4 + c);
+    } else if constexpr (__is_same(KP, FP8) || __is_same(KP, BF8)) {
       float x[8];
       load8_plain(static_cast<const KS*>(nullptr), src, si, x);
       *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(pool) + di) =
@@ -149,7 +202,7 @@ static void launch_append_i(const AppendArgs& a, int idx_dtype, dim3 grid, hipSt
 
 hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  const int64_t per_token = 2 * a.hkv * (a.head_dim / 8) +
+  const int64_t per_token = 2 * a.hkv * (a.head_dim / (kv_dtype == 4 ? 32 : 8)) +
                             (a.idx_v_pool != nullptr ? 2 : 1) * a.hidx * (a.idx_dim / 8);
   const int64_t blocks = (static_cast<int64_t>(a.num_tokens) * per_token + 255) / 256;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -157,6 +210,7 @@ hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipSt
   if (kv_dtype == 0) launch_append_i<BF16, BF16>(a, idx_dtype, grid, s);
   else if (kv_dtype == 2) launch_append_i<BF16, FP8>(a, idx_dtype, grid, s);
   else if (kv_dtype == 3) launch_append_i<BF16, BF8>(a, idx_dtype, grid, s);
+  else if (kv_dtype == 4) launch_append_i<BF16, FP4>(a, idx_dtype, grid, s);
   else launch_append_i<F32, F32>(a, idx_dtype, grid, s);
   return hipGetLastError();
 }

@@ -115,6 +115,13 @@ template <>
 struct Row<F32> {
   f32x4v_t c[8];
 };
+// MX-fp4: the four 8-code words of dims 32c + 8q .. +8 and the row's four
+// scale bytes (byte c scales dims 32c .. 32c + 31).
+template <>
+struct Row<FP4> {
+  uint32_t c[4];
+  uint32_t sc;
+};
 
 __device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, Row<BF16>& r) {
 #pragma unroll
@@ -130,6 +137,20 @@ __device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, 
 #pragma unroll
   for (int c = 0; c < 4; ++c)
     r.c[c] = load_raw(static_cast<const BF8*>(nullptr), pool, row0 + 32 * c + 8 * q);
+}
+// row0 is the element offset (page * Hkv + g) * 128 * 128 + token * 128 that
+// the other formats use; an MX-fp4 (page, head) run is kFp4Run bytes.
+__device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, Row<FP4>& r) {
+  const uint8_t* run = reinterpret_cast<const uint8_t*>(pool) + (row0 >> 14) * kFp4Run;
+  const int tok = static_cast<int>(row0 >> 7) & 127;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    r.c[c] = __builtin_nontemporal_load(
+        reinterpret_cast<const uint32_t*>(run + tok * 64 + 16 * c + 4 * q));
+  r.sc = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(run + kFp4Codes + tok * 4));
+}
+__device__ __forceinline__ bf16x8_t fp4_chunk(const Row<FP4>& r, int c) {
+  return fp4x8_to_bf16x8(r.c[c], e8m0_to_f32((r.sc >> (8 * c)) & 0xffu));
 }
 __device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, Row<F32>& r) {
 #pragma unroll
@@ -178,6 +199,13 @@ __device__ __forceinline__ f32x4_t st_tile(const QFrag<BF16>& qf, const Row<K8>&
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8_to_bf16x8(k.c[c]), qf.a[c], acc, 0, 0, 0);
   return acc;
 }
+__device__ __forceinline__ f32x4_t st_tile(const QFrag<BF16>& qf, const Row<FP4>& k) {
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4_chunk(k, c), qf.a[c], acc, 0, 0, 0);
+  return acc;
+}
 __device__ __forceinline__ f32x4_t st_tile(const QFrag<F32>& qf, const Row<F32>& k) {
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -201,6 +229,10 @@ __device__ __forceinline__ f32x4_t vt_tile(const Row<BF16>& v, int m, const bf16
 template <class K8>
 __device__ __forceinline__ f32x4_t vt_tile(const Row<K8>& v, int m, const bf16x8_t (&sel)[2]) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8_to_bf16x8(v.c[m >> 1]), sel[m & 1],
+                                                 f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t vt_tile(const Row<FP4>& v, int m, const bf16x8_t (&sel)[2]) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4_chunk(v, m >> 1), sel[m & 1],
                                                  f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 }
 // f32: four 16x16x4 steps; step e contracts dim 16m + 4q + e against the

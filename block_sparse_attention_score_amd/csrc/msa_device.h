@@ -20,6 +20,12 @@ struct BF16 {};
 struct F32 {};
 struct FP8 {};   // OCP fp8 E4M3 ("e4m3fn") codes
 struct BF8 {};   // OCP fp8 E5M2 codes
+struct FP4 {};   // OCP MX-fp4: E2M1 codes with an E8M0 scale per 32 elements
+
+// MX-fp4 pools hold, per (page, head), the 128 x 128 / 2 code bytes (element
+// 2i of a row in the low nibble of byte i) and then the 128 x 4 scale bytes.
+constexpr int kFp4Codes = 128 * 128 / 2;
+constexpr int kFp4Run = kFp4Codes + 128 * 4;
 
 // ---------------------------------------------------------------- loads
 
@@ -184,6 +190,26 @@ __device__ __forceinline__ bf16x8_t bf8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, 1.0f, true);
   const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, 1.0f, false);
   const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// E8M0 scale code -> float: 2^(code - 127) (code 0 is the float32 subnormal
+// 2^-127), 0xFF -> NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
+  return code == 255u ? __uint_as_float(0x7fc00000u)
+                      : (code == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(code << 23));
+}
+
+// Eight E2M1 codes (one little-endian word, element 2i in the low nibble of
+// byte i) times a scale, to bf16: the gfx950 scaled conversion, two codes per
+// instruction (exact while the products are bf16 values: every E2M1 value
+// times a power of two in bf16's range is one).
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t w, float scale) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
   return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 

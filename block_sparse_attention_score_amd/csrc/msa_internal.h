@@ -220,7 +220,7 @@ hipError_t launch_prefill_attend(const PrefillAttnArgs& a, int kv_dtype, int gro
                                  hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipStream_t s);
 hipError_t launch_prefill_value(const PrefillValueArgs& a, int idx_dim, hipStream_t s);
-hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale, bool e5m2,
+hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale, int dtype,
                               hipStream_t s);
 
 }  // namespace msa

@@ -96,6 +96,10 @@ template <>
 struct RawOf<BF8> {
   typedef uint8_t elem;
 };
+template <>
+struct RawOf<FP4> {
+  typedef uint8_t elem;  // (unused: MX-fp4 runs are addressed in bytes below)
+};
 // Eight elements at byte offset voff + soff of a run, as bf16.
 __device__ __forceinline__ bf16x8_t load8_buf(const BF16*, __amdgpu_buffer_rsrc_t r, uint32_t voff,
                                               uint32_t soff) {
@@ -338,12 +342,36 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
   const uint32_t v_lane = static_cast<uint32_t>(4 * kr * 128 + dc) * kEb;
   auto load_block = [&](const Tile& m) {
     const int64_t h0 = m.head0 + kv_off;
-    const auto kr_src = run_rsrc(a.k_pool, h0 * kEb);
-    const auto vr_src = run_rsrc(a.v_pool, h0 * kEb);
+    if constexpr (__is_same(KT, FP4)) {
+      // an MX-fp4 run per (page, head): per key row 64 code bytes, and its
+      // four scale bytes after all codes; 8 dims = 4 code bytes + 1 scale
+      const int64_t rb = (h0 >> 14) * kFp4Run;
+      const auto ks = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(reinterpret_cast<const char*>(a.k_pool)) + rb, 0, kFp4Run, 0x00020000);
+      const auto vs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(reinterpret_cast<const char*>(a.v_pool)) + rb, 0, kFp4Run, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kraw[i] = load8_buf(ktag, kr_src, k_lane, 32 * i * 128 * kEb);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(ks, kr * 64 + dc / 2, 32 * i * 64, 0);
+        const uint32_t e = __builtin_amdgcn_raw_buffer_load_b8(ks, kFp4Codes + kr * 4 + dc / 32,
+                                                               32 * i * 4, 0);
+        kraw[i] = fp4x8_to_bf16x8(w, e8m0_to_f32(e));
+      }
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) vraw[kk] = load8_buf(ktag, vr_src, v_lane, kk * 128 * kEb);
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(vs, 4 * kr * 64 + dc / 2, kk * 64, 0);
+        const uint32_t e = __builtin_amdgcn_raw_buffer_load_b8(vs, kFp4Codes + 4 * kr * 4 + dc / 32,
+                                                               kk * 4, 0);
+        vraw[kk] = fp4x8_to_bf16x8(w, e8m0_to_f32(e));
+      }
+    } else {
+      const auto kr_src = run_rsrc(a.k_pool, h0 * kEb);
+      const auto vr_src = run_rsrc(a.v_pool, h0 * kEb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kraw[i] = load8_buf(ktag, kr_src, k_lane, 32 * i * 128 * kEb);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) vraw[kk] = load8_buf(ktag, vr_src, v_lane, kk * 128 * kEb);
+    }
   };
   // V rows at or past the sequence end (stale bytes, possibly NaN) are
   // cleared: their probabilities are 0, but 0 * NaN would reach the MFMA
@@ -705,6 +733,7 @@ hipError_t launch_prefill_attend(const PrefillAttnArgs& a, int kv_dtype, int gro
     if (kv_dtype == 0) ok = launch_pf_attend_g<BF16>(a, group, s);
     else if (kv_dtype == 2) ok = launch_pf_attend_g<FP8>(a, group, s);
     else if (kv_dtype == 3) ok = launch_pf_attend_g<BF8>(a, group, s);
+    else if (kv_dtype == 4) ok = launch_pf_attend_g<FP4>(a, group, s);
     if (!ok) return hipErrorInvalidValue;
   }
   // 16 / G (token, kv head) units per combine workgroup

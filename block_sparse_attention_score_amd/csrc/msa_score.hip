@@ -140,13 +140,24 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale, bool e5m2,
+// MX-fp4: n / 2 code bytes, then n / 32 scale bytes; 8 elements per thread.
+__global__ void fp4_dequant_kernel(const uint8_t* in, float* out, int64_t n, float scale) {
+  const int64_t i = (blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x) * 8;
+  if (i >= n) return;
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(in + i / 2);
+  const bf16x8_t v = fp4x8_to_bf16x8(w, e8m0_to_f32(in[n / 2 + i / 32]));
+  for (int k = 0; k < 8; ++k) out[i + k] = static_cast<float>(v[k]) * scale;
+}
+
+hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale, int dtype,
                               hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t threads = (n + 7) / 8;
   const int64_t blocks = (threads + 255) / 256;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  if (e5m2)
+  if (dtype == 4)
+    fp4_dequant_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(in, out, n, scale);
+  else if (dtype == 3)
     fp8_dequant_kernel<BF8><<<static_cast<unsigned>(blocks), 256, 0, s>>>(in, out, n, scale);
   else
     fp8_dequant_kernel<FP8><<<static_cast<unsigned>(blocks), 256, 0, s>>>(in, out, n, scale);

@@ -90,9 +90,17 @@ typedef enum {
   MSA_BF16 = 0,
   MSA_F32 = 1,
   MSA_FP8_E4M3 = 2, /* OCP e4m3 ("e4m3fn"): bias 7, no inf, S.1111.111 = NaN */
-  MSA_FP8_E5M2 = 3  /* OCP e5m2: bias 15, S.11111.00 = inf, other S.11111.xx NaN
+  MSA_FP8_E5M2 = 3, /* OCP e5m2: bias 15, S.11111.00 = inf, other S.11111.xx NaN
                        (the sglang page keeps fp8 main caches of either format
                        on its sparse path that dequantises on load) */
+  MSA_MXFP4 = 4     /* OCP MX-fp4 K/V pools: E2M1 codes (s.ee.m, bias 1: 0, 0.5,
+                       1, 1.5, 2, 3, 4, 6) with an E8M0 scale 2^(e - 127) (0xFF
+                       NaN) per 32 elements; per (page, head) the 128 x 64 code
+                       bytes (element 2i of a row in the low nibble of byte i)
+                       then the 128 x 4 scale bytes: pools [P, Hkv, 8704] bytes
+                       at head_dim 128.  The gfx950 counterpart of the vLLM
+                       page's 4-bit K/V caches with block scales in per-head
+                       slots (MiniMaxM3SparseMSANvfp4Backend). */
 } msa_dtype_t;
 
 /*
@@ -103,7 +111,7 @@ typedef enum {
  *   idx_dim in {64, 128}, topk in {4, 8, 16, 32}, 0 <= init, local <= 64,
  *   Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8, 16}, Hkv % Hidx == 0,
  *   (q_dtype, kv_dtype) in {(bf16, bf16), (bf16, fp8_e4m3), (bf16, fp8_e5m2),
- *   (f32, f32)},
+ *   (bf16, mxfp4), (f32, f32)},
  *   idx_dtype in {bf16, f32} (idx_q and idx_k share it).
  */
 typedef struct {
@@ -120,8 +128,8 @@ typedef struct {
   int32_t q_dtype;       /* msa_dtype_t */
   int32_t kv_dtype;      /* msa_dtype_t */
   int32_t idx_dtype;     /* msa_dtype_t */
-  float k_scale;         /* fp8 only: k = code value * k_scale            */
-  float v_scale;         /* fp8 only: v = code value * v_scale            */
+  float k_scale;         /* fp8 and MX-fp4 only: k = stored value * k_scale */
+  float v_scale;         /* fp8 and MX-fp4 only: v = stored value * v_scale */
   int32_t forced_in_budget; /* 0: S = F U top-k of the rest (|S| = min(nb,
                             |F| + topk)); 1: the forced blocks count inside
                             the budget, S = F U top-max(topk - |F|, 0) of the
@@ -305,7 +313,12 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q,
  *   k_new, v_new [T, Hkv, D]: bf16 for bf16 and fp8 pools, f32 for f32 pools
  *                (q_dtype); idx_k_new [T, Hidx, Di] in idx_dtype.
  *   fp8 pools store e4m3fn(RNE(clamp(x / k_scale, +-448))) (v_scale for V;
- *   the division in float32); e5m2 pools the same with +-57344.
+ *   the division in float32); e5m2 pools the same with +-57344.  MX-fp4
+ *   pools store y = x / k_scale (float32) per group of 32: the E8M0 scale
+ *   2^(floor(log2 max|y|) - 2) clamped to the code range (an all-zero group
+ *   takes code 0, a group with a NaN the NaN code and zero codes) and each
+ *   element's E2M1 code nearest to y / 2^(code - 127), ties to the even code,
+ *   clamped at 6 (the OCP Microscaling rule).
  *   With params->index_value, idx_v_new [T, Hidx, Di] (idx_dtype) goes to
  *   idx_v_pool beside the index keys (the page stores idx_v unless the layer
  *   disables the value branch); otherwise both must be NULL.
@@ -330,6 +343,9 @@ msa_status_t msa_fp8_e4m3_dequant(const uint8_t* in, float* out, int64_t n,
  * The same for either fp8 format of the K/V pools (dtype MSA_FP8_E4M3 or
  * MSA_FP8_E5M2; e5m2 infinities stay infinite, NaN codes give NaN):
  * out[i] = value(in[i]) * scale, through the loaders' bf16 conversion.
+ * MSA_MXFP4: in holds n / 2 code bytes then n / 32 scale bytes (n a
+ * multiple of 32, the order of one pool run) and out[i] = code value times
+ * its group's scale, through the loaders' conversion, times scale.
  * MSA_ERR_UNSUPPORTED for any other dtype.
  */
 msa_status_t msa_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale,

@@ -88,6 +88,11 @@ WORKLOADS = {
         kind="prefill", B=4, n_new=4096, prefix=16384, Hq=16, Hkv=2, Hidx=2,
         D=128, Di=128, topk=16, init=1, local=2, q="bf16", kv="bf16", idx="bf16",
         idx_value=True),
+    # MX-fp4 K/V pools (4-bit codes with a scale per 32 elements): the fp8
+    # decode workload's shape
+    "decode_mxfp4_b32_l64k": dict(
+        kind="decode", B=32, seq_lens=("fixed", 65536), Hq=16, Hkv=2, Hidx=2,
+        D=128, Di=128, topk=32, init=1, local=2, q="bf16", kv="mxfp4", idx="bf16"),
 }
 
 # Seeds of the workloads, in the order above.
