@@ -297,10 +297,9 @@ def test_index_value_pointers_follow_the_flag():
     assert "index_value" in lib.msa_last_error().decode()
     assert append_call(base_cfg(index_value=True)) == _lib.MSA_ERR_INVALID_ARG
     assert append_call(base_cfg(), idx_v_new=FAKE, idx_v_pool=FAKE) == _lib.MSA_ERR_INVALID_ARG
-    # the decode workspace grows by the scan's value partials
-    a = msa.decode_workspace_size(base_cfg(), 8, 256)
+    # the decode workspace holds the scores and the scan's value partials
     b = msa.decode_workspace_size(base_cfg(index_value=True), 8, 256)
-    assert b >= a + 8 * 2 * 32 * 130 * 4
+    assert b >= 8 * 2 * 256 * 4 + 8 * 2 * 32 * 130 * 4
     bad = base_cfg().params()
     bad.index_value = 2
     assert lib.msa_decode_workspace_size(ctypes.byref(bad), 4, 16) == 0
