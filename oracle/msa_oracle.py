@@ -163,8 +163,34 @@ def num_visible_blocks(p: int) -> int:
 # Step 1: block scores from the index heads
 # --------------------------------------------------------------------------
 
-def block_scores_for_query(iq: np.ndarray, ik_rows: np.ndarray, p: int) -> np.ndarray:
-    """score[j] = max over tokens t of block j with t <= p of iq . ik[t].
+# Block score types.  The sglang page reads a score type from the model
+# config and hands it to the sparse ops without printing its values; "max" is
+# the reading the spec fixes.  Two other reductions over a block's visible
+# tokens are offered beside it (names and definitions of this library):
+#   "mean": the mean of q_idx . k_idx (equivalently q_idx . the mean visible
+#           key of the block);
+#   "lse":  log sum exp(q_idx . k_idx / sqrt(Di)), the block's share of a
+#           softmax over the index logits, in the log domain.
+SCORE_TYPES = ("max", "mean", "lse")
+
+
+def reduce_block(dots: np.ndarray, score_type: str, Di: int) -> float:
+    """One block's score from the dots of its visible tokens (non-empty)."""
+    if score_type == "max":
+        return float(np.max(dots))
+    if score_type == "mean":
+        return float(np.mean(dots))
+    if score_type == "lse":
+        z = dots / math.sqrt(Di)
+        m = float(np.max(z))
+        return m + math.log(float(np.sum(np.exp(z - m))))
+    raise ValueError(score_type)
+
+
+def block_scores_for_query(iq: np.ndarray, ik_rows: np.ndarray, p: int,
+                           score_type: str = "max") -> np.ndarray:
+    """score[j] = the score_type reduction over tokens t of block j with t <= p
+    of iq . ik[t] (max by default).
 
     ``ik_rows`` holds at least the sequence's tokens 0..p (float64).
     """
@@ -172,13 +198,17 @@ def block_scores_for_query(iq: np.ndarray, ik_rows: np.ndarray, p: int) -> np.nd
     if nb == 0:
         return np.zeros(0)
     dots = ik_rows[: p + 1] @ iq                      # [p+1]
+    if score_type != "max":
+        return np.array([reduce_block(dots[j * BLOCK:min((j + 1) * BLOCK, p + 1)], score_type,
+                                      iq.shape[-1]) for j in range(nb)])
     pad = nb * BLOCK - (p + 1)
     dots = np.concatenate([dots, np.full(pad, -np.inf)])
     return dots.reshape(nb, BLOCK).max(axis=1)
 
 
 def block_scores(inp: dict) -> np.ndarray:
-    """Scores [T, Hidx, max_blocks] float64; -inf for blocks past the query.
+    """Scores [T, Hidx, max_blocks] float64 of ``inp["score_type"]`` (max when
+    absent); -inf for blocks past the query.
 
     The queries of one sequence and index head are scored together with one
     matrix product (chunks of 1024 queries); each row is then masked to its
@@ -207,8 +237,25 @@ def block_scores(inp: dict) -> np.ndarray:
                 dots = np.full((len(chunk), nbL * BLOCK), -np.inf)
                 dots[:, :L] = iq_all[ts, h] @ ik.T
                 tok = np.arange(nbL * BLOCK)
-                dots[tok[None, :] > ps[:, None]] = -np.inf
-                s = dots.reshape(len(chunk), nbL, BLOCK).max(axis=2)
+                vis = tok[None, :] <= ps[:, None]
+                dots[~vis] = -np.inf
+                d3 = dots.reshape(len(chunk), nbL, BLOCK)
+                v3 = vis.reshape(len(chunk), nbL, BLOCK)
+                st = inp.get("score_type", "max")
+                if st == "max":
+                    s = d3.max(axis=2)
+                elif st == "mean":
+                    cnt = v3.sum(axis=2)
+                    s = np.where(v3, d3, 0.0).sum(axis=2) / np.maximum(cnt, 1)
+                elif st == "lse":
+                    z = d3 / math.sqrt(iq_all.shape[-1])
+                    m = z.max(axis=2)
+                    msafe = np.where(np.isfinite(m), m, 0.0)
+                    with np.errstate(divide="ignore"):   # blocks past the query: log 0
+                        s = msafe + np.log(np.where(v3, np.exp(z - msafe[..., None]), 0.0)
+                                           .sum(axis=2))
+                else:
+                    raise ValueError(st)
                 for r, (t, p) in enumerate(chunk):
                     nb = num_visible_blocks(p)
                     out[t, h, :nb] = s[r, :nb]

@@ -348,5 +348,6 @@ def host_view(case: Case, pages: Optional[np.ndarray] = None) -> dict:
         k_scale=case.k_scale, v_scale=case.v_scale,
         topk=spec["topk"], init=spec["init"], local=spec["local"],
         forced_in_budget=bool(spec.get("forced_in_budget", False)),
+        score_type=spec.get("score_type", "max"),
         Hq=spec["Hq"], Hkv=spec["Hkv"], Hidx=spec["Hidx"],
     )

@@ -122,11 +122,13 @@ def test_planted_scores_and_selection(case):
 # ---------------------------------------------------- brute force, tiny
 
 def _tiny_case(seed, B=2, lens=(300, 77), Hq=4, Hkv=2, Hidx=1, D=8, Di=8, topk=2,
-               init=1, local=1, kv="bf16", prefill_new=None, idx_value=False):
+               init=1, local=1, kv="bf16", prefill_new=None, idx_value=False,
+               score_type="max"):
     spec = dict(kind="decode", B=B, seq_lens=list(lens), Hq=Hq, Hkv=Hkv, Hidx=Hidx,
                 D=D, Di=Di, topk=topk, init=init, local=local, q="bf16", kv=kv,
                 idx="bf16", k_scale=0.5 if kv == "fp8" else 1.0,
-                v_scale=0.25 if kv == "fp8" else 1.0, idx_value=idx_value)
+                v_scale=0.25 if kv == "fp8" else 1.0, idx_value=idx_value,
+                score_type=score_type)
     if prefill_new is not None:
         spec.update(kind="prefill", n_new=list(prefill_new),
                     prefix=[L - n for L, n in zip(lens, prefill_new)])
@@ -974,3 +976,59 @@ def test_mxfp4_append_oracle():
         changed[page, :, off * D // 2:(off + 1) * D // 2] = True
         changed[page, :, 128 * D // 2 + off * 2:128 * D // 2 + off * 2 + 2] = True
     assert np.array_equal(k2[~changed], k_pool[~changed])
+
+
+# -------------------------------------------------------------- score types
+
+def _py_block_reduce(ds, score_type, Di):
+    """A block's score from its visible dots, written out with the math module."""
+    if score_type == "max":
+        return max(ds)
+    if score_type == "mean":
+        return math.fsum(ds) / len(ds)
+    zs = [d / math.sqrt(Di) for d in ds]
+    m = max(zs)
+    return m + math.log(math.fsum(math.exp(z - m) for z in zs))
+
+
+@pytest.mark.parametrize("score_type", ["mean", "lse"])
+@pytest.mark.parametrize("prefill", [None, (40, 100)])
+def test_score_types_brute_force(score_type, prefill):
+    """Mean and log-sum-exp block scores by explicit loops at the positions of
+    the case description, decode and prefill, against the oracle's batched
+    form and its per-query form."""
+    inp = _tiny_case(71, lens=(700, 260), Hidx=2, Hkv=2, prefill_new=prefill,
+                     score_type=score_type)
+    sc = oracle.block_scores(inp)
+    ikc = _RowCache(inp["idx_k_pool"], "bf16")
+    for t, (b, p) in enumerate(inp["_pos"]):
+        for h in range(2):
+            iq = [_py_value(x, "bf16") for x in inp["idx_q"][t, h]]
+            nb = p // 128 + 1
+            for j in range(nb):
+                page = int(inp["block_table"][b, j])
+                ds = [sum(a * c for a, c in zip(iq, ikc(page, h, s_)))
+                      for s_ in range(min(128, p + 1 - 128 * j))]
+                want = _py_block_reduce(ds, score_type, 8)
+                assert abs(sc[t, h, j] - want) <= 1e-12 * max(1.0, abs(want)), (t, h, j)
+            assert np.all(np.isneginf(sc[t, h, nb:]))
+            ik = oracle.decode(inp["idx_k_pool"][inp["block_table"][b, :nb], h].reshape(-1, 8),
+                               "bf16")
+            one = oracle.block_scores_for_query(oracle.decode(inp["idx_q"][t, h], "bf16"), ik, p,
+                                                score_type)
+            assert np.allclose(sc[t, h, :nb], one, rtol=1e-12, atol=1e-12)
+
+
+def test_score_types_closed_forms():
+    """Blocks whose visible index keys are all equal: mean = max = the common
+    dot, and lse = dot / sqrt(Di) + log(number of visible tokens); the
+    partial last block counts only its visible tokens."""
+    inp = _tiny_case(72, lens=(300,), B=1, Hidx=1, Hkv=1, Hq=2)
+    one = _bf16_bits([0.5])[0]
+    inp["idx_k_pool"] = np.full_like(inp["idx_k_pool"], one)
+    inp["idx_q"] = np.full_like(inp["idx_q"], one)
+    d = 8 * 0.25                                          # Di = 8 products of 0.5 * 0.5
+    for st, want in (("max", [d, d, d]), ("mean", [d, d, d]),
+                     ("lse", [d / math.sqrt(8) + math.log(n) for n in (128, 128, 44)])):
+        sc = oracle.block_scores(dict(inp, score_type=st))
+        assert np.allclose(sc[0, 0, :3], want, rtol=1e-14, atol=1e-14), st
