@@ -41,6 +41,7 @@ class Params(ctypes.Structure):
         ("v_scale", ctypes.c_float),
         ("forced_in_budget", ctypes.c_int32),
         ("index_value", ctypes.c_int32),
+        ("score_type", ctypes.c_int32),
     ]
 
 

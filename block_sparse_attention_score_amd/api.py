@@ -21,6 +21,10 @@ from ._lib import MSA_BF16, MSA_F32, MSA_FP8_E4M3, MSA_FP8_E5M2, MSA_MXFP4, Para
 BLOCK = 128
 
 
+# block score types by name, as msa_params_t.score_type codes them
+SCORE_TYPES = {"max": 0, "mean": 1, "lse": 2}
+
+
 @dataclass
 class MsaConfig:
     """Model parameters (see msa_params_t in include/msa.h)."""
@@ -42,6 +46,7 @@ class MsaConfig:
     block_size: int = BLOCK
     forced_in_budget: bool = False  # forced blocks count inside topk
     index_value: bool = False       # the index-value branch (idx_v pool, idx_out)
+    score_type: str = "max"         # block score: "max", "mean" or "lse"
 
     @property
     def kmax(self) -> int:
@@ -54,7 +59,8 @@ class MsaConfig:
                       self.idx_dim, self.block_size, self.topk, self.init_blocks,
                       self.local_blocks, self.softmax_scale, code[self.q_dtype],
                       code[self.kv_dtype], code[self.idx_dtype], self.k_scale, self.v_scale,
-                      int(self.forced_in_budget), int(self.index_value))
+                      int(self.forced_in_budget), int(self.index_value),
+                      SCORE_TYPES[self.score_type])
 
     @staticmethod
     def from_spec(spec: dict) -> "MsaConfig":
@@ -66,7 +72,8 @@ class MsaConfig:
                          k_scale=float(spec.get("k_scale", 1.0)),
                          v_scale=float(spec.get("v_scale", 1.0)),
                          forced_in_budget=bool(spec.get("forced_in_budget", False)),
-                         index_value=bool(spec.get("idx_value", False)))
+                         index_value=bool(spec.get("idx_value", False)),
+                         score_type=spec.get("score_type", "max"))
 
 
 def blocks_from_tokens(init_tokens: int, local_tokens: int, block_size: int = BLOCK):

@@ -92,6 +92,8 @@ msa_status_t check_params(const msa_params_t* p) {
     return fail(MSA_ERR_INVALID_ARG, "forced_in_budget=%d (0 or 1)", p->forced_in_budget);
   if (p->index_value != 0 && p->index_value != 1)
     return fail(MSA_ERR_INVALID_ARG, "index_value=%d (0 or 1)", p->index_value);
+  if (p->score_type < 0 || p->score_type > 2)
+    return fail(MSA_ERR_INVALID_ARG, "score_type=%d (0 max, 1 mean, 2 lse)", p->score_type);
   if (p->init_blocks > 64 || p->local_blocks > 64)
     return fail(MSA_ERR_UNSUPPORTED, "init/local block counts above 64");
   if (!std::isfinite(p->softmax_scale) || p->softmax_scale < 0.f)
@@ -195,6 +197,11 @@ bool prefill_key_major(const msa_params_t& p, int32_t B, int32_t T) {
          (p.kv_dtype == MSA_BF16 || scaled_kv(p.kv_dtype));
 }
 
+// log2(e) / sqrt(Di): the log-sum-exp block score accumulates in base 2.
+float score_scale_log2(const msa_params_t& p) {
+  return 1.4426950408889634f / std::sqrt(float(p.idx_dim));
+}
+
 // Index scan of the short-chunk path (all queries of a sequence per pass).
 msa::ScoreArgs multi_score_args(const msa_params_t& p, const void* idx_q, const void* idx_k_pool,
                                 int64_t num_pages, const int32_t* block_table,
@@ -214,6 +221,7 @@ msa::ScoreArgs multi_score_args(const msa_params_t& p, const void* idx_q, const 
   a.chunks_per_pair = (max_blocks + kPagesPerItem - 1) / kPagesPerItem;
   a.scores = scores;
   a.fill_tail = 0;
+  a.st_scale_log2 = score_scale_log2(p);
   return a;
 }
 
@@ -292,6 +300,7 @@ msa::PrefillScoreArgs prefill_score_args(const msa_params_t& p, const void* idx_
   a.blocks_per_chunk = kPrefillBlocksPerChunk;
   a.kchunks = (max_blocks + kPrefillBlocksPerChunk - 1) / kPrefillBlocksPerChunk;
   a.scores = scores;
+  a.st_scale_log2 = score_scale_log2(p);
   return a;
 }
 
@@ -499,12 +508,14 @@ msa_status_t sparse_decode_impl(const msa_params_t* params, const void* q, const
   a.fill_tail = 0;
   a.zero_words = reinterpret_cast<uint32_t*>(w + l.tickets);
   a.zero_count = num_seqs * p.num_kv_heads;
+  a.st_scale_log2 = score_scale_log2(p);
   if (p.index_value) {
     a.idx_v = idx_v_pool;
     a.iv_part = reinterpret_cast<float*>(w + l.iv_part);
     a.iv_scale_log2 = 1.4426950408889634f / std::sqrt(float(p.idx_dim));
   }
-  st = hip_status(msa::launch_decode_score(a, p.idx_dtype, p.idx_dim, s), "score launch");
+  st = hip_status(msa::launch_decode_score(a, p.idx_dtype, p.idx_dim, p.score_type, s),
+                  "score launch");
   if (st != MSA_OK) return st;
   // 2. selection inside each attention workgroup, split-K attention, combine
   msa::AttendArgs aa = attend_args(p, q, k_pool, v_pool, num_pages, block_table, max_blocks,
@@ -605,13 +616,15 @@ msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
       const msa::ScoreArgs ma =
           multi_score_args(*params, idx_q, idx_k_pool, num_pages, block_table, max_blocks,
                            seq_lens, cu_seqlens_q, num_seqs, scores);
-      st = hip_status(msa::launch_multi_score(ma, params->idx_dim, s), "chunk scan launch");
+      st = hip_status(msa::launch_multi_score(ma, params->idx_dim, params->score_type, s),
+                      "chunk scan launch");
       return st == MSA_OK ? ok() : st;
     }
     const msa::PrefillScoreArgs pa =
         prefill_score_args(*params, idx_q, idx_k_pool, num_pages, block_table, max_blocks,
                            seq_lens, cu_seqlens_q, num_seqs, num_q_tokens, scores);
-    st = hip_status(msa::launch_prefill_score(pa, params->idx_dim, s), "prefill score launch");
+    st = hip_status(msa::launch_prefill_score(pa, params->idx_dim, params->score_type, s),
+                    "prefill score launch");
     return st == MSA_OK ? ok() : st;
   }
   if ((st = check_grid(scan_workgroups(num_seqs, params->num_idx_heads, max_blocks),
@@ -630,8 +643,9 @@ msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
   a.chunks_per_pair = (max_blocks + kPagesPerItem - 1) / kPagesPerItem;
   a.scores = scores;
   a.fill_tail = 1;
+  a.st_scale_log2 = score_scale_log2(*params);
   st = hip_status(msa::launch_decode_score(a, params->idx_dtype, params->idx_dim,
-                                           static_cast<hipStream_t>(stream)),
+                                           params->score_type, static_cast<hipStream_t>(stream)),
                   "block score launch");
   return st == MSA_OK ? ok() : st;
 }
@@ -891,12 +905,13 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
     const msa::ScoreArgs ma = multi_score_args(p, idx_q, idx_k_pool, num_pages, block_table,
                                                max_blocks, seq_lens, cu_seqlens_q, num_seqs,
                                                scores);
-    st = hip_status(msa::launch_multi_score(ma, p.idx_dim, s), "chunk scan launch");
+    st = hip_status(msa::launch_multi_score(ma, p.idx_dim, p.score_type, s), "chunk scan launch");
   } else {
     const msa::PrefillScoreArgs pa =
         prefill_score_args(p, idx_q, idx_k_pool, num_pages, block_table, max_blocks, seq_lens,
                            cu_seqlens_q, num_seqs, num_q_tokens, scores);
-    st = hip_status(msa::launch_prefill_score(pa, p.idx_dim, s), "prefill score launch");
+    st = hip_status(msa::launch_prefill_score(pa, p.idx_dim, p.score_type, s),
+                    "prefill score launch");
   }
   if (st != MSA_OK) return st;
   // 2. per-token selection

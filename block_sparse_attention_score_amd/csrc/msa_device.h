@@ -274,6 +274,96 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Sum over the whole wavefront, result in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// ------------------------------------------------------- block scores
+//
+// A block's score from the index dots of its visible tokens, by score type:
+// 0 max (the reading the spec fixes), 1 the mean, 2 the log-sum-exp of the
+// dots times 1/sqrt(Di) (kept in base 2 while accumulating: c = log2(e) /
+// sqrt(Di) scales the dots, the result is converted back).  A wave feeds each
+// token's dot from every lane of its row; for the mean and the log-sum-exp
+// only the row's owner lane counts it.
+constexpr int kScoreMax = 0;
+constexpr int kScoreMean = 1;
+constexpr int kScoreLse = 2;
+constexpr float kLn2d = 0.69314718055994531f;
+
+template <int ST>
+struct BlockScore;
+template <>
+struct BlockScore<kScoreMax> {
+  float m = -INFINITY;
+  template <int N>
+  __device__ __forceinline__ void add(const float (&d)[N], const bool (&ok)[N], bool, float) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) m = fmaxf(m, ok[i] ? d[i] : -INFINITY);
+  }
+  __device__ __forceinline__ float finish(int) { return wave_max(m); }
+};
+template <>
+struct BlockScore<kScoreMean> {
+  float s = 0.f;
+  template <int N>
+  __device__ __forceinline__ void add(const float (&d)[N], const bool (&ok)[N], bool owner, float) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) s += (ok[i] && owner) ? d[i] : 0.f;
+  }
+  // nvalid: visible tokens of the block (none: the block is not visible)
+  __device__ __forceinline__ float finish(int nvalid) {
+    const float t = wave_sum(s);
+    return nvalid > 0 ? t / static_cast<float>(nvalid) : -INFINITY;
+  }
+  // the same over the four lanes 16 apart that share a column of an MFMA
+  // result tile (every lane counts its own tokens)
+  __device__ __forceinline__ float finish_q4(int nvalid) {
+    float t = s + __shfl_xor(s, 16);
+    t += __shfl_xor(t, 32);
+    return nvalid > 0 ? t / static_cast<float>(nvalid) : -INFINITY;
+  }
+};
+template <>
+struct BlockScore<kScoreLse> {
+  float m = -INFINITY, e = 0.f;
+  template <int N>
+  __device__ __forceinline__ void add(const float (&d)[N], const bool (&ok)[N], bool owner,
+                                      float c) {
+    float z[N];
+    float mb = m;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      z[i] = (ok[i] && owner) ? d[i] * c : -INFINITY;
+      mb = fmaxf(mb, z[i]);
+    }
+    const float mu = mb == -INFINITY ? 0.f : mb;
+    e *= __builtin_amdgcn_exp2f(m - mu);
+#pragma unroll
+    for (int i = 0; i < N; ++i) e += __builtin_amdgcn_exp2f(z[i] - mu);
+    m = mb;
+  }
+  __device__ __forceinline__ float finish(int) {
+    const float M = wave_max(m);
+    const float mu = M == -INFINITY ? 0.f : M;
+    const float E = wave_sum(e * __builtin_amdgcn_exp2f(m - mu));
+    return E > 0.f ? (mu + __builtin_amdgcn_logf(E)) * kLn2d : -INFINITY;
+  }
+  __device__ __forceinline__ float finish_q4(int) {
+    float M = fmaxf(m, __shfl_xor(m, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float mu = M == -INFINITY ? 0.f : M;
+    float E = e * __builtin_amdgcn_exp2f(m - mu);
+    E += __shfl_xor(E, 16);
+    E += __shfl_xor(E, 32);
+    return E > 0.f ? (mu + __builtin_amdgcn_logf(E)) * kLn2d : -INFINITY;
+  }
+};
+
 // --------------------------------------------------------- score keys
 
 // Order-preserving map float -> uint32 (larger float, larger key); -0 and +0

@@ -32,6 +32,7 @@ struct ScoreArgs {
   const void* idx_v;
   float* iv_part;            // [B * Hidx * chunks_per_pair, Di + 2]
   float iv_scale_log2;       // log2(e) / sqrt(Di)
+  float st_scale_log2;       // log-sum-exp block scores: log2(e) / sqrt(Di)
 };
 
 // Prefill index scoring (causal GEMM with a block-max epilogue).
@@ -49,6 +50,7 @@ struct PrefillScoreArgs {
   int32_t blocks_per_chunk;  // key blocks per workgroup
   int32_t kchunks;           // ceil(max_blocks / blocks_per_chunk)
   float* scores;             // [T, Hidx, max_blocks]
+  float st_scale_log2;       // log-sum-exp block scores: log2(e) / sqrt(Di)
 };
 
 // Standalone selection over precomputed score rows.
@@ -205,11 +207,12 @@ struct PrefillAttnArgs {
 };
 
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
-hipError_t launch_decode_score(const ScoreArgs& a, int idx_dtype, int idx_dim,
+hipError_t launch_decode_score(const ScoreArgs& a, int idx_dtype, int idx_dim, int score_type,
                                hipStream_t s);
-hipError_t launch_multi_score(const ScoreArgs& a, int idx_dim, hipStream_t s);
+hipError_t launch_multi_score(const ScoreArgs& a, int idx_dim, int score_type, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
-hipError_t launch_prefill_score(const PrefillScoreArgs& a, int idx_dim, hipStream_t s);
+hipError_t launch_prefill_score(const PrefillScoreArgs& a, int idx_dim, int score_type,
+                                hipStream_t s);
 bool select_wave_fits(int max_blocks);
 hipError_t launch_select_wave(const SelectArgs& a, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);

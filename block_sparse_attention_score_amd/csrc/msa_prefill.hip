@@ -16,7 +16,9 @@
 // v_mfma_f32_16x16x32_bf16, so each result tile is S^T (tokens down, queries
 // across) and a lane folds its four tokens per tile into its query's maximum
 // with no cross-lane step until the block ends.  Blocks that end before a
-// wave's first query skip the causal mask.
+// wave's first query skip the causal mask.  The mean and log-sum-exp block
+// scores use the same tiles: a lane sums (or exp-accumulates) its tokens and
+// the four lanes of a query column combine at the block's end.
 #include "msa_device.h"
 #include "msa_internal.h"
 #include "msa_select.h"
@@ -25,7 +27,7 @@ namespace msa {
 
 constexpr int kPrefillRows = 256;  // query rows per scoring workgroup
 
-template <int DI>
+template <int DI, int ST>
 __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillScoreArgs a) {
   constexpr int KS = DI / 32;              // 32-dim k-steps
   constexpr int ROW_BYTES = DI * 2 + 16;   // padded LDS row
@@ -168,7 +170,33 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
     float mx[4];  // per query column: max over this lane's tokens
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) mx[rt] = -INFINITY;
-    if (page_ok && kBlock * j + kBlock - 1 <= pos_w0) {
+    if constexpr (ST != kScoreMax) {
+      // mean or log-sum-exp: each lane reduces its own tokens of a column,
+      // then the four lanes of the column combine
+      BlockScore<ST> red[4];
+      if (page_ok) {
+        const bool full = kBlock * j + kBlock - 1 <= pos_w0;
+        for (int n = 0; n < 8; ++n) {
+          f32x4_t acc[4];
+          tile(buf, n, acc);
+          const int tok = kBlock * j + 16 * n + 4 * q4;
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            const int pos = pos_w0 + 16 * rt + l16;
+            const float d[4] = {acc[rt][0], acc[rt][1], acc[rt][2], acc[rt][3]};
+            const bool ok[4] = {full || tok <= pos, full || tok + 1 <= pos,
+                                full || tok + 2 <= pos, full || tok + 3 <= pos};
+            red[rt].add(d, ok, true, a.st_scale_log2);
+          }
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int pos = pos_w0 + 16 * rt + l16;
+        const int nvis = page_ok ? min(kBlock, max(0, pos + 1 - kBlock * j)) : 0;
+        mx[rt] = red[rt].finish_q4(nvis);
+      }
+    } else if (page_ok && kBlock * j + kBlock - 1 <= pos_w0) {
 #pragma unroll 2
       for (int n = 0; n < 8; ++n) {
         f32x4_t acc[4];
@@ -192,10 +220,12 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
         }
       }
     }
+    if constexpr (ST == kScoreMax) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      mx[rt] = max_nan(mx[rt], __shfl_xor(mx[rt], 16));
-      mx[rt] = max_nan(mx[rt], __shfl_xor(mx[rt], 32));
+      for (int rt = 0; rt < 4; ++rt) {
+        mx[rt] = max_nan(mx[rt], __shfl_xor(mx[rt], 16));
+        mx[rt] = max_nan(mx[rt], __shfl_xor(mx[rt], 32));
+      }
     }
     // The next block goes to LDS before this block's scores are stored: the
     // staging waits for the block's loads, and loads and stores retire in
@@ -266,13 +296,22 @@ __global__ __launch_bounds__(kWgThreads) void select_wave_kernel(SelectArgs a) {
 
 // ------------------------------------------------------------- launchers
 
-hipError_t launch_prefill_score(const PrefillScoreArgs& a, int idx_dim, hipStream_t s) {
+template <int ST>
+static void launch_prefill_score_st(const PrefillScoreArgs& a, int idx_dim, int grid,
+                                    hipStream_t s) {
+  if (idx_dim == 128)
+    prefill_score_kernel<128, ST><<<grid, kWgThreads, 0, s>>>(a);
+  else
+    prefill_score_kernel<64, ST><<<grid, kWgThreads, 0, s>>>(a);
+}
+
+hipError_t launch_prefill_score(const PrefillScoreArgs& a, int idx_dim, int score_type,
+                                hipStream_t s) {
   const int grid = a.num_seqs * a.max_tiles * a.hidx * a.kchunks;
   if (grid == 0) return hipSuccess;
-  if (idx_dim == 128)
-    prefill_score_kernel<128><<<grid, kWgThreads, 0, s>>>(a);
-  else
-    prefill_score_kernel<64><<<grid, kWgThreads, 0, s>>>(a);
+  if (score_type == kScoreMean) launch_prefill_score_st<kScoreMean>(a, idx_dim, grid, s);
+  else if (score_type == kScoreLse) launch_prefill_score_st<kScoreLse>(a, idx_dim, grid, s);
+  else launch_prefill_score_st<kScoreMax>(a, idx_dim, grid, s);
   return hipGetLastError();
 }
 

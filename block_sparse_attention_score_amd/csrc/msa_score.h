@@ -75,7 +75,7 @@ __device__ __forceinline__ float dot8(const QSlice<F32>& q, const Raw8<F32>& k) 
   return d;
 }
 
-template <class IT, int DI>
+template <class IT, int DI, int ST = kScoreMax>
 __device__ void score_chunk(const ScoreArgs& a, int pair, int chunk) {
   constexpr int LPR = DI / 8;          // lanes per token row
   constexpr int RPL = kWave / LPR;     // token rows per wave load
@@ -116,6 +116,7 @@ __device__ void score_chunk(const ScoreArgs& a, int pair, int chunk) {
       const int nvalid = min(kBlock, p + 1 - j * kBlock);
       const int64_t base =
           (static_cast<int64_t>(page) * a.hidx + h) * kBlock * DI + row * DI + col * 8;
+      BlockScore<ST> red;
 #pragma unroll
       for (int i0 = 0; i0 < NLOAD; i0 += BATCH) {
         Raw8<IT> raw[BATCH];
@@ -126,14 +127,16 @@ __device__ void score_chunk(const ScoreArgs& a, int pair, int chunk) {
         // scheduler would otherwise interleave loads and dot products and
         // keep about ten loads in flight)
         __builtin_amdgcn_sched_barrier(0);
+        float d[BATCH];
+        bool ok[BATCH];
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
-          const float d = group_sum<LPR>(dot8(qs, raw[i]));
-          const int t = (i0 + i) * RPL + row;
-          m = fmaxf(m, t < nvalid ? d : -INFINITY);
+          d[i] = group_sum<LPR>(dot8(qs, raw[i]));
+          ok[i] = (i0 + i) * RPL + row < nvalid;
         }
+        red.add(d, ok, col == 0, a.st_scale_log2);
       }
-      m = wave_max(m);
+      m = red.finish(nvalid);
     }
     if (lane == 0) srow[j] = m;
   }
@@ -182,7 +185,7 @@ __device__ __forceinline__ void iv_merge(float& m, float& l, float (&o)[8], floa
   m = M;
 }
 
-template <class IT, int DI>
+template <class IT, int DI, int ST = kScoreMax>
 __device__ void score_value_chunk(const ScoreArgs& a, int pair, int chunk, IvLds<DI>& S) {
   constexpr int LPR = DI / 8;          // lanes per token row
   constexpr int RPL = kWave / LPR;     // token rows per wave load
@@ -224,6 +227,7 @@ __device__ void score_value_chunk(const ScoreArgs& a, int pair, int chunk, IvLds
       const int nvalid = min(kBlock, p + 1 - j * kBlock);
       const int64_t base =
           (static_cast<int64_t>(page) * a.hidx + h) * kBlock * DI + row * DI + col * 8;
+      BlockScore<ST> red;
 #pragma unroll
       for (int i0 = 0; i0 < NLOAD; i0 += BATCH) {
         Raw8<IT> rk[BATCH], rv[BATCH];
@@ -233,16 +237,17 @@ __device__ void score_value_chunk(const ScoreArgs& a, int pair, int chunk, IvLds
 #pragma unroll
         for (int i = 0; i < BATCH; ++i)
           rv[i] = load_raw(tag, a.idx_v, base + static_cast<int64_t>((i0 + i) * RPL) * DI);
-        float sc[BATCH];
+        float sc[BATCH], dd[BATCH];
+        bool okv[BATCH];
         float mb = om;
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
-          const float d = group_sum<LPR>(dot8(qs, rk[i]));
-          const bool ok = (i0 + i) * RPL + row < nvalid;
-          m = fmaxf(m, ok ? d : -INFINITY);
-          sc[i] = ok ? d * a.iv_scale_log2 : -INFINITY;
+          dd[i] = group_sum<LPR>(dot8(qs, rk[i]));
+          okv[i] = (i0 + i) * RPL + row < nvalid;
+          sc[i] = okv[i] ? dd[i] * a.iv_scale_log2 : -INFINITY;
           mb = fmaxf(mb, sc[i]);
         }
+        red.add(dd, okv, col == 0, a.st_scale_log2);
         // online softmax over this lane's rows: rescale by the new maximum
         const float mu = mb == -INFINITY ? 0.f : mb;
         const float alpha = __builtin_amdgcn_exp2f(om - mu);
@@ -261,7 +266,7 @@ __device__ void score_value_chunk(const ScoreArgs& a, int pair, int chunk, IvLds
         }
         om = mb;
       }
-      m = wave_max(m);
+      m = red.finish(nvalid);
     }
     if (lane == 0) srow[j] = m;
   }
@@ -308,7 +313,7 @@ __device__ void score_value_chunk(const ScoreArgs& a, int pair, int chunk, IvLds
 // that query's own position, so a page is read once for up to QG queries
 // (and re-read from the L2 for further groups).  Rows of the sequence's
 // queries get -inf past their last visible block.
-template <class IT, int DI, int QG>
+template <class IT, int DI, int QG, int ST = kScoreMax>
 __device__ void score_chunk_multi(const ScoreArgs& a, int pair, int chunk) {
   constexpr int LPR = DI / 8;
   constexpr int RPL = kWave / LPR;
@@ -361,6 +366,7 @@ __device__ void score_chunk_multi(const ScoreArgs& a, int pair, int chunk) {
       float m[QG];
 #pragma unroll
       for (int qi = 0; qi < QG; ++qi) m[qi] = -INFINITY;
+      BlockScore<ST> red[QG];
       if (page >= 0 && page < a.num_pages) {
         const int64_t base =
             (static_cast<int64_t>(page) * a.hidx + h) * kBlock * DI + row * DI + col * 8;
@@ -377,13 +383,17 @@ __device__ void score_chunk_multi(const ScoreArgs& a, int pair, int chunk) {
             const int t = j * kBlock + (i0 + i) * RPL + row;  // token position
 #pragma unroll
             for (int qi = 0; qi < QG; ++qi) {
-              const float d = group_sum<LPR>(dot8(qs[qi], raw[i]));
-              m[qi] = fmaxf(m[qi], t <= pq[qi] ? d : -INFINITY);
+              const float d[1] = {group_sum<LPR>(dot8(qs[qi], raw[i]))};
+              const bool ok[1] = {t <= pq[qi]};
+              red[qi].add(d, ok, col == 0, a.st_scale_log2);
             }
           }
         }
+        // visible tokens of the block for each query (keys past the sequence
+        // end are after every query)
 #pragma unroll
-        for (int qi = 0; qi < QG; ++qi) m[qi] = wave_max(m[qi]);
+        for (int qi = 0; qi < QG; ++qi)
+          m[qi] = red[qi].finish(min(kBlock, pq[qi] + 1 - j * kBlock));
       }
       if (lane == 0) {
 #pragma unroll

@@ -6,30 +6,30 @@
 namespace msa {
 
 // One workgroup per (pair, chunk); scores only.
-template <class IT, int DI>
+template <class IT, int DI, int ST>
 __global__ __launch_bounds__(kWgThreads) void decode_score_kernel(ScoreArgs a) {
   if (blockIdx.x == 0 && a.zero_words != nullptr)
     for (int i = threadIdx.x; i < a.zero_count; i += kWgThreads) a.zero_words[i] = 0u;
   const int pair = blockIdx.x / a.chunks_per_pair;
-  score_chunk<IT, DI>(a, pair, blockIdx.x - pair * a.chunks_per_pair);
+  score_chunk<IT, DI, ST>(a, pair, blockIdx.x - pair * a.chunks_per_pair);
 }
 
 // The same grid with the index-value branch on: scores and value partials.
-template <class IT, int DI>
+template <class IT, int DI, int ST>
 __global__ __launch_bounds__(kWgThreads) void decode_score_value_kernel(ScoreArgs a) {
   __shared__ IvLds<DI> lds;
   if (blockIdx.x == 0 && a.zero_words != nullptr)
     for (int i = threadIdx.x; i < a.zero_count; i += kWgThreads) a.zero_words[i] = 0u;
   const int pair = blockIdx.x / a.chunks_per_pair;
-  score_value_chunk<IT, DI>(a, pair, blockIdx.x - pair * a.chunks_per_pair, lds);
+  score_value_chunk<IT, DI, ST>(a, pair, blockIdx.x - pair * a.chunks_per_pair, lds);
 }
 
 // Short chunks: one workgroup per (pair, chunk), every query of the pair's
 // sequence.
-template <class IT, int DI>
+template <class IT, int DI, int ST>
 __global__ __launch_bounds__(kWgThreads) void multi_score_kernel(ScoreArgs a) {
   const int pair = blockIdx.x / a.chunks_per_pair;
-  score_chunk_multi<IT, DI, 4>(a, pair, blockIdx.x - pair * a.chunks_per_pair);
+  score_chunk_multi<IT, DI, 4, ST>(a, pair, blockIdx.x - pair * a.chunks_per_pair);
 }
 
 // One workgroup per (query token, index head) row.
@@ -101,32 +101,46 @@ hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s) {
 }
 
 
-template <class IT, int DI>
+template <class IT, int DI, int ST>
 static void launch_score_t(const ScoreArgs& a, hipStream_t s) {
   const int grid = a.num_seqs * a.hidx * a.chunks_per_pair;
   if (a.idx_v != nullptr)
-    decode_score_value_kernel<IT, DI><<<grid, kWgThreads, 0, s>>>(a);
+    decode_score_value_kernel<IT, DI, ST><<<grid, kWgThreads, 0, s>>>(a);
   else
-    decode_score_kernel<IT, DI><<<grid, kWgThreads, 0, s>>>(a);
+    decode_score_kernel<IT, DI, ST><<<grid, kWgThreads, 0, s>>>(a);
 }
 
-hipError_t launch_decode_score(const ScoreArgs& a, int idx_dtype, int idx_dim,
-                               hipStream_t s) {
-  if (a.num_seqs * a.hidx * a.chunks_per_pair == 0) return hipSuccess;
+template <int ST>
+static void launch_score_st(const ScoreArgs& a, int idx_dtype, int idx_dim, hipStream_t s) {
   const bool f32 = idx_dtype == 1;
   if (idx_dim == 128) {
-    if (f32) launch_score_t<F32, 128>(a, s); else launch_score_t<BF16, 128>(a, s);
+    if (f32) launch_score_t<F32, 128, ST>(a, s); else launch_score_t<BF16, 128, ST>(a, s);
   } else {
-    if (f32) launch_score_t<F32, 64>(a, s); else launch_score_t<BF16, 64>(a, s);
+    if (f32) launch_score_t<F32, 64, ST>(a, s); else launch_score_t<BF16, 64, ST>(a, s);
   }
+}
+
+hipError_t launch_decode_score(const ScoreArgs& a, int idx_dtype, int idx_dim, int score_type,
+                               hipStream_t s) {
+  if (a.num_seqs * a.hidx * a.chunks_per_pair == 0) return hipSuccess;
+  if (score_type == kScoreMean) launch_score_st<kScoreMean>(a, idx_dtype, idx_dim, s);
+  else if (score_type == kScoreLse) launch_score_st<kScoreLse>(a, idx_dtype, idx_dim, s);
+  else launch_score_st<kScoreMax>(a, idx_dtype, idx_dim, s);
   return hipGetLastError();
 }
 
-hipError_t launch_multi_score(const ScoreArgs& a, int idx_dim, hipStream_t s) {
+template <int ST>
+static void launch_multi_st(const ScoreArgs& a, int idx_dim, int grid, hipStream_t s) {
+  if (idx_dim == 128) multi_score_kernel<BF16, 128, ST><<<grid, kWgThreads, 0, s>>>(a);
+  else multi_score_kernel<BF16, 64, ST><<<grid, kWgThreads, 0, s>>>(a);
+}
+
+hipError_t launch_multi_score(const ScoreArgs& a, int idx_dim, int score_type, hipStream_t s) {
   const int grid = a.num_seqs * a.hidx * a.chunks_per_pair;
   if (grid == 0) return hipSuccess;
-  if (idx_dim == 128) multi_score_kernel<BF16, 128><<<grid, kWgThreads, 0, s>>>(a);
-  else multi_score_kernel<BF16, 64><<<grid, kWgThreads, 0, s>>>(a);
+  if (score_type == kScoreMean) launch_multi_st<kScoreMean>(a, idx_dim, grid, s);
+  else if (score_type == kScoreLse) launch_multi_st<kScoreLse>(a, idx_dim, grid, s);
+  else launch_multi_st<kScoreMax>(a, idx_dim, grid, s);
   return hipGetLastError();
 }
 

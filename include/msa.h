@@ -141,6 +141,12 @@ typedef struct {
                             idx_out, the append stores index values; 0: off
                             (the sglang page's disable_index_value), those
                             pointers must be NULL */
+  int32_t score_type;    /* block score of step 1 (the sglang page reads a
+                            score type from the model config without printing
+                            its values): 0 max (the default above), 1 the mean
+                            of q_idx . k_idx over the block's tokens t <= p,
+                            2 log sum exp(q_idx . k_idx / sqrt(Di)) over them;
+                            1 and 2 are this library's definitions */
 } msa_params_t;
 
 /* Library version, (major << 16) | minor. */

@@ -49,8 +49,10 @@ def kth_score(scores_row, sel_row, forced):
 
 
 def check_selection(gpu_sel, gpu_cnt, ora_scores, ora_sel, ora_cnt, positions, init, local,
-                    rows=None):
-    """Selections [T, Hidx, Kmax] / counts [T, Hidx]; positions: list of (b, p)."""
+                    rows=None, abs_band=0.0):
+    """Selections [T, Hidx, Kmax] / counts [T, Hidx]; positions: list of (b, p).
+    abs_band widens the tie band to an absolute floor (scores near zero, whose
+    own tolerance is absolute)."""
     T, H, K = ora_sel.shape
     n_band = 0
     rows = range(T) if rows is None else rows
@@ -72,7 +74,7 @@ def check_selection(gpu_sel, gpu_cnt, ora_scores, ora_sel, ora_cnt, positions, i
                 s = ora_scores[t, h]
                 sk = kth_score(s, o, F)
                 assert sk is not None
-                lim = TIE_BAND * max(abs(sk), 1e-30)
+                lim = max(TIE_BAND * max(abs(sk), 1e-30), abs_band)
                 for j in diff:
                     assert abs(s[j] - sk) <= lim, (
                         f"row {t},{h}: block {j} score {s[j]!r} vs k-th {sk!r}")

@@ -42,8 +42,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_params_struct_layout_matches_header():
-    # 17 four-byte int32 / float fields, no padding
-    assert ctypes.sizeof(_lib.Params) == 17 * 4
+    # 18 four-byte int32 / float fields, no padding
+    assert ctypes.sizeof(_lib.Params) == 18 * 4
 
 
 def base_cfg(**kw):
@@ -88,6 +88,19 @@ def test_bad_params_rejected(kw, code):
     assert msa.load().msa_last_error().decode()
     p = base_cfg(**kw).params()
     assert msa.load().msa_decode_workspace_size(ctypes.byref(p), 4, 16) == 0
+
+
+@pytest.mark.parametrize("code", [-1, 3])
+def test_bad_score_type_rejected(code):
+    lib = msa.load()
+    p = base_cfg().params()
+    p.score_type = code
+    assert lib.msa_decode_workspace_size(ctypes.byref(p), 4, 16) == 0
+    assert "score_type" in lib.msa_last_error().decode()
+    for name in ("mean", "lse"):
+        p = base_cfg(score_type=name).params()
+        assert p.score_type == msa.api.SCORE_TYPES[name]
+        assert lib.msa_decode_workspace_size(ctypes.byref(p), 4, 16) > 0
 
 
 def test_null_params_and_pointers():
