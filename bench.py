@@ -10,7 +10,10 @@ in the same run and reported under "configs": decode 2 x 2048, decode
 32 x 32768, fp8-e4m3 decode 32 x 65536 and chunked prefill 4 x 4096 over a
 16384-token prefix.  ``--workload NAME`` makes NAME the headline (prefill and
 append workloads report tokens/s); ``--no-configs`` measures the headline
-alone (profiling runs).
+alone (profiling runs).  In the default run every workload is measured in a
+process of its own (this process only starts them and joins their lines), so
+that no workload runs in memory the previous one allocated and freed; with
+``--no-configs`` the measurement runs in this process.
 
 A decode step is one msa_sparse_decode call (score every block of the index keys,
 select, split-K attend over the selected blocks, combine) over one batch of
@@ -52,6 +55,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sub-config", action="store_true",
+                    help="measure as a workload beside the headline (no warm steps)")
     ap.add_argument("--no-configs", action="store_true",
                     help="measure the headline workload only")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -363,21 +368,40 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-
     from synth import workload
 
-    measure = {"decode": measure_decode, "prefill": measure_prefill, "append": measure_append}
-    spec = workload(args.workload)
-    res = measure[spec["kind"]](args, args.workload, headline=True)
     if not args.no_configs and args.workload == DEFAULT_WORKLOAD:
+        # (this process does not touch the GPU: the children measure)
+        res = measure_in_child(args, args.workload, headline=True)
         res["configs"] = {}
         for name in SUB_CONFIGS:
             print(f"[bench] {name}", file=sys.stderr, flush=True)
-            sub = measure[workload(name)["kind"]](args, name, headline=False)
-            res["configs"][name] = sub_entry(sub)
-            torch.cuda.empty_cache()
+            res["configs"][name] = sub_entry(measure_in_child(args, name, headline=False))
+        print(json.dumps(res), flush=True)
+        return
+    measure = {"decode": measure_decode, "prefill": measure_prefill, "append": measure_append}
+    spec = workload(args.workload)
+    res = measure[spec["kind"]](args, args.workload, headline=not args.sub_config)
     print(json.dumps(res), flush=True)
+
+
+def measure_in_child(args, name, headline):
+    """One workload measured by ``bench.py --workload name --no-configs`` in a
+    child process; its JSON line."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--no-configs",
+           "--steps", str(args.steps), "--warmup", str(args.warmup),
+           "--cpu-seconds", str(args.cpu_seconds)]
+    if not headline:
+        cmd += ["--sub-config", "--no-cpu-baseline"]
+    elif args.no_cpu_baseline:
+        cmd.append("--no-cpu-baseline")
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+    if r.returncode != 0:
+        print(r.stdout, file=sys.stderr)
+        raise SystemExit(f"bench.py: measuring {name} failed (exit {r.returncode})")
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    return json.loads(lines[-1])
 
 
 def measure_decode(args, name, headline):

@@ -16,6 +16,8 @@
 
 namespace {
 
+using msa::kPrefillBlocksPerChunk;
+
 thread_local char g_err[512] = "";
 
 msa_status_t fail(msa_status_t st, const char* fmt, ...) {
@@ -148,8 +150,6 @@ int blocks_per_split(const msa_params_t& p, int32_t num_units) {
 constexpr int kPagesPerItem = 8;
 // Prefill list entries pack a token index above an 8-bit selection slot.
 constexpr int kMaxPrefillTokens = 1 << 23;
-// Blocks of keys per prefill scoring (and index-value) workgroup.
-constexpr int kPrefillBlocksPerChunk = 16;
 
 // Decode workspace: block scores, split partials and the split tickets (and,
 // with the index-value branch, the scan's per-chunk value partials).
@@ -367,6 +367,14 @@ msa_status_t check_grid(int64_t workgroups, int threads, const char* what) {
 
 constexpr int kScanThreads = 256;     // decode and short-chunk scans, selection, combine
 constexpr int kAttendThreads = 512;   // decode attention: eight waves
+// Prefill scoring grid: (sequence, index head, 16-block run) triples rounded
+// up to a multiple of 8, times the 256-row tiles of the longest possible
+// sequence (launch_prefill_score).
+int64_t prefill_score_workgroups(int32_t B, int hidx, int32_t MB, int32_t T) {
+  const int64_t runs = int64_t(B) * hidx * ((MB + kPrefillBlocksPerChunk - 1) / kPrefillBlocksPerChunk);
+  return (runs + 7) / 8 * 8 * ((int64_t(T) + 255) / 256);
+}
+
 int64_t scan_workgroups(int32_t B, int hidx, int32_t MB) {
   return int64_t(B) * hidx * ((MB + kPagesPerItem - 1) / kPagesPerItem);
 }
@@ -601,9 +609,8 @@ msa_status_t msa_block_score(const msa_params_t* params, const void* idx_q,
       st = check_grid(scan_workgroups(num_seqs, params->num_idx_heads, max_blocks), kScanThreads,
                       "chunk scan");
     } else {
-      const int64_t tiles = (int64_t(num_q_tokens) + 255) / 256;
-      st = check_grid(int64_t(num_seqs) * tiles * params->num_idx_heads *
-                          ((max_blocks + kPrefillBlocksPerChunk - 1) / kPrefillBlocksPerChunk),
+      st = check_grid(prefill_score_workgroups(num_seqs, params->num_idx_heads, max_blocks,
+                                               num_q_tokens),
                       kScanThreads, "prefill scoring");
     }
     if (st != MSA_OK) return st;
@@ -814,9 +821,7 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
     st = check_grid(scan_workgroups(num_seqs, p.num_idx_heads, max_blocks), kScanThreads,
                     "chunk scan");
   } else {
-    const int64_t tiles = (int64_t(num_q_tokens) + 255) / 256;
-    st = check_grid(int64_t(num_seqs) * tiles * p.num_idx_heads *
-                        ((max_blocks + kPrefillBlocksPerChunk - 1) / kPrefillBlocksPerChunk),
+    st = check_grid(prefill_score_workgroups(num_seqs, p.num_idx_heads, max_blocks, num_q_tokens),
                     kScanThreads, "prefill scoring");
   }
   if (st != MSA_OK) return st;

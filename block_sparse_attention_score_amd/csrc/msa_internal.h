@@ -47,7 +47,7 @@ struct PrefillScoreArgs {
   int32_t num_seqs;
   int32_t hidx;
   int32_t max_tiles;         // 256-row query tiles of the longest possible sequence
-  int32_t blocks_per_chunk;  // key blocks per workgroup
+  int32_t blocks_per_chunk;  // key blocks per workgroup (kPrefillBlocksPerChunk)
   int32_t kchunks;           // ceil(max_blocks / blocks_per_chunk)
   float* scores;             // [T, Hidx, max_blocks]
   float st_scale_log2;       // log-sum-exp block scores: log2(e) / sqrt(Di)
@@ -157,7 +157,7 @@ struct PrefillValueArgs {
   int32_t num_tokens;
   int32_t hidx;
   int32_t max_tiles;         // 256-row query tiles of the longest possible sequence
-  int32_t blocks_per_chunk;  // key blocks per workgroup
+  int32_t blocks_per_chunk;  // key blocks per workgroup (kPrefillBlocksPerChunk)
   int32_t kchunks;           // ceil(max_blocks / blocks_per_chunk)
   float scale_log2;          // log2(e) / sqrt(Di)
   float* part_o;             // [T, Hidx, kchunks, Di] normalised partial outputs
@@ -169,6 +169,8 @@ struct PrefillValueArgs {
 // Key-major prefill attention over the k2q lists (bf16 q; bf16 or fp8 K/V).
 constexpr int kMaxSelect = 160;        // topk + init + local, at most
 constexpr int kPrefillTileRows = 256;  // query rows (token x GQA head) per tile
+// Blocks of keys per prefill scoring (and index-value) workgroup.
+constexpr int kPrefillBlocksPerChunk = 16;
 struct PrefillAttnArgs {
   const void* q;             // [T, Hq, D] bf16
   const void* k_pool;        // [P, Hkv, 128, D]

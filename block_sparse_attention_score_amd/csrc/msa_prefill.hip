@@ -30,19 +30,26 @@ constexpr int kPrefillRows = 256;  // query rows per scoring workgroup
 template <int DI, int ST>
 __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillScoreArgs a) {
   constexpr int KS = DI / 32;              // 32-dim k-steps
-  constexpr int ROW_BYTES = DI * 2 + 16;   // padded LDS row
+  // padded LDS row: at Di = 128 a 288-byte row keeps the 16-byte fragment
+  // reads of 16 rows free of bank conflicts on gfx950 (272 bytes: a fifth
+  // more LDS cycles, measured)
+  constexpr int ROW_BYTES = DI == 128 ? DI * 2 + 32 : DI * 2 + 16;
   constexpr int CHUNKS = DI * 2 / 16;      // 16-byte chunks per key row
   constexpr int LOADS = 128 * CHUNKS / kWgThreads;  // per thread per block
   __shared__ __attribute__((aligned(16))) char kbuf[2][128 * ROW_BYTES];
 
-  // workgroup -> (256-row query tile, sequence, index head, key-block chunk),
-  // query tile outermost: the grid is sized for the longest possible
-  // sequence (all tokens), and tiles past a sequence's new tokens exit at
-  // once, so ordering by tile puts those empty workgroups after every real
-  // one (they are dispatched last instead of holding slots in between)
-  const int per_tile = a.num_seqs * a.hidx * a.kchunks;
-  const int qt = blockIdx.x / per_tile;
-  int rem = blockIdx.x - qt * per_tile;
+  // workgroup -> (key-block run, 256-row query tile): a run (sequence, index
+  // head, chunk of 16 key blocks) goes to XCD run % 8, whose workgroups
+  // (blockIdx x, x + 8, ...) take its query tiles one after another, so the
+  // tiles reading the same 16 key blocks run together on one L2.  The tiles
+  // are counted for the longest possible sequence (all tokens); those past a
+  // sequence's new tokens exit at once.
+  const int runs = a.num_seqs * a.hidx * a.kchunks;
+  const int xl = blockIdx.x >> 3;
+  const int qt = xl % a.max_tiles;
+  const int run = (xl / a.max_tiles) * 8 + (blockIdx.x & 7);
+  if (run >= runs) return;
+  int rem = run;
   const int b = rem / (a.hidx * a.kchunks);
   rem -= b * a.hidx * a.kchunks;
   const int h = rem / a.kchunks;
@@ -56,8 +63,8 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
   const int p_last = prefix + min(nq, i0 + kPrefillRows) - 1;
   if (p_last < 0) return;
   const int nb_tile = min(p_last / kBlock + 1, a.max_blocks);
-  const int j0 = kc * a.blocks_per_chunk;
-  const int j1 = min(nb_tile, j0 + a.blocks_per_chunk);
+  const int j0 = kc * kPrefillBlocksPerChunk;
+  const int j1 = min(nb_tile, j0 + kPrefillBlocksPerChunk);
   if (j0 >= j1) return;
 
   const int tid = threadIdx.x;
@@ -123,10 +130,11 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
   };
   // Scores of this tile's rows through a buffer descriptor whose range ends
   // at the sequence's last new token: stores of rows past it are dropped by
-  // the range check, so every lane stores unconditionally (the four lanes of
-  // a query store the same value), with a loop-invariant row offset and the
-  // block in the scalar offset.  A fixed store sequence keeps the waits the
-  // compiler derives from draining stores.
+  // the range check.  The scores stay in registers until the run ends: lane
+  // q4 of a query column keeps blocks j0 + 4 q4 .. + 3 (-inf past the
+  // tile's last block), and the four lanes of the column then write the
+  // row's 64 bytes of the run with one store (single 4-byte stores per block
+  // reached memory as partial lines, several times the scores' bytes).
   const int rows = min(nq - i0, kPrefillRows);
   const auto srsrc = __builtin_amdgcn_make_buffer_rsrc(
       a.scores + (static_cast<int64_t>(cu0 + i0) * a.hidx + h) * a.max_blocks, 0,
@@ -134,6 +142,11 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
   int srow[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) srow[rt] = (64 * w + 16 * rt + l16) * a.hidx * a.max_blocks * 4;
+  float sv[4][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[rt][e] = -INFINITY;
 
   // Staging into LDS: thread chunk c = tid + 256 k is row c / CHUNKS, bytes
   // 16 (c % CHUNKS) of the block (rows padded to ROW_BYTES).
@@ -227,13 +240,12 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
         mx[rt] = max_nan(mx[rt], __shfl_xor(mx[rt], 32));
       }
     }
-    // The next block goes to LDS before this block's scores are stored: the
-    // staging waits for the block's loads, and loads and stores retire in
-    // order, so stores issued earlier would be waited for as well.
     if (j + 1 < j1) store(buf ^ 1, next);
+    const int jj = j - j0;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mx[rt]), srsrc, srow[rt], 4 * j, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[rt][e] = jj == 4 * q4 + e ? mx[rt] : sv[rt][e];
     __syncthreads();
   };
 
@@ -245,6 +257,23 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
   for (int j = j0; j < j1; j += 2) {
     step(j, 0, sa, sb);
     if (j + 1 < j1) step(j + 1, 1, sb, sa);
+  }
+  const int jb = 4 * q4;  // this lane's blocks j0 + jb .. + 3
+  if (j0 + kPrefillBlocksPerChunk <= a.max_blocks) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const u32x4_t v = {__float_as_uint(sv[rt][0]), __float_as_uint(sv[rt][1]),
+                         __float_as_uint(sv[rt][2]), __float_as_uint(sv[rt][3])};
+      __builtin_amdgcn_raw_buffer_store_b128(v, srsrc, srow[rt] + 4 * jb, 4 * j0, 0);
+    }
+  } else {  // the row's last run: only blocks below max_blocks
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j0 + jb + e < a.max_blocks)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv[rt][e]), srsrc,
+                                                srow[rt] + 4 * (jb + e), 4 * j0, 0);
   }
 }
 
@@ -307,7 +336,8 @@ static void launch_prefill_score_st(const PrefillScoreArgs& a, int idx_dim, int 
 
 hipError_t launch_prefill_score(const PrefillScoreArgs& a, int idx_dim, int score_type,
                                 hipStream_t s) {
-  const int grid = a.num_seqs * a.max_tiles * a.hidx * a.kchunks;
+  // runs rounded up to a multiple of 8 (one set per XCD), times the tiles
+  const int grid = (a.num_seqs * a.hidx * a.kchunks + 7) / 8 * 8 * a.max_tiles;
   if (grid == 0) return hipSuccess;
   if (score_type == kScoreMean) launch_prefill_score_st<kScoreMean>(a, idx_dim, grid, s);
   else if (score_type == kScoreLse) launch_prefill_score_st<kScoreLse>(a, idx_dim, grid, s);

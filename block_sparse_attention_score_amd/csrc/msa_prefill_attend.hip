@@ -12,9 +12,10 @@
 //      the counts into list offsets and 256-row work tiles, fill the lists;
 //   2. per tile: up to 256 query rows (tokens x GQA heads of one kv head,
 //      eight waves of 32 rows) against block j, staged once in LDS (K as
-//      [key][dim], V as [dim][key]); S^T = K Q^T and O^T = V^T P^T on bf16
-//      MFMA, causal mask per row; a normalised partial (o in bf16, lse in
-//      f32) per (token, kv head, slot);
+//      [key][dim], V as [dim][key] with the dims permuted so that each lane
+//      ends up holding 8-dim runs of its output row); S^T = K Q^T and
+//      O^T = V^T P^T on bf16 MFMA, causal mask per row; a normalised partial
+//      (o in bf16, lse in f32) per (token, kv head, slot);
 //   3. per (token, kv head), the log-sum-exp combine of its partials.
 #include "msa_device.h"
 #include "msa_internal.h"
@@ -27,12 +28,19 @@ constexpr int kPfWaves = 8;                 // waves of a tile workgroup
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kRows = kPrefillTileRows;     // query rows (token x head) per tile
 static_assert(kRows == 32 * kPfWaves, "each wave owns 32 query rows");
-constexpr int kStride = 136;     // LDS row stride in bf16 elements (128 + 8)
+// LDS row strides in bf16 elements, chosen by the bank conflicts measured on
+// gfx950 (rocprofv3 SQ_LDS_BANK_CONFLICT over each access pattern): the
+// 16-byte K fragment reads of 16 rows are conflict-free at a 288-byte row
+// (272 bytes cost a fifth more cycles), the 8-byte V^T fragment reads at 264
+// bytes (272: a fifth more), and the transposing 8-byte V^T stores conflict
+// half as often at 264 as at 272 bytes.
+constexpr int kStrideK = 144;
+constexpr int kStrideV = 132;
 constexpr float kLn2f = 0.69314718055994531f;
 
 struct PfStage {
-  alignas(16) uint16_t k[kBlock * kStride];   // K   [key][dim]
-  alignas(16) uint16_t vt[kBlock * kStride];  // V^T [dim][key]
+  alignas(16) uint16_t k[kBlock * kStrideK];   // K   [key][dim]
+  alignas(16) uint16_t vt[kBlock * kStrideV];  // V^T [dim][key]
   int tok[kRows];                 // token of each token slot of the tile (-1: none)
   int slot[kRows];                // its slot in the token's selection
   int pos[kRows];                 // its position in the sequence
@@ -114,6 +122,15 @@ __device__ __forceinline__ bf16x8_t load8_buf(const BF8*, __amdgpu_buffer_rsrc_t
                                               uint32_t soff) {
   const auto raw = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
   return bf8x8_to_bf16x8(raw[0], raw[1]);
+}
+
+// V^T rows are staged in a permuted dim order: MFMA result row 16 dt + 4 q4
+// + r of O^T holds dim 32 (dt / 2) + 8 q4 + 4 (dt % 2) + r, so lane q4 of a
+// query row holds dims 32 k + 8 q4 .. + 8 (from dt = 2k, 2k + 1) and the
+// four lanes of the row store 64 contiguous bytes per instruction.  The LDS
+// row of dim D is the inverse map.
+__device__ __forceinline__ int vt_row_of_dim(int D) {
+  return 16 * (2 * (D >> 5) + ((D >> 2) & 1)) + 4 * ((D >> 3) & 3) + (D & 3);
 }
 
 // Clears v unless keep, without a branch.
@@ -415,7 +432,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
       B.pos[tl] = ok ? m.p0 + (et >> 8) : -1;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8_t*>(&B.k[(32 * i + krl) * kStride + dcl]) = kraw[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8_t*>(&B.k[(32 * i + krl) * kStrideK + dcl]) = kraw[i];
     uint16_t v[4][8];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) __builtin_memcpy(&v[kk][0], &vraw[kk], 16);
@@ -424,7 +441,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
       const uint32_t w0 = static_cast<uint32_t>(v[0][d]) | (static_cast<uint32_t>(v[1][d]) << 16);
       const uint32_t w1 = static_cast<uint32_t>(v[2][d]) | (static_cast<uint32_t>(v[3][d]) << 16);
       const u32x2_t pr = {w0, w1};
-      *reinterpret_cast<u32x2_t*>(&B.vt[(dcl + d) * kStride + 4 * krl]) = pr;
+      *reinterpret_cast<u32x2_t*>(&B.vt[vt_row_of_dim(dcl + d) * kStrideV + 4 * krl]) = pr;
     }
   };
 
@@ -457,9 +474,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
   load_q(q_off);
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    uint16_t* po = a.sink_o + qhh[nt] * 128 + 4 * q4;
+    uint16_t* po = a.sink_o + qhh[nt] * 128 + 8 * q4;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<u32x2_t*>(po + 16 * dt) = u32x2_t{0u, 0u};
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4_t*>(po + 32 * k) = u32x4_t{0u, 0u, 0u, 0u};
     a.sink_lse[qhh[nt]] = 0.f;
   }
   __syncthreads();
@@ -510,7 +527,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const bf16x8_t kf =
-              lds_b128(&B.k[(64 * kh + 16 * mt + l16) * kStride + 32 * ks + 8 * q4]);
+              lds_b128(&B.k[(64 * kh + 16 * mt + l16) * kStrideK + 32 * ks + 8 * q4]);
           st[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], st[mt][0], 0, 0, 0);
           st[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], st[mt][1], 0, 0, 0);
         }
@@ -585,7 +602,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
         const int kk = 2 * kh + k2;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const uint16_t* row = &B.vt[(16 * dt + l16) * kStride + 32 * kk + 4 * q4];
+          const uint16_t* row = &B.vt[(16 * dt + l16) * kStrideV + 32 * kk + 4 * q4];
           const u32x2_t lo = lds_b64(row), hi2 = lds_b64(row + 16);
           const u32x4_t cat = {lo[0], lo[1], hi2[0], hi2[1]};
           bf16x8_t vf;
@@ -608,13 +625,15 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
       const float inv = l > 0.f ? a.v_scale * __builtin_amdgcn_rcpf(l) : 0.f;
       const int64_t base =
           ((static_cast<int64_t>(max(t, 0)) * a.hkv + g) * a.kmax + B.slot[qtl[nt]]) * G + qhh[nt];
-      uint16_t* po = (t >= 0 ? a.part_o + base * 128 : a.sink_o + qhh[nt] * 128) + 4 * q4;
+      uint16_t* po = (t >= 0 ? a.part_o + base * 128 : a.sink_o + qhh[nt] * 128) + 8 * q4;
       float* pl = t >= 0 ? a.part_lse + base : a.sink_lse + qhh[nt];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const u32x2_t v = {pack2_rne(o[dt][nt][0] * inv, o[dt][nt][1] * inv),
-                           pack2_rne(o[dt][nt][2] * inv, o[dt][nt][3] * inv)};
-        *reinterpret_cast<u32x2_t*>(po + 16 * dt) = v;
+      for (int k = 0; k < 4; ++k) {
+        const u32x4_t v = {pack2_rne(o[2 * k][nt][0] * inv, o[2 * k][nt][1] * inv),
+                           pack2_rne(o[2 * k][nt][2] * inv, o[2 * k][nt][3] * inv),
+                           pack2_rne(o[2 * k + 1][nt][0] * inv, o[2 * k + 1][nt][1] * inv),
+                           pack2_rne(o[2 * k + 1][nt][2] * inv, o[2 * k + 1][nt][3] * inv)};
+        *reinterpret_cast<u32x4_t*>(po + 32 * k) = v;
       }
       // (the four lanes of the row store the same value)
       *pl = l > 0.f ? (mrow[nt] + __builtin_amdgcn_logf(l)) * kLn2f : -INFINITY;
