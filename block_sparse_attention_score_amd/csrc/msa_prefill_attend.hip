@@ -504,112 +504,92 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) rpos[nt] = B.pos[qtl[nt]];
 
-    // ---- the block in two halves of 64 keys, online softmax across them.
-    // S^T tiles: keys 64 kh + 16 mt + 4 q4 + r (rows), query rows 16 nt + l16.
-    // O^T = V^T P^T: dims 16 dt + 4 q4 + r (rows), query rows 16 nt + l16;
-    // k-slots e of the 32-key step kk: keys 32 kk + 4 q4 + e (e < 4) and
-    // 32 kk + 16 + 4 q4 + (e - 4), the keys the S^T tiles 2 kk, 2 kk + 1 hold.
+    // ---- the whole block at once: S^T for its 128 keys, one softmax, O^T.
+    // S^T tiles: keys 16 mt + 4 q4 + r (rows), query rows 16 nt + l16.
+    // O^T = V^T P^T: dims (permuted, see vt_row_of_dim) rows 16 dt + 4 q4 +
+    // r, query rows 16 nt + l16; k-slots e of the 32-key step kk: keys
+    // 32 kk + 4 q4 + e (e < 4) and 32 kk + 16 + 4 q4 + (e - 4), the keys the
+    // S^T tiles 2 kk, 2 kk + 1 hold.  One maximum over the block means the
+    // output accumulator is never rescaled.
     const int tok0 = m0.j * kBlock;
-    float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
-    f32x4_t o[8][2];
+    float mrow[2], lrow[2];
+    f32x4_t st[8][2];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      o[dt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      o[dt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 8; ++mt) {
+      st[mt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      st[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8_t kf = lds_b128(&B.k[(16 * mt + l16) * kStrideK + 32 * ks + 8 * q4]);
+        st[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], st[mt][0], 0, 0, 0);
+        st[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], st[mt][1], 0, 0, 0);
+      }
     }
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      f32x4_t st[4][2];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        st[mt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        st[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8_t kf =
-              lds_b128(&B.k[(64 * kh + 16 * mt + l16) * kStrideK + 32 * ks + 8 * q4]);
-          st[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], st[mt][0], 0, 0, 0);
-          st[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], st[mt][1], 0, 0, 0);
-        }
-      }
-      // the query rows of tile i+1, once S^T no longer needs qf
-      if (kh == 1) load_q(q_off);
+    // the query rows of tile i+1, now that S^T no longer needs qf
+    load_q(q_off);
 
-      // Softmax over this half in base 2: p = 2^(s c - m), c = scale * log2(e)
-      // > 0, so the row max of the raw scores gives m.  Masking (keys past the
-      // sequence end or after the row's position) only where the half is not
-      // entirely visible to every row of the wave.
-      const bool full = 64 * kh + 63 < m0.nvalid && tok0 + 64 * kh + 63 <= min(rpos[0], rpos[1]);
-      if (__builtin_amdgcn_ballot_w64(!full) != 0) {
+    // Softmax in base 2: p = 2^(s c - m), c = scale * log2(e) > 0, so the row
+    // max of the raw scores gives m.  Masking (keys past the sequence end or
+    // after the row's position) only where the block is not entirely visible
+    // to every row of the wave.
+    const bool full = kBlock - 1 < m0.nvalid && tok0 + kBlock - 1 <= min(rpos[0], rpos[1]);
+    if (__builtin_amdgcn_ballot_w64(!full) != 0) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = 64 * kh + 16 * mt + 4 * q4 + r;
-              const bool ok = key < m0.nvalid && tok0 + key <= rpos[nt];
-              st[mt][nt][r] = ok ? st[mt][nt][r] : -INFINITY;
-            }
-      }
-      float alpha[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float mr = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mr = max_nan(mr, st[mt][nt][r]);
-        const float mn = fmaxf(mrow[nt], rows_max(mr) * a.qk_scale_log2);
-        // a row with nothing visible yet keeps m = -inf; its p are 2^-inf = 0
-        const float mu = mn == -INFINITY ? 0.f : mn;
-        alpha[nt] = exp2_raw(mrow[nt] - mu);
-        float l = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float e = exp2_raw(fmaf(st[mt][nt][r], a.qk_scale_log2, -mu));
-            st[mt][nt][r] = e;
-            l += e;
+            const int key = 16 * mt + 4 * q4 + r;
+            const bool ok = key < m0.nvalid && tok0 + key <= rpos[nt];
+            st[mt][nt][r] = ok ? st[mt][nt][r] : -INFINITY;
           }
-        l = rows_sum(l);
-        mrow[nt] = mn;
-        lrow[nt] = lrow[nt] * alpha[nt] + l;
-      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float mr = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mr = max_nan(mr, st[mt][nt][r]);
+      const float mn = rows_max(mr) * a.qk_scale_log2;
+      // a row with nothing visible keeps m = -inf; its p are 2^-inf = 0
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      float l = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = exp2_raw(fmaf(st[mt][nt][r], a.qk_scale_log2, -mu));
+          st[mt][nt][r] = e;
+          l += e;
+        }
+      mrow[nt] = mn;
+      lrow[nt] = rows_sum(l);
+    }
+    f32x4_t o[8][2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
       // P as bf16 B operands
-      bf16x8_t pb[2][2];
+      bf16x8_t pb[2];
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const uint32_t u[4] = {pack2_rne(st[2 * k2][nt][0], st[2 * k2][nt][1]),
-                                 pack2_rne(st[2 * k2][nt][2], st[2 * k2][nt][3]),
-                                 pack2_rne(st[2 * k2 + 1][nt][0], st[2 * k2 + 1][nt][1]),
-                                 pack2_rne(st[2 * k2 + 1][nt][2], st[2 * k2 + 1][nt][3])};
-          __builtin_memcpy(&pb[k2][nt], u, 16);
-        }
-      if (kh == 1) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[dt][nt][r] *= alpha[nt];
+      for (int nt = 0; nt < 2; ++nt) {
+        const uint32_t u[4] = {pack2_rne(st[2 * kk][nt][0], st[2 * kk][nt][1]),
+                               pack2_rne(st[2 * kk][nt][2], st[2 * kk][nt][3]),
+                               pack2_rne(st[2 * kk + 1][nt][0], st[2 * kk + 1][nt][1]),
+                               pack2_rne(st[2 * kk + 1][nt][2], st[2 * kk + 1][nt][3])};
+        __builtin_memcpy(&pb[nt], u, 16);
       }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int kk = 2 * kh + k2;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const uint16_t* row = &B.vt[(16 * dt + l16) * kStrideV + 32 * kk + 4 * q4];
-          const u32x2_t lo = lds_b64(row), hi2 = lds_b64(row + 16);
-          const u32x4_t cat = {lo[0], lo[1], hi2[0], hi2[1]};
-          bf16x8_t vf;
-          __builtin_memcpy(&vf, &cat, 16);
-          o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[k2][0], o[dt][0], 0, 0, 0);
-          o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[k2][1], o[dt][1], 0, 0, 0);
-        }
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint16_t* row = &B.vt[(16 * dt + l16) * kStrideV + 32 * kk + 4 * q4];
+        const u32x2_t lo = lds_b64(row), hi2 = lds_b64(row + 16);
+        const u32x4_t cat = {lo[0], lo[1], hi2[0], hi2[1]};
+        bf16x8_t vf;
+        __builtin_memcpy(&vf, &cat, 16);
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[0], kk == 0 ? z : o[dt][0], 0, 0, 0);
+        o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[1], kk == 0 ? z : o[dt][1], 0, 0, 0);
       }
     }
 
