@@ -197,21 +197,35 @@ TRAFFIC_WR = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum"]
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 
 
-def traffic_json(workload_name: str) -> str:
-    return os.path.join(PROFILES, f"{workload_name}_scan_hbm_traffic.json")
 COPY_PROBE_BYTES = 1 << 30
+# The kernels whose counters make a workload's roofline traffic, and the
+# sources a measurement stays valid for: the decode index scan; the prefill
+# attention stage (k2q lists, key-major tiles, combine), per step.
 SCAN_SOURCES = ["msa_score.h", "msa_score.hip", "msa_device.h", "msa_internal.h"]
+STAGE_SOURCES = ["msa_prefill_attend.hip", "msa_device.h", "msa_internal.h"]
+STAGE_KERNELS = ["k2q_count_kernel", "k2q_scan_kernel", "k2q_fill_kernel",
+                 "prefill_attend_kernel", "prefill_combine_kernel"]
 
 
-def scan_source_hash() -> str:
+def traffic_json(workload_name: str) -> str:
+    from synth import workload
+    part = "scan" if workload(workload_name)["kind"] == "decode" else "attention"
+    return os.path.join(PROFILES, f"{workload_name}_{part}_hbm_traffic.json")
+
+
+def source_hash(names=SCAN_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "block_sparse_attention_score_amd", "csrc")
-    for name in SCAN_SOURCES:
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def scan_source_hash() -> str:
+    return source_hash(SCAN_SOURCES)
 
 
 def copy_probe():
@@ -259,10 +273,14 @@ def _write_bytes(c):
 
 
 def traffic_summary(name, scan_rd, scan_wr, copy_rd, copy_wr):
-    """Write the scan's calibrated HBM traffic of decode workload ``name`` to
-    profiles/ (JSON for bench.py, Markdown for readers)."""
+    """Write the calibrated HBM traffic of workload ``name`` to profiles/
+    (JSON for bench.py, Markdown for readers): the index scan of a decode
+    workload, the attention stage of a prefill workload."""
     from synth import WORKLOAD_SEEDS, workload
     from synth.inputs import _draw_seq_lens
+
+    if workload(name)["kind"] == "prefill":
+        return stage_traffic_summary(name, scan_rd, scan_wr, copy_rd, copy_wr)
 
     med = lambda xs: float(np.median(xs))
     s_rd = _counters(scan_rd, "decode_score_kernel")
@@ -312,15 +330,60 @@ def traffic_summary(name, scan_rd, scan_wr, copy_rd, copy_wr):
     print(json.dumps(res))
 
 
+def stage_traffic_summary(name, pf_rd, pf_wr, copy_rd, copy_wr):
+    """Prefill: calibrated HBM bytes per step of each attention-stage kernel
+    and their sum (the stage's roofline traffic), with the scoring and
+    selection kernels beside them for reference."""
+    med = lambda xs: float(np.median(xs))
+    c_rd = _counters(copy_rd, "neg")
+    c_wr = _counters(copy_wr, "neg")
+    f_rd = COPY_PROBE_BYTES / med([_read_bytes(c) for c in c_rd])
+    f_wr = COPY_PROBE_BYTES / med([_write_bytes(c) for c in c_wr])
+    rows = {}
+    for k in STAGE_KERNELS + ["prefill_score_kernel", "select_wave_kernel"]:
+        rd = med([_read_bytes(c) for c in _counters(pf_rd, k)]) * f_rd
+        wr = med([_write_bytes(c) for c in _counters(pf_wr, k)]) * f_wr
+        rows[k] = {"read": rd, "write": wr}
+    total = sum(rows[k]["read"] + rows[k]["write"] for k in STAGE_KERNELS)
+    res = {"kernel": "prefill attention stage", "workload": name, "kernels": rows,
+           "traffic_bytes_per_launch": total, "copy_factor_read": f_rd,
+           "copy_factor_write": f_wr, "source_sha256": source_hash(STAGE_SOURCES)}
+    path = traffic_json(name)
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+    table = "".join(f"| `{k}` | {v['read'] / 1e6:.1f} | {v['write'] / 1e6:.1f} |\n"
+                    for k, v in rows.items())
+    with open(path[:-5] + ".md", "w") as f:
+        f.write(
+            f"# HBM traffic of the prefill attention stage, {name}\n\n"
+            "Commands (run from the repository root on one MI355X; each pass alone):\n\n"
+            "    cd /tmp && export TMPDIR=/tmp\n"
+            f"    rocprofv3 --pmc {' '.join(TRAFFIC_RD)} --output-format csv -d <pf_rd> -- python3 <repo>/bench.py --workload {name} --no-configs --steps 3 --warmup 1 --no-cpu-baseline\n"
+            f"    rocprofv3 --pmc {' '.join(TRAFFIC_WR)} --output-format csv -d <pf_wr> -- python3 <repo>/bench.py --workload {name} --no-configs --steps 3 --warmup 1 --no-cpu-baseline\n"
+            f"    rocprofv3 --pmc {' '.join(TRAFFIC_RD)} --output-format csv -d <copy_rd> -- python3 <repo>/bench.py --copy-probe\n"
+            f"    rocprofv3 --pmc {' '.join(TRAFFIC_WR)} --output-format csv -d <copy_wr> -- python3 <repo>/bench.py --copy-probe\n"
+            f"    python3 bench.py --workload {name} --traffic-summary <pf_rd> <pf_wr> <copy_rd> <copy_wr>\n\n"
+            "L2-to-memory bytes per launch (medians over the dispatches, the same byte counts and\n"
+            "copy-probe scaling as the decode scan's summary), in MB:\n\n"
+            "| kernel | read | write |\n|---|---|---|\n" + table +
+            f"\nAttention stage (the first five rows) per step: {total / 1e6:.1f} MB.  Copy-probe factors "
+            f"{f_rd:.3f} (reads), {f_wr:.3f} (writes).  sha256 of {', '.join(STAGE_SOURCES)}: "
+            f"`{res['source_sha256'][:16]}...`\n")
+    print(json.dumps(res))
+
+
 def measured_traffic(name):
-    """The calibrated scan traffic per launch of decode workload ``name``,
-    while the scan's sources are the ones it was measured on; else None."""
+    """The calibrated roofline traffic per launch of workload ``name`` (decode:
+    the index scan; prefill: the attention stage per step), while the sources
+    are the ones it was measured on; else None."""
     try:
         with open(traffic_json(name)) as f:
             t = json.load(f)
     except OSError:
         return None
-    if t.get("source_sha256") != scan_source_hash():
+    from synth import workload
+    names = SCAN_SOURCES if workload(name)["kind"] == "decode" else STAGE_SOURCES
+    if t.get("source_sha256") != source_hash(names):
         return None
     return t["traffic_bytes_per_launch"]
 
@@ -568,7 +631,7 @@ def measure_prefill(args, name, headline):
     dominant = "attention" if attn_ms >= score_ms else "score"
     roof = {"kernel": "prefill attention stage (k2q lists, key-major MFMA tiles, combine)",
             "bound": "mfma", "achieved": attn_tf, "peak": peak, "unit": "TFLOP/s",
-            "frac": attn_tf / peak, "traffic": None, "flops_per_launch": f_attn,
+            "frac": attn_tf / peak, "traffic": measured_traffic(name), "flops_per_launch": f_attn,
             "ms_per_launch": attn_ms} if dominant == "attention" else \
            {"kernel": "prefill_score_kernel (causal index-score GEMM)", "bound": "mfma",
             "achieved": score_tf, "peak": peak, "unit": "TFLOP/s", "frac": score_tf / peak,

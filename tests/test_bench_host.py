@@ -22,9 +22,9 @@ def test_measured_traffic_only_for_the_measured_sources(monkeypatch):
     import bench
     with open(os.path.join(ROOT, "profiles", "decode_b32_l32k_scan_hbm_traffic.json")) as f:
         stored = json.load(f)
-    monkeypatch.setattr(bench, "scan_source_hash", lambda: stored["source_sha256"])
+    monkeypatch.setattr(bench, "source_hash", lambda names=None: stored["source_sha256"])
     assert bench.measured_traffic("decode_b32_l32k") == stored["traffic_bytes_per_launch"]
-    monkeypatch.setattr(bench, "scan_source_hash", lambda: "0" * 64)
+    monkeypatch.setattr(bench, "source_hash", lambda names=None: "0" * 64)
     assert bench.measured_traffic("decode_b32_l32k") is None
     # a workload whose scan traffic was never measured reports none
     assert bench.measured_traffic("decode_b2_l2048") is None
