@@ -892,18 +892,6 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
   }
 
   const bool key_major = prefill_key_major(p, num_seqs, num_q_tokens);
-  if (key_major) {
-    st = hip_status(msa::launch_fill_u32(reinterpret_cast<uint32_t*>(w + l.counts),
-                                         2 * int64_t(num_seqs) * p.num_idx_heads * max_blocks,
-                                         0u, s),
-                    "list reset launch");
-    if (st != MSA_OK) return st;
-  } else if (l.nsplit_max > 1) {
-    st = hip_status(msa::launch_fill_u32(reinterpret_cast<uint32_t*>(w + l.tickets),
-                                         int64_t(num_q_tokens) * p.num_kv_heads, 0u, s),
-                    "ticket reset launch");
-    if (st != MSA_OK) return st;
-  }
   // 1. scores (short chunks: page scan, several queries per pass; long
   //    chunks: causal GEMM with a block-max epilogue)
   if (short_chunks(num_seqs, num_q_tokens)) {
@@ -919,9 +907,17 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
                     "prefill score launch");
   }
   if (st != MSA_OK) return st;
-  // 2. per-token selection
-  const msa::SelectArgs sa = select_args(p, scores, max_blocks, seq_lens, cu_seqlens_q, num_seqs,
-                                         num_q_tokens, sel, cnt);
+  // 2. per-token selection; its workgroups also clear the k2q list counts
+  //    (key-major attention) or the split tickets (per-token attention)
+  msa::SelectArgs sa = select_args(p, scores, max_blocks, seq_lens, cu_seqlens_q, num_seqs,
+                                   num_q_tokens, sel, cnt);
+  if (key_major) {
+    sa.zero_words = reinterpret_cast<uint32_t*>(w + l.counts);
+    sa.zero_count = 2 * int64_t(num_seqs) * p.num_idx_heads * max_blocks;
+  } else if (l.nsplit_max > 1) {
+    sa.zero_words = reinterpret_cast<uint32_t*>(w + l.tickets);
+    sa.zero_count = int64_t(num_q_tokens) * p.num_kv_heads;
+  }
   st = hip_status(launch_selection(sa, s), "prefill select launch");
   if (st != MSA_OK) return st;
   // 3. attention over each token's selection

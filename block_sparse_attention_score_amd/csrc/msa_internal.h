@@ -66,6 +66,10 @@ struct SelectArgs {
   int32_t forced_in_budget;  // forced blocks count inside topk
   int32_t* sel;
   int32_t* cnt;
+  // words the launch clears for the kernels after it (the prefill's k2q list
+  // counts or split tickets), nullptr for none
+  uint32_t* zero_words;
+  int64_t zero_count;
 };
 
 // Decode split-K attention with a fused log-sum-exp combine.
@@ -217,6 +221,14 @@ hipError_t launch_prefill_score(const PrefillScoreArgs& a, int idx_dim, int scor
                                 hipStream_t s);
 bool select_wave_fits(int max_blocks);
 hipError_t launch_select_wave(const SelectArgs& a, hipStream_t s);
+// Grid-stride clear of a.zero_words (every workgroup of a selection launch
+// calls it first).
+__device__ __forceinline__ void clear_words(const SelectArgs& a) {
+  const int64_t n = a.zero_count;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    a.zero_words[i] = 0u;
+}
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t s);
 hipError_t launch_decode_attend(const AttendArgs& a, int q_dtype, int kv_dtype,
                                 int group, hipStream_t s);

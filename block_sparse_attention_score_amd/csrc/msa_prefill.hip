@@ -281,6 +281,7 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
 // blocks (select_wave).
 template <int E>
 __global__ __launch_bounds__(kWgThreads) void select_wave_kernel(SelectArgs a) {
+  if (a.zero_words != nullptr) clear_words(a);
   const int lane = threadIdx.x & (kWave - 1);
   const int row = blockIdx.x * (kWgThreads / kWave) + threadIdx.x / kWave;
   if (row >= a.num_tokens * a.hidx) return;

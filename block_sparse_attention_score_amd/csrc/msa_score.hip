@@ -36,6 +36,7 @@ __global__ __launch_bounds__(kWgThreads) void multi_score_kernel(ScoreArgs a) {
 template <int MAXPER>
 __global__ __launch_bounds__(kWgThreads) void select_kernel(SelectArgs a) {
   __shared__ SelectLds sl;
+  if (a.zero_words != nullptr) clear_words(a);
   const int rowi = blockIdx.x;
   const int t = rowi / a.hidx;
   int b, p;
