@@ -11,11 +11,15 @@
 // i) and index head h, score[i][j] = max over tokens t <= p_i of block j of
 // q_idx[i] . k_idx[t].  A workgroup takes 256 query rows (4 waves x 64) and a
 // run of key blocks; the query rows stay in registers as MFMA B operands; each
-// key block (128 tokens x Di) is staged once in LDS (double-buffered, rows
-// padded against bank conflicts) and read by all four waves as A operands of
-// v_mfma_f32_16x16x32_bf16, so each result tile is S^T (tokens down, queries
-// across) and a lane folds its four tokens per tile into its query's maximum
-// with no cross-lane step until the block ends.  Blocks that end before a
+// key block (128 tokens x Di) is staged once in LDS by direct-to-LDS buffer
+// loads (each lane's 16 bytes land at the instruction's LDS base + 16 lane;
+// the chunks of a row XOR-swizzled so that fragment reads do not conflict)
+// and read by all four waves as A operands of v_mfma_f32_16x16x32_bf16, so
+// each result tile is S^T (tokens down, queries across) and a lane folds its
+// four tokens per tile into its query's maximum with no cross-lane step until
+// the block ends.  With no staging registers the kernel fits 128 VGPRs and one
+// 32 KB buffer, so four workgroups share a CU and each one's wait for its
+// next block is covered by the others' MFMAs.  Blocks that end before a
 // wave's first query skip the causal mask.  The mean and log-sum-exp block
 // scores use the same tiles: a lane sums (or exp-accumulates) its tokens and
 // the four lanes of a query column combine at the block's end.
@@ -27,23 +31,16 @@ namespace msa {
 
 constexpr int kPrefillRows = 256;  // query rows per scoring workgroup
 
+// (four workgroups per CU need at most 128 VGPRs; the log-sum-exp reducer at
+// Di = 128 needs more and runs two per CU instead of spilling)
 template <int DI, int ST>
-__global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillScoreArgs a) {
+__global__ __launch_bounds__(kWgThreads, (ST == kScoreLse && DI == 128) ? 2 : 4) void
+prefill_score_kernel(PrefillScoreArgs a) {
   constexpr int KS = DI / 32;              // 32-dim k-steps
-  // padded LDS row: at Di = 128 a 288-byte row keeps the 16-byte fragment
-  // reads of 16 rows free of bank conflicts on gfx950 (272 bytes: a fifth
-  // more LDS cycles, measured)
-  constexpr int ROW_BYTES = DI == 128 ? DI * 2 + 32 : DI * 2 + 16;
-  constexpr int CHUNKS = DI * 2 / 16;      // 16-byte chunks per key row
-  constexpr int LOADS = 128 * CHUNKS / kWgThreads;  // per thread per block
-  __shared__ __attribute__((aligned(16))) char kbuf[2][128 * ROW_BYTES];
-
-  // workgroup -> (key-block run, 256-row query tile): a run (sequence, index
-  // head, chunk of 16 key blocks) goes to XCD run % 8, whose workgroups
-  // (blockIdx x, x + 8, ...) take its query tiles one after another, so the
-  // tiles reading the same 16 key blocks run together on one L2.  The tiles
-  // are counted for the longest possible sequence (all tokens); those past a
-  // sequence's new tokens exit at once.
+  constexpr int CH = DI * 2 / 16;          // 16-byte chunks per key row
+  constexpr int RPI = kWave / CH;          // rows per direct-to-LDS instruction
+  constexpr int NI = kBlock / RPI / 4;     // instructions per wave per block
+  __shared__ __attribute__((aligned(16))) uint16_t kb[kBlock * DI];
   const int runs = a.num_seqs * a.hidx * a.kchunks;
   const int xl = blockIdx.x >> 3;
   const int qt = xl % a.max_tiles;
@@ -69,12 +66,10 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int w = tid / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
 
-  // B operands of S^T = K Q^T: this wave's 64 query rows as columns (4 column
-  // tiles of 16); lane holds dims 32s + 8*q4 .. +8 of query row l16 of tile rt.
   bf16x8_t qb[4][KS];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
@@ -90,51 +85,11 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
       }
     }
   }
-  // Position of this wave's first query row: a block ending at or before it
-  // is visible to all 64 rows and needs no causal mask.
-  const int pos_w0 = prefix + i0 + 64 * __builtin_amdgcn_readfirstlane(w);
-
-  // (the table is read through the constant address space: scalar loads,
-  // off the vector memory counter, whatever the stores below may alias)
+  const int pos_w0 = prefix + i0 + 64 * w;
   const __attribute__((address_space(4))) int32_t* bt_row =
       (const __attribute__((address_space(4))) int32_t*)(
           reinterpret_cast<uintptr_t>(a.block_table + static_cast<int64_t>(b) * a.max_blocks));
-  auto page_of = [&](int j) { return bt_row[j]; };
-  // (32-bit page bound, so the checks below stay on the scalar unit)
   const int np32 = static_cast<int>(a.num_pages < 0x7fffffff ? a.num_pages : 0x7fffffff);
-  // A key block is one contiguous run of 128 * Di bf16; thread chunk
-  // c = tid + 256 k sits at byte 16 c of it.  Buffer loads: the run's base in
-  // a scalar descriptor, the lane offset 16 tid loop-invariant, 4096 k as the
-  // scalar offset, so a fetch computes no vector addresses.
-  auto block_rsrc = [&](int j) {
-    int page = page_of(j);
-    if (page < 0 || page >= np32) page = 0;  // never read: the block scores -inf
-    return __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(reinterpret_cast<const char*>(a.idx_k)) +
-            (static_cast<int64_t>(page) * a.hidx + h) * kBlock * DI * 2,
-        0, kBlock * DI * 2, 0x00020000);
-  };
-  // Two register sets take turns holding a block in flight, so each block's
-  // loads are issued two blocks ahead of its use.  Every iteration issues one
-  // block of loads (past the last block the clamped index re-reads it), so
-  // the wait before staging covers exactly the block it stages.
-  typedef uint4 Stage[LOADS];
-  const int lane_off = 16 * tid;
-  auto fetch = [&](int j, Stage& st) {
-    const auto r = block_rsrc(min(j, j1 - 1));
-#pragma unroll
-    for (int k = 0; k < LOADS; ++k) {
-      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, 16 * kWgThreads * k, 0);
-      st[k] = uint4{v.x, v.y, v.z, v.w};
-    }
-  };
-  // Scores of this tile's rows through a buffer descriptor whose range ends
-  // at the sequence's last new token: stores of rows past it are dropped by
-  // the range check.  The scores stay in registers until the run ends: lane
-  // q4 of a query column keeps blocks j0 + 4 q4 .. + 3 (-inf past the
-  // tile's last block), and the four lanes of the column then write the
-  // row's 64 bytes of the run with one store (single 4-byte stores per block
-  // reached memory as partial lines, several times the scores' bytes).
   const int rows = min(nq - i0, kPrefillRows);
   const auto srsrc = __builtin_amdgcn_make_buffer_rsrc(
       a.scores + (static_cast<int64_t>(cu0 + i0) * a.hidx + h) * a.max_blocks, 0,
@@ -148,50 +103,63 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
 #pragma unroll
     for (int e = 0; e < 4; ++e) sv[rt][e] = -INFINITY;
 
-  // Staging into LDS: thread chunk c = tid + 256 k is row c / CHUNKS, bytes
-  // 16 (c % CHUNKS) of the block (rows padded to ROW_BYTES).
-  auto store = [&](int buf, const Stage& st) {
-#pragma unroll
-    for (int k = 0; k < LOADS; ++k) {
-      const int c = tid + kWgThreads * k;
-      *reinterpret_cast<uint4*>(&kbuf[buf][(c / CHUNKS) * ROW_BYTES + 16 * (c % CHUNKS)]) = st[k];
-    }
-  };
-
-  // 16 tokens x 64 queries of S^T for token tile n: lane holds tokens
-  // 16n + 4*q4 + r of query column 16rt + l16.
-  auto tile = [&](int buf, int n, f32x4_t (&acc)[4]) {
+  // Chunk c of key row r sits at chunk swz(c, r): 16 rows of a fragment read
+  // then hit 16 distinct 16-byte bank groups (Di = 128: 256-byte rows, XOR
+  // with r mod 16; Di = 64: 128-byte rows, two per bank group, XOR with
+  // (r / 2) mod 8).
+  auto swz = [](int c, int r) { return DI == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7)); };
+  auto tile = [&](int n, f32x4_t (&acc)[4]) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(
-          &kbuf[buf][(16 * n + l16) * ROW_BYTES + 2 * (32 * s + 8 * q4)]);
+          &kb[(16 * n + l16) * DI + 8 * swz(4 * s + q4, 16 * n + l16)]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
         acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[rt][s], acc[rt], 0, 0, 0);
     }
   };
 
-  // Block j from LDS buffer buf; `next` holds block j+1 (in flight), `spare`
-  // receives block j+2.
-  auto step = [&](int j, int buf, Stage& next, Stage& spare) {
-    fetch(j + 2, spare);
-    const int pg = page_of(j);
+  for (int j = j0; j < j1; ++j) {
+    const int pg = bt_row[j];
     const bool page_ok = pg >= 0 && pg < np32;
-
-    float mx[4];  // per query column: max over this lane's tokens
+    {
+      // (LDS pointers cast in place: a helper returning an LDS pointer type
+      // would not compile for the host side; source offsets from a fresh
+      // thread index, so they are not kept live across the loop)
+      const auto r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(reinterpret_cast<const char*>(a.idx_k)) +
+              (static_cast<int64_t>(page_ok ? pg : 0) * a.hidx + h) * kBlock * DI * 2,
+          0, page_ok ? kBlock * DI * 2 : 0, 0x00020000);
+      int tl = tid;
+      asm volatile("" : "+v"(tl));
+      const int ln = tl & (kWave - 1);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row0 = RPI * (NI * w + i);
+        const int row = row0 + ln / CH;
+        const int cp = ln % CH;
+        // (the offset goes through a local: written into the builtin's
+        // argument list, the swizzle call made the host side of the kernel
+        // drop its launch stub)
+        const int off = row * DI * 2 + 16 * swz(cp, row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(kb + row0 * DI), 16, off, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    float mx[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) mx[rt] = -INFINITY;
     if constexpr (ST != kScoreMax) {
-      // mean or log-sum-exp: each lane reduces its own tokens of a column,
-      // then the four lanes of the column combine
       BlockScore<ST> red[4];
       if (page_ok) {
         const bool full = kBlock * j + kBlock - 1 <= pos_w0;
         for (int n = 0; n < 8; ++n) {
           f32x4_t acc[4];
-          tile(buf, n, acc);
+          tile(n, acc);
           const int tok = kBlock * j + 16 * n + 4 * q4;
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt) {
@@ -213,7 +181,7 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
 #pragma unroll 2
       for (int n = 0; n < 8; ++n) {
         f32x4_t acc[4];
-        tile(buf, n, acc);
+        tile(n, acc);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
           mx[rt] = max_nan(max_nan(max_nan(max_nan(mx[rt], acc[rt][0]), acc[rt][1]), acc[rt][2]),
@@ -223,7 +191,7 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
 #pragma unroll 2
       for (int n = 0; n < 8; ++n) {
         f32x4_t acc[4];
-        tile(buf, n, acc);
+        tile(n, acc);
         const int tok = kBlock * j + 16 * n + 4 * q4;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -240,25 +208,15 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
         mx[rt] = max_nan(mx[rt], __shfl_xor(mx[rt], 32));
       }
     }
-    if (j + 1 < j1) store(buf ^ 1, next);
     const int jj = j - j0;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) sv[rt][e] = jj == 4 * q4 + e ? mx[rt] : sv[rt][e];
+    // every wave is done with the buffer before the next block overwrites it
     __syncthreads();
-  };
-
-  Stage sa, sb;
-  fetch(j0, sb);
-  store(0, sb);
-  fetch(j0 + 1, sa);
-  __syncthreads();
-  for (int j = j0; j < j1; j += 2) {
-    step(j, 0, sa, sb);
-    if (j + 1 < j1) step(j + 1, 1, sb, sa);
   }
-  const int jb = 4 * q4;  // this lane's blocks j0 + jb .. + 3
+  const int jb = 4 * q4;
   if (j0 + kPrefillBlocksPerChunk <= a.max_blocks) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
@@ -266,7 +224,7 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
                          __float_as_uint(sv[rt][2]), __float_as_uint(sv[rt][3])};
       __builtin_amdgcn_raw_buffer_store_b128(v, srsrc, srow[rt] + 4 * jb, 4 * j0, 0);
     }
-  } else {  // the row's last run: only blocks below max_blocks
+  } else {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -276,6 +234,7 @@ __global__ __launch_bounds__(kWgThreads, 2) void prefill_score_kernel(PrefillSco
                                                 srow[rt] + 4 * (jb + e), 4 * j0, 0);
   }
 }
+
 
 // One wavefront per (query token, index head) row, for rows of up to 64 * E
 // blocks (select_wave).
