@@ -273,10 +273,11 @@ def _gather_rows_raw(pool: np.ndarray, bt_row: np.ndarray, head: int, n_tokens: 
 def _gather_values(pool: np.ndarray, bt_row: np.ndarray, head: int, n_tokens: int, dtype: str,
                    scale: float, D: int) -> np.ndarray:
     """Values (float64) of rows 0..n_tokens-1 of one head of a sequence."""
-    if dtype == "mxfp4":
+    if dtype in ("mxfp4", "mxfp6"):
         nbk = (n_tokens + BLOCK - 1) // BLOCK
         pages = np.asarray(bt_row[:nbk], dtype=np.int64)
-        vals = mxfp4_decode_runs(pool[pages, head], D, scale)
+        dec = mxfp4_decode_runs if dtype == "mxfp4" else mxfp6_decode_runs
+        vals = dec(pool[pages, head], D, scale)
         return vals.reshape(nbk * BLOCK, D)[:n_tokens]
     return decode(_gather_rows_raw(pool, bt_row, head, n_tokens), dtype, scale)
 
@@ -510,6 +511,9 @@ def append_kv(k_pool, v_pool, idx_k_pool, k_new, v_new, idx_k_new, slots, *,
         if kv_dtype == "mxfp4":
             for pool, new, sc in ((k_pool, k_new, k_scale), (v_pool, v_new, v_scale)):
                 _store_mxfp4_row(pool, page, off, new[t], kv_src, sc)
+        elif kv_dtype == "mxfp6":
+            for pool, new, sc in ((k_pool, k_new, k_scale), (v_pool, v_new, v_scale)):
+                _store_mxfp6_row(pool, page, off, new[t], kv_src, sc)
         else:
             k_pool[page, :, off, :] = store_values(k_new[t], kv_src, kv_dtype, k_scale)
             v_pool[page, :, off, :] = store_values(v_new[t], kv_src, kv_dtype, v_scale)
@@ -529,6 +533,17 @@ def _store_mxfp4_row(pool, page, off, new_row, src, scale):
     D = new_row.shape[-1]
     nc = BLOCK * D // 2
     pool[page, :, off * D // 2:(off + 1) * D // 2] = codes
+    pool[page, :, nc + off * D // MXFP4_GROUP:nc + (off + 1) * D // MXFP4_GROUP] = sc
+
+
+def _store_mxfp6_row(pool, page, off, new_row, src, scale):
+    """One token's rows [H, D] (bf16 bits) into an MX-fp6 pool: the float32
+    quotient x / scale encoded per group of 32 (mxfp6_encode_rows)."""
+    x32 = decode(new_row, src).astype(np.float32) / np.float32(scale)
+    codes, sc = mxfp6_encode_rows(x32)
+    D = new_row.shape[-1]
+    nc = BLOCK * D * 3 // 4
+    pool[page, :, off * D * 3 // 4:(off + 1) * D * 3 // 4] = codes
     pool[page, :, nc + off * D // MXFP4_GROUP:nc + (off + 1) * D // MXFP4_GROUP] = sc
 
 
@@ -661,5 +676,103 @@ def mxfp4_encode_rows(x32: np.ndarray):
 def mxfp4_encode_run_rows(x32: np.ndarray):
     """Convenience: [..., 128, D] float32 -> [..., run bytes] (codes, then scales)."""
     codes, sc = mxfp4_encode_rows(x32)
+    lead = codes.shape[:-2]
+    return np.concatenate([codes.reshape(lead + (-1,)), sc.reshape(lead + (-1,))], axis=-1)
+
+
+# --------------------------------------------------------------------------
+# MX-fp6 K/V pools
+# --------------------------------------------------------------------------
+#
+# The other microscaling width gfx950 converts in hardware, beside MX-fp4:
+# OCP FP6 E2M3 element codes (s.ee.mmm, exponent bias 1; exponent field 0
+# encodes the subnormal m / 8; the largest value 7.5; no infinities or NaN)
+# with an E8M0 scale per 32 consecutive elements.  A group's 32 codes pack
+# into 24 bytes, element i at bits 6 i .. 6 i + 5 of the group read as one
+# little-endian number.  Pool layout per (page, head): the 128 x D x 3 / 4
+# code bytes, then the 128 x D / 32 scale bytes; k_scale / v_scale multiply
+# on top.
+
+def fp6_e2m3_table() -> np.ndarray:
+    """Values of the 64 E2M3 codes."""
+    tab = np.empty(64, dtype=np.float64)
+    for code in range(64):
+        sign = -1.0 if code & 0x20 else 1.0
+        e = (code >> 3) & 0x3
+        m = code & 0x7
+        tab[code] = sign * (m / 8.0 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 1))
+    return tab
+
+
+def mxfp6_run_bytes(D: int) -> int:
+    return BLOCK * D * 3 // 4 + BLOCK * D // MXFP4_GROUP
+
+
+def fp6_pack(codes: np.ndarray) -> np.ndarray:
+    """[..., D] codes (0..63) -> [..., 3 D / 4] bytes: every four codes are
+    three bytes, c0 | c1 << 6 | c2 << 12 | c3 << 18 little-endian."""
+    c = np.asarray(codes, dtype=np.uint32).reshape(codes.shape[:-1] + (-1, 4))
+    v = c[..., 0] | (c[..., 1] << 6) | (c[..., 2] << 12) | (c[..., 3] << 18)
+    b = np.stack([v & 0xFF, (v >> 8) & 0xFF, (v >> 16) & 0xFF], axis=-1)
+    return b.reshape(codes.shape[:-1] + (-1,)).astype(np.uint8)
+
+
+def fp6_unpack(packed: np.ndarray) -> np.ndarray:
+    """Inverse of fp6_pack."""
+    b = np.asarray(packed, dtype=np.uint32).reshape(packed.shape[:-1] + (-1, 3))
+    v = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16)
+    c = np.stack([(v >> (6 * i)) & 0x3F for i in range(4)], axis=-1)
+    return c.reshape(packed.shape[:-1] + (-1,)).astype(np.uint8)
+
+
+def mxfp6_decode_runs(runs: np.ndarray, D: int, scale: float = 1.0) -> np.ndarray:
+    """[..., run bytes] uint8 -> [..., 128, D] float64 values times scale."""
+    runs = np.asarray(runs, dtype=np.uint8)
+    nc = BLOCK * D * 3 // 4
+    codes = fp6_unpack(runs[..., :nc].reshape(runs.shape[:-1] + (BLOCK, D * 3 // 4)))
+    sc = runs[..., nc:].reshape(runs.shape[:-1] + (BLOCK, D // MXFP4_GROUP))
+    el = fp6_e2m3_table()[codes]
+    s = e8m0_table()[sc]
+    return el * np.repeat(s, MXFP4_GROUP, axis=-1) * float(scale)
+
+
+def fp6_e2m3_encode(y: np.ndarray) -> np.ndarray:
+    """Magnitudes to E2M3 codes: nearest of the 32 values, an exact tie to the
+    even mantissa, clamped at 7.5; the sign is kept (-0 -> 0x20)."""
+    y = np.asarray(y, dtype=np.float64)
+    tab = fp6_e2m3_table()[:32]
+    mag = np.minimum(np.abs(np.where(np.isnan(y), 0.0, y)), 7.5)
+    dist = np.abs(mag[..., None] - tab)
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best
+    even = cand & ((np.arange(32) & 1) == 0)
+    pick = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    return (pick | np.where(np.signbit(y), 0x20, 0)).astype(np.uint8)
+
+
+def mxfp6_encode_rows(x32: np.ndarray):
+    """Rows [..., D] of float32 values -> (packed codes [..., 3 D / 4], scale
+    codes [..., D / 32]) by the OCP rule: per group of 32, the shared exponent
+    floor(log2(max |x|)) - 2 (2 being E2M3's largest exponent), clamped to the
+    E8M0 range (an all-zero group takes code 0); every element encoded as
+    x / 2^exponent; a group holding a NaN gets the NaN scale code and zero
+    codes."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    D = x.shape[-1]
+    g = x.reshape(x.shape[:-1] + (D // MXFP4_GROUP, MXFP4_GROUP))
+    nan = np.isnan(g).any(axis=-1)
+    amax = np.max(np.abs(np.where(np.isnan(g), 0.0, g)), axis=-1)
+    _, e = np.frexp(amax)
+    k = np.where(amax > 0, e - 1 - 2, -127)
+    sc = np.clip(k + 127, 0, 254)
+    X = np.ldexp(1.0, (sc - 127).astype(np.int64))
+    codes = fp6_e2m3_encode(g / X[..., None]).reshape(x.shape)
+    codes = np.where(np.repeat(nan, MXFP4_GROUP, axis=-1), np.uint8(0), codes)
+    return fp6_pack(codes), np.where(nan, 255, sc).astype(np.uint8)
+
+
+def mxfp6_encode_run_rows(x32: np.ndarray):
+    """Convenience: [..., 128, D] float32 -> [..., run bytes] (codes, then scales)."""
+    codes, sc = mxfp6_encode_rows(x32)
     lead = codes.shape[:-2]
     return np.concatenate([codes.reshape(lead + (-1,)), sc.reshape(lead + (-1,))], axis=-1)

@@ -93,6 +93,10 @@ WORKLOADS = {
     "decode_mxfp4_b32_l64k": dict(
         kind="decode", B=32, seq_lens=("fixed", 65536), Hq=16, Hkv=2, Hidx=2,
         D=128, Di=128, topk=32, init=1, local=2, q="bf16", kv="mxfp4", idx="bf16"),
+    # MX-fp6 (E2M3) K/V pools, same shape
+    "decode_mxfp6_b32_l64k": dict(
+        kind="decode", B=32, seq_lens=("fixed", 65536), Hq=16, Hkv=2, Hidx=2,
+        D=128, Di=128, topk=32, init=1, local=2, q="bf16", kv="mxfp6", idx="bf16"),
 }
 
 # Seeds of the workloads, in the order above.
@@ -121,7 +125,35 @@ def _mxfp4_runs(y: torch.Tensor) -> torch.Tensor:
     code = (code | (torch.signbit(g).to(torch.int32) << 3)).reshape(n, H, T, D)
     packed = (code[..., 0::2] | (code[..., 1::2] << 4)).to(torch.uint8)
     return torch.cat([packed.reshape(n, H, -1), sc.to(torch.uint8).reshape(n, H, -1)], dim=-1)
-_POISON_KV = {"bf16": float("nan"), "f32": float("nan"), "mxfp4": 0.0}
+
+
+def mxfp6_run_bytes(D: int) -> int:
+    return BLOCK * D * 3 // 4 + BLOCK * D // MX_GROUP
+
+
+def _mxfp6_runs(y: torch.Tensor) -> torch.Tensor:
+    """[n, H, 128, D] float32 -> [n, H, run bytes] uint8: E2M3 codes packed four
+    to three bytes (element i of a 32-group at bits 6 i of its 24 bytes, little
+    endian), then the E8M0 scales."""
+    n, H, T, D = y.shape
+    g = y.reshape(n, H, T, D // MX_GROUP, MX_GROUP)
+    amax = g.abs().amax(dim=-1)
+    _, e = torch.frexp(amax)
+    k = torch.where(amax > 0, e - 3, torch.full_like(e, -127))
+    sc = (k + 127).clamp(0, 254)
+    a = torch.ldexp(g, (127 - sc).unsqueeze(-1)).abs().clamp(max=7.5)
+    step = torch.where(a < 2.0, 0.125, torch.where(a < 4.0, 0.25, 0.5))
+    v = torch.round(a / step) * step                      # half to even
+    code = torch.where(v < 2.0, v * 8, torch.where(v < 4.0, 8 + v * 4, 16 + v * 2))
+    code = (code.to(torch.int32) | (torch.signbit(g).to(torch.int32) << 5)).reshape(n, H, T, D // 4, 4)
+    w = code[..., 0] | (code[..., 1] << 6) | (code[..., 2] << 12) | (code[..., 3] << 18)
+    packed = torch.stack([w & 0xFF, (w >> 8) & 0xFF, (w >> 16) & 0xFF], dim=-1).to(torch.uint8)
+    return torch.cat([packed.reshape(n, H, -1), sc.to(torch.uint8).reshape(n, H, -1)], dim=-1)
+
+
+_MX_RUN_BYTES = {"mxfp4": mxfp4_run_bytes, "mxfp6": mxfp6_run_bytes}
+_MX_RUNS = {"mxfp4": _mxfp4_runs, "mxfp6": _mxfp6_runs}
+_POISON_KV = {"bf16": float("nan"), "f32": float("nan"), "mxfp4": 0.0, "mxfp6": 0.0}
 FP8_NAN_BYTE = 0x7F
 IDX_POISON = 1.0e4
 
@@ -199,8 +231,8 @@ def _quantise(x: torch.Tensor, dtype: str, scale: float) -> torch.Tensor:
 
 
 def _draw_pool(P, H, Dm, dtype, scale, g, device) -> torch.Tensor:
-    if dtype == "mxfp4":
-        pool = torch.empty((P, H, mxfp4_run_bytes(Dm)), dtype=torch.uint8, device=device)
+    if dtype in _MX_RUNS:
+        pool = torch.empty((P, H, _MX_RUN_BYTES[dtype](Dm)), dtype=torch.uint8, device=device)
     else:
         out_dt = torch.uint8 if dtype.startswith("fp8") else _TORCH_DT[dtype]
         pool = torch.empty((P, H, BLOCK, Dm), dtype=out_dt, device=device)
@@ -208,8 +240,8 @@ def _draw_pool(P, H, Dm, dtype, scale, g, device) -> torch.Tensor:
         p1 = min(P, p0 + PAGE_CHUNK)
         x = torch.randn((p1 - p0, H, BLOCK, Dm), generator=g, device=device,
                         dtype=torch.float32)
-        if dtype == "mxfp4":
-            pool[p0:p1] = _mxfp4_runs(x / scale)
+        if dtype in _MX_RUNS:
+            pool[p0:p1] = _MX_RUNS[dtype](x / scale)
         else:
             pool[p0:p1] = _quantise(x, dtype, scale)
     return pool
@@ -219,9 +251,11 @@ def _poison(pool: torch.Tensor, valid: torch.Tensor, dtype: str, value: float):
     """Overwrite token slots ``t >= valid[page]`` of every page."""
     tok = torch.arange(BLOCK, device=pool.device)
     bad = tok[None, :] >= valid.to(pool.device)[:, None]          # [P,128]
-    if dtype == "mxfp4":
-        # the NaN scale code (0xFF) for every group of the slot
-        D = pool.shape[-1] // (BLOCK // 2 + BLOCK // MX_GROUP)   # run = 128 D / 2 + 128 D / 32
+    if dtype in _MX_RUNS:
+        # the NaN scale code (0xFF) for every group of the slot; the run is
+        # 128 D / 2 (fp4) or 128 D 3 / 4 (fp6) code bytes, then 128 D / 32 scales
+        per_d = BLOCK // 2 if dtype == "mxfp4" else BLOCK * 3 // 4
+        D = pool.shape[-1] // (per_d + BLOCK // MX_GROUP)
         nsc = D // MX_GROUP
         sc = pool[:, :, pool.shape[-1] - BLOCK * nsc:].view(pool.shape[0], pool.shape[1], BLOCK, nsc)
         sc.masked_fill_(bad[:, None, :, None].expand(sc.shape), 0xFF)

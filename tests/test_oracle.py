@@ -839,10 +839,12 @@ def test_e8m0_table_matches_torch_all_codes():
     assert np.array_equal(mine[:255], ref[:255])
 
 
-def _brute_group(x):
+def _brute_group(x, tab=None, maxv=6.0):
     """One group of 32 float32 values, brute force: the largest k with
     2^k <= max|x| (by repeated doubling), scale 2^(k-2) (clamped to the E8M0
-    range), and per element the E2M1 code nearest to x / scale among all 16,
+    range; 2 is the largest exponent of E2M1 and of E2M3 alike), and per
+    element the code nearest to x / scale among all of the element format's
+    codes (E2M1 by default; the upper half of the codes are the negatives),
     ties to the even code."""
     amax = max(abs(float(v)) for v in x)
     if amax == 0:
@@ -855,12 +857,13 @@ def _brute_group(x):
             k -= 1
         sc = min(max(k - 2 + 127, 0), 254)
     X = 2.0 ** (sc - 127)
-    tab = oracle.fp4_e2m1_table()
+    tab = oracle.fp4_e2m1_table() if tab is None else tab
+    n = len(tab)
     codes = []
     for v in x:
-        y = min(max(float(v) / X, -6.0), 6.0)
-        d = [abs(y - tab[c]) for c in range(16)]
-        sign_ok = [c for c in range(16) if (c >= 8) == (math.copysign(1.0, y) < 0)]
+        y = min(max(float(v) / X, -maxv), maxv)
+        d = [abs(y - tab[c]) for c in range(n)]
+        sign_ok = [c for c in range(n) if (c >= n // 2) == (math.copysign(1.0, y) < 0)]
         best = min(d[c] for c in sign_ok)
         cands = [c for c in sign_ok if d[c] == best]
         even = [c for c in cands if c % 2 == 0]
@@ -975,6 +978,170 @@ def test_mxfp4_append_oracle():
         page, off = divmod(int(s), 128)
         changed[page, :, off * D // 2:(off + 1) * D // 2] = True
         changed[page, :, 128 * D // 2 + off * 2:128 * D // 2 + off * 2 + 2] = True
+    assert np.array_equal(k2[~changed], k_pool[~changed])
+
+
+# ------------------------------------------------------------- MX-fp6 pools
+
+def test_e2m3_table_from_the_format():
+    """E2M3 (bias 1): exponent field 0 holds the subnormals m / 8, fields 1..3
+    the normals 2^(e-1) (1 + m / 8) up to 7.5; the sign bit negates.  The
+    normals are e4m3 values with the same mantissa bits and the exponent field
+    rebiased from 1 to 7 (e4m3 table pinned against torch's cast above)."""
+    tab = oracle.fp6_e2m3_table()
+    want = [m / 8 for m in range(8)] + [1 + m / 8 for m in range(8)] \
+        + [2 + m / 4 for m in range(8)] + [4 + m / 2 for m in range(8)]
+    assert list(tab[:32]) == want
+    assert tab[31] == 7.5 and tab[1] == 0.125 and tab[8] == 1.0
+    assert np.array_equal(tab[32:], -tab[:32]) and math.copysign(1.0, tab[32]) < 0
+    e4 = oracle.fp8_e4m3fn_table()
+    for c in range(64):
+        s, e, m = c >> 5, (c >> 3) & 3, c & 7
+        if e:
+            assert tab[c] == e4[(s << 7) | ((e + 6) << 3) | m], c
+
+
+def test_fp6_bit_order():
+    """Element i of a 32-group sits at bits 6 i .. 6 i + 5 of the group's 24
+    bytes read as one little-endian number: checked with a literal and with
+    Python's big integers on random codes."""
+    assert list(oracle.fp6_pack(np.array([1, 2, 3, 4]))) == [0x81, 0x30, 0x10]
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 64, (5, 32))
+    packed = oracle.fp6_pack(codes)
+    assert packed.shape == (5, 24)
+    for r in range(5):
+        v = int.from_bytes(bytes(packed[r].tolist()), "little")
+        assert [(v >> (6 * i)) & 63 for i in range(32)] == list(codes[r])
+    assert np.array_equal(oracle.fp6_unpack(packed), codes)
+
+
+def test_mxfp6_encoder_brute_force():
+    rng = np.random.default_rng(19)
+    groups = [rng.standard_normal(32).astype(np.float32) * np.float32(2.0 ** rng.integers(-6, 7))
+              for _ in range(40)]
+    tab = oracle.fp6_e2m3_table()
+    # exact midpoints between neighbouring codes (ties to the even code), and 7.5
+    mids = np.array([(tab[i] + tab[i + 1]) / 2 for i in range(31)] + [7.5], dtype=np.float32)
+    groups.append(mids)
+    groups.append(-mids)
+    groups.append(np.zeros(32, dtype=np.float32))
+    groups.append(np.array([7.9] + [0.01] * 31, dtype=np.float32))   # saturates at 7.5 * scale
+    groups.append(np.array([1e-39] * 32, dtype=np.float32))          # subnormal float32 group
+    x = np.stack(groups)
+    packed, sc = oracle.mxfp6_encode_rows(x)
+    codes = oracle.fp6_unpack(packed)
+    for gi, grp in enumerate(groups):
+        want_sc, want_codes = _brute_group(grp, tab, 7.5)
+        assert sc[gi, 0] == want_sc, gi
+        assert list(codes[gi]) == want_codes, gi
+
+
+def test_mxfp6_run_layout_and_round_trip():
+    """Run layout (codes of token t at bytes t * 3 D / 4 ..; scales after all
+    codes) and values of the form code * 2^k that come back exactly."""
+    D = 64
+    rng = np.random.default_rng(6)
+    tab = oracle.fp6_e2m3_table()
+    codes = rng.integers(0, 64, (128, D))
+    codes[:, ::32] = 31                      # every group holds a 7.5: scale = its 2^k
+    k = rng.integers(-4, 5, (128, D // 32))
+    vals = (tab[codes] * np.repeat(2.0 ** k, 32, axis=1)).astype(np.float32)
+    run = oracle.mxfp6_encode_run_rows(vals[None])[0]
+    assert run.shape == (oracle.mxfp6_run_bytes(D),) == (128 * D * 3 // 4 + 128 * D // 32,)
+    assert run[0] & 0x3F == codes[0, 0] and (run[0] >> 6 | (run[1] & 0xF) << 2) == codes[0, 1]
+    t0 = 5 * D * 3 // 4
+    v = int.from_bytes(bytes(run[t0 + 24:t0 + 48].tolist()), "little")
+    assert [(v >> (6 * i)) & 63 for i in range(32)] == list(codes[5, 32:])
+    assert run[128 * D * 3 // 4 + 2 * 9 + 1] == k[9, 1] + 127
+    dec = oracle.mxfp6_decode_runs(run[None], D)[0]
+    assert np.array_equal(dec, np.where(codes == 32, -0.0, vals.astype(np.float64)))
+    bad = run.copy()
+    bad[128 * D * 3 // 4] = 0xFF
+    dec = oracle.mxfp6_decode_runs(bad[None], D)[0]
+    assert np.isnan(dec[0, :32]).all() and not np.isnan(dec[0, 32:]).any()
+
+
+def test_mxfp6_synthetic_pools_follow_the_encoder():
+    """The generator's MX-fp6 pools are the oracle encoder's bytes of the same
+    float draws (the generator holds its own vectorised copy of the rule)."""
+    from synth.inputs import _mxfp6_runs
+    g = torch.Generator().manual_seed(10)
+    x = torch.randn((3, 2, 128, 128), generator=g) * 1.7
+    x[0, 0, 0, :32] = torch.tensor(np.array([(a + b) / 2 for a, b in zip(
+        oracle.fp6_e2m3_table()[:31], oracle.fp6_e2m3_table()[1:32])] + [7.5], dtype=np.float32))
+    mine = _mxfp6_runs(x).numpy()
+    ref = oracle.mxfp6_encode_run_rows(x.numpy())
+    assert np.array_equal(mine, ref)
+
+
+@pytest.mark.parametrize("prefill", [None, (100, 256)])
+def test_mxfp6_attention_dense_equivalence(prefill):
+    inp = _tiny_case(62, lens=(1000, 600), Hq=6, Hkv=3, Hidx=1, D=64, Di=8, topk=8,
+                     kv="mxfp6", prefill_new=prefill)
+    res = oracle.sparse_attention(inp)
+    q = torch.from_numpy(oracle.decode(inp["q"], "bf16"))
+    tab = oracle.fp6_e2m3_table()
+    for b, L in enumerate(inp["seq_lens"]):
+        L = int(L)
+        nbk = (L + 127) // 128
+        pages = inp["block_table"][b, :nbk].astype(np.int64)
+        kv = []
+        for pool in (inp["k_pool"], inp["v_pool"]):
+            # decoded here from the bit layout, independently of the oracle's reader
+            run = pool[pages]                                         # [nbk, H, bytes]
+            nc = 128 * 64 * 3 // 4
+            grp = run[..., :nc].reshape(nbk, 3, 128, 2, 24).astype(np.uint64)
+            vals = np.zeros((nbk, 3, 128, 2, 32))
+            for i in range(32):
+                byte, sh = divmod(6 * i, 8)
+                c = grp[..., byte] >> np.uint64(sh)
+                if sh > 2:
+                    c = c | (grp[..., byte + 1] << np.uint64(8 - sh))
+                vals[..., i] = tab[(c & np.uint64(63)).astype(np.int64)]
+            sc = run[..., nc:].reshape(nbk, 3, 128, 2).astype(np.float64)
+            kv.append(torch.from_numpy((vals * np.exp2(sc - 127)[..., None]).reshape(nbk, 3, 128, 64)))
+        k, v = kv
+        k = k.permute(1, 0, 2, 3).reshape(3, -1, 64)[:, :L].repeat_interleave(2, dim=0)
+        v = v.permute(1, 0, 2, 3).reshape(3, -1, 64)[:, :L].repeat_interleave(2, dim=0)
+        toks = [t for t, (bb, _) in enumerate(inp["_pos"]) if bb == b]
+        ps = torch.tensor([inp["_pos"][t][1] for t in toks])
+        mask = torch.arange(L)[None, :] <= ps[:, None]
+        o = torch.nn.functional.scaled_dot_product_attention(q[toks].permute(1, 0, 2), k, v,
+                                                             attn_mask=mask)
+        assert np.allclose(res["out"][toks], o.permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_mxfp6_append_oracle():
+    rng = np.random.default_rng(29)
+    P, H, D, T = 3, 2, 64, 4
+    run = oracle.mxfp6_run_bytes(D)
+    k_pool = rng.integers(0, 256, (P, H, run)).astype(np.uint8)
+    v_pool = rng.integers(0, 256, (P, H, run)).astype(np.uint8)
+    ik = np.zeros((P, 1, 128, 8), dtype=np.uint16)
+    xs = rng.standard_normal((T, H, D)).astype(np.float32)
+    bits = (xs.view(np.uint32) >> 16).astype(np.uint16)
+    new_ik = np.zeros((T, 1, 8), dtype=np.uint16)
+    slots = np.array([5, 130, -1, 383])
+    k2, v2, _ = oracle.append_kv(k_pool, v_pool, ik, bits, bits, new_ik, slots, kv_src="bf16",
+                                 kv_dtype="mxfp6", idx_dtype="bf16", k_scale=0.5, v_scale=2.0)
+    dk = oracle.mxfp6_decode_runs(k2, D, 0.5)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        page, off = divmod(int(s), 128)
+        x = oracle.decode(bits[t], "bf16")
+        err = np.abs(dk[page, :, off] - x)
+        # half a step of the top binade (a quarter of the scale), or the clamp
+        # from below 8 to 7.5 scales: at most max|x| / 8 per group
+        bound = np.repeat(np.abs(x).reshape(H, -1, 32).max(axis=-1), 32, axis=-1) / 8
+        assert (err <= bound + 1e-30).all()
+    nc = 128 * D * 3 // 4
+    changed = np.zeros((P, H, run), dtype=bool)
+    for s in slots[slots >= 0]:
+        page, off = divmod(int(s), 128)
+        changed[page, :, off * D * 3 // 4:(off + 1) * D * 3 // 4] = True
+        changed[page, :, nc + off * 2:nc + off * 2 + 2] = True
     assert np.array_equal(k2[~changed], k_pool[~changed])
 
 
