@@ -71,8 +71,9 @@ def parse():
 
 
 def elem_bytes(dt: str) -> float:
-    # MX-fp4: half a byte per element plus one scale byte per 32
-    return {"bf16": 2, "f32": 4, "fp8": 1, "fp8_e5m2": 1, "mxfp4": 17 / 32}[dt]
+    # MX-fp4 / MX-fp6: half a byte / three quarters of a byte per element,
+    # plus one scale byte per 32
+    return {"bf16": 2, "f32": 4, "fp8": 1, "fp8_e5m2": 1, "mxfp4": 17 / 32, "mxfp6": 25 / 32}[dt]
 
 
 def step_bytes(spec, seq_lens, sel, cnt):

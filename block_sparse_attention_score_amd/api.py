@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import MSA_BF16, MSA_F32, MSA_FP8_E4M3, MSA_FP8_E5M2, MSA_MXFP4, Params, check, load
+from ._lib import (MSA_BF16, MSA_F32, MSA_FP8_E4M3, MSA_FP8_E5M2, MSA_MXFP4, MSA_MXFP6, Params,
+                   check, load)
 
 BLOCK = 128
 
@@ -54,7 +55,7 @@ class MsaConfig:
 
     def params(self) -> Params:
         code = {"bf16": MSA_BF16, "f32": MSA_F32, "fp8": MSA_FP8_E4M3,
-                "fp8_e5m2": MSA_FP8_E5M2, "mxfp4": MSA_MXFP4}
+                "fp8_e5m2": MSA_FP8_E5M2, "mxfp4": MSA_MXFP4, "mxfp6": MSA_MXFP6}
         return Params(self.num_q_heads, self.num_kv_heads, self.num_idx_heads, self.head_dim,
                       self.idx_dim, self.block_size, self.topk, self.init_blocks,
                       self.local_blocks, self.softmax_scale, code[self.q_dtype],
@@ -306,13 +307,16 @@ def fp8_dequant(codes: torch.Tensor, scale: float = 1.0, out=None, fmt: str = "f
                 stream=None):
     """fp8 codes (uint8; fmt "fp8" = e4m3, "fp8_e5m2") -> float32 values times
     scale, as the loaders do it.  fmt "mxfp4": ``codes`` holds n / 2 code bytes
-    then n / 32 scale bytes (17 n / 32 bytes), and n values come back."""
+    then n / 32 scale bytes (17 n / 32 bytes), and n values come back; fmt
+    "mxfp6": 3 n / 4 code bytes then n / 32 scale bytes (25 n / 32 bytes)."""
     if codes.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2):
         raise ValueError("codes must be uint8, float8_e4m3fn or float8_e5m2")
-    code = {"fp8": MSA_FP8_E4M3, "fp8_e5m2": MSA_FP8_E5M2, "mxfp4": MSA_MXFP4}[fmt]
-    n = codes.numel() if fmt != "mxfp4" else codes.numel() * 32 // 17
+    code = {"fp8": MSA_FP8_E4M3, "fp8_e5m2": MSA_FP8_E5M2, "mxfp4": MSA_MXFP4,
+            "mxfp6": MSA_MXFP6}[fmt]
+    per32 = {"mxfp4": 17, "mxfp6": 25}.get(fmt)
+    n = codes.numel() if per32 is None else codes.numel() * 32 // per32
     if out is None:
-        shape = codes.shape if fmt != "mxfp4" else (n,)
+        shape = codes.shape if per32 is None else (n,)
         out = torch.empty(shape, dtype=torch.float32, device=codes.device)
     if out.numel() < n:
         raise ValueError("out holds fewer values than the codes")

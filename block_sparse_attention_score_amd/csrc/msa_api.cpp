@@ -62,8 +62,10 @@ int kmax_of(const msa_params_t& p) { return p.topk + p.init_blocks + p.local_blo
 int group_of(const msa_params_t& p) { return p.num_q_heads / p.num_kv_heads; }
 
 bool is_fp8(int dtype) { return dtype == MSA_FP8_E4M3 || dtype == MSA_FP8_E5M2; }
-// K/V formats whose per-tensor k_scale / v_scale apply (fp8 codes, MX-fp4)
-bool scaled_kv(int dtype) { return is_fp8(dtype) || dtype == MSA_MXFP4; }
+// K/V formats whose per-tensor k_scale / v_scale apply (fp8 codes, MX-fp4,
+// MX-fp6)
+bool is_mx(int dtype) { return dtype == MSA_MXFP4 || dtype == MSA_MXFP6; }
+bool scaled_kv(int dtype) { return is_fp8(dtype) || is_mx(dtype); }
 
 msa_status_t check_params(const msa_params_t* p) {
   if (p == nullptr) return fail(MSA_ERR_INVALID_ARG, "params is NULL");
@@ -104,6 +106,7 @@ msa_status_t check_params(const msa_params_t* p) {
                       (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_FP8_E4M3) ||
                       (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_FP8_E5M2) ||
                       (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_MXFP4) ||
+                      (p->q_dtype == MSA_BF16 && p->kv_dtype == MSA_MXFP6) ||
                       (p->q_dtype == MSA_F32 && p->kv_dtype == MSA_F32);
   if (!qkv_ok)
     return fail(MSA_ERR_UNSUPPORTED, "(q_dtype=%d, kv_dtype=%d) not supported", p->q_dtype,
@@ -1000,9 +1003,9 @@ msa_status_t msa_fp8_dequant(const uint8_t* in, float* out, int64_t n, float sca
   if (n > 0 && (!in || !out)) return fail(MSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!std::isfinite(scale)) return fail(MSA_ERR_INVALID_ARG, "scale must be finite");
   if (!scaled_kv(dtype))
-    return fail(MSA_ERR_UNSUPPORTED, "dtype=%d is not an fp8 or MX-fp4 format", dtype);
-  if (dtype == MSA_MXFP4 && n % 32 != 0)
-    return fail(MSA_ERR_INVALID_ARG, "MX-fp4: n=%lld is not a multiple of 32", (long long)n);
+    return fail(MSA_ERR_UNSUPPORTED, "dtype=%d is not an fp8 or MX format", dtype);
+  if (is_mx(dtype) && n % 32 != 0)
+    return fail(MSA_ERR_INVALID_ARG, "MX format: n=%lld is not a multiple of 32", (long long)n);
   msa_status_t st = check_grid((n / 8 + 1 + 255) / 256, 256, "fp8 dequant");
   if (st != MSA_OK) return st;
   st = hip_status(

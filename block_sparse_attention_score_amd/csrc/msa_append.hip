@@ -139,12 +139,65 @@ __device__ void quant_group_fp4(const void* src, int64_t si, float tscale, uint8
   *scale_byte = static_cast<uint8_t>(nan ? 255 : sc);
 }
 
+// E2M3 code of y (already divided by its group's power-of-two scale): the
+// nearest of the 32 magnitudes (k / 8 below 2, k / 4 in [2, 4), k / 2 from 4
+// to 7.5; clamped at 7.5), an exact tie going to the even code; the sign is
+// kept.  Within each range the value times its code density is rounded to
+// the nearest integer, ties to even (a power-of-two product, so exact), and
+// the code is that integer plus the range's offset (0, 8, 16), which keeps
+// the parity.
+__device__ __forceinline__ uint32_t e2m3_code(float y) {
+  const float m = fminf(fabsf(y), 7.5f);
+  const float dens = m < 2.f ? 8.f : (m < 4.f ? 4.f : 2.f);
+  const uint32_t off = m < 2.f ? 0u : (m < 4.f ? 8u : 16u);
+  const uint32_t c = static_cast<uint32_t>(__builtin_rintf(m * dens)) + off;
+  return c | (__float_as_uint(y) >> 31 << 5);
+}
+
+// One 32-element group of an MX-fp6 row, by the rule of quant_group_fp4 with
+// E2M3 codes (2 is also E2M3's largest exponent): 24 code bytes (element e at
+// bits 6 e of their little-endian value) and the scale byte.
+template <class KS>
+__device__ void quant_group_fp6(const void* src, int64_t si, float tscale, uint8_t* codes24,
+                                uint8_t* scale_byte) {
+  float y[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float x[8];
+    load8_plain(static_cast<const KS*>(nullptr), src, si + 8 * q, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[8 * q + e] = x[e] / tscale;
+  }
+  float amax = 0.f;
+  bool nan = false;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    nan |= y[e] != y[e];
+    amax = fmaxf(amax, fabsf(y[e]));
+  }
+  const int k = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 3 : -127;
+  const int sc = min(max(k + 127, 0), 254);
+  uint64_t w[3] = {0u, 0u, 0u};
+  if (!nan) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const uint64_t c = e2m3_code(ldexpf(y[e], 127 - sc));
+      const int pos = 6 * e;
+      w[pos / 64] |= c << (pos % 64);
+      if (pos % 64 > 58) w[pos / 64 + 1] |= c >> (64 - pos % 64);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) reinterpret_cast<uint64_t*>(codes24)[i] = w[i];
+  *scale_byte = static_cast<uint8_t>(nan ? 255 : sc);
+}
+
 // KS: storage of the new K/V rows; KP: of the K/V pools; IT: of the index
-// keys (new rows and pool alike).  A K/V piece is 8 elements, or, for MX-fp4
+// keys (new rows and pool alike).  A K/V piece is 8 elements, or, for MX
 // pools, one 32-element scale group.
 template <class KS, class KP, class IT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  constexpr int kPiece = __is_same(KP, FP4) ? 32 : 8;
+  constexpr int kPiece = __is_same(KP, FP4) || __is_same(KP, FP6) ? 32 : 8;
   const int vd = a.head_dim / kPiece;   // pieces per K/V row
   const int vi = a.idx_dim / 8;    // per index row
   const int n_kv = a.hkv * vd;
@@ -172,6 +225,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       quant_group_fp4<KS>(src, (static_cast<int64_t>(t) * a.hkv + h) * a.head_dim + c * 32,
                           is_v ? a.v_scale : a.k_scale, run + off * 64 + c * 16,
                           run + kFp4Codes + off * 4 + c);
+    } else if constexpr (__is_same(KP, FP6)) {
+      uint8_t* run = reinterpret_cast<uint8_t*>(pool) + (page * a.hkv + h) * kFp6Run;
+      quant_group_fp6<KS>(src, (static_cast<int64_t>(t) * a.hkv + h) * a.head_dim + c * 32,
+                          is_v ? a.v_scale : a.k_scale, run + off * 96 + c * 24,
+                          run + kFp6Codes + off * 4 + c);
     } else if constexpr (__is_same(KP, FP8) || __is_same(KP, BF8)) {
       float x[8];
       load8_plain(static_cast<const KS*>(nullptr), src, si, x);
@@ -202,7 +260,7 @@ static void launch_append_i(const AppendArgs& a, int idx_dtype, dim3 grid, hipSt
 
 hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  const int64_t per_token = 2 * a.hkv * (a.head_dim / (kv_dtype == 4 ? 32 : 8)) +
+  const int64_t per_token = 2 * a.hkv * (a.head_dim / (kv_dtype == 4 || kv_dtype == 5 ? 32 : 8)) +
                             (a.idx_v_pool != nullptr ? 2 : 1) * a.hidx * (a.idx_dim / 8);
   const int64_t blocks = (static_cast<int64_t>(a.num_tokens) * per_token + 255) / 256;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -211,6 +269,7 @@ hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipSt
   else if (kv_dtype == 2) launch_append_i<BF16, FP8>(a, idx_dtype, grid, s);
   else if (kv_dtype == 3) launch_append_i<BF16, BF8>(a, idx_dtype, grid, s);
   else if (kv_dtype == 4) launch_append_i<BF16, FP4>(a, idx_dtype, grid, s);
+  else if (kv_dtype == 5) launch_append_i<BF16, FP6>(a, idx_dtype, grid, s);
   else launch_append_i<F32, F32>(a, idx_dtype, grid, s);
   return hipGetLastError();
 }

@@ -60,21 +60,24 @@ struct QFrag<F32> {
   float4 a[8];
 };
 
-template <int G>
+// kGroupMajor (MX-fp6 K/V, below): step s takes dims 32 * (lane / 16) + 8 s
+// .. +8 instead, the dims a lane converts from one 32-element scale group.
+template <int G, bool kGroupMajor = false>
 __device__ __forceinline__ void load_qfrag(const BF16*, const void* q, int64_t row0,
                                            int qrow, int kgrp, QFrag<BF16>& f) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     if (qrow < G) {
+      const int d0 = kGroupMajor ? 32 * kgrp + 8 * s : 32 * s + 8 * kgrp;
       f.a[s] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const uint16_t*>(q) +
-                                                  (row0 + qrow) * 128 + 32 * s + 8 * kgrp);
+                                                  (row0 + qrow) * 128 + d0);
     } else {
       f.a[s] = bf16x8_t{};
     }
   }
 }
 
-template <int G>
+template <int G, bool kGroupMajor = false>
 __device__ __forceinline__ void load_qfrag(const F32*, const void* q, int64_t row0,
                                            int qrow, int kgrp, QFrag<F32>& f) {
 #pragma unroll
@@ -122,6 +125,16 @@ struct Row<FP4> {
   uint32_t c[4];
   uint32_t sc;
 };
+// MX-fp6: the lane's whole 32-element group q (dims 32q .. 32q + 31: 24 code
+// bytes) and its scale byte, converted by one instruction.  Chunk c is then
+// dims 32q + 8c .. +8: the contraction runs over the dims in another order
+// (the q fragment follows, load_qfrag<G, true>), and the V^T tiles come out
+// with dims permuted (fp6_dim_of below).
+template <>
+struct Row<FP6> {
+  uint32_t c[6];
+  uint32_t sc;
+};
 
 __device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, Row<BF16>& r) {
 #pragma unroll
@@ -151,6 +164,28 @@ __device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, 
 }
 __device__ __forceinline__ bf16x8_t fp4_chunk(const Row<FP4>& r, int c) {
   return fp4x8_to_bf16x8(r.c[c], e8m0_to_f32((r.sc >> (8 * c)) & 0xffu));
+}
+// An MX-fp6 (page, head) run is kFp6Run bytes: the lane's group sits at
+// token * 96 + 24 q (8-byte aligned), its scale at kFp6Codes + token * 4 + q.
+__device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, Row<FP6>& r) {
+  const uint8_t* run = reinterpret_cast<const uint8_t*>(pool) + (row0 >> 14) * kFp6Run;
+  const int tok = static_cast<int>(row0 >> 7) & 127;
+  const uint8_t* g = run + tok * 96 + 24 * q;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(g + 8 * i));
+    r.c[2 * i] = v[0];
+    r.c[2 * i + 1] = v[1];
+  }
+  r.sc = __builtin_nontemporal_load(run + kFp6Codes + tok * 4 + q);
+}
+__device__ __forceinline__ bf16x32_t fp6_group(const Row<FP6>& r) {
+  return fp6x32_to_bf16x32(r.c, e8m0_to_f32(r.sc));
+}
+// Dim of result row 4 q + rr of V^T tile m (MX-fp6 order): tile m takes chunk
+// m / 2 of lane groups 2 (m % 2) and 2 (m % 2) + 1.
+__device__ __forceinline__ int fp6_dim_of(int m, int q, int rr) {
+  return 64 * (m & 1) + 32 * (q >> 1) + 8 * (m >> 1) + 4 * (q & 1) + rr;
 }
 __device__ __forceinline__ void load_row(const void* pool, int64_t row0, int q, Row<F32>& r) {
 #pragma unroll
@@ -206,6 +241,14 @@ __device__ __forceinline__ f32x4_t st_tile(const QFrag<BF16>& qf, const Row<FP4>
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4_chunk(k, c), qf.a[c], acc, 0, 0, 0);
   return acc;
 }
+__device__ __forceinline__ f32x4_t st_tile(const QFrag<BF16>& qf, const Row<FP6>& k) {
+  const bf16x32_t kv = fp6_group(k);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16x32_part(kv, c), qf.a[c], acc, 0, 0, 0);
+  return acc;
+}
 __device__ __forceinline__ f32x4_t st_tile(const QFrag<F32>& qf, const Row<F32>& k) {
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -234,6 +277,19 @@ __device__ __forceinline__ f32x4_t vt_tile(const Row<K8>& v, int m, const bf16x8
 __device__ __forceinline__ f32x4_t vt_tile(const Row<FP4>& v, int m, const bf16x8_t (&sel)[2]) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4_chunk(v, m >> 1), sel[m & 1],
                                                  f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+// The V operand of the tiles: the stored row, or for MX-fp6 its group
+// converted once to bf16 (chunk c = dims 32 q + 8 c .. +8).
+template <class KT>
+__device__ __forceinline__ const Row<KT>& v_operand(const Row<KT>& r) {
+  return r;
+}
+__device__ __forceinline__ Row<BF16> v_operand(const Row<FP6>& r) {
+  const bf16x32_t v = fp6_group(r);
+  Row<BF16> o;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o.c[c] = bf16x32_part(v, c);
+  return o;
 }
 // f32: four 16x16x4 steps; step e contracts dim 16m + 4q + e against the
 // selector column (4q + e == lane % 16).
@@ -398,8 +454,9 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   const int q4 = lane >> 4;   // k-slot group; D rows 4*q4 .. +3
 
   // q^T as the B operand of S^T = K q^T (heads past G are zero columns).
+  constexpr bool kGroupMajor = __is_same(KT, FP6);
   QFrag<QT> qf;
-  load_qfrag<G>(qtag, a.q, hq0, l16, q4, qf);
+  load_qfrag<G, kGroupMajor>(qtag, a.q, hq0, l16, q4, qf);
 
   // Block ids and pages of this split (at most kMaxBps), resolved up front.
   const int bi0 = split * a.bps;
@@ -551,10 +608,12 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
 #pragma unroll
       for (int tp = 0; tp < TILES; tp += 2) {
         const bf16x8_t pb = pack8_rne(st[tp], st[tp + 1]);
+        const auto v0 = v_operand(vr[tp]);
+        const auto v1 = v_operand(vr[tp + 1]);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const f32x4_t va = vt_tile(vr[tp], m, sel_bf);
-          const f32x4_t vb = vt_tile(vr[tp + 1], m, sel_bf);
+          const f32x4_t va = vt_tile(v0, m, sel_bf);
+          const f32x4_t vb = vt_tile(v1, m, sel_bf);
           acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8_exact(va, vb), pb, acc[m], 0, 0, 0);
         }
       }
@@ -567,11 +626,13 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   for (int c = 0; c + 1 < nchunk; ++c) chunk(c, true);
   if (nchunk > 0) chunk(nchunk - 1, false);
 
-  // Merge the waves: lane (l16, q4) holds O^T[16m + 4q4 + r][head l16].
+  // Merge the waves: lane (l16, q4) holds O^T[16m + 4q4 + r][head l16]
+  // (MX-fp6: O^T[fp6_dim_of(m, q4, r)][head l16]).
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S.o[w][l16][16 * m + 4 * q4 + r] = acc[m][r];
+    for (int r = 0; r < 4; ++r)
+      S.o[w][l16][kGroupMajor ? fp6_dim_of(m, q4, r) : 16 * m + 4 * q4 + r] = acc[m][r];
   if (q4 == 0) {
     S.m[w][l16] = m_run;
     S.l[w][l16] = l_run;

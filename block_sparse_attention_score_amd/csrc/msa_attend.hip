@@ -55,6 +55,7 @@ hipError_t launch_decode_attend(const AttendArgs& a, int q_dtype, int kv_dtype, 
   else if (q_dtype == 0 && kv_dtype == 2) ok = launch_attend_g<BF16, FP8>(a, group, s);
   else if (q_dtype == 0 && kv_dtype == 3) ok = launch_attend_g<BF16, BF8>(a, group, s);
   else if (q_dtype == 0 && kv_dtype == 4) ok = launch_attend_g<BF16, FP4>(a, group, s);
+  else if (q_dtype == 0 && kv_dtype == 5) ok = launch_attend_g<BF16, FP6>(a, group, s);
   else if (q_dtype == 1 && kv_dtype == 1) ok = launch_attend_g<F32, F32>(a, group, s);
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();

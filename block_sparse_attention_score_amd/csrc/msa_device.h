@@ -21,11 +21,17 @@ struct F32 {};
 struct FP8 {};   // OCP fp8 E4M3 ("e4m3fn") codes
 struct BF8 {};   // OCP fp8 E5M2 codes
 struct FP4 {};   // OCP MX-fp4: E2M1 codes with an E8M0 scale per 32 elements
+struct FP6 {};   // OCP MX-fp6: E2M3 codes with an E8M0 scale per 32 elements
 
 // MX-fp4 pools hold, per (page, head), the 128 x 128 / 2 code bytes (element
 // 2i of a row in the low nibble of byte i) and then the 128 x 4 scale bytes.
 constexpr int kFp4Codes = 128 * 128 / 2;
 constexpr int kFp4Run = kFp4Codes + 128 * 4;
+// MX-fp6 pools: per (page, head) the 128 x 96 code bytes (a 32-element group
+// in 24 bytes, element i at bits 6 i .. 6 i + 5 of their little-endian value)
+// and then the 128 x 4 scale bytes.
+constexpr int kFp6Codes = 128 * 128 * 3 / 4;
+constexpr int kFp6Run = kFp6Codes + 128 * 4;
 
 // ---------------------------------------------------------------- loads
 
@@ -211,6 +217,23 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t w, float scale) {
   const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
   const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
   return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// One 32-element E2M3 group (its 24 bytes in the low six words) times a
+// scale, to bf16, in one gfx950 scaled conversion (exact for the same reason
+// as E2M1: every E2M3 value times a power of two in bf16's range is a bf16
+// value).
+typedef int i32x6_t __attribute__((ext_vector_type(6)));
+typedef __bf16 bf16x32_t __attribute__((ext_vector_type(32)));
+__device__ __forceinline__ bf16x32_t fp6x32_to_bf16x32(const uint32_t (&w)[6], float scale) {
+  const i32x6_t v = {static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]),
+                     static_cast<int>(w[3]), static_cast<int>(w[4]), static_cast<int>(w[5])};
+  return __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(v, scale);
+}
+// Elements 8 c .. 8 c + 7 of a converted group.
+__device__ __forceinline__ bf16x8_t bf16x32_part(const bf16x32_t& v, int c) {
+  return bf16x8_t{v[8 * c], v[8 * c + 1], v[8 * c + 2], v[8 * c + 3],
+                  v[8 * c + 4], v[8 * c + 5], v[8 * c + 6], v[8 * c + 7]};
 }
 
 // Eight consecutive elements packed as bf16 for an MFMA operand.  fp8 codes

@@ -108,6 +108,26 @@ template <>
 struct RawOf<FP4> {
   typedef uint8_t elem;  // (unused: MX-fp4 runs are addressed in bytes below)
 };
+template <>
+struct RawOf<FP6> {
+  typedef uint8_t elem;  // (unused: MX-fp6 runs are addressed in bytes below)
+};
+// Eight E2M3 codes (dims d0 .. d0 + 7, d0 a multiple of 8, of a key row) from
+// an MX-fp6 run, times their group's scale: the 6 code bytes start at row * 96
+// + 3 d0 / 4, 4-byte aligned when d0 / 8 is even and 2 bytes past that
+// otherwise, so one dword-aligned 8-byte load covers them; the codes are
+// shifted down to bit 0 and converted by the 32-code instruction (its upper
+// 24 codes zero and unused).
+__device__ __forceinline__ bf16x8_t fp6x8_load(__amdgpu_buffer_rsrc_t r, uint32_t row_byte,
+                                               int d0, uint32_t soff, uint32_t scale_off) {
+  const uint32_t b = static_cast<uint32_t>(3 * d0 / 4);
+  const auto raw = __builtin_amdgcn_raw_buffer_load_b64(r, row_byte + (b & ~3u), soff, 0);
+  const uint64_t v = (static_cast<uint64_t>(raw[1]) << 32 | raw[0]) >> (8 * (b & 3u));
+  const uint32_t e = __builtin_amdgcn_raw_buffer_load_b8(r, scale_off, 0, 0);
+  const uint32_t w[6] = {static_cast<uint32_t>(v), static_cast<uint32_t>(v >> 32) & 0xffffu,
+                         0u, 0u, 0u, 0u};
+  return bf16x32_part(fp6x32_to_bf16x32(w, e8m0_to_f32(e)), 0);
+}
 // Eight elements at byte offset voff + soff of a run, as bf16.
 __device__ __forceinline__ bf16x8_t load8_buf(const BF16*, __amdgpu_buffer_rsrc_t r, uint32_t voff,
                                               uint32_t soff) {
@@ -381,6 +401,20 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
                                                                kk * 4, 0);
         vraw[kk] = fp4x8_to_bf16x8(w, e8m0_to_f32(e));
       }
+    } else if constexpr (__is_same(KT, FP6)) {
+      // an MX-fp6 run per (page, head): per key row 96 code bytes, and its
+      // four scale bytes after all codes
+      const int64_t rb = (h0 >> 14) * kFp6Run;
+      const auto ks = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(reinterpret_cast<const char*>(a.k_pool)) + rb, 0, kFp6Run, 0x00020000);
+      const auto vs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(reinterpret_cast<const char*>(a.v_pool)) + rb, 0, kFp6Run, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        kraw[i] = fp6x8_load(ks, kr * 96, dc, 32 * i * 96, kFp6Codes + (32 * i + kr) * 4 + dc / 32);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        vraw[kk] = fp6x8_load(vs, (4 * kr + kk) * 96, dc, 0, kFp6Codes + (4 * kr + kk) * 4 + dc / 32);
     } else {
       const auto kr_src = run_rsrc(a.k_pool, h0 * kEb);
       const auto vr_src = run_rsrc(a.v_pool, h0 * kEb);
@@ -733,6 +767,7 @@ hipError_t launch_prefill_attend(const PrefillAttnArgs& a, int kv_dtype, int gro
     else if (kv_dtype == 2) ok = launch_pf_attend_g<FP8>(a, group, s);
     else if (kv_dtype == 3) ok = launch_pf_attend_g<BF8>(a, group, s);
     else if (kv_dtype == 4) ok = launch_pf_attend_g<FP4>(a, group, s);
+    else if (kv_dtype == 5) ok = launch_pf_attend_g<FP6>(a, group, s);
     if (!ok) return hipErrorInvalidValue;
   }
   // 16 / G (token, kv head) units per combine workgroup

@@ -164,13 +164,28 @@ __global__ void fp4_dequant_kernel(const uint8_t* in, float* out, int64_t n, flo
   for (int k = 0; k < 8; ++k) out[i + k] = static_cast<float>(v[k]) * scale;
 }
 
+// MX-fp6: 3 n / 4 code bytes, then n / 32 scale bytes; one 32-element group
+// per thread (byte copies: the buffer's alignment is not known).
+__global__ void fp6_dequant_kernel(const uint8_t* in, float* out, int64_t n, float scale) {
+  const int64_t grp = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (grp * 32 >= n) return;
+  uint32_t w[6];
+  __builtin_memcpy(w, in + grp * 24, 24);
+  const bf16x32_t v = fp6x32_to_bf16x32(w, e8m0_to_f32(in[n / 32 * 24 + grp]));
+  for (int k = 0; k < 32; ++k) out[grp * 32 + k] = static_cast<float>(v[k]) * scale;
+}
+
 hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale, int dtype,
                               hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t threads = (n + 7) / 8;
   const int64_t blocks = (threads + 255) / 256;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  if (dtype == 4)
+  if (dtype == 5) {
+    const int64_t groups = n / 32;
+    const int64_t gblocks = (groups + 255) / 256;
+    if (gblocks > 0) fp6_dequant_kernel<<<static_cast<unsigned>(gblocks), 256, 0, s>>>(in, out, n, scale);
+  } else if (dtype == 4)
     fp4_dequant_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(in, out, n, scale);
   else if (dtype == 3)
     fp8_dequant_kernel<BF8><<<static_cast<unsigned>(blocks), 256, 0, s>>>(in, out, n, scale);

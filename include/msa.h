@@ -93,7 +93,7 @@ typedef enum {
   MSA_FP8_E5M2 = 3, /* OCP e5m2: bias 15, S.11111.00 = inf, other S.11111.xx NaN
                        (the sglang page keeps fp8 main caches of either format
                        on its sparse path that dequantises on load) */
-  MSA_MXFP4 = 4     /* OCP MX-fp4 K/V pools: E2M1 codes (s.ee.m, bias 1: 0, 0.5,
+  MSA_MXFP4 = 4,    /* OCP MX-fp4 K/V pools: E2M1 codes (s.ee.m, bias 1: 0, 0.5,
                        1, 1.5, 2, 3, 4, 6) with an E8M0 scale 2^(e - 127) (0xFF
                        NaN) per 32 elements; per (page, head) the 128 x 64 code
                        bytes (element 2i of a row in the low nibble of byte i)
@@ -101,6 +101,15 @@ typedef enum {
                        at head_dim 128.  The gfx950 counterpart of the vLLM
                        page's 4-bit K/V caches with block scales in per-head
                        slots (MiniMaxM3SparseMSANvfp4Backend). */
+  MSA_MXFP6 = 5     /* OCP MX-fp6 K/V pools: E2M3 codes (s.ee.mmm, bias 1:
+                       k / 8 below 2, then steps of 1/4 and 1/2 up to 7.5)
+                       with the same E8M0 scale per 32 elements; per (page,
+                       head) the 128 x 96 code bytes (a 32-element group in 24
+                       bytes, element i at bits 6i .. 6i + 5 of their
+                       little-endian value) then the 128 x 4 scale bytes:
+                       pools [P, Hkv, 12800] bytes at head_dim 128.  The other
+                       block-scaled width gfx950 converts in hardware; a finer
+                       grid than E2M1 at 25/32 byte per element. */
 } msa_dtype_t;
 
 /*
@@ -111,7 +120,7 @@ typedef enum {
  *   idx_dim in {64, 128}, topk in {4, 8, 16, 32}, 0 <= init, local <= 64,
  *   Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8, 16}, Hkv % Hidx == 0,
  *   (q_dtype, kv_dtype) in {(bf16, bf16), (bf16, fp8_e4m3), (bf16, fp8_e5m2),
- *   (bf16, mxfp4), (f32, f32)},
+ *   (bf16, mxfp4), (bf16, mxfp6), (f32, f32)},
  *   idx_dtype in {bf16, f32} (idx_q and idx_k share it).
  */
 typedef struct {
@@ -128,8 +137,8 @@ typedef struct {
   int32_t q_dtype;       /* msa_dtype_t */
   int32_t kv_dtype;      /* msa_dtype_t */
   int32_t idx_dtype;     /* msa_dtype_t */
-  float k_scale;         /* fp8 and MX-fp4 only: k = stored value * k_scale */
-  float v_scale;         /* fp8 and MX-fp4 only: v = stored value * v_scale */
+  float k_scale;         /* fp8 and MX only: k = stored value * k_scale */
+  float v_scale;         /* fp8 and MX only: v = stored value * v_scale */
   int32_t forced_in_budget; /* 0: S = F U top-k of the rest (|S| = min(nb,
                             |F| + topk)); 1: the forced blocks count inside
                             the budget, S = F U top-max(topk - |F|, 0) of the
@@ -324,7 +333,8 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q,
  *   2^(floor(log2 max|y|) - 2) clamped to the code range (an all-zero group
  *   takes code 0, a group with a NaN the NaN code and zero codes) and each
  *   element's E2M1 code nearest to y / 2^(code - 127), ties to the even code,
- *   clamped at 6 (the OCP Microscaling rule).
+ *   clamped at 6 (the OCP Microscaling rule).  MX-fp6 pools the same with
+ *   E2M3 codes, clamped at 7.5.
  *   With params->index_value, idx_v_new [T, Hidx, Di] (idx_dtype) goes to
  *   idx_v_pool beside the index keys (the page stores idx_v unless the layer
  *   disables the value branch); otherwise both must be NULL.
@@ -352,6 +362,7 @@ msa_status_t msa_fp8_e4m3_dequant(const uint8_t* in, float* out, int64_t n,
  * MSA_MXFP4: in holds n / 2 code bytes then n / 32 scale bytes (n a
  * multiple of 32, the order of one pool run) and out[i] = code value times
  * its group's scale, through the loaders' conversion, times scale.
+ * MSA_MXFP6: the same with 3 n / 4 code bytes then n / 32 scale bytes.
  * MSA_ERR_UNSUPPORTED for any other dtype.
  */
 msa_status_t msa_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale,
