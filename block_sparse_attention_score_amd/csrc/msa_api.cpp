@@ -232,6 +232,7 @@ struct PrefillLayout {
   size_t scores, sel, cnt, part_o, part_lse, tickets;
   size_t iv_o, iv_lse;  // index-value branch: partials per (token, index head, key run)
   size_t counts, cursor, tok_off, tile_off, csr, items, n_items, sink;  // key-major only
+  size_t forced_off;  // key-major: forced-block token groups before each sequence [B + 1]
   size_t total;
   int bps, nsplit_max;
   int tq, max_items;  // key-major only
@@ -262,6 +263,7 @@ PrefillLayout prefill_layout(const msa_params_t& p, int32_t B, int32_t T, int32_
     l.csr = take(sizeof(int32_t) * entries);
     l.items = take(sizeof(msa::Tile) * size_t(l.max_items));
     l.n_items = take(sizeof(int32_t));
+    l.forced_off = take(sizeof(int32_t) * (size_t(B) + 1));
     const size_t parts = size_t(T) * p.num_kv_heads * kmax * G;
     l.part_o = take(sizeof(uint16_t) * parts * p.head_dim);  // bf16
     l.part_lse = take(sizeof(float) * parts);
@@ -942,6 +944,9 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
     ka.hkv = p.num_kv_heads;
     ka.hidx = p.num_idx_heads;
     ka.tq = l.tq;
+    ka.init = p.init_blocks;
+    ka.local = p.local_blocks;
+    ka.forced_split = p.init_blocks + p.local_blocks > 0 ? 1 : 0;
     ka.counts = reinterpret_cast<int32_t*>(w + l.counts);
     ka.cursor = reinterpret_cast<int32_t*>(w + l.cursor);
     ka.tok_off = reinterpret_cast<int32_t*>(w + l.tok_off);
@@ -949,6 +954,8 @@ msa_status_t msa_sparse_prefill(const msa_params_t* params, const void* q, const
     ka.csr = reinterpret_cast<int32_t*>(w + l.csr);
     ka.items = reinterpret_cast<msa::Tile*>(w + l.items);
     ka.n_items = reinterpret_cast<int32_t*>(w + l.n_items);
+    ka.forced_off = reinterpret_cast<int32_t*>(w + l.forced_off);
+    ka.tqf = msa::kForcedRows / group_of(p);
     ka.max_items = l.max_items;
     const float ks = scaled_kv(p.kv_dtype) ? p.k_scale : 1.f;
     ka.qk_scale_log2 = softmax_scale_of(p) * ks * 1.4426950408889634f;

@@ -175,6 +175,7 @@ constexpr int kMaxSelect = 160;        // topk + init + local, at most
 constexpr int kPrefillTileRows = 256;  // query rows (token x GQA head) per tile
 // Blocks of keys per prefill scoring (and index-value) workgroup.
 constexpr int kPrefillBlocksPerChunk = 16;
+constexpr int kForcedRows = 128;       // query rows (token x GQA head) per forced-block group
 struct PrefillAttnArgs {
   const void* q;             // [T, Hq, D] bf16
   const void* k_pool;        // [P, Hkv, 128, D]
@@ -191,6 +192,15 @@ struct PrefillAttnArgs {
   int32_t kmax;
   int32_t hkv, hidx;
   int32_t tq;                // tokens per tile: kPrefillTileRows / G
+  // forced_split: the forced blocks (the first `init` and the last `local`
+  // visible ones of every token) run in the query-major forced kernel, which
+  // writes one partial per (token, kv head) into the token's first forced
+  // slot; the lists leave them out and the combine reads only that slot of
+  // them
+  int32_t init, local;
+  int32_t forced_split;
+  int32_t* forced_off;       // [B + 1] forced-block token groups before each sequence
+  int32_t tqf;               // tokens per forced-block group: kForcedRows / G
   // k2q lists, per (b, index head, block j): counts and cursor zero on entry
   int32_t* counts;           // [B * Hidx * max_blocks]
   int32_t* cursor;           // [B * Hidx * max_blocks]
@@ -235,6 +245,7 @@ hipError_t launch_decode_attend(const AttendArgs& a, int q_dtype, int kv_dtype,
 hipError_t launch_prefill_k2q(const PrefillAttnArgs& a, hipStream_t s);
 hipError_t launch_prefill_attend(const PrefillAttnArgs& a, int kv_dtype, int group,
                                  hipStream_t s);
+
 hipError_t launch_append(const AppendArgs& a, int kv_dtype, int idx_dtype, hipStream_t s);
 hipError_t launch_prefill_value(const PrefillValueArgs& a, int idx_dim, hipStream_t s);
 hipError_t launch_fp8_dequant(const uint8_t* in, float* out, int64_t n, float scale, int dtype,

@@ -16,7 +16,12 @@
 //      ends up holding 8-dim runs of its output row); S^T = K Q^T and
 //      O^T = V^T P^T on bf16 MFMA, causal mask per row; a normalised partial
 //      (o in bf16, lse in f32) per (token, kv head, slot);
-//   3. per (token, kv head), the log-sum-exp combine of its partials.
+//   3. the forced blocks (the first `init` and the last `local` visible blocks
+//      of every token) query-major: consecutive tokens share them, so one
+//      workgroup runs a group of tokens over their union with an online
+//      softmax and writes one partial per (token, kv head); the lists of
+//      step 1 hold only the top-k entries;
+//   4. per (token, kv head), the log-sum-exp combine of its partials.
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -192,6 +197,30 @@ __device__ __forceinline__ Tile read_tile(const ConstTile* p) {
 
 }  // namespace
 
+// The forced blocks of the token at position p (a selection row of nb = p /
+// 128 + 1 visible blocks, clipped to the table): [0, init') and [lo, nb), as
+// the selection forces them, and the token's first forced selection slot,
+// where its forced partial goes.  All empty when the forced blocks are not
+// split off.
+struct ForcedRange {
+  int init_end;  // init' = min(init, nb)
+  int lo;        // first local block, max(0, nb - local) (nb when local = 0)
+  int nb;
+  __device__ bool has(int j) const { return j < init_end || (j >= lo && j < nb); }
+  __device__ int count() const { return init_end + (nb - lo) - max(0, init_end - lo); }
+  // the selection lists the forced blocks first (init) and last (local), in
+  // ascending order: the first forced slot is 0, or cnt - (forced count) when
+  // init' = 0
+  __device__ int first_slot(int cnt) const { return init_end > 0 ? 0 : cnt - count(); }
+};
+__device__ __forceinline__ ForcedRange forced_range(const PrefillAttnArgs& a, int p) {
+  ForcedRange r;
+  r.nb = (a.forced_split && p >= 0) ? min(p / kBlock + 1, a.max_blocks) : 0;
+  r.init_end = min(a.init, r.nb);
+  r.lo = a.local > 0 ? max(0, r.nb - a.local) : r.nb;
+  return r;
+}
+
 // ---------------------------------------------------------------- k2q CSR
 
 // Workgroup (chunk c, sequence b, index head h): the 256 tokens
@@ -212,9 +241,10 @@ __global__ __launch_bounds__(kWgThreads) void k2q_count_kernel(PrefillAttnArgs a
   if (i_tok < n_b) {
     const int row = (cu0 + i_tok) * a.hidx + h;
     const int n = min(max(a.cnt[row], 0), a.kmax);
+    const ForcedRange fr = forced_range(a, a.seq_lens[b] - n_b + i_tok);
     for (int s = 0; s < n; ++s) {
       const int j = a.sel[static_cast<int64_t>(row) * a.kmax + s];
-      if (j >= 0 && j < a.max_blocks) atomicAdd(&hist[j], 1);
+      if (j >= 0 && j < a.max_blocks && !fr.has(j)) atomicAdd(&hist[j], 1);
     }
   }
   __syncthreads();
@@ -250,6 +280,25 @@ __global__ __launch_bounds__(1024) void k2q_scan_kernel(PrefillAttnArgs a, int n
     __syncthreads();
   }
   if (tid == 0) *a.n_items = min(carry[1], a.max_items);
+  // forced-block token groups of each sequence, exclusive prefix (the forced
+  // kernel's units, sequence by sequence)
+  if (a.forced_split) {
+    __syncthreads();
+    if (tid == 0) carry[0] = 0;
+    __syncthreads();
+    for (int base = 0; base < a.num_seqs; base += 1024) {
+      const int i = base + tid;
+      const int ng = i < a.num_seqs
+                         ? (a.cu_seqlens_q[i + 1] - a.cu_seqlens_q[i] + a.tqf - 1) / a.tqf
+                         : 0;
+      const int c0 = carry[0];
+      const int incl = block_incl_scan(ng, wsum);
+      if (i < a.num_seqs) a.forced_off[i] = c0 + incl - ng;
+      if (tid == 1023) carry[0] = c0 + incl;
+      __syncthreads();
+    }
+    if (tid == 0) a.forced_off[a.num_seqs] = carry[0];
+  }
 }
 
 // Same workgroups as the count: append (token, slot) to the list of every
@@ -271,9 +320,10 @@ __global__ __launch_bounds__(kWgThreads) void k2q_fill_kernel(PrefillAttnArgs a)
   const int t = cu0 + i_tok;
   const int row = t * a.hidx + h;
   const int n = i_tok < n_b ? min(max(a.cnt[row], 0), a.kmax) : 0;
+  const ForcedRange fr = forced_range(a, a.seq_lens[b] - n_b + i_tok);
   for (int s = 0; s < n; ++s) {
     const int j = a.sel[static_cast<int64_t>(row) * a.kmax + s];
-    if (j >= 0 && j < a.max_blocks) atomicAdd(&hist[j], 1);
+    if (j >= 0 && j < a.max_blocks && !fr.has(j)) atomicAdd(&hist[j], 1);
   }
   __syncthreads();
   const int64_t bh0 = (static_cast<int64_t>(b) * a.hidx + h) * a.max_blocks;
@@ -282,7 +332,7 @@ __global__ __launch_bounds__(kWgThreads) void k2q_fill_kernel(PrefillAttnArgs a)
   __syncthreads();
   for (int s = 0; s < n; ++s) {
     const int j = a.sel[static_cast<int64_t>(row) * a.kmax + s];
-    if (j < 0 || j >= a.max_blocks) continue;
+    if (j < 0 || j >= a.max_blocks || fr.has(j)) continue;
     a.csr[atomicAdd(&hist[j], 1)] = (t << 8) | s;
   }
 
@@ -665,6 +715,303 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_attend_kernel(PrefillAt
   }
 }
 
+// ---------------------------------------------------------- forced blocks
+
+// Workgroup (group grp of TQ = 128 / G consecutive tokens of sequence b, kv
+// head g; four waves): the 128 query rows (token x G heads, row r = 32 w +
+// 16 nt + l16 is token slot r / G, head r % G) keep their query rows in
+// registers and run the union of their tokens' forced blocks: [0, init') and
+// the local windows [nb_t - local, nb_t), which for consecutive tokens form
+// one range.  Per block: K and V^T staged in LDS as in the tiles, S^T on the
+// matrix cores, each row masking the keys after its position and the blocks
+// outside its own forced set, an online softmax (base 2), O^T += V^T P^T.
+// The normalised partial and its lse go to the token's first forced slot.
+// Two workgroups share a CU, so one's block loads run under the other's
+// matrix work; the grid holds two per CU over the kv heads, each walking
+// units (sequence, token group) from the offsets the list scan computes.
+constexpr int kFwWaves = 4;
+constexpr int kFwThreads = kFwWaves * kWave;
+constexpr int kFwRows = kForcedRows;
+static_assert(kFwRows == 32 * kFwWaves, "each wave owns 32 query rows");
+
+// One unit of the forced-block kernel: token group grp of sequence b, kv
+// head blockIdx.y.
+template <class KT, int G>
+__device__ void forced_unit(const PrefillAttnArgs& a, int b, int grp, PfStage& S) {
+  constexpr int TQ = kFwRows / G;
+  const KT* ktag = nullptr;
+  const BF16* qtag = nullptr;
+  const int g = blockIdx.y;
+  const int h = g / (a.hkv / a.hidx);
+  const int cu0 = a.cu_seqlens_q[b];
+  const int n_b = a.cu_seqlens_q[b + 1] - cu0;
+  const int i0 = grp * TQ;
+  if (i0 >= n_b) return;
+  const int L = a.seq_lens[b];
+  const int prefix = L - n_b;
+  const int ilast = min(n_b, i0 + TQ) - 1;
+  const ForcedRange f0 = forced_range(a, prefix + i0);
+  const ForcedRange f1 = forced_range(a, prefix + ilast);
+  // the union: blocks [0, f1.init_end), then [max(f1.init_end, f0.lo), f1.nb)
+  // (f1.nb - 1 is the last token's own block, forced whenever local > 0)
+  const int e_init = f1.init_end;
+  const int lo2 = max(e_init, f0.lo);
+  const int hi2 = a.local > 0 ? f1.nb : lo2;
+  const int nblk = e_init + max(0, hi2 - lo2);
+  if (nblk == 0) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = tid / kWave;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int kr = tid >> 4;           // staging: K keys 16 i + kr, V keys 8 kr .. + 8
+  const int dc = (tid & 15) * 8;     // staging dims dc .. dc + 8
+
+  // this lane's two query rows, their positions and their tokens'
+  // selection sizes (all loads of the unit's start in flight together with
+  // the first block's); the rest is recomputed from them where needed
+  int pos[2], cntv[2];
+  bf16x8_t qf[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = 32 * w + 16 * nt + l16;
+    const int i = i0 + r / G;
+    pos[nt] = i <= ilast ? prefix + i : -1;  // -1 masks every key
+    const int t = cu0 + min(i, ilast);
+    cntv[nt] = a.cnt[static_cast<int64_t>(t) * a.hidx + h];
+    const int64_t qo = (static_cast<int64_t>(t) * a.hkv * G + g * G + r % G) * 128 + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[nt][ks] = load8_cached(qtag, a.q, qo + 32 * ks);
+  }
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4_t o[8][2];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt][0] = o[dt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto block_of = [&](int u) { return u < e_init ? u : lo2 + (u - e_init); };
+  const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+  int page_next = bt_row[block_of(0)];
+  for (int u = 0; u < nblk; ++u) {
+    const int j = block_of(u);
+    // ---- stage block j: K rows as they are, V^T in the tiles' permuted dim
+    // order; a missing page reads page 0 with every key masked (nvalid = 0),
+    // V rows at or past the sequence end cleared (0 * NaN would reach the sums)
+    const int page = page_next;
+    if (u + 1 < nblk) page_next = bt_row[block_of(u + 1)];
+    const bool page_ok = page >= 0 && page < a.num_pages;
+    const int nvalid = page_ok ? max(0, min(kBlock, L - j * kBlock)) : 0;
+    const int64_t h0 = (static_cast<int64_t>(page_ok ? page : 0) * a.hkv + g) * kBlock * 128;
+    // K rows 16 i + kr and V rows 8 kr + i of the thread: all eight of each in
+    // one pass, or for the MX formats in two passes of four, which keeps the
+    // conversions' registers to one half
+    constexpr int RP = (__is_same(KT, FP4) || __is_same(KT, FP6)) ? 4 : 8;  // rows per pass
+#pragma unroll
+    for (int hh = 0; hh < 8 / RP; ++hh) {
+      bf16x8_t kraw[RP], vraw[RP];
+      if constexpr (__is_same(KT, FP4)) {
+        const int64_t rb = (h0 >> 14) * kFp4Run;
+        const auto ks = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(reinterpret_cast<const char*>(a.k_pool)) + rb, 0, kFp4Run, 0x00020000);
+        const auto vs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(reinterpret_cast<const char*>(a.v_pool)) + rb, 0, kFp4Run, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+          const int kro = 16 * (RP * hh + i) + kr, vro = 8 * kr + RP * hh + i;
+          const uint32_t kw = __builtin_amdgcn_raw_buffer_load_b32(ks, kro * 64 + dc / 2, 0, 0);
+          const uint32_t ke = __builtin_amdgcn_raw_buffer_load_b8(ks, kFp4Codes + kro * 4 + dc / 32, 0, 0);
+          const uint32_t vw = __builtin_amdgcn_raw_buffer_load_b32(vs, vro * 64 + dc / 2, 0, 0);
+          const uint32_t ve = __builtin_amdgcn_raw_buffer_load_b8(vs, kFp4Codes + vro * 4 + dc / 32, 0, 0);
+          kraw[i] = fp4x8_to_bf16x8(kw, e8m0_to_f32(ke));
+          vraw[i] = fp4x8_to_bf16x8(vw, e8m0_to_f32(ve));
+        }
+      } else if constexpr (__is_same(KT, FP6)) {
+        const int64_t rb = (h0 >> 14) * kFp6Run;
+        const auto ks = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(reinterpret_cast<const char*>(a.k_pool)) + rb, 0, kFp6Run, 0x00020000);
+        const auto vs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(reinterpret_cast<const char*>(a.v_pool)) + rb, 0, kFp6Run, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+          const int kro = 16 * (RP * hh + i) + kr, vro = 8 * kr + RP * hh + i;
+          kraw[i] = fp6x8_load(ks, kro * 96, dc, 0, kFp6Codes + kro * 4 + dc / 32);
+          vraw[i] = fp6x8_load(vs, vro * 96, dc, 0, kFp6Codes + vro * 4 + dc / 32);
+        }
+      } else {
+        constexpr int kEb = sizeof(typename RawOf<KT>::elem);
+        const auto kr_src = run_rsrc(a.k_pool, h0 * kEb);
+        const auto vr_src = run_rsrc(a.v_pool, h0 * kEb);
+        const uint32_t k_lane = static_cast<uint32_t>(kr * 128 + dc) * kEb;
+        const uint32_t v_lane = static_cast<uint32_t>(8 * kr * 128 + dc) * kEb;
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+          kraw[i] = load8_buf(ktag, kr_src, k_lane, 16 * (RP * hh + i) * 128 * kEb);
+#pragma unroll
+        for (int i = 0; i < RP; ++i) vraw[i] = load8_buf(ktag, vr_src, v_lane, (RP * hh + i) * 128 * kEb);
+      }
+      if (nvalid < kBlock) {
+#pragma unroll
+        for (int i = 0; i < RP; ++i) mask_bf16x8(vraw[i], 8 * kr + RP * hh + i < nvalid);
+      }
+#pragma unroll
+      for (int i = 0; i < RP; ++i)
+        *reinterpret_cast<bf16x8_t*>(&S.k[(16 * (RP * hh + i) + kr) * kStrideK + dc]) = kraw[i];
+      uint16_t v[RP][8];
+#pragma unroll
+      for (int i = 0; i < RP; ++i) __builtin_memcpy(&v[i][0], &vraw[i], 16);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+#pragma unroll
+        for (int q = 0; q < RP / 4; ++q) {
+          const uint32_t w0 = static_cast<uint32_t>(v[4 * q][d]) | (static_cast<uint32_t>(v[4 * q + 1][d]) << 16);
+          const uint32_t w1 = static_cast<uint32_t>(v[4 * q + 2][d]) | (static_cast<uint32_t>(v[4 * q + 3][d]) << 16);
+          *reinterpret_cast<u32x2_t*>(&S.vt[vt_row_of_dim(dc + d) * kStrideV + 8 * kr + RP * hh + 4 * q]) =
+              u32x2_t{w0, w1};
+        }
+      }
+    }
+    __syncthreads();
+
+    // The whole block at once: S^T for its 128 keys, one online-softmax step.
+    // S^T tiles: keys 16 mt + 4 q4 + r, query rows 16 nt + l16.
+    const int tok0 = j * kBlock;
+    f32x4_t st[8][2];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      st[mt][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      st[mt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8_t kf = lds_b128(&S.k[(16 * mt + l16) * kStrideK + 32 * ks + 8 * q4]);
+        st[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], st[mt][0], 0, 0, 0);
+        st[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], st[mt][1], 0, 0, 0);
+      }
+    }
+    // Masking (keys past the sequence end or after the row's position, or a
+    // block outside the row's forced set) only where the block is not
+    // entirely visible to every row of the wave.
+    bool in[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) in[nt] = forced_range(a, pos[nt]).has(j);
+    const bool full = in[0] && in[1] && nvalid == kBlock && tok0 + kBlock - 1 <= min(pos[0], pos[1]);
+    if (__builtin_amdgcn_ballot_w64(!full) != 0) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = 16 * mt + 4 * q4 + r;
+            const bool ok = in[nt] && key < nvalid && tok0 + key <= pos[nt];
+            st[mt][nt][r] = ok ? st[mt][nt][r] : -INFINITY;
+          }
+    }
+    float alpha[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float mr = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mr = max_nan(mr, st[mt][nt][r]);
+      const float mn = max_nan(m_run[nt], rows_max(mr) * a.qk_scale_log2);
+      // a row with nothing visible so far keeps m = -inf; its p are 2^-inf = 0
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      alpha[nt] = exp2_raw(m_run[nt] - mu);
+      float ls = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = exp2_raw(fmaf(st[mt][nt][r], a.qk_scale_log2, -mu));
+          st[mt][nt][r] = e;
+          ls += e;
+        }
+      l_run[nt] = l_run[nt] * alpha[nt] + rows_sum(ls);
+      m_run[nt] = mn;
+    }
+    // the output is rescaled only where some row's maximum moved
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f) != 0) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        o[dt][0] *= alpha[0];
+        o[dt][1] *= alpha[1];
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      // 32-key step: keys 32 kk + 4 q4 + e (e < 4) and + 16 (e >= 4)
+      bf16x8_t pb[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const uint32_t pu[4] = {pack2_rne(st[2 * kk][nt][0], st[2 * kk][nt][1]),
+                                pack2_rne(st[2 * kk][nt][2], st[2 * kk][nt][3]),
+                                pack2_rne(st[2 * kk + 1][nt][0], st[2 * kk + 1][nt][1]),
+                                pack2_rne(st[2 * kk + 1][nt][2], st[2 * kk + 1][nt][3])};
+        __builtin_memcpy(&pb[nt], pu, 16);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint16_t* row = &S.vt[(16 * dt + l16) * kStrideV + 32 * kk + 4 * q4];
+        const u32x2_t lo = lds_b64(row), hi2 = lds_b64(row + 16);
+        const u32x4_t cat = {lo[0], lo[1], hi2[0], hi2[1]};
+        bf16x8_t vf;
+        __builtin_memcpy(&vf, &cat, 16);
+        o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[0], o[dt][0], 0, 0, 0);
+        o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[1], o[dt][1], 0, 0, 0);
+      }
+    }
+    // every wave is done with the stage before the next block is written
+    __syncthreads();
+  }
+
+  // the normalised partial and its lse, in the token's first forced slot
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    if (pos[nt] < 0) continue;
+    const int r = 32 * (threadIdx.x / kWave) + 16 * nt + (threadIdx.x & 15);
+    const int t = cu0 + i0 + r / G;
+    const int cnt = min(max(cntv[nt], 0), a.kmax);
+    // (a selection always holds its forced blocks: cnt >= their count)
+    const int slot = min(max(forced_range(a, pos[nt]).first_slot(cnt), 0), a.kmax - 1);
+    const float l = l_run[nt];
+    const float inv = l > 0.f ? a.v_scale * __builtin_amdgcn_rcpf(l) : 0.f;
+    const int64_t base = ((static_cast<int64_t>(t) * a.hkv + g) * a.kmax + slot) * G + r % G;
+    uint16_t* po = a.part_o + base * 128 + 8 * q4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4_t v = {pack2_rne(o[2 * k][nt][0] * inv, o[2 * k][nt][1] * inv),
+                         pack2_rne(o[2 * k][nt][2] * inv, o[2 * k][nt][3] * inv),
+                         pack2_rne(o[2 * k + 1][nt][0] * inv, o[2 * k + 1][nt][1] * inv),
+                         pack2_rne(o[2 * k + 1][nt][2] * inv, o[2 * k + 1][nt][3] * inv)};
+      *reinterpret_cast<u32x4_t*>(po + 32 * k) = v;
+    }
+    if (q4 == 0)
+      a.part_lse[base] = l > 0.f ? (m_run[nt] + __builtin_amdgcn_logf(l)) * kLn2f : -INFINITY;
+  }
+}
+
+
+template <class KT, int G>
+__global__ __launch_bounds__(kFwThreads, 2) void prefill_forced_kernel(PrefillAttnArgs a) {
+  __shared__ PfStage S;
+  // the workgroups of one XCD (x, x + 8, ...) walk a contiguous range of
+  // units, so a sequence's init blocks and the local blocks its neighbouring
+  // groups share are fetched into one L2
+  const int total = a.forced_off[a.num_seqs];
+  const int per = (total + 7) / 8;
+  const int hi = min((static_cast<int>(blockIdx.x) % 8 + 1) * per, total);
+  for (int unit = (blockIdx.x % 8) * per + blockIdx.x / 8; unit < hi; unit += gridDim.x / 8) {
+    int lo = 0, up = a.num_seqs;  // forced_off[lo] <= unit < forced_off[up]
+    while (up - lo > 1) {
+      const int mid = (lo + up) / 2;
+      if (a.forced_off[mid] <= unit) lo = mid; else up = mid;
+    }
+    forced_unit<KT, G>(a, lo, unit - a.forced_off[lo], S);
+  }
+}
+
 // ---------------------------------------------------------------- combine
 
 // out = sum_s exp(lse_s - lse) o_s per (token, kv head), lse = log sum_s
@@ -684,7 +1031,27 @@ __global__ __launch_bounds__(kWgThreads) void prefill_combine_kernel(PrefillAttn
   const int hh = (tid / 16) % G;
   const int d0 = (tid % 16) * 8;
   const int h = g / (a.hkv / a.hidx);
-  const int n = min(max(a.cnt[t * a.hidx + h], 0), a.kmax);
+  const int cnt = min(max(a.cnt[t * a.hidx + h], 0), a.kmax);
+  // With the forced blocks split off, the token's forced slots hold one
+  // partial, in the first of them (slot 0, or the first local slot when
+  // init' = 0): the slots read are that one and the top-k slots
+  // [init', cnt - local'), n = cnt - forced + 1 of them.
+  int n = cnt, skip_from = 1, skip = 0;
+  if (a.forced_split) {
+    int lo = 0, hi = a.num_seqs;  // cu[lo] <= t < cu[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (a.cu_seqlens_q[mid] <= t) lo = mid; else hi = mid;
+    }
+    const int p = a.seq_lens[lo] - (a.cu_seqlens_q[lo + 1] - a.cu_seqlens_q[lo]) +
+                  (t - a.cu_seqlens_q[lo]);
+    const ForcedRange fr = forced_range(a, p);
+    const int nf = fr.count();
+    if (nf > 0 && cnt >= nf) {
+      n = cnt - nf + 1;
+      skip = fr.init_end > 0 ? fr.init_end - 1 : 0;  // read u >= 1 at slot u + skip
+    }
+  }
   const int64_t row0 = (static_cast<int64_t>(t) * a.hkv + g) * a.kmax * G + hh;  // slot 0
   const float* lse_p = a.part_lse + row0;
   const uint16_t* po = a.part_o + row0 * 128 + d0;
@@ -696,7 +1063,8 @@ __global__ __launch_bounds__(kWgThreads) void prefill_combine_kernel(PrefillAttn
     u32x4_t v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t s = min(s0 + u, n - 1);
+      const int uc = min(s0 + u, n - 1);
+      const int64_t s = uc >= skip_from ? uc + skip : uc;
       ls[u] = lse_p[s * G];
       v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(po + s * G * 128));
     }
@@ -758,6 +1126,23 @@ static bool launch_pf_attend_g(const PrefillAttnArgs& a, int group, hipStream_t 
   }
 }
 
+// Two resident four-wave workgroups per CU over all kv heads.
+constexpr int kForcedWorkgroups = 512;
+
+template <class KT>
+static bool launch_pf_forced_g(const PrefillAttnArgs& a, int group, hipStream_t s) {
+  // (a multiple of 8: one set per XCD)
+  const dim3 grid(static_cast<unsigned>(max(8, kForcedWorkgroups / a.hkv / 8 * 8)), a.hkv);
+  switch (group) {
+    case 1: prefill_forced_kernel<KT, 1><<<grid, kFwThreads, 0, s>>>(a); return true;
+    case 2: prefill_forced_kernel<KT, 2><<<grid, kFwThreads, 0, s>>>(a); return true;
+    case 4: prefill_forced_kernel<KT, 4><<<grid, kFwThreads, 0, s>>>(a); return true;
+    case 8: prefill_forced_kernel<KT, 8><<<grid, kFwThreads, 0, s>>>(a); return true;
+    case 16: prefill_forced_kernel<KT, 16><<<grid, kFwThreads, 0, s>>>(a); return true;
+    default: return false;
+  }
+}
+
 hipError_t launch_prefill_attend(const PrefillAttnArgs& a, int kv_dtype, int group,
                                  hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
@@ -768,6 +1153,15 @@ hipError_t launch_prefill_attend(const PrefillAttnArgs& a, int kv_dtype, int gro
     else if (kv_dtype == 3) ok = launch_pf_attend_g<BF8>(a, group, s);
     else if (kv_dtype == 4) ok = launch_pf_attend_g<FP4>(a, group, s);
     else if (kv_dtype == 5) ok = launch_pf_attend_g<FP6>(a, group, s);
+    if (!ok) return hipErrorInvalidValue;
+  }
+  if (a.forced_split) {
+    if (kv_dtype == 0) ok = launch_pf_forced_g<BF16>(a, group, s);
+    else if (kv_dtype == 2) ok = launch_pf_forced_g<FP8>(a, group, s);
+    else if (kv_dtype == 3) ok = launch_pf_forced_g<BF8>(a, group, s);
+    else if (kv_dtype == 4) ok = launch_pf_forced_g<FP4>(a, group, s);
+    else if (kv_dtype == 5) ok = launch_pf_forced_g<FP6>(a, group, s);
+    else ok = false;
     if (!ok) return hipErrorInvalidValue;
   }
   // 16 / G (token, kv head) units per combine workgroup

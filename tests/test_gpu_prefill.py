@@ -92,6 +92,32 @@ def test_prefill_small(msa, name):
     print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
 
 
+# The forced blocks (init and local) of long chunks run query-major over
+# groups of consecutive tokens, one merged partial per token in its first
+# forced slot: no init blocks (that slot is the first local one), no local
+# blocks, every visible block forced, none forced, and groups that straddle a
+# block boundary (prefixes off the 128 grid).
+FORCED_SPLIT = {
+    "init0_local2": _spec([300, 200], [1000, 77], Hq=8, Hkv=2, Hidx=2, topk=4, init=0, local=2),
+    "init2_local0": _spec([300], [2000], Hq=8, Hkv=1, Hidx=1, topk=4, init=2, local=0),
+    "all_forced": _spec([300, 50], [0, 100], Hq=8, Hkv=2, Hidx=1, topk=4, init=3, local=3),
+    "none_forced": _spec([200], [1500], Hq=8, Hkv=2, Hidx=2, topk=8, init=0, local=0),
+    "init3_local4_g16": _spec([400, 33], [5000, 1234], Hq=16, Hkv=1, Hidx=1, topk=8, init=3,
+                              local=4),
+}
+
+
+@pytest.mark.parametrize("name", list(FORCED_SPLIT))
+def test_prefill_forced_split(msa, name):
+    spec = FORCED_SPLIT[name]
+    seed = 2100 + sorted(FORCED_SPLIT).index(name)
+    print(f"[prefill_forced_split] {name} seed={seed}", flush=True)
+    case = generate(spec, seed, device="cuda")
+    g = _run(msa, case, spec)
+    err, nband = _compare(host_view(case), g, spec, np.arange(case.T))
+    print(f"  max {err[0]:.3g} mean {err[1]:.3g} band-rows {nband}", flush=True)
+
+
 # Multi-token decode (speculative verification): a few new tokens per
 # sequence over long contexts, causal among themselves, each with its own
 # selection -- the prefill call with short chunks.
