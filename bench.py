@@ -201,11 +201,12 @@ PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 COPY_PROBE_BYTES = 1 << 30
 # The kernels whose counters make a workload's roofline traffic, and the
 # sources a measurement stays valid for: the decode index scan; the prefill
-# attention stage (k2q lists, key-major tiles, combine), per step.
+# attention stage (k2q lists, key-major tiles, forced blocks, combine), per
+# step.
 SCAN_SOURCES = ["msa_score.h", "msa_score.hip", "msa_device.h", "msa_internal.h"]
 STAGE_SOURCES = ["msa_prefill_attend.hip", "msa_device.h", "msa_internal.h"]
 STAGE_KERNELS = ["k2q_count_kernel", "k2q_scan_kernel", "k2q_fill_kernel",
-                 "prefill_attend_kernel", "prefill_combine_kernel"]
+                 "prefill_attend_kernel", "prefill_forced_kernel", "prefill_combine_kernel"]
 
 
 def traffic_json(workload_name: str) -> str:
@@ -630,7 +631,8 @@ def measure_prefill(args, name, headline):
     score_tf = f_score / (score_ms * 1e-3) / 1e12
     attn_tf = f_attn / (attn_ms * 1e-3) / 1e12
     dominant = "attention" if attn_ms >= score_ms else "score"
-    roof = {"kernel": "prefill attention stage (k2q lists, key-major MFMA tiles, combine)",
+    roof = {"kernel": "prefill attention stage (k2q lists, key-major MFMA tiles, forced blocks, "
+                      "combine)",
             "bound": "mfma", "achieved": attn_tf, "peak": peak, "unit": "TFLOP/s",
             "frac": attn_tf / peak, "traffic": measured_traffic(name), "flops_per_launch": f_attn,
             "ms_per_launch": attn_ms} if dominant == "attention" else \
