@@ -226,7 +226,8 @@ __device__ __forceinline__ ForcedRange forced_range(const PrefillAttnArgs& a, in
 // Workgroup (chunk c, sequence b, index head h): the 256 tokens
 // cu[b] + 256 c + tid count their selected blocks in an LDS histogram of the
 // sequence's max_blocks bins, then add the non-zero bins to the lists' counts
-// (the forced blocks are shared by every token: one global atomic per bin).
+// (blocks many tokens select cost one global atomic per bin).  With the
+// forced blocks split off, a token's init and local entries are left out.
 __global__ __launch_bounds__(kWgThreads) void k2q_count_kernel(PrefillAttnArgs a) {
   extern __shared__ int hist[];
   const int b = blockIdx.y;
