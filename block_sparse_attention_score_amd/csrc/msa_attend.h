@@ -40,6 +40,7 @@ namespace msa {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kMaxBps = 32;  // selected blocks per split workgroup, at most
+constexpr int kWaveSelectMax = 1024;  // longest row selected on one wave
 
 // ----------------------------------------------------------- q fragments
 
@@ -357,6 +358,7 @@ struct AttendLds {
   int blk_nvalid[kMaxBps];
   int blk_page[kMaxBps];
   int blk_j[kMaxBps];      // block ids of the split (selection inside the kernel)
+  int row_page[kWaveSelectMax];  // the row's block-table entries (one-wave selections)
   int is_last;
   SelectLds sl;
 };
@@ -386,9 +388,33 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   constexpr int kThreads = kWave * W;
   const int h = g / (a.hkv / a.hidx);
   const int sel_row = t * a.hidx + h;
+  const bool self_select = a.scores != nullptr;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = tid / kWave;
+  // Rows of at most kWaveSelectMax blocks are selected on wave 0.  Their
+  // scores (wave 0) and block-table entries (the other waves, into LDS) are
+  // fetched over the whole max_blocks row before the sequence length is
+  // known, so that neither waits for it; slots past the row are ignored.
+  static_assert(W >= 2, "waves 1.. stage the block table");
+  const bool wave_rows = self_select && a.max_blocks > 0 && a.max_blocks <= kWaveSelectMax;
+  float sv[16];
+  if (wave_rows && w == 0) {
+    const float* srow = a.scores + static_cast<int64_t>(sel_row) * a.max_blocks;
+    if (a.max_blocks <= 256) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[e] = srow[min(lane + kWave * e, a.max_blocks - 1)];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sv[e] = srow[min(lane + kWave * e, a.max_blocks - 1)];
+    }
+  }
   int b, p;
   query_of(a, t, b, p);
-  const bool self_select = a.scores != nullptr;
+  if (wave_rows && w > 0) {
+    const int* bt = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
+    for (int j = tid - kWave; j < a.max_blocks; j += kThreads - kWave) S.row_page[j] = bt[j];
+  }
   // Blocks visible to the query, and the selection size that follows from
   // them alone (init and local blocks plus min(topk, rest)).
   const int nb_vis = p >= 0 ? min(p / kBlock + 1, a.max_blocks) : 0;
@@ -406,9 +432,6 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   // the index head.
   const bool sel_writer = self_select && a.sel_out != nullptr && split == 0 &&
                           g % (a.hkv / a.hidx) == 0;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int w = tid / kWave;
   const int64_t hq0 = static_cast<int64_t>(t) * a.hkv * G + static_cast<int64_t>(g) * G;
   const QT* qtag = nullptr;
   const KT* ktag = nullptr;
@@ -471,9 +494,20 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
     };
     // One wave selects rows of up to 1024 blocks; longer rows take the
     // workgroup radix select.
-    if (nb_vis <= 256) {
+    if (wave_rows) {
+      if (w == 0) {
+        if (nb_vis <= 256) {
+          float v4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = sv[e];
+          select_wave_loaded<4>(v4, nb_vis, topk_row, a.init, a.local, emit);
+        } else {
+          select_wave_loaded<16>(sv, nb_vis, topk_row, a.init, a.local, emit);
+        }
+      }
+    } else if (nb_vis <= 256) {
       if (w == 0) select_wave<4>(srow, nb_vis, topk_row, a.init, a.local, emit);
-    } else if (nb_vis <= 1024) {
+    } else if (nb_vis <= kWaveSelectMax) {
       if (w == 0) select_wave<16>(srow, nb_vis, topk_row, a.init, a.local, emit);
     } else {
       select_core<div_up(8192, kThreads), kThreads>(srow, nb_vis, topk_row, a.init, a.local, S.sl,
@@ -488,8 +522,10 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   if (tid < nblk) {
     const int64_t at = static_cast<int64_t>(sel_row) * a.kmax + bi0 + tid;
     const int j = self_select ? S.blk_j[tid] : a.sel[at];
-    const int page =
-        j >= 0 && j < a.max_blocks ? a.block_table[static_cast<int64_t>(b) * a.max_blocks + j] : -1;
+    const int page = j >= 0 && j < a.max_blocks
+                         ? (wave_rows ? S.row_page[j]
+                                      : a.block_table[static_cast<int64_t>(b) * a.max_blocks + j])
+                         : -1;
     const bool ok = page >= 0 && page < a.num_pages && j >= 0;
     S.blk_nvalid[tid] = ok ? max(0, min(kBlock, p + 1 - j * kBlock)) : 0;
     S.blk_page[tid] = ok ? page : 0;

@@ -160,7 +160,9 @@ __device__ int select_core(const float* __restrict__ s, int nb, int topk, int in
 
 // The same selection on one wave (no barrier, no LDS): block j sits in lane
 // j % 64, slot j / 64, with E >= ceil(nb / 64).  T, the key of the k-th best
-// candidate, is found bit by bit from the top with ballot counts; candidates
+// candidate, is found bit by bit with ballot counts, from the highest bit in
+// which the candidates' keys differ (the wave's largest and smallest key give
+// it; the bits above are common to all candidates and so to T); candidates
 // above T are taken, and of those equal to T the first ones in block order
 // (ranks from ballot prefix counts), which is the lower-index tie rule.
 // Output slots come from the same prefix counts, so the list is ascending.
@@ -173,6 +175,26 @@ __device__ __forceinline__ void load_row_scores(const float* __restrict__ s, int
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int e = 0; e < E; ++e) v[e] = s[min(lane + kWave * e, max(n - 1, 0))];
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum of an unsigned value over the wavefront (all lanes active), as a
+// uniform value: DPP maxima within each row of 16 lanes, then the four rows.
+__device__ __forceinline__ uint32_t wave_umax_uniform(uint32_t v) {
+  v = max(v, dpp_u<kDppXor1>(v));
+  v = max(v, dpp_u<kDppXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  v = max(v, dpp_u<kDppMirror>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(static_cast<int>(v), 0);
+  const uint32_t r1 = __builtin_amdgcn_readlane(static_cast<int>(v), 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(static_cast<int>(v), 32);
+  const uint32_t r3 = __builtin_amdgcn_readlane(static_cast<int>(v), 48);
+  return max(max(r0, r1), max(r2, r3));
 }
 
 template <int E, class Emit>
@@ -203,11 +225,34 @@ __device__ int select_wave_loaded(const float (&v)[E], int nb, int topk, int ini
   if (!take_all && keff == 0) {
     T = 0xFFFFFFFFu;  // no candidate joins the forced blocks
   } else if (!take_all) {
-    for (int bit = 31; bit >= 0; --bit) {
+    // Bits above the highest one in which the candidates' keys differ are
+    // the same in every candidate, hence in T: the search starts below them
+    // (for those bits every probe would count all candidates or none).
+    uint32_t hi = 0u, lo_inv = 0u;  // max key, ~min key over the candidates
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      hi = max(hi, cand[e] ? key[e] : 0u);
+      lo_inv = max(lo_inv, cand[e] ? ~key[e] : 0u);
+    }
+    hi = wave_umax_uniform(hi);
+    const uint32_t diff = hi ^ ~wave_umax_uniform(lo_inv);
+    int top = -1;
+    if (diff == 0u) {
+      T = hi;  // all candidates equal: T is their key
+    } else {
+      top = 31 - __builtin_clz(diff);
+      T = hi & ~((2u << top) - 1u);
+    }
+    for (int bit = top; bit >= 0; --bit) {
       const uint32_t c = T | (1u << bit);
+      // all masks first, then their counts: each compare writes a mask of
+      // its own, so the compares do not wait for one another's counts
+      uint64_t bm[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) bm[e] = __builtin_amdgcn_ballot_w64(key[e] >= c);
       int n = 0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) n += count(key[e] >= c);
+      for (int e = 0; e < E; ++e) n += __popcll(bm[e]);
       if (n == keff) {
         // exactly the selection: it is {key > c - 1}, with no tie to break
         T = c - 1;

@@ -208,6 +208,49 @@ def test_planted_selection_exact(msa, case):
     assert sel.cpu()[0, 0, : int(cnt.cpu()[0, 0])].tolist() == case["expected"]
 
 
+@pytest.mark.parametrize("width", [0, 300, 1100], ids=["mb_nb", "mb300", "mb1100"])
+@pytest.mark.parametrize("case", [c for c in _golden_cases() if c["topk"] in (4, 8, 16, 32)],
+                         ids=lambda c: c["name"])
+def test_planted_selection_in_decode(msa, case, width):
+    """The same planted rows through msa_sparse_decode, whose attention
+    workgroups select in-kernel: with the table as wide as the row, 300 wide
+    (a row fetched 16 slots per lane, selected as 4) and 1100 wide (past the
+    one-wave rows, the row fetched after the length).  Unused table columns
+    hold -1."""
+    nb, tail, Di = case["nb"], case["tail"], 64
+    L = (nb - 1) * 128 + tail
+    MB = max(width, nb)
+    P = nb + 3
+    g = torch.Generator().manual_seed(nb)
+    perm = torch.randperm(P, generator=g)
+    bt = torch.full((1, MB), -1, dtype=torch.int32)
+    bt[0, :nb] = perm[:nb].to(torch.int32)
+    ik = torch.randn((P, 1, 128, Di), generator=g)
+    ik[:, :, :, 0] = -1000.0
+    scores = [(-0.0 if s == "-0" else float(s)) for s in case["scores"]]
+    for j in range(nb):
+        valid = 128 if j < nb - 1 else tail
+        ik[bt[0, j], 0, (37 * j + 11) % valid, 0] = scores[j]
+    if "decoy" in case and tail < 128:
+        ik[bt[0, nb - 1], 0, tail:, 0] = case["decoy"]
+    iq = torch.zeros((1, 1, Di))
+    iq[0, 0, 0] = 1.0
+    kp = torch.randn((P, 1, 128, 128), generator=g).to(torch.bfloat16).cuda()
+    vp = torch.randn((P, 1, 128, 128), generator=g).to(torch.bfloat16).cuda()
+    q = torch.randn((1, 1, 128), generator=g).to(torch.bfloat16).cuda()
+    cfg = msa.MsaConfig(num_q_heads=1, num_kv_heads=1, num_idx_heads=1, idx_dim=Di,
+                        topk=case["topk"], init_blocks=case["init"],
+                        local_blocks=case["local"])
+    sl = torch.tensor([L], dtype=torch.int32).cuda()
+    _, _, sel, cnt = msa.sparse_decode(cfg, q, iq.to(torch.bfloat16).cuda(), kp, vp,
+                                       ik.to(torch.bfloat16).cuda(), bt.cuda(), sl,
+                                       return_selection=True)
+    torch.cuda.synchronize()
+    n = int(cnt.cpu()[0, 0])
+    assert sel.cpu()[0, 0, :n].tolist() == case["expected"]
+    assert (sel.cpu()[0, 0, n:] == -1).all()
+
+
 # ----------------------------------------------------------- full sizes
 
 FULL = ["decode_b32_l32k", "decode_b64_lvar", "decode_fp8_b32_l64k"]
