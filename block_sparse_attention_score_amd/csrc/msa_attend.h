@@ -434,7 +434,6 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
                           g % (a.hkv / a.hidx) == 0;
   const int64_t hq0 = static_cast<int64_t>(t) * a.hkv * G + static_cast<int64_t>(g) * G;
   const QT* qtag = nullptr;
-  const KT* ktag = nullptr;
 
   // Index-value branch (decode): split 0 of the first kv head of each index
   // head merges the scan's chunk partials of its row into idx_out,
