@@ -348,9 +348,14 @@ __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp
 
 // ---------------------------------------------------------- split unit
 
+// Row stride of the per-wave partial outputs in LDS: 132 floats (528 bytes)
+// put the 16 head rows of one 16-byte store pass on 16 distinct groups of
+// four banks; at 128 floats every row of the pass would hit the same banks.
+constexpr int kOStride = kBlock + 4;
+
 template <int G, int W>
 struct AttendLds {
-  float o[W][16][kBlock];  // per-wave partial outputs, [head][dim]
+  alignas(16) float o[W][16][kOStride];  // per-wave partial outputs, [head][dim]
   float m[W][16];          // per-wave running max (base 2, scaled logits)
   float l[W][16];          // per-wave running sum
   float m_all[16];
@@ -662,12 +667,13 @@ __device__ void attend_split(const AttendArgs& a, int split, int g, int t, Atten
   if (nchunk > 0) chunk(nchunk - 1, false);
 
   // Merge the waves: lane (l16, q4) holds O^T[16m + 4q4 + r][head l16]
-  // (MX-fp6: O^T[fp6_dim_of(m, q4, r)][head l16]).
+  // (MX-fp6: O^T[fp6_dim_of(m, q4, r)][head l16]), four consecutive dims per
+  // m, stored as one 16-byte write.
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      S.o[w][l16][kGroupMajor ? fp6_dim_of(m, q4, r) : 16 * m + 4 * q4 + r] = acc[m][r];
+  for (int m = 0; m < 8; ++m) {
+    const int d0 = kGroupMajor ? fp6_dim_of(m, q4, 0) : 16 * m + 4 * q4;
+    *reinterpret_cast<f32x4_t*>(&S.o[w][l16][d0]) = acc[m];
+  }
   if (q4 == 0) {
     S.m[w][l16] = m_run;
     S.l[w][l16] = l_run;
