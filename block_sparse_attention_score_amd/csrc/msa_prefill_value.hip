@@ -27,12 +27,19 @@ namespace {
 constexpr int kIvWaves = 8;
 constexpr int kIvThreads = kIvWaves * kWave;  // 512
 constexpr int kIvRows = 32 * kIvWaves;        // query rows per workgroup
-constexpr int kKeyStride = kBlock + 8;        // V^T row stride (bf16 elements)
+// LDS row strides in bf16 elements, by gfx950's bank rules (64 banks of 4
+// bytes): the 8-byte V^T fragment reads of 16 rows are conflict-free at a
+// 264-byte row, and the 16-byte K fragment reads of 16 rows at a 288-byte
+// row (Di = 128); the transposing V^T stores are conflict-free at 264 bytes
+// with the staging map below.
+constexpr int kKeyStride = kBlock + 4;  // V^T row stride
+template <int DI>
+constexpr int kKStride = DI == 128 ? DI + 16 : DI + 8;  // K row stride
 constexpr float kLn2v = 0.69314718055994531f;
 
 template <int DI>
 struct IvStage {
-  alignas(16) uint16_t k[kBlock * (DI + 8)];  // K   [key][dim]
+  alignas(16) uint16_t k[kBlock * kKStride<DI>];  // K   [key][dim]
   alignas(16) uint16_t vt[DI * kKeyStride];   // V^T [dim][key]
 };
 
@@ -128,6 +135,11 @@ __global__ __launch_bounds__(kIvThreads, 1) void prefill_value_kernel(PrefillVal
   // staging: K rows KPP * i + kr, dims dc .. dc + 8; V rows VKEYS * kr + kk
   const int kr = tid / LPK;
   const int dc = (tid % LPK) * 8;
+  // V: at Di = 128 the lanes of a wave take 8 key groups x 8 dim chunks, so
+  // that one transposing store of the wave (rows 8 c + d, 4 keys each) covers
+  // every bank exactly twice
+  const int kvr = DI == 128 ? (tid % 8) + 8 * (tid / 128) : kr;
+  const int vdc = DI == 128 ? ((tid / 8) % 16) * 8 : dc;
   const int* bt_row = a.block_table + static_cast<int64_t>(b) * a.max_blocks;
   u32x4_t kraw[KPASS], vraw[VKEYS];
   int nvalid_next = 0;
@@ -146,16 +158,16 @@ __global__ __launch_bounds__(kIvThreads, 1) void prefill_value_kernel(PrefillVal
 #pragma unroll
     for (int kk = 0; kk < VKEYS; ++kk)
       vraw[kk] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4_t*>(vp + (VKEYS * kr + kk) * DI + dc));
+          reinterpret_cast<const u32x4_t*>(vp + (VKEYS * kvr + kk) * DI + vdc));
   };
   auto stage = [&](IvStage<DI>& B, int nvalid) {
 #pragma unroll
     for (int i = 0; i < KPASS; ++i)
-      *reinterpret_cast<u32x4_t*>(&B.k[(KPP * i + kr) * (DI + 8) + dc]) = kraw[i];
+      *reinterpret_cast<u32x4_t*>(&B.k[(KPP * i + kr) * kKStride<DI> + dc]) = kraw[i];
     // value rows past the sequence end hold stale bytes (possibly NaN):
     // cleared, since 0 * NaN would reach the MFMA sums
 #pragma unroll
-    for (int kk = 0; kk < VKEYS; ++kk) clear8(vraw[kk], VKEYS * kr + kk < nvalid);
+    for (int kk = 0; kk < VKEYS; ++kk) clear8(vraw[kk], VKEYS * kvr + kk < nvalid);
     uint16_t v[VKEYS][8];
 #pragma unroll
     for (int kk = 0; kk < VKEYS; ++kk) __builtin_memcpy(&v[kk][0], &vraw[kk], 16);
@@ -164,9 +176,9 @@ __global__ __launch_bounds__(kIvThreads, 1) void prefill_value_kernel(PrefillVal
       if constexpr (VKEYS == 4) {
         const u32x2_t pr = {static_cast<uint32_t>(v[0][d]) | (static_cast<uint32_t>(v[1][d]) << 16),
                             static_cast<uint32_t>(v[2][d]) | (static_cast<uint32_t>(v[3][d]) << 16)};
-        *reinterpret_cast<u32x2_t*>(&B.vt[(dc + d) * kKeyStride + 4 * kr]) = pr;
+        *reinterpret_cast<u32x2_t*>(&B.vt[(vdc + d) * kKeyStride + 4 * kvr]) = pr;
       } else {
-        *reinterpret_cast<uint32_t*>(&B.vt[(dc + d) * kKeyStride + 2 * kr]) =
+        *reinterpret_cast<uint32_t*>(&B.vt[(vdc + d) * kKeyStride + 2 * kvr]) =
             static_cast<uint32_t>(v[0][d]) | (static_cast<uint32_t>(v[1][d]) << 16);
       }
     }
@@ -199,7 +211,7 @@ __global__ __launch_bounds__(kIvThreads, 1) void prefill_value_kernel(PrefillVal
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-              &B.k[(64 * kh + 16 * mt + l16) * (DI + 8) + 32 * ks + 8 * q4]);
+              &B.k[(64 * kh + 16 * mt + l16) * kKStride<DI> + 32 * ks + 8 * q4]);
           st[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], st[mt][0], 0, 0, 0);
           st[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], st[mt][1], 0, 0, 0);
         }
