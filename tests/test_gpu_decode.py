@@ -251,6 +251,52 @@ def test_planted_selection_in_decode(msa, case, width):
     assert (sel.cpu()[0, 0, n:] == -1).all()
 
 
+@pytest.mark.parametrize("nb,topk,width,seed", [(257, 4, 257, 0), (300, 16, 305, 1),
+                                                (600, 32, 600, 2), (1024, 32, 1024, 3)])
+def test_long_row_ties(msa, nb, topk, width, seed):
+    """Rows of 257 to 1024 blocks (one wave, 16 slots per lane) whose scores
+    come from eight values, so that many blocks tie at the cutoff and -0 meets
+    +0: the selection made inside msa_sparse_decode's attention workgroups
+    and the one of msa_select_blocks must both be the oracle's (score desc,
+    lower block first on ties, forced init and local blocks added).  Table
+    columns past the row hold -1."""
+    print(f"[long_row_ties] nb={nb} topk={topk} width={width} seed={seed}", flush=True)
+    rng = np.random.default_rng(seed)
+    vals = np.array([-3.0, -2.0, -1.0, -0.0, 0.0, 0.5, 1.0, 2.0])
+    scores = vals[rng.integers(0, len(vals), nb)]
+    tail = 1 + int(rng.integers(0, 128))
+    L = (nb - 1) * 128 + tail
+    P, Di, init, local = nb + 3, 64, 1, 2
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(P, generator=g)
+    bt = torch.full((1, width), -1, dtype=torch.int32)
+    bt[0, :nb] = perm[:nb].to(torch.int32)
+    ik = torch.zeros((P, 1, 128, Di))
+    ik[:, :, :, 0] = -1000.0
+    for j in range(nb):
+        valid = 128 if j < nb - 1 else tail
+        ik[bt[0, j], 0, (37 * j + 11) % valid, 0] = float(scores[j])
+    iq = torch.zeros((1, 1, Di))
+    iq[0, 0, 0] = 1.0
+    kp = torch.randn((P, 1, 128, 128), generator=g).to(torch.bfloat16).cuda()
+    vp = torch.randn((P, 1, 128, 128), generator=g).to(torch.bfloat16).cuda()
+    q = torch.randn((1, 1, 128), generator=g).to(torch.bfloat16).cuda()
+    cfg = msa.MsaConfig(num_q_heads=1, num_kv_heads=1, num_idx_heads=1, idx_dim=Di, topk=topk,
+                        init_blocks=init, local_blocks=local)
+    sl = torch.tensor([L], dtype=torch.int32).cuda()
+    ikd, iqd, btd = ik.to(torch.bfloat16).cuda(), iq.to(torch.bfloat16).cuda(), bt.cuda()
+    expected = oracle.select_for_query(scores, nb, topk, init, local)
+    _, _, sel, cnt = msa.sparse_decode(cfg, q, iqd, kp, vp, ikd, btd, sl, return_selection=True)
+    s = msa.block_score(cfg, iqd, ikd, btd, sl)
+    sel2, cnt2 = msa.select_blocks(cfg, s, sl)
+    torch.cuda.synchronize()
+    assert [float(x) for x in s.cpu()[0, 0, :nb]] == [float(x) for x in scores]
+    for name, sl_, cn in (("decode", sel, cnt), ("select_blocks", sel2, cnt2)):
+        n = int(cn.cpu()[0, 0])
+        assert sl_.cpu()[0, 0, :n].tolist() == expected, name
+        assert (sl_.cpu()[0, 0, n:] == -1).all(), name
+
+
 # ----------------------------------------------------------- full sizes
 
 FULL = ["decode_b32_l32k", "decode_b64_lvar", "decode_fp8_b32_l64k"]
